@@ -1,0 +1,256 @@
+"""CPU fp64 oracle for the masked linear-attention sequence mixer (Mamba-2 /
+Mamba-2S / 2Mamba) -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this module.  It shares no code with the HIP path and imports nothing from it:
+it receives plain numpy arrays (the stored input values, upcast exactly to
+fp64) and computes everything in fp64, in the order the definitions state.
+
+Sources (2Mamba2Furious: Linear in Complexity, Competitive in Accuracy,
+Mongaras & Larson):
+
+* Algorithm 1 (linear attention): masked product y = (phi(Q) phi(K)^T * M) V,
+  normaliser = row sum of the same masked score matrix, output y / normaliser.
+* Algorithm 3 (Mamba-2 forward pass): A = -exp(A_log), dt = softplus(dt_P +
+  dt_bias), V_dt = V * dt, A^CS = cumsum(A * dt).
+* Algorithms 4 and 5 (Mamba-2S, 2Mamba): decay mask A^M_ij = exp(A^CS_i -
+  A^CS_j), causal mask M_ij = [i >= j], and for 2Mamba the scores are squared
+  and the normaliser is the row sum of the squared, masked scores.
+* Algorithm 6 (2Mamba inference, appendix): the recurrent form, with order-2
+  features k (x) k and the two states H_up (numerator) and H_down (normaliser)
+  decayed by a_t each step.
+
+Readings where the pages are silent or garbled (each is also listed with its
+reasoning in the design notes):
+
+* the cumulative sum is inclusive (torch/numpy cumsum), so M_ii = 1;
+* the normaliser is divided exactly: no epsilon, no absolute value;
+* the value operand is V * dt for both orders (Algorithm 5 prints plain V; a
+  caller reproduces that by passing the value operand directly);
+* phi is the identity inside the mixer (SiLU is applied upstream); order 2 uses
+  phi(x) = vec(x x^T) flattened row-major, D = d_h**2;
+* the missing output line of Algorithm 6 is y_t = phi(q_t)^T H_up_t /
+  phi(q_t)^T H_down_t using the states after the update at t;
+* the initial state is zero;
+* exp is only ever evaluated on masked (j <= i) differences, never on the
+  literal A^M over the whole square (which would overflow above the diagonal).
+
+Parity status: every function here is pinned by the CPU tests in
+tests/test_oracle.py (two independent forms agreeing to 1e-10, closed forms,
+special cases that reduce to textbook routines, invariants, and the hand-worked
+fixtures in tests/golden/).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# Discretisation (Algorithm 3)
+# ---------------------------------------------------------------------------
+
+def softplus(x):
+    """softplus(x) = log(1 + e^x), evaluated as max(x, 0) + log1p(exp(-|x|))."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+
+
+def discretise(dt_proj, dt_bias, A_log):
+    """Algorithm 3: dt = softplus(dt_P + dt_bias), A = -exp(A_log), a = A * dt.
+
+    dt_proj: [..., H, N]; dt_bias, A_log: [H].  Returns (dt, a) with the shape
+    of dt_proj; a is the per-token log-decay (always <= 0).
+    """
+    dt_proj = np.asarray(dt_proj, dtype=np.float64)
+    dt_bias = np.asarray(dt_bias, dtype=np.float64)
+    A = -np.exp(np.asarray(A_log, dtype=np.float64))
+    dt = softplus(dt_proj + dt_bias[:, None])
+    a = A[:, None] * dt
+    return dt, a
+
+
+def prep_ref(dt_proj, dt_bias, A_log, chunk):
+    """What ssd_prep returns, in fp64.
+
+    Returns (dt, a_cs, a_chunk): dt [B,H,N]; a_cs [B,H,N] the inclusive
+    cumulative sum of a = A*dt restarted at every chunk start (positions
+    c*chunk .. c*chunk+chunk-1); a_chunk [B,H,n_chunks] the total of a over each
+    chunk (the last chunk may be partial).  The global A^CS of Algorithm 3 is
+    a_cs plus the sum of the earlier chunk totals.
+    """
+    dt, a = discretise(dt_proj, dt_bias, A_log)
+    N = a.shape[-1]
+    n_chunks = -(-N // chunk)
+    a_cs = np.empty_like(a)
+    a_chunk = np.empty(a.shape[:-1] + (n_chunks,), dtype=np.float64)
+    for c in range(n_chunks):
+        seg = a[..., c * chunk:(c + 1) * chunk]
+        cs = np.cumsum(seg, axis=-1)
+        a_cs[..., c * chunk:(c + 1) * chunk] = cs
+        a_chunk[..., c] = cs[..., -1]
+    return dt, a_cs, a_chunk
+
+
+# ---------------------------------------------------------------------------
+# Feature maps
+# ---------------------------------------------------------------------------
+
+def features(x, order):
+    """phi(x): identity at order 1; vec(x x^T) (row-major, D = d_h^2) at order 2."""
+    x = np.asarray(x, dtype=np.float64)
+    if order == 1:
+        return x
+    if order == 2:
+        outer = x[..., :, None] * x[..., None, :]
+        return outer.reshape(x.shape[:-1] + (x.shape[-1] ** 2,))
+    raise ValueError("order must be 1 or 2")
+
+
+# ---------------------------------------------------------------------------
+# Quadratic (masked attention) form -- Algorithms 1, 4, 5
+# ---------------------------------------------------------------------------
+
+def _head_quadratic(q, k, vop, a, order, rows):
+    """One head.  q, k: [N,d]; vop: [N,dv]; a: [N] log-decays.
+
+    w_ij = (q_i . k_j)^order * exp(A^CS_i - A^CS_j) for j <= i, else 0.
+    Returns num [R,dv], den [R], kappa [R], scale [R] for the requested rows.
+    """
+    cs = np.cumsum(a)  # inclusive A^CS
+    if rows is None:
+        G = q @ k.T
+        Gp = G ** order
+        diff = cs[:, None] - cs[None, :]
+        causal = np.tril(np.ones(G.shape, dtype=bool))
+        # mask first, then exponentiate only the kept (non-positive) differences
+        decay = np.exp(np.where(causal, diff, -np.inf))
+        W = Gp * decay
+        num = W @ vop
+        den = W.sum(axis=1)
+        absW = np.abs(W)
+        abs_sum = absW.sum(axis=1)
+        abs_num = absW @ np.abs(vop)
+    else:
+        R = len(rows)
+        dv = vop.shape[1]
+        num = np.empty((R, dv))
+        den = np.empty(R)
+        abs_sum = np.empty(R)
+        abs_num = np.empty((R, dv))
+        for r, i in enumerate(rows):
+            g = k[: i + 1] @ q[i]
+            w = (g ** order) * np.exp(cs[i] - cs[: i + 1])
+            num[r] = w @ vop[: i + 1]
+            den[r] = w.sum()
+            aw = np.abs(w)
+            abs_sum[r] = aw.sum()
+            abs_num[r] = aw @ np.abs(vop[: i + 1])
+    with np.errstate(divide="ignore", invalid="ignore"):
+        kappa = abs_sum / np.abs(den)
+        scale = abs_num.max(axis=1) / np.abs(den)
+    return num, den, kappa, scale
+
+
+def forward_quadratic(q, k, vop, a, order, rows=None):
+    """Masked quadratic form over [B,H,N,.] arrays (fp64).
+
+    q, k: [B,H,N,d_h]; vop: [B,H,N,d_v] (the value operand, V*dt end to end);
+    a: [B,H,N] per-token log-decay.  rows: optional sorted 1-D array of token
+    indices to evaluate (one by one, so that long sequences can be sampled).
+
+    Returns dict with y = num/den, num, den, and the per-row diagnostics
+    kappa = sum_j |w_ij| / |den_i| and
+    scale = max_c sum_j |w_ij| |vop_jc| / |den_i|
+    (the magnitude a floating-point evaluation of the row is accurate to).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    vop = np.asarray(vop, dtype=np.float64)
+    a = np.asarray(a, dtype=np.float64)
+    B, H, N, _ = q.shape
+    R = N if rows is None else len(rows)
+    dv = vop.shape[-1]
+    out = {n: np.empty((B, H, R, dv)) for n in ("num",)}
+    out.update({n: np.empty((B, H, R)) for n in ("den", "kappa", "scale")})
+    for b in range(B):
+        for h in range(H):
+            num, den, kap, sc = _head_quadratic(q[b, h], k[b, h], vop[b, h], a[b, h], order, rows)
+            out["num"][b, h] = num
+            out["den"][b, h] = den
+            out["kappa"][b, h] = kap
+            out["scale"][b, h] = sc
+    with np.errstate(divide="ignore", invalid="ignore"):
+        out["y"] = out["num"] / out["den"][..., None]
+    return out
+
+
+def forward_ref(q, k, v, dt_proj, dt_bias, A_log, order, rows=None):
+    """End-to-end forward from stored inputs: Algorithm 3 discretisation, then
+    the masked quadratic form with V_dt = V * dt as the value operand."""
+    dt, a = discretise(dt_proj, dt_bias, A_log)
+    vdt = np.asarray(v, dtype=np.float64) * dt[..., None]
+    out = forward_quadratic(q, k, vdt, a, order, rows=rows)
+    out["dt"] = dt
+    out["a"] = a
+    return out
+
+
+# ---------------------------------------------------------------------------
+# Recurrent form -- Algorithm 6 (and the SSM recurrence h_t = A_t h_{t-1} + B_t x_t)
+# ---------------------------------------------------------------------------
+
+def recurrent_step(S, z, q, k, vop, a, order):
+    """One recurrence step for a batch of heads (leading dims broadcast).
+
+    S: [..., D, d_v] numerator state (H_up); z: [..., D] normaliser state
+    (H_down); q, k: [..., d_h]; vop: [..., d_v]; a: [...] log-decay of this step.
+    S <- e^a S + phi(k) vop^T ; z <- e^a z + phi(k) ; y = phi(q)^T S / phi(q)^T z.
+    Returns (S, z, y, den).
+    """
+    alpha = np.exp(np.asarray(a, dtype=np.float64))
+    fk = features(k, order)
+    fq = features(q, order)
+    S = alpha[..., None, None] * S + fk[..., :, None] * np.asarray(vop, dtype=np.float64)[..., None, :]
+    z = alpha[..., None] * z + fk
+    num = np.einsum("...d,...dv->...v", fq, S)
+    den = np.einsum("...d,...d->...", fq, z)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = num / den[..., None]
+    return S, z, y, den
+
+
+def forward_recurrent(q, k, vop, a, order, S0=None, z0=None):
+    """Token-by-token recurrence over [B,H,N,.] arrays from a zero state.
+
+    Returns (y [B,H,N,d_v], den [B,H,N], S_N [B,H,D,d_v], z_N [B,H,D]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    vop = np.asarray(vop, dtype=np.float64)
+    a = np.asarray(a, dtype=np.float64)
+    B, H, N, d = q.shape
+    dv = vop.shape[-1]
+    D = d ** order
+    S = np.zeros((B, H, D, dv)) if S0 is None else np.array(S0, dtype=np.float64)
+    z = np.zeros((B, H, D)) if z0 is None else np.array(z0, dtype=np.float64)
+    y = np.empty((B, H, N, dv))
+    den = np.empty((B, H, N))
+    for t in range(N):
+        S, z, y[:, :, t], den[:, :, t] = recurrent_step(S, z, q[:, :, t], k[:, :, t], vop[:, :, t],
+                                                        a[:, :, t], order)
+    return y, den, S, z
+
+
+def decode_step_ref(state, norm_state, q, k, v, dt_proj, dt_bias, A_log, order):
+    """One decode step for S sequences x H heads (what ssd_decode_step computes).
+
+    state [S,H,D,d_h], norm_state [S,H,D]; q, k, v [S,H,d_h]; dt_proj [S,H];
+    dt_bias, A_log [H].  dt = softplus(dt_P + dt_bias), a = -exp(A_log) dt,
+    value operand v * dt.  Returns (y [S,H,d_h], new_state, new_norm, den).
+    """
+    dt_proj = np.asarray(dt_proj, dtype=np.float64)
+    dt = softplus(dt_proj + np.asarray(dt_bias, dtype=np.float64)[None, :])
+    a = -np.exp(np.asarray(A_log, dtype=np.float64))[None, :] * dt
+    vop = np.asarray(v, dtype=np.float64) * dt[..., None]
+    S, z, y, den = recurrent_step(state, norm_state, q, k, vop, a, order)
+    return y, S, z, den

@@ -1,0 +1,318 @@
+"""Pins for the CPU fp64 oracle, against facts other than the oracle itself.
+
+Each test names the passage of 2Mamba2Furious (Mongaras & Larson) it checks.
+The pins are chosen so that a plausible slip in the oracle -- a dropped
+diagonal term, an exclusive instead of inclusive cumsum, a sign flip in the
+decay, q and k swapped, the power applied to the normaliser only, V instead of
+V*dt -- fails at least one of them.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import ssd_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_worked.json")
+
+
+def frac(s):
+    return float(Fraction(s))
+
+
+def fracs(x):
+    if isinstance(x, list):
+        return [fracs(e) for e in x]
+    return frac(x)
+
+
+def rand_case(rng, B, H, N, d, dv=None, a_scale=1.0, signed=True):
+    dv = d if dv is None else dv
+    q = rng.standard_normal((B, H, N, d))
+    k = rng.standard_normal((B, H, N, d))
+    if not signed:
+        q, k = np.abs(q), np.abs(k)
+    v = rng.standard_normal((B, H, N, dv))
+    a = -a_scale * rng.uniform(0.0, 1.0, (B, H, N))
+    return q, k, v, a
+
+
+def rel_err(x, y, scale):
+    return np.max(np.abs(x - y) / scale[..., None])
+
+
+# ---------------------------------------------------------------------------
+# Hand-worked fixtures (tests/golden/hand_worked.json)
+# ---------------------------------------------------------------------------
+
+def load_golden():
+    with open(GOLDEN) as f:
+        return {c["name"]: c for c in json.load(f)["cases"]}
+
+
+@pytest.mark.parametrize("order", [1, 2])
+@pytest.mark.parametrize("name", ["kernel_level_dh1", "order2_state_dh2"])
+def test_golden_kernel_level(name, order):
+    """Algorithms 1, 4, 5 on exact hand-worked values (inclusive A^CS)."""
+    c = load_golden()[name]
+    q = np.array(c["q"], float)[None, None]
+    k = np.array(c["k"], float)[None, None]
+    vop = np.array(c["vop"], float)[None, None]
+    a = np.log(np.array(c["exp_a"], float))[None, None]
+    exp = c["expected"][str(order)]
+    out = O.forward_quadratic(q, k, vop, a, order)
+    np.testing.assert_allclose(out["y"][0, 0], fracs(exp["y"]), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(out["den"][0, 0], fracs(exp["den"]), rtol=1e-14)
+    y, den, S, z = O.forward_recurrent(q, k, vop, a, order)
+    np.testing.assert_allclose(y[0, 0], fracs(exp["y"]), rtol=1e-14, atol=1e-14)
+    np.testing.assert_allclose(den[0, 0], fracs(exp["den"]), rtol=1e-14)
+    if "S_final" in exp:
+        np.testing.assert_allclose(S[0, 0], fracs(exp["S_final"]), rtol=1e-14)
+        np.testing.assert_allclose(z[0, 0], fracs(exp["z_final"]), rtol=1e-14)
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_golden_end_to_end(order):
+    """Algorithm 3 discretisation + mixer: dt = softplus(0) = ln 2, e^{A dt} = 1/2."""
+    c = load_golden()["end_to_end_dh1_ln2"]
+    q = np.array(c["q"], float)[None, None]
+    k = np.array(c["k"], float)[None, None]
+    v = np.array(c["v"], float)[None, None]
+    dtp = np.array(c["dt_proj"], float)[None, None]
+    out = O.forward_ref(q, k, v, dtp, np.array(c["dt_bias"]), np.array(c["A_log"]), order)
+    exp = c["expected"][str(order)]
+    ln2 = math.log(2.0)
+    np.testing.assert_allclose(out["y"][0, 0] / ln2, fracs(exp["y_over_ln2"]), rtol=1e-14)
+    np.testing.assert_allclose(out["den"][0, 0], fracs(exp["den"]), rtol=1e-14)
+    dt, a_cs, a_chunk = O.prep_ref(dtp, np.array(c["dt_bias"]), np.array(c["A_log"]), c["chunk"])
+    ep = c["expected_prep"]
+    np.testing.assert_allclose(dt[0, 0] / ln2, fracs(ep["dt_over_ln2"]), rtol=1e-15)
+    np.testing.assert_allclose(a_cs[0, 0] / ln2, fracs(ep["a_cs_over_ln2"]), rtol=1e-15)
+    np.testing.assert_allclose(a_chunk[0, 0] / ln2, fracs(ep["a_chunk_over_ln2"]), rtol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# Two independent derivations: quadratic form vs token recurrence (Algorithm 6)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("order", [1, 2])
+@pytest.mark.parametrize("N,d", [(1, 1), (2, 3), (17, 2), (64, 4), (130, 8)])
+def test_quadratic_equals_recurrence(order, N, d):
+    rng = np.random.default_rng(1000 * N + 10 * d + order)
+    # non-negative features at order 1 keep den away from 0 so y is comparable
+    q, k, v, a = rand_case(rng, 2, 2, N, d, a_scale=0.5, signed=(order == 2))
+    quad = O.forward_quadratic(q, k, v, a, order)
+    y, den, S, z = O.forward_recurrent(q, k, v, a, order)
+    assert rel_err(quad["y"], y, quad["scale"]) <= 1e-10
+    np.testing.assert_allclose(den, quad["den"], rtol=1e-10, atol=1e-12)
+    # final state = sum_j exp(A^CS_N - A^CS_j) phi(k_j) v_j^T
+    cs = np.cumsum(a, axis=-1)
+    w = np.exp(cs[..., -1:] - cs)
+    fk = O.features(k, order)
+    S_ref = np.einsum("bhn,bhnd,bhnv->bhdv", w, fk, v)
+    np.testing.assert_allclose(S, S_ref, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(z, np.einsum("bhn,bhnd->bhd", w, fk), rtol=1e-10, atol=1e-12)
+
+
+def test_sampled_rows_equal_full():
+    rng = np.random.default_rng(7)
+    q, k, v, a = rand_case(rng, 1, 2, 200, 4)
+    full = O.forward_quadratic(q, k, v, a, 2)
+    rows = np.array([0, 1, 63, 64, 65, 199])
+    part = O.forward_quadratic(q, k, v, a, 2, rows=rows)
+    for key in ("y", "den", "scale", "kappa"):
+        np.testing.assert_allclose(part[key], full[key][:, :, rows], rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Closed forms and special cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_single_token(order):
+    """N = 1: the only weight is on the diagonal, so y_0 = value_0 exactly."""
+    rng = np.random.default_rng(3)
+    q, k, v, a = rand_case(rng, 1, 3, 1, 5)
+    out = O.forward_quadratic(q, k, v, a, order)
+    np.testing.assert_allclose(out["y"], v, rtol=1e-15)
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_two_tokens_closed_form(order):
+    """N = 2: y_1 = (g10 e^{a_1} v_0 + g11 v_1) / (g10 e^{a_1} + g11), g_ij = (q_i.k_j)^p."""
+    rng = np.random.default_rng(4)
+    q, k, v, a = rand_case(rng, 1, 1, 2, 3, signed=False)
+    out = O.forward_quadratic(q, k, v, a, order)
+    g10 = float(q[0, 0, 1] @ k[0, 0, 0]) ** order
+    g11 = float(q[0, 0, 1] @ k[0, 0, 1]) ** order
+    e1 = math.exp(a[0, 0, 1])
+    y1 = (g10 * e1 * v[0, 0, 0] + g11 * v[0, 0, 1]) / (g10 * e1 + g11)
+    np.testing.assert_allclose(out["y"][0, 0, 1], y1, rtol=1e-13)
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_full_decay_is_identity(order):
+    """A_log = 25 => a ~ -7e10 dt: every off-diagonal decay underflows, mask = I, y = V dt."""
+    rng = np.random.default_rng(5)
+    B, H, N, d = 1, 2, 40, 4
+    q = np.abs(rng.standard_normal((B, H, N, d))) + 0.1
+    k = np.abs(rng.standard_normal((B, H, N, d))) + 0.1
+    v = rng.standard_normal((B, H, N, d))
+    dtp = rng.standard_normal((B, H, N))
+    out = O.forward_ref(q, k, v, dtp, np.zeros(H), np.full(H, 25.0), order)
+    np.testing.assert_allclose(out["y"], v * out["dt"][..., None], rtol=1e-14)
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_no_decay_is_causal_linear_attention(order):
+    """A^CS = 0: plain causal linear attention (Algorithm 1 with causal M), computed
+    independently with running prefix sums of phi(k) v^T and phi(k) ("Transformers
+    are RNNs" style), using numpy's cumsum."""
+    rng = np.random.default_rng(6)
+    B, H, N, d = 2, 2, 50, 3
+    q = np.abs(rng.standard_normal((B, H, N, d)))
+    k = np.abs(rng.standard_normal((B, H, N, d)))
+    v = rng.standard_normal((B, H, N, d))
+    a = np.zeros((B, H, N))
+    out = O.forward_quadratic(q, k, v, a, order)
+    if order == 1:
+        fq, fk = q, k
+    else:
+        fq = np.stack([q[..., i] * q[..., j] for i in range(d) for j in range(d)], axis=-1)
+        fk = np.stack([k[..., i] * k[..., j] for i in range(d) for j in range(d)], axis=-1)
+    KV = np.cumsum(fk[..., :, None] * v[..., None, :], axis=2)
+    Ks = np.cumsum(fk, axis=2)
+    num = np.einsum("bhnd,bhndv->bhnv", fq, KV)
+    den = np.einsum("bhnd,bhnd->bhn", fq, Ks)
+    np.testing.assert_allclose(out["y"], num / den[..., None], rtol=1e-11)
+    # end to end the same holds when dt_P is very negative: dt -> e^{dt_P}, a -> 0
+    dtp = np.full((B, H, N), -40.0)
+    e2e = O.forward_ref(q, k, v, dtp, np.zeros(H), np.zeros(H), order)
+    assert np.all(np.abs(e2e["a"]) < 1e-16)
+    np.testing.assert_allclose(e2e["y"], num / den[..., None] * e2e["dt"][..., None], rtol=1e-11)
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_constant_value_operand(order):
+    """A constant value operand c gives y = c on every row whose normaliser is nonzero."""
+    rng = np.random.default_rng(8)
+    q, k, _, a = rand_case(rng, 1, 2, 70, 4, signed=False)
+    c = np.array([1.5, -2.0, 0.25, 7.0])
+    v = np.broadcast_to(c, q.shape)
+    out = O.forward_quadratic(q, k, v, a, order)
+    np.testing.assert_allclose(out["y"], np.broadcast_to(c, out["y"].shape), rtol=1e-13)
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_homogeneity_and_affine_values(order):
+    """y(alpha Q, beta K, lam V + mu) = lam y(Q, K, V) + mu."""
+    rng = np.random.default_rng(9)
+    q, k, v, a = rand_case(rng, 1, 2, 33, 3, signed=False)
+    base = O.forward_quadratic(q, k, v, a, order)
+    alt = O.forward_quadratic(-2.5 * q, 0.3 * k, 4.0 * v + 1.25, a, order)
+    # the factor (alpha beta)^p, of either sign, cancels between numerator and normaliser
+    np.testing.assert_allclose(alt["y"], 4.0 * base["y"] + 1.25, rtol=1e-11, atol=1e-11)
+
+
+def test_order2_is_order1_on_flattened_features():
+    """(q.k)^2 = vec(q q^T).vec(k k^T): order 2 equals order 1 on D = d^2 features."""
+    rng = np.random.default_rng(10)
+    q, k, v, a = rand_case(rng, 1, 2, 45, 3)
+    o2 = O.forward_quadratic(q, k, v, a, 2)
+    fq = np.einsum("bhni,bhnj->bhnij", q, q).reshape(q.shape[:-1] + (9,))
+    fk = np.einsum("bhni,bhnj->bhnij", k, k).reshape(k.shape[:-1] + (9,))
+    o1 = O.forward_quadratic(fq, fk, v, a, 1)
+    np.testing.assert_allclose(o2["y"], o1["y"], rtol=1e-11)
+    np.testing.assert_allclose(o2["den"], o1["den"], rtol=1e-11)
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_prefix_consistency(order):
+    """Causality: the first n outputs do not depend on later tokens."""
+    rng = np.random.default_rng(11)
+    q, k, v, a = rand_case(rng, 1, 1, 140, 4, signed=False)
+    full = O.forward_quadratic(q, k, v, a, order)
+    for n in (1, 63, 64, 65, 127, 128, 129):
+        part = O.forward_quadratic(q[:, :, :n], k[:, :, :n], v[:, :, :n], a[:, :, :n], order)
+        np.testing.assert_allclose(part["y"], full["y"][:, :, :n], rtol=1e-12)
+
+
+def test_order2_weights_nonnegative_and_decays_bounded():
+    rng = np.random.default_rng(12)
+    q, k, v, a = rand_case(rng, 1, 2, 90, 4, a_scale=3.0)
+    out = O.forward_quadratic(q, k, v, a, 2)
+    assert np.all(out["den"] > 0)
+    np.testing.assert_allclose(out["kappa"], 1.0, rtol=1e-12)
+    dt, a2 = O.discretise(rng.standard_normal((1, 2, 90)), np.array([-1.0, 2.0]), np.array([0.3, 2.7]))
+    cs = np.cumsum(a2, axis=-1)
+    diff = cs[..., :, None] - cs[..., None, :]
+    kept = np.broadcast_to(np.tril(np.ones((90, 90), bool)), diff.shape)
+    assert np.all(diff[kept] <= 0.0)  # masked exponents never positive: no overflow
+    dec = np.exp(diff[kept])
+    assert np.all(dec >= 0.0) and np.all(dec <= 1.0)
+    assert np.all(dt > 0) and np.all(a2 < 0)
+
+
+# ---------------------------------------------------------------------------
+# Discretisation (Algorithms 2, 3)
+# ---------------------------------------------------------------------------
+
+def test_softplus_matches_library_logaddexp():
+    x = np.concatenate([np.linspace(-50, 50, 2001), [-745.0, -700.0, 700.0, 0.0]])
+    np.testing.assert_allclose(O.softplus(x), np.logaddexp(0.0, x), rtol=1e-15, atol=0)
+
+
+def test_softplus_inverse_of_dt_bias_init():
+    """Algorithm 2: dt_bias = dt_init + log(1 - exp(-dt_init)) inverts softplus."""
+    dt_init = np.exp(np.linspace(math.log(1e-3), math.log(1e-1), 101))
+    dt_bias = dt_init + np.log(-np.expm1(-dt_init))
+    np.testing.assert_allclose(O.softplus(dt_bias), dt_init, rtol=1e-13)
+
+
+def test_prep_chunks_reconstruct_global_cumsum():
+    """Chunk-local inclusive cumsums plus the preceding chunk totals give
+    cumsum(A*dt) over the whole sequence, for any chunk size (incl. ragged tails)."""
+    rng = np.random.default_rng(13)
+    B, H, N = 2, 3, 301
+    dtp = rng.standard_normal((B, H, N))
+    bias = rng.standard_normal(H)
+    alog = np.log(rng.uniform(1, 16, H))
+    dt, a = O.discretise(dtp, bias, alog)
+    ref = np.cumsum(-np.exp(alog)[:, None] * np.logaddexp(0.0, dtp + bias[:, None]), axis=-1)
+    for chunk in (1, 7, 64, 128, 301, 512):
+        dt2, cs, tot = O.prep_ref(dtp, bias, alog, chunk)
+        np.testing.assert_allclose(dt2, np.logaddexp(0.0, dtp + bias[:, None]), rtol=1e-14)
+        offs = np.concatenate([np.zeros((B, H, 1)), np.cumsum(tot, axis=-1)[..., :-1]], axis=-1)
+        glob = cs + np.repeat(offs, chunk, axis=-1)[..., :N]
+        np.testing.assert_allclose(glob, ref, rtol=1e-12)
+        assert tot.shape[-1] == -(-N // chunk)
+
+
+# ---------------------------------------------------------------------------
+# Decode step (Algorithm 6) against the forward form
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_decode_steps_equal_forward(order):
+    rng = np.random.default_rng(14)
+    S, H, T, d = 3, 2, 20, 3
+    A_log = np.log(rng.uniform(1, 16, H))
+    bias = rng.standard_normal(H) - 2.0
+    qs = rng.standard_normal((T, S, H, d))
+    ks = rng.standard_normal((T, S, H, d))
+    vs = rng.standard_normal((T, S, H, d))
+    dtps = rng.standard_normal((T, S, H))
+    D = d ** order
+    st = np.zeros((S, H, D, d))
+    nz = np.zeros((S, H, D))
+    ys = []
+    for t in range(T):
+        y, st, nz, _ = O.decode_step_ref(st, nz, qs[t], ks[t], vs[t], dtps[t], bias, A_log, order)
+        ys.append(y)
+    ys = np.stack(ys, axis=2)  # [S,H,T,d]
+    tr = lambda x: np.moveaxis(x, 0, 2)  # [T,S,H,...] -> [S,H,T,...]
+    fwd = O.forward_ref(tr(qs), tr(ks), tr(vs), np.moveaxis(dtps, 0, 2), bias, A_log, order)
+    assert rel_err(ys, fwd["y"], fwd["scale"]) <= 1e-10

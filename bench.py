@@ -1,0 +1,321 @@
+"""Throughput of the SSD / 2Mamba sequence mixer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-extra]
+                    [--no-cpu-baseline]
+
+A step is one pass of the whole hot path over one batch of synthetic inputs
+already resident in HBM: ssd_prep (softplus, A*dt, chunk-local cumsum) followed
+by ssd_forward (every kernel of the chunked forward).  The default workload is
+the order-2 (2Mamba) forward at N = 4096 (B 2, H 16, d_h 64, bf16 inputs, fp32
+accumulation).  One JSON line is printed on stdout; progress goes to stderr.
+
+roofline: the dominant kernel of the step, timed with HIP events that the
+library records on its own stream around each of its kernels over the timed
+steps, against MI355X's published dense bf16 MFMA peak (2.5 PFLOP/s) or HBM
+bandwidth (8 TB/s).  Algorithmic work per launch (see the design notes):
+  order-2 numerator state scan: 4 * D * d_h flops per token and head
+      (2 D d_h for phi(q)^T S, 2 D d_h for the phi(k) (v dt)^T update),
+  decode step: 2 * 4 * (D * d_h + D) bytes per sequence and head.
+cpu_baseline: the fp64 oracle (tests' reference implementation, untuned) on a
+bounded sample of the same workload, on this machine's host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from mamba_ssd_sequence_amd import inputs as I  # noqa: E402
+
+METRIC = "SSD fwd tokens/sec at N=4K and 64K (order 1/2); % bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+KERNELS_O1 = ["block_state", "state_pass", "output"]
+KERNELS_O2 = ["norm_block_state", "norm_state_pass", "o2_state_scan", "output"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(x, dtype, dev):
+    import torch
+    if dtype == I.BF16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+
+
+# ---------------------------------------------------------------------------
+# forward
+# ---------------------------------------------------------------------------
+
+def bench_forward(cfg: I.Config, steps: int, warmup: int, dev):
+    import torch
+    from mamba_ssd_sequence_amd import ssd
+
+    t = time.time()
+    inp = I.make_forward_inputs(cfg)
+    log(f"[bench] {cfg.name}: inputs drawn in {time.time() - t:.1f}s")
+    q, k, v = (to_dev(x, cfg.dtype, dev) for x in (inp.q, inp.k, inp.v))
+    dtp, bias, alog = (to_dev(x, I.F32, dev) for x in (inp.dt_proj, inp.dt_bias, inp.A_log))
+    B, H, N, d = q.shape
+    nc = -(-N // cfg.chunk)
+    dt = torch.empty((B, H, N), device=dev)
+    a_cs = torch.empty((B, H, N), device=dev)
+    a_chunk = torch.empty((B, H, nc), device=dev)
+    y = torch.empty((B, H, N, d), device=dev)
+    ws = torch.empty(ssd.workspace_size(B, H, N, d, cfg.order, cfg.chunk,
+                                        ssd.SSD_BF16 if cfg.dtype == I.BF16 else ssd.SSD_F32),
+                     dtype=torch.uint8, device=dev)
+
+    def step(timer=None):
+        ssd.prep(dtp, bias, alog, cfg.chunk, out=(dt, a_cs, a_chunk))
+        if timer is not None:
+            timer.arm()
+        ssd.forward(q, k, v, dt, a_cs, cfg.order, cfg.chunk, y=y, workspace=ws)
+        if timer is not None:
+            timer.collect()
+
+    for _ in range(warmup):
+        step()
+    timers = [ssd.KernelTimer() for _ in range(steps)]
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(timers[i])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    names = KERNELS_O2 if cfg.order == 2 else KERNELS_O1
+    per = np.array([tm.durations_ms() for tm in timers])  # [steps, kernels]
+    kern_ms = dict(zip(names, per.mean(axis=0).tolist()))
+    assert bool(torch.isfinite(y).all())
+    tokens = B * N
+    res = {"workload": cfg.name, "ms_per_step": ms, "tokens_per_s": tokens / (ms * 1e-3),
+           "kernels_ms": kern_ms, "B": B, "H": H, "N": N, "d_h": d, "order": cfg.order,
+           "chunk": cfg.chunk, "dtype": cfg.dtype}
+    if cfg.order == 2:
+        D = d * d
+        flops = 4.0 * D * d * B * H * N
+        t_ms = kern_ms["o2_state_scan"]
+        ach = flops / (t_ms * 1e-3) / 1e12
+        res["roofline"] = {"kernel": "k_o2_state", "bound": "mfma", "achieved": ach,
+                           "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                           "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                           "alg_flops_per_launch": flops, "avg_launch_ms": t_ms}
+        # whole-step MFMA fraction of the method's chunked work (SURVEY-style count)
+        res["step_mfma_frac"] = flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+    else:
+        es = 2 if cfg.dtype == I.BF16 else 4
+        nb = -(-N // 64)
+        # output kernel: q,k,v + dt + a_cs read, entering states read, y written
+        by = B * H * (N * (3 * d * es + 8 + 4 * d) + nb * (d * d + d) * 4)
+        t_ms = kern_ms["output"]
+        ach = by / (t_ms * 1e-3) / 1e9
+        res["roofline"] = {"kernel": "k_output", "bound": "hbm", "achieved": ach,
+                           "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                           "traffic": None, "alg_bytes_per_launch": by, "avg_launch_ms": t_ms}
+    return res, inp
+
+
+def cpu_baseline_forward(cfg: I.Config, inp, budget_s=12.0):
+    """Oracle throughput on a bounded sample: whole heads (quadratic form) when
+    they fit the budget, else uniformly sampled rows of one head, extrapolated."""
+    from oracle import ssd_oracle as O
+    q, k, v = inp.qkv_f64()
+    dt, a = O.discretise(inp.dt_proj, inp.dt_bias, inp.A_log)
+    vdt = v * dt[..., None]
+    B, H, N, _ = q.shape
+    if N <= 8192:
+        t0 = time.time()
+        heads = 0
+        while heads < B * H and (heads == 0 or time.time() - t0 < budget_s):
+            b, h = divmod(heads, H)
+            O.forward_quadratic(q[b:b + 1, h:h + 1], k[b:b + 1, h:h + 1], vdt[b:b + 1, h:h + 1],
+                                a[b:b + 1, h:h + 1], cfg.order)
+            heads += 1
+        el = time.time() - t0
+        t_head = el / heads
+        sample = f"quadratic-form oracle over {heads} whole head(s) of {B * H}, N={N}"
+    else:
+        rng = np.random.default_rng(0)
+        rows = np.sort(rng.integers(0, N, 48))
+        t0 = time.time()
+        O.forward_quadratic(q[:1, :1], k[:1, :1], vdt[:1, :1], a[:1, :1], cfg.order, rows=rows)
+        el = time.time() - t0
+        t_head = el / len(rows) * N
+        sample = (f"quadratic-form oracle on {len(rows)} uniformly sampled rows of 1 head (N={N}), "
+                  f"extrapolated to all rows and {B * H} heads")
+    tokens_per_s = N / (H * t_head)  # B*N tokens need B*H head evaluations
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": sample, "wall_s": el}
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+def bench_decode(cfg: I.DecodeConfig, steps: int, warmup: int, dev):
+    import torch
+    from mamba_ssd_sequence_amd import ssd
+
+    t = time.time()
+    dec = I.make_decode_inputs(cfg, steps=steps + warmup)
+    toks = [tuple(to_dev(x, cfg.dtype, dev) for x in s[:3]) + (to_dev(s[3], I.F32, dev),)
+            for s in dec.steps()]
+    log(f"[bench] {cfg.name}: inputs drawn in {time.time() - t:.1f}s")
+    D = cfg.d_h ** cfg.order
+    state = torch.zeros((cfg.S, cfg.H, D, cfg.d_h), device=dev)
+    norm = torch.zeros((cfg.S, cfg.H, D), device=dev)
+    y = torch.empty((cfg.S, cfg.H, cfg.d_h), device=dev)
+    bias, alog = to_dev(dec.dt_bias, I.F32, dev), to_dev(dec.A_log, I.F32, dev)
+    for i in range(warmup):
+        q, k, v, dtp = toks[i]
+        ssd.decode_step(q, k, v, dtp, bias, alog, state, norm, cfg.order, y=y)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        q, k, v, dtp = toks[warmup + i]
+        ev[i].record()
+        ssd.decode_step(q, k, v, dtp, bias, alog, state, norm, cfg.order, y=y)
+    ev[steps].record()
+    torch.cuda.synchronize()
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    ms = ev[0].elapsed_time(ev[steps]) / steps
+    by = 2.0 * 4 * (D * cfg.d_h + D) * cfg.S * cfg.H
+    t_ms = float(np.mean(per))
+    ach = by / (t_ms * 1e-3) / 1e9
+    return {"workload": cfg.name, "ms_per_step": ms, "tokens_per_s": cfg.S / (ms * 1e-3),
+            "S": cfg.S, "H": cfg.H, "d_h": cfg.d_h, "order": cfg.order, "steps": steps,
+            "roofline": {"kernel": "k_decode", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None,
+                         "alg_bytes_per_launch": by, "avg_launch_ms": t_ms}}, dec
+
+
+def cpu_baseline_decode(cfg: I.DecodeConfig, dec, budget_s=10.0):
+    from oracle import ssd_oracle as O
+    D = cfg.d_h ** cfg.order
+    M = 8  # (sequence, head) pairs per oracle call
+    St = np.zeros((1, M, D, cfg.d_h))
+    zt = np.zeros((1, M, D))
+    t0 = time.time()
+    n = 0
+    for (q, k, v, dtp) in dec.steps(n_steps=cfg.steps):
+        sl = (slice(0, 1), slice(0, M))
+        _, St, zt, _ = O.decode_step_ref(St, zt, I.bf16_bits_to_f64(q[sl]), I.bf16_bits_to_f64(k[sl]),
+                                         I.bf16_bits_to_f64(v[sl]), dtp[sl], dec.dt_bias[:M],
+                                         dec.A_log[:M], cfg.order)
+        n += 1
+        if time.time() - t0 > budget_s:
+            break
+    el = time.time() - t0
+    t_head_step = el / (n * M)
+    return {"value": 1.0 / (cfg.H * t_head_step), "unit": "tokens/s", "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 recurrence oracle, {M} (sequence, head) pairs x {n} steps, "
+                      f"extrapolated to {cfg.S} x {cfg.H} per step", "wall_s": el}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        n = max((d.get("num_threads", 1) for d in info if d.get("user_api") == "blas"), default=1)
+        return int(n)
+    except Exception:
+        return 1
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="o2_bf16_4k",
+                    choices=list(I.CONFIGS) + list(I.DECODE_CONFIGS))
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the secondary workloads (64K forward, decode)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the mixer's workloads are per-head independent "
+              "and this build has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    from mamba_ssd_sequence_amd import ssd
+    ssd.lib()
+
+    if a.workload in I.CONFIGS:
+        cfg = I.CONFIGS[a.workload]
+        res, inp = bench_forward(cfg, a.steps, a.warmup, dev)
+    else:
+        cfg = I.DECODE_CONFIGS[a.workload]
+        res, inp = bench_decode(cfg, a.steps, a.warmup, dev)
+    log(f"[bench] {a.workload}: {res['ms_per_step']:.4f} ms/step, {res['tokens_per_s']:.4g} tokens/s, "
+        f"roofline frac {res['roofline']['frac']:.3f}")
+
+    extra = []
+    if not a.no_extra:
+        for name in ("o2_bf16_64k", "o1_bf16_2k", "o2_decode"):
+            if name == a.workload:
+                continue
+            torch.cuda.empty_cache()
+            if name in I.CONFIGS:
+                r, _ = bench_forward(I.CONFIGS[name], max(3, a.steps // 4), 2, dev)
+            else:
+                c = I.DECODE_CONFIGS[name]
+                r, _ = bench_decode(c, c.steps, 3, dev)
+            log(f"[bench] extra {name}: {r['ms_per_step']:.4f} ms/step, {r['tokens_per_s']:.4g} tokens/s, "
+                f"roofline frac {r['roofline']['frac']:.3f}")
+            extra.append(r)
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        if a.workload in I.CONFIGS:
+            cpu = cpu_baseline_forward(cfg, inp)
+        else:
+            cpu = cpu_baseline_decode(cfg, inp)
+        cpu["host_cpus"] = os.cpu_count()
+        cpu["affinity_cpus"] = len(os.sched_getaffinity(0))
+
+    config = {k: res[k] for k in ("workload", "B", "H", "N", "d_h", "order", "chunk", "S", "steps")
+              if k in res}
+    out = {
+        "metric": METRIC,
+        "value": res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if getattr(cfg, "dtype", I.BF16) == I.BF16 else "f32",
+        "data": "synthetic",
+        "config": config,
+        "roofline": res["roofline"],
+        "cpu_baseline": cpu,
+        "kernels_ms": res.get("kernels_ms"),
+        "step_mfma_frac": res.get("step_mfma_frac"),
+        "extra": extra,
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,175 @@
+/*
+ * ssd.h -- C ABI of the MI355X (gfx950) SSD / 2Mamba sequence-mixer library
+ * (libssd.so).
+ *
+ * The library computes the masked linear-attention mixer of Mamba-2,
+ * Mamba-2S and 2Mamba ("2Mamba2Furious: Linear in Complexity, Competitive in
+ * Accuracy", Mongaras & Larson):
+ *
+ *     y_i = sum_{j<=i} w_ij V_dt,j / sum_{j<=i} w_ij,
+ *     w_ij = (q_i . k_j)^order * exp(A^CS_i - A^CS_j),
+ *
+ * with A^CS the inclusive cumulative sum of A*dt (Algorithm 3, the Mamba-2
+ * forward pass), the decay and causal masks of Algorithms 4 and 5, the
+ * squared scores of 2Mamba at order 2 (Algorithm 5) and the row-sum
+ * normaliser of Algorithm 1.  The recurrent decode step is the order-p
+ * state update of Algorithm 6 (2Mamba inference).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All array pointers are DEVICE pointers owned by the caller; the library
+ *    never allocates, frees or retains them.  Arrays are dense, row-major,
+ *    with the batch index outermost: [B,H,N,d_h] for q/k/v/y (the pages'
+ *    R^{H,N,d_h} per sequence), [B,H,N] for per-token scalars, [H] for
+ *    per-head parameters.  Every pointer must be 16-byte aligned.
+ *  - order p is 1 (Mamba-2 / Mamba-2S) or 2 (2Mamba); the state width is
+ *    D = d_h^p and the order-2 feature of x is vec(x x^T) flattened row-major
+ *    (index a*d_h + b).
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *    the call returns without synchronising.  SSD_OK means "validated and
+ *    enqueued"; a device fault surfaces at the caller's next synchronisation.
+ *  - Every argument check runs before any HIP call, so a rejected call has no
+ *    side effects.  On failure a nonzero ssd_status is returned and
+ *    ssd_last_error() describes it (thread-local).  No C++ exception crosses
+ *    the ABI.
+ *  - Outputs must not overlap inputs (SSD_ERR_ALIAS), except the decode
+ *    state, which is updated in place by design.
+ */
+#ifndef SSD_H_
+#define SSD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+typedef enum {
+  SSD_OK = 0,
+  SSD_ERR_NULL = 1,        /* a required pointer is NULL */
+  SSD_ERR_SHAPE = 2,       /* a size is < 1, or sizes overflow */
+  SSD_ERR_UNSUPPORTED = 3, /* a parameter combination this build does not implement */
+  SSD_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned */
+  SSD_ERR_ALIAS = 5,       /* an output overlaps an input or another output */
+  SSD_ERR_WORKSPACE = 6,   /* workspace missing or smaller than required */
+  SSD_ERR_HIP = 7          /* the HIP runtime reported an error (see ssd_last_error) */
+} ssd_status;
+
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+/* ABI version of the loaded library (SSD_ABI_VERSION). */
+int ssd_abi_version(void);
+
+/* Static, human-readable name of a status code. */
+const char* ssd_status_str(int status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* ssd_last_error(void);
+
+/*
+ * ssd_prep -- discretisation and chunk-local log-decay cumsum
+ * (Algorithm 3: A = -exp(A_log), dt = softplus(dt_P + dt_bias),
+ *  A^CS = cumsum(A * dt); initialisation of dt_bias and A_log per Algorithm 2).
+ *
+ *   dt_proj [B,H,N] f32   per-token dt logits dt_P
+ *   dt_bias [H]     f32
+ *   A_log   [H]     f32
+ *   chunk           cumsum segment length: 64 or 128
+ *   dt      [B,H,N] f32   out: softplus(dt_P + dt_bias)
+ *   a_cs    [B,H,N] f32   out: inclusive cumsum of A*dt restarted at every
+ *                         multiple of `chunk` (chunk-local A^CS)
+ *   a_chunk [B,H,ceil(N/chunk)] f32  out: total of A*dt over each chunk
+ *
+ * The global A^CS of Algorithm 3 is a_cs plus the sum of the earlier chunk
+ * totals; it is never formed, so that decays are always exponentials of
+ * non-positive sums of at most `chunk` terms.
+ */
+ssd_status ssd_prep(const float* dt_proj, const float* dt_bias, const float* A_log,
+                    int64_t B, int64_t H, int64_t N, int64_t chunk,
+                    float* dt, float* a_cs, float* a_chunk, hipStream_t stream);
+
+/* Workspace bytes ssd_forward needs for these sizes (0 if none; the same
+ * validation as ssd_forward applies, and an invalid combination returns 0). */
+size_t ssd_forward_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d_h,
+                                  int order, int64_t chunk, int dtype);
+
+/*
+ * ssd_forward -- chunked parallel form of the masked mixer
+ * (Algorithm 1 normaliser and product; Algorithms 4/5 masks; order-2 squared
+ *  scores of Algorithm 5; the inter-chunk state is the Algorithm 6 state).
+ *
+ *   q, k, v [B,H,N,d_h]  dtype (SSD_F32: float, SSD_BF16: bfloat16 bits)
+ *   dt      [B,H,N] f32  from ssd_prep; the value operand is V*dt.  NULL means
+ *                        v already is the value operand (as Algorithm 5
+ *                        prints it, plain V).
+ *   a_cs    [B,H,N] f32  chunk-local cumsum from ssd_prep with the same
+ *                        `chunk` (every decay is derived from it alone)
+ *   d_h                  32 or 64 (order 1); 64 (order 2)
+ *   order                1 or 2 (order 2 requires SSD_BF16)
+ *   chunk                64 or 128 (the a_cs segmentation)
+ *   y       [B,H,N,d_h] f32  out: normalised output
+ *   den     [B,H,N] f32  out, optional (NULL): the row-sum normaliser
+ *   final_state [B,H,D,d_h] f32, final_norm [B,H,D] f32: out, optional
+ *                        (both or neither): the numerator and normaliser
+ *                        states after token N-1 (Algorithm 6 H_up, H_down),
+ *                        the hand-off to ssd_decode_step.
+ *   workspace            device scratch of >= ssd_forward_workspace_size bytes
+ *
+ * Internally the sequence is processed in blocks of 64 tokens; the result
+ * does not depend on `chunk` beyond floating-point rounding.  The division
+ * by the normaliser is exact (no epsilon): rows whose normaliser is 0 give
+ * inf/nan, as the definition does.
+ */
+ssd_status ssd_forward(const void* q, const void* k, const void* v, const float* dt,
+                       const float* a_cs, int64_t B, int64_t H, int64_t N, int64_t d_h, int order, int64_t chunk,
+                       int dtype, float* y, float* den, float* final_state, float* final_norm,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ssd_decode_step -- one recurrent token step (Algorithm 6), in place.
+ *
+ *   q, k, v    [S,H,d_h] dtype      this step's token for S sequences
+ *   dt_proj    [S,H] f32; dt_bias, A_log [H] f32
+ *   state      [S,H,D,d_h] f32 in/out  numerator state H_up
+ *   norm_state [S,H,D] f32 in/out      normaliser state H_down
+ *   y          [S,H,d_h] f32 out
+ *
+ * dt = softplus(dt_P + dt_bias); alpha = exp(-exp(A_log) dt);
+ * state <- alpha state + phi(k) (v dt)^T; norm_state <- alpha norm_state + phi(k);
+ * y = phi(q)^T state / phi(q)^T norm_state, using the updated states.
+ * d_h is 32 or 64; order 1 or 2.
+ */
+/*
+ * ssd_set_timing_events -- optional per-kernel timing of the next ssd_forward
+ * call on the calling thread (used by the benchmark; not part of the math).
+ *
+ *   events  caller-owned hipEvent_t array of length n (created by the caller)
+ *   n       must be >= 5
+ *
+ * The next ssd_forward on this thread records events[0] on its stream before
+ * its first kernel and events[i] after its i-th kernel (i = 1..count); the
+ * kernel count is returned by that call's ssd_timing_count().  The
+ * registration is consumed by that call.  Passing events = NULL clears it.
+ * Order 1 runs 3 kernels (block states, state pass, output); order 2 runs 4
+ * (normaliser block states, normaliser pass, numerator state scan, output).
+ */
+ssd_status ssd_set_timing_events(hipEvent_t* events, int n);
+
+/* Number of kernels the last ssd_forward on this thread timed (0 if none). */
+int ssd_timing_count(void);
+
+ssd_status ssd_decode_step(const void* q, const void* k, const void* v,
+                           const float* dt_proj, const float* dt_bias, const float* A_log,
+                           int64_t S, int64_t H, int64_t d_h, int order, int dtype,
+                           float* state, float* norm_state, float* y, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H_ */

@@ -1,0 +1,284 @@
+// C ABI of libssd.so: argument validation (before any HIP call) and dispatch
+// to the gfx950 kernels.  See include/ssd.h for the contract of every call.
+#include "ssd.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = {0};
+thread_local hipEvent_t* g_events = nullptr;
+thread_local int g_n_events = 0;
+thread_local int g_timed = 0;
+
+// Records the next timing event (if a registration is active) on `stream`.
+struct Timer {
+  hipEvent_t* ev;
+  int n, i = 0;
+  hipStream_t stream;
+  Timer(hipStream_t s) : ev(g_events), n(g_n_events), stream(s) {
+    g_events = nullptr;
+    g_n_events = 0;
+    g_timed = 0;
+    mark();
+  }
+  void mark() {
+    if (ev && i < n) {
+      (void)hipEventRecord(ev[i], stream);
+      g_timed = i;
+      ++i;
+    }
+  }
+};
+
+ssd_status fail(ssd_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+void clear_err() { g_err[0] = 0; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// product of positive sizes with overflow detection (limit 2^62)
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a <= 0 || b <= 0) return false;
+  if (a > ((int64_t)1 << 62) / b) return false;
+  *out = a * b;
+  return true;
+}
+
+struct Range {
+  const char* name;
+  const void* p;
+  size_t bytes;
+};
+
+bool overlap(const Range& a, const Range& b) {
+  if (!a.p || !b.p || !a.bytes || !b.bytes) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, b0 = (uintptr_t)b.p;
+  return a0 < b0 + b.bytes && b0 < a0 + a.bytes;
+}
+
+ssd_status check_alias(const Range* outs, int n_out, const Range* ins, int n_in) {
+  for (int i = 0; i < n_out; ++i) {
+    for (int j = 0; j < n_in; ++j)
+      if (overlap(outs[i], ins[j]))
+        return fail(SSD_ERR_ALIAS, "output %s overlaps input %s", outs[i].name, ins[j].name);
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(outs[i], outs[j]))
+        return fail(SSD_ERR_ALIAS, "outputs %s and %s overlap", outs[i].name, outs[j].name);
+  }
+  return SSD_OK;
+}
+
+ssd_status check_aligned(const Range* rs, int n) {
+  for (int i = 0; i < n; ++i)
+    if (rs[i].p && !aligned16(rs[i].p))
+      return fail(SSD_ERR_ALIGN, "%s is not 16-byte aligned", rs[i].name);
+  return SSD_OK;
+}
+
+ssd_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return SSD_OK;
+  return fail(SSD_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Shared validation of the forward arguments; fills element counts.
+ssd_status validate_forward_sizes(int64_t B, int64_t H, int64_t N, int64_t d_h, int order,
+                                  int64_t chunk, int dtype, int64_t* BH, int64_t* BHN,
+                                  int64_t* BHNd) {
+  if (!mul_ok(B, H, BH) || !mul_ok(*BH, N, BHN) || !mul_ok(*BHN, d_h, BHNd))
+    return fail(SSD_ERR_SHAPE, "B, H, N, d_h must be >= 1 and their product must not overflow");
+  if (dtype != SSD_F32 && dtype != SSD_BF16) return fail(SSD_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (order != 1 && order != 2) return fail(SSD_ERR_UNSUPPORTED, "order %d (1 or 2)", order);
+  if (chunk != 64 && chunk != 128) return fail(SSD_ERR_UNSUPPORTED, "chunk %lld (64 or 128)", (long long)chunk);
+  if (order == 1 && d_h != 32 && d_h != 64)
+    return fail(SSD_ERR_UNSUPPORTED, "d_h %lld at order 1 (32 or 64)", (long long)d_h);
+  if (order == 2 && d_h != 64) return fail(SSD_ERR_UNSUPPORTED, "d_h %lld at order 2 (64)", (long long)d_h);
+  if (order == 2 && dtype != SSD_BF16) return fail(SSD_ERR_UNSUPPORTED, "order 2 requires bf16 inputs");
+  if (*BH * ((N + 63) / 64) > (int64_t)0x7fffffff) return fail(SSD_ERR_SHAPE, "grid too large");
+  return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+const char* ssd_status_str(int s) {
+  switch (s) {
+    case SSD_OK: return "SSD_OK";
+    case SSD_ERR_NULL: return "SSD_ERR_NULL";
+    case SSD_ERR_SHAPE: return "SSD_ERR_SHAPE";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED";
+    case SSD_ERR_ALIGN: return "SSD_ERR_ALIGN";
+    case SSD_ERR_ALIAS: return "SSD_ERR_ALIAS";
+    case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE";
+    case SSD_ERR_HIP: return "SSD_ERR_HIP";
+    default: return "SSD_ERR_UNKNOWN";
+  }
+}
+
+const char* ssd_last_error(void) { return g_err; }
+
+ssd_status ssd_prep(const float* dt_proj, const float* dt_bias, const float* A_log, int64_t B,
+                    int64_t H, int64_t N, int64_t chunk, float* dt, float* a_cs, float* a_chunk,
+                    hipStream_t stream) {
+  try {
+    clear_err();
+    if (!dt_proj || !dt_bias || !A_log || !dt || !a_cs || !a_chunk)
+      return fail(SSD_ERR_NULL, "ssd_prep: a required pointer is NULL");
+    int64_t BH, BHN;
+    if (!mul_ok(B, H, &BH) || !mul_ok(BH, N, &BHN))
+      return fail(SSD_ERR_SHAPE, "ssd_prep: B, H, N must be >= 1 and must not overflow");
+    if (chunk != 64 && chunk != 128)
+      return fail(SSD_ERR_UNSUPPORTED, "ssd_prep: chunk %lld (64 or 128)", (long long)chunk);
+    const int64_t nc = (N + chunk - 1) / chunk;
+    if ((BH * nc + 3) / 4 > (int64_t)0x7fffffff) return fail(SSD_ERR_SHAPE, "ssd_prep: grid too large");
+    const Range ins[] = {{"dt_proj", dt_proj, (size_t)BHN * 4},
+                         {"dt_bias", dt_bias, (size_t)H * 4},
+                         {"A_log", A_log, (size_t)H * 4}};
+    const Range outs[] = {{"dt", dt, (size_t)BHN * 4},
+                          {"a_cs", a_cs, (size_t)BHN * 4},
+                          {"a_chunk", a_chunk, (size_t)(BH * nc) * 4}};
+    ssd_status s;
+    if ((s = check_aligned(ins, 3)) != SSD_OK || (s = check_aligned(outs, 3)) != SSD_OK) return s;
+    if ((s = check_alias(outs, 3, ins, 3)) != SSD_OK) return s;
+    return hip_status(ssd::launch_prep(dt_proj, dt_bias, A_log, B, H, N, chunk, dt, a_cs, a_chunk, stream),
+                      "ssd_prep launch");
+  } catch (...) {
+    return fail(SSD_ERR_HIP, "ssd_prep: unexpected exception");
+  }
+}
+
+size_t ssd_forward_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d_h, int order,
+                                  int64_t chunk, int dtype) {
+  int64_t BH, BHN, BHNd;
+  if (validate_forward_sizes(B, H, N, d_h, order, chunk, dtype, &BH, &BHN, &BHNd) != SSD_OK) return 0;
+  return ssd::ws_layout(B, H, N, d_h, order).total_floats * sizeof(float);
+}
+
+ssd_status ssd_forward(const void* q, const void* k, const void* v, const float* dt,
+                       const float* a_cs, int64_t B, int64_t H, int64_t N, int64_t d_h, int order,
+                       int64_t chunk, int dtype, float* y, float* den, float* final_state,
+                       float* final_norm, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  try {
+    clear_err();
+    if (!q || !k || !v || !a_cs || !y) return fail(SSD_ERR_NULL, "ssd_forward: a required pointer is NULL");
+    if ((final_state == nullptr) != (final_norm == nullptr))
+      return fail(SSD_ERR_NULL, "ssd_forward: final_state and final_norm must be given together");
+    int64_t BH, BHN, BHNd;
+    ssd_status s = validate_forward_sizes(B, H, N, d_h, order, chunk, dtype, &BH, &BHN, &BHNd);
+    if (s != SSD_OK) return s;
+    const size_t es = dtype == SSD_BF16 ? 2 : 4;
+    const int64_t D = order == 1 ? d_h : d_h * d_h;
+    const size_t need = ssd::ws_layout(B, H, N, d_h, order).total_floats * sizeof(float);
+    if (workspace_bytes < need || (need && !workspace))
+      return fail(SSD_ERR_WORKSPACE, "ssd_forward: workspace of %zu bytes needed, %zu given", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    const Range ins[] = {{"q", q, (size_t)BHNd * es},  {"k", k, (size_t)BHNd * es},
+                         {"v", v, (size_t)BHNd * es},  {"dt", dt, (size_t)BHN * 4},
+                         {"a_cs", a_cs, (size_t)BHN * 4}};
+    const Range outs[] = {{"y", y, (size_t)BHNd * 4},
+                          {"den", den, (size_t)BHN * 4},
+                          {"final_state", final_state, (size_t)(BH * D * d_h) * 4},
+                          {"final_norm", final_norm, (size_t)(BH * D) * 4},
+                          {"workspace", workspace, need}};
+    if ((s = check_aligned(ins, 5)) != SSD_OK || (s = check_aligned(outs, 5)) != SSD_OK) return s;
+    if ((s = check_alias(outs, 5, ins, 5)) != SSD_OK) return s;
+
+    const bool bf = dtype == SSD_BF16;
+    Timer tm(stream);
+    const ssd::WsLayout L = ssd::ws_layout(B, H, N, d_h, order);
+    float* ws = static_cast<float*>(workspace);
+    float* tb = ws + L.tb;
+    float* st = ws + L.state;
+    hipError_t e;
+    if (order == 1) {
+      if ((e = ssd::launch_chunk_state(bf, d_h, k, v, dt, a_cs, BH, N, chunk, tb, st, stream)) != hipSuccess)
+        return hip_status(e, "chunk_state launch");
+      tm.mark();
+      if ((e = ssd::launch_state_pass(d_h, BH, N, tb, st, final_state, final_norm, stream)) != hipSuccess)
+        return hip_status(e, "state_pass launch");
+      tm.mark();
+      e = ssd::launch_output(bf, d_h, 1, q, k, v, dt, a_cs, BH, N, chunk, st, nullptr, 0, y, den, stream);
+      tm.mark();
+      return hip_status(e, "output launch");
+    }
+    // order 2: Z (normaliser state, a d_h x d_h matrix) by the block machinery
+    // with k as its own value operand; the D x d_h numerator state on chip.
+    float* part = ws + L.part;
+    if ((e = ssd::launch_chunk_state(true, 64, k, k, nullptr, a_cs, BH, N, chunk, tb, st, stream)) != hipSuccess)
+      return hip_status(e, "chunk_state launch");
+    tm.mark();
+    if ((e = ssd::launch_state_pass(64, BH, N, tb, st, final_norm, nullptr, stream)) != hipSuccess)
+      return hip_status(e, "state_pass launch");
+    tm.mark();
+    if ((e = ssd::launch_o2_state(q, k, v, dt, a_cs, BH, N, chunk, part, final_state, stream)) != hipSuccess)
+      return hip_status(e, "o2_state launch");
+    tm.mark();
+    e = ssd::launch_output(true, 64, 2, q, k, v, dt, a_cs, BH, N, chunk, st, part, ssd::o2_pa(BH), y, den, stream);
+    tm.mark();
+    return hip_status(e, "output launch");
+  } catch (...) {
+    return fail(SSD_ERR_HIP, "ssd_forward: unexpected exception");
+  }
+}
+
+ssd_status ssd_set_timing_events(hipEvent_t* events, int n) {
+  clear_err();
+  if (events && n < 5) return fail(SSD_ERR_SHAPE, "ssd_set_timing_events: n must be >= 5");
+  g_events = events;
+  g_n_events = events ? n : 0;
+  return SSD_OK;
+}
+
+int ssd_timing_count(void) { return g_timed; }
+
+ssd_status ssd_decode_step(const void* q, const void* k, const void* v, const float* dt_proj,
+                           const float* dt_bias, const float* A_log, int64_t S, int64_t H,
+                           int64_t d_h, int order, int dtype, float* state, float* norm_state,
+                           float* y, hipStream_t stream) {
+  try {
+    clear_err();
+    if (!q || !k || !v || !dt_proj || !dt_bias || !A_log || !state || !norm_state || !y)
+      return fail(SSD_ERR_NULL, "ssd_decode_step: a required pointer is NULL");
+    int64_t SH, SHd;
+    if (!mul_ok(S, H, &SH) || !mul_ok(SH, d_h, &SHd))
+      return fail(SSD_ERR_SHAPE, "ssd_decode_step: S, H, d_h must be >= 1 and must not overflow");
+    if (dtype != SSD_F32 && dtype != SSD_BF16) return fail(SSD_ERR_UNSUPPORTED, "dtype %d", dtype);
+    if (order != 1 && order != 2) return fail(SSD_ERR_UNSUPPORTED, "order %d (1 or 2)", order);
+    if (d_h != 32 && d_h != 64) return fail(SSD_ERR_UNSUPPORTED, "d_h %lld (32 or 64)", (long long)d_h);
+    if (SH > (int64_t)0x7fffffff) return fail(SSD_ERR_SHAPE, "ssd_decode_step: grid too large");
+    const int64_t D = order == 1 ? d_h : d_h * d_h;
+    int64_t nstate;
+    if (!mul_ok(SH, D * d_h, &nstate)) return fail(SSD_ERR_SHAPE, "ssd_decode_step: state too large");
+    const size_t es = dtype == SSD_BF16 ? 2 : 4;
+    const Range ins[] = {{"q", q, (size_t)SHd * es},          {"k", k, (size_t)SHd * es},
+                         {"v", v, (size_t)SHd * es},          {"dt_proj", dt_proj, (size_t)SH * 4},
+                         {"dt_bias", dt_bias, (size_t)H * 4}, {"A_log", A_log, (size_t)H * 4}};
+    const Range outs[] = {{"state", state, (size_t)nstate * 4},
+                          {"norm_state", norm_state, (size_t)(SH * D) * 4},
+                          {"y", y, (size_t)SHd * 4}};
+    ssd_status s;
+    if ((s = check_aligned(ins, 6)) != SSD_OK || (s = check_aligned(outs, 3)) != SSD_OK) return s;
+    if ((s = check_alias(outs, 3, ins, 6)) != SSD_OK) return s;
+    return hip_status(ssd::launch_decode(dtype == SSD_BF16, d_h, order, q, k, v, dt_proj, dt_bias, A_log,
+                                         S, H, state, norm_state, y, stream),
+                      "decode launch");
+  } catch (...) {
+    return fail(SSD_ERR_HIP, "ssd_decode_step: unexpected exception");
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,407 @@
+// Block-parallel pieces of the chunked forward (both orders), 64-token blocks.
+//
+//   k_chunk_state : per block, the state contribution sum_j w_j k_j val_j^T
+//                   and sum_j w_j k_j, w_j = exp(A^CS_last - A^CS_j)
+//                   (Algorithm 6's update summed over one block; MFMA).
+//   k_state_pass  : exclusive scan over blocks, S <- exp(T_blk) S + dS, in
+//                   place, so each block slot ends up holding the state that
+//                   enters it (elementwise, one thread per state entry).
+//   k_output      : the masked product within the block (Algorithms 1, 4, 5:
+//                   w_ij = (q_i.k_j)^p exp(A^CS_i - A^CS_j), j <= i), plus the
+//                   inter-block part exp(A^CS_i - A^CS_start) phi(q_i)^T S_in,
+//                   then y = num / den (Algorithm 1's row-sum normaliser).
+//
+// The decays are exponentials of non-positive differences of chunk-local
+// cumsums only (mask first, then exp).
+//
+// MFMA use: bf16 inputs run v_mfma_f32_16x16x32_bf16 (bf16 operands, fp32
+// accumulate); fp32 inputs run v_mfma_f32_16x16x4_f32 so that fp32 mode stays
+// fp32 throughout.  Each wave of the output kernel owns one 16-row tile of
+// queries; the score tile is produced transposed (K Q^T) so its accumulator
+// layout is directly the B operand of the (scores * mask) x V product.
+#include "common.h"
+#include "launch.h"
+
+namespace ssd {
+
+template <bool BF> struct Cfg;
+template <> struct Cfg<true> {
+  using C = __bf16;        // operand type staged in LDS
+  using St = uint16_t;     // storage type of q/k/v in HBM
+  using F = bf16x8;        // MFMA operand fragment
+  static constexpr int KS = 32;   // k per MFMA
+  static constexpr int PAD = 8;   // LDS row padding (elements)
+  static __device__ __forceinline__ F ld(const C* M, int P, int row, int ks, int g) {
+    return *reinterpret_cast<const bf16x8*>(&M[row * P + ks * 32 + 8 * g]);
+  }
+  static __device__ __forceinline__ f32x4 mma(const F& a, const F& b, const f32x4& c) {
+    return mfma_bf16(a, b, c);
+  }
+};
+template <> struct Cfg<false> {
+  using C = float;
+  using St = float;
+  using F = float;
+  static constexpr int KS = 4;
+  static constexpr int PAD = 4;
+  static __device__ __forceinline__ F ld(const C* M, int P, int row, int ks, int g) {
+    return M[row * P + ks * 4 + g];
+  }
+  static __device__ __forceinline__ f32x4 mma(const F& a, const F& b, const f32x4& c) {
+    return mfma_f32(a, b, c);
+  }
+};
+
+// ---------------------------------------------------------------------------
+// k_chunk_state
+// ---------------------------------------------------------------------------
+template <bool BF, int DH>
+__global__ __launch_bounds__(256) void k_chunk_state(const void* __restrict__ kp,
+                                                     const void* __restrict__ vp,
+                                                     const float* __restrict__ dt,
+                                                     const float* __restrict__ a_cs, int64_t N,
+                                                     int64_t chunk, int64_t nblk,
+                                                     float* __restrict__ tb,
+                                                     float* __restrict__ state) {
+  using G = Cfg<BF>;
+  using C = typename G::C;
+  using St = typename G::St;
+  constexpr int P = BLK + G::PAD;
+  __shared__ __attribute__((aligned(16))) C wKT[DH * P];  // [b][j] = w_j k_jb
+  __shared__ __attribute__((aligned(16))) C VT[DH * P];   // [c][j] = val_jc
+  __shared__ float wv[BLK];
+  __shared__ float dtv[BLK];
+
+  const St* k = static_cast<const St*>(kp);
+  const St* v = static_cast<const St*>(vp);
+  const int64_t bh = blockIdx.x / nblk, blk = blockIdx.x - bh * nblk;
+  const int64_t t0 = blk * BLK;
+  const int nvalid = (int)((N - t0) < BLK ? (N - t0) : BLK);
+  const int64_t row = bh * N;
+  const int tid = threadIdx.x;
+
+  const float base = (t0 % chunk == 0) ? 0.f : a_cs[row + t0 - 1];
+  const float cs_last = a_cs[row + t0 + nvalid - 1];
+  if (tid < BLK) {
+    float w = 0.f, d = 0.f;
+    if (tid < nvalid) {
+      w = expf(cs_last - a_cs[row + t0 + tid]);
+      d = dt ? dt[row + t0 + tid] : 1.f;
+    }
+    wv[tid] = w;
+    dtv[tid] = d;
+  }
+  if (tid == 0) tb[bh * nblk + blk] = cs_last - base;
+  __syncthreads();
+
+  for (int e = tid; e < BLK * DH; e += 256) {
+    const int j = e / DH, d = e - (e / DH) * DH;
+    float kv = 0.f, vv = 0.f;
+    if (j < nvalid) {
+      kv = Elem<St>::ld(k, (row + t0 + j) * DH + d);
+      vv = Elem<St>::ld(v, (row + t0 + j) * DH + d);
+    }
+    wKT[d * P + j] = (C)(wv[j] * kv);
+    VT[d * P + j] = (C)(vv * dtv[j]);
+  }
+  __syncthreads();
+
+  const int wave = tid / WAVE, lane = tid & (WAVE - 1), n = lane & 15, g = lane >> 4;
+  constexpr int NT = DH / 16;
+  float* out = state + (bh * nblk + blk) * (int64_t)(DH * DH + DH);
+  for (int tile = wave; tile < NT * NT; tile += 4) {
+    const int ct = tile / NT, bt = tile - (tile / NT) * NT;
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int ks = 0; ks < BLK / G::KS; ++ks)
+      acc = G::mma(G::ld(VT, P, ct * 16 + n, ks, g), G::ld(wKT, P, bt * 16 + n, ks, g), acc);
+    // acc[r] = dS^T[c = 16ct + 4g + r][b = 16bt + n]  ->  dS[b][c]
+    *reinterpret_cast<f32x4*>(&out[(bt * 16 + n) * DH + ct * 16 + 4 * g]) = acc;
+  }
+  if (tid < DH) {
+    float s = 0.f;
+    for (int j = 0; j < BLK; ++j) s += (float)wKT[tid * P + j];
+    out[DH * DH + tid] = s;
+  }
+}
+
+hipError_t launch_chunk_state(bool bf16, int64_t DH, const void* k, const void* v, const float* dt,
+                              const float* a_cs, int64_t BH, int64_t N, int64_t chunk, float* tb,
+                              float* state, hipStream_t stream) {
+  const int64_t nb = n_blocks(N);
+  const dim3 grid((unsigned)(BH * nb)), blk(256);
+  if (bf16 && DH == 64)
+    hipLaunchKernelGGL((k_chunk_state<true, 64>), grid, blk, 0, stream, k, v, dt, a_cs, N, chunk, nb, tb, state);
+  else if (bf16 && DH == 32)
+    hipLaunchKernelGGL((k_chunk_state<true, 32>), grid, blk, 0, stream, k, v, dt, a_cs, N, chunk, nb, tb, state);
+  else if (!bf16 && DH == 64)
+    hipLaunchKernelGGL((k_chunk_state<false, 64>), grid, blk, 0, stream, k, v, dt, a_cs, N, chunk, nb, tb, state);
+  else
+    hipLaunchKernelGGL((k_chunk_state<false, 32>), grid, blk, 0, stream, k, v, dt, a_cs, N, chunk, nb, tb, state);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// k_state_pass
+// ---------------------------------------------------------------------------
+template <int DH>
+__global__ __launch_bounds__(256) void k_state_pass(int64_t nblk, int eblocks,
+                                                    const float* __restrict__ tb,
+                                                    float* __restrict__ state,
+                                                    float* __restrict__ fS,
+                                                    float* __restrict__ fz) {
+  constexpr int E = DH * DH + DH;
+  const int64_t bh = blockIdx.x / eblocks;
+  const int e = (int)(blockIdx.x - bh * eblocks) * 256 + threadIdx.x;
+  if (e >= E) return;
+  float* p = state + bh * nblk * E + e;
+  const float* t = tb + bh * nblk;
+  float s = 0.f;
+  int64_t b = 0;
+  for (; b + 8 <= nblk; b += 8) {
+    float d[8], T[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      d[u] = p[(b + u) * E];
+      T[u] = t[b + u];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      p[(b + u) * E] = s;
+      s = expf(T[u]) * s + d[u];
+    }
+  }
+  for (; b < nblk; ++b) {
+    const float d = p[b * E];
+    const float T = t[b];
+    p[b * E] = s;
+    s = expf(T) * s + d;
+  }
+  if (e < DH * DH) {
+    if (fS) fS[bh * DH * DH + e] = s;
+  } else {
+    if (fz) fz[bh * DH + (e - DH * DH)] = s;
+  }
+}
+
+hipError_t launch_state_pass(int64_t DH, int64_t BH, int64_t N, const float* tb, float* state,
+                             float* final_S, float* final_z, hipStream_t stream) {
+  const int64_t nb = n_blocks(N);
+  const int E = (int)(DH * DH + DH);
+  const int eblocks = (E + 255) / 256;
+  const dim3 grid((unsigned)(BH * eblocks)), blk(256);
+  if (DH == 64)
+    hipLaunchKernelGGL(k_state_pass<64>, grid, blk, 0, stream, nb, eblocks, tb, state, final_S, final_z);
+  else
+    hipLaunchKernelGGL(k_state_pass<32>, grid, blk, 0, stream, nb, eblocks, tb, state, final_S, final_z);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// k_output
+// ---------------------------------------------------------------------------
+template <bool BF, int DH, int ORDER>
+__global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
+                                                const void* __restrict__ kp,
+                                                const void* __restrict__ vp,
+                                                const float* __restrict__ dt,
+                                                const float* __restrict__ a_cs, int64_t BH,
+                                                int64_t N, int64_t chunk, int64_t nblk,
+                                                const float* __restrict__ state,
+                                                const float* __restrict__ part, int P_a,
+                                                float* __restrict__ y, float* __restrict__ den) {
+  using G = Cfg<BF>;
+  using C = typename G::C;
+  using St = typename G::St;
+  constexpr int PQ = DH + G::PAD;   // pitch of rows indexed by feature
+  constexpr int PJ = BLK + G::PAD;  // pitch of rows indexed by token
+  constexpr int NT = DH / 16;
+  __shared__ __attribute__((aligned(16))) C Qs[BLK * PQ];   // [i][d]
+  __shared__ __attribute__((aligned(16))) C Ks[BLK * PQ];   // [j][d]
+  __shared__ __attribute__((aligned(16))) C VT[DH * PJ];    // [c][j]  value operand, transposed
+  __shared__ __attribute__((aligned(16))) C SinT[DH * PQ];  // [c][b]  entering state, transposed
+  __shared__ float zin[DH];
+  __shared__ float csl[BLK];
+  __shared__ float dtv[BLK];
+
+  const St* q = static_cast<const St*>(qp);
+  const St* k = static_cast<const St*>(kp);
+  const St* v = static_cast<const St*>(vp);
+  const int64_t bh = blockIdx.x / nblk, blk = blockIdx.x - bh * nblk;
+  const int64_t t0 = blk * BLK;
+  const int nvalid = (int)((N - t0) < BLK ? (N - t0) : BLK);
+  const int64_t row = bh * N;
+  const int tid = threadIdx.x;
+
+  const float base = (t0 % chunk == 0) ? 0.f : a_cs[row + t0 - 1];
+  if (tid < BLK) {
+    float c = 0.f, d = 0.f;
+    if (tid < nvalid) {
+      c = a_cs[row + t0 + tid] - base;
+      d = dt ? dt[row + t0 + tid] : 1.f;
+    }
+    csl[tid] = c;
+    dtv[tid] = d;
+  }
+  __syncthreads();
+  for (int e = tid; e < BLK * DH; e += 256) {
+    const int j = e / DH, d = e - (e / DH) * DH;
+    float qv = 0.f, kv = 0.f, vv = 0.f;
+    if (j < nvalid) {
+      const int64_t off = (row + t0 + j) * DH + d;
+      qv = Elem<St>::ld(q, off);
+      kv = Elem<St>::ld(k, off);
+      vv = Elem<St>::ld(v, off);
+    }
+    Qs[j * PQ + d] = (C)qv;
+    Ks[j * PQ + d] = (C)kv;
+    VT[d * PJ + j] = (C)(vv * dtv[j]);
+  }
+  const float* st = state + (bh * nblk + blk) * (int64_t)(DH * DH + DH);
+  for (int e = tid; e < DH * DH; e += 256) {
+    const int b = e / DH, c = e - (e / DH) * DH;
+    SinT[c * PQ + b] = (C)st[e];
+  }
+  if (ORDER == 1 && tid < DH) zin[tid] = st[DH * DH + tid];
+  __syncthreads();
+
+  const int it = tid / WAVE, lane = tid & (WAVE - 1), n = lane & 15, g = lane >> 4;
+  const int il = it * 16 + n;  // this lane's query row within the block
+  const float cs_i = csl[il];
+
+  // scores, transposed: W[jt][r] = w(i = il, j = 16 jt + 4g + r)
+  f32x4 W[4];
+  float den_l = 0.f;
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    W[jt] = zero4();
+    if (jt <= it) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < DH / G::KS; ++ks)
+        acc = G::mma(G::ld(Ks, PQ, jt * 16 + n, ks, g), G::ld(Qs, PQ, il, ks, g), acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = jt * 16 + 4 * g + r;
+        float s = acc[r];
+        if (ORDER == 2) s = s * s;
+        const float w = (j <= il && j < nvalid) ? s * expf(cs_i - csl[j]) : 0.f;
+        W[jt][r] = w;
+        den_l += w;
+      }
+    }
+  }
+
+  // num^T[c][i] = sum_j VT[c][j] W[i][j]
+  f32x4 num[NT];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) num[ct] = zero4();
+  if constexpr (BF) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      if (2 * kb <= it) {
+        bf16x8 bw;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          bw[r] = (__bf16)W[2 * kb][r];
+          bw[4 + r] = (__bf16)W[2 * kb + 1][r];
+        }
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+          const C* base_p = &VT[(ct * 16 + n) * PJ + kb * 32 + 4 * g];
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(base_p);
+          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(base_p + 16);
+          bf16x8 a;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            a[r] = lo[r];
+            a[4 + r] = hi[r];
+          }
+          num[ct] = mfma_bf16(a, bw, num[ct]);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      if (jt <= it) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+#pragma unroll
+          for (int ct = 0; ct < NT; ++ct)
+            num[ct] = mfma_f32(VT[(ct * 16 + n) * PJ + jt * 16 + 4 * g + r], W[jt][r], num[ct]);
+        }
+      }
+    }
+  }
+  den_l = sum_over_groups(den_l);
+
+  // inter-block part: D[c][i] = sum_b SinT[c][b] Q[i][b]
+  const float eci = expf(cs_i);
+  f32x4 inter[NT];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) {
+    f32x4 acc = zero4();
+#pragma unroll
+    for (int ks = 0; ks < DH / G::KS; ++ks)
+      acc = G::mma(G::ld(SinT, PQ, ct * 16 + n, ks, g), G::ld(Qs, PQ, il, ks, g), acc);
+    inter[ct] = acc;
+  }
+  float den_x = 0.f;
+  if constexpr (ORDER == 1) {
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) num[ct] += eci * inter[ct];
+    for (int b = g * (DH / 4); b < (g + 1) * (DH / 4); ++b) den_x += (float)Qs[il * PQ + b] * zin[b];
+  } else {
+    // q^T Z q: inter[ct][r] = (Q Z)[i][c = 16ct + 4g + r]
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) den_x += (float)Qs[il * PQ + ct * 16 + 4 * g + r] * inter[ct][r];
+    if (il < nvalid) {
+      for (int pa = 0; pa < P_a; ++pa) {
+        const float* pp = part + (((int64_t)pa * BH + bh) * N + t0 + il) * 64;
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) num[ct] += *reinterpret_cast<const f32x4*>(pp + ct * 16 + 4 * g);
+      }
+    }
+  }
+  den_x = sum_over_groups(den_x);
+  const float dtot = den_l + eci * den_x;
+
+  if (il < nvalid) {
+    float* yp = y + (row + t0 + il) * DH;
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      f32x4 o;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[r] = num[ct][r] / dtot;
+      *reinterpret_cast<f32x4*>(yp + ct * 16 + 4 * g) = o;
+    }
+    if (den && g == 0) den[row + t0 + il] = dtot;
+  }
+}
+
+hipError_t launch_output(bool bf16, int64_t DH, int order, const void* q, const void* k,
+                         const void* v, const float* dt, const float* a_cs, int64_t BH, int64_t N,
+                         int64_t chunk, const float* state, const float* part, int P_a, float* y,
+                         float* den, hipStream_t stream) {
+  const int64_t nb = n_blocks(N);
+  const dim3 grid((unsigned)(BH * nb)), blk(256);
+#define SSD_LAUNCH_OUT(BFV, DHV, ORD)                                                           \
+  hipLaunchKernelGGL((k_output<BFV, DHV, ORD>), grid, blk, 0, stream, q, k, v, dt, a_cs, BH, N, \
+                     chunk, nb, state, part, P_a, y, den)
+  if (order == 2) {
+    SSD_LAUNCH_OUT(true, 64, 2);
+  } else if (bf16) {
+    if (DH == 64) SSD_LAUNCH_OUT(true, 64, 1);
+    else SSD_LAUNCH_OUT(true, 32, 1);
+  } else {
+    if (DH == 64) SSD_LAUNCH_OUT(false, 64, 1);
+    else SSD_LAUNCH_OUT(false, 32, 1);
+  }
+#undef SSD_LAUNCH_OUT
+  return hipGetLastError();
+}
+
+}  // namespace ssd

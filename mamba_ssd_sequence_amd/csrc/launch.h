@@ -1,0 +1,75 @@
+// Internal (non-exported) launchers and workspace layout of libssd.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssd {
+
+// Forward work is organised in blocks of 64 tokens.
+__host__ __device__ inline int64_t n_blocks(int64_t N) { return (N + 63) / 64; }
+
+// Order-2 state kernel: a-rows per wave (AW), and the resulting number of
+// a-slices per head (P_a = 64 / (8 * AW)).  Fewer heads -> thinner slices so
+// that the grid still covers the chip.
+inline int o2_aw(int64_t BH) { return BH >= 32 ? 4 : (BH >= 16 ? 2 : 1); }
+inline int o2_pa(int64_t BH) { return 64 / (8 * o2_aw(BH)); }
+
+// Workspace layout (float offsets), in this order:
+//   tb     [BH, nblk]                 block decay totals
+//   state  [BH, nblk, DH*DH + DH]     per-block state contributions, then
+//                                     (in place) the state entering each block
+//                                     (order 1: S and z; order 2: Z and unused)
+//   part   [P_a, BH, N, 64]           order 2 only: inter-block numerator
+//                                     partials of each a-slice
+struct WsLayout {
+  size_t tb, state, part, total_floats;
+};
+
+inline WsLayout ws_layout(int64_t B, int64_t H, int64_t N, int64_t DH, int order) {
+  const int64_t BH = B * H, nb = n_blocks(N);
+  WsLayout L;
+  L.tb = 0;
+  size_t off = (size_t)(BH * nb);
+  off = (off + 63) & ~(size_t)63;
+  L.state = off;
+  off += (size_t)(BH * nb) * (size_t)(DH * DH + DH);
+  off = (off + 63) & ~(size_t)63;
+  L.part = off;
+  if (order == 2) off += (size_t)o2_pa(BH) * (size_t)BH * (size_t)N * 64;
+  L.total_floats = off;
+  return L;
+}
+
+hipError_t launch_prep(const float* dt_proj, const float* dt_bias, const float* A_log, int64_t B,
+                       int64_t H, int64_t N, int64_t chunk, float* dt, float* a_cs, float* a_chunk,
+                       hipStream_t stream);
+
+// Per-block state contributions: state[bh,blk] = sum_j w_j k_j val_j^T and
+// sum_j w_j k_j with w_j = exp(A^CS_last - A^CS_j); val = v*dt (dt != NULL) or v.
+hipError_t launch_chunk_state(bool bf16, int64_t DH, const void* k, const void* v, const float* dt,
+                              const float* a_cs, int64_t BH, int64_t N, int64_t chunk, float* tb,
+                              float* state, hipStream_t stream);
+
+// In-place exclusive scan over blocks: state[bh,blk] <- state entering blk.
+hipError_t launch_state_pass(int64_t DH, int64_t BH, int64_t N, const float* tb, float* state,
+                             float* final_S, float* final_z, hipStream_t stream);
+
+// Intra-block masked product + inter-block part + normalisation -> y, den.
+hipError_t launch_output(bool bf16, int64_t DH, int order, const void* q, const void* k,
+                         const void* v, const float* dt, const float* a_cs, int64_t BH, int64_t N,
+                         int64_t chunk, const float* state, const float* part, int P_a, float* y,
+                         float* den, hipStream_t stream);
+
+// Order-2 inter-block numerator: on-chip state scan over blocks.
+hipError_t launch_o2_state(const void* q, const void* k, const void* v, const float* dt,
+                           const float* a_cs, int64_t BH, int64_t N, int64_t chunk, float* part,
+                           float* final_state, hipStream_t stream);
+
+hipError_t launch_decode(bool bf16, int64_t DH, int order, const void* q, const void* k,
+                         const void* v, const float* dt_proj, const float* dt_bias,
+                         const float* A_log, int64_t S, int64_t H, float* state, float* norm_state,
+                         float* y, hipStream_t stream);
+
+}  // namespace ssd

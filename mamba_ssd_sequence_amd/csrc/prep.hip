@@ -1,0 +1,86 @@
+// ssd_prep: discretisation and chunk-local cumulative log-decay.
+//
+// 2Mamba2Furious, Algorithm 3 (Mamba-2 forward pass): A = -exp(A_log),
+// dt = softplus(dt_P + dt_bias), A^CS = cumsum(A * dt).  The cumsum is
+// inclusive and restarts at every chunk boundary; chunk totals are written
+// separately, so no decay is ever computed from a large global sum.
+//
+// One wave per chunk.  Each lane owns chunk/64 consecutive tokens (1 or 2):
+// it forms dt and a = A*dt for them, a running sum over its own tokens, then
+// a wave-wide inclusive scan of the lane totals (Hillis-Steele over
+// __shfl_up) supplies each lane's offset.  HBM traffic per token and head:
+// 4 B in, 8 B out.
+#include "common.h"
+#include "launch.h"
+
+namespace ssd {
+
+template <int TPL>  // tokens per lane: chunk / 64
+__global__ __launch_bounds__(256) void k_prep(const float* __restrict__ dt_proj,
+                                              const float* __restrict__ dt_bias,
+                                              const float* __restrict__ A_log, int64_t H, int64_t N,
+                                              int64_t n_chunks, int64_t total_chunks,
+                                              float* __restrict__ dt_out, float* __restrict__ a_cs,
+                                              float* __restrict__ a_chunk) {
+  constexpr int CHUNK = TPL * WAVE;
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int64_t gchunk = (int64_t)blockIdx.x * (blockDim.x / WAVE) + (threadIdx.x / WAVE);
+  if (gchunk >= total_chunks) return;
+  const int64_t bh = gchunk / n_chunks;
+  const int64_t c = gchunk - bh * n_chunks;
+  const int64_t h = bh % H;
+  const float A = -expf(A_log[h]);
+  const float bias = dt_bias[h];
+  const int64_t t0 = c * CHUNK + (int64_t)lane * TPL;
+  const int64_t row = bh * N;
+
+  float dts[TPL], run[TPL];
+  float acc = 0.f;
+#pragma unroll
+  for (int s = 0; s < TPL; ++s) {
+    const int64_t t = t0 + s;
+    float d = 0.f, a = 0.f;
+    if (t < N) {
+      d = softplus_f(dt_proj[row + t] + bias);
+      a = A * d;
+    }
+    dts[s] = d;
+    acc += a;
+    run[s] = acc;
+  }
+  // inclusive scan of the lane totals across the wave
+  float incl = acc;
+#pragma unroll
+  for (int off = 1; off < WAVE; off <<= 1) {
+    const float o = __shfl_up(incl, off, WAVE);
+    if (lane >= off) incl += o;
+  }
+  const float offset = incl - acc;
+#pragma unroll
+  for (int s = 0; s < TPL; ++s) {
+    const int64_t t = t0 + s;
+    if (t < N) {
+      dt_out[row + t] = dts[s];
+      a_cs[row + t] = offset + run[s];
+    }
+  }
+  if (lane == WAVE - 1) a_chunk[bh * n_chunks + c] = incl;
+}
+
+hipError_t launch_prep(const float* dt_proj, const float* dt_bias, const float* A_log, int64_t B,
+                       int64_t H, int64_t N, int64_t chunk, float* dt, float* a_cs, float* a_chunk,
+                       hipStream_t stream) {
+  const int64_t n_chunks = (N + chunk - 1) / chunk;
+  const int64_t total = B * H * n_chunks;
+  const int waves_per_block = 4;
+  const int64_t grid = (total + waves_per_block - 1) / waves_per_block;
+  if (chunk == 64)
+    hipLaunchKernelGGL(k_prep<1>, dim3((unsigned)grid), dim3(256), 0, stream, dt_proj, dt_bias, A_log,
+                       H, N, n_chunks, total, dt, a_cs, a_chunk);
+  else
+    hipLaunchKernelGGL(k_prep<2>, dim3((unsigned)grid), dim3(256), 0, stream, dt_proj, dt_bias, A_log,
+                       H, N, n_chunks, total, dt, a_cs, a_chunk);
+  return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -1,0 +1,220 @@
+"""Thin Python binding of libssd.so (ctypes).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of include/ssd.h.  PyTorch supplies device memory and
+the current HIP stream.  There is no fallback: if the library is missing or a
+call fails, an exception is raised.
+
+    dt, a_cs, a_chunk = prep(dt_proj, dt_bias, A_log, chunk)
+    y = forward(q, k, v, dt, a_cs, order=2, chunk=64)
+    y = decode_step(q, k, v, dt_proj, dt_bias, A_log, state, norm_state, order=2)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libssd.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "ssd.h")
+
+SSD_OK = 0
+SSD_F32 = 0
+SSD_BF16 = 1
+STATUS = ["SSD_OK", "SSD_ERR_NULL", "SSD_ERR_SHAPE", "SSD_ERR_UNSUPPORTED", "SSD_ERR_ALIGN",
+          "SSD_ERR_ALIAS", "SSD_ERR_WORKSPACE", "SSD_ERR_HIP"]
+
+_lib = None
+
+
+class SSDError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        name = STATUS[status] if 0 <= status < len(STATUS) else str(status)
+        super().__init__(f"{name}: {msg}")
+        self.status = status
+
+
+def _declare(lib):
+    i64, vp, fp, i32, sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.ssd_abi_version.restype = ctypes.c_int
+    lib.ssd_abi_version.argtypes = []
+    lib.ssd_status_str.restype = ctypes.c_char_p
+    lib.ssd_status_str.argtypes = [ctypes.c_int]
+    lib.ssd_last_error.restype = ctypes.c_char_p
+    lib.ssd_last_error.argtypes = []
+    lib.ssd_prep.restype = ctypes.c_int
+    lib.ssd_prep.argtypes = [fp, fp, fp, i64, i64, i64, i64, fp, fp, fp, vp]
+    lib.ssd_forward_workspace_size.restype = sz
+    lib.ssd_forward_workspace_size.argtypes = [i64, i64, i64, i64, i32, i64, i32]
+    lib.ssd_forward.restype = ctypes.c_int
+    lib.ssd_forward.argtypes = [vp, vp, vp, fp, fp, i64, i64, i64, i64, i32, i64, i32,
+                                fp, fp, fp, fp, vp, sz, vp]
+    lib.ssd_set_timing_events.restype = ctypes.c_int
+    lib.ssd_set_timing_events.argtypes = [vp, ctypes.c_int]
+    lib.ssd_timing_count.restype = ctypes.c_int
+    lib.ssd_timing_count.argtypes = []
+    lib.ssd_decode_step.restype = ctypes.c_int
+    lib.ssd_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, i64, i64, i64, i32, i32, fp, fp, fp, vp]
+    return lib
+
+
+def lib():
+    """Load libssd.so (built in-tree by ``python -m mamba_ssd_sequence_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m mamba_ssd_sequence_amd.build` (no fallback path exists)")
+        _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def header_functions() -> list[str]:
+    """Names of the functions declared in include/ssd.h."""
+    with open(HEADER) as f:
+        txt = f.read()
+    return sorted(set(re.findall(r"^\s*(?:ssd_status|size_t|int|const char\*)\s+(ssd_\w+)\s*\(", txt, re.M)))
+
+
+def _check(status: int):
+    if status != SSD_OK:
+        raise SSDError(status, lib().ssd_last_error().decode())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require(t, name, dtype=None, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _qkv_dtype(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return SSD_BF16
+    if t.dtype == torch.float32:
+        return SSD_F32
+    raise ValueError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def prep(dt_proj, dt_bias, A_log, chunk: int, out=None):
+    """ssd_prep: returns (dt [B,H,N], a_cs [B,H,N], a_chunk [B,H,ceil(N/chunk)])."""
+    torch = _torch()
+    f32 = torch.float32
+    _require(dt_proj, "dt_proj", f32)
+    dev = dt_proj.device
+    _require(dt_bias, "dt_bias", f32, dev)
+    _require(A_log, "A_log", f32, dev)
+    B, H, N = dt_proj.shape
+    if dt_bias.shape != (H,) or A_log.shape != (H,):
+        raise ValueError("dt_bias and A_log must have shape [H]")
+    nc = -(-N // chunk)
+    if out is None:
+        out = (torch.empty_like(dt_proj), torch.empty_like(dt_proj),
+               torch.empty((B, H, nc), dtype=f32, device=dev))
+    dt, a_cs, a_chunk = out
+    _check(lib().ssd_prep(_ptr(dt_proj), _ptr(dt_bias), _ptr(A_log), B, H, N, chunk,
+                          _ptr(dt), _ptr(a_cs), _ptr(a_chunk), _stream(dev)))
+    return dt, a_cs, a_chunk
+
+
+def workspace_size(B, H, N, d_h, order, chunk, dtype) -> int:
+    return int(lib().ssd_forward_workspace_size(B, H, N, d_h, order, chunk, dtype))
+
+
+def forward(q, k, v, dt, a_cs, order: int, chunk: int, *, y=None, den=None,
+            final_state=None, final_norm=None, workspace=None):
+    """ssd_forward: y [B,H,N,d_h] fp32 (den and final states optional outputs)."""
+    torch = _torch()
+    _require(q, "q")
+    dev = q.device
+    dtype = _qkv_dtype(q)
+    for name, t in (("k", k), ("v", v)):
+        _require(t, name, q.dtype, dev)
+        if t.shape != q.shape:
+            raise ValueError(f"{name} shape {tuple(t.shape)} != q shape {tuple(q.shape)}")
+    B, H, N, d_h = q.shape
+    if dt is not None:
+        _require(dt, "dt", torch.float32, dev)
+    _require(a_cs, "a_cs", torch.float32, dev)
+    if y is None:
+        y = torch.empty((B, H, N, d_h), dtype=torch.float32, device=dev)
+    for name, t in (("y", y), ("den", den), ("final_state", final_state), ("final_norm", final_norm)):
+        if t is not None:
+            _require(t, name, torch.float32, dev)
+    need = workspace_size(B, H, N, d_h, order, chunk, dtype)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib().ssd_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(dt), _ptr(a_cs), B, H, N, d_h, order,
+                             chunk, dtype, _ptr(y), _ptr(den), _ptr(final_state), _ptr(final_norm),
+                             _ptr(workspace), wbytes, _stream(dev)))
+    return y
+
+
+class KernelTimer:
+    """Per-kernel HIP-event timing of one ssd_forward call (events recorded by
+    the library on its own stream, between its kernel launches)."""
+
+    N_EVENTS = 8
+
+    def __init__(self):
+        torch = _torch()
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(self.N_EVENTS)]
+        for e in self.events:  # materialise the underlying hipEvent_t
+            e.record()
+        self._arr = (ctypes.c_void_p * self.N_EVENTS)(*[e.cuda_event for e in self.events])
+        self.count = 0
+
+    def arm(self):
+        _check(lib().ssd_set_timing_events(self._arr, self.N_EVENTS))
+
+    def collect(self):
+        """After ssd_forward: remember how many kernels were bracketed."""
+        self.count = lib().ssd_timing_count()
+
+    def durations_ms(self):
+        """Per-kernel durations (call after synchronising)."""
+        return [self.events[i].elapsed_time(self.events[i + 1]) for i in range(self.count)]
+
+
+def decode_step(q, k, v, dt_proj, dt_bias, A_log, state, norm_state, order: int, *, y=None):
+    """ssd_decode_step: updates state/norm_state in place, returns y [S,H,d_h] fp32."""
+    torch = _torch()
+    _require(q, "q")
+    dev = q.device
+    dtype = _qkv_dtype(q)
+    for name, t in (("k", k), ("v", v)):
+        _require(t, name, q.dtype, dev)
+    S, H, d_h = q.shape
+    for name, t in (("dt_proj", dt_proj), ("dt_bias", dt_bias), ("A_log", A_log),
+                    ("state", state), ("norm_state", norm_state)):
+        _require(t, name, torch.float32, dev)
+    if y is None:
+        y = torch.empty((S, H, d_h), dtype=torch.float32, device=dev)
+    _check(lib().ssd_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(dt_proj), _ptr(dt_bias), _ptr(A_log),
+                                 S, H, d_h, order, dtype, _ptr(state), _ptr(norm_state), _ptr(y),
+                                 _stream(dev)))
+    return y

@@ -1,0 +1,112 @@
+"""The C ABI on the CPU: the library loads, exports every function include/ssd.h
+declares, and rejects bad arguments before any HIP call (fake, never
+dereferenced addresses are passed; no call here reaches a kernel launch)."""
+import ctypes
+
+import pytest
+
+from mamba_ssd_sequence_amd import ssd
+
+A = [0x100000 * (i + 1) for i in range(24)]  # distinct, 16-byte aligned fake addresses
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return ssd.lib()
+
+
+def test_exports_every_header_function(lib):
+    names = ssd.header_functions()
+    assert set(names) >= {"ssd_prep", "ssd_forward", "ssd_forward_workspace_size", "ssd_decode_step",
+                          "ssd_abi_version", "ssd_status_str", "ssd_last_error"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings(lib):
+    assert lib.ssd_abi_version() == 1
+    for i, name in enumerate(ssd.STATUS):
+        assert lib.ssd_status_str(i).decode() == name
+    assert lib.ssd_status_str(99).decode() == "SSD_ERR_UNKNOWN"
+
+
+def prep(lib, *, ptrs=None, B=1, H=2, N=100, chunk=64):
+    p = list(A[:6]) if ptrs is None else ptrs
+    return lib.ssd_prep(p[0], p[1], p[2], B, H, N, chunk, p[3], p[4], p[5], None)
+
+
+def test_prep_errors(lib):
+    assert prep(lib, ptrs=[A[0], None, A[2], A[3], A[4], A[5]]) == 1
+    assert "NULL" in lib.ssd_last_error().decode()
+    assert prep(lib, B=0) == 2
+    assert prep(lib, N=-5) == 2
+    assert prep(lib, B=1 << 40, H=1 << 40) == 2
+    assert prep(lib, chunk=32) == 3
+    assert prep(lib, ptrs=[A[0] + 4] + A[1:6]) == 4
+    assert prep(lib, ptrs=A[:3] + [A[0]] + A[4:6]) == 5  # dt output aliases dt_proj
+    assert prep(lib, ptrs=A[:3] + [A[3], A[3] + 16, A[5]]) == 5  # outputs overlap each other
+
+
+def fwd(lib, *, B=1, H=2, N=100, d_h=64, order=1, chunk=64, dtype=1, ws=None, wbytes=None,
+        q=A[0], dt=A[3], y=A[10], den=None, fs=None, fn=None):
+    need = lib.ssd_forward_workspace_size(B, H, N, d_h, order, chunk, dtype)
+    ws = A[20] if ws is None else ws
+    wbytes = need if wbytes is None else wbytes
+    return lib.ssd_forward(q, A[1], A[2], dt, A[4], B, H, N, d_h, order, chunk, dtype,
+                           y, den, fs, fn, ws, wbytes, None)
+
+
+def test_forward_errors(lib):
+    assert fwd(lib, q=None) == 1
+    assert fwd(lib, y=None) == 1
+    assert fwd(lib, fs=A[11], fn=None) == 1
+    assert fwd(lib, N=0) == 2
+    assert fwd(lib, d_h=48) == 3
+    assert fwd(lib, order=3) == 3
+    assert fwd(lib, chunk=256) == 3
+    assert fwd(lib, dtype=7) == 3
+    assert fwd(lib, order=2, d_h=32) == 3
+    assert fwd(lib, order=2, dtype=0) == 3
+    assert fwd(lib, q=A[0] + 2) == 4
+    assert fwd(lib, y=A[1]) == 5  # y aliases k
+    assert "output y overlaps input k" in lib.ssd_last_error().decode()
+    assert fwd(lib, den=A[10] + 16) == 5  # den overlaps y
+    assert fwd(lib, wbytes=16) == 6
+    assert fwd(lib, ws=0) == 6
+
+
+def test_workspace_size(lib):
+    # order 1: block totals + per-block states; order 2 adds the a-slice partials
+    B, H, N, d = 2, 3, 200, 64
+    nb = -(-N // 64)
+    w1 = lib.ssd_forward_workspace_size(B, H, N, d, 1, 64, 1)
+    assert w1 >= 4 * (B * H * nb + B * H * nb * (d * d + d))
+    w2 = lib.ssd_forward_workspace_size(B, H, N, d, 2, 64, 1)
+    assert w2 > w1 + 4 * B * H * N * 64
+    assert lib.ssd_forward_workspace_size(B, H, N, 48, 1, 64, 1) == 0
+    assert lib.ssd_forward_workspace_size(0, H, N, d, 1, 64, 1) == 0
+
+
+def dec(lib, *, S=1, H=1, d_h=64, order=2, dtype=1, q=A[0], state=A[6], norm=A[7], y=A[8]):
+    return lib.ssd_decode_step(q, A[1], A[2], A[3], A[4], A[5], S, H, d_h, order, dtype,
+                               state, norm, y, None)
+
+
+def test_decode_errors(lib):
+    assert dec(lib, q=None) == 1
+    assert dec(lib, state=None) == 1
+    assert dec(lib, S=0) == 2
+    assert dec(lib, d_h=16) == 3
+    assert dec(lib, order=0) == 3
+    assert dec(lib, dtype=2) == 3
+    assert dec(lib, y=A[8] + 8) == 4
+    assert dec(lib, y=A[0]) == 5
+    assert "y" in lib.ssd_last_error().decode() and "q" in lib.ssd_last_error().decode()
+    assert dec(lib, norm=A[6] + 64) == 5  # norm_state inside state
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 2, 64)
+    with pytest.raises(ValueError):
+        ssd.prep(x, torch.zeros(2), torch.zeros(2), 64)

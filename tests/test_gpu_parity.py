@@ -1,0 +1,292 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU fp64 oracle.
+
+Every test runs the library on seeded inputs and compares element by element
+with the oracle on the same stored values, using the row-scaled metric of
+tests/parity.py (tol 1e-4 for fp32 inputs, 2e-2 for bf16 inputs).  Small
+cases check every row; the full-size workloads are run in the launch
+configuration the benchmark times and checked on sampled rows (first and last
+block, block boundaries +-1, random rows), which the oracle evaluates one by
+one.
+"""
+import numpy as np
+import pytest
+
+from mamba_ssd_sequence_amd import inputs as I
+from oracle import ssd_oracle as O
+from parity import TOL, row_error, sample_rows, to_dev_f32, to_dev_qkv
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from mamba_ssd_sequence_amd import ssd
+    ssd.lib()
+
+
+def ssd_mod():
+    from mamba_ssd_sequence_amd import ssd
+    return ssd
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def run_forward(inp, order, chunk, *, with_dt=True, want_den=False, want_final=False):
+    ssd = ssd_mod()
+    c = inp.cfg
+    q, k, v = (to_dev_qkv(x, c.dtype) for x in (inp.q, inp.k, inp.v))
+    dtp, bias, alog = to_dev_f32(inp.dt_proj), to_dev_f32(inp.dt_bias), to_dev_f32(inp.A_log)
+    dt, a_cs, a_chunk = ssd.prep(dtp, bias, alog, chunk)
+    B, H, N, d = q.shape
+    D = d ** order
+    den = torch.empty((B, H, N), device="cuda") if want_den else None
+    fs = torch.empty((B, H, D, d), device="cuda") if want_final else None
+    fn = torch.empty((B, H, D), device="cuda") if want_final else None
+    y = ssd.forward(q, k, v, dt if with_dt else None, a_cs, order, chunk, den=den,
+                    final_state=fs, final_norm=fn)
+    torch.cuda.synchronize()
+    out = {"y": y.cpu().numpy(), "dt": dt.cpu().numpy(), "a_cs": a_cs.cpu().numpy(),
+           "a_chunk": a_chunk.cpu().numpy()}
+    if want_den:
+        out["den"] = den.cpu().numpy()
+    if want_final:
+        out["fs"] = fs.cpu().numpy()
+        out["fn"] = fn.cpu().numpy()
+    return out
+
+
+def oracle_forward(inp, order, rows=None, with_dt=True):
+    q, k, v = inp.qkv_f64()
+    if with_dt:
+        return O.forward_ref(q, k, v, inp.dt_proj, inp.dt_bias, inp.A_log, order, rows=rows)
+    _, a = O.discretise(inp.dt_proj, inp.dt_bias, inp.A_log)
+    return O.forward_quadratic(q, k, v, a, order, rows=rows)
+
+
+# ---------------------------------------------------------------------------
+# prep
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(I.CONFIGS))
+def test_prep_full_size(name):
+    cfg = I.CONFIGS[name]
+    say("prep", name)
+    inp = I.make_forward_inputs(cfg)
+    ssd = ssd_mod()
+    dt, a_cs, a_chunk = ssd.prep(to_dev_f32(inp.dt_proj), to_dev_f32(inp.dt_bias),
+                                 to_dev_f32(inp.A_log), cfg.chunk)
+    torch.cuda.synchronize()
+    dt_r, cs_r, tot_r = O.prep_ref(inp.dt_proj, inp.dt_bias, inp.A_log, cfg.chunk)
+    np.testing.assert_allclose(dt.cpu().numpy(), dt_r, rtol=2e-6, atol=0)
+    # a <= 0, so |chunk-local cumsum| is the running sum of |a|; an fp32 scan of
+    # at most 128 terms is accurate to a small multiple of eps times that sum
+    err = np.abs(a_cs.cpu().numpy() - cs_r)
+    bound = 1e-5 * np.abs(cs_r) + 1e-6
+    assert np.all(err <= bound), float((err / bound).max())
+    np.testing.assert_allclose(a_chunk.cpu().numpy(), tot_r, rtol=2e-6, atol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# forward: small shapes, every row, ragged tails
+# ---------------------------------------------------------------------------
+
+SMALL = [
+    # (config to draw from, order, d_h override via config, N, chunk)
+    ("o1_f32_small", 1, 1, 2, 1, 64), ("o1_f32_small", 1, 1, 2, 63, 64), ("o1_f32_small", 1, 1, 2, 65, 128),
+    ("o1_f32_small", 1, 2, 1, 200, 64), ("o1_f32_small", 1, 1, 1, 300, 128),
+    ("o1_bf16_2k", 1, 1, 2, 1, 64), ("o1_bf16_2k", 1, 1, 2, 129, 64), ("o1_bf16_2k", 1, 2, 2, 333, 128),
+    ("o2_bf16_4k", 2, 1, 1, 1, 64), ("o2_bf16_4k", 2, 1, 2, 64, 64), ("o2_bf16_4k", 2, 1, 2, 65, 64),
+    ("o2_bf16_4k", 2, 2, 1, 257, 128), ("o2_bf16_4k", 2, 1, 3, 700, 64),
+]
+
+
+@pytest.mark.parametrize("name,order,B,H,N,chunk", SMALL)
+def test_forward_small(name, order, B, H, N, chunk):
+    say("forward small", name, order, B, H, N, chunk)
+    cfg = I.CONFIGS[name]
+    inp = I.make_forward_inputs(cfg, B=B, H=H, N=N, seed=N + 7 * H)
+    got = run_forward(inp, order, chunk, want_den=True)
+    ref = oracle_forward(inp, order)
+    err = row_error(got["y"], ref["y"], ref["scale"])
+    say("  err", err)
+    assert err <= TOL[cfg.dtype]
+    den_err = np.abs(got["den"] - ref["den"]) / (ref["kappa"] * np.abs(ref["den"]))
+    assert float(den_err.max()) <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("name", ["o1_bf16_2k", "o2_bf16_4k"])
+def test_forward_plain_value_operand(name):
+    """dt = NULL: v itself is the value operand (Algorithm 5 as printed)."""
+    cfg = I.CONFIGS[name]
+    inp = I.make_forward_inputs(cfg, B=1, H=2, N=190, seed=3)
+    got = run_forward(inp, cfg.order, 64, with_dt=False)
+    ref = oracle_forward(inp, cfg.order, with_dt=False)
+    assert row_error(got["y"], ref["y"], ref["scale"]) <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("name", ["o1_f32_small", "o1_bf16_2k", "o2_bf16_4k"])
+def test_chunk_size_invariance(name):
+    cfg = I.CONFIGS[name]
+    inp = I.make_forward_inputs(cfg, B=1, H=2, N=640, seed=5)
+    a = run_forward(inp, cfg.order, 64)
+    b = run_forward(inp, cfg.order, 128)
+    ref = oracle_forward(inp, cfg.order)
+    assert row_error(a["y"], ref["y"], ref["scale"]) <= TOL[cfg.dtype]
+    assert row_error(b["y"], ref["y"], ref["scale"]) <= TOL[cfg.dtype]
+
+
+@pytest.mark.parametrize("name", ["o1_f32_small", "o1_bf16_2k", "o2_bf16_4k"])
+def test_final_state_matches_recurrence(name):
+    cfg = I.CONFIGS[name]
+    N = 200
+    inp = I.make_forward_inputs(cfg, B=1, H=2, N=N, seed=11)
+    got = run_forward(inp, cfg.order, cfg.chunk, want_final=True)
+    q, k, v = inp.qkv_f64()
+    dt, a = O.discretise(inp.dt_proj, inp.dt_bias, inp.A_log)
+    _, _, S, z = O.forward_recurrent(q, k, v * dt[..., None], a, cfg.order)
+    tol = TOL[cfg.dtype]
+    assert np.abs(got["fs"] - S).max() <= tol * np.abs(S).max()
+    assert np.abs(got["fn"] - z).max() <= tol * np.abs(z).max()
+
+
+def test_deterministic():
+    cfg = I.CONFIGS["o2_bf16_4k"]
+    inp = I.make_forward_inputs(cfg, B=1, H=2, N=300, seed=2)
+    a = run_forward(inp, 2, 64)["y"]
+    b = run_forward(inp, 2, 64)["y"]
+    assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------------------
+# forward: the full-size workloads, sampled rows
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name,n_random", [("o1_f32_small", None), ("o1_bf16_2k", 48),
+                                            ("o2_bf16_4k", 48), ("o2_bf16_64k", 24)])
+def test_forward_full_size(name, n_random):
+    cfg = I.CONFIGS[name]
+    say("forward full", name)
+    inp = I.make_forward_inputs(cfg)
+    got = run_forward(inp, cfg.order, cfg.chunk, want_den=True)
+    rng = np.random.default_rng(99)
+    rows = None if n_random is None else sample_rows(cfg.N, n_random, rng)
+    say("  oracle rows", "all" if rows is None else len(rows))
+    ref = oracle_forward(inp, cfg.order, rows=rows)
+    y = got["y"] if rows is None else got["y"][:, :, rows]
+    err = row_error(y, ref["y"], ref["scale"])
+    say("  err", err)
+    assert err <= TOL[cfg.dtype]
+    assert np.all(np.isfinite(got["y"]))
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+def run_decode_steps(dec, order, steps, S=None, check_heads=None):
+    """Run `steps` decode steps on the GPU from a zero state; returns per-step
+    y (all, or only check_heads rows) and the final state/norm of check_heads."""
+    ssd = ssd_mod()
+    c = dec.cfg
+    S = c.S if S is None else S
+    D = c.d_h ** order
+    state = torch.zeros((S, c.H, D, c.d_h), device="cuda")
+    norm = torch.zeros((S, c.H, D), device="cuda")
+    bias, alog = to_dev_f32(dec.dt_bias), to_dev_f32(dec.A_log)
+    ys, ins = [], []
+    for (q, k, v, dtp) in dec.steps(steps, S=S):
+        y = ssd.decode_step(to_dev_qkv(q, c.dtype), to_dev_qkv(k, c.dtype), to_dev_qkv(v, c.dtype),
+                            to_dev_f32(dtp), bias, alog, state, norm, order)
+        if check_heads is None:
+            ys.append(y.cpu().numpy())
+            ins.append((q, k, v, dtp))
+        else:
+            s_idx, h_idx = check_heads
+            ys.append(y[s_idx, h_idx].cpu().numpy())
+            ins.append(tuple(x[s_idx, h_idx] for x in (q, k, v, dtp)))
+    torch.cuda.synchronize()
+    if check_heads is None:
+        return ys, ins, state.cpu().numpy(), norm.cpu().numpy()
+    s_idx, h_idx = check_heads
+    return ys, ins, state[s_idx, h_idx].cpu().numpy(), norm[s_idx, h_idx].cpu().numpy()
+
+
+def decode_reference(ins, dtype, A_log, dt_bias, order, h_idx=None):
+    """The oracle over the decode steps (recurrence), plus the quadratic-form
+    diagnostics for the row-scaled metric."""
+    up = I.bf16_bits_to_f64 if dtype == I.BF16 else (lambda x: x.astype(np.float64))
+    qs = np.stack([up(x[0]) for x in ins], axis=-2)  # [S,H,T,d] or [M,T,d]
+    ks = np.stack([up(x[1]) for x in ins], axis=-2)
+    vs = np.stack([up(x[2]) for x in ins], axis=-2)
+    dtp = np.stack([x[3] for x in ins], axis=-1).astype(np.float64)
+    if h_idx is not None:  # [M,T,...] rows of (s,h) pairs: treat as B=1, H=M with per-row params
+        qs, ks, vs, dtp = qs[None], ks[None], vs[None], dtp[None]
+        A_log, dt_bias = A_log[h_idx], dt_bias[h_idx]
+    return O.forward_ref(qs, ks, vs, dtp, dt_bias, A_log, order)
+
+
+@pytest.mark.parametrize("order,d_h,dtype", [(1, 32, I.F32), (1, 64, I.BF16), (2, 32, I.BF16),
+                                             (2, 64, I.BF16), (2, 64, I.F32)])
+def test_decode_small(order, d_h, dtype):
+    say("decode small", order, d_h, dtype)
+    cfg = I.DecodeConfig("t", S=3, H=2, d_h=d_h, order=order, steps=17, dtype=dtype, seed=order * 10 + d_h)
+    dec = I.make_decode_inputs(cfg)
+    ys, ins, st, nz = run_decode_steps(dec, order, cfg.steps)
+    ref = decode_reference(ins, dtype, dec.A_log.astype(np.float64), dec.dt_bias.astype(np.float64), order)
+    y = np.stack(ys, axis=2)  # [S,H,T,d]
+    assert row_error(y, ref["y"], ref["scale"]) <= TOL[dtype]
+    # final state against the token recurrence
+    up = I.bf16_bits_to_f64 if dtype == I.BF16 else (lambda x: x.astype(np.float64))
+    Sx = np.zeros((cfg.S, cfg.H, d_h ** order, d_h))
+    zx = np.zeros((cfg.S, cfg.H, d_h ** order))
+    for (q, k, v, dtp) in ins:
+        _, Sx, zx, _ = O.decode_step_ref(Sx, zx, up(q), up(k), up(v), dtp, dec.dt_bias, dec.A_log, order)
+    assert np.abs(st - Sx).max() <= 1e-5 * np.abs(Sx).max()
+    assert np.abs(nz - zx).max() <= 1e-5 * np.abs(zx).max()
+
+
+def test_decode_full_size_sampled():
+    """The order-2 decode workload (256 x 32 heads, 128 steps) run at full size;
+    16 (sequence, head) pairs are checked at every step and at the end."""
+    cfg = I.DECODE_CONFIGS["o2_decode"]
+    say("decode full")
+    dec = I.make_decode_inputs(cfg)
+    rng = np.random.default_rng(5)
+    s_idx = rng.integers(0, cfg.S, 16)
+    h_idx = rng.integers(0, cfg.H, 16)
+    ys, ins, st, nz = run_decode_steps(dec, cfg.order, cfg.steps, check_heads=(s_idx, h_idx))
+    ref = decode_reference(ins, cfg.dtype, dec.A_log.astype(np.float64), dec.dt_bias.astype(np.float64),
+                           cfg.order, h_idx=h_idx)
+    y = np.stack(ys, axis=1)[None]  # [1,M,T,d]
+    err = row_error(y, ref["y"], ref["scale"])
+    say("  err", err)
+    assert err <= TOL[cfg.dtype]
+
+
+def test_prefill_then_decode():
+    """Forward over N tokens hands its final states to decode; continuing for T
+    tokens equals the oracle over N + T tokens."""
+    ssd = ssd_mod()
+    cfg = I.CONFIGS["o2_bf16_4k"]
+    N, T = 130, 6
+    inp = I.make_forward_inputs(cfg, B=2, H=2, N=N + T, seed=21)
+    pre = I.ForwardInputs(I.CONFIGS["o2_bf16_4k"], inp.q[:, :, :N], inp.k[:, :, :N], inp.v[:, :, :N],
+                          inp.dt_proj[:, :, :N], inp.A_log, inp.dt_bias)
+    got = run_forward(pre, 2, 64, want_final=True)
+    state = torch.from_numpy(got["fs"]).cuda()
+    norm = torch.from_numpy(got["fn"]).cuda()
+    B, H = 2, 2
+    bias, alog = to_dev_f32(inp.dt_bias), to_dev_f32(inp.A_log)
+    ys = []
+    for t in range(N, N + T):
+        q, k, v = (to_dev_qkv(np.ascontiguousarray(x[:, :, t]), cfg.dtype) for x in (inp.q, inp.k, inp.v))
+        y = ssd.decode_step(q, k, v, to_dev_f32(inp.dt_proj[:, :, t]), bias, alog, state, norm, 2)
+        ys.append(y.cpu().numpy())
+    ref = oracle_forward(inp, 2, rows=np.arange(N, N + T))
+    y = np.stack(ys, axis=2)
+    assert row_error(y, ref["y"], ref["scale"]) <= TOL[cfg.dtype]

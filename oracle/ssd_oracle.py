@@ -147,7 +147,10 @@ def _head_quadratic(q, k, vop, a, order, rows):
             abs_num[r] = aw @ np.abs(vop[: i + 1])
     with np.errstate(divide="ignore", invalid="ignore"):
         kappa = abs_sum / np.abs(den)
-        scale = abs_num.max(axis=1) / np.abs(den)
+        y = num / den[:, None]
+        # first-order rounding bound of a quotient of two sums:
+        # |d(n/d)| <= (|dn| + |n/d| |dd|) / |d|, |dn| <= eps sum|w||v|, |dd| <= eps sum|w|
+        scale = (abs_num + np.abs(y) * abs_sum[:, None]) / np.abs(den)[:, None]
     return num, den, kappa, scale
 
 
@@ -158,10 +161,12 @@ def forward_quadratic(q, k, vop, a, order, rows=None):
     a: [B,H,N] per-token log-decay.  rows: optional sorted 1-D array of token
     indices to evaluate (one by one, so that long sequences can be sampled).
 
-    Returns dict with y = num/den, num, den, and the per-row diagnostics
-    kappa = sum_j |w_ij| / |den_i| and
-    scale = max_c sum_j |w_ij| |vop_jc| / |den_i|
-    (the magnitude a floating-point evaluation of the row is accurate to).
+    Returns dict with y = num/den, num, den, and the diagnostics
+    kappa[i] = sum_j |w_ij| / |den_i| (condition of the normaliser) and
+    scale[i, c] = (sum_j |w_ij| |vop_jc| + |y_ic| sum_j |w_ij|) / |den_i|,
+    the first-order rounding-error bound of y_ic = num_ic / den_i divided by
+    the unit roundoff: a floating-point evaluation of y_ic with relative
+    accuracy eps in its sums is off by at most about eps * scale[i, c].
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -171,7 +176,8 @@ def forward_quadratic(q, k, vop, a, order, rows=None):
     R = N if rows is None else len(rows)
     dv = vop.shape[-1]
     out = {n: np.empty((B, H, R, dv)) for n in ("num",)}
-    out.update({n: np.empty((B, H, R)) for n in ("den", "kappa", "scale")})
+    out.update({n: np.empty((B, H, R)) for n in ("den", "kappa")})
+    out["scale"] = np.empty((B, H, R, dv))
     for b in range(B):
         for h in range(H):
             num, den, kap, sc = _head_quadratic(q[b, h], k[b, h], vop[b, h], a[b, h], order, rows)

@@ -41,7 +41,7 @@ def rand_case(rng, B, H, N, d, dv=None, a_scale=1.0, signed=True):
 
 
 def rel_err(x, y, scale):
-    return np.max(np.abs(x - y) / scale[..., None])
+    return np.max(np.abs(x - y) / scale)
 
 
 # ---------------------------------------------------------------------------
@@ -316,3 +316,27 @@ def test_decode_steps_equal_forward(order):
     tr = lambda x: np.moveaxis(x, 0, 2)  # [T,S,H,...] -> [S,H,T,...]
     fwd = O.forward_ref(tr(qs), tr(ks), tr(vs), np.moveaxis(dtps, 0, 2), bias, A_log, order)
     assert rel_err(ys, fwd["y"], fwd["scale"]) <= 1e-10
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_error_scale_bounds_an_fp32_evaluation(order):
+    """The oracle's per-element error scale is the first-order rounding bound of
+    y = num/den: an fp32 evaluation of the same quadratic form (signed features,
+    so order-1 normalisers nearly cancel on some rows) stays within a small
+    multiple of fp32's unit roundoff times that scale on every element."""
+    rng = np.random.default_rng(15)
+    q, k, v, a = rand_case(rng, 1, 2, 160, 8, a_scale=0.3)
+    ref = O.forward_quadratic(q, k, v, a, order)
+    q32, k32, v32 = (x.astype(np.float32) for x in (q, k, v))
+    cs = np.cumsum(a, axis=-1).astype(np.float32)
+    y32 = np.empty_like(v32)
+    for h in range(2):
+        G = (q32[0, h] @ k32[0, h].T) ** order
+        D = np.exp(np.where(np.tril(np.ones((160, 160), bool)), cs[0, h][:, None] - cs[0, h][None, :],
+                            -np.inf)).astype(np.float32)
+        W = (G * D).astype(np.float32)
+        y32[0, h] = (W @ v32[0, h]) / W.sum(axis=1, dtype=np.float32)[:, None]
+    err = np.abs(y32 - ref["y"]) / ref["scale"]
+    assert err.max() <= 1e-5
+    if order == 1:
+        assert ref["kappa"].max() > 50  # the case really contains ill-conditioned rows

@@ -67,7 +67,8 @@ __global__ __launch_bounds__(256) void k_chunk_state(const void* __restrict__ kp
   using C = typename G::C;
   using St = typename G::St;
   constexpr int P = BLK + G::PAD;
-  __shared__ __attribute__((aligned(16))) C wKT[DH * P];  // [b][j] = w_j k_jb
+  __shared__ __attribute__((aligned(16))) C wKT[DH * P];  // [b][j] = w_j k_jb (bf16: high part)
+  __shared__ __attribute__((aligned(16))) C wKL[BF ? DH * P : 1];  // bf16: w_j k_jb - high part
   __shared__ __attribute__((aligned(16))) C VT[DH * P];   // [c][j] = val_jc
   __shared__ float wv[BLK];
   __shared__ float dtv[BLK];
@@ -101,7 +102,10 @@ __global__ __launch_bounds__(256) void k_chunk_state(const void* __restrict__ kp
       kv = Elem<St>::ld(k, (row + t0 + j) * DH + d);
       vv = Elem<St>::ld(v, (row + t0 + j) * DH + d);
     }
-    wKT[d * P + j] = (C)(wv[j] * kv);
+    const float wk = wv[j] * kv;
+    const C hi = (C)wk;
+    wKT[d * P + j] = hi;
+    if constexpr (BF) wKL[d * P + j] = (C)(wk - (float)hi);
     VT[d * P + j] = (C)(vv * dtv[j]);
   }
   __syncthreads();
@@ -109,18 +113,27 @@ __global__ __launch_bounds__(256) void k_chunk_state(const void* __restrict__ kp
   const int wave = tid / WAVE, lane = tid & (WAVE - 1), n = lane & 15, g = lane >> 4;
   constexpr int NT = DH / 16;
   float* out = state + (bh * nblk + blk) * (int64_t)(DH * DH + DH);
+  // bf16 operands: w*k is split into high + low bf16 parts (two products), so
+  // the state keeps ~16 significant bits of each weighted key; the value
+  // operand is used as rounded once.
   for (int tile = wave; tile < NT * NT; tile += 4) {
     const int ct = tile / NT, bt = tile - (tile / NT) * NT;
     f32x4 acc = zero4();
 #pragma unroll
-    for (int ks = 0; ks < BLK / G::KS; ++ks)
-      acc = G::mma(G::ld(VT, P, ct * 16 + n, ks, g), G::ld(wKT, P, bt * 16 + n, ks, g), acc);
+    for (int ks = 0; ks < BLK / G::KS; ++ks) {
+      const auto a = G::ld(VT, P, ct * 16 + n, ks, g);
+      acc = G::mma(a, G::ld(wKT, P, bt * 16 + n, ks, g), acc);
+      if constexpr (BF) acc = G::mma(a, G::ld(wKL, P, bt * 16 + n, ks, g), acc);
+    }
     // acc[r] = dS^T[c = 16ct + 4g + r][b = 16bt + n]  ->  dS[b][c]
     *reinterpret_cast<f32x4*>(&out[(bt * 16 + n) * DH + ct * 16 + 4 * g]) = acc;
   }
   if (tid < DH) {
     float s = 0.f;
-    for (int j = 0; j < BLK; ++j) s += (float)wKT[tid * P + j];
+    for (int j = 0; j < BLK; ++j) {
+      s += (float)wKT[tid * P + j];
+      if constexpr (BF) s += (float)wKL[tid * P + j];
+    }
     out[DH * DH + tid] = s;
   }
 }
@@ -220,6 +233,7 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
   __shared__ __attribute__((aligned(16))) C Ks[BLK * PQ];   // [j][d]
   __shared__ __attribute__((aligned(16))) C VT[DH * PJ];    // [c][j]  value operand, transposed
   __shared__ __attribute__((aligned(16))) C SinT[DH * PQ];  // [c][b]  entering state, transposed
+  __shared__ __attribute__((aligned(16))) C SinL[BF ? DH * PQ : 1];  // bf16: low part of the same
   __shared__ float zin[DH];
   __shared__ float csl[BLK];
   __shared__ float dtv[BLK];
@@ -260,7 +274,10 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
   const float* st = state + (bh * nblk + blk) * (int64_t)(DH * DH + DH);
   for (int e = tid; e < DH * DH; e += 256) {
     const int b = e / DH, c = e - (e / DH) * DH;
-    SinT[c * PQ + b] = (C)st[e];
+    const float x = st[e];
+    const C hi = (C)x;
+    SinT[c * PQ + b] = hi;
+    if constexpr (BF) SinL[c * PQ + b] = (C)(x - (float)hi);
   }
   if (ORDER == 1 && tid < DH) zin[tid] = st[DH * DH + tid];
   __syncthreads();
@@ -336,15 +353,21 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
   }
   den_l = sum_over_groups(den_l);
 
-  // inter-block part: D[c][i] = sum_b SinT[c][b] Q[i][b]
+  // inter-block part: D[c][i] = sum_b S_in[b][c] Q[i][b].  With bf16
+  // operands the state is split into high + low bf16 parts: the factored sum
+  // over b can cancel (q nearly orthogonal to the keys), so a single bf16
+  // rounding of the state would be amplified.
   const float eci = expf(cs_i);
   f32x4 inter[NT];
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct) {
     f32x4 acc = zero4();
 #pragma unroll
-    for (int ks = 0; ks < DH / G::KS; ++ks)
-      acc = G::mma(G::ld(SinT, PQ, ct * 16 + n, ks, g), G::ld(Qs, PQ, il, ks, g), acc);
+    for (int ks = 0; ks < DH / G::KS; ++ks) {
+      const auto b = G::ld(Qs, PQ, il, ks, g);
+      acc = G::mma(G::ld(SinT, PQ, ct * 16 + n, ks, g), b, acc);
+      if constexpr (BF) acc = G::mma(G::ld(SinL, PQ, ct * 16 + n, ks, g), b, acc);
+    }
     inter[ct] = acc;
   }
   float den_x = 0.f;

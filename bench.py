@@ -39,7 +39,7 @@ METRIC = "SSD fwd tokens/sec at N=4K and 64K (order 1/2); % bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 KERNELS_O1 = ["block_state", "state_pass", "output"]
-KERNELS_O2 = ["norm_block_state", "norm_state_pass", "o2_state_scan", "output"]
+KERNELS_O2 = ["block_prep", "norm_state_pass", "o2_state_scan", "output"]
 
 
 def log(*a):
@@ -148,12 +148,15 @@ def cpu_baseline_forward(cfg: I.Config, inp, budget_s=12.0):
         sample = f"quadratic-form oracle over {heads} whole head(s) of {B * H}, N={N}"
     else:
         rng = np.random.default_rng(0)
-        rows = np.sort(rng.integers(0, N, 48))
         t0 = time.time()
-        O.forward_quadratic(q[:1, :1], k[:1, :1], vdt[:1, :1], a[:1, :1], cfg.order, rows=rows)
+        done = 0
+        while done == 0 or time.time() - t0 < budget_s:
+            rows = np.sort(rng.integers(0, N, 64))
+            O.forward_quadratic(q[:1, :1], k[:1, :1], vdt[:1, :1], a[:1, :1], cfg.order, rows=rows)
+            done += len(rows)
         el = time.time() - t0
-        t_head = el / len(rows) * N
-        sample = (f"quadratic-form oracle on {len(rows)} uniformly sampled rows of 1 head (N={N}), "
+        t_head = el / done * N
+        sample = (f"quadratic-form oracle on {done} uniformly sampled rows of 1 head (N={N}), "
                   f"extrapolated to all rows and {B * H} heads")
     tokens_per_s = N / (H * t_head)  # B*N tokens need B*H head evaluations
     return {"value": tokens_per_s, "unit": "tokens/s", "cores": blas_threads(), "kind": "oracle",
@@ -245,6 +248,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (64K forward, decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a device-to-device copy of MIB MiB (reference for HBM counters)")
     a = ap.parse_args()
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the mixer's workloads are per-head independent "
@@ -254,6 +259,15 @@ def main():
     import torch
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if a.copy_calibration:
+        nbytes = a.copy_calibration << 20
+        src = torch.ones(nbytes // 4, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {nbytes} bytes device to device 3 times")
+        return
     from mamba_ssd_sequence_amd import ssd
     ssd.lib()
 

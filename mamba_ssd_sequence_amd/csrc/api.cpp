@@ -215,16 +215,18 @@ ssd_status ssd_forward(const void* q, const void* k, const void* v, const float*
       tm.mark();
       return hip_status(e, "output launch");
     }
-    // order 2: Z (normaliser state, a d_h x d_h matrix) by the block machinery
-    // with k as its own value operand; the D x d_h numerator state on chip.
+    // order 2: per-block preparation (normaliser contributions Z_blk and the
+    // numerator operand records), the Z scan, the on-chip numerator scan, and
+    // the output kernel.
     float* part = ws + L.part;
-    if ((e = ssd::launch_chunk_state(true, 64, k, k, nullptr, a_cs, BH, N, chunk, tb, st, stream)) != hipSuccess)
-      return hip_status(e, "chunk_state launch");
+    void* rec = ws + L.rec;
+    if ((e = ssd::launch_o2_blockprep(q, k, v, dt, a_cs, BH, N, chunk, tb, st, rec, stream)) != hipSuccess)
+      return hip_status(e, "o2_blockprep launch");
     tm.mark();
     if ((e = ssd::launch_state_pass(64, BH, N, tb, st, final_norm, nullptr, stream)) != hipSuccess)
       return hip_status(e, "state_pass launch");
     tm.mark();
-    if ((e = ssd::launch_o2_state(q, k, v, dt, a_cs, BH, N, chunk, part, final_state, stream)) != hipSuccess)
+    if ((e = ssd::launch_o2_state(rec, BH, N, part, final_state, stream)) != hipSuccess)
       return hip_status(e, "o2_state launch");
     tm.mark();
     e = ssd::launch_output(true, 64, 2, q, k, v, dt, a_cs, BH, N, chunk, st, part, ssd::o2_pa(BH), y, den, stream);

@@ -1,0 +1,243 @@
+// Order-2 block preparation: everything about a 64-token block that does not
+// depend on the blocks before it, computed for all blocks in parallel.
+//
+// For block (b, h, blk) with chunk-local cumsum cs (2Mamba2Furious,
+// Algorithm 3's A^CS restricted to the block), T = cs_last - cs_start and
+// w_j = exp(T - cs_j):
+//   1. the normaliser state contribution of Algorithm 6's H_down at order 2,
+//      kept as the d_h x d_h matrix Z_blk = sum_j w_j k_j k_j^T (and the unused
+//      sum_j w_j k_j), on bf16 MFMA with w k split into high + low parts;
+//   2. the operand record the numerator state scan consumes (layout in
+//      launch.h): fp16 q 2^tau (columns permuted for the MFMA operand), fp16
+//      k^T 2^kap, fp16 X^T 2^xi with X_jc = w_j dt_j v_jc, e^{cs_i}, and the
+//      block scalars (T, the bound delta = max|k|^2 sum_j max_c |X_jc| of
+//      any entry of the block's state increment, and the three exponents).
+//      The exponents put max|q| 2^tau below 2^13, max|k| 2^kap below 1 and
+//      max|X| 2^xi below 2^14, so every fp16 value is exact for bf16 inputs
+//      (q, k) or rounded once (X).
+//
+// One 256-thread workgroup per (head, block); grid B*H*nblk.
+#include "common.h"
+#include "launch.h"
+
+namespace ssd {
+
+namespace {
+constexpr int DH = 64;
+constexpr int P = DH + 8;  // LDS row pitch (16-bit elements)
+
+__device__ __forceinline__ float lo16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ int exp_ceil(float x) {
+  if (!(x > 0.f) || !isfinite(x)) return 0;
+  int e;
+  frexpf(x, &e);
+  return e;
+}
+__device__ __forceinline__ int clamp64(int x) { return x < -64 ? -64 : (x > 64 ? 64 : x); }
+
+__device__ __forceinline__ float wmax(float x) {
+#pragma unroll
+  for (int off = 1; off < WAVE; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, WAVE));
+  return x;
+}
+__device__ __forceinline__ float wsum(float x) {
+#pragma unroll
+  for (int off = 1; off < WAVE; off <<= 1) x += __shfl_xor(x, off, WAVE);
+  return x;
+}
+}  // namespace
+
+typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
+
+__global__ __launch_bounds__(256) void k_o2_blockprep(const uint16_t* __restrict__ q,
+                                                      const uint16_t* __restrict__ k,
+                                                      const uint16_t* __restrict__ v,
+                                                      const float* __restrict__ dt,
+                                                      const float* __restrict__ a_cs, int64_t N,
+                                                      int64_t chunk, int64_t nblk,
+                                                      float* __restrict__ tb,
+                                                      float* __restrict__ state,
+                                                      uint8_t* __restrict__ rec) {
+  __shared__ __attribute__((aligned(16))) __bf16 wKT[DH * P];  // [b][j] high part of w_j k_jb
+  __shared__ __attribute__((aligned(16))) __bf16 wKL[DH * P];  // [b][j] low part
+  __shared__ __attribute__((aligned(16))) __bf16 KTb[DH * P];  // [b][j] k_jb
+  __shared__ __attribute__((aligned(16))) __bf16 VTb[DH * P];  // [c][j] v_jc
+  __shared__ float wv[BLK], wdt[BLK], vrow[BLK];
+  __shared__ float red_q[4], red_k[4];
+  __shared__ float s_xsum, s_xmax;
+
+  const int64_t bh = blockIdx.x / nblk, blk = blockIdx.x - bh * nblk;
+  const int64_t t0 = blk * BLK;
+  const int nv = (int)((N - t0) < BLK ? (N - t0) : BLK);
+  const int64_t row = bh * N;
+  const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
+  uint8_t* R = rec + (bh * nblk + blk) * (int64_t)REC_BYTES;
+
+  const float base = (t0 % chunk == 0) ? 0.f : a_cs[row + t0 - 1];
+  const float cs_last = a_cs[row + t0 + nv - 1];
+  const float T = cs_last - base;
+  if (tid < BLK) {
+    float w = 0.f, d = 0.f, e = 1.f;
+    if (tid < nv) {
+      const float acs = a_cs[row + t0 + tid];
+      w = expf(cs_last - acs);
+      d = dt ? dt[row + t0 + tid] : 1.f;
+      e = expf(acs - base);
+    }
+    wv[tid] = w;
+    wdt[tid] = w * d;
+    reinterpret_cast<float*>(R + REC_ECS)[tid] = e;
+  }
+  if (tid == 0) tb[bh * nblk + blk] = T;
+  __syncthreads();
+
+  // pass 1: q, k, v segments (8 values each) -> maxima, Z operands, v^T
+  float qm = 0.f, km = 0.f;
+  uint4 qs[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int s = tid + u * 256, j = s >> 3, seg = s & 7;
+    uint4 qv = make_uint4(0, 0, 0, 0), kv = qv, vv = qv;
+    if (j < nv) {
+      const int64_t off = (row + t0 + j) * DH + seg * 8;
+      qv = *reinterpret_cast<const uint4*>(q + off);
+      kv = *reinterpret_cast<const uint4*>(k + off);
+      vv = *reinterpret_cast<const uint4*>(v + off);
+    }
+    qs[u] = qv;
+    const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w}, kw[4] = {kv.x, kv.y, kv.z, kv.w},
+                   vw[4] = {vv.x, vv.y, vv.z, vv.w};
+    const float w = wv[j];
+    float vm = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float q0 = lo16(qw[i]), q1 = hi16(qw[i]);
+      const float k0 = lo16(kw[i]), k1 = hi16(kw[i]);
+      const float v0 = lo16(vw[i]), v1 = hi16(vw[i]);
+      qm = fmaxf(qm, fmaxf(fabsf(q0), fabsf(q1)));
+      km = fmaxf(km, fmaxf(fabsf(k0), fabsf(k1)));
+      vm = fmaxf(vm, fmaxf(fabsf(v0), fabsf(v1)));
+      const int d0 = seg * 8 + 2 * i;
+      const float wk0 = w * k0, wk1 = w * k1;
+      const __bf16 h0 = (__bf16)wk0, h1 = (__bf16)wk1;
+      wKT[d0 * P + j] = h0;
+      wKT[(d0 + 1) * P + j] = h1;
+      wKL[d0 * P + j] = (__bf16)(wk0 - (float)h0);
+      wKL[(d0 + 1) * P + j] = (__bf16)(wk1 - (float)h1);
+      KTb[d0 * P + j] = __builtin_bit_cast(__bf16, (uint16_t)(kw[i] & 0xffffu));
+      KTb[(d0 + 1) * P + j] = __builtin_bit_cast(__bf16, (uint16_t)(kw[i] >> 16));
+      VTb[d0 * P + j] = __builtin_bit_cast(__bf16, (uint16_t)(vw[i] & 0xffffu));
+      VTb[(d0 + 1) * P + j] = __builtin_bit_cast(__bf16, (uint16_t)(vw[i] >> 16));
+    }
+    // the 8 consecutive lanes of a row: max |v_jc| over the row
+    vm = fmaxf(vm, __shfl_xor(vm, 1, WAVE));
+    vm = fmaxf(vm, __shfl_xor(vm, 2, WAVE));
+    vm = fmaxf(vm, __shfl_xor(vm, 4, WAVE));
+    if (seg == 0) vrow[j] = vm;
+  }
+  qm = wmax(qm);
+  km = wmax(km);
+  if (lane == 0) {
+    red_q[wave] = qm;
+    red_k[wave] = km;
+  }
+  __syncthreads();
+  if (wave == 0) {
+    const float xm = fabsf(wdt[lane]) * vrow[lane];  // max_c |X_jc|
+    const float xs = wsum(xm), xmx = wmax(xm);
+    if (lane == 0) {
+      s_xsum = xs;
+      s_xmax = xmx;
+    }
+  }
+
+  // normaliser contribution Z_blk (bf16 MFMA, w k in high + low parts)
+  {
+    const int n = lane & 15, g = lane >> 4;
+    float* out = state + (bh * nblk + blk) * (int64_t)(DH * DH + DH);
+    for (int tile = wave; tile < 16; tile += 4) {
+      const int ct = tile >> 2, bt = tile & 3;
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&KTb[(ct * 16 + n) * P + ks * 32 + 8 * g]);
+        acc = mfma_bf16(a, *reinterpret_cast<const bf16x8*>(&wKT[(bt * 16 + n) * P + ks * 32 + 8 * g]), acc);
+        acc = mfma_bf16(a, *reinterpret_cast<const bf16x8*>(&wKL[(bt * 16 + n) * P + ks * 32 + 8 * g]), acc);
+      }
+      // acc[r] = Z^T[c = 16ct + 4g + r][b = 16bt + n] -> Z[b][c]
+      *reinterpret_cast<f32x4*>(&out[(bt * 16 + n) * DH + ct * 16 + 4 * g]) = acc;
+    }
+    if (tid < DH) {
+      float s = 0.f;
+      for (int j = 0; j < BLK; ++j) s += (float)wKT[tid * P + j] + (float)wKL[tid * P + j];
+      out[DH * DH + tid] = s;
+    }
+  }
+  __syncthreads();
+
+  // pass 2: scales and the fp16 record
+  const float qmax = fmaxf(fmaxf(red_q[0], red_q[1]), fmaxf(red_q[2], red_q[3]));
+  const float kmax = fmaxf(fmaxf(red_k[0], red_k[1]), fmaxf(red_k[2], red_k[3]));
+  const int tau = clamp64(13 - exp_ceil(qmax));
+  const int kap = clamp64(-exp_ceil(kmax));
+  const int xi = clamp64(14 - exp_ceil(s_xmax));
+  const float sq = ldexpf(1.f, tau), sk = ldexpf(1.f, kap), sx = ldexpf(1.f, xi);
+  if (tid == 0) {
+    float* sc = reinterpret_cast<float*>(R + REC_SC);
+    int* si = reinterpret_cast<int*>(R + REC_SC);
+    sc[0] = T;
+    sc[1] = kmax * kmax * s_xsum;
+    si[2] = tau;
+    si[3] = kap;
+    si[4] = xi;
+  }
+  // q rows: columns of each 32-block permuted to (4g..4g+3, 16+4g..16+4g+3)
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int s = tid + u * 256, j = s >> 3, seg = s & 7;
+    const uint32_t qw[4] = {qs[u].x, qs[u].y, qs[u].z, qs[u].w};
+    h16x4 h0, h1;
+    h0[0] = (_Float16)(lo16(qw[0]) * sq);
+    h0[1] = (_Float16)(hi16(qw[0]) * sq);
+    h0[2] = (_Float16)(lo16(qw[1]) * sq);
+    h0[3] = (_Float16)(hi16(qw[1]) * sq);
+    h1[0] = (_Float16)(lo16(qw[2]) * sq);
+    h1[1] = (_Float16)(hi16(qw[2]) * sq);
+    h1[2] = (_Float16)(lo16(qw[3]) * sq);
+    h1[3] = (_Float16)(hi16(qw[3]) * sq);
+    const int sl = seg & 3;
+    const int p0 = (seg >> 2) * 32 + (sl < 2 ? 16 * sl : 16 * (sl - 2) + 4);
+    _Float16* QH = reinterpret_cast<_Float16*>(R + REC_QH) + j * DH;
+    *reinterpret_cast<h16x4*>(QH + p0) = h0;
+    *reinterpret_cast<h16x4*>(QH + p0 + 8) = h1;
+  }
+  // k^T and X^T rows: thread -> (row r, 8 consecutive j)
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int s = tid + u * 256, r = s >> 3, j0 = (s & 7) * 8;
+    h16x8 hk, hx;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      hk[i] = (_Float16)((float)KTb[r * P + j0 + i] * sk);
+      hx[i] = (_Float16)((float)VTb[r * P + j0 + i] * wdt[j0 + i] * sx);
+    }
+    *reinterpret_cast<h16x8*>(reinterpret_cast<_Float16*>(R + REC_KT) + r * DH + j0) = hk;
+    *reinterpret_cast<h16x8*>(reinterpret_cast<_Float16*>(R + REC_XT) + r * DH + j0) = hx;
+  }
+}
+
+hipError_t launch_o2_blockprep(const void* q, const void* k, const void* v, const float* dt,
+                               const float* a_cs, int64_t BH, int64_t N, int64_t chunk, float* tb,
+                               float* state, void* rec, hipStream_t stream) {
+  const int64_t nb = n_blocks(N);
+  hipLaunchKernelGGL(k_o2_blockprep, dim3((unsigned)(BH * nb)), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                     static_cast<const uint16_t*>(v), dt, a_cs, N, chunk, nb, tb, state,
+                     static_cast<uint8_t*>(rec));
+  return hipGetLastError();
+}
+
+}  // namespace ssd

@@ -16,6 +16,18 @@ __host__ __device__ inline int64_t n_blocks(int64_t N) { return (N + 63) / 64; }
 inline int o2_aw(int64_t BH) { return BH >= 32 ? 4 : (BH >= 16 ? 2 : 1); }
 inline int o2_pa(int64_t BH) { return 64 / (8 * o2_aw(BH)); }
 
+// Order-2 per-block operand record (bytes), written by the block-prep kernel
+// and read by the state scan:
+//   QH  [64 i][64]   fp16 q_ib 2^tau, columns of each 32-block in the order the
+//                    permuted-k MFMA operand reads them
+//   KT  [64 b][64 j] fp16 k_jb 2^kap (transposed)
+//   XT  [64 c][64 j] fp16 X_jc 2^xi, X_jc = w_j dt_j v_jc, w_j = e^{T - cs_j}
+//   ECS [64]         fp32 e^{cs_i} (decay from the block start to token i)
+//   SC               fp32 T, fp32 delta (bound of any |state increment|),
+//                    int32 tau, kap, xi
+constexpr int REC_QH = 0, REC_KT = 8192, REC_XT = 16384, REC_ECS = 24576, REC_SC = 24832;
+constexpr int REC_BYTES = 24864;
+
 // Workspace layout (float offsets), in this order:
 //   tb     [BH, nblk]                 block decay totals
 //   state  [BH, nblk, DH*DH + DH]     per-block state contributions, then
@@ -23,8 +35,9 @@ inline int o2_pa(int64_t BH) { return 64 / (8 * o2_aw(BH)); }
 //                                     (order 1: S and z; order 2: Z and unused)
 //   part   [P_a, BH, N, 64]           order 2 only: inter-block numerator
 //                                     partials of each a-slice
+//   rec    [BH, nblk] x REC_BYTES     order 2 only: operand records
 struct WsLayout {
-  size_t tb, state, part, total_floats;
+  size_t tb, state, part, rec, total_floats;
 };
 
 inline WsLayout ws_layout(int64_t B, int64_t H, int64_t N, int64_t DH, int order) {
@@ -38,6 +51,9 @@ inline WsLayout ws_layout(int64_t B, int64_t H, int64_t N, int64_t DH, int order
   off = (off + 63) & ~(size_t)63;
   L.part = off;
   if (order == 2) off += (size_t)o2_pa(BH) * (size_t)BH * (size_t)N * 64;
+  off = (off + 63) & ~(size_t)63;
+  L.rec = off;
+  if (order == 2) off += (size_t)(BH * nb) * (REC_BYTES / 4);
   L.total_floats = off;
   return L;
 }
@@ -62,9 +78,15 @@ hipError_t launch_output(bool bf16, int64_t DH, int order, const void* q, const 
                          int64_t chunk, const float* state, const float* part, int P_a, float* y,
                          float* den, hipStream_t stream);
 
-// Order-2 inter-block numerator: on-chip state scan over blocks.
-hipError_t launch_o2_state(const void* q, const void* k, const void* v, const float* dt,
-                           const float* a_cs, int64_t BH, int64_t N, int64_t chunk, float* part,
+// Order 2, per block (parallel): the normaliser state contribution
+// sum_j w_j k_j k_j^T (as launch_chunk_state with k as the value) and the
+// operand record of the numerator scan.
+hipError_t launch_o2_blockprep(const void* q, const void* k, const void* v, const float* dt,
+                               const float* a_cs, int64_t BH, int64_t N, int64_t chunk, float* tb,
+                               float* state, void* rec, hipStream_t stream);
+
+// Order-2 inter-block numerator: on-chip state scan over the block records.
+hipError_t launch_o2_state(const void* rec, int64_t BH, int64_t N, float* part,
                            float* final_state, hipStream_t stream);
 
 hipError_t launch_decode(bool bf16, int64_t DH, int order, const void* q, const void* k,

@@ -193,6 +193,7 @@ __global__ __launch_bounds__(256) void k_o2_blockprep(const uint16_t* __restrict
     si[2] = tau;
     si[3] = kap;
     si[4] = xi;
+    sc[5] = expf(T);
   }
   // q rows: columns of each 32-block permuted to (4g..4g+3, 16+4g..16+4g+3)
 #pragma unroll

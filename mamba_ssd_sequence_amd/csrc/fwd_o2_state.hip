@@ -39,7 +39,9 @@
 // (LDS) into the workspace; decide the scales of block n+1 and copy its
 // record (prefetched into registers one iteration earlier) into the other LDS
 // slot; issue the loads of block n+2; run block n's MFMA work and write its
-// partial output to LDS.  The per-block operands arrive pre-converted from
+// partial output to LDS.  Half of the waves do the MFMA work first and the
+// other half last, so every SIMD keeps its matrix core busy while the other
+// wave does the bookkeeping.  The per-block operands arrive pre-converted from
 // the block-prep kernel, so staging is plain copies.
 //
 // Grid: B*H x P_a x 4 workgroups (P_a = 64 / (8*AW)), 512 threads each; when
@@ -109,12 +111,14 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
   constexpr int PA = DH / SL;         // a-slices per head
   static_assert(BLK * DH / 8 == NT && CW * DH / 2 == NT, "thread mapping");
 
-  // staging and partial-output buffers, double-buffered by block parity so
-  // that one barrier per block suffices
+  // staging (by block parity) and partial-output buffers; e^{cs} rows rotate
+  // over three slots because the drain of block n-1 may still read them while
+  // block n+1 is staged
   __shared__ __attribute__((aligned(16))) _Float16 Qh[2][BLK * PH];  // [i][perm b] q 2^tau
   __shared__ __attribute__((aligned(16))) _Float16 KTh[2][DH * PH];  // [b][j] k 2^kap
   __shared__ __attribute__((aligned(16))) _Float16 Xh[2][CW * PH];   // [c][j] X 2^xi
-  __shared__ __attribute__((aligned(16))) float red[2][NW * 16 * WAVE];
+  __shared__ __attribute__((aligned(16))) float red[2][NW][BLK * CW];  // [i][c] per wave
+  __shared__ float st_ecs[3][BLK];
 
   const int tid = threadIdx.x;
   const int wave = tid / WAVE, lane = tid & (WAVE - 1), n = lane & 15, g = lane >> 4;
@@ -152,45 +156,41 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
 
   // ---- registers of the prefetched block -------------------------------------
   uint4 pq, pk;
-  uint32_t px;
-  float pT, pdelta;
+  uint32_t px, pe = 0;
+  float pdelta, peT;
   int ptau, pkap, pxi;
-  f32x4 pecs;  // e^{cs_i} for this lane's rows i = 16 it + n
   auto prefetch = [&](int64_t blk) {
     const uint8_t* R = rec_h + blk * (int64_t)REC_BYTES;
     pq = *reinterpret_cast<const uint4*>(R + REC_QH + (r8 * DH + sg * 8) * 2);
     pk = *reinterpret_cast<const uint4*>(R + REC_KT + (r8 * DH + sg * 8) * 2);
     px = *reinterpret_cast<const uint32_t*>(R + REC_XT + ((c0 + xr) * DH + 2 * xw) * 2);
-    const float* sc = reinterpret_cast<const float*>(R + REC_SC);
-    pT = sc[0];
+    if (tid < BLK) pe = *reinterpret_cast<const uint32_t*>(R + REC_ECS + 4 * tid);
+    const float* sc = reinterpret_cast<const float*>(R + REC_SC);  // uniform address
     pdelta = sc[1];
     ptau = __float_as_int(sc[2]);
     pkap = __float_as_int(sc[3]);
     pxi = __float_as_int(sc[4]);
-    const float* ecs = reinterpret_cast<const float*>(R + REC_ECS);
-#pragma unroll
-    for (int it = 0; it < 4; ++it) pecs[it] = ecs[it * 16 + n];
+    peT = sc[5];
   };
 
-  // scale state of the staged (next) block and of the block being computed
+  // scale state, identical in every thread
   float M = 0.f;     // upper bound of max |S| (true units) after the last decided block
   int sig_dec = 0;   // sigma of the last decided block: S is held as S * 2^sigma
   struct Blk {
     int sig, shift, tau, kap, xi;
     float eT;
-    f32x4 ecs;
   };
-  Blk nx{}, cur{};
+  Blk nx{}, cur{}, prv{};
 
-  // decide the scales of the prefetched block and copy it into slot sl
-  auto stage = [&](int sl) {
+  // decide the scales of the prefetched block blk and copy it into its slots
+  auto stage = [&](int64_t blk) {
+    const int sl = (int)(blk & 1);
     nx.tau = ptau;
     nx.kap = pkap;
     nx.xi = pxi;
-    nx.ecs = pecs;
-    nx.eT = expf(pT);
+    nx.eT = peT;
     // every update operand X 2^(sig - 2 kap) < 4 delta 2^sig <= 4 M 2^sig <= 2^15
-    const float m_after = nx.eT * M + pdelta;
+    const float m_after = peT * M + pdelta;
     const float mh = fmaxf(M, m_after);
     int sig = sig_dec;
     if (mh > 0.f && isfinite(mh)) {
@@ -204,20 +204,22 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
     *reinterpret_cast<uint4*>(&Qh[sl][r8 * PH + sg * 8]) = pq;
     *reinterpret_cast<uint4*>(&KTh[sl][r8 * PH + sg * 8]) = pk;
     *reinterpret_cast<uint32_t*>(&Xh[sl][xr * PH + 2 * xw]) = px;
+    if (tid < BLK) st_ecs[blk % 3][tid] = __uint_as_float(pe);
   };
 
-  // partial output of block blk (slot sl) -> workspace
-  auto drain = [&](int64_t blk, int sl) {
-    const int64_t t0 = blk * BLK;
-    const int nv = (int)((N - t0) < BLK ? (N - t0) : BLK);
-    for (int o = tid; o < 16 * WAVE; o += NT) {
-      float s = 0.f;
+  // partial output of block blk (its scales in p) -> workspace, scaled to
+  // true units: e^{cs_i} 2^-(sig + 2 tau)
+  auto drain = [&](int64_t blk, const Blk& p) {
+    if (tid < BLK * CW / 4) {
+      const int64_t t0 = blk * BLK;
+      const int nv = (int)((N - t0) < BLK ? (N - t0) : BLK);
+      const int i = tid >> 2, c4 = (tid & 3) * 4;
+      const float* rd = &red[blk & 1][0][i * CW + c4];
+      f32x4 s = *reinterpret_cast<const f32x4*>(rd);
 #pragma unroll
-      for (int w = 0; w < NW; ++w) s += red[sl][w * 16 * WAVE + o];
-      const int reg = o / WAVE, ln = o - (o / WAVE) * WAVE;
-      const int it = reg >> 2, r = reg & 3;
-      const int i = it * 16 + (ln & 15), c = 4 * (ln >> 4) + r;
-      if (i < nv) part[(((int64_t)pa * BH + bh) * N + t0 + i) * DH + c0 + c] = s;
+      for (int w = 1; w < NW; ++w) s += *reinterpret_cast<const f32x4*>(rd + w * BLK * CW);
+      const float f = st_ecs[blk % 3][i] * ldexpf(ldexpf(1.f, -p.sig), -2 * p.tau);
+      if (i < nv) *reinterpret_cast<f32x4*>(&part[(((int64_t)pa * BH + bh) * N + t0 + i) * DH + c0 + c4]) = s * f;
     }
   };
 
@@ -227,22 +229,9 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
 #pragma unroll
     for (int bt = 0; bt < 4; ++bt) S[ai][bt] = zero4();
 
-  // prologue: stage block 0, prefetch block 1
-  prefetch(0);
-  stage(0);
-  cur = nx;
-  if (nblk > 1) prefetch(1);
-  __syncthreads();
-
-  for (int64_t blk = 0; blk < nblk; ++blk) {
+  // MFMA work of block blk: output with the entering state, then the update
+  auto compute = [&](int64_t blk) {
     const int sl = (int)(blk & 1);
-    if (blk > 0) drain(blk - 1, sl ^ 1);
-    if (blk + 1 < nblk) {
-      stage(sl ^ 1);
-      if (blk + 2 < nblk) prefetch(blk + 2);
-    }
-
-    // ---- MFMA work of block blk from slot sl ---------------------------------
     if (cur.shift != 0) {
       const float f = ldexpf(1.f, cur.shift);
 #pragma unroll
@@ -250,91 +239,191 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
 #pragma unroll
         for (int bt = 0; bt < 4; ++bt) S[ai][bt] *= f;
     }
-    // output pass over this wave's a values, with the entering state:
-    // T^T[c][i] = sum_b S[b][c] Q[i][b];  Y[i][c] += q_ia T^T[c][i]
-    {
-      const _Float16* Q = Qh[sl];
-      f16x8 Qf[4][2];  // B operand: Q^T[b][i], permuted k = b (pre-ordered)
-#pragma unroll
-      for (int it = 0; it < 4; ++it)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          Qf[it][kb] = *reinterpret_cast<const f16x8*>(&Q[(it * 16 + n) * PH + kb * 32 + 8 * g]);
-      f32x4 Y[4];
-#pragma unroll
-      for (int it = 0; it < 4; ++it) Y[it] = zero4();
-#pragma unroll
-      for (int ai = 0; ai < AW; ++ai) {
-        f16x8 SA[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            SA[kb][r] = (_Float16)S[ai][2 * kb][r];
-            SA[kb][4 + r] = (_Float16)S[ai][2 * kb + 1][r];
+    if constexpr (AW >= 4) {
+      // four a values per wave: output pass then update pass, so that the
+      // Q and K^T operand fragments are never live together (register file)
+      // T^T[c][i] = sum_b S[b][c] Q[i][b];  Y[i][c] += q_ia T^T[c][i]
+      {
+        const _Float16* Q = Qh[sl];
+        f16x8 Qf[4][2];  // B operand: Q^T[b][i], permuted k = b (pre-ordered)
+  #pragma unroll
+        for (int it = 0; it < 4; ++it)
+  #pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            Qf[it][kb] = *reinterpret_cast<const f16x8*>(&Q[(it * 16 + n) * PH + kb * 32 + 8 * g]);
+        f32x4 Y[4];
+  #pragma unroll
+        for (int it = 0; it < 4; ++it) Y[it] = zero4();
+  #pragma unroll
+        for (int ai = 0; ai < AW; ++ai) {
+          f16x8 SA[2];
+  #pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+  #pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              SA[kb][r] = (_Float16)S[ai][2 * kb][r];
+              SA[kb][4 + r] = (_Float16)S[ai][2 * kb + 1][r];
+            }
+  #pragma unroll
+          for (int it = 0; it < 4; ++it) {
+            f32x4 T = mfma_f16(SA[0], Qf[it][0], zero4());
+            T = mfma_f16(SA[1], Qf[it][1], T);
+            Y[it] += (float)Q[(it * 16 + n) * PH + qpos[ai]] * T;
           }
-#pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          f32x4 T = mfma_f16(SA[0], Qf[it][0], zero4());
-          T = mfma_f16(SA[1], Qf[it][1], T);
-          Y[it] += (float)Q[(it * 16 + n) * PH + qpos[ai]] * T;
+        }
+        float* rd = red[sl][wave];
+  #pragma unroll
+        for (int it = 0; it < 4; ++it) *reinterpret_cast<f32x4*>(&rd[(it * 16 + n) * CW + 4 * g]) = Y[it];
+      }
+      // S = e^T S + K^T ((k_:a 2^kap) * X 2^(sig - 2 kap))
+      {
+        const _Float16* KT = KTh[sl];
+        f16x8 Kf[4][2];  // A operand: K^T[b][j], k = j contiguous
+  #pragma unroll
+        for (int bt = 0; bt < 4; ++bt)
+  #pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            Kf[bt][kb] = *reinterpret_cast<const f16x8*>(&KT[(bt * 16 + n) * PH + kb * 32 + 8 * g]);
+        // X 2^xi -> X 2^(sig - 2 kap): exact power-of-two factors (d <= 2 since
+        // max X 2^xi >= 2^13; below 2^-48 the terms are negligible and dropped)
+        const int d = cur.sig - 2 * cur.kap - cur.xi;
+        f16x8 xh[2];
+  #pragma unroll
+        for (int kb = 0; kb < 2; ++kb) xh[kb] = *reinterpret_cast<const f16x8*>(&Xh[sl][n * PH + kb * 32 + 8 * g]);
+        if (d < -48) {
+  #pragma unroll
+          for (int kb = 0; kb < 2; ++kb) xh[kb] = xh[kb] * (_Float16)0.f;
+        } else if (d >= -14) {
+          if (d != 0) {
+            const _Float16 f = (_Float16)ldexpf(1.f, d);
+  #pragma unroll
+            for (int kb = 0; kb < 2; ++kb) xh[kb] = xh[kb] * f;
+          }
+        } else {
+          const int d1 = d / 2, d2 = d - d1;
+          const _Float16 f1 = (_Float16)ldexpf(1.f, d1), f2 = (_Float16)ldexpf(1.f, d2);
+  #pragma unroll
+          for (int kb = 0; kb < 2; ++kb) xh[kb] = (xh[kb] * f1) * f2;
+        }
+  #pragma unroll
+        for (int ai = 0; ai < AW; ++ai) {
+          const int a = a0 + wave * AW + ai;  // the K^T row of k_:a
+          f16x8 Bu[2];
+  #pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+            Bu[kb] = *reinterpret_cast<const f16x8*>(&KT[a * PH + kb * 32 + 8 * g]) * xh[kb];
+  #pragma unroll
+          for (int bt = 0; bt < 4; ++bt) {
+            f32x4 acc = cur.eT * S[ai][bt];
+            acc = mfma_f16(Kf[bt][0], Bu[0], acc);
+            acc = mfma_f16(Kf[bt][1], Bu[1], acc);
+            S[ai][bt] = acc;
+          }
         }
       }
-      // true output: e^{cs_i} 2^-(sig + 2 tau) Y
-      const float ys = ldexpf(ldexpf(1.f, -cur.sig), -2 * cur.tau);
-      float* rd = red[sl];
-#pragma unroll
-      for (int it = 0; it < 4; ++it) {
-        const float f = cur.ecs[it] * ys;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) rd[(wave * 16 + it * 4 + r) * WAVE + lane] = Y[it][r] * f;
-      }
-    }
-
-    // update pass: S = e^T S + K^T ((k_:a 2^kap) * X 2^(sig - 2 kap))
-    {
+    } else {
+      // per a: output with the entering state, T^T[c][i] = sum_b S[b][c] Q[i][b],
+      // Y[i][c] += q_ia T^T[c][i]; then the update
+      // S = e^T S + K^T ((k_:a 2^kap) * X 2^(sig - 2 kap)).  The two chains of
+      // each a are independent, so their MFMA and VALU work interleave.
+      const _Float16* Q = Qh[sl];
       const _Float16* KT = KTh[sl];
-      f16x8 Kf[4][2];  // A operand: K^T[b][j], k = j contiguous
-#pragma unroll
+      f16x8 Qf[4][2];  // output B operand: Q^T[b][i], permuted k = b (pre-ordered)
+  #pragma unroll
+      for (int it = 0; it < 4; ++it)
+  #pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+          Qf[it][kb] = *reinterpret_cast<const f16x8*>(&Q[(it * 16 + n) * PH + kb * 32 + 8 * g]);
+      f16x8 Kf[4][2];  // update A operand: K^T[b][j], k = j contiguous
+  #pragma unroll
       for (int bt = 0; bt < 4; ++bt)
-#pragma unroll
+  #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
           Kf[bt][kb] = *reinterpret_cast<const f16x8*>(&KT[(bt * 16 + n) * PH + kb * 32 + 8 * g]);
       // X 2^xi -> X 2^(sig - 2 kap): exact power-of-two factors (d <= 2 since
       // max X 2^xi >= 2^13; below 2^-48 the terms are negligible and dropped)
       const int d = cur.sig - 2 * cur.kap - cur.xi;
       f16x8 xh[2];
-#pragma unroll
+  #pragma unroll
       for (int kb = 0; kb < 2; ++kb) xh[kb] = *reinterpret_cast<const f16x8*>(&Xh[sl][n * PH + kb * 32 + 8 * g]);
       if (d < -48) {
-#pragma unroll
+  #pragma unroll
         for (int kb = 0; kb < 2; ++kb) xh[kb] = xh[kb] * (_Float16)0.f;
-      } else if (d != 0) {
+      } else if (d >= -14) {
+        if (d != 0) {
+          const _Float16 f = (_Float16)ldexpf(1.f, d);
+  #pragma unroll
+          for (int kb = 0; kb < 2; ++kb) xh[kb] = xh[kb] * f;
+        }
+      } else {
         const int d1 = d / 2, d2 = d - d1;
         const _Float16 f1 = (_Float16)ldexpf(1.f, d1), f2 = (_Float16)ldexpf(1.f, d2);
-#pragma unroll
+  #pragma unroll
         for (int kb = 0; kb < 2; ++kb) xh[kb] = (xh[kb] * f1) * f2;
       }
-#pragma unroll
+      f32x4 Y[4];
+  #pragma unroll
+      for (int it = 0; it < 4; ++it) Y[it] = zero4();
+  #pragma unroll
       for (int ai = 0; ai < AW; ++ai) {
+        f16x8 SA[2];
+  #pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            SA[kb][r] = (_Float16)S[ai][2 * kb][r];
+            SA[kb][4 + r] = (_Float16)S[ai][2 * kb + 1][r];
+          }
         const int a = a0 + wave * AW + ai;  // the K^T row of k_:a
         f16x8 Bu[2];
-#pragma unroll
+  #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
           Bu[kb] = *reinterpret_cast<const f16x8*>(&KT[a * PH + kb * 32 + 8 * g]) * xh[kb];
-#pragma unroll
-        for (int bt = 0; bt < 4; ++bt) {
+  #pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          f32x4 T = mfma_f16(SA[0], Qf[it][0], zero4());
+          T = mfma_f16(SA[1], Qf[it][1], T);
+          const int bt = it;
           f32x4 acc = cur.eT * S[ai][bt];
           acc = mfma_f16(Kf[bt][0], Bu[0], acc);
           acc = mfma_f16(Kf[bt][1], Bu[1], acc);
           S[ai][bt] = acc;
+          Y[it] += (float)Q[(it * 16 + n) * PH + qpos[ai]] * T;
         }
       }
+      float* rd = red[sl][wave];
+  #pragma unroll
+      for (int it = 0; it < 4; ++it) *reinterpret_cast<f32x4*>(&rd[(it * 16 + n) * CW + 4 * g]) = Y[it];
     }
+  };
+
+  // prologue: stage block 0, prefetch block 1
+  prefetch(0);
+  stage(0);
+  cur = nx;
+  if (nblk > 1) prefetch(1);
+  __syncthreads();
+
+  // Per block: the first four waves run the MFMA work first, the other four
+  // drain/stage first, so each SIMD (waves w and w+4) overlaps the matrix
+  // work of one wave with the bookkeeping of the other.
+  for (int64_t blk = 0; blk < nblk; ++blk) {
+    const bool more = blk + 1 < nblk;
+    if (wave < NW / 2) {
+      compute(blk);
+      if (blk > 0) drain(blk - 1, prv);
+      if (more) stage(blk + 1);
+    } else {
+      if (blk > 0) drain(blk - 1, prv);
+      if (more) stage(blk + 1);
+      compute(blk);
+    }
+    if (blk + 2 < nblk) prefetch(blk + 2);
+    prv = cur;
     cur = nx;
     __syncthreads();
   }
-  drain(nblk - 1, (int)((nblk - 1) & 1));
+  drain(nblk - 1, prv);
 
   if (final_state) {
     const float f = ldexpf(1.f, -sig_dec);

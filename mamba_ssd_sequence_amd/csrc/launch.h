@@ -24,7 +24,7 @@ inline int o2_pa(int64_t BH) { return 64 / (8 * o2_aw(BH)); }
 //   XT  [64 c][64 j] fp16 X_jc 2^xi, X_jc = w_j dt_j v_jc, w_j = e^{T - cs_j}
 //   ECS [64]         fp32 e^{cs_i} (decay from the block start to token i)
 //   SC               fp32 T, fp32 delta (bound of any |state increment|),
-//                    int32 tau, kap, xi
+//                    int32 tau, kap, xi, fp32 e^T
 constexpr int REC_QH = 0, REC_KT = 8192, REC_XT = 16384, REC_ECS = 24576, REC_SC = 24832;
 constexpr int REC_BYTES = 24864;
 

@@ -36,6 +36,38 @@ sys.path.insert(0, ROOT)
 from mamba_ssd_sequence_amd import inputs as I  # noqa: E402
 
 METRIC = "SSD fwd tokens/sec at N=4K and 64K (order 1/2); % bf16 MFMA peak"
+CSRC = os.path.join(ROOT, "mamba_ssd_sequence_amd", "csrc")
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+# sources each profiled kernel is built from: a traffic figure measured on one
+# version of a kernel is reported only while these files are unchanged
+KERNEL_SOURCES = {
+    "k_o2_state": ["fwd_o2_state.hip", "launch.h", "common.h"],
+    "k_output": ["fwd_blocks.hip", "launch.h", "common.h"],
+    "k_decode": ["decode.hip", "launch.h", "common.h"],
+}
+
+
+def kernel_source_sha(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary (calibrated against a plain copy), or None if absent or if the
+    kernel's sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_JSON) as f:
+            t = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not t or t.get("workload") != workload or t.get("source_sha256") != kernel_source_sha(kernel):
+        return None
+    return t["traffic_bytes"]
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 KERNELS_O1 = ["block_state", "state_pass", "output"]
@@ -110,7 +142,8 @@ def bench_forward(cfg: I.Config, steps: int, warmup: int, dev):
         ach = flops / (t_ms * 1e-3) / 1e12
         res["roofline"] = {"kernel": "k_o2_state", "bound": "mfma", "achieved": ach,
                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                           "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                           "frac": ach / PEAK_BF16_TFLOPS,
+                           "traffic": measured_traffic("k_o2_state", cfg.name),
                            "alg_flops_per_launch": flops, "avg_launch_ms": t_ms}
         # whole-step MFMA fraction of the method's chunked work (SURVEY-style count)
         res["step_mfma_frac"] = flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
@@ -123,7 +156,8 @@ def bench_forward(cfg: I.Config, steps: int, warmup: int, dev):
         ach = by / (t_ms * 1e-3) / 1e9
         res["roofline"] = {"kernel": "k_output", "bound": "hbm", "achieved": ach,
                            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                           "traffic": None, "alg_bytes_per_launch": by, "avg_launch_ms": t_ms}
+                           "traffic": measured_traffic("k_output", cfg.name),
+                           "alg_bytes_per_launch": by, "avg_launch_ms": t_ms}
     return res, inp
 
 
@@ -200,7 +234,8 @@ def bench_decode(cfg: I.DecodeConfig, steps: int, warmup: int, dev):
     return {"workload": cfg.name, "ms_per_step": ms, "tokens_per_s": cfg.S / (ms * 1e-3),
             "S": cfg.S, "H": cfg.H, "d_h": cfg.d_h, "order": cfg.order, "steps": steps,
             "roofline": {"kernel": "k_decode", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None,
+                         "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                         "traffic": measured_traffic("k_decode", cfg.name),
                          "alg_bytes_per_launch": by, "avg_launch_ms": t_ms}}, dec
 
 

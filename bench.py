@@ -71,7 +71,7 @@ def measured_traffic(kernel: str, workload: str):
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 KERNELS_O1 = ["block_state", "state_pass", "output"]
-KERNELS_O2 = ["block_prep", "norm_state_pass", "o2_state_scan", "output"]
+KERNELS_O2 = ["block_prep", "scale_and_norm_scans", "o2_state_scan", "output"]
 
 
 def log(*a):

@@ -383,7 +383,7 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
       for (int r = 0; r < 4; ++r) den_x += (float)Qs[il * PQ + ct * 16 + 4 * g + r] * inter[ct][r];
     if (il < nvalid) {
       for (int pa = 0; pa < P_a; ++pa) {
-        const float* pp = part + (((int64_t)pa * BH + bh) * N + t0 + il) * 64;
+        const float* pp = part + (((int64_t)pa * BH + bh) * (nblk * BLK) + t0 + il) * 64;
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) num[ct] += *reinterpret_cast<const f32x4*>(pp + ct * 16 + 4 * g);
       }

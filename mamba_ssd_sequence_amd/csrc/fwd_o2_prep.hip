@@ -49,6 +49,7 @@ __device__ __forceinline__ float wsum(float x) {
 }
 }  // namespace
 
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 
@@ -188,14 +189,14 @@ __global__ __launch_bounds__(256) void k_o2_blockprep(const uint16_t* __restrict
   if (tid == 0) {
     float* sc = reinterpret_cast<float*>(R + REC_SC);
     int* si = reinterpret_cast<int*>(R + REC_SC);
-    sc[0] = T;
-    sc[1] = kmax * kmax * s_xsum;
-    si[2] = tau;
-    si[3] = kap;
-    si[4] = xi;
-    sc[5] = expf(T);
+    sc[SC_T] = T;
+    sc[SC_DELTA] = kmax * kmax * s_xsum;
+    si[SC_TAU] = tau;
+    si[SC_KAP] = kap;
+    si[SC_XI] = xi;
+    sc[SC_ET] = expf(T);
   }
-  // q rows: columns of each 32-block permuted to (4g..4g+3, 16+4g..16+4g+3)
+  // q rows: in each 16-column group the 4-column subgroups go to slots 0, 2, 1, 3
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
     const int s = tid + u * 256, j = s >> 3, seg = s & 7;
@@ -209,8 +210,7 @@ __global__ __launch_bounds__(256) void k_o2_blockprep(const uint16_t* __restrict
     h1[1] = (_Float16)(hi16(qw[2]) * sq);
     h1[2] = (_Float16)(lo16(qw[3]) * sq);
     h1[3] = (_Float16)(hi16(qw[3]) * sq);
-    const int sl = seg & 3;
-    const int p0 = (seg >> 2) * 32 + (sl < 2 ? 16 * sl : 16 * (sl - 2) + 4);
+    const int p0 = 16 * (seg >> 1) + 4 * (seg & 1);
     _Float16* QH = reinterpret_cast<_Float16*>(R + REC_QH) + j * DH;
     *reinterpret_cast<h16x4*>(QH + p0) = h0;
     *reinterpret_cast<h16x4*>(QH + p0 + 8) = h1;
@@ -238,6 +238,80 @@ hipError_t launch_o2_blockprep(const void* q, const void* k, const void* v, cons
                      static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                      static_cast<const uint16_t*>(v), dt, a_cs, N, chunk, nb, tb, state,
                      static_cast<uint8_t*>(rec));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Scale scan of the order-2 numerator state (one wave per head).
+//
+// The state scan holds its state S_n (after block n) as S_n 2^sig_n in fp32
+// accumulators and feeds S 2^sig to fp16 MFMA operands, so sig_n must keep
+// every entry below 2^13.  An upper bound of max |S_n| follows the state's
+// own recurrence, M_n = e^{T_n} M_{n-1} + delta_n with delta_n (block-prep)
+// bounding every entry of block n's increment; sig_n = 13 - ceil(log2 M_n).
+// The recurrence is linear, so the wave scans it in parallel: each lane
+// composes a contiguous run of blocks into (prod e^T, local M), a lane scan
+// combines the runs, and each lane replays its run from the incoming bound.
+// Per block it writes sig_in = sig_{n-1}, the combined decay-and-rescale
+// factor eTs = e^{T_n} 2^(sig_n - sig_{n-1}) (0 while the state is still
+// zero), and the fp16 factors taking the record's X 2^xi to X 2^(sig_n - 2 kap).
+// ---------------------------------------------------------------------------
+namespace {
+__device__ __forceinline__ int sig_of(float m) {
+  return (m > 0.f && isfinite(m)) ? clamp64(13 - exp_ceil(m)) : 0;
+}
+}  // namespace
+
+__global__ __launch_bounds__(64) void k_o2_scale_scan(uint8_t* __restrict__ rec, int64_t nblk) {
+  const int64_t bh = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int64_t seg = (nblk + WAVE - 1) / WAVE;
+  const int64_t b0 = lane * seg, b1 = (b0 + seg < nblk) ? b0 + seg : nblk;
+  uint8_t* base = rec + bh * nblk * (int64_t)REC_BYTES + REC_SC;
+  // run of this lane as a map M -> A M + B
+  float A = 1.f, B = 0.f;
+  for (int64_t b = b0; b < b1; ++b) {
+    const float* sc = reinterpret_cast<const float*>(base + b * (int64_t)REC_BYTES);
+    const float e = sc[SC_ET];
+    A *= e;
+    B = e * B + sc[SC_DELTA];
+  }
+  // inclusive scan of the maps over lanes: (A1, B1) then (A2, B2) = (A1 A2, A2 B1 + B2)
+#pragma unroll
+  for (int off = 1; off < WAVE; off <<= 1) {
+    const float pA = __shfl_up(A, off, WAVE), pB = __shfl_up(B, off, WAVE);
+    if (lane >= off) {
+      B = A * pB + B;
+      A = A * pA;
+    }
+  }
+  float M = __shfl_up(B, 1, WAVE);  // bound after the previous lane's run (M_{-1} = 0)
+  if (lane == 0) M = 0.f;
+  for (int64_t b = b0; b < b1; ++b) {
+    uint8_t* p = base + b * (int64_t)REC_BYTES;
+    float* sc = reinterpret_cast<float*>(p);
+    int* si = reinterpret_cast<int*>(p);
+    const float e = sc[SC_ET];
+    const float Mn = e * M + sc[SC_DELTA];
+    const int sin = sig_of(M), sout = sig_of(Mn);
+    si[SC_SIG_IN] = sin;
+    si[SC_SIG_OUT] = sout;
+    sc[SC_ETS] = M > 0.f ? ldexpf(e, sout - sin) : 0.f;
+    // X 2^xi -> X 2^(sig - 2 kap): exact power-of-two factors (d <= 2 since
+    // max X 2^xi >= 2^13; below 2^-48 the terms are negligible and dropped)
+    const int d = sout - 2 * si[SC_KAP] - si[SC_XI];
+    const int d1 = d >= -14 ? d : d / 2, d2 = d >= -14 ? 0 : d - d / 2;
+    h16x2 xf;
+    xf[0] = d < -48 ? (_Float16)0.f : (_Float16)ldexpf(1.f, d1);
+    xf[1] = (_Float16)ldexpf(1.f, d2);
+    *reinterpret_cast<h16x2*>(&sc[SC_XF]) = xf;
+    M = Mn;
+  }
+}
+
+hipError_t launch_o2_scale_scan(void* rec, int64_t BH, int64_t N, hipStream_t stream) {
+  hipLaunchKernelGGL(k_o2_scale_scan, dim3((unsigned)BH), dim3(WAVE), 0, stream,
+                     static_cast<uint8_t*>(rec), n_blocks(N));
   return hipGetLastError();
 }
 

@@ -16,33 +16,39 @@
 // Decomposition.  The 1 MiB state never leaves the chip: each workgroup owns
 // an a-slice (8*AW values of a) x a 16-column value slice, held as MFMA
 // accumulators (fp32) across the whole sequence, and walks the blocks in
-// order.  Wave w owns AW values of a (AW x 64 x 16 fp32 = 16*AW VGPRs/lane).
+// order.  Wave w owns AW values of a, taken in pairs: one 32x32 accumulator
+// tile covers 32 values of b x (2 values of a x 16 columns), so the state of
+// a pair is two tiles (32 VGPRs/lane).  On gfx950 the 32x32x16 MFMA (32
+// cycles) absorbs the per-element VALU work of this scan (decay, fp16
+// conversion, row scalings) with little loss, and its operand fragments
+// (32 rows x 16 bytes at a 144-byte pitch) read LDS without bank conflicts.
 // The A operand of the output product is the state itself (its accumulator
 // layout read as a permuted-k operand), the A operand of the update is K^T.
 // The workgroup's partial output (its a-slice) is reduced over its waves in
 // LDS and written to the workspace; the output kernel adds the P_a partials.
 //
-// Precision.  Both products run on v_mfma_f32_16x16x32_f16 (same rate as
-// bf16) with exact power-of-two scales chosen per block: q*2^tau < 2^13 and
-// k*2^kap in (-1, 1) (bf16 inputs convert to fp16 exactly), the state operand
-// S*2^sig where sig follows a running upper bound M >= max|S|
-// (M <- e^T M + sum_j w_j max|k_j|^2 max|v_j dt_j|, kept below 2^13 after
-// scaling), and the update operand (k_ja 2^kap) * X_jc with
-// X_jc = w_j (v dt)_jc 2^(sig - 2 kap) < 2^15, formed by packed fp16 multiplies.
-// fp16's 11-bit significand matters here: the factored sum over (a, b) can
-// cancel when q is nearly orthogonal to the block's keys, and a bf16 rounding
-// of the state is amplified there beyond the bf16 tolerance.  Every thread
-// reads the block's scalars itself and takes the same scale decisions, so no
-// barrier is needed for them.
+// Precision.  Both products run on v_mfma_f32_32x32x16_f16 (same rate as
+// bf16) with exact power-of-two scales: q*2^tau < 2^13 and k*2^kap in (-1, 1)
+// per block (bf16 inputs convert to fp16 exactly), the state held as
+// S*2^sig with sig from the scale scan (a running upper bound M >= max|S|,
+// M <- e^T M + sum_j w_j max|k_j|^2 max|v_j dt_j|, keeps S*2^sig below 2^13),
+// and the update operand (k_ja 2^kap) * X_jc with X_jc = w_j (v dt)_jc
+// 2^(sig - 2 kap) < 2^15, formed by packed fp16 multiplies.  fp16's 11-bit
+// significand matters here: the factored sum over (a, b) can cancel when q is
+// nearly orthogonal to the block's keys, and a bf16 rounding of the state is
+// amplified there beyond the bf16 tolerance.  A change of sig between blocks
+// is folded into the decay factor, e^T 2^(sig_n - sig_{n-1}), so rescaling
+// costs nothing; all per-block scalars come precomputed in the record.
 //
 // Pipeline, one barrier per block n: reduce block n-1's partial outputs
-// (LDS) into the workspace; decide the scales of block n+1 and copy its
-// record (prefetched into registers one iteration earlier) into the other LDS
-// slot; issue the loads of block n+2; run block n's MFMA work and write its
-// partial output to LDS.  Half of the waves do the MFMA work first and the
-// other half last, so every SIMD keeps its matrix core busy while the other
-// wave does the bookkeeping.  The per-block operands arrive pre-converted from
-// the block-prep kernel, so staging is plain copies.
+// (LDS) into the workspace; copy block n+1's record (prefetched into
+// registers one iteration earlier) into the other LDS slot; issue the loads
+// of block n+2 at once, so they have a whole block to arrive; run block n's
+// MFMA work and write its partial output to LDS.
+// Half of the waves do the MFMA work first and the other half last, so every
+// SIMD keeps its matrix core busy while the other wave does the bookkeeping.
+// The per-block operands arrive pre-converted from the block-prep kernel, so
+// staging is plain copies.
 //
 // Grid: B*H x P_a x 4 workgroups (P_a = 64 / (8*AW)), 512 threads each; when
 // B*H is a multiple of 8 the workgroups of one head share an XCD (and its L2).
@@ -52,76 +58,52 @@
 namespace ssd {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 namespace {
 constexpr int DH = 64;
 constexpr int CW = 16;      // value columns per workgroup
 constexpr int PH = DH + 8;  // fp16 row pitch (elements): 144 B
-constexpr int EXP_CLAMP = 64;
 
-__device__ __forceinline__ f32x4 mfma_f16(const f16x8& a, const f16x8& b, const f32x4& c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-// exponent e with x < 2^e (x > 0 finite); 0 otherwise
-__device__ __forceinline__ int exp_ceil(float x) {
-  if (!(x > 0.f) || !isfinite(x)) return 0;
-  int e;
-  frexpf(x, &e);
-  return e;
-}
 
-__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
-__device__ __forceinline__ float max8_abs_bf16(const uint4& u) {
-  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-  float m = 0.f;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m = fmaxf(m, fabsf(__uint_as_float(w[i] << 16)));
-    m = fmaxf(m, fabsf(__uint_as_float(w[i] & 0xffff0000u)));
-  }
-  return m;
-}
 
-__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int off = 1; off < WAVE; off <<= 1) x += __shfl_xor(x, off, WAVE);
-  return x;
-}
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int off = 1; off < WAVE; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, WAVE));
-  return x;
-}
 }  // namespace
 
-template <int AW>
-__global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ rec, int64_t BH,
-                                                  int64_t N, int xcd_map,
-                                                  float* __restrict__ part,
-                                                  float* __restrict__ final_state) {
-  constexpr int NW = 8;               // waves per workgroup
+template <int NW, int AW>
+__global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict__ rec, int64_t BH,
+                                                      int64_t N, int xcd_map,
+                                                      float* __restrict__ part,
+                                                      float* __restrict__ final_state) {
   constexpr int NT = NW * WAVE;       // threads
   constexpr int SL = NW * AW;         // a values per workgroup
   constexpr int PA = DH / SL;         // a-slices per head
-  static_assert(BLK * DH / 8 == NT && CW * DH / 2 == NT, "thread mapping");
+  constexpr int NP = AW / 2;          // a pairs per wave
+  constexpr int QP = SL + 4;          // row pitch of the q copy (elements)
+  constexpr int NI = BLK * DH / 8 / NT;   // 16-byte q / k^T segments per thread
+  constexpr int NX = CW * DH / 2 / NT;    // 32-bit X^T words per thread
+  constexpr int NQ = (BLK * SL / 4 + NT - 1) / NT;  // 4-value q groups per thread
+  constexpr bool STAGGER = NW == 8;   // two waves per SIMD
+  static_assert(AW % 2 == 0 && NI >= 1 && NX >= 1, "thread mapping");
 
   // staging (by block parity) and partial-output buffers; e^{cs} rows rotate
   // over three slots because the drain of block n-1 may still read them while
   // block n+1 is staged
   __shared__ __attribute__((aligned(16))) _Float16 Qh[2][BLK * PH];  // [i][perm b] q 2^tau
   __shared__ __attribute__((aligned(16))) _Float16 KTh[2][DH * PH];  // [b][j] k 2^kap
-  __shared__ __attribute__((aligned(16))) _Float16 Xh[2][CW * PH];   // [c][j] X 2^xi
-  __shared__ __attribute__((aligned(16))) float red[2][NW][BLK * CW];  // [i][c] per wave
+  __shared__ __attribute__((aligned(16))) _Float16 Xh[2][CW * PH];   // [c][j] X 2^(sig - 2 kap)
+  __shared__ __attribute__((aligned(16))) _Float16 Qa[2][BLK * QP];  // [i][a - a0] q 2^tau
+  __shared__ f32x4 red[2][NW][4 * WAVE];  // per wave, in accumulator order
   __shared__ float st_ecs[3][BLK];
 
   const int tid = threadIdx.x;
-  const int wave = tid / WAVE, lane = tid & (WAVE - 1), n = lane & 15, g = lane >> 4;
+  const int wave = tid / WAVE, lane = tid & (WAVE - 1), n32 = lane & 31, h = lane >> 5;
   int pc, pa;
   int64_t bh;
   if (xcd_map) {
@@ -140,260 +122,186 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
   const int a0 = pa * SL;
   const int c0 = pc * CW;
   const int64_t nblk = n_blocks(N);
+  const int64_t Np = nblk * BLK;  // partial rows per head (padded)
   const uint8_t* rec_h = rec + bh * nblk * (int64_t)REC_BYTES;
 
-  // copy roles: q / k^T row r8 and 16-byte segment sg; one 32-bit word of
-  // the workgroup's 16 X^T rows
-  const int r8 = tid >> 3, sg = tid & 7;
-  const int xr = tid >> 5, xw = tid & 31;
-  // column of q_:a in the permuted q layout, for this wave's a values
-  int qpos[AW];
-#pragma unroll
-  for (int ai = 0; ai < AW; ++ai) {
-    const int a = a0 + wave * AW + ai, bl = a & 31;
-    qpos[ai] = (a & ~31) + (bl < 16 ? 8 * (bl >> 2) + (bl & 3) : 8 * ((bl - 16) >> 2) + 4 + (bl & 3));
-  }
-
   // ---- registers of the prefetched block -------------------------------------
-  uint4 pq, pk;
-  uint32_t px, pe = 0;
-  float pdelta, peT;
-  int ptau, pkap, pxi;
-  auto prefetch = [&](int64_t blk) {
-    const uint8_t* R = rec_h + blk * (int64_t)REC_BYTES;
-    pq = *reinterpret_cast<const uint4*>(R + REC_QH + (r8 * DH + sg * 8) * 2);
-    pk = *reinterpret_cast<const uint4*>(R + REC_KT + (r8 * DH + sg * 8) * 2);
-    px = *reinterpret_cast<const uint32_t*>(R + REC_XT + ((c0 + xr) * DH + 2 * xw) * 2);
-    if (tid < BLK) pe = *reinterpret_cast<const uint32_t*>(R + REC_ECS + 4 * tid);
-    const float* sc = reinterpret_cast<const float*>(R + REC_SC);  // uniform address
-    pdelta = sc[1];
-    ptau = __float_as_int(sc[2]);
-    pkap = __float_as_int(sc[3]);
-    pxi = __float_as_int(sc[4]);
-    peT = sc[5];
-  };
-
-  // scale state, identical in every thread
-  float M = 0.f;     // upper bound of max |S| (true units) after the last decided block
-  int sig_dec = 0;   // sigma of the last decided block: S is held as S * 2^sigma
+  uint4 pq[NI], pk[NI];
+  uint32_t px[NX];
+  uint2 pqa[NQ];
+  uint32_t pe;
   struct Blk {
-    int sig, shift, tau, kap, xi;
-    float eT;
+    int sig_in, tau;  // scale exponents of the entering state and of q
+    float eTs;        // decay and rescale factor of the state
+    uint32_t xf;      // two fp16 factors for X
+    int sig_out;      // scale exponent of the state after the block
   };
   Blk nx{}, cur{}, prv{};
+  auto prefetch = [&](int64_t blk) {
+    const uint8_t* R = rec_h + blk * (int64_t)REC_BYTES;
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      const int idx = tid + u * NT, r = idx >> 3, sg = idx & 7;
+      pq[u] = *reinterpret_cast<const uint4*>(R + REC_QH + (r * DH + sg * 8) * 2);
+      pk[u] = *reinterpret_cast<const uint4*>(R + REC_KT + (r * DH + sg * 8) * 2);
+    }
+#pragma unroll
+    for (int u = 0; u < NX; ++u) {
+      const int idx = tid + u * NT, xr = idx >> 5, xw = idx & 31;
+      px[u] = *reinterpret_cast<const uint32_t*>(R + REC_XT + ((c0 + xr) * DH + 2 * xw) * 2);
+    }
+    // this workgroup's q columns a0 + 4 g4 .. +3 of row r (record column order
+    // within a 16-group: 4-column subgroups at slots 0, 2, 1, 3)
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int idx = (tid + u * NT) % (BLK * SL / 4), r = idx / (SL / 4), g4 = idx % (SL / 4);
+      const int b = a0 + 4 * g4, G = (b >> 2) & 3;
+      const int pos = (b & ~15) + 4 * (G == 1 ? 2 : (G == 2 ? 1 : G));
+      pqa[u] = *reinterpret_cast<const uint2*>(R + REC_QH + (r * DH + pos) * 2);
+    }
+    pe = *reinterpret_cast<const uint32_t*>(R + REC_ECS + 4 * (tid & (BLK - 1)));
+    const int* sc = reinterpret_cast<const int*>(R + REC_SC);  // uniform address
+    nx.sig_in = sc[SC_SIG_IN];
+    nx.tau = sc[SC_TAU];
+    nx.eTs = __int_as_float(sc[SC_ETS]);
+    nx.xf = (uint32_t)sc[SC_XF];
+    nx.sig_out = sc[SC_SIG_OUT];
+  };
 
-  // decide the scales of the prefetched block blk and copy it into its slots
+  // copy the prefetched block blk into its LDS slot, X scaled to the state's
+  // scale (a block beyond the last one is copied into the slot no block
+  // reads any more)
   auto stage = [&](int64_t blk) {
     const int sl = (int)(blk & 1);
-    nx.tau = ptau;
-    nx.kap = pkap;
-    nx.xi = pxi;
-    nx.eT = peT;
-    // every update operand X 2^(sig - 2 kap) < 4 delta 2^sig <= 4 M 2^sig <= 2^15
-    const float m_after = peT * M + pdelta;
-    const float mh = fmaxf(M, m_after);
-    int sig = sig_dec;
-    if (mh > 0.f && isfinite(mh)) {
-      const int target = clampi(13 - exp_ceil(mh), -EXP_CLAMP, EXP_CLAMP);
-      if (sig > target || sig < target - 12) sig = target;
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      const int idx = tid + u * NT, r = idx >> 3, sg = idx & 7;
+      *reinterpret_cast<uint4*>(&Qh[sl][r * PH + sg * 8]) = pq[u];
+      *reinterpret_cast<uint4*>(&KTh[sl][r * PH + sg * 8]) = pk[u];
     }
-    nx.shift = sig - sig_dec;
-    nx.sig = sig;
-    sig_dec = sig;
-    M = m_after;
-    *reinterpret_cast<uint4*>(&Qh[sl][r8 * PH + sg * 8]) = pq;
-    *reinterpret_cast<uint4*>(&KTh[sl][r8 * PH + sg * 8]) = pk;
-    *reinterpret_cast<uint32_t*>(&Xh[sl][xr * PH + 2 * xw]) = px;
-    if (tid < BLK) st_ecs[blk % 3][tid] = __uint_as_float(pe);
+    const f16x2 xf = __builtin_bit_cast(f16x2, nx.xf);
+#pragma unroll
+    for (int u = 0; u < NX; ++u) {
+      const int idx = tid + u * NT, xr = idx >> 5, xw = idx & 31;
+      const f16x2 x = (__builtin_bit_cast(f16x2, px[u]) * xf[0]) * xf[1];
+      *reinterpret_cast<f16x2*>(&Xh[sl][xr * PH + 2 * xw]) = x;
+    }
+#pragma unroll
+    for (int u = 0; u < NQ; ++u) {
+      const int idx = tid + u * NT;
+      if (NT * NQ == BLK * SL / 4 || idx < BLK * SL / 4) {
+        const int r = idx / (SL / 4), g4 = idx % (SL / 4);
+        *reinterpret_cast<uint2*>(&Qa[sl][r * QP + 4 * g4]) = pqa[u];
+      }
+    }
+    st_ecs[blk % 3][tid & (BLK - 1)] = __uint_as_float(pe);
   };
 
   // partial output of block blk (its scales in p) -> workspace, scaled to
-  // true units: e^{cs_i} 2^-(sig + 2 tau)
+  // true units: e^{cs_i} 2^-(sig_in + 2 tau)
   auto drain = [&](int64_t blk, const Blk& p) {
-    if (tid < BLK * CW / 4) {
+    if (NT == BLK * CW / 4 || tid < BLK * CW / 4) {
       const int64_t t0 = blk * BLK;
-      const int nv = (int)((N - t0) < BLK ? (N - t0) : BLK);
       const int i = tid >> 2, c4 = (tid & 3) * 4;
-      const float* rd = &red[blk & 1][0][i * CW + c4];
-      f32x4 s = *reinterpret_cast<const f32x4*>(rd);
+      // element (i, c4..c4+3) sits in accumulator slot (i/32, c4/8) of lane
+      // i%32 + 32 ((c4/4) & 1)
+      const int idx = ((i >> 5) * 2 + (c4 >> 3)) * WAVE + (i & 31) + 32 * ((c4 >> 2) & 1);
+      f32x4 s = red[blk & 1][0][idx];
 #pragma unroll
-      for (int w = 1; w < NW; ++w) s += *reinterpret_cast<const f32x4*>(rd + w * BLK * CW);
-      const float f = st_ecs[blk % 3][i] * ldexpf(ldexpf(1.f, -p.sig), -2 * p.tau);
-      if (i < nv) *reinterpret_cast<f32x4*>(&part[(((int64_t)pa * BH + bh) * N + t0 + i) * DH + c0 + c4]) = s * f;
+      for (int w = 1; w < NW; ++w) s += red[blk & 1][w][idx];
+      const float f = st_ecs[blk % 3][i] * ldexpf(ldexpf(1.f, -p.sig_in), -2 * p.tau);
+      *reinterpret_cast<f32x4*>(&part[(((int64_t)pa * BH + bh) * Np + t0 + i) * DH + c0 + c4]) = s * f;
     }
   };
 
-  f32x4 S[AW][4];
+  // state: pair p, b-tile bt (32 rows) -> 32 x 32 accumulator over
+  // (b) x (a = a_p + n32/16, c = c0 + n32%16); lane (n32, h) holds the rows
+  // b = 32 bt + 8 q + 4 h + s in register 4 q + s
+  f32x16 S[NP][2];
 #pragma unroll
-  for (int ai = 0; ai < AW; ++ai)
+  for (int p = 0; p < NP; ++p)
 #pragma unroll
-    for (int bt = 0; bt < 4; ++bt) S[ai][bt] = zero4();
+    for (int bt = 0; bt < 2; ++bt) S[p][bt] = f32x16{};
 
-  // MFMA work of block blk: output with the entering state, then the update
+  // MFMA work of block blk: the output product with the entering state for
+  // every pair, then the update.  Output: T^T[(a, c)][i] = sum_b S[b][(a, c)]
+  // Q[i][b] over 16-row k-steps kk (b in 16 kk + {4h..4h+3, 8+4h..8+4h+3} on
+  // lane half h, matching the record's q column order), then
+  // Y[i][c] += q_ia T^T[(a, c)][i].  Update: S = e^T S + K^T ((k_:a 2^kap) *
+  // X 2^(sig - 2 kap)) over 16-token k-steps (tokens 16 kk + 8 h .. +7 on
+  // lane half h).  The two passes keep the Q and K^T operand fragments from
+  // being live together (register file).
   auto compute = [&](int64_t blk) {
     const int sl = (int)(blk & 1);
-    if (cur.shift != 0) {
-      const float f = ldexpf(1.f, cur.shift);
-#pragma unroll
-      for (int ai = 0; ai < AW; ++ai)
-#pragma unroll
-        for (int bt = 0; bt < 4; ++bt) S[ai][bt] *= f;
-    }
-    if constexpr (AW >= 4) {
-      // four a values per wave: output pass then update pass, so that the
-      // Q and K^T operand fragments are never live together (register file)
-      // T^T[c][i] = sum_b S[b][c] Q[i][b];  Y[i][c] += q_ia T^T[c][i]
-      {
-        const _Float16* Q = Qh[sl];
-        f16x8 Qf[4][2];  // B operand: Q^T[b][i], permuted k = b (pre-ordered)
-  #pragma unroll
-        for (int it = 0; it < 4; ++it)
-  #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-            Qf[it][kb] = *reinterpret_cast<const f16x8*>(&Q[(it * 16 + n) * PH + kb * 32 + 8 * g]);
-        f32x4 Y[4];
-  #pragma unroll
-        for (int it = 0; it < 4; ++it) Y[it] = zero4();
-  #pragma unroll
-        for (int ai = 0; ai < AW; ++ai) {
-          f16x8 SA[2];
-  #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-  #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              SA[kb][r] = (_Float16)S[ai][2 * kb][r];
-              SA[kb][4 + r] = (_Float16)S[ai][2 * kb + 1][r];
-            }
-  #pragma unroll
-          for (int it = 0; it < 4; ++it) {
-            f32x4 T = mfma_f16(SA[0], Qf[it][0], zero4());
-            T = mfma_f16(SA[1], Qf[it][1], T);
-            Y[it] += (float)Q[(it * 16 + n) * PH + qpos[ai]] * T;
-          }
-        }
-        float* rd = red[sl][wave];
-  #pragma unroll
-        for (int it = 0; it < 4; ++it) *reinterpret_cast<f32x4*>(&rd[(it * 16 + n) * CW + 4 * g]) = Y[it];
-      }
-      // S = e^T S + K^T ((k_:a 2^kap) * X 2^(sig - 2 kap))
-      {
-        const _Float16* KT = KTh[sl];
-        f16x8 Kf[4][2];  // A operand: K^T[b][j], k = j contiguous
-  #pragma unroll
-        for (int bt = 0; bt < 4; ++bt)
-  #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-            Kf[bt][kb] = *reinterpret_cast<const f16x8*>(&KT[(bt * 16 + n) * PH + kb * 32 + 8 * g]);
-        // X 2^xi -> X 2^(sig - 2 kap): exact power-of-two factors (d <= 2 since
-        // max X 2^xi >= 2^13; below 2^-48 the terms are negligible and dropped)
-        const int d = cur.sig - 2 * cur.kap - cur.xi;
-        f16x8 xh[2];
-  #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) xh[kb] = *reinterpret_cast<const f16x8*>(&Xh[sl][n * PH + kb * 32 + 8 * g]);
-        if (d < -48) {
-  #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) xh[kb] = xh[kb] * (_Float16)0.f;
-        } else if (d >= -14) {
-          if (d != 0) {
-            const _Float16 f = (_Float16)ldexpf(1.f, d);
-  #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) xh[kb] = xh[kb] * f;
-          }
-        } else {
-          const int d1 = d / 2, d2 = d - d1;
-          const _Float16 f1 = (_Float16)ldexpf(1.f, d1), f2 = (_Float16)ldexpf(1.f, d2);
-  #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) xh[kb] = (xh[kb] * f1) * f2;
-        }
-  #pragma unroll
-        for (int ai = 0; ai < AW; ++ai) {
-          const int a = a0 + wave * AW + ai;  // the K^T row of k_:a
-          f16x8 Bu[2];
-  #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-            Bu[kb] = *reinterpret_cast<const f16x8*>(&KT[a * PH + kb * 32 + 8 * g]) * xh[kb];
-  #pragma unroll
-          for (int bt = 0; bt < 4; ++bt) {
-            f32x4 acc = cur.eT * S[ai][bt];
-            acc = mfma_f16(Kf[bt][0], Bu[0], acc);
-            acc = mfma_f16(Kf[bt][1], Bu[1], acc);
-            S[ai][bt] = acc;
-          }
-        }
-      }
-    } else {
-      // per a: output with the entering state, T^T[c][i] = sum_b S[b][c] Q[i][b],
-      // Y[i][c] += q_ia T^T[c][i]; then the update
-      // S = e^T S + K^T ((k_:a 2^kap) * X 2^(sig - 2 kap)).  The two chains of
-      // each a are independent, so their MFMA and VALU work interleave.
+    {
       const _Float16* Q = Qh[sl];
+      f16x8 Qf[2][4];  // B operand: Q^T[b][i], i = 32 it + n32
+#pragma unroll
+      for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          Qf[it][kk] = *reinterpret_cast<const f16x8*>(&Q[(it * 32 + n32) * PH + kk * 16 + 8 * h]);
+      typedef _Float16 qv_t __attribute__((ext_vector_type(AW)));
+      qv_t qv[2];
+#pragma unroll
+      for (int it = 0; it < 2; ++it)
+        qv[it] = *reinterpret_cast<const qv_t*>(&Qa[sl][(it * 32 + n32) * QP + wave * AW]);
+      f32x4 Y[2][2];
+#pragma unroll
+      for (int it = 0; it < 2; ++it) Y[it][0] = Y[it][1] = zero4();
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        f16x8 SA[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) SA[kk][e] = (_Float16)S[p][kk >> 1][8 * (kk & 1) + e];
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          f32x16 T = mfma32(SA[0], Qf[it][0], f32x16{});
+#pragma unroll
+          for (int kk = 1; kk < 4; ++kk) T = mfma32(SA[kk], Qf[it][kk], T);
+          const float qa = (float)qv[it][2 * p], qb = (float)qv[it][2 * p + 1];
+#pragma unroll
+          for (int qq = 0; qq < 2; ++qq)
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+              Y[it][qq][s] = fmaf(qb, T[4 * (qq + 2) + s], fmaf(qa, T[4 * qq + s], Y[it][qq][s]));
+        }
+      }
+#pragma unroll
+      for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) red[sl][wave][(it * 2 + qq) * WAVE + lane] = Y[it][qq];
+    }
+    {
       const _Float16* KT = KTh[sl];
-      f16x8 Qf[4][2];  // output B operand: Q^T[b][i], permuted k = b (pre-ordered)
-  #pragma unroll
-      for (int it = 0; it < 4; ++it)
-  #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          Qf[it][kb] = *reinterpret_cast<const f16x8*>(&Q[(it * 16 + n) * PH + kb * 32 + 8 * g]);
-      f16x8 Kf[4][2];  // update A operand: K^T[b][j], k = j contiguous
-  #pragma unroll
-      for (int bt = 0; bt < 4; ++bt)
-  #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          Kf[bt][kb] = *reinterpret_cast<const f16x8*>(&KT[(bt * 16 + n) * PH + kb * 32 + 8 * g]);
-      // X 2^xi -> X 2^(sig - 2 kap): exact power-of-two factors (d <= 2 since
-      // max X 2^xi >= 2^13; below 2^-48 the terms are negligible and dropped)
-      const int d = cur.sig - 2 * cur.kap - cur.xi;
-      f16x8 xh[2];
-  #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) xh[kb] = *reinterpret_cast<const f16x8*>(&Xh[sl][n * PH + kb * 32 + 8 * g]);
-      if (d < -48) {
-  #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) xh[kb] = xh[kb] * (_Float16)0.f;
-      } else if (d >= -14) {
-        if (d != 0) {
-          const _Float16 f = (_Float16)ldexpf(1.f, d);
-  #pragma unroll
-          for (int kb = 0; kb < 2; ++kb) xh[kb] = xh[kb] * f;
-        }
-      } else {
-        const int d1 = d / 2, d2 = d - d1;
-        const _Float16 f1 = (_Float16)ldexpf(1.f, d1), f2 = (_Float16)ldexpf(1.f, d2);
-  #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) xh[kb] = (xh[kb] * f1) * f2;
-      }
-      f32x4 Y[4];
-  #pragma unroll
-      for (int it = 0; it < 4; ++it) Y[it] = zero4();
-  #pragma unroll
-      for (int ai = 0; ai < AW; ++ai) {
-        f16x8 SA[2];
-  #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-  #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            SA[kb][r] = (_Float16)S[ai][2 * kb][r];
-            SA[kb][4 + r] = (_Float16)S[ai][2 * kb + 1][r];
-          }
-        const int a = a0 + wave * AW + ai;  // the K^T row of k_:a
-        f16x8 Bu[2];
-  #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-          Bu[kb] = *reinterpret_cast<const f16x8*>(&KT[a * PH + kb * 32 + 8 * g]) * xh[kb];
-  #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          f32x4 T = mfma_f16(SA[0], Qf[it][0], zero4());
-          T = mfma_f16(SA[1], Qf[it][1], T);
-          const int bt = it;
-          f32x4 acc = cur.eT * S[ai][bt];
-          acc = mfma_f16(Kf[bt][0], Bu[0], acc);
-          acc = mfma_f16(Kf[bt][1], Bu[1], acc);
-          S[ai][bt] = acc;
-          Y[it] += (float)Q[(it * 16 + n) * PH + qpos[ai]] * T;
+      f16x8 Kf[2][4];  // A operand: K^T[b][j], b = 32 bt + n32
+#pragma unroll
+      for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          Kf[bt][kk] = *reinterpret_cast<const f16x8*>(&KT[(bt * 32 + n32) * PH + kk * 16 + 8 * h]);
+      f16x8 xh[4];  // X^T[c][j], c = n32 % 16
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        xh[kk] = *reinterpret_cast<const f16x8*>(&Xh[sl][(n32 & 15) * PH + kk * 16 + 8 * h]);
+      const float eT = cur.eTs;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int a = a0 + wave * AW + 2 * p + (n32 >> 4);  // the K^T row of k_:a
+        f16x8 Bu[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          Bu[kk] = *reinterpret_cast<const f16x8*>(&KT[a * PH + kk * 16 + 8 * h]) * xh[kk];
+#pragma unroll
+        for (int bt = 0; bt < 2; ++bt) {
+          f32x16 acc = eT * S[p][bt];
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) acc = mfma32(Kf[bt][kk], Bu[kk], acc);
+          S[p][bt] = acc;
         }
       }
-      float* rd = red[sl][wave];
-  #pragma unroll
-      for (int it = 0; it < 4; ++it) *reinterpret_cast<f32x4*>(&rd[(it * 16 + n) * CW + 4 * g]) = Y[it];
     }
   };
 
@@ -401,41 +309,53 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
   prefetch(0);
   stage(0);
   cur = nx;
-  if (nblk > 1) prefetch(1);
+  prefetch(nblk > 1 ? 1 : 0);
   __syncthreads();
 
-  // Per block: the first four waves run the MFMA work first, the other four
-  // drain/stage first, so each SIMD (waves w and w+4) overlaps the matrix
-  // work of one wave with the bookkeeping of the other.
+  // Per block n: MFMA work of n, drain of n-1, staging of n+1, loads of n+2,
+  // one barrier.  With two waves per SIMD the first four waves run the MFMA
+  // work first and the other four the bookkeeping first.
   for (int64_t blk = 0; blk < nblk; ++blk) {
-    const bool more = blk + 1 < nblk;
-    if (wave < NW / 2) {
-      compute(blk);
-      if (blk > 0) drain(blk - 1, prv);
-      if (more) stage(blk + 1);
+    const Blk nxt = nx;  // scales of block blk + 1 (prefetched)
+    const int64_t pf = blk + 2 < nblk ? blk + 2 : nblk - 1;
+    if constexpr (STAGGER) {
+      // the loads for block n+2 are issued right after the registers are
+      // free, a whole block ahead of their use
+      if (wave < NW / 2) {
+        compute(blk);
+        if (blk > 0) drain(blk - 1, prv);
+        stage(blk + 1);
+        prefetch(pf);
+      } else {
+        if (blk > 0) drain(blk - 1, prv);
+        stage(blk + 1);
+        prefetch(pf);
+        compute(blk);
+      }
     } else {
-      if (blk > 0) drain(blk - 1, prv);
-      if (more) stage(blk + 1);
       compute(blk);
+      if (blk > 0) drain(blk - 1, prv);
+      stage(blk + 1);
+      prefetch(pf);
     }
-    if (blk + 2 < nblk) prefetch(blk + 2);
     prv = cur;
-    cur = nx;
+    cur = nxt;
     __syncthreads();
   }
   drain(nblk - 1, prv);
 
   if (final_state) {
-    const float f = ldexpf(1.f, -sig_dec);
+    const float f = ldexpf(1.f, -prv.sig_out);
+    const int c = c0 + (n32 & 15);
 #pragma unroll
-    for (int ai = 0; ai < AW; ++ai) {
-      const int a = a0 + wave * AW + ai;
+    for (int p = 0; p < NP; ++p) {
+      const int a = a0 + wave * AW + 2 * p + (n32 >> 4);
 #pragma unroll
-      for (int bt = 0; bt < 4; ++bt)
+      for (int bt = 0; bt < 2; ++bt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int b = bt * 16 + 4 * g + r;
-          final_state[((bh * DH + a) * DH + b) * DH + c0 + n] = S[ai][bt][r] * f;
+        for (int r = 0; r < 16; ++r) {
+          const int b = bt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          final_state[((bh * DH + a) * DH + b) * DH + c] = S[p][bt][r] * f;
         }
     }
   }
@@ -446,14 +366,12 @@ hipError_t launch_o2_state(const void* rec, int64_t BH, int64_t N, float* part,
   const int AW = o2_aw(BH);
   const int PA = o2_pa(BH);
   const int xcd_map = (BH % 8) == 0;
-  const dim3 grid((unsigned)(BH * PA * 4)), blk(8 * WAVE);
   const uint8_t* r = static_cast<const uint8_t*>(rec);
+  const dim3 grid((unsigned)(BH * PA * 4));
   if (AW == 4)
-    hipLaunchKernelGGL((k_o2_state<4>), grid, blk, 0, stream, r, BH, N, xcd_map, part, final_state);
-  else if (AW == 2)
-    hipLaunchKernelGGL((k_o2_state<2>), grid, blk, 0, stream, r, BH, N, xcd_map, part, final_state);
+    hipLaunchKernelGGL((k_o2_state<8, 4>), grid, dim3(8 * WAVE), 0, stream, r, BH, N, xcd_map, part, final_state);
   else
-    hipLaunchKernelGGL((k_o2_state<1>), grid, blk, 0, stream, r, BH, N, xcd_map, part, final_state);
+    hipLaunchKernelGGL((k_o2_state<8, 2>), grid, dim3(8 * WAVE), 0, stream, r, BH, N, xcd_map, part, final_state);
   return hipGetLastError();
 }
 

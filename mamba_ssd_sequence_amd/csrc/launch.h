@@ -10,31 +10,42 @@ namespace ssd {
 // Forward work is organised in blocks of 64 tokens.
 __host__ __device__ inline int64_t n_blocks(int64_t N) { return (N + 63) / 64; }
 
-// Order-2 state kernel: a-rows per wave (AW), and the resulting number of
-// a-slices per head (P_a = 64 / (8 * AW)).  Fewer heads -> thinner slices so
-// that the grid still covers the chip.
-inline int o2_aw(int64_t BH) { return BH >= 32 ? 4 : (BH >= 16 ? 2 : 1); }
-inline int o2_pa(int64_t BH) { return 64 / (8 * o2_aw(BH)); }
+// Order-2 state kernel (8 waves per workgroup): a values per wave (AW, taken
+// in pairs) and per workgroup (SL = 8 AW), and the resulting number of
+// a-slices per head (P_a = 64 / SL).  Fewer heads -> thinner slices so that
+// the grid still covers the chip.
+inline int o2_aw(int64_t BH) { return BH >= 32 ? 4 : 2; }
+inline int o2_sl(int64_t BH) { return 8 * o2_aw(BH); }
+inline int o2_pa(int64_t BH) { return 64 / o2_sl(BH); }
 
 // Order-2 per-block operand record (bytes), written by the block-prep kernel
 // and read by the state scan:
-//   QH  [64 i][64]   fp16 q_ib 2^tau, columns of each 32-block in the order the
-//                    permuted-k MFMA operand reads them
+//   QH  [64 i][64]   fp16 q_ib 2^tau; within each 16-column group the 4-column
+//                    subgroups are stored in the order 0, 2, 1, 3 (the order in
+//                    which the permuted-k 32x32 MFMA operand reads them)
 //   KT  [64 b][64 j] fp16 k_jb 2^kap (transposed)
 //   XT  [64 c][64 j] fp16 X_jc 2^xi, X_jc = w_j dt_j v_jc, w_j = e^{T - cs_j}
 //   ECS [64]         fp32 e^{cs_i} (decay from the block start to token i)
-//   SC               fp32 T, fp32 delta (bound of any |state increment|),
-//                    int32 tau, kap, xi, fp32 e^T
+//   SC  [12 words]   written by the block-prep kernel: fp32 T, fp32 delta
+//                    (bound of any |state increment|), int32 tau, kap, xi,
+//                    fp32 e^T; then by the scale scan: int32 sig_in (scale
+//                    exponent of the state entering the block), fp32 eTs
+//                    (e^T 2^(sig_out - sig_in), the factor that decays and
+//                    rescales the state), two fp16 factors taking X 2^xi to
+//                    X 2^(sig_out - 2 kap), int32 sig_out
 constexpr int REC_QH = 0, REC_KT = 8192, REC_XT = 16384, REC_ECS = 24576, REC_SC = 24832;
-constexpr int REC_BYTES = 24864;
+constexpr int SC_T = 0, SC_DELTA = 1, SC_TAU = 2, SC_KAP = 3, SC_XI = 4, SC_ET = 5, SC_SIG_IN = 6,
+              SC_ETS = 7, SC_XF = 8, SC_SIG_OUT = 9;
+constexpr int REC_BYTES = 24880;
 
 // Workspace layout (float offsets), in this order:
 //   tb     [BH, nblk]                 block decay totals
 //   state  [BH, nblk, DH*DH + DH]     per-block state contributions, then
 //                                     (in place) the state entering each block
 //                                     (order 1: S and z; order 2: Z and unused)
-//   part   [P_a, BH, N, 64]           order 2 only: inter-block numerator
-//                                     partials of each a-slice
+//   part   [P_a, BH, nblk*64, 64]     order 2 only: inter-block numerator
+//                                     partials of each a-slice (rows padded
+//                                     to whole blocks)
 //   rec    [BH, nblk] x REC_BYTES     order 2 only: operand records
 struct WsLayout {
   size_t tb, state, part, rec, total_floats;
@@ -50,7 +61,7 @@ inline WsLayout ws_layout(int64_t B, int64_t H, int64_t N, int64_t DH, int order
   off += (size_t)(BH * nb) * (size_t)(DH * DH + DH);
   off = (off + 63) & ~(size_t)63;
   L.part = off;
-  if (order == 2) off += (size_t)o2_pa(BH) * (size_t)BH * (size_t)N * 64;
+  if (order == 2) off += (size_t)o2_pa(BH) * (size_t)BH * (size_t)(nb * 64) * 64;
   off = (off + 63) & ~(size_t)63;
   L.rec = off;
   if (order == 2) off += (size_t)(BH * nb) * (REC_BYTES / 4);
@@ -84,6 +95,10 @@ hipError_t launch_output(bool bf16, int64_t DH, int order, const void* q, const 
 hipError_t launch_o2_blockprep(const void* q, const void* k, const void* v, const float* dt,
                                const float* a_cs, int64_t BH, int64_t N, int64_t chunk, float* tb,
                                float* state, void* rec, hipStream_t stream);
+
+// Order-2 scale scan: per head, the running bound of the numerator state and
+// the per-block scale exponents of the state scan (record words SC_SIG_IN ..).
+hipError_t launch_o2_scale_scan(void* rec, int64_t BH, int64_t N, hipStream_t stream);
 
 // Order-2 inter-block numerator: on-chip state scan over the block records.
 hipError_t launch_o2_state(const void* rec, int64_t BH, int64_t N, float* part,

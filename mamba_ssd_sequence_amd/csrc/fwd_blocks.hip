@@ -258,26 +258,80 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
     dtv[tid] = d;
   }
   __syncthreads();
-  for (int e = tid; e < BLK * DH; e += 256) {
-    const int j = e / DH, d = e - (e / DH) * DH;
-    float qv = 0.f, kv = 0.f, vv = 0.f;
-    if (j < nvalid) {
-      const int64_t off = (row + t0 + j) * DH + d;
-      qv = Elem<St>::ld(q, off);
-      kv = Elem<St>::ld(k, off);
-      vv = Elem<St>::ld(v, off);
-    }
-    Qs[j * PQ + d] = (C)qv;
-    Ks[j * PQ + d] = (C)kv;
-    VT[d * PJ + j] = (C)(vv * dtv[j]);
-  }
   const float* st = state + (bh * nblk + blk) * (int64_t)(DH * DH + DH);
-  for (int e = tid; e < DH * DH; e += 256) {
-    const int b = e / DH, c = e - (e / DH) * DH;
-    const float x = st[e];
-    const C hi = (C)x;
-    SinT[c * PQ + b] = hi;
-    if constexpr (BF) SinL[c * PQ + b] = (C)(x - (float)hi);
+  if constexpr (BF) {
+    // q and k rows: 16-byte segments copied as they are (bf16 bits)
+    constexpr int SEG = DH / 8;
+    for (int e = tid; e < BLK * SEG; e += 256) {
+      const int j = e / SEG, sg = e % SEG;
+      uint4 qv = make_uint4(0, 0, 0, 0), kv = qv;
+      if (j < nvalid) {
+        const int64_t off = (row + t0 + j) * DH + sg * 8;
+        qv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(qp) + off);
+        kv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(kp) + off);
+      }
+      *reinterpret_cast<uint4*>(&Qs[j * PQ + sg * 8]) = qv;
+      *reinterpret_cast<uint4*>(&Ks[j * PQ + sg * 8]) = kv;
+    }
+    // value operand v dt, transposed: two consecutive tokens per thread so
+    // that each LDS store carries a pair of tokens
+    for (int e = tid; e < (BLK / 2) * SEG; e += 256) {
+      const int jp = e / SEG, sg = e % SEG, j0 = 2 * jp;
+      uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
+      const int64_t off = (row + t0 + j0) * DH + sg * 8;
+      if (j0 < nvalid) v0 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(vp) + off);
+      if (j0 + 1 < nvalid) v1 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(vp) + off + DH);
+      const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w}, w1[4] = {v1.x, v1.y, v1.z, v1.w};
+      const float d0 = dtv[j0], d1 = dtv[j0 + 1];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const float a0 = __uint_as_float(hh ? (w0[u] & 0xffff0000u) : (w0[u] << 16)) * d0;
+          const float a1 = __uint_as_float(hh ? (w1[u] & 0xffff0000u) : (w1[u] << 16)) * d1;
+          C pr[2] = {(C)a0, (C)a1};
+          *reinterpret_cast<uint32_t*>(&VT[(sg * 8 + 2 * u + hh) * PJ + j0]) = __builtin_bit_cast(uint32_t, pr);
+        }
+      }
+    }
+  } else {
+    for (int e = tid; e < BLK * DH; e += 256) {
+      const int j = e / DH, d = e - (e / DH) * DH;
+      float qv = 0.f, kv = 0.f, vv = 0.f;
+      if (j < nvalid) {
+        const int64_t off = (row + t0 + j) * DH + d;
+        qv = Elem<St>::ld(q, off);
+        kv = Elem<St>::ld(k, off);
+        vv = Elem<St>::ld(v, off);
+      }
+      Qs[j * PQ + d] = (C)qv;
+      Ks[j * PQ + d] = (C)kv;
+      VT[d * PJ + j] = (C)(vv * dtv[j]);
+    }
+  }
+  if constexpr (ORDER == 2) {
+    // the normaliser state Z = sum_j w_j k_j k_j^T is symmetric, so its rows
+    // serve as the transposed operand: float4 loads, high + low bf16 parts
+    for (int e = tid; e < DH * DH / 4; e += 256) {
+      const int c = e / (DH / 4), b4 = (e % (DH / 4)) * 4;
+      const f32x4 x = *reinterpret_cast<const f32x4*>(&st[c * DH + b4]);
+      C hi[4], lo[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        hi[r] = (C)x[r];
+        lo[r] = (C)(x[r] - (float)hi[r]);
+      }
+      *reinterpret_cast<uint2*>(&SinT[c * PQ + b4]) = __builtin_bit_cast(uint2, hi);
+      if constexpr (BF) *reinterpret_cast<uint2*>(&SinL[c * PQ + b4]) = __builtin_bit_cast(uint2, lo);
+    }
+  } else {
+    for (int e = tid; e < DH * DH; e += 256) {
+      const int b = e / DH, c = e - (e / DH) * DH;
+      const float x = st[e];
+      const C hi = (C)x;
+      SinT[c * PQ + b] = hi;
+      if constexpr (BF) SinL[c * PQ + b] = (C)(x - (float)hi);
+    }
   }
   if (ORDER == 1 && tid < DH) zin[tid] = st[DH * DH + tid];
   __syncthreads();

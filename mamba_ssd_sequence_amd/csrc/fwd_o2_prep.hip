@@ -95,49 +95,66 @@ __global__ __launch_bounds__(256) void k_o2_blockprep(const uint16_t* __restrict
   if (tid == 0) tb[bh * nblk + blk] = T;
   __syncthreads();
 
-  // pass 1: q, k, v segments (8 values each) -> maxima, Z operands, v^T
+  // pass 1: q, k, v segments (8 values each, two consecutive tokens per
+  // thread) -> maxima, Z operands and v^T; each transposing LDS store carries
+  // the pair of tokens
   float qm = 0.f, km = 0.f;
   uint4 qs[2];
+  {
+    const int jp = tid >> 3, seg = tid & 7, j0 = 2 * jp;
+    uint4 qv[2], kv[2], vv[2];
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int s = tid + u * 256, j = s >> 3, seg = s & 7;
-    uint4 qv = make_uint4(0, 0, 0, 0), kv = qv, vv = qv;
-    if (j < nv) {
-      const int64_t off = (row + t0 + j) * DH + seg * 8;
-      qv = *reinterpret_cast<const uint4*>(q + off);
-      kv = *reinterpret_cast<const uint4*>(k + off);
-      vv = *reinterpret_cast<const uint4*>(v + off);
+    for (int u = 0; u < 2; ++u) {
+      qv[u] = kv[u] = vv[u] = make_uint4(0, 0, 0, 0);
+      if (j0 + u < nv) {
+        const int64_t off = (row + t0 + j0 + u) * DH + seg * 8;
+        qv[u] = *reinterpret_cast<const uint4*>(q + off);
+        kv[u] = *reinterpret_cast<const uint4*>(k + off);
+        vv[u] = *reinterpret_cast<const uint4*>(v + off);
+      }
+      qs[u] = qv[u];
     }
-    qs[u] = qv;
-    const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w}, kw[4] = {kv.x, kv.y, kv.z, kv.w},
-                   vw[4] = {vv.x, vv.y, vv.z, vv.w};
-    const float w = wv[j];
-    float vm = 0.f;
+    const float w0 = wv[j0], w1 = wv[j0 + 1];
+    float vm0 = 0.f, vm1 = 0.f;
+    const uint32_t qw0[4] = {qv[0].x, qv[0].y, qv[0].z, qv[0].w}, qw1[4] = {qv[1].x, qv[1].y, qv[1].z, qv[1].w};
+    const uint32_t kw0[4] = {kv[0].x, kv[0].y, kv[0].z, kv[0].w}, kw1[4] = {kv[1].x, kv[1].y, kv[1].z, kv[1].w};
+    const uint32_t vw0[4] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w}, vw1[4] = {vv[1].x, vv[1].y, vv[1].z, vv[1].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float q0 = lo16(qw[i]), q1 = hi16(qw[i]);
-      const float k0 = lo16(kw[i]), k1 = hi16(kw[i]);
-      const float v0 = lo16(vw[i]), v1 = hi16(vw[i]);
-      qm = fmaxf(qm, fmaxf(fabsf(q0), fabsf(q1)));
-      km = fmaxf(km, fmaxf(fabsf(k0), fabsf(k1)));
-      vm = fmaxf(vm, fmaxf(fabsf(v0), fabsf(v1)));
-      const int d0 = seg * 8 + 2 * i;
-      const float wk0 = w * k0, wk1 = w * k1;
-      const __bf16 h0 = (__bf16)wk0, h1 = (__bf16)wk1;
-      wKT[d0 * P + j] = h0;
-      wKT[(d0 + 1) * P + j] = h1;
-      wKL[d0 * P + j] = (__bf16)(wk0 - (float)h0);
-      wKL[(d0 + 1) * P + j] = (__bf16)(wk1 - (float)h1);
-      KTb[d0 * P + j] = __builtin_bit_cast(__bf16, (uint16_t)(kw[i] & 0xffffu));
-      KTb[(d0 + 1) * P + j] = __builtin_bit_cast(__bf16, (uint16_t)(kw[i] >> 16));
-      VTb[d0 * P + j] = __builtin_bit_cast(__bf16, (uint16_t)(vw[i] & 0xffffu));
-      VTb[(d0 + 1) * P + j] = __builtin_bit_cast(__bf16, (uint16_t)(vw[i] >> 16));
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int d = seg * 8 + 2 * i + hh;
+        const uint32_t kb0 = hh ? (kw0[i] >> 16) : (kw0[i] & 0xffffu);
+        const uint32_t kb1 = hh ? (kw1[i] >> 16) : (kw1[i] & 0xffffu);
+        const uint32_t vb0 = hh ? (vw0[i] >> 16) : (vw0[i] & 0xffffu);
+        const uint32_t vb1 = hh ? (vw1[i] >> 16) : (vw1[i] & 0xffffu);
+        const float q0 = hh ? hi16(qw0[i]) : lo16(qw0[i]), q1 = hh ? hi16(qw1[i]) : lo16(qw1[i]);
+        const float k0 = __uint_as_float(kb0 << 16), k1 = __uint_as_float(kb1 << 16);
+        const float v0 = __uint_as_float(vb0 << 16), v1 = __uint_as_float(vb1 << 16);
+        qm = fmaxf(qm, fmaxf(fabsf(q0), fabsf(q1)));
+        km = fmaxf(km, fmaxf(fabsf(k0), fabsf(k1)));
+        vm0 = fmaxf(vm0, fabsf(v0));
+        vm1 = fmaxf(vm1, fabsf(v1));
+        const float wk0 = w0 * k0, wk1 = w1 * k1;
+        const __bf16 h0 = (__bf16)wk0, h1 = (__bf16)wk1;
+        const __bf16 pw[2] = {h0, h1};
+        const __bf16 pl[2] = {(__bf16)(wk0 - (float)h0), (__bf16)(wk1 - (float)h1)};
+        *reinterpret_cast<uint32_t*>(&wKT[d * P + j0]) = __builtin_bit_cast(uint32_t, pw);
+        *reinterpret_cast<uint32_t*>(&wKL[d * P + j0]) = __builtin_bit_cast(uint32_t, pl);
+        *reinterpret_cast<uint32_t*>(&KTb[d * P + j0]) = kb0 | (kb1 << 16);
+        *reinterpret_cast<uint32_t*>(&VTb[d * P + j0]) = vb0 | (vb1 << 16);
+      }
     }
-    // the 8 consecutive lanes of a row: max |v_jc| over the row
-    vm = fmaxf(vm, __shfl_xor(vm, 1, WAVE));
-    vm = fmaxf(vm, __shfl_xor(vm, 2, WAVE));
-    vm = fmaxf(vm, __shfl_xor(vm, 4, WAVE));
-    if (seg == 0) vrow[j] = vm;
+    // the 8 consecutive lanes of a token pair: max |v_jc| over each row
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+      vm0 = fmaxf(vm0, __shfl_xor(vm0, off, WAVE));
+      vm1 = fmaxf(vm1, __shfl_xor(vm1, off, WAVE));
+    }
+    if (seg == 0) {
+      vrow[j0] = vm0;
+      vrow[j0 + 1] = vm1;
+    }
   }
   qm = wmax(qm);
   km = wmax(km);
@@ -199,7 +216,7 @@ __global__ __launch_bounds__(256) void k_o2_blockprep(const uint16_t* __restrict
   // q rows: in each 16-column group the 4-column subgroups go to slots 0, 2, 1, 3
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int s = tid + u * 256, j = s >> 3, seg = s & 7;
+    const int j = 2 * (tid >> 3) + u, seg = tid & 7;
     const uint32_t qw[4] = {qs[u].x, qs[u].y, qs[u].z, qs[u].w};
     h16x4 h0, h1;
     h0[0] = (_Float16)(lo16(qw[0]) * sq);
@@ -220,10 +237,12 @@ __global__ __launch_bounds__(256) void k_o2_blockprep(const uint16_t* __restrict
   for (int u = 0; u < 2; ++u) {
     const int s = tid + u * 256, r = s >> 3, j0 = (s & 7) * 8;
     h16x8 hk, hx;
+    const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&KTb[r * P + j0]);
+    const bf16x8 vr = *reinterpret_cast<const bf16x8*>(&VTb[r * P + j0]);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      hk[i] = (_Float16)((float)KTb[r * P + j0 + i] * sk);
-      hx[i] = (_Float16)((float)VTb[r * P + j0 + i] * wdt[j0 + i] * sx);
+      hk[i] = (_Float16)((float)kr[i] * sk);
+      hx[i] = (_Float16)((float)vr[i] * wdt[j0 + i] * sx);
     }
     *reinterpret_cast<h16x8*>(reinterpret_cast<_Float16*>(R + REC_KT) + r * DH + j0) = hk;
     *reinterpret_cast<h16x8*>(reinterpret_cast<_Float16*>(R + REC_XT) + r * DH + j0) = hx;
@@ -268,13 +287,23 @@ __global__ __launch_bounds__(64) void k_o2_scale_scan(uint8_t* __restrict__ rec,
   const int64_t seg = (nblk + WAVE - 1) / WAVE;
   const int64_t b0 = lane * seg, b1 = (b0 + seg < nblk) ? b0 + seg : nblk;
   uint8_t* base = rec + bh * nblk * (int64_t)REC_BYTES + REC_SC;
-  // run of this lane as a map M -> A M + B
+  // run of this lane as a map M -> A M + B (loads issued 8 blocks at a time)
   float A = 1.f, B = 0.f;
-  for (int64_t b = b0; b < b1; ++b) {
-    const float* sc = reinterpret_cast<const float*>(base + b * (int64_t)REC_BYTES);
-    const float e = sc[SC_ET];
-    A *= e;
-    B = e * B + sc[SC_DELTA];
+  for (int64_t c0 = b0; c0 < b1; c0 += 8) {
+    float e[8], dl[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float* sc = reinterpret_cast<const float*>(base + (c0 + u < b1 ? c0 + u : b0) * (int64_t)REC_BYTES);
+      e[u] = sc[SC_ET];
+      dl[u] = sc[SC_DELTA];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (c0 + u < b1) {
+        A *= e[u];
+        B = e[u] * B + dl[u];
+      }
+    }
   }
   // inclusive scan of the maps over lanes: (A1, B1) then (A2, B2) = (A1 A2, A2 B1 + B2)
 #pragma unroll
@@ -287,25 +316,39 @@ __global__ __launch_bounds__(64) void k_o2_scale_scan(uint8_t* __restrict__ rec,
   }
   float M = __shfl_up(B, 1, WAVE);  // bound after the previous lane's run (M_{-1} = 0)
   if (lane == 0) M = 0.f;
-  for (int64_t b = b0; b < b1; ++b) {
-    uint8_t* p = base + b * (int64_t)REC_BYTES;
-    float* sc = reinterpret_cast<float*>(p);
-    int* si = reinterpret_cast<int*>(p);
-    const float e = sc[SC_ET];
-    const float Mn = e * M + sc[SC_DELTA];
-    const int sin = sig_of(M), sout = sig_of(Mn);
-    si[SC_SIG_IN] = sin;
-    si[SC_SIG_OUT] = sout;
-    sc[SC_ETS] = M > 0.f ? ldexpf(e, sout - sin) : 0.f;
-    // X 2^xi -> X 2^(sig - 2 kap): exact power-of-two factors (d <= 2 since
-    // max X 2^xi >= 2^13; below 2^-48 the terms are negligible and dropped)
-    const int d = sout - 2 * si[SC_KAP] - si[SC_XI];
-    const int d1 = d >= -14 ? d : d / 2, d2 = d >= -14 ? 0 : d - d / 2;
-    h16x2 xf;
-    xf[0] = d < -48 ? (_Float16)0.f : (_Float16)ldexpf(1.f, d1);
-    xf[1] = (_Float16)ldexpf(1.f, d2);
-    *reinterpret_cast<h16x2*>(&sc[SC_XF]) = xf;
-    M = Mn;
+  for (int64_t c0 = b0; c0 < b1; c0 += 8) {
+    float e[8], dl[8];
+    int kx[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int* si = reinterpret_cast<const int*>(base + (c0 + u < b1 ? c0 + u : b0) * (int64_t)REC_BYTES);
+      e[u] = __int_as_float(si[SC_ET]);
+      dl[u] = __int_as_float(si[SC_DELTA]);
+      kx[u] = 2 * si[SC_KAP] + si[SC_XI];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (c0 + u < b1) {
+        uint8_t* p = base + (c0 + u) * (int64_t)REC_BYTES;
+        float* sc = reinterpret_cast<float*>(p);
+        int* si = reinterpret_cast<int*>(p);
+        const float Mn = e[u] * M + dl[u];
+        const int sin = sig_of(M), sout = sig_of(Mn);
+        si[SC_SIG_IN] = sin;
+        si[SC_SIG_OUT] = sout;
+        sc[SC_ETS] = M > 0.f ? ldexpf(e[u], sout - sin) : 0.f;
+        // X 2^xi -> X 2^(sig - 2 kap): exact power-of-two factors (d <= 2
+        // since max X 2^xi >= 2^13; below 2^-48 the terms are negligible and
+        // dropped)
+        const int d = sout - kx[u];
+        const int d1 = d >= -14 ? d : d / 2, d2 = d >= -14 ? 0 : d - d / 2;
+        h16x2 xf;
+        xf[0] = d < -48 ? (_Float16)0.f : (_Float16)ldexpf(1.f, d1);
+        xf[1] = (_Float16)ldexpf(1.f, d2);
+        *reinterpret_cast<h16x2*>(&sc[SC_XF]) = xf;
+        M = Mn;
+      }
+    }
   }
 }
 

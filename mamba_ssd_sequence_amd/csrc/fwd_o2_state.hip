@@ -55,6 +55,10 @@
 #include "common.h"
 #include "launch.h"
 
+#ifndef O2_SCHED
+#define O2_SCHED 0
+#endif
+
 namespace ssd {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -303,6 +307,35 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
         }
       }
     }
+#if O2_SCHED
+    if constexpr (NP == 2) {
+      // output: operand reads, first fp16 state operand; the second pair's
+      // conversion under the first pair's MFMAs, the first pair's q scaling
+      // under the second pair's; the update's operand reads under the second
+      // pair's q scaling; the second pair's update operands under the first
+      // pair's update MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
+      for (int m = 0; m < 8; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+      }
+      for (int m = 0; m < 8; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
+      __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 48, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      for (int m = 0; m < 8; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
+#endif
   };
 
   // prologue: stage block 0, prefetch block 1

@@ -107,7 +107,9 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
   __shared__ float st_ecs[3][BLK];
 
   const int tid = threadIdx.x;
-  const int wave = tid / WAVE, lane = tid & (WAVE - 1), n32 = lane & 31, h = lane >> 5;
+  // the wave index, provably uniform across the wave (scalar branches)
+  const int wave = __builtin_amdgcn_readfirstlane(tid / WAVE);
+  const int lane = tid & (WAVE - 1), n32 = lane & 31, h = lane >> 5;
   int pc, pa;
   int64_t bh;
   if (xcd_map) {
@@ -347,33 +349,33 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
 
   // Per block n: MFMA work of n, drain of n-1, staging of n+1, loads of n+2,
   // one barrier.  With two waves per SIMD the first four waves run the MFMA
-  // work first and the other four the bookkeeping first.
-  for (int64_t blk = 0; blk < nblk; ++blk) {
-    const Blk nxt = nx;  // scales of block blk + 1 (prefetched)
-    const int64_t pf = blk + 2 < nblk ? blk + 2 : nblk - 1;
-    if constexpr (STAGGER) {
-      // the loads for block n+2 are issued right after the registers are
-      // free, a whole block ahead of their use
-      if (wave < NW / 2) {
-        compute(blk);
-        if (blk > 0) drain(blk - 1, prv);
-        stage(blk + 1);
-        prefetch(pf);
-      } else {
-        if (blk > 0) drain(blk - 1, prv);
-        stage(blk + 1);
-        prefetch(pf);
-        compute(blk);
-      }
-    } else {
+  // work first and the other four the bookkeeping first; each group has a
+  // loop of its own (every wave passes the same barriers), so the loads of a
+  // block have a single destination and are waited for only where the staging
+  // consumes them.  The loads for block n+2 are issued right after the
+  // registers are free, a whole block ahead of their use.
+  if (!STAGGER || wave < NW / 2) {
+    for (int64_t blk = 0; blk < nblk; ++blk) {
+      const Blk nxt = nx;  // scales of block blk + 1 (prefetched)
       compute(blk);
       if (blk > 0) drain(blk - 1, prv);
       stage(blk + 1);
-      prefetch(pf);
+      prefetch(blk + 2 < nblk ? blk + 2 : nblk - 1);
+      prv = cur;
+      cur = nxt;
+      __syncthreads();
     }
-    prv = cur;
-    cur = nxt;
-    __syncthreads();
+  } else {
+    for (int64_t blk = 0; blk < nblk; ++blk) {
+      const Blk nxt = nx;
+      if (blk > 0) drain(blk - 1, prv);
+      stage(blk + 1);
+      prefetch(blk + 2 < nblk ? blk + 2 : nblk - 1);
+      compute(blk);
+      prv = cur;
+      cur = nxt;
+      __syncthreads();
+    }
   }
   drain(nblk - 1, prv);
 

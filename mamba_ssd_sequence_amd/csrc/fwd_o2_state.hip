@@ -14,18 +14,20 @@
 // so phi(q), phi(k) are never formed, only the per-row scalings.
 //
 // Decomposition.  The 1 MiB state never leaves the chip: each workgroup owns
-// an a-slice (8*AW values of a) x a 16-column value slice, held as MFMA
+// an a-slice (SL values of a) x a 16-column value slice, held as MFMA
 // accumulators (fp32) across the whole sequence, and walks the blocks in
-// order.  Wave w owns AW values of a, taken in pairs: one 32x32 accumulator
-// tile covers 32 values of b x (2 values of a x 16 columns), so the state of
-// a pair is two tiles (32 VGPRs/lane).  On gfx950 the 32x32x16 MFMA (32
+// order.  Its 8 waves are 4 a groups x 2 halves of the 16 columns: wave w
+// owns AW values of a (in quads) and 8 columns, and one 32x32 accumulator
+// tile covers 32 values of b x (4 values of a x 8 columns), so the state of
+// a quad is two tiles (32 VGPRs/lane).  On gfx950 the 32x32x16 MFMA (32
 // cycles) absorbs the per-element VALU work of this scan (decay, fp16
 // conversion, row scalings) with little loss, and its operand fragments
 // (32 rows x 16 bytes at a 144-byte pitch) read LDS without bank conflicts.
 // The A operand of the output product is the state itself (its accumulator
 // layout read as a permuted-k operand), the A operand of the update is K^T.
-// The workgroup's partial output (its a-slice) is reduced over its waves in
-// LDS and written to the workspace; the output kernel adds the P_a partials.
+// The workgroup's partial output (its a-slice) is reduced over the 4 waves of
+// each column half in LDS and written to the workspace; the output kernel
+// adds the P_a partials.
 //
 // Precision.  Both products run on v_mfma_f32_32x32x16_f16 (same rate as
 // bf16) with exact power-of-two scales: q*2^tau < 2^13 and k*2^kap in (-1, 1)
@@ -50,7 +52,7 @@
 // The per-block operands arrive pre-converted from the block-prep kernel, so
 // staging is plain copies.
 //
-// Grid: B*H x P_a x 4 workgroups (P_a = 64 / (8*AW)), 512 threads each; when
+// Grid: B*H x P_a x 4 workgroups (P_a = 64 / (4*AW)), 512 threads each; when
 // B*H is a multiple of 8 the workgroups of one head share an XCD (and its L2).
 #include "common.h"
 #include "launch.h"
@@ -63,6 +65,7 @@ namespace ssd {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 constexpr int DH = 64;
@@ -86,15 +89,16 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
                                                       float* __restrict__ part,
                                                       float* __restrict__ final_state) {
   constexpr int NT = NW * WAVE;       // threads
-  constexpr int SL = NW * AW;         // a values per workgroup
+  constexpr int NAG = NW / 2;         // a groups (each wave: one a group x one half of the columns)
+  constexpr int SL = NAG * AW;        // a values per workgroup
   constexpr int PA = DH / SL;         // a-slices per head
-  constexpr int NP = AW / 2;          // a pairs per wave
+  constexpr int NQD = AW / 4;         // a quads per wave
   constexpr int QP = SL + 4;          // row pitch of the q copy (elements)
   constexpr int NI = BLK * DH / 8 / NT;   // 16-byte q / k^T segments per thread
   constexpr int NX = CW * DH / 2 / NT;    // 32-bit X^T words per thread
   constexpr int NQ = (BLK * SL / 4 + NT - 1) / NT;  // 4-value q groups per thread
   constexpr bool STAGGER = NW == 8;   // two waves per SIMD
-  static_assert(AW % 2 == 0 && NI >= 1 && NX >= 1, "thread mapping");
+  static_assert(AW % 4 == 0 && NI >= 1 && NX >= 1, "thread mapping");
 
   // staging (by block parity) and partial-output buffers; e^{cs} rows rotate
   // over three slots because the drain of block n-1 may still read them while
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
   __shared__ __attribute__((aligned(16))) _Float16 KTh[2][DH * PH];  // [b][j] k 2^kap
   __shared__ __attribute__((aligned(16))) _Float16 Xh[2][CW * PH];   // [c][j] X 2^(sig - 2 kap)
   __shared__ __attribute__((aligned(16))) _Float16 Qa[2][BLK * QP];  // [i][a - a0] q 2^tau
-  __shared__ f32x4 red[2][NW][4 * WAVE];  // per wave, in accumulator order
+  __shared__ f32x4 red[2][NW][2 * WAVE];  // per wave, in accumulator order
   __shared__ float st_ecs[3][BLK];
 
   const int tid = threadIdx.x;
@@ -127,6 +131,11 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
   }
   const int a0 = pa * SL;
   const int c0 = pc * CW;
+  // this wave: a values a0 + ag AW .. + AW - 1 (in quads), value columns
+  // c0 + 8 ch .. + 7; lane n32 of a 32x32 tile column holds a quad member
+  // n32 / 8 and column n32 % 8
+  const int ag = wave % NAG, ch = wave / NAG;
+  const int aw0 = a0 + ag * AW;
   const int64_t nblk = n_blocks(N);
   const int64_t Np = nblk * BLK;  // partial rows per head (padded)
   const uint8_t* rec_h = rec + bh * nblk * (int64_t)REC_BYTES;
@@ -209,34 +218,35 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
     if (NT == BLK * CW / 4 || tid < BLK * CW / 4) {
       const int64_t t0 = blk * BLK;
       const int i = tid >> 2, c4 = (tid & 3) * 4;
-      // element (i, c4..c4+3) sits in accumulator slot (i/32, c4/8) of lane
-      // i%32 + 32 ((c4/4) & 1)
-      const int idx = ((i >> 5) * 2 + (c4 >> 3)) * WAVE + (i & 31) + 32 * ((c4 >> 2) & 1);
-      f32x4 s = red[blk & 1][0][idx];
+      // element (i, c4..c4+3) sits in accumulator slot i/32 of lane
+      // i%32 + 32 ((c4/4) & 1) of the waves of column half c4/8
+      const int idx = (i >> 5) * WAVE + (i & 31) + 32 * ((c4 >> 2) & 1);
+      const int wh = (c4 >> 3) * NAG;
+      f32x4 s = red[blk & 1][wh][idx];
 #pragma unroll
-      for (int w = 1; w < NW; ++w) s += red[blk & 1][w][idx];
+      for (int w = 1; w < NAG; ++w) s += red[blk & 1][wh + w][idx];
       const float f = st_ecs[blk % 3][i] * ldexpf(ldexpf(1.f, -p.sig_in), -2 * p.tau);
       *reinterpret_cast<f32x4*>(&part[(((int64_t)pa * BH + bh) * Np + t0 + i) * DH + c0 + c4]) = s * f;
     }
   };
 
-  // state: pair p, b-tile bt (32 rows) -> 32 x 32 accumulator over
-  // (b) x (a = a_p + n32/16, c = c0 + n32%16); lane (n32, h) holds the rows
-  // b = 32 bt + 8 q + 4 h + s in register 4 q + s
-  f32x16 S[NP][2];
+  // state: quad qd, b-tile bt (32 rows) -> 32 x 32 accumulator over
+  // (b) x (a = aw0 + 4 qd + n32/8, c = c0 + 8 ch + n32%8); lane (n32, h)
+  // holds the rows b = 32 bt + 8 q + 4 h + s in register 4 q + s
+  f32x16 S[NQD][2];
 #pragma unroll
-  for (int p = 0; p < NP; ++p)
+  for (int p = 0; p < NQD; ++p)
 #pragma unroll
     for (int bt = 0; bt < 2; ++bt) S[p][bt] = f32x16{};
 
   // MFMA work of block blk: the output product with the entering state for
-  // every pair, then the update.  Output: T^T[(a, c)][i] = sum_b S[b][(a, c)]
+  // every quad, then the update.  Output: T^T[(a, c)][i] = sum_b S[b][(a, c)]
   // Q[i][b] over 16-row k-steps kk (b in 16 kk + {4h..4h+3, 8+4h..8+4h+3} on
   // lane half h, matching the record's q column order), then
-  // Y[i][c] += q_ia T^T[(a, c)][i].  Update: S = e^T S + K^T ((k_:a 2^kap) *
-  // X 2^(sig - 2 kap)) over 16-token k-steps (tokens 16 kk + 8 h .. +7 on
-  // lane half h).  The two passes keep the Q and K^T operand fragments from
-  // being live together (register file).
+  // Y[i][c] += sum_a q_ia T^T[(a, c)][i].  Update: S = eTs S + K^T ((k_:a
+  // 2^kap) * X 2^(sig - 2 kap)) over 16-token k-steps (tokens 16 kk + 8 h ..
+  // +7 on lane half h).  The two passes keep the Q and K^T operand fragments
+  // from being live together (register file).
   auto compute = [&](int64_t blk) {
     const int sl = (int)(blk & 1);
     {
@@ -247,38 +257,33 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           Qf[it][kk] = *reinterpret_cast<const f16x8*>(&Q[(it * 32 + n32) * PH + kk * 16 + 8 * h]);
-      typedef _Float16 qv_t __attribute__((ext_vector_type(AW)));
-      qv_t qv[2];
+      f32x4 Y[2];
 #pragma unroll
-      for (int it = 0; it < 2; ++it)
-        qv[it] = *reinterpret_cast<const qv_t*>(&Qa[sl][(it * 32 + n32) * QP + wave * AW]);
-      f32x4 Y[2][2];
+      for (int it = 0; it < 2; ++it) Y[it] = zero4();
 #pragma unroll
-      for (int it = 0; it < 2; ++it) Y[it][0] = Y[it][1] = zero4();
-#pragma unroll
-      for (int p = 0; p < NP; ++p) {
+      for (int qd = 0; qd < NQD; ++qd) {
         f16x8 SA[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) SA[kk][e] = (_Float16)S[p][kk >> 1][8 * (kk & 1) + e];
+          for (int e = 0; e < 8; ++e) SA[kk][e] = (_Float16)S[qd][kk >> 1][8 * (kk & 1) + e];
 #pragma unroll
         for (int it = 0; it < 2; ++it) {
           f32x16 T = mfma32(SA[0], Qf[it][0], f32x16{});
 #pragma unroll
           for (int kk = 1; kk < 4; ++kk) T = mfma32(SA[kk], Qf[it][kk], T);
-          const float qa = (float)qv[it][2 * p], qb = (float)qv[it][2 * p + 1];
+          // rows 8 q + 4 h + s of T: quad member q, column 4 h + s
+          const f16x4 qv = *reinterpret_cast<const f16x4*>(&Qa[sl][(it * 32 + n32) * QP + ag * AW + 4 * qd]);
 #pragma unroll
-          for (int qq = 0; qq < 2; ++qq)
+          for (int q = 0; q < 4; ++q) {
+            const float qa = (float)qv[q];
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-              Y[it][qq][s] = fmaf(qb, T[4 * (qq + 2) + s], fmaf(qa, T[4 * qq + s], Y[it][qq][s]));
+            for (int s = 0; s < 4; ++s) Y[it][s] = fmaf(qa, T[4 * q + s], Y[it][s]);
+          }
         }
       }
 #pragma unroll
-      for (int it = 0; it < 2; ++it)
-#pragma unroll
-        for (int qq = 0; qq < 2; ++qq) red[sl][wave][(it * 2 + qq) * WAVE + lane] = Y[it][qq];
+      for (int it = 0; it < 2; ++it) red[sl][wave][it * WAVE + lane] = Y[it];
     }
     {
       const _Float16* KT = KTh[sl];
@@ -288,56 +293,27 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           Kf[bt][kk] = *reinterpret_cast<const f16x8*>(&KT[(bt * 32 + n32) * PH + kk * 16 + 8 * h]);
-      f16x8 xh[4];  // X^T[c][j], c = n32 % 16
+      f16x8 xh[4];  // X^T[c][j], c = 8 ch + n32 % 8
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        xh[kk] = *reinterpret_cast<const f16x8*>(&Xh[sl][(n32 & 15) * PH + kk * 16 + 8 * h]);
+        xh[kk] = *reinterpret_cast<const f16x8*>(&Xh[sl][(8 * ch + (n32 & 7)) * PH + kk * 16 + 8 * h]);
       const float eT = cur.eTs;
 #pragma unroll
-      for (int p = 0; p < NP; ++p) {
-        const int a = a0 + wave * AW + 2 * p + (n32 >> 4);  // the K^T row of k_:a
+      for (int qd = 0; qd < NQD; ++qd) {
+        const int a = aw0 + 4 * qd + (n32 >> 3);  // the K^T row of k_:a
         f16x8 Bu[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           Bu[kk] = *reinterpret_cast<const f16x8*>(&KT[a * PH + kk * 16 + 8 * h]) * xh[kk];
 #pragma unroll
         for (int bt = 0; bt < 2; ++bt) {
-          f32x16 acc = eT * S[p][bt];
+          f32x16 acc = eT * S[qd][bt];
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) acc = mfma32(Kf[bt][kk], Bu[kk], acc);
-          S[p][bt] = acc;
+          S[qd][bt] = acc;
         }
       }
     }
-#if O2_SCHED
-    if constexpr (NP == 2) {
-      // output: operand reads, first fp16 state operand; the second pair's
-      // conversion under the first pair's MFMAs, the first pair's q scaling
-      // under the second pair's; the update's operand reads under the second
-      // pair's q scaling; the second pair's update operands under the first
-      // pair's update MFMAs
-      __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 16, 0);
-      for (int m = 0; m < 8; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
-      }
-      for (int m = 0; m < 8; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 32, 0);
-      __builtin_amdgcn_sched_group_barrier(0x200, 4, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 48, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      for (int m = 0; m < 8; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x002, 6, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
-    }
-#endif
   };
 
   // prologue: stage block 0, prefetch block 1
@@ -381,16 +357,16 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
 
   if (final_state) {
     const float f = ldexpf(1.f, -prv.sig_out);
-    const int c = c0 + (n32 & 15);
+    const int c = c0 + 8 * ch + (n32 & 7);
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-      const int a = a0 + wave * AW + 2 * p + (n32 >> 4);
+    for (int qd = 0; qd < NQD; ++qd) {
+      const int a = aw0 + 4 * qd + (n32 >> 3);
 #pragma unroll
       for (int bt = 0; bt < 2; ++bt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int b = bt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          final_state[((bh * DH + a) * DH + b) * DH + c] = S[p][bt][r] * f;
+          final_state[((bh * DH + a) * DH + b) * DH + c] = S[qd][bt][r] * f;
         }
     }
   }
@@ -403,10 +379,10 @@ hipError_t launch_o2_state(const void* rec, int64_t BH, int64_t N, float* part,
   const int xcd_map = (BH % 8) == 0;
   const uint8_t* r = static_cast<const uint8_t*>(rec);
   const dim3 grid((unsigned)(BH * PA * 4));
-  if (AW == 4)
-    hipLaunchKernelGGL((k_o2_state<8, 4>), grid, dim3(8 * WAVE), 0, stream, r, BH, N, xcd_map, part, final_state);
+  if (AW == 8)
+    hipLaunchKernelGGL((k_o2_state<8, 8>), grid, dim3(8 * WAVE), 0, stream, r, BH, N, xcd_map, part, final_state);
   else
-    hipLaunchKernelGGL((k_o2_state<8, 2>), grid, dim3(8 * WAVE), 0, stream, r, BH, N, xcd_map, part, final_state);
+    hipLaunchKernelGGL((k_o2_state<8, 4>), grid, dim3(8 * WAVE), 0, stream, r, BH, N, xcd_map, part, final_state);
   return hipGetLastError();
 }
 

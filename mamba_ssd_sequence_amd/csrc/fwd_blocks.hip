@@ -171,15 +171,18 @@ __global__ __launch_bounds__(256) void k_state_pass(int64_t nblk, int eblocks,
   const float* t = tb + bh * nblk;
   float s = 0.f;
   int64_t b = 0;
-  for (; b + 8 <= nblk; b += 8) {
-    float d[8], T[8];
+  // 32 blocks' loads in flight per thread: the scan is latency-bound
+  // otherwise (one state entry per thread, a strided walk over the blocks)
+  constexpr int U = 32;
+  for (; b + U <= nblk; b += U) {
+    float d[U], T[U];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < U; ++u) {
       d[u] = p[(b + u) * E];
       T[u] = t[b + u];
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < U; ++u) {
       p[(b + u) * E] = s;
       s = expf(T[u]) * s + d[u];
     }

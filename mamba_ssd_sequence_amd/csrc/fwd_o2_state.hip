@@ -14,20 +14,20 @@
 // so phi(q), phi(k) are never formed, only the per-row scalings.
 //
 // Decomposition.  The 1 MiB state never leaves the chip: each workgroup owns
-// an a-slice (SL values of a) x a 16-column value slice, held as MFMA
+// an a-slice (SL values of a) x an 8-column value slice, held as MFMA
 // accumulators (fp32) across the whole sequence, and walks the blocks in
-// order.  Its 8 waves are 4 a groups x 2 halves of the 16 columns: wave w
-// owns AW values of a (in quads) and 8 columns, and one 32x32 accumulator
-// tile covers 32 values of b x (4 values of a x 8 columns), so the state of
-// a quad is two tiles (32 VGPRs/lane).  On gfx950 the 32x32x16 MFMA (32
+// order.  Each of its 8 waves owns AW values of a (in quads) on the 8
+// columns; one 32x32 accumulator tile covers 32 values of b x (4 values of
+// a x 8 columns), so the state of a quad is two tiles (32 VGPRs/lane).  With
+// >= 32 heads a workgroup holds all 64 values of a (no partial outputs to
+// combine), with fewer heads half of them.  On gfx950 the 32x32x16 MFMA (32
 // cycles) absorbs the per-element VALU work of this scan (decay, fp16
 // conversion, row scalings) with little loss, and its operand fragments
 // (32 rows x 16 bytes at a 144-byte pitch) read LDS without bank conflicts.
 // The A operand of the output product is the state itself (its accumulator
 // layout read as a permuted-k operand), the A operand of the update is K^T.
-// The workgroup's partial output (its a-slice) is reduced over the 4 waves of
-// each column half in LDS and written to the workspace; the output kernel
-// adds the P_a partials.
+// The workgroup's output (over its a-slice) is reduced over its waves in LDS
+// and written to the workspace; the output kernel adds the P_a a-slices.
 //
 // Precision.  Both products run on v_mfma_f32_32x32x16_f16 (same rate as
 // bf16) with exact power-of-two scales: q*2^tau < 2^13 and k*2^kap in (-1, 1)
@@ -52,7 +52,7 @@
 // The per-block operands arrive pre-converted from the block-prep kernel, so
 // staging is plain copies.
 //
-// Grid: B*H x P_a x 4 workgroups (P_a = 64 / (4*AW)), 512 threads each; when
+// Grid: B*H x P_a x 8 workgroups (P_a = 64 / (8*AW)), 512 threads each; when
 // B*H is a multiple of 8 the workgroups of one head share an XCD (and its L2).
 #include "common.h"
 #include "launch.h"
@@ -69,7 +69,8 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 namespace {
 constexpr int DH = 64;
-constexpr int CW = 16;      // value columns per workgroup
+constexpr int CW = 8;       // value columns per workgroup
+constexpr int NCS = 64 / CW;  // column slices per head
 constexpr int PH = DH + 8;  // fp16 row pitch (elements): 144 B
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -89,13 +90,14 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
                                                       float* __restrict__ part,
                                                       float* __restrict__ final_state) {
   constexpr int NT = NW * WAVE;       // threads
-  constexpr int NAG = NW / 2;         // a groups (each wave: one a group x one half of the columns)
+  constexpr int NAG = NW;             // a groups (one per wave)
   constexpr int SL = NAG * AW;        // a values per workgroup
   constexpr int PA = DH / SL;         // a-slices per head
   constexpr int NQD = AW / 4;         // a quads per wave
   constexpr int QP = SL + 4;          // row pitch of the q copy (elements)
   constexpr int NI = BLK * DH / 8 / NT;   // 16-byte q / k^T segments per thread
-  constexpr int NX = CW * DH / 2 / NT;    // 32-bit X^T words per thread
+  constexpr int NXW = CW * DH / 2;        // 32-bit X^T words per block
+  constexpr int NX = (NXW + NT - 1) / NT; // ... per thread
   constexpr int NQ = (BLK * SL / 4 + NT - 1) / NT;  // 4-value q groups per thread
   constexpr bool STAGGER = NW == 8;   // two waves per SIMD
   static_assert(AW % 4 == 0 && NI >= 1 && NX >= 1, "thread mapping");
@@ -120,21 +122,21 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
     // workgroups are dispatched round-robin over the 8 XCDs: give all the
     // workgroups of one head the same id mod 8, so they share one L2
     const int xcd = blockIdx.x & 7, s = blockIdx.x >> 3;
-    const int p = s % (PA * 4);
-    bh = (int64_t)(s / (PA * 4)) * 8 + xcd;
-    pa = p >> 2;
-    pc = p & 3;
+    const int p = s % (PA * NCS);
+    bh = (int64_t)(s / (PA * NCS)) * 8 + xcd;
+    pa = p / NCS;
+    pc = p % NCS;
   } else {
-    pc = blockIdx.x & 3;
-    pa = (blockIdx.x >> 2) % PA;
-    bh = (blockIdx.x >> 2) / PA;
+    pc = blockIdx.x % NCS;
+    pa = (blockIdx.x / NCS) % PA;
+    bh = (blockIdx.x / NCS) / PA;
   }
   const int a0 = pa * SL;
   const int c0 = pc * CW;
   // this wave: a values a0 + ag AW .. + AW - 1 (in quads), value columns
-  // c0 + 8 ch .. + 7; lane n32 of a 32x32 tile column holds a quad member
-  // n32 / 8 and column n32 % 8
-  const int ag = wave % NAG, ch = wave / NAG;
+  // c0 .. c0 + 7; lane n32 of a 32x32 tile column holds a quad member n32 / 8
+  // and column n32 % 8
+  const int ag = wave;
   const int aw0 = a0 + ag * AW;
   const int64_t nblk = n_blocks(N);
   const int64_t Np = nblk * BLK;  // partial rows per head (padded)
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
     }
 #pragma unroll
     for (int u = 0; u < NX; ++u) {
-      const int idx = tid + u * NT, xr = idx >> 5, xw = idx & 31;
+      const int idx = (tid + u * NT) % NXW, xr = idx >> 5, xw = idx & 31;
       px[u] = *reinterpret_cast<const uint32_t*>(R + REC_XT + ((c0 + xr) * DH + 2 * xw) * 2);
     }
     // this workgroup's q columns a0 + 4 g4 .. +3 of row r (record column order
@@ -198,8 +200,10 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
 #pragma unroll
     for (int u = 0; u < NX; ++u) {
       const int idx = tid + u * NT, xr = idx >> 5, xw = idx & 31;
-      const f16x2 x = (__builtin_bit_cast(f16x2, px[u]) * xf[0]) * xf[1];
-      *reinterpret_cast<f16x2*>(&Xh[sl][xr * PH + 2 * xw]) = x;
+      if (NT * NX == NXW || idx < NXW) {
+        const f16x2 x = (__builtin_bit_cast(f16x2, px[u]) * xf[0]) * xf[1];
+        *reinterpret_cast<f16x2*>(&Xh[sl][xr * PH + 2 * xw]) = x;
+      }
     }
 #pragma unroll
     for (int u = 0; u < NQ; ++u) {
@@ -217,21 +221,20 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
   auto drain = [&](int64_t blk, const Blk& p) {
     if (NT == BLK * CW / 4 || tid < BLK * CW / 4) {
       const int64_t t0 = blk * BLK;
-      const int i = tid >> 2, c4 = (tid & 3) * 4;
+      const int i = tid >> 1, c4 = (tid & 1) * 4;
       // element (i, c4..c4+3) sits in accumulator slot i/32 of lane
-      // i%32 + 32 ((c4/4) & 1) of the waves of column half c4/8
-      const int idx = (i >> 5) * WAVE + (i & 31) + 32 * ((c4 >> 2) & 1);
-      const int wh = (c4 >> 3) * NAG;
-      f32x4 s = red[blk & 1][wh][idx];
+      // i%32 + 32 (c4/4) of every wave
+      const int idx = (i >> 5) * WAVE + (i & 31) + 32 * (c4 >> 2);
+      f32x4 s = red[blk & 1][0][idx];
 #pragma unroll
-      for (int w = 1; w < NAG; ++w) s += red[blk & 1][wh + w][idx];
+      for (int w = 1; w < NW; ++w) s += red[blk & 1][w][idx];
       const float f = st_ecs[blk % 3][i] * ldexpf(ldexpf(1.f, -p.sig_in), -2 * p.tau);
       *reinterpret_cast<f32x4*>(&part[(((int64_t)pa * BH + bh) * Np + t0 + i) * DH + c0 + c4]) = s * f;
     }
   };
 
   // state: quad qd, b-tile bt (32 rows) -> 32 x 32 accumulator over
-  // (b) x (a = aw0 + 4 qd + n32/8, c = c0 + 8 ch + n32%8); lane (n32, h)
+  // (b) x (a = aw0 + 4 qd + n32/8, c = c0 + n32%8); lane (n32, h)
   // holds the rows b = 32 bt + 8 q + 4 h + s in register 4 q + s
   f32x16 S[NQD][2];
 #pragma unroll
@@ -293,10 +296,10 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
           Kf[bt][kk] = *reinterpret_cast<const f16x8*>(&KT[(bt * 32 + n32) * PH + kk * 16 + 8 * h]);
-      f16x8 xh[4];  // X^T[c][j], c = 8 ch + n32 % 8
+      f16x8 xh[4];  // X^T[c][j], c = n32 % 8
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        xh[kk] = *reinterpret_cast<const f16x8*>(&Xh[sl][(8 * ch + (n32 & 7)) * PH + kk * 16 + 8 * h]);
+        xh[kk] = *reinterpret_cast<const f16x8*>(&Xh[sl][(n32 & 7) * PH + kk * 16 + 8 * h]);
       const float eT = cur.eTs;
 #pragma unroll
       for (int qd = 0; qd < NQD; ++qd) {
@@ -357,7 +360,7 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
 
   if (final_state) {
     const float f = ldexpf(1.f, -prv.sig_out);
-    const int c = c0 + 8 * ch + (n32 & 7);
+    const int c = c0 + (n32 & 7);
 #pragma unroll
     for (int qd = 0; qd < NQD; ++qd) {
       const int a = aw0 + 4 * qd + (n32 >> 3);
@@ -378,7 +381,7 @@ hipError_t launch_o2_state(const void* rec, int64_t BH, int64_t N, float* part,
   const int PA = o2_pa(BH);
   const int xcd_map = (BH % 8) == 0;
   const uint8_t* r = static_cast<const uint8_t*>(rec);
-  const dim3 grid((unsigned)(BH * PA * 4));
+  const dim3 grid((unsigned)(BH * PA * NCS));
   if (AW == 8)
     hipLaunchKernelGGL((k_o2_state<8, 8>), grid, dim3(8 * WAVE), 0, stream, r, BH, N, xcd_map, part, final_state);
   else

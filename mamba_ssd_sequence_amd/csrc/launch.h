@@ -10,12 +10,13 @@ namespace ssd {
 // Forward work is organised in blocks of 64 tokens.
 __host__ __device__ inline int64_t n_blocks(int64_t N) { return (N + 63) / 64; }
 
-// Order-2 state kernel (8 waves per workgroup: 4 a groups x 2 halves of the
-// 16 value columns): a values per wave (AW, in quads) and per workgroup
-// (SL = 4 AW), and the resulting number of a-slices per head (P_a = 64 / SL).
-// Fewer heads -> thinner slices so that the grid still covers the chip.
+// Order-2 state kernel (8 waves per workgroup, one a group each, all on the
+// workgroup's 8 value columns): a values per wave (AW, in quads) and per
+// workgroup (SL = 8 AW), and the resulting number of a-slices per head
+// (P_a = 64 / SL).  Fewer heads -> thinner slices so that the grid still
+// covers the chip.
 inline int o2_aw(int64_t BH) { return BH >= 32 ? 8 : 4; }
-inline int o2_sl(int64_t BH) { return 4 * o2_aw(BH); }
+inline int o2_sl(int64_t BH) { return 8 * o2_aw(BH); }
 inline int o2_pa(int64_t BH) { return 64 / o2_sl(BH); }
 
 // Order-2 per-block operand record (bytes), written by the block-prep kernel

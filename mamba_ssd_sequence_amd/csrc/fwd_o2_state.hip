@@ -219,17 +219,27 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
   // partial output of block blk (its scales in p) -> workspace, scaled to
   // true units: e^{cs_i} 2^-(sig_in + 2 tau)
   auto drain = [&](int64_t blk, const Blk& p) {
-    if (NT == BLK * CW / 4 || tid < BLK * CW / 4) {
+    // two columns per thread, so that the first NT/2 threads share the work
+    constexpr int ND = BLK * CW / 2;
+    if (NT == ND || tid < ND) {
       const int64_t t0 = blk * BLK;
-      const int i = tid >> 1, c4 = (tid & 1) * 4;
-      // element (i, c4..c4+3) sits in accumulator slot i/32 of lane
-      // i%32 + 32 (c4/4) of every wave
-      const int idx = (i >> 5) * WAVE + (i & 31) + 32 * (c4 >> 2);
-      f32x4 s = red[blk & 1][0][idx];
+      const int i = tid / (CW / 2), c2 = (tid % (CW / 2)) * 2;
+      // element (i, c2..c2+1) sits in components c2%4.. of accumulator slot
+      // i/32 of lane i%32 + 32 (c2/4) of every wave
+      const int idx = (i >> 5) * WAVE + (i & 31) + 32 * (c2 >> 2);
+      const float* rb = reinterpret_cast<const float*>(&red[blk & 1][0][idx]) + (c2 & 3);
+      constexpr int WS = 2 * WAVE * 4;  // floats per wave
+      float s0 = rb[0], s1 = rb[1];
 #pragma unroll
-      for (int w = 1; w < NW; ++w) s += red[blk & 1][w][idx];
+      for (int w = 1; w < NW; ++w) {
+        s0 += rb[w * WS];
+        s1 += rb[w * WS + 1];
+      }
       const float f = st_ecs[blk % 3][i] * ldexpf(ldexpf(1.f, -p.sig_in), -2 * p.tau);
-      *reinterpret_cast<f32x4*>(&part[(((int64_t)pa * BH + bh) * Np + t0 + i) * DH + c0 + c4]) = s * f;
+      float2 o;
+      o.x = s0 * f;
+      o.y = s1 * f;
+      *reinterpret_cast<float2*>(&part[(((int64_t)pa * BH + bh) * Np + t0 + i) * DH + c0 + c2]) = o;
     }
   };
 

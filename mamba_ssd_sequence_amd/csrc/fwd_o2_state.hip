@@ -94,11 +94,9 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
   constexpr int SL = NAG * AW;        // a values per workgroup
   constexpr int PA = DH / SL;         // a-slices per head
   constexpr int NQD = AW / 4;         // a quads per wave
-  constexpr int QP = SL + 4;          // row pitch of the q copy (elements)
   constexpr int NI = BLK * DH / 8 / NT;   // 16-byte q / k^T segments per thread
   constexpr int NXW = CW * DH / 2;        // 32-bit X^T words per block
   constexpr int NX = (NXW + NT - 1) / NT; // ... per thread
-  constexpr int NQ = (BLK * SL / 4 + NT - 1) / NT;  // 4-value q groups per thread
   constexpr bool STAGGER = NW == 8;   // two waves per SIMD
   static_assert(AW % 4 == 0 && NI >= 1 && NX >= 1, "thread mapping");
 
@@ -108,7 +106,6 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
   __shared__ __attribute__((aligned(16))) _Float16 Qh[2][BLK * PH];  // [i][perm b] q 2^tau
   __shared__ __attribute__((aligned(16))) _Float16 KTh[2][DH * PH];  // [b][j] k 2^kap
   __shared__ __attribute__((aligned(16))) _Float16 Xh[2][CW * PH];   // [c][j] X 2^(sig - 2 kap)
-  __shared__ __attribute__((aligned(16))) _Float16 Qa[2][BLK * QP];  // [i][a - a0] q 2^tau
   __shared__ f32x4 red[2][NW][2 * WAVE];  // per wave, in accumulator order
   __shared__ float st_ecs[3][BLK];
 
@@ -138,6 +135,14 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
   // and column n32 % 8
   const int ag = wave;
   const int aw0 = a0 + ag * AW;
+  // slot of q_{:, a} for the first a of each quad in the record's q row (its
+  // 4-column subgroups are stored in the order 0, 2, 1, 3 of each 16-group)
+  int qpos[NQD];
+#pragma unroll
+  for (int qd = 0; qd < NQD; ++qd) {
+    const int a = aw0 + 4 * qd, G = (a >> 2) & 3;
+    qpos[qd] = (a & ~15) + 4 * (G == 1 ? 2 : (G == 2 ? 1 : G));
+  }
   const int64_t nblk = n_blocks(N);
   const int64_t Np = nblk * BLK;  // partial rows per head (padded)
   const uint8_t* rec_h = rec + bh * nblk * (int64_t)REC_BYTES;
@@ -145,7 +150,6 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
   // ---- registers of the prefetched block -------------------------------------
   uint4 pq[NI], pk[NI];
   uint32_t px[NX];
-  uint2 pqa[NQ];
   uint32_t pe;
   struct Blk {
     int sig_in, tau;  // scale exponents of the entering state and of q
@@ -166,15 +170,6 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
     for (int u = 0; u < NX; ++u) {
       const int idx = (tid + u * NT) % NXW, xr = idx >> 5, xw = idx & 31;
       px[u] = *reinterpret_cast<const uint32_t*>(R + REC_XT + ((c0 + xr) * DH + 2 * xw) * 2);
-    }
-    // this workgroup's q columns a0 + 4 g4 .. +3 of row r (record column order
-    // within a 16-group: 4-column subgroups at slots 0, 2, 1, 3)
-#pragma unroll
-    for (int u = 0; u < NQ; ++u) {
-      const int idx = (tid + u * NT) % (BLK * SL / 4), r = idx / (SL / 4), g4 = idx % (SL / 4);
-      const int b = a0 + 4 * g4, G = (b >> 2) & 3;
-      const int pos = (b & ~15) + 4 * (G == 1 ? 2 : (G == 2 ? 1 : G));
-      pqa[u] = *reinterpret_cast<const uint2*>(R + REC_QH + (r * DH + pos) * 2);
     }
     pe = *reinterpret_cast<const uint32_t*>(R + REC_ECS + 4 * (tid & (BLK - 1)));
     const int* sc = reinterpret_cast<const int*>(R + REC_SC);  // uniform address
@@ -203,14 +198,6 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
       if (NT * NX == NXW || idx < NXW) {
         const f16x2 x = (__builtin_bit_cast(f16x2, px[u]) * xf[0]) * xf[1];
         *reinterpret_cast<f16x2*>(&Xh[sl][xr * PH + 2 * xw]) = x;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < NQ; ++u) {
-      const int idx = tid + u * NT;
-      if (NT * NQ == BLK * SL / 4 || idx < BLK * SL / 4) {
-        const int r = idx / (SL / 4), g4 = idx % (SL / 4);
-        *reinterpret_cast<uint2*>(&Qa[sl][r * QP + 4 * g4]) = pqa[u];
       }
     }
     st_ecs[blk % 3][tid & (BLK - 1)] = __uint_as_float(pe);
@@ -285,8 +272,9 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
           f32x16 T = mfma32(SA[0], Qf[it][0], f32x16{});
 #pragma unroll
           for (int kk = 1; kk < 4; ++kk) T = mfma32(SA[kk], Qf[it][kk], T);
-          // rows 8 q + 4 h + s of T: quad member q, column 4 h + s
-          const f16x4 qv = *reinterpret_cast<const f16x4*>(&Qa[sl][(it * 32 + n32) * QP + ag * AW + 4 * qd]);
+          // rows 8 q + 4 h + s of T: quad member q, column 4 h + s; the quad's
+          // q values are 4 contiguous slots of the staged q row
+          const f16x4 qv = *reinterpret_cast<const f16x4*>(&Q[(it * 32 + n32) * PH + qpos[qd]]);
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float qa = (float)qv[q];

@@ -49,6 +49,9 @@
 // MFMA work and write its partial output to LDS.
 // Half of the waves do the MFMA work first and the other half last, so every
 // SIMD keeps its matrix core busy while the other wave does the bookkeeping.
+// Within the MFMA work the VALU operations are placed by hand between the
+// MFMAs (a wave issues in order, so VALU work that waits on a chain's result
+// would otherwise leave the matrix core idle).
 // The per-block operands arrive pre-converted from the block-prep kernel, so
 // staging is plain copies.
 //
@@ -56,10 +59,6 @@
 // B*H is a multiple of 8 the workgroups of one head share an XCD (and its L2).
 #include "common.h"
 #include "launch.h"
-
-#ifndef O2_SCHED
-#define O2_SCHED 0
-#endif
 
 namespace ssd {
 
@@ -99,6 +98,7 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
   constexpr int NX = (NXW + NT - 1) / NT; // ... per thread
   constexpr bool STAGGER = NW == 8;   // two waves per SIMD
   static_assert(AW % 4 == 0 && NI >= 1 && NX >= 1, "thread mapping");
+  static_assert(NQD == 1 || NQD == 2, "one or two a-quads per wave");
 
   // staging (by block parity) and partial-output buffers; e^{cs} rows rotate
   // over three slots because the drain of block n-1 may still read them while
@@ -238,82 +238,156 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
   for (int p = 0; p < NQD; ++p)
 #pragma unroll
     for (int bt = 0; bt < 2; ++bt) S[p][bt] = f32x16{};
+  // fp16 copy of quad 0's state, made at the end of the previous block's
+  // update so that the first output chain can start at once
+  f16x8 SA0[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) SA0[kk] = f16x8{};
 
-  // MFMA work of block blk: the output product with the entering state for
-  // every quad, then the update.  Output: T^T[(a, c)][i] = sum_b S[b][(a, c)]
+  // MFMA work of block blk.  Output: T^T[(a, c)][i] = sum_b S[b][(a, c)]
   // Q[i][b] over 16-row k-steps kk (b in 16 kk + {4h..4h+3, 8+4h..8+4h+3} on
   // lane half h, matching the record's q column order), then
   // Y[i][c] += sum_a q_ia T^T[(a, c)][i].  Update: S = eTs S + K^T ((k_:a
   // 2^kap) * X 2^(sig - 2 kap)) over 16-token k-steps (tokens 16 kk + 8 h ..
-  // +7 on lane half h).  The two passes keep the Q and K^T operand fragments
-  // from being live together (register file).
+  // +7 on lane half h).
+  //
+  // A wave issues in order, so the VALU work (fp16 conversion of the state,
+  // decay, row scalings, update operands) is interleaved by hand with the
+  // MFMA chains: slot m holds one MFMA and the VALU work that is ready by
+  // then (results of a chain are used two or more slots after its last
+  // MFMA, LDS operands are read two to four slots ahead).  Scheduling
+  // barriers keep the compiler from regrouping the slots.
   auto compute = [&](int64_t blk) {
     const int sl = (int)(blk & 1);
-    {
-      const _Float16* Q = Qh[sl];
-      f16x8 Qf[2][4];  // B operand: Q^T[b][i], i = 32 it + n32
-#pragma unroll
-      for (int it = 0; it < 2; ++it)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          Qf[it][kk] = *reinterpret_cast<const f16x8*>(&Q[(it * 32 + n32) * PH + kk * 16 + 8 * h]);
-      f32x4 Y[2];
-#pragma unroll
-      for (int it = 0; it < 2; ++it) Y[it] = zero4();
-#pragma unroll
-      for (int qd = 0; qd < NQD; ++qd) {
-        f16x8 SA[4];
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) SA[kk][e] = (_Float16)S[qd][kk >> 1][8 * (kk & 1) + e];
-#pragma unroll
-        for (int it = 0; it < 2; ++it) {
-          f32x16 T = mfma32(SA[0], Qf[it][0], f32x16{});
-#pragma unroll
-          for (int kk = 1; kk < 4; ++kk) T = mfma32(SA[kk], Qf[it][kk], T);
-          // rows 8 q + 4 h + s of T: quad member q, column 4 h + s; the quad's
-          // q values are 4 contiguous slots of the staged q row
-          const f16x4 qv = *reinterpret_cast<const f16x4*>(&Q[(it * 32 + n32) * PH + qpos[qd]]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float qa = (float)qv[q];
-#pragma unroll
-            for (int s = 0; s < 4; ++s) Y[it][s] = fmaf(qa, T[4 * q + s], Y[it][s]);
-          }
-        }
-      }
-#pragma unroll
-      for (int it = 0; it < 2; ++it) red[sl][wave][it * WAVE + lane] = Y[it];
-    }
-    {
-      const _Float16* KT = KTh[sl];
-      f16x8 Kf[2][4];  // A operand: K^T[b][j], b = 32 bt + n32
-#pragma unroll
-      for (int bt = 0; bt < 2; ++bt)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          Kf[bt][kk] = *reinterpret_cast<const f16x8*>(&KT[(bt * 32 + n32) * PH + kk * 16 + 8 * h]);
-      f16x8 xh[4];  // X^T[c][j], c = n32 % 8
+    const _Float16* Q = Qh[sl];
+    const _Float16* KT = KTh[sl];
+    const _Float16* XT = Xh[sl];
+    const float eT = cur.eTs;
+
+    f16x8 SA1[4];          // fp16 copy of quad 1's state
+    f16x8 Qf[2][4];        // B operand of the output: Q^T[b][i], i = 32 it + n32
+    f16x4 qv[NQD][2];      // q values of the quad's a's for token 32 it + n32
+    f32x16 T[NQD][2];      // output chains (quad, it)
+    f32x4 Y[2] = {zero4(), zero4()};
+    f16x8 xh[4];           // X^T[c][j], c = n32 % 8
+    f16x8 Kr[NQD][4];      // K^T row of k_:a for the quad's a = aw0 + 4 qd + n32/8
+    f16x8 Bu[NQD][4];      // update B operand
+    f16x8 Kf[2][4];        // update A operand: K^T[b][j], b = 32 bt + n32
+
+    auto SB = [] { __builtin_amdgcn_sched_barrier(0); };
+    auto rdQ = [&](int it) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        xh[kk] = *reinterpret_cast<const f16x8*>(&Xh[sl][(n32 & 7) * PH + kk * 16 + 8 * h]);
-      const float eT = cur.eTs;
+        Qf[it][kk] = *reinterpret_cast<const f16x8*>(&Q[(it * 32 + n32) * PH + kk * 16 + 8 * h]);
+    };
+    auto rdK = [&](int bt) {
 #pragma unroll
-      for (int qd = 0; qd < NQD; ++qd) {
-        const int a = aw0 + 4 * qd + (n32 >> 3);  // the K^T row of k_:a
-        f16x8 Bu[4];
+      for (int kk = 0; kk < 4; ++kk)
+        Kf[bt][kk] = *reinterpret_cast<const f16x8*>(&KT[(bt * 32 + n32) * PH + kk * 16 + 8 * h]);
+    };
+    auto rdX = [&] {
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          Bu[kk] = *reinterpret_cast<const f16x8*>(&KT[a * PH + kk * 16 + 8 * h]) * xh[kk];
+      for (int kk = 0; kk < 4; ++kk)
+        xh[kk] = *reinterpret_cast<const f16x8*>(&XT[(n32 & 7) * PH + kk * 16 + 8 * h]);
+    };
+    auto rdKr = [&](int q) {
+      const int a = aw0 + 4 * q + (n32 >> 3);
 #pragma unroll
-        for (int bt = 0; bt < 2; ++bt) {
-          f32x16 acc = eT * S[qd][bt];
+      for (int kk = 0; kk < 4; ++kk)
+        Kr[q][kk] = *reinterpret_cast<const f16x8*>(&KT[a * PH + kk * 16 + 8 * h]);
+    };
+    auto rdqv = [&] {
 #pragma unroll
-          for (int kk = 0; kk < 4; ++kk) acc = mfma32(Kf[bt][kk], Bu[kk], acc);
-          S[qd][bt] = acc;
-        }
-      }
+      for (int q = 0; q < NQD; ++q)
+#pragma unroll
+        for (int it = 0; it < 2; ++it)
+          qv[q][it] = *reinterpret_cast<const f16x4*>(&Q[(it * 32 + n32) * PH + qpos[q]]);
+    };
+    // MFMAs
+    auto out = [&](int q, int it, int kk, const f16x8* SA) {
+      T[q][it] = mfma32(SA[kk], Qf[it][kk], kk == 0 ? f32x16{} : T[q][it]);
+    };
+    auto upd = [&](int q, int bt, int kk) { S[q][bt] = mfma32(Kf[bt][kk], Bu[q][kk], S[q][bt]); };
+    // VALU units (four instructions each)
+    // (the empty asm consumes the result in place, so that the conversion is
+    // not moved to the loop's end where its value is carried)
+    auto cvt = [&](f16x8* SA, int q, int kk) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) SA[kk][e] = (_Float16)S[q][kk >> 1][8 * (kk & 1) + e];
+      asm volatile("" ::"v"(SA[kk]));
+    };
+    auto mul = [&](int q, int bt, int g) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) S[q][bt][4 * g + e] *= eT;
+    };
+    // rows 8 m + 4 h + s of T: quad member m, column 4 h + s
+    auto fy = [&](int q, int it, int m) {
+      const float qa = (float)qv[q][it][m];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) Y[it][s] = fmaf(qa, T[q][it][4 * m + s], Y[it][s]);
+    };
+    auto bu = [&](int q, int kk) { Bu[q][kk] = Kr[q][kk] * xh[kk]; };
+    auto wr = [&] {
+#pragma unroll
+      for (int it = 0; it < 2; ++it) red[sl][wave][it * WAVE + lane] = Y[it];
+    };
+
+    if constexpr (NQD == 2) {
+      // chains: C(q, it) = out over kk, U(q, bt) = upd over kk, in the order
+      // C00 C10 C01 C11 U00 U01 U10 U11
+      rdQ(0); rdqv(); cvt(SA1, 1, 0); cvt(SA1, 1, 1); SB();
+      out(0, 0, 0, SA0); cvt(SA1, 1, 2); rdQ(1); SB();
+      out(0, 0, 1, SA0); cvt(SA1, 1, 3); mul(0, 0, 0); SB();
+      out(0, 0, 2, SA0); mul(0, 0, 1); SB();
+      out(0, 0, 3, SA0); mul(0, 0, 2); mul(0, 0, 3); SB();
+      out(1, 0, 0, SA1); mul(0, 1, 0); SB();
+      out(1, 0, 1, SA1); mul(0, 1, 1); mul(0, 1, 2); SB();
+      out(1, 0, 2, SA1); mul(0, 1, 3); rdX(); SB();
+      out(1, 0, 3, SA1); fy(0, 0, 0); fy(0, 0, 1); SB();
+      out(0, 1, 0, SA0); fy(0, 0, 2); rdKr(0); SB();
+      out(0, 1, 1, SA0); fy(0, 0, 3); SB();
+      out(0, 1, 2, SA0); fy(1, 0, 0); fy(1, 0, 1); SB();
+      out(0, 1, 3, SA0); fy(1, 0, 2); SB();
+      out(1, 1, 0, SA1); fy(1, 0, 3); bu(0, 0); SB();
+      out(1, 1, 1, SA1); bu(0, 1); rdK(0); SB();
+      out(1, 1, 2, SA1); bu(0, 2); bu(0, 3); SB();
+      out(1, 1, 3, SA1); fy(0, 1, 0); SB();
+      upd(0, 0, 0); fy(0, 1, 1); fy(0, 1, 2); rdK(1); SB();
+      upd(0, 0, 1); fy(0, 1, 3); rdKr(1); SB();
+      upd(0, 0, 2); mul(1, 0, 0); mul(1, 0, 1); SB();
+      upd(0, 0, 3); mul(1, 0, 2); SB();
+      upd(0, 1, 0); mul(1, 0, 3); bu(1, 0); SB();
+      upd(0, 1, 1); bu(1, 1); SB();
+      upd(0, 1, 2); bu(1, 2); bu(1, 3); SB();
+      upd(0, 1, 3); fy(1, 1, 0); SB();
+      upd(1, 0, 0); fy(1, 1, 1); fy(1, 1, 2); SB();
+      upd(1, 0, 1); fy(1, 1, 3); SB();
+      upd(1, 0, 2); mul(1, 1, 0); mul(1, 1, 1); SB();
+      upd(1, 0, 3); mul(1, 1, 2); mul(1, 1, 3); SB();
+      upd(1, 1, 0); cvt(SA0, 0, 0); cvt(SA0, 0, 1); SB();
+      upd(1, 1, 1); cvt(SA0, 0, 2); SB();
+      upd(1, 1, 2); cvt(SA0, 0, 3); wr(); SB();
+      upd(1, 1, 3); SB();
+    } else {
+      // chains C00 C01 U00 U01
+      rdQ(0); rdqv(); SB();
+      out(0, 0, 0, SA0); mul(0, 0, 0); rdQ(1); SB();
+      out(0, 0, 1, SA0); mul(0, 0, 1); mul(0, 0, 2); SB();
+      out(0, 0, 2, SA0); mul(0, 0, 3); rdX(); rdKr(0); SB();
+      out(0, 0, 3, SA0); mul(0, 1, 0); mul(0, 1, 1); SB();
+      out(0, 1, 0, SA0); mul(0, 1, 2); rdK(0); SB();
+      out(0, 1, 1, SA0); mul(0, 1, 3); bu(0, 0); SB();
+      out(0, 1, 2, SA0); bu(0, 1); bu(0, 2); rdK(1); SB();
+      out(0, 1, 3, SA0); bu(0, 3); fy(0, 0, 0); SB();
+      upd(0, 0, 0); fy(0, 0, 1); fy(0, 0, 2); SB();
+      upd(0, 0, 1); fy(0, 0, 3); SB();
+      upd(0, 0, 2); fy(0, 1, 0); fy(0, 1, 1); SB();
+      upd(0, 0, 3); fy(0, 1, 2); SB();
+      upd(0, 1, 0); fy(0, 1, 3); SB();
+      upd(0, 1, 1); SB();
+      upd(0, 1, 2); cvt(SA0, 0, 0); cvt(SA0, 0, 1); wr(); SB();
+      upd(0, 1, 3); SB();
+      cvt(SA0, 0, 2); cvt(SA0, 0, 3); SB();
     }
   };
 

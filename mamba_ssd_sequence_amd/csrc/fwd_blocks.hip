@@ -260,6 +260,31 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
     csl[tid] = c;
     dtv[tid] = d;
   }
+  // Order 2: the numerator scan advances over steps of two blocks and gives
+  // the second block of a step only the state entering the step, so the first
+  // block's tokens reach it here as a direct (unmasked) term.  Its k and v
+  // rows are loaded now and staged after the block's own products.
+  constexpr bool PAIRS = ORDER == 2 && BF;
+  const bool partner = PAIRS && (blk & 1);
+  uint4 pka = make_uint4(0, 0, 0, 0), pkb = pka, pva = pka, pvb = pka;  // (registers, not an array)
+  float pcs = 0.f, pdt = 0.f, pT = 0.f;
+  if (PAIRS && partner) {
+    const int64_t tp = t0 - BLK;  // the first block of the step (always full)
+    const float base_p = (tp % chunk == 0) ? 0.f : a_cs[row + tp - 1];
+    pT = a_cs[row + tp + BLK - 1] - base_p;
+    if (tid < BLK) {
+      pcs = a_cs[row + tp + tid] - base_p;
+      pdt = dt ? dt[row + tp + tid] : 1.f;
+    }
+    // k: the 16-byte segment tid % 8 of rows tid / 8 and 32 + tid / 8; v: the
+    // same segment of the token pair 2 (tid / 8), 2 (tid / 8) + 1
+    const uint16_t* kb = static_cast<const uint16_t*>(kp) + (row + tp) * DH;
+    const uint16_t* vb = static_cast<const uint16_t*>(vp) + (row + tp) * DH;
+    pka = *reinterpret_cast<const uint4*>(kb + (tid >> 3) * DH + (tid & 7) * 8);
+    pkb = *reinterpret_cast<const uint4*>(kb + (32 + (tid >> 3)) * DH + (tid & 7) * 8);
+    pva = *reinterpret_cast<const uint4*>(vb + (2 * (tid >> 3)) * DH + (tid & 7) * 8);
+    pvb = *reinterpret_cast<const uint4*>(vb + (2 * (tid >> 3) + 1) * DH + (tid & 7) * 8);
+  }
   __syncthreads();
   const float* st = state + (bh * nblk + blk) * (int64_t)(DH * DH + DH);
   if constexpr (BF) {
@@ -410,6 +435,77 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
   }
   den_l = sum_over_groups(den_l);
 
+  if constexpr (PAIRS) {
+   if (partner) {
+    // direct term of the step's first block: num^T[c][i] += sum_j
+    // (v dt)_jc (q_i . k_j)^2 e^{cs_i + T' - cs'_j}, with every j before i.
+    // Ks, VT and dtv are restaged with the partner block once every wave is
+    // done with them.
+    __syncthreads();
+    *reinterpret_cast<uint4*>(&Ks[(tid >> 3) * PQ + (tid & 7) * 8]) = pka;
+    *reinterpret_cast<uint4*>(&Ks[(32 + (tid >> 3)) * PQ + (tid & 7) * 8]) = pkb;
+    if (tid < BLK) {
+      csl[tid] = pcs;  // the block's own values stay in cs_i (registers)
+      dtv[tid] = pdt;
+    }
+    __syncthreads();
+    {
+      const int j0 = 2 * (tid >> 3), sg = tid & 7;
+      const uint32_t w0[4] = {pva.x, pva.y, pva.z, pva.w};
+      const uint32_t w1[4] = {pvb.x, pvb.y, pvb.z, pvb.w};
+      const float d0 = dtv[j0], d1 = dtv[j0 + 1];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const float a0 = __uint_as_float(hh ? (w0[u] & 0xffff0000u) : (w0[u] << 16)) * d0;
+          const float a1 = __uint_as_float(hh ? (w1[u] & 0xffff0000u) : (w1[u] << 16)) * d1;
+          C pr[2] = {(C)a0, (C)a1};
+          *reinterpret_cast<uint32_t*>(&VT[(sg * 8 + 2 * u + hh) * PJ + j0]) = __builtin_bit_cast(uint32_t, pr);
+        }
+      }
+    }
+    __syncthreads();
+    f32x4 Wp[4];
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < DH / G::KS; ++ks)
+        acc = G::mma(G::ld(Ks, PQ, jt * 16 + n, ks, g), G::ld(Qs, PQ, il, ks, g), acc);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int j = jt * 16 + 4 * g + r;
+        Wp[jt][r] = acc[r] * acc[r] * expf(cs_i + pT - csl[j]);
+      }
+    }
+    if constexpr (BF) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 bw;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          bw[r] = (__bf16)Wp[2 * kb][r];
+          bw[4 + r] = (__bf16)Wp[2 * kb + 1][r];
+        }
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+          const C* base_p = &VT[(ct * 16 + n) * PJ + kb * 32 + 4 * g];
+          const bf16x4 lo = *reinterpret_cast<const bf16x4*>(base_p);
+          const bf16x4 hi = *reinterpret_cast<const bf16x4*>(base_p + 16);
+          bf16x8 a;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            a[r] = lo[r];
+            a[4 + r] = hi[r];
+          }
+          num[ct] = mfma_bf16(a, bw, num[ct]);
+        }
+      }
+    }
+   }
+  }
+
   // inter-block part: D[c][i] = sum_b S_in[b][c] Q[i][b].  With bf16
   // operands the state is split into high + low bf16 parts: the factored sum
   // over b can cancel (q nearly orthogonal to the keys), so a single bf16
@@ -440,7 +536,7 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
       for (int r = 0; r < 4; ++r) den_x += (float)Qs[il * PQ + ct * 16 + 4 * g + r] * inter[ct][r];
     if (il < nvalid) {
       for (int pa = 0; pa < P_a; ++pa) {
-        const float* pp = part + (((int64_t)pa * BH + bh) * (nblk * BLK) + t0 + il) * 64;
+        const float* pp = part + (((int64_t)pa * BH + bh) * o2_part_rows(N) + t0 + il) * 64;
 #pragma unroll
         for (int ct = 0; ct < NT; ++ct) num[ct] += *reinterpret_cast<const f32x4*>(pp + ct * 16 + 4 * g);
       }

@@ -9,7 +9,9 @@
 //      sum_j w_j k_j), on bf16 MFMA with w k split into high + low parts;
 //   2. the operand record the numerator state scan consumes (layout in
 //      launch.h): fp16 q 2^tau (columns permuted for the MFMA operand), fp16
-//      k^T 2^kap, fp16 X^T 2^xi with X_jc = w_j dt_j v_jc, e^{cs_i}, and the
+//      k^T 2^kap, fp16 X^T 2^xi with X_jc = w_j dt_j v_jc (for the first
+//      block of a two-block step w_j also carries the second block's decay
+//      e^{T'}, as the scan adds both blocks to its state at once), e^{cs_i}, and the
 //      block scalars (T, the bound delta = max|k|^2 sum_j max_c |X_jc| of
 //      any entry of the block's state increment, and the three exponents).
 //      The exponents put max|q| 2^tau below 2^13, max|k| 2^kap below 1 and
@@ -80,16 +82,27 @@ __global__ __launch_bounds__(256) void k_o2_blockprep(const uint16_t* __restrict
   const float base = (t0 % chunk == 0) ? 0.f : a_cs[row + t0 - 1];
   const float cs_last = a_cs[row + t0 + nv - 1];
   const float T = cs_last - base;
+  // the numerator scan advances over steps of two blocks (2m, 2m+1): the
+  // first block of a step weights its X to the end of the step, i.e. also by
+  // the decay total T' of the second block
+  float Tn = 0.f;
+  if ((blk & 1) == 0 && blk + 1 < nblk) {
+    const int64_t t1 = t0 + BLK;
+    const int nv1 = (int)((N - t1) < BLK ? (N - t1) : BLK);
+    const float base1 = (t1 % chunk == 0) ? 0.f : a_cs[row + t1 - 1];
+    Tn = a_cs[row + t1 + nv1 - 1] - base1;
+  }
   if (tid < BLK) {
-    float w = 0.f, d = 0.f, e = 1.f;
+    float w = 0.f, wx = 0.f, d = 0.f, e = 1.f;
     if (tid < nv) {
       const float acs = a_cs[row + t0 + tid];
       w = expf(cs_last - acs);
+      wx = expf(cs_last - acs + Tn);
       d = dt ? dt[row + t0 + tid] : 1.f;
       e = expf(acs - base);
     }
     wv[tid] = w;
-    wdt[tid] = w * d;
+    wdt[tid] = wx * d;
     reinterpret_cast<float*>(R + REC_ECS)[tid] = e;
   }
   if (tid == 0) tb[bh * nblk + blk] = T;
@@ -263,17 +276,21 @@ hipError_t launch_o2_blockprep(const void* q, const void* k, const void* v, cons
 // ---------------------------------------------------------------------------
 // Scale scan of the order-2 numerator state (one wave per head).
 //
-// The state scan holds its state S_n (after block n) as S_n 2^sig_n in fp32
-// accumulators and feeds S 2^sig to fp16 MFMA operands, so sig_n must keep
-// every entry below 2^13.  An upper bound of max |S_n| follows the state's
-// own recurrence, M_n = e^{T_n} M_{n-1} + delta_n with delta_n (block-prep)
-// bounding every entry of block n's increment; sig_n = 13 - ceil(log2 M_n).
-// The recurrence is linear, so the wave scans it in parallel: each lane
-// composes a contiguous run of blocks into (prod e^T, local M), a lane scan
-// combines the runs, and each lane replays its run from the incoming bound.
-// Per block it writes sig_in = sig_{n-1}, the combined decay-and-rescale
-// factor eTs = e^{T_n} 2^(sig_n - sig_{n-1}) (0 while the state is still
-// zero), and the fp16 factors taking the record's X 2^xi to X 2^(sig_n - 2 kap).
+// The state scan advances its state over steps of two blocks (2m, 2m+1) and
+// holds S_m (after step m) as S_m 2^sig_m in fp32 accumulators, feeding
+// S 2^sig to fp16 MFMA operands, so sig_m must keep every entry below 2^13.
+// An upper bound of max |S_m| follows the state's own recurrence,
+// M_m = e^{T_2m + T_2m+1} M_{m-1} + delta_2m + delta_2m+1, with delta_n
+// (block-prep) bounding every entry of block n's share of the increment;
+// sig_m = 13 - ceil(log2 M_m).  The recurrence is linear, so the wave scans
+// it in parallel: each lane composes a contiguous run of steps into
+// (prod e^T, local M), a lane scan combines the runs, and each lane replays
+// its run from the incoming bound.  Both records of step m get sig_in =
+// sig_{m-1}, the decay-and-rescale factor eTs = e^{T_2m + T_2m+1}
+// 2^(sig_m - sig_{m-1}) (0 while the state is still zero), sig_out = sig_m,
+// the fp16 factors taking their X 2^xi to X 2^(sig_m - 2 kap), and the decay
+// from the start of the step to the start of the block (1, or e^{T_2m} for
+// the second block).
 // ---------------------------------------------------------------------------
 namespace {
 __device__ __forceinline__ int sig_of(float m) {
@@ -284,24 +301,35 @@ __device__ __forceinline__ int sig_of(float m) {
 __global__ __launch_bounds__(64) void k_o2_scale_scan(uint8_t* __restrict__ rec, int64_t nblk) {
   const int64_t bh = blockIdx.x;
   const int lane = threadIdx.x;
-  const int64_t seg = (nblk + WAVE - 1) / WAVE;
-  const int64_t b0 = lane * seg, b1 = (b0 + seg < nblk) ? b0 + seg : nblk;
+  const int64_t nstep = (nblk + 1) / 2;
+  const int64_t seg = (nstep + WAVE - 1) / WAVE;
+  const int64_t s0 = lane * seg, s1 = (s0 + seg < nstep) ? s0 + seg : nstep;
   uint8_t* base = rec + bh * nblk * (int64_t)REC_BYTES + REC_SC;
-  // run of this lane as a map M -> A M + B (loads issued 8 blocks at a time)
-  float A = 1.f, B = 0.f;
-  for (int64_t c0 = b0; c0 < b1; c0 += 8) {
-    float e[8], dl[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float* sc = reinterpret_cast<const float*>(base + (c0 + u < b1 ? c0 + u : b0) * (int64_t)REC_BYTES);
-      e[u] = sc[SC_ET];
-      dl[u] = sc[SC_DELTA];
+  auto scal = [&](int64_t b) { return reinterpret_cast<int*>(base + b * (int64_t)REC_BYTES); };
+  // decay e^{T} and bound increment of step st (a missing second block adds
+  // nothing)
+  auto step_vals = [&](int64_t st, float& eA, float& E, float& D) {
+    const int* a = scal(2 * st);
+    eA = __int_as_float(a[SC_ET]);
+    E = eA;
+    D = __int_as_float(a[SC_DELTA]);
+    if (2 * st + 1 < nblk) {
+      const int* b = scal(2 * st + 1);
+      E *= __int_as_float(b[SC_ET]);
+      D += __int_as_float(b[SC_DELTA]);
     }
+  };
+  // run of this lane as a map M -> A M + B (loads issued 4 steps at a time)
+  float A = 1.f, B = 0.f;
+  for (int64_t c0 = s0; c0 < s1; c0 += 4) {
+    float eA[4], E[4], D[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (c0 + u < b1) {
-        A *= e[u];
-        B = e[u] * B + dl[u];
+    for (int u = 0; u < 4; ++u) step_vals(c0 + u < s1 ? c0 + u : s0, eA[u], E[u], D[u]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (c0 + u < s1) {
+        A *= E[u];
+        B = E[u] * B + D[u];
       }
     }
   }
@@ -316,36 +344,37 @@ __global__ __launch_bounds__(64) void k_o2_scale_scan(uint8_t* __restrict__ rec,
   }
   float M = __shfl_up(B, 1, WAVE);  // bound after the previous lane's run (M_{-1} = 0)
   if (lane == 0) M = 0.f;
-  for (int64_t c0 = b0; c0 < b1; c0 += 8) {
-    float e[8], dl[8];
-    int kx[8];
+  for (int64_t c0 = s0; c0 < s1; c0 += 4) {
+    float eA[4], E[4], D[4];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int* si = reinterpret_cast<const int*>(base + (c0 + u < b1 ? c0 + u : b0) * (int64_t)REC_BYTES);
-      e[u] = __int_as_float(si[SC_ET]);
-      dl[u] = __int_as_float(si[SC_DELTA]);
-      kx[u] = 2 * si[SC_KAP] + si[SC_XI];
-    }
+    for (int u = 0; u < 4; ++u) step_vals(c0 + u < s1 ? c0 + u : s0, eA[u], E[u], D[u]);
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      if (c0 + u < b1) {
-        uint8_t* p = base + (c0 + u) * (int64_t)REC_BYTES;
-        float* sc = reinterpret_cast<float*>(p);
-        int* si = reinterpret_cast<int*>(p);
-        const float Mn = e[u] * M + dl[u];
+    for (int u = 0; u < 4; ++u) {
+      if (c0 + u < s1) {
+        const float Mn = E[u] * M + D[u];
         const int sin = sig_of(M), sout = sig_of(Mn);
-        si[SC_SIG_IN] = sin;
-        si[SC_SIG_OUT] = sout;
-        sc[SC_ETS] = M > 0.f ? ldexpf(e[u], sout - sin) : 0.f;
-        // X 2^xi -> X 2^(sig - 2 kap): exact power-of-two factors (d <= 2
-        // since max X 2^xi >= 2^13; below 2^-48 the terms are negligible and
-        // dropped)
-        const int d = sout - kx[u];
-        const int d1 = d >= -14 ? d : d / 2, d2 = d >= -14 ? 0 : d - d / 2;
-        h16x2 xf;
-        xf[0] = d < -48 ? (_Float16)0.f : (_Float16)ldexpf(1.f, d1);
-        xf[1] = (_Float16)ldexpf(1.f, d2);
-        *reinterpret_cast<h16x2*>(&sc[SC_XF]) = xf;
+        const float ets = M > 0.f ? ldexpf(E[u], sout - sin) : 0.f;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const int64_t b = 2 * (c0 + u) + hb;
+          if (b < nblk) {
+            int* si = scal(b);
+            float* sc = reinterpret_cast<float*>(si);
+            si[SC_SIG_IN] = sin;
+            si[SC_SIG_OUT] = sout;
+            sc[SC_ETS] = ets;
+            sc[SC_EPRE] = hb ? eA[u] : 1.f;
+            // X 2^xi -> X 2^(sig - 2 kap): exact power-of-two factors (d <= 2
+            // since max X 2^xi >= 2^13; below 2^-48 the terms are negligible
+            // and dropped)
+            const int d = sout - 2 * si[SC_KAP] - si[SC_XI];
+            const int d1 = d >= -14 ? d : d / 2, d2 = d >= -14 ? 0 : d - d / 2;
+            h16x2 xf;
+            xf[0] = d < -48 ? (_Float16)0.f : (_Float16)ldexpf(1.f, d1);
+            xf[1] = (_Float16)ldexpf(1.f, d2);
+            *reinterpret_cast<h16x2*>(&sc[SC_XF]) = xf;
+          }
+        }
         M = Mn;
       }
     }

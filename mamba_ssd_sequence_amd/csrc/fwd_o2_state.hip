@@ -1,21 +1,25 @@
 // Order-2 (2Mamba) inter-block numerator: an on-chip scan of the d_h^2 x d_h
-// state over 64-token blocks.
+// state over steps of two 64-token blocks.
 //
 // 2Mamba2Furious, Algorithm 6: with order-2 features phi(x) = vec(x x^T) the
 // numerator state H_up is D x d_h (D = d_h^2 = 4096 at d_h = 64, 1 MiB fp32
-// per head).  Over one block of tokens j with decay weights
-// w_j = exp(A^CS_last - A^CS_j) it evolves as
-//     S <- exp(T_blk) S + sum_j w_j phi(k_j) (v dt)_j^T,
-// and the inter-block contribution to the numerator of token i is
+// per head).  Over a step of tokens j (two blocks, 2m and 2m+1) with decay
+// weights w_j = exp(A^CS_end - A^CS_j) it evolves as
+//     S <- exp(T_2m + T_2m+1) S + sum_j w_j phi(k_j) (v dt)_j^T,
+// and the contribution of the state entering the step to the numerator of
+// a token i of the step is
 //     exp(A^CS_i - A^CS_start) phi(q_i)^T S_in.
 // Writing the state row index as (a, b), both contractions factor per a:
 //     update : S_a += K^T diag(k_:a) X,          X_jc = w_j (v dt)_jc
 //     output : Y   += diag(qe_:a) (Q S_a),       qe_ia = q_ia exp(A^CS_i - A^CS_start)
-// so phi(q), phi(k) are never formed, only the per-row scalings.
+// so phi(q), phi(k) are never formed, only the per-row scalings.  The second
+// block of a step misses the first block's tokens in this product; the
+// output kernel adds them as a direct term.  Steps of two blocks halve the
+// per-element work on the state (decay, fp16 conversion) per token.
 //
 // Decomposition.  The 1 MiB state never leaves the chip: each workgroup owns
 // an a-slice (SL values of a) x an 8-column value slice, held as MFMA
-// accumulators (fp32) across the whole sequence, and walks the blocks in
+// accumulators (fp32) across the whole sequence, and walks the steps in
 // order.  Each of its 8 waves owns AW values of a (in quads) on the 8
 // columns; one 32x32 accumulator tile covers 32 values of b x (4 values of
 // a x 8 columns), so the state of a quad is two tiles (32 VGPRs/lane).  With
@@ -38,22 +42,26 @@
 // 2^(sig - 2 kap) < 2^15, formed by packed fp16 multiplies.  fp16's 11-bit
 // significand matters here: the factored sum over (a, b) can cancel when q is
 // nearly orthogonal to the block's keys, and a bf16 rounding of the state is
-// amplified there beyond the bf16 tolerance.  A change of sig between blocks
-// is folded into the decay factor, e^T 2^(sig_n - sig_{n-1}), so rescaling
-// costs nothing; all per-block scalars come precomputed in the record.
+// amplified there beyond the bf16 tolerance.  A change of sig between steps
+// is folded into the decay factor, e^T 2^(sig_m - sig_{m-1}), so rescaling
+// costs nothing; all scalars come precomputed in the block records.
 //
-// Pipeline, one barrier per block n: reduce block n-1's partial outputs
-// (LDS) into the workspace; copy block n+1's record (prefetched into
+// Pipeline, one barrier per step m: reduce step m-1's partial outputs (LDS)
+// into the workspace; copy step m+1's two records (prefetched into
 // registers one iteration earlier) into the other LDS slot; issue the loads
-// of block n+2 at once, so they have a whole block to arrive; run block n's
-// MFMA work and write its partial output to LDS.
+// of step m+2 at once, so they have a whole step to arrive; run step m's
+// MFMA work and write its partial outputs to LDS.
 // Half of the waves do the MFMA work first and the other half last, so every
 // SIMD keeps its matrix core busy while the other wave does the bookkeeping.
 // Within the MFMA work the VALU operations are placed by hand between the
 // MFMAs (a wave issues in order, so VALU work that waits on a chain's result
-// would otherwise leave the matrix core idle).
-// The per-block operands arrive pre-converted from the block-prep kernel, so
-// staging is plain copies.
+// would otherwise leave the matrix core idle): slot m holds one MFMA and
+// the VALU work that is ready by then (a chain's result is used three or
+// more slots after its last MFMA, LDS operands are read ahead), the output
+// and update chains of the two blocks alternate, and scheduling barriers
+// keep the compiler from regrouping the slots.  The per-block operands
+// arrive pre-converted from the block-prep kernel, so staging is plain
+// copies.
 //
 // Grid: B*H x P_a x 8 workgroups (P_a = 64 / (8*AW)), 512 threads each; when
 // B*H is a multiple of 8 the workgroups of one head share an XCD (and its L2).
@@ -77,10 +85,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 __device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
-
-
-
-
 }  // namespace
 
 template <int NW, int AW>
@@ -93,21 +97,19 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
   constexpr int SL = NAG * AW;        // a values per workgroup
   constexpr int PA = DH / SL;         // a-slices per head
   constexpr int NQD = AW / 4;         // a quads per wave
-  constexpr int NI = BLK * DH / 8 / NT;   // 16-byte q / k^T segments per thread
+  constexpr int NI = BLK * DH / 8 / NT;   // 16-byte q / k^T segments per thread and block
   constexpr int NXW = CW * DH / 2;        // 32-bit X^T words per block
-  constexpr int NX = (NXW + NT - 1) / NT; // ... per thread
-  constexpr bool STAGGER = NW == 8;   // two waves per SIMD
-  static_assert(AW % 4 == 0 && NI >= 1 && NX >= 1, "thread mapping");
+  static_assert(NT == 512 && NI == 1 && 2 * NXW == NT, "thread mapping: 8 waves");
   static_assert(NQD == 1 || NQD == 2, "one or two a-quads per wave");
 
-  // staging (by block parity) and partial-output buffers; e^{cs} rows rotate
-  // over three slots because the drain of block n-1 may still read them while
-  // block n+1 is staged
-  __shared__ __attribute__((aligned(16))) _Float16 Qh[2][BLK * PH];  // [i][perm b] q 2^tau
-  __shared__ __attribute__((aligned(16))) _Float16 KTh[2][DH * PH];  // [b][j] k 2^kap
-  __shared__ __attribute__((aligned(16))) _Float16 Xh[2][CW * PH];   // [c][j] X 2^(sig - 2 kap)
-  __shared__ f32x4 red[2][NW][2 * WAVE];  // per wave, in accumulator order
-  __shared__ float st_ecs[3][BLK];
+  // staging (by step parity, then block within the step) and partial-output
+  // buffers; e^{cs} rows rotate over three slots because the drain of step
+  // m-1 may still read them while step m+1 is staged
+  __shared__ __attribute__((aligned(16))) _Float16 Qh[2][2][BLK * PH];  // [i][perm b] q 2^tau
+  __shared__ __attribute__((aligned(16))) _Float16 KTh[2][2][DH * PH];  // [b][j] k 2^kap
+  __shared__ __attribute__((aligned(16))) _Float16 Xh[2][2][CW * PH];   // [c][j] X 2^(sig - 2 kap)
+  __shared__ f32x4 red[2][NW][4 * WAVE];  // per wave, in accumulator order (4 token tiles)
+  __shared__ float st_ecs[3][2][BLK];
 
   const int tid = threadIdx.x;
   // the wave index, provably uniform across the wave (scalar branches)
@@ -143,91 +145,109 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
     const int a = aw0 + 4 * qd, G = (a >> 2) & 3;
     qpos[qd] = (a & ~15) + 4 * (G == 1 ? 2 : (G == 2 ? 1 : G));
   }
-  const int64_t nblk = n_blocks(N);
-  const int64_t Np = nblk * BLK;  // partial rows per head (padded)
+  const int nblk = (int)n_blocks(N);
+  const int nstep = (nblk + 1) / 2;
+  const int64_t Np = o2_part_rows(N);  // partial rows per head (whole steps)
   const uint8_t* rec_h = rec + bh * nblk * (int64_t)REC_BYTES;
 
-  // ---- registers of the prefetched block -------------------------------------
-  uint4 pq[NI], pk[NI];
-  uint32_t px[NX];
+  // ---- registers of the prefetched step ---------------------------------------
+  // thread tid copies the 16-byte q / k^T segment tid of each block, the X^T
+  // word tid % 256 of block tid / 256 and the e^{cs} entry tid % 64 of block
+  // (tid / 64) % 2
+  // (named registers rather than arrays, which the compiler would place in
+  // memory)
+  uint4 pq0, pq1, pk0, pk1;
+  uint32_t px;
   uint32_t pe;
-  struct Blk {
-    int sig_in, tau;  // scale exponents of the entering state and of q
-    float eTs;        // decay and rescale factor of the state
-    uint32_t xf;      // two fp16 factors for X
-    int sig_out;      // scale exponent of the state after the block
+  struct Stp {
+    int sig_in;       // scale exponent of the state entering the step
+    int sig_out;      // ... after the step
+    float eTs;        // decay and rescale factor of the state over the step
+    int tau0, tau1;   // q scale exponents of the two blocks
+    uint32_t xf0, xf1;  // two fp16 factors for X of each block (0 for an empty block)
+    float epre0, epre1;  // decay from the start of the step to the start of each block
   };
-  Blk nx{}, cur{}, prv{};
-  auto prefetch = [&](int64_t blk) {
-    const uint8_t* R = rec_h + blk * (int64_t)REC_BYTES;
-#pragma unroll
-    for (int u = 0; u < NI; ++u) {
-      const int idx = tid + u * NT, r = idx >> 3, sg = idx & 7;
-      pq[u] = *reinterpret_cast<const uint4*>(R + REC_QH + (r * DH + sg * 8) * 2);
-      pk[u] = *reinterpret_cast<const uint4*>(R + REC_KT + (r * DH + sg * 8) * 2);
+  Stp nx{}, cur{}, prv{};
+  auto prefetch = [&](int st) {
+    const int b0 = 2 * st, b1 = 2 * st + 1 < nblk ? 2 * st + 1 : nblk - 1;
+    const uint8_t* R0 = rec_h + b0 * (int64_t)REC_BYTES;
+    const uint8_t* R1 = rec_h + b1 * (int64_t)REC_BYTES;
+    {
+      const int r = tid >> 3, sg = tid & 7;
+      pq0 = *reinterpret_cast<const uint4*>(R0 + REC_QH + (r * DH + sg * 8) * 2);
+      pk0 = *reinterpret_cast<const uint4*>(R0 + REC_KT + (r * DH + sg * 8) * 2);
+      pq1 = *reinterpret_cast<const uint4*>(R1 + REC_QH + (r * DH + sg * 8) * 2);
+      pk1 = *reinterpret_cast<const uint4*>(R1 + REC_KT + (r * DH + sg * 8) * 2);
     }
-#pragma unroll
-    for (int u = 0; u < NX; ++u) {
-      const int idx = (tid + u * NT) % NXW, xr = idx >> 5, xw = idx & 31;
-      px[u] = *reinterpret_cast<const uint32_t*>(R + REC_XT + ((c0 + xr) * DH + 2 * xw) * 2);
+    const int* sc0 = reinterpret_cast<const int*>(R0 + REC_SC);  // uniform addresses
+    const int* sc1 = reinterpret_cast<const int*>(R1 + REC_SC);
+    nx.sig_in = sc0[SC_SIG_IN];
+    nx.sig_out = sc0[SC_SIG_OUT];
+    nx.eTs = __int_as_float(sc0[SC_ETS]);
+    nx.tau0 = sc0[SC_TAU];
+    nx.tau1 = sc1[SC_TAU];
+    nx.xf0 = (uint32_t)sc0[SC_XF];
+    nx.xf1 = 2 * st + 1 < nblk ? (uint32_t)sc1[SC_XF] : 0u;  // an empty second block
+    nx.epre0 = __int_as_float(sc0[SC_EPRE]);
+    nx.epre1 = __int_as_float(sc1[SC_EPRE]);
+    {
+      const int hb = tid >> 8, idx = tid & (NXW - 1), xr = idx >> 5, xw = idx & 31;
+      const int b = 2 * st + hb < nblk ? 2 * st + hb : nblk - 1;
+      px = *reinterpret_cast<const uint32_t*>(rec_h + b * (int64_t)REC_BYTES + REC_XT +
+                                              ((c0 + xr) * DH + 2 * xw) * 2);
     }
-    pe = *reinterpret_cast<const uint32_t*>(R + REC_ECS + 4 * (tid & (BLK - 1)));
-    const int* sc = reinterpret_cast<const int*>(R + REC_SC);  // uniform address
-    nx.sig_in = sc[SC_SIG_IN];
-    nx.tau = sc[SC_TAU];
-    nx.eTs = __int_as_float(sc[SC_ETS]);
-    nx.xf = (uint32_t)sc[SC_XF];
-    nx.sig_out = sc[SC_SIG_OUT];
-  };
-
-  // copy the prefetched block blk into its LDS slot, X scaled to the state's
-  // scale (a block beyond the last one is copied into the slot no block
-  // reads any more)
-  auto stage = [&](int64_t blk) {
-    const int sl = (int)(blk & 1);
-#pragma unroll
-    for (int u = 0; u < NI; ++u) {
-      const int idx = tid + u * NT, r = idx >> 3, sg = idx & 7;
-      *reinterpret_cast<uint4*>(&Qh[sl][r * PH + sg * 8]) = pq[u];
-      *reinterpret_cast<uint4*>(&KTh[sl][r * PH + sg * 8]) = pk[u];
+    {
+      const int hb = (tid >> 6) & 1;
+      const int b = 2 * st + hb < nblk ? 2 * st + hb : nblk - 1;
+      pe = *reinterpret_cast<const uint32_t*>(rec_h + b * (int64_t)REC_BYTES + REC_ECS + 4 * (tid & (BLK - 1)));
     }
-    const f16x2 xf = __builtin_bit_cast(f16x2, nx.xf);
-#pragma unroll
-    for (int u = 0; u < NX; ++u) {
-      const int idx = tid + u * NT, xr = idx >> 5, xw = idx & 31;
-      if (NT * NX == NXW || idx < NXW) {
-        const f16x2 x = (__builtin_bit_cast(f16x2, px[u]) * xf[0]) * xf[1];
-        *reinterpret_cast<f16x2*>(&Xh[sl][xr * PH + 2 * xw]) = x;
-      }
-    }
-    st_ecs[blk % 3][tid & (BLK - 1)] = __uint_as_float(pe);
   };
 
-  // partial output of block blk (its scales in p) -> workspace, scaled to
-  // true units: e^{cs_i} 2^-(sig_in + 2 tau)
-  auto drain = [&](int64_t blk, const Blk& p) {
-    // two columns per thread, so that the first NT/2 threads share the work
-    constexpr int ND = BLK * CW / 2;
-    if (NT == ND || tid < ND) {
-      const int64_t t0 = blk * BLK;
-      const int i = tid / (CW / 2), c2 = (tid % (CW / 2)) * 2;
-      // element (i, c2..c2+1) sits in components c2%4.. of accumulator slot
-      // i/32 of lane i%32 + 32 (c2/4) of every wave
-      const int idx = (i >> 5) * WAVE + (i & 31) + 32 * (c2 >> 2);
-      const float* rb = reinterpret_cast<const float*>(&red[blk & 1][0][idx]) + (c2 & 3);
-      constexpr int WS = 2 * WAVE * 4;  // floats per wave
-      float s0 = rb[0], s1 = rb[1];
-#pragma unroll
-      for (int w = 1; w < NW; ++w) {
-        s0 += rb[w * WS];
-        s1 += rb[w * WS + 1];
-      }
-      const float f = st_ecs[blk % 3][i] * ldexpf(ldexpf(1.f, -p.sig_in), -2 * p.tau);
-      float2 o;
-      o.x = s0 * f;
-      o.y = s1 * f;
-      *reinterpret_cast<float2*>(&part[(((int64_t)pa * BH + bh) * Np + t0 + i) * DH + c0 + c2]) = o;
+  // copy the prefetched step st into its LDS slot, X scaled to the state's
+  // scale (a step beyond the last one is copied into the slot no step reads
+  // any more)
+  auto stage = [&](int st) {
+    const int sl = st & 1;
+    {
+      const int r = tid >> 3, sg = tid & 7;
+      *reinterpret_cast<uint4*>(&Qh[sl][0][r * PH + sg * 8]) = pq0;
+      *reinterpret_cast<uint4*>(&KTh[sl][0][r * PH + sg * 8]) = pk0;
+      *reinterpret_cast<uint4*>(&Qh[sl][1][r * PH + sg * 8]) = pq1;
+      *reinterpret_cast<uint4*>(&KTh[sl][1][r * PH + sg * 8]) = pk1;
     }
+    {
+      const int hb = tid >> 8, idx = tid & (NXW - 1), xr = idx >> 5, xw = idx & 31;
+      const f16x2 xf = __builtin_bit_cast(f16x2, hb ? nx.xf1 : nx.xf0);
+      const f16x2 x = (__builtin_bit_cast(f16x2, px) * xf[0]) * xf[1];
+      *reinterpret_cast<f16x2*>(&Xh[sl][hb][xr * PH + 2 * xw]) = x;
+    }
+    if (tid < 2 * BLK) st_ecs[st % 3][tid >> 6][tid & (BLK - 1)] = __uint_as_float(pe);
+  };
+
+  // partial outputs of step st (its scales in p) -> workspace, scaled to
+  // true units: e^{cs_i} epre 2^-(sig_in + 2 tau).  Thread tid handles block
+  // tid / 256, token (tid / 4) % 64 and columns 2 (tid % 4) .. + 1, which sit
+  // in components c2 % 4 .. of accumulator slot (token tile) of lane
+  // i % 32 + 32 (c2 / 4) of every wave.
+  auto drain = [&](int st, const Stp& p) {
+    const int hb = tid >> 8, i = (tid >> 2) & (BLK - 1), c2 = (tid & 3) * 2;
+    const int t = 2 * hb + (i >> 5);
+    const int idx = t * WAVE + (i & 31) + 32 * (c2 >> 2);
+    const float* rb = reinterpret_cast<const float*>(&red[st & 1][0][idx]) + (c2 & 3);
+    constexpr int WS = 4 * WAVE * 4;  // floats per wave
+    float s0 = rb[0], s1 = rb[1];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      s0 += rb[w * WS];
+      s1 += rb[w * WS + 1];
+    }
+    const float f = st_ecs[st % 3][hb][i] * (hb ? p.epre1 : p.epre0) *
+                    ldexpf(ldexpf(1.f, -p.sig_in), -2 * (hb ? p.tau1 : p.tau0));
+    float2 o;
+    o.x = s0 * f;
+    o.y = s1 * f;
+    const int64_t row = (int64_t)(2 * st + hb) * BLK + i;
+    *reinterpret_cast<float2*>(&part[(((int64_t)pa * BH + bh) * Np + row) * DH + c0 + c2]) = o;
   };
 
   // state: quad qd, b-tile bt (32 rows) -> 32 x 32 accumulator over
@@ -238,79 +258,72 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
   for (int p = 0; p < NQD; ++p)
 #pragma unroll
     for (int bt = 0; bt < 2; ++bt) S[p][bt] = f32x16{};
-  // fp16 copy of quad 0's state, made at the end of the previous block's
+  // fp16 copy of quad 0's state, made at the end of the previous step's
   // update so that the first output chain can start at once
   f16x8 SA0[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) SA0[kk] = f16x8{};
 
-  // MFMA work of block blk.  Output: T^T[(a, c)][i] = sum_b S[b][(a, c)]
-  // Q[i][b] over 16-row k-steps kk (b in 16 kk + {4h..4h+3, 8+4h..8+4h+3} on
-  // lane half h, matching the record's q column order), then
-  // Y[i][c] += sum_a q_ia T^T[(a, c)][i].  Update: S = eTs S + K^T ((k_:a
-  // 2^kap) * X 2^(sig - 2 kap)) over 16-token k-steps (tokens 16 kk + 8 h ..
-  // +7 on lane half h).
-  //
-  // A wave issues in order, so the VALU work (fp16 conversion of the state,
-  // decay, row scalings, update operands) is interleaved by hand with the
-  // MFMA chains: slot m holds one MFMA and the VALU work that is ready by
-  // then (results of a chain are used two or more slots after its last
-  // MFMA, LDS operands are read two to four slots ahead).  Scheduling
-  // barriers keep the compiler from regrouping the slots.
-  auto compute = [&](int64_t blk) {
-    const int sl = (int)(blk & 1);
-    const _Float16* Q = Qh[sl];
-    const _Float16* KT = KTh[sl];
-    const _Float16* XT = Xh[sl];
+  // MFMA work of step st.  Output over token tiles t (32 tokens: block t / 2,
+  // rows 32 (t % 2) ..): T^T[(a, c)][i] = sum_b S[b][(a, c)] Q[i][b] over
+  // 16-row k-steps kk (b in 16 kk + {4h..4h+3, 8+4h..8+4h+3} on lane half h,
+  // matching the record's q column order), then Y[i][c] += sum_a q_ia
+  // T^T[(a, c)][i].  Update: S = eTs S + sum over both blocks hb of K^T
+  // ((k_:a 2^kap) * X 2^(sig - 2 kap)) over 16-token k-steps (tokens 16 kk +
+  // 8 h .. +7 on lane half h).
+  auto compute = [&](int st) {
+    const int sl = st & 1;
     const float eT = cur.eTs;
 
     f16x8 SA1[4];          // fp16 copy of quad 1's state
-    f16x8 Qf[2][4];        // B operand of the output: Q^T[b][i], i = 32 it + n32
-    f16x4 qv[NQD][2];      // q values of the quad's a's for token 32 it + n32
-    f32x16 T[NQD][2];      // output chains (quad, it)
-    f32x4 Y[2] = {zero4(), zero4()};
-    f16x8 xh[4];           // X^T[c][j], c = n32 % 8
-    f16x8 Kr[NQD][4];      // K^T row of k_:a for the quad's a = aw0 + 4 qd + n32/8
-    f16x8 Bu[NQD][4];      // update B operand
-    f16x8 Kf[2][4];        // update A operand: K^T[b][j], b = 32 bt + n32
+    f16x8 Qf[4][4];        // B operand of the output: Q^T[b][i] of token tile t
+    f16x4 qv[NQD][4];      // q values of the quad's a's for the lane's token of tile t
+    f32x16 T[NQD][4];      // output chains (quad, token tile)
+    f32x4 Y[4] = {zero4(), zero4(), zero4(), zero4()};
+    f16x8 xh[2][4];        // X^T[c][j] of block hb, c = n32 % 8
+    f16x8 Kr[NQD][2][4];   // K^T row of k_:a of block hb for a = aw0 + 4 qd + n32/8
+    f16x8 Bu[NQD][2][4];   // update B operand
+    f16x8 Kf[2][2][4];     // update A operand: K^T[b][j] of block hb, b = 32 bt + n32
 
     auto SB = [] { __builtin_amdgcn_sched_barrier(0); };
-    auto rdQ = [&](int it) {
+    auto rdQ = [&](int t) {
+      const _Float16* Q = Qh[sl][t >> 1];
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        Qf[it][kk] = *reinterpret_cast<const f16x8*>(&Q[(it * 32 + n32) * PH + kk * 16 + 8 * h]);
+        Qf[t][kk] = *reinterpret_cast<const f16x8*>(&Q[((t & 1) * 32 + n32) * PH + kk * 16 + 8 * h]);
     };
-    auto rdK = [&](int bt) {
+    auto rdqv = [&](int t) {
+      const _Float16* Q = Qh[sl][t >> 1];
+#pragma unroll
+      for (int q = 0; q < NQD; ++q)
+        qv[q][t] = *reinterpret_cast<const f16x4*>(&Q[((t & 1) * 32 + n32) * PH + qpos[q]]);
+    };
+    auto rdK = [&](int bt, int hb) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        Kf[bt][kk] = *reinterpret_cast<const f16x8*>(&KT[(bt * 32 + n32) * PH + kk * 16 + 8 * h]);
+        Kf[hb][bt][kk] = *reinterpret_cast<const f16x8*>(&KTh[sl][hb][(bt * 32 + n32) * PH + kk * 16 + 8 * h]);
     };
-    auto rdX = [&] {
+    auto rdX = [&](int hb) {
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        xh[kk] = *reinterpret_cast<const f16x8*>(&XT[(n32 & 7) * PH + kk * 16 + 8 * h]);
+        xh[hb][kk] = *reinterpret_cast<const f16x8*>(&Xh[sl][hb][(n32 & 7) * PH + kk * 16 + 8 * h]);
     };
-    auto rdKr = [&](int q) {
+    auto rdKr = [&](int q, int hb) {
       const int a = aw0 + 4 * q + (n32 >> 3);
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        Kr[q][kk] = *reinterpret_cast<const f16x8*>(&KT[a * PH + kk * 16 + 8 * h]);
-    };
-    auto rdqv = [&] {
-#pragma unroll
-      for (int q = 0; q < NQD; ++q)
-#pragma unroll
-        for (int it = 0; it < 2; ++it)
-          qv[q][it] = *reinterpret_cast<const f16x4*>(&Q[(it * 32 + n32) * PH + qpos[q]]);
+        Kr[q][hb][kk] = *reinterpret_cast<const f16x8*>(&KTh[sl][hb][a * PH + kk * 16 + 8 * h]);
     };
     // MFMAs
-    auto out = [&](int q, int it, int kk, const f16x8* SA) {
-      T[q][it] = mfma32(SA[kk], Qf[it][kk], kk == 0 ? f32x16{} : T[q][it]);
+    auto out = [&](int q, int t, int kk, const f16x8* SA) {
+      T[q][t] = mfma32(SA[kk], Qf[t][kk], kk == 0 ? f32x16{} : T[q][t]);
     };
-    auto upd = [&](int q, int bt, int kk) { S[q][bt] = mfma32(Kf[bt][kk], Bu[q][kk], S[q][bt]); };
-    // VALU units (four instructions each)
-    // (the empty asm consumes the result in place, so that the conversion is
-    // not moved to the loop's end where its value is carried)
+    auto upd = [&](int q, int bt, int hb, int kk) {
+      S[q][bt] = mfma32(Kf[hb][bt][kk], Bu[q][hb][kk], S[q][bt]);
+    };
+    // VALU units (four instructions each); the empty asm consumes a
+    // conversion's result in place, so that it is not moved to the loop's
+    // end where its value is carried
     auto cvt = [&](f16x8* SA, int q, int kk) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) SA[kk][e] = (_Float16)S[q][kk >> 1][8 * (kk & 1) + e];
@@ -321,114 +334,159 @@ __global__ __launch_bounds__(NW * 64) void k_o2_state(const uint8_t* __restrict_
       for (int e = 0; e < 4; ++e) S[q][bt][4 * g + e] *= eT;
     };
     // rows 8 m + 4 h + s of T: quad member m, column 4 h + s
-    auto fy = [&](int q, int it, int m) {
-      const float qa = (float)qv[q][it][m];
+    auto fy = [&](int q, int t, int m) {
+      const float qa = (float)qv[q][t][m];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) Y[it][s] = fmaf(qa, T[q][it][4 * m + s], Y[it][s]);
+      for (int s = 0; s < 4; ++s) Y[t][s] = fmaf(qa, T[q][t][4 * m + s], Y[t][s]);
     };
-    auto bu = [&](int q, int kk) { Bu[q][kk] = Kr[q][kk] * xh[kk]; };
+    auto bu = [&](int q, int hb, int kk) { Bu[q][hb][kk] = Kr[q][hb][kk] * xh[hb][kk]; };
     auto wr = [&] {
 #pragma unroll
-      for (int it = 0; it < 2; ++it) red[sl][wave][it * WAVE + lane] = Y[it];
+      for (int t = 0; t < 4; ++t) red[sl][wave][t * WAVE + lane] = Y[t];
     };
 
     if constexpr (NQD == 2) {
-      // chains: C(q, it) = out over kk, U(q, bt) = upd over kk, in the order
-      // C00 C10 C01 C11 U00 U01 U10 U11
-      rdQ(0); rdqv(); cvt(SA1, 1, 0); cvt(SA1, 1, 1); SB();
-      out(0, 0, 0, SA0); cvt(SA1, 1, 2); rdQ(1); SB();
+      rdQ(0); rdqv(0); cvt(SA1, 1, 0); cvt(SA1, 1, 1); SB();
+      out(0, 0, 0, SA0); cvt(SA1, 1, 2); SB();
       out(0, 0, 1, SA0); cvt(SA1, 1, 3); mul(0, 0, 0); SB();
       out(0, 0, 2, SA0); mul(0, 0, 1); SB();
-      out(0, 0, 3, SA0); mul(0, 0, 2); mul(0, 0, 3); SB();
+      out(0, 0, 3, SA0); mul(0, 0, 2); mul(0, 0, 3); rdQ(1); SB();
       out(1, 0, 0, SA1); mul(0, 1, 0); SB();
-      out(1, 0, 1, SA1); mul(0, 1, 1); mul(0, 1, 2); SB();
-      out(1, 0, 2, SA1); mul(0, 1, 3); rdX(); SB();
-      out(1, 0, 3, SA1); fy(0, 0, 0); fy(0, 0, 1); SB();
-      out(0, 1, 0, SA0); fy(0, 0, 2); rdKr(0); SB();
-      out(0, 1, 1, SA0); fy(0, 0, 3); SB();
-      out(0, 1, 2, SA0); fy(1, 0, 0); fy(1, 0, 1); SB();
-      out(0, 1, 3, SA0); fy(1, 0, 2); SB();
-      out(1, 1, 0, SA1); fy(1, 0, 3); bu(0, 0); SB();
-      out(1, 1, 1, SA1); bu(0, 1); rdK(0); SB();
-      out(1, 1, 2, SA1); bu(0, 2); bu(0, 3); SB();
-      out(1, 1, 3, SA1); fy(0, 1, 0); SB();
-      upd(0, 0, 0); fy(0, 1, 1); fy(0, 1, 2); rdK(1); SB();
-      upd(0, 0, 1); fy(0, 1, 3); rdKr(1); SB();
-      upd(0, 0, 2); mul(1, 0, 0); mul(1, 0, 1); SB();
-      upd(0, 0, 3); mul(1, 0, 2); SB();
-      upd(0, 1, 0); mul(1, 0, 3); bu(1, 0); SB();
-      upd(0, 1, 1); bu(1, 1); SB();
-      upd(0, 1, 2); bu(1, 2); bu(1, 3); SB();
-      upd(0, 1, 3); fy(1, 1, 0); SB();
-      upd(1, 0, 0); fy(1, 1, 1); fy(1, 1, 2); SB();
-      upd(1, 0, 1); fy(1, 1, 3); SB();
-      upd(1, 0, 2); mul(1, 1, 0); mul(1, 1, 1); SB();
-      upd(1, 0, 3); mul(1, 1, 2); mul(1, 1, 3); SB();
-      upd(1, 1, 0); cvt(SA0, 0, 0); cvt(SA0, 0, 1); SB();
-      upd(1, 1, 1); cvt(SA0, 0, 2); SB();
-      upd(1, 1, 2); cvt(SA0, 0, 3); wr(); SB();
-      upd(1, 1, 3); SB();
+      out(1, 0, 1, SA1); mul(0, 1, 1); mul(0, 1, 2); rdqv(1); SB();
+      out(1, 0, 2, SA1); fy(0, 0, 0); SB();
+      out(1, 0, 3, SA1); fy(0, 0, 1); fy(0, 0, 2); SB();
+      out(0, 1, 0, SA0); fy(0, 0, 3); SB();
+      out(0, 1, 1, SA0); mul(0, 1, 3); mul(1, 0, 0); SB();
+      out(0, 1, 2, SA0); fy(1, 0, 0); SB();
+      out(0, 1, 3, SA0); fy(1, 0, 1); fy(1, 0, 2); rdQ(2); SB();
+      out(1, 1, 0, SA1); fy(1, 0, 3); SB();
+      out(1, 1, 1, SA1); mul(1, 0, 1); mul(1, 0, 2); rdqv(2); SB();
+      out(1, 1, 2, SA1); fy(0, 1, 0); SB();
+      out(1, 1, 3, SA1); fy(0, 1, 1); fy(0, 1, 2); SB();
+      out(0, 2, 0, SA0); fy(0, 1, 3); SB();
+      out(0, 2, 1, SA0); mul(1, 0, 3); mul(1, 1, 0); SB();
+      out(0, 2, 2, SA0); fy(1, 1, 0); SB();
+      out(0, 2, 3, SA0); fy(1, 1, 1); fy(1, 1, 2); rdQ(3); SB();
+      out(1, 2, 0, SA1); fy(1, 1, 3); SB();
+      out(1, 2, 1, SA1); mul(1, 1, 1); mul(1, 1, 2); rdqv(3); SB();
+      out(1, 2, 2, SA1); fy(0, 2, 0); SB();
+      out(1, 2, 3, SA1); fy(0, 2, 1); fy(0, 2, 2); SB();
+      out(0, 3, 0, SA0); fy(0, 2, 3); rdX(0); rdKr(0, 0); SB();
+      out(0, 3, 1, SA0); mul(1, 1, 3); SB();
+      out(0, 3, 2, SA0); fy(1, 2, 0); SB();
+      out(0, 3, 3, SA0); fy(1, 2, 1); fy(1, 2, 2); SB();
+      out(1, 3, 0, SA1); fy(1, 2, 3); rdK(0, 0); SB();
+      out(1, 3, 1, SA1); bu(0, 0, 0); bu(0, 0, 1); SB();
+      out(1, 3, 2, SA1); bu(0, 0, 2); SB();
+      out(1, 3, 3, SA1); bu(0, 0, 3); fy(0, 3, 0); SB();
+      upd(0, 0, 0, 0); fy(0, 3, 1); rdKr(1, 0); rdK(1, 0); SB();
+      upd(0, 0, 0, 1); fy(0, 3, 2); SB();
+      upd(0, 0, 0, 2); fy(0, 3, 3); SB();
+      upd(0, 0, 0, 3); fy(1, 3, 0); SB();
+      upd(0, 1, 0, 0); fy(1, 3, 1); SB();
+      upd(0, 1, 0, 1); fy(1, 3, 2); fy(1, 3, 3); SB();
+      upd(0, 1, 0, 2); bu(1, 0, 0); bu(1, 0, 1); wr(); SB();
+      upd(0, 1, 0, 3); bu(1, 0, 2); bu(1, 0, 3); SB();
+      upd(1, 0, 0, 0); rdX(1); rdKr(0, 1); SB();
+      upd(1, 0, 0, 1); SB();
+      upd(1, 0, 0, 2); rdK(0, 1); SB();
+      upd(1, 0, 0, 3); bu(0, 1, 0); SB();
+      upd(1, 1, 0, 0); bu(0, 1, 1); SB();
+      upd(1, 1, 0, 1); bu(0, 1, 2); SB();
+      upd(1, 1, 0, 2); bu(0, 1, 3); rdK(1, 1); SB();
+      upd(1, 1, 0, 3); SB();
+      upd(0, 0, 1, 0); rdKr(1, 1); SB();
+      upd(0, 0, 1, 1); SB();
+      upd(0, 0, 1, 2); SB();
+      upd(0, 0, 1, 3); bu(1, 1, 0); SB();
+      upd(0, 1, 1, 0); bu(1, 1, 1); SB();
+      upd(0, 1, 1, 1); bu(1, 1, 2); SB();
+      upd(0, 1, 1, 2); bu(1, 1, 3); SB();
+      upd(0, 1, 1, 3); cvt(SA0, 0, 0); SB();
+      upd(1, 0, 1, 0); cvt(SA0, 0, 1); SB();
+      upd(1, 0, 1, 1); SB();
+      upd(1, 0, 1, 2); cvt(SA0, 0, 2); SB();
+      upd(1, 0, 1, 3); cvt(SA0, 0, 3); SB();
+      upd(1, 1, 1, 0); SB();
+      upd(1, 1, 1, 1); SB();
+      upd(1, 1, 1, 2); SB();
+      upd(1, 1, 1, 3); SB();
     } else {
-      // chains C00 C01 U00 U01
-      rdQ(0); rdqv(); SB();
+      rdQ(0); rdqv(0); SB();
       out(0, 0, 0, SA0); mul(0, 0, 0); rdQ(1); SB();
-      out(0, 0, 1, SA0); mul(0, 0, 1); mul(0, 0, 2); SB();
-      out(0, 0, 2, SA0); mul(0, 0, 3); rdX(); rdKr(0); SB();
-      out(0, 0, 3, SA0); mul(0, 1, 0); mul(0, 1, 1); SB();
-      out(0, 1, 0, SA0); mul(0, 1, 2); rdK(0); SB();
-      out(0, 1, 1, SA0); mul(0, 1, 3); bu(0, 0); SB();
-      out(0, 1, 2, SA0); bu(0, 1); bu(0, 2); rdK(1); SB();
-      out(0, 1, 3, SA0); bu(0, 3); fy(0, 0, 0); SB();
-      upd(0, 0, 0); fy(0, 0, 1); fy(0, 0, 2); SB();
-      upd(0, 0, 1); fy(0, 0, 3); SB();
-      upd(0, 0, 2); fy(0, 1, 0); fy(0, 1, 1); SB();
-      upd(0, 0, 3); fy(0, 1, 2); SB();
-      upd(0, 1, 0); fy(0, 1, 3); SB();
-      upd(0, 1, 1); SB();
-      upd(0, 1, 2); cvt(SA0, 0, 0); cvt(SA0, 0, 1); wr(); SB();
-      upd(0, 1, 3); SB();
+      out(0, 0, 1, SA0); mul(0, 0, 1); rdqv(1); SB();
+      out(0, 0, 2, SA0); mul(0, 0, 2); SB();
+      out(0, 0, 3, SA0); mul(0, 0, 3); rdQ(2); SB();
+      out(0, 1, 0, SA0); mul(0, 1, 0); SB();
+      out(0, 1, 1, SA0); mul(0, 1, 1); rdqv(2); SB();
+      out(0, 1, 2, SA0); fy(0, 0, 0); SB();
+      out(0, 1, 3, SA0); fy(0, 0, 1); rdQ(3); SB();
+      out(0, 2, 0, SA0); fy(0, 0, 2); rdX(0); rdKr(0, 0); SB();
+      out(0, 2, 1, SA0); fy(0, 0, 3); rdqv(3); SB();
+      out(0, 2, 2, SA0); fy(0, 1, 0); SB();
+      out(0, 2, 3, SA0); bu(0, 0, 0); SB();
+      out(0, 3, 0, SA0); bu(0, 0, 1); rdK(0, 0); SB();
+      out(0, 3, 1, SA0); bu(0, 0, 2); SB();
+      out(0, 3, 2, SA0); bu(0, 0, 3); SB();
+      out(0, 3, 3, SA0); fy(0, 1, 1); SB();
+      upd(0, 0, 0, 0); fy(0, 1, 2); rdX(1); rdKr(0, 1); rdK(1, 0); SB();
+      upd(0, 0, 0, 1); fy(0, 1, 3); SB();
+      upd(0, 0, 0, 2); mul(0, 1, 2); rdK(0, 1); SB();
+      upd(0, 0, 0, 3); mul(0, 1, 3); SB();
+      upd(0, 1, 0, 0); fy(0, 2, 0); fy(0, 2, 1); SB();
+      upd(0, 1, 0, 1); fy(0, 2, 2); fy(0, 2, 3); SB();
+      upd(0, 1, 0, 2); bu(0, 1, 0); bu(0, 1, 1); rdK(1, 1); SB();
+      upd(0, 1, 0, 3); bu(0, 1, 2); bu(0, 1, 3); SB();
+      upd(0, 0, 1, 0); fy(0, 3, 0); fy(0, 3, 1); SB();
+      upd(0, 0, 1, 1); fy(0, 3, 2); fy(0, 3, 3); SB();
+      upd(0, 0, 1, 2); wr(); SB();
+      upd(0, 0, 1, 3); SB();
+      upd(0, 1, 1, 0); SB();
+      upd(0, 1, 1, 1); SB();
+      upd(0, 1, 1, 2); cvt(SA0, 0, 0); SB();
+      upd(0, 1, 1, 3); cvt(SA0, 0, 1); SB();
       cvt(SA0, 0, 2); cvt(SA0, 0, 3); SB();
     }
   };
 
-  // prologue: stage block 0, prefetch block 1
+  // prologue: stage step 0, prefetch step 1
   prefetch(0);
   stage(0);
   cur = nx;
-  prefetch(nblk > 1 ? 1 : 0);
+  prefetch(nstep > 1 ? 1 : 0);
   __syncthreads();
 
-  // Per block n: MFMA work of n, drain of n-1, staging of n+1, loads of n+2,
+  // Per step m: MFMA work of m, drain of m-1, staging of m+1, loads of m+2,
   // one barrier.  With two waves per SIMD the first four waves run the MFMA
   // work first and the other four the bookkeeping first; each group has a
   // loop of its own (every wave passes the same barriers), so the loads of a
-  // block have a single destination and are waited for only where the staging
-  // consumes them.  The loads for block n+2 are issued right after the
-  // registers are free, a whole block ahead of their use.
-  if (!STAGGER || wave < NW / 2) {
-    for (int64_t blk = 0; blk < nblk; ++blk) {
-      const Blk nxt = nx;  // scales of block blk + 1 (prefetched)
-      compute(blk);
-      if (blk > 0) drain(blk - 1, prv);
-      stage(blk + 1);
-      prefetch(blk + 2 < nblk ? blk + 2 : nblk - 1);
+  // step have a single destination and are waited for only where the staging
+  // consumes them.  The loads for step m+2 are issued right after the
+  // registers are free, a whole step ahead of their use.
+  if (wave < NW / 2) {
+    for (int st = 0; st < nstep; ++st) {
+      const Stp nxt = nx;  // scales of step st + 1 (prefetched)
+      compute(st);
+      if (st > 0) drain(st - 1, prv);
+      stage(st + 1);
+      prefetch(st + 2 < nstep ? st + 2 : nstep - 1);
       prv = cur;
       cur = nxt;
       __syncthreads();
     }
   } else {
-    for (int64_t blk = 0; blk < nblk; ++blk) {
-      const Blk nxt = nx;
-      if (blk > 0) drain(blk - 1, prv);
-      stage(blk + 1);
-      prefetch(blk + 2 < nblk ? blk + 2 : nblk - 1);
-      compute(blk);
+    for (int st = 0; st < nstep; ++st) {
+      const Stp nxt = nx;
+      if (st > 0) drain(st - 1, prv);
+      stage(st + 1);
+      prefetch(st + 2 < nstep ? st + 2 : nstep - 1);
+      compute(st);
       prv = cur;
       cur = nxt;
       __syncthreads();
     }
   }
-  drain(nblk - 1, prv);
+  drain(nstep - 1, prv);
 
   if (final_state) {
     const float f = ldexpf(1.f, -prv.sig_out);

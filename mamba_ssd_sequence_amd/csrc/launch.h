@@ -19,6 +19,11 @@ inline int o2_aw(int64_t BH) { return BH >= 32 ? 8 : 4; }
 inline int o2_sl(int64_t BH) { return 8 * o2_aw(BH); }
 inline int o2_pa(int64_t BH) { return 64 / o2_sl(BH); }
 
+// The order-2 numerator state scan advances over steps of two blocks
+// (2m, 2m+1); a last step without partner gets an empty second block.
+// Partial-output rows per head are padded to whole steps.
+__host__ __device__ inline int64_t o2_part_rows(int64_t N) { return (n_blocks(N) + 1) / 2 * 2 * 64; }
+
 // Order-2 per-block operand record (bytes), written by the block-prep kernel
 // and read by the state scan:
 //   QH  [64 i][64]   fp16 q_ib 2^tau; within each 16-column group the 4-column
@@ -26,17 +31,23 @@ inline int o2_pa(int64_t BH) { return 64 / o2_sl(BH); }
 //                    which the permuted-k 32x32 MFMA operand reads them)
 //   KT  [64 b][64 j] fp16 k_jb 2^kap (transposed)
 //   XT  [64 c][64 j] fp16 X_jc 2^xi, X_jc = w_j dt_j v_jc, w_j = e^{T - cs_j}
+//                    for the second block of a step; the first block weights
+//                    its tokens to the end of the step, w_j = e^{T + T' - cs_j}
+//                    with T' the decay total of the second block
 //   ECS [64]         fp32 e^{cs_i} (decay from the block start to token i)
 //   SC  [12 words]   written by the block-prep kernel: fp32 T, fp32 delta
-//                    (bound of any |state increment|), int32 tau, kap, xi,
-//                    fp32 e^T; then by the scale scan: int32 sig_in (scale
-//                    exponent of the state entering the block), fp32 eTs
-//                    (e^T 2^(sig_out - sig_in), the factor that decays and
-//                    rescales the state), two fp16 factors taking X 2^xi to
-//                    X 2^(sig_out - 2 kap), int32 sig_out
+//                    (bound of any |entry| of the block's share of the step's
+//                    state increment), int32 tau, kap, xi, fp32 e^T; then by
+//                    the scale scan, for the step the block belongs to: int32
+//                    sig_in (scale exponent of the state entering the step),
+//                    fp32 eTs (e^{T_2m + T_2m+1} 2^(sig_out - sig_in), the
+//                    factor that decays and rescales the state), two fp16
+//                    factors taking X 2^xi to X 2^(sig_out - 2 kap), int32
+//                    sig_out, fp32 epre (decay from the start of the step to
+//                    the start of the block: 1 or e^{T_2m})
 constexpr int REC_QH = 0, REC_KT = 8192, REC_XT = 16384, REC_ECS = 24576, REC_SC = 24832;
 constexpr int SC_T = 0, SC_DELTA = 1, SC_TAU = 2, SC_KAP = 3, SC_XI = 4, SC_ET = 5, SC_SIG_IN = 6,
-              SC_ETS = 7, SC_XF = 8, SC_SIG_OUT = 9;
+              SC_ETS = 7, SC_XF = 8, SC_SIG_OUT = 9, SC_EPRE = 10;
 constexpr int REC_BYTES = 24880;
 
 // Workspace layout (float offsets), in this order:
@@ -44,9 +55,9 @@ constexpr int REC_BYTES = 24880;
 //   state  [BH, nblk, DH*DH + DH]     per-block state contributions, then
 //                                     (in place) the state entering each block
 //                                     (order 1: S and z; order 2: Z and unused)
-//   part   [P_a, BH, nblk*64, 64]     order 2 only: inter-block numerator
-//                                     partials of each a-slice (rows padded
-//                                     to whole blocks)
+//   part   [P_a, BH, rows, 64]        order 2 only: inter-block numerator
+//                                     partials of each a-slice (rows =
+//                                     o2_part_rows(N), padded to whole steps)
 //   rec    [BH, nblk] x REC_BYTES     order 2 only: operand records
 struct WsLayout {
   size_t tb, state, part, rec, total_floats;
@@ -62,7 +73,7 @@ inline WsLayout ws_layout(int64_t B, int64_t H, int64_t N, int64_t DH, int order
   off += (size_t)(BH * nb) * (size_t)(DH * DH + DH);
   off = (off + 63) & ~(size_t)63;
   L.part = off;
-  if (order == 2) off += (size_t)o2_pa(BH) * (size_t)BH * (size_t)(nb * 64) * 64;
+  if (order == 2) off += (size_t)o2_pa(BH) * (size_t)BH * (size_t)o2_part_rows(N) * 64;
   off = (off + 63) & ~(size_t)63;
   L.rec = off;
   if (order == 2) off += (size_t)(BH * nb) * (REC_BYTES / 4);

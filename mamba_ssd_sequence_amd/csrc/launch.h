@@ -10,14 +10,13 @@ namespace ssd {
 // Forward work is organised in blocks of 64 tokens.
 __host__ __device__ inline int64_t n_blocks(int64_t N) { return (N + 63) / 64; }
 
-// Order-2 state kernel (8 waves per workgroup, one a group each, all on the
-// workgroup's 8 value columns): a values per wave (AW, in quads) and per
-// workgroup (SL = 8 AW), and the resulting number of a-slices per head
-// (P_a = 64 / SL).  Fewer heads -> thinner slices so that the grid still
-// covers the chip.
-inline int o2_aw(int64_t BH) { return BH >= 32 ? 8 : 4; }
-inline int o2_sl(int64_t BH) { return 8 * o2_aw(BH); }
-inline int o2_pa(int64_t BH) { return 64 / o2_sl(BH); }
+// Order-2 state kernel (8 waves per workgroup): a-tiles of 32 values of a
+// per wave, 2 (one value column per wave, 8 columns per workgroup) with
+// >= 32 heads, else 1 (two waves per column, 4 columns per workgroup), so that
+// the grid still covers the chip.  A workgroup holds all 64 values of a, so
+// there is one partial-output slice per head.
+inline int o2_nat(int64_t BH) { return BH >= 32 ? 2 : 1; }
+inline int o2_pa(int64_t) { return 1; }
 
 // The order-2 numerator state scan advances over steps of two blocks
 // (2m, 2m+1); a last step without partner gets an empty second block.

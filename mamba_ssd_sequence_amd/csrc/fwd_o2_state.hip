@@ -52,12 +52,12 @@
 // costs nothing; all scalars come precomputed in the block records.
 //
 // Pipeline, one barrier per step m: write step m-1's outputs (LDS) to the
-// workspace; copy step m+1's two records (prefetched into registers one
-// iteration earlier) into the other LDS slot; issue the loads of step m+2 at
-// once, so they have a whole step to arrive; run step m's MFMA work and
-// write its outputs to LDS.  Half of the waves do the MFMA work first and
-// the other half last, so every SIMD keeps its matrix core busy while the
-// other wave does the bookkeeping.  Within the MFMA work the VALU operations
+// workspace (compute-first waves only); copy step m+1's two records
+// (prefetched into registers one iteration earlier) into the other LDS slot;
+// issue the loads of step m+2 at once, so they have a whole step to arrive;
+// run step m's MFMA work and write its outputs to LDS.  Half of the waves do
+// the MFMA work first and the other half last, so every SIMD keeps its
+// matrix core busy while the other wave does the bookkeeping.  Within the MFMA work the VALU operations
 // are placed by hand between the MFMAs (a wave issues in order, so VALU work
 // that waits on a chain's result would otherwise leave the matrix core
 // idle): slot m holds one MFMA and the VALU work that is ready by then (a
@@ -202,23 +202,27 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
   };
 
   // outputs of step st (its scales in p) -> workspace, scaled to true units:
-  // e^{cs_i} epre 2^-(sig_in + 2 tau).  Thread tid handles block tid / 256,
-  // token (tid / 4) % 64 and, with eight columns per workgroup, the columns
-  // 2 (tid % 4) .. + 1; with four, column tid % 4 (the sum of its two a-half
-  // waves).
+  // e^{cs_i} epre 2^-(sig_in + 2 tau).  Only the compute-first waves write
+  // outputs (their bookkeeping is off the critical path); thread tid < 256
+  // handles, for both blocks, token tid / 4 and, with eight columns per
+  // workgroup, the columns 2 (tid % 4) .. + 1; with four, column tid % 4 (the
+  // sum of its two a-half waves).
   auto drain = [&](int st, const Stp& p) {
-    const int hb = tid >> 8, i = (tid >> 2) & (BLK - 1), q4 = tid & 3;
-    const float* yr = &yo[st & 1][hb][i * RP];
-    const float f = st_ecs[st % 3][hb][i] * (hb ? p.epre1 : p.epre0) *
-                    ldexpf(ldexpf(1.f, -p.sig_in), -2 * (hb ? p.tau1 : p.tau0));
-    float* dst = &part[(bh * Np + (int64_t)(2 * st + hb) * BLK + i) * DH + c0];
-    if constexpr (NAT == 2) {
-      float2 o;
-      o.x = yr[2 * q4] * f;
-      o.y = yr[2 * q4 + 1] * f;
-      *reinterpret_cast<float2*>(dst + 2 * q4) = o;
-    } else {
-      dst[q4] = (yr[2 * q4] + yr[2 * q4 + 1]) * f;
+    const int i = (tid >> 2) & (BLK - 1), q4 = tid & 3;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const float* yr = &yo[st & 1][hb][i * RP];
+      const float f = st_ecs[st % 3][hb][i] * (hb ? p.epre1 : p.epre0) *
+                      ldexpf(ldexpf(1.f, -p.sig_in), -2 * (hb ? p.tau1 : p.tau0));
+      float* dst = &part[(bh * Np + (int64_t)(2 * st + hb) * BLK + i) * DH + c0];
+      if constexpr (NAT == 2) {
+        float2 o;
+        o.x = yr[2 * q4] * f;
+        o.y = yr[2 * q4 + 1] * f;
+        *reinterpret_cast<float2*>(dst + 2 * q4) = o;
+      } else {
+        dst[q4] = (yr[2 * q4] + yr[2 * q4 + 1]) * f;
+      }
     }
   };
 
@@ -421,8 +425,8 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
   prefetch(nstep > 1 ? 1 : 0);
   __syncthreads();
 
-  // Per step m: MFMA work of m, write-out of m-1, staging of m+1, loads of
-  // m+2, one barrier.  With two waves per SIMD the first four waves run the
+  // Per step m: MFMA work of m, write-out of m-1 (compute-first waves),
+  // staging of m+1, loads of m+2, one barrier.  With two waves per SIMD the first four waves run the
   // MFMA work first and the other four the bookkeeping first; each group has
   // a loop of its own (every wave passes the same barriers), so the loads of
   // a step have a single destination and are waited for only where the
@@ -442,7 +446,6 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
   } else {
     for (int st = 0; st < nstep; ++st) {
       const Stp nxt = nx;
-      if (st > 0) drain(st - 1, prv);
       stage(st + 1);
       prefetch(st + 2 < nstep ? st + 2 : nstep - 1);
       compute(st, std::integral_constant<int, NAT == 2 ? 0 : 1>{});
@@ -451,7 +454,7 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
       __syncthreads();
     }
   }
-  drain(nstep - 1, prv);
+  if (wave < NW / 2) drain(nstep - 1, prv);
 
   if (final_state) {
     const float f = ldexpf(1.f, -prv.sig_out);

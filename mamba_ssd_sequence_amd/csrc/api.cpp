@@ -216,8 +216,8 @@ ssd_status ssd_forward(const void* q, const void* k, const void* v, const float*
       return hip_status(e, "output launch");
     }
     // order 2: per-block preparation (normaliser contributions Z_blk and the
-    // numerator operand records), the scale scan and the Z scan, the on-chip
-    // numerator scan, and the output kernel.
+    // numerator operand records), the scale scan, the on-chip numerator scan
+    // (which also scans Z), and the output kernel.
     float* part = ws + L.part;
     void* rec = ws + L.rec;
     if ((e = ssd::launch_o2_blockprep(q, k, v, dt, a_cs, BH, N, chunk, tb, st, rec, stream)) != hipSuccess)
@@ -225,10 +225,8 @@ ssd_status ssd_forward(const void* q, const void* k, const void* v, const float*
     tm.mark();
     if ((e = ssd::launch_o2_scale_scan(rec, BH, N, stream)) != hipSuccess)
       return hip_status(e, "o2_scale_scan launch");
-    if ((e = ssd::launch_state_pass(64, BH, N, tb, st, final_norm, nullptr, stream)) != hipSuccess)
-      return hip_status(e, "state_pass launch");
     tm.mark();
-    if ((e = ssd::launch_o2_state(rec, BH, N, part, final_state, stream)) != hipSuccess)
+    if ((e = ssd::launch_o2_state(rec, BH, N, part, final_state, st, final_norm, stream)) != hipSuccess)
       return hip_status(e, "o2_state launch");
     tm.mark();
     e = ssd::launch_output(true, 64, 2, q, k, v, dt, a_cs, BH, N, chunk, st, part, ssd::o2_pa(BH), y, den, stream);

@@ -96,13 +96,17 @@ template <int NAT>
 __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ rec, int64_t BH,
                                                   int64_t N, int xcd_map,
                                                   float* __restrict__ part,
-                                                  float* __restrict__ final_state) {
+                                                  float* __restrict__ final_state,
+                                                  float* __restrict__ zst,
+                                                  float* __restrict__ final_norm) {
   constexpr int NW = 8, NT = NW * WAVE;  // waves, threads
   constexpr int CWG = NW * NAT / 2;      // value columns per workgroup
   constexpr int NCS = DH / CWG;          // column slices per head
   constexpr int NXW = CWG * DH / 2;      // 32-bit X^T words per block
   static_assert(NAT == 1 || NAT == 2, "one or two a-tiles per wave");
+  constexpr int ZE = DH * DH / NCS / (NT / 2);  // normaliser entries per compute-first thread
   static_assert(BLK * DH / 8 == NT && 2 * NXW <= NT, "thread mapping");
+  static_assert(ZE * NCS * (NT / 2) == DH * DH && (ZE == 1 || ZE == 2), "normaliser mapping");
 
   // staging (by step parity, then block within the step), outputs, and the
   // e^{cs} rows (over three slots, because the write-out of step m-1 may
@@ -112,6 +116,7 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
   __shared__ __attribute__((aligned(16))) _Float16 Xh[2][2][CWG * PH];  // [c][j] X 2^(sig - 2 kap)
   __shared__ float yo[2][2][BLK * RP];                                  // [i][wave] outputs
   __shared__ float st_ecs[3][2][BLK];
+  __shared__ float zrun[NT / 2][ZE];  // running normaliser state (compute-first threads)
 
   const int tid = threadIdx.x;
   // the wave index, provably uniform across the wave (scalar branches)
@@ -224,6 +229,52 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
         dst[q4] = (yr[2 * q4] + yr[2 * q4 + 1]) * f;
       }
     }
+  };
+
+  // normaliser state Z = sum_j w_j k_j k_j^T (2Mamba2Furious, Algorithm 6:
+  // the denominator q_i^T Z q_i), scanned over the blocks in place: the slot
+  // of block b holds Z_blk(b) (from the block-prep kernel) and receives Z
+  // entering b, Z_in(b + 1) = e^{T_b} Z_in(b) + Z_blk(b).  Each workgroup
+  // scans its 1 / NCS share of the d_h^2 entries, ZE per compute-first thread,
+  // in the slack of those threads' bookkeeping: the loads are issued after
+  // their MFMA work and consumed before the barrier, so no register is held
+  // across the MFMA work; the running sums stay in LDS.
+  constexpr int64_t ZS = DH * DH + DH;  // floats per block slot
+  float* zp = zst + bh * nblk * ZS + pc * (DH * DH / NCS) + tid * ZE;
+  float2 zd0{}, zd1{};
+  float zT0 = 0.f, zT1 = 0.f;
+  auto zload = [&](int st) {
+    const int b0 = 2 * st, b1 = 2 * st + 1;
+    zT0 = __int_as_float(reinterpret_cast<const int*>(rec_h + b0 * (int64_t)REC_BYTES + REC_SC)[SC_ET]);
+    if constexpr (ZE == 2) zd0 = *reinterpret_cast<const float2*>(zp + b0 * ZS);
+    else zd0.x = zp[b0 * ZS];
+    if (b1 < nblk) {
+      zT1 = __int_as_float(reinterpret_cast<const int*>(rec_h + b1 * (int64_t)REC_BYTES + REC_SC)[SC_ET]);
+      if constexpr (ZE == 2) zd1 = *reinterpret_cast<const float2*>(zp + b1 * ZS);
+      else zd1.x = zp[b1 * ZS];
+    }
+  };
+  auto zscan = [&](int st) {
+    const int b0 = 2 * st, b1 = 2 * st + 1;
+    float2 s{}, s1{}, s2{};
+    s.x = zrun[tid][0];
+    if constexpr (ZE == 2) s.y = zrun[tid][1];
+    s1.x = zT0 * s.x + zd0.x;
+    s1.y = zT0 * s.y + zd0.y;
+    s2 = s1;
+    if (b1 < nblk) {
+      s2.x = zT1 * s1.x + zd1.x;
+      s2.y = zT1 * s1.y + zd1.y;
+    }
+    if constexpr (ZE == 2) {
+      *reinterpret_cast<float2*>(zp + b0 * ZS) = s;
+      if (b1 < nblk) *reinterpret_cast<float2*>(zp + b1 * ZS) = s1;
+    } else {
+      zp[b0 * ZS] = s.x;
+      if (b1 < nblk) zp[b1 * ZS] = s1.x;
+    }
+    zrun[tid][0] = s2.x;
+    if constexpr (ZE == 2) zrun[tid][1] = s2.y;
   };
 
   // state: a-tile at (32 values of a), b-tile bt -> 32 x 32 accumulator over
@@ -423,6 +474,12 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
   stage(0);
   cur = nx;
   prefetch(nstep > 1 ? 1 : 0);
+  if (wave < NW / 2) {
+#pragma unroll
+    for (int e = 0; e < ZE; ++e) zrun[tid][e] = 0.f;
+    zload(0);
+    zscan(0);
+  }
   __syncthreads();
 
   // Per step m: MFMA work of m, write-out of m-1 (compute-first waves),
@@ -436,9 +493,12 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
     for (int st = 0; st < nstep; ++st) {
       const Stp nxt = nx;  // scales of step st + 1 (prefetched)
       compute(st, std::integral_constant<int, 0>{});
+      const bool zs = st + 1 < nstep;
+      if (zs) zload(st + 1);
       if (st > 0) drain(st - 1, prv);
       stage(st + 1);
       prefetch(st + 2 < nstep ? st + 2 : nstep - 1);
+      if (zs) zscan(st + 1);
       prv = cur;
       cur = nxt;
       __syncthreads();
@@ -454,7 +514,14 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
       __syncthreads();
     }
   }
-  if (wave < NW / 2) drain(nstep - 1, prv);
+  if (wave < NW / 2) {
+    drain(nstep - 1, prv);
+    if (final_norm) {
+      float* fz = final_norm + bh * DH * DH + pc * (DH * DH / NCS) + tid * ZE;
+#pragma unroll
+      for (int e = 0; e < ZE; ++e) fz[e] = zrun[tid][e];
+    }
+  }
 
   if (final_state) {
     const float f = ldexpf(1.f, -prv.sig_out);
@@ -474,13 +541,14 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
 }
 
 hipError_t launch_o2_state(const void* rec, int64_t BH, int64_t N, float* part,
-                           float* final_state, hipStream_t stream) {
+                           float* final_state, float* zstate, float* final_norm,
+                           hipStream_t stream) {
   const int xcd_map = (BH % 8) == 0;
   const uint8_t* r = static_cast<const uint8_t*>(rec);
   if (o2_nat(BH) == 2)
-    hipLaunchKernelGGL((k_o2_state<2>), dim3((unsigned)(BH * 8)), dim3(512), 0, stream, r, BH, N, xcd_map, part, final_state);
+    hipLaunchKernelGGL((k_o2_state<2>), dim3((unsigned)(BH * 8)), dim3(512), 0, stream, r, BH, N, xcd_map, part, final_state, zstate, final_norm);
   else
-    hipLaunchKernelGGL((k_o2_state<1>), dim3((unsigned)(BH * 16)), dim3(512), 0, stream, r, BH, N, xcd_map, part, final_state);
+    hipLaunchKernelGGL((k_o2_state<1>), dim3((unsigned)(BH * 16)), dim3(512), 0, stream, r, BH, N, xcd_map, part, final_state, zstate, final_norm);
   return hipGetLastError();
 }
 

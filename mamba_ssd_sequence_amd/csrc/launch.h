@@ -112,8 +112,12 @@ hipError_t launch_o2_blockprep(const void* q, const void* k, const void* v, cons
 hipError_t launch_o2_scale_scan(void* rec, int64_t BH, int64_t N, hipStream_t stream);
 
 // Order-2 inter-block numerator: on-chip state scan over the block records.
+// The same kernel scans the normaliser state in place over the per-block
+// slots of `zstate` (Z_blk -> Z entering the block, as launch_state_pass) and
+// writes the final Z to final_norm (if not NULL).
 hipError_t launch_o2_state(const void* rec, int64_t BH, int64_t N, float* part,
-                           float* final_state, hipStream_t stream);
+                           float* final_state, float* zstate, float* final_norm,
+                           hipStream_t stream);
 
 hipError_t launch_decode(bool bf16, int64_t DH, int order, const void* q, const void* k,
                          const void* v, const float* dt_proj, const float* dt_bias,

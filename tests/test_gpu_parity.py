@@ -140,11 +140,14 @@ def test_chunk_size_invariance(name):
     assert row_error(b["y"], ref["y"], ref["scale"]) <= TOL[cfg.dtype]
 
 
-@pytest.mark.parametrize("name", ["o1_f32_small", "o1_bf16_2k", "o2_bf16_4k"])
-def test_final_state_matches_recurrence(name):
+# (B, H, N): at order 2, 2 heads use the two-wave-per-column state layout and
+# 32 heads the one-wave layout; N = 300 ends on a step with one block
+@pytest.mark.parametrize("name,B,H,N", [("o1_f32_small", 1, 2, 200), ("o1_bf16_2k", 1, 2, 200),
+                                        ("o2_bf16_4k", 1, 2, 200), ("o2_bf16_4k", 2, 16, 300)])
+def test_final_state_matches_recurrence(name, B, H, N):
     cfg = I.CONFIGS[name]
-    N = 200
-    inp = I.make_forward_inputs(cfg, B=1, H=2, N=N, seed=11)
+    say("final state", name, B, H, N)
+    inp = I.make_forward_inputs(cfg, B=B, H=H, N=N, seed=11)
     got = run_forward(inp, cfg.order, cfg.chunk, want_final=True)
     q, k, v = inp.qkv_f64()
     dt, a = O.discretise(inp.dt_proj, inp.dt_bias, inp.A_log)

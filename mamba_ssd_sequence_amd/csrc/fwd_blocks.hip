@@ -250,16 +250,80 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
   const int64_t row = bh * N;
   const int tid = threadIdx.x;
 
+  // Every global read of the block is issued here, before the first barrier,
+  // so that a block costs one memory round trip: the block's cumsum and dt,
+  // q / k / v (bf16), the entering state, and at order 2 the inter-block
+  // partials of this thread's query row and the partner block (below).
   const float base = (t0 % chunk == 0) ? 0.f : a_cs[row + t0 - 1];
-  if (tid < BLK) {
-    float c = 0.f, d = 0.f;
-    if (tid < nvalid) {
-      c = a_cs[row + t0 + tid] - base;
-      d = dt ? dt[row + t0 + tid] : 1.f;
-    }
-    csl[tid] = c;
-    dtv[tid] = d;
+  float c_own = 0.f, d_own = 0.f;
+  if (tid < nvalid) {  // tid < BLK
+    c_own = a_cs[row + t0 + tid] - base;
+    d_own = dt ? dt[row + t0 + tid] : 1.f;
   }
+  const int it = tid / WAVE, lane = tid & (WAVE - 1), n = lane & 15, g = lane >> 4;
+  const int il = it * 16 + n;  // this lane's query row within the block
+
+  // bf16: q and k rows as 16-byte segments (segment e % SEG of row e / SEG
+  // for e = tid, tid + 256), v as the same segment of the token pair
+  // 2 (tid / SEG), + 1, with the two tokens' dt
+  constexpr int SEG = DH / 8;
+  constexpr int NQ = BF ? BLK * SEG / 256 : 1;
+  static_assert(!BF || ((NQ == 1 || NQ == 2) && (BLK / 2) * SEG <= 256), "segment mapping");
+  uint4 gq0 = make_uint4(0, 0, 0, 0), gk0 = gq0, gq1 = gq0, gk1 = gq0, gv0 = gq0, gv1 = gq0;
+  float gd0 = 0.f, gd1 = 0.f;
+  if constexpr (BF) {
+    const uint16_t* qb = static_cast<const uint16_t*>(qp) + (row + t0) * DH;
+    const uint16_t* kb = static_cast<const uint16_t*>(kp) + (row + t0) * DH;
+    const uint16_t* vb = static_cast<const uint16_t*>(vp) + (row + t0) * DH;
+    {
+      const int j = tid / SEG, sg = tid % SEG;
+      if (j < nvalid) {
+        gq0 = *reinterpret_cast<const uint4*>(qb + j * DH + sg * 8);
+        gk0 = *reinterpret_cast<const uint4*>(kb + j * DH + sg * 8);
+      }
+    }
+    if constexpr (NQ == 2) {
+      const int j = (tid + 256) / SEG, sg = tid % SEG;
+      if (j < nvalid) {
+        gq1 = *reinterpret_cast<const uint4*>(qb + j * DH + sg * 8);
+        gk1 = *reinterpret_cast<const uint4*>(kb + j * DH + sg * 8);
+      }
+    }
+    if (tid < (BLK / 2) * SEG) {
+      const int j0 = 2 * (tid / SEG), sg = tid % SEG;
+      if (j0 < nvalid) {
+        gv0 = *reinterpret_cast<const uint4*>(vb + j0 * DH + sg * 8);
+        gd0 = dt ? dt[row + t0 + j0] : 1.f;
+      }
+      if (j0 + 1 < nvalid) {
+        gv1 = *reinterpret_cast<const uint4*>(vb + (j0 + 1) * DH + sg * 8);
+        gd1 = dt ? dt[row + t0 + j0 + 1] : 1.f;
+      }
+    }
+  }
+  // entering state: DH * DH floats as float4 (element 4 e4 .. of the block
+  // slot for e4 = tid + 256 u), and at order 1 the d_h normaliser entries
+  const float* st = state + (bh * nblk + blk) * (int64_t)(DH * DH + DH);
+  constexpr int NS4 = DH * DH / 4 / 256;
+  static_assert(NS4 * 256 * 4 == DH * DH, "state mapping");
+  f32x4 gs[NS4];
+#pragma unroll
+  for (int u = 0; u < NS4; ++u) gs[u] = *reinterpret_cast<const f32x4*>(&st[4 * (tid + 256 * u)]);
+  float gzin = 0.f;
+  if (ORDER == 1 && tid < DH) gzin = st[DH * DH + tid];
+  // order 2: the inter-block numerator partials of row il (columns 16 ct +
+  // 4 g ..)
+  f32x4 gp[NT];
+#pragma unroll
+  for (int ct = 0; ct < NT; ++ct) gp[ct] = zero4();
+  if (ORDER == 2 && il < nvalid) {
+    for (int pa = 0; pa < P_a; ++pa) {
+      const float* pp = part + (((int64_t)pa * BH + bh) * o2_part_rows(N) + t0 + il) * 64;
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) gp[ct] += *reinterpret_cast<const f32x4*>(pp + ct * 16 + 4 * g);
+    }
+  }
+
   // Order 2: the numerator scan advances over steps of two blocks and gives
   // the second block of a step only the state entering the step, so the first
   // block's tokens reach it here as a direct (unmasked) term.  Its k and v
@@ -285,44 +349,71 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
     pva = *reinterpret_cast<const uint4*>(vb + (2 * (tid >> 3)) * DH + (tid & 7) * 8);
     pvb = *reinterpret_cast<const uint4*>(vb + (2 * (tid >> 3) + 1) * DH + (tid & 7) * 8);
   }
-  __syncthreads();
-  const float* st = state + (bh * nblk + blk) * (int64_t)(DH * DH + DH);
+
+  // ---- staging into LDS ---------------------------------------------------
+  if (tid < BLK) {
+    csl[tid] = c_own;
+    dtv[tid] = d_own;
+  }
   if constexpr (BF) {
-    // q and k rows: 16-byte segments copied as they are (bf16 bits)
-    constexpr int SEG = DH / 8;
-    for (int e = tid; e < BLK * SEG; e += 256) {
-      const int j = e / SEG, sg = e % SEG;
-      uint4 qv = make_uint4(0, 0, 0, 0), kv = qv;
-      if (j < nvalid) {
-        const int64_t off = (row + t0 + j) * DH + sg * 8;
-        qv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(qp) + off);
-        kv = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(kp) + off);
-      }
-      *reinterpret_cast<uint4*>(&Qs[j * PQ + sg * 8]) = qv;
-      *reinterpret_cast<uint4*>(&Ks[j * PQ + sg * 8]) = kv;
+    {
+      const int j = tid / SEG, sg = tid % SEG;
+      *reinterpret_cast<uint4*>(&Qs[j * PQ + sg * 8]) = gq0;
+      *reinterpret_cast<uint4*>(&Ks[j * PQ + sg * 8]) = gk0;
     }
-    // value operand v dt, transposed: two consecutive tokens per thread so
-    // that each LDS store carries a pair of tokens
-    for (int e = tid; e < (BLK / 2) * SEG; e += 256) {
-      const int jp = e / SEG, sg = e % SEG, j0 = 2 * jp;
-      uint4 v0 = make_uint4(0, 0, 0, 0), v1 = v0;
-      const int64_t off = (row + t0 + j0) * DH + sg * 8;
-      if (j0 < nvalid) v0 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(vp) + off);
-      if (j0 + 1 < nvalid) v1 = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(vp) + off + DH);
-      const uint32_t w0[4] = {v0.x, v0.y, v0.z, v0.w}, w1[4] = {v1.x, v1.y, v1.z, v1.w};
-      const float d0 = dtv[j0], d1 = dtv[j0 + 1];
+    if constexpr (NQ == 2) {
+      const int j = (tid + 256) / SEG, sg = tid % SEG;
+      *reinterpret_cast<uint4*>(&Qs[j * PQ + sg * 8]) = gq1;
+      *reinterpret_cast<uint4*>(&Ks[j * PQ + sg * 8]) = gk1;
+    }
+    // value operand v dt, transposed: each LDS store carries the token pair
+    if (tid < (BLK / 2) * SEG) {
+      const int j0 = 2 * (tid / SEG), sg = tid % SEG;
+      const uint32_t w0[4] = {gv0.x, gv0.y, gv0.z, gv0.w}, w1[4] = {gv1.x, gv1.y, gv1.z, gv1.w};
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const float a0 = __uint_as_float(hh ? (w0[u] & 0xffff0000u) : (w0[u] << 16)) * d0;
-          const float a1 = __uint_as_float(hh ? (w1[u] & 0xffff0000u) : (w1[u] << 16)) * d1;
+          const float a0 = __uint_as_float(hh ? (w0[u] & 0xffff0000u) : (w0[u] << 16)) * gd0;
+          const float a1 = __uint_as_float(hh ? (w1[u] & 0xffff0000u) : (w1[u] << 16)) * gd1;
           C pr[2] = {(C)a0, (C)a1};
           *reinterpret_cast<uint32_t*>(&VT[(sg * 8 + 2 * u + hh) * PJ + j0]) = __builtin_bit_cast(uint32_t, pr);
         }
       }
     }
+  }
+  if constexpr (ORDER == 2) {
+    // the normaliser state Z = sum_j w_j k_j k_j^T is symmetric, so its rows
+    // serve as the transposed operand: high + low bf16 parts
+#pragma unroll
+    for (int u = 0; u < NS4; ++u) {
+      const int e = 4 * (tid + 256 * u), c = e / DH, b4 = e % DH;
+      C hi[4], lo[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        hi[r] = (C)gs[u][r];
+        lo[r] = (C)(gs[u][r] - (float)hi[r]);
+      }
+      *reinterpret_cast<uint2*>(&SinT[c * PQ + b4]) = __builtin_bit_cast(uint2, hi);
+      if constexpr (BF) *reinterpret_cast<uint2*>(&SinL[c * PQ + b4]) = __builtin_bit_cast(uint2, lo);
+    }
   } else {
+#pragma unroll
+    for (int u = 0; u < NS4; ++u) {
+      const int e = 4 * (tid + 256 * u), b = e / DH, c4 = e % DH;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float x = gs[u][r];
+        const C hi = (C)x;
+        SinT[(c4 + r) * PQ + b] = hi;
+        if constexpr (BF) SinL[(c4 + r) * PQ + b] = (C)(x - (float)hi);
+      }
+    }
+  }
+  if (ORDER == 1 && tid < DH) zin[tid] = gzin;
+  if constexpr (!BF) {
+    // fp32 inputs: element-wise staging, v scaled by dt from LDS
+    __syncthreads();
     for (int e = tid; e < BLK * DH; e += 256) {
       const int j = e / DH, d = e - (e / DH) * DH;
       float qv = 0.f, kv = 0.f, vv = 0.f;
@@ -337,35 +428,7 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
       VT[d * PJ + j] = (C)(vv * dtv[j]);
     }
   }
-  if constexpr (ORDER == 2) {
-    // the normaliser state Z = sum_j w_j k_j k_j^T is symmetric, so its rows
-    // serve as the transposed operand: float4 loads, high + low bf16 parts
-    for (int e = tid; e < DH * DH / 4; e += 256) {
-      const int c = e / (DH / 4), b4 = (e % (DH / 4)) * 4;
-      const f32x4 x = *reinterpret_cast<const f32x4*>(&st[c * DH + b4]);
-      C hi[4], lo[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        hi[r] = (C)x[r];
-        lo[r] = (C)(x[r] - (float)hi[r]);
-      }
-      *reinterpret_cast<uint2*>(&SinT[c * PQ + b4]) = __builtin_bit_cast(uint2, hi);
-      if constexpr (BF) *reinterpret_cast<uint2*>(&SinL[c * PQ + b4]) = __builtin_bit_cast(uint2, lo);
-    }
-  } else {
-    for (int e = tid; e < DH * DH; e += 256) {
-      const int b = e / DH, c = e - (e / DH) * DH;
-      const float x = st[e];
-      const C hi = (C)x;
-      SinT[c * PQ + b] = hi;
-      if constexpr (BF) SinL[c * PQ + b] = (C)(x - (float)hi);
-    }
-  }
-  if (ORDER == 1 && tid < DH) zin[tid] = st[DH * DH + tid];
   __syncthreads();
-
-  const int it = tid / WAVE, lane = tid & (WAVE - 1), n = lane & 15, g = lane >> 4;
-  const int il = it * 16 + n;  // this lane's query row within the block
   const float cs_i = csl[il];
 
   // scores, transposed: W[jt][r] = w(i = il, j = 16 jt + 4g + r)
@@ -534,13 +597,8 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
     for (int ct = 0; ct < NT; ++ct)
 #pragma unroll
       for (int r = 0; r < 4; ++r) den_x += (float)Qs[il * PQ + ct * 16 + 4 * g + r] * inter[ct][r];
-    if (il < nvalid) {
-      for (int pa = 0; pa < P_a; ++pa) {
-        const float* pp = part + (((int64_t)pa * BH + bh) * o2_part_rows(N) + t0 + il) * 64;
 #pragma unroll
-        for (int ct = 0; ct < NT; ++ct) num[ct] += *reinterpret_cast<const f32x4*>(pp + ct * 16 + 4 * g);
-      }
-    }
+    for (int ct = 0; ct < NT; ++ct) num[ct] += gp[ct];
   }
   den_x = sum_over_groups(den_x);
   const float dtot = den_l + eci * den_x;

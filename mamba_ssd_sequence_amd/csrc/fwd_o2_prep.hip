@@ -79,6 +79,25 @@ __global__ __launch_bounds__(256) void k_o2_blockprep(const uint16_t* __restrict
   const int tid = threadIdx.x, lane = tid & (WAVE - 1), wave = tid / WAVE;
   uint8_t* R = rec + (bh * nblk + blk) * (int64_t)REC_BYTES;
 
+  // q, k, v segments (8 values each) of two consecutive tokens per thread,
+  // loaded before anything else so that the block costs one memory round
+  // trip
+  const int jp = tid >> 3, seg = tid & 7, j0 = 2 * jp;
+  uint4 qv0 = make_uint4(0, 0, 0, 0), qv1 = qv0, kv0 = qv0, kv1 = qv0, vv0 = qv0, vv1 = qv0;
+  {
+    const int64_t off = (row + t0 + j0) * DH + seg * 8;
+    if (j0 < nv) {
+      qv0 = *reinterpret_cast<const uint4*>(q + off);
+      kv0 = *reinterpret_cast<const uint4*>(k + off);
+      vv0 = *reinterpret_cast<const uint4*>(v + off);
+    }
+    if (j0 + 1 < nv) {
+      qv1 = *reinterpret_cast<const uint4*>(q + off + DH);
+      kv1 = *reinterpret_cast<const uint4*>(k + off + DH);
+      vv1 = *reinterpret_cast<const uint4*>(v + off + DH);
+    }
+  }
+
   const float base = (t0 % chunk == 0) ? 0.f : a_cs[row + t0 - 1];
   const float cs_last = a_cs[row + t0 + nv - 1];
   const float T = cs_last - base;
@@ -108,30 +127,15 @@ __global__ __launch_bounds__(256) void k_o2_blockprep(const uint16_t* __restrict
   if (tid == 0) tb[bh * nblk + blk] = T;
   __syncthreads();
 
-  // pass 1: q, k, v segments (8 values each, two consecutive tokens per
-  // thread) -> maxima, Z operands and v^T; each transposing LDS store carries
-  // the pair of tokens
+  // pass 1: the q, k, v segments -> maxima, Z operands and v^T; each
+  // transposing LDS store carries the pair of tokens
   float qm = 0.f, km = 0.f;
-  uint4 qs[2];
   {
-    const int jp = tid >> 3, seg = tid & 7, j0 = 2 * jp;
-    uint4 qv[2], kv[2], vv[2];
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      qv[u] = kv[u] = vv[u] = make_uint4(0, 0, 0, 0);
-      if (j0 + u < nv) {
-        const int64_t off = (row + t0 + j0 + u) * DH + seg * 8;
-        qv[u] = *reinterpret_cast<const uint4*>(q + off);
-        kv[u] = *reinterpret_cast<const uint4*>(k + off);
-        vv[u] = *reinterpret_cast<const uint4*>(v + off);
-      }
-      qs[u] = qv[u];
-    }
     const float w0 = wv[j0], w1 = wv[j0 + 1];
     float vm0 = 0.f, vm1 = 0.f;
-    const uint32_t qw0[4] = {qv[0].x, qv[0].y, qv[0].z, qv[0].w}, qw1[4] = {qv[1].x, qv[1].y, qv[1].z, qv[1].w};
-    const uint32_t kw0[4] = {kv[0].x, kv[0].y, kv[0].z, kv[0].w}, kw1[4] = {kv[1].x, kv[1].y, kv[1].z, kv[1].w};
-    const uint32_t vw0[4] = {vv[0].x, vv[0].y, vv[0].z, vv[0].w}, vw1[4] = {vv[1].x, vv[1].y, vv[1].z, vv[1].w};
+    const uint32_t qw0[4] = {qv0.x, qv0.y, qv0.z, qv0.w}, qw1[4] = {qv1.x, qv1.y, qv1.z, qv1.w};
+    const uint32_t kw0[4] = {kv0.x, kv0.y, kv0.z, kv0.w}, kw1[4] = {kv1.x, kv1.y, kv1.z, kv1.w};
+    const uint32_t vw0[4] = {vv0.x, vv0.y, vv0.z, vv0.w}, vw1[4] = {vv1.x, vv1.y, vv1.z, vv1.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -229,8 +233,9 @@ __global__ __launch_bounds__(256) void k_o2_blockprep(const uint16_t* __restrict
   // q rows: in each 16-column group the 4-column subgroups go to slots 0, 2, 1, 3
 #pragma unroll
   for (int u = 0; u < 2; ++u) {
-    const int j = 2 * (tid >> 3) + u, seg = tid & 7;
-    const uint32_t qw[4] = {qs[u].x, qs[u].y, qs[u].z, qs[u].w};
+    const int j = j0 + u;
+    const uint4 qsu = u ? qv1 : qv0;
+    const uint32_t qw[4] = {qsu.x, qsu.y, qsu.z, qsu.w};
     h16x4 h0, h1;
     h0[0] = (_Float16)(lo16(qw[0]) * sq);
     h0[1] = (_Float16)(hi16(qw[0]) * sq);

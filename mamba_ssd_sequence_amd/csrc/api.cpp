@@ -211,7 +211,7 @@ ssd_status ssd_forward(const void* q, const void* k, const void* v, const float*
       if ((e = ssd::launch_state_pass(d_h, BH, N, tb, st, final_state, final_norm, stream)) != hipSuccess)
         return hip_status(e, "state_pass launch");
       tm.mark();
-      e = ssd::launch_output(bf, d_h, 1, q, k, v, dt, a_cs, BH, N, chunk, st, nullptr, 0, y, den, stream);
+      e = ssd::launch_output(bf, d_h, 1, q, k, v, dt, a_cs, BH, N, chunk, st, nullptr, y, den, stream);
       tm.mark();
       return hip_status(e, "output launch");
     }
@@ -229,7 +229,7 @@ ssd_status ssd_forward(const void* q, const void* k, const void* v, const float*
     if ((e = ssd::launch_o2_state(rec, BH, N, part, final_state, st, final_norm, stream)) != hipSuccess)
       return hip_status(e, "o2_state launch");
     tm.mark();
-    e = ssd::launch_output(true, 64, 2, q, k, v, dt, a_cs, BH, N, chunk, st, part, ssd::o2_pa(BH), y, den, stream);
+    e = ssd::launch_output(true, 64, 2, q, k, v, dt, a_cs, BH, N, chunk, st, part, y, den, stream);
     tm.mark();
     return hip_status(e, "output launch");
   } catch (...) {

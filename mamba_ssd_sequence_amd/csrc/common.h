@@ -42,6 +42,12 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// 2^x on the hardware exponential (v_exp_f32, about 1 ulp; results below the
+// smallest normal flush to 0, which only ever happens for decays that are 0
+// to fp32 accuracy anyway); with x = y log2(e) it gives e^y.
+constexpr float LOG2E = 1.4426950408889634f;
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // softplus(x) = max(x, 0) + log1p(exp(-|x|)), written from its definition.
 __device__ __forceinline__ float softplus_f(float x) {
   return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x)));

@@ -224,7 +224,7 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
                                                 const float* __restrict__ a_cs, int64_t BH,
                                                 int64_t N, int64_t chunk, int64_t nblk,
                                                 const float* __restrict__ state,
-                                                const float* __restrict__ part, int P_a,
+                                                const float* __restrict__ part,
                                                 float* __restrict__ y, float* __restrict__ den) {
   using G = Cfg<BF>;
   using C = typename G::C;
@@ -254,10 +254,11 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
   // so that a block costs one memory round trip: the block's cumsum and dt,
   // q / k / v (bf16), the entering state, and at order 2 the inter-block
   // partials of this thread's query row and the partner block (below).
+  // Decays are exp2 of differences of cumsums kept in log2 units (cs log2 e).
   const float base = (t0 % chunk == 0) ? 0.f : a_cs[row + t0 - 1];
   float c_own = 0.f, d_own = 0.f;
   if (tid < nvalid) {  // tid < BLK
-    c_own = a_cs[row + t0 + tid] - base;
+    c_own = (a_cs[row + t0 + tid] - base) * LOG2E;
     d_own = dt ? dt[row + t0 + tid] : 1.f;
   }
   const int it = tid / WAVE, lane = tid & (WAVE - 1), n = lane & 15, g = lane >> 4;
@@ -316,12 +317,11 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
   f32x4 gp[NT];
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct) gp[ct] = zero4();
-  if (ORDER == 2 && il < nvalid) {
-    for (int pa = 0; pa < P_a; ++pa) {
-      const float* pp = part + (((int64_t)pa * BH + bh) * o2_part_rows(N) + t0 + il) * 64;
+  if constexpr (ORDER == 2) {
+    // (rows past a ragged block's end read a padding row; results unused)
+    const float* pp = part + (bh * o2_part_rows(N) + t0 + il) * 64;
 #pragma unroll
-      for (int ct = 0; ct < NT; ++ct) gp[ct] += *reinterpret_cast<const f32x4*>(pp + ct * 16 + 4 * g);
-    }
+    for (int ct = 0; ct < NT; ++ct) gp[ct] = *reinterpret_cast<const f32x4*>(pp + ct * 16 + 4 * g);
   }
 
   // Order 2: the numerator scan advances over steps of two blocks and gives
@@ -335,9 +335,9 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
   if (PAIRS && partner) {
     const int64_t tp = t0 - BLK;  // the first block of the step (always full)
     const float base_p = (tp % chunk == 0) ? 0.f : a_cs[row + tp - 1];
-    pT = a_cs[row + tp + BLK - 1] - base_p;
+    pT = (a_cs[row + tp + BLK - 1] - base_p) * LOG2E;
     if (tid < BLK) {
-      pcs = a_cs[row + tp + tid] - base_p;
+      pcs = (a_cs[row + tp + tid] - base_p) * LOG2E;
       pdt = dt ? dt[row + tp + tid] : 1.f;
     }
     // k: the 16-byte segment tid % 8 of rows tid / 8 and 32 + tid / 8; v: the
@@ -447,7 +447,7 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
         const int j = jt * 16 + 4 * g + r;
         float s = acc[r];
         if (ORDER == 2) s = s * s;
-        const float w = (j <= il && j < nvalid) ? s * expf(cs_i - csl[j]) : 0.f;
+        const float w = (j <= il && j < nvalid) ? s * exp2_fast(cs_i - csl[j]) : 0.f;
         W[jt][r] = w;
         den_l += w;
       }
@@ -539,7 +539,7 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int j = jt * 16 + 4 * g + r;
-        Wp[jt][r] = acc[r] * acc[r] * expf(cs_i + pT - csl[j]);
+        Wp[jt][r] = acc[r] * acc[r] * exp2_fast(cs_i + pT - csl[j]);
       }
     }
     if constexpr (BF) {
@@ -573,7 +573,7 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
   // operands the state is split into high + low bf16 parts: the factored sum
   // over b can cancel (q nearly orthogonal to the keys), so a single bf16
   // rounding of the state would be amplified.
-  const float eci = expf(cs_i);
+  const float eci = exp2_fast(cs_i);
   f32x4 inter[NT];
 #pragma unroll
   for (int ct = 0; ct < NT; ++ct) {
@@ -605,11 +605,12 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
 
   if (il < nvalid) {
     float* yp = y + (row + t0 + il) * DH;
+    const float rd = 1.f / dtot;
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) {
       f32x4 o;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) o[r] = num[ct][r] / dtot;
+      for (int r = 0; r < 4; ++r) o[r] = num[ct][r] * rd;
       *reinterpret_cast<f32x4*>(yp + ct * 16 + 4 * g) = o;
     }
     if (den && g == 0) den[row + t0 + il] = dtot;
@@ -618,13 +619,13 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
 
 hipError_t launch_output(bool bf16, int64_t DH, int order, const void* q, const void* k,
                          const void* v, const float* dt, const float* a_cs, int64_t BH, int64_t N,
-                         int64_t chunk, const float* state, const float* part, int P_a, float* y,
+                         int64_t chunk, const float* state, const float* part, float* y,
                          float* den, hipStream_t stream) {
   const int64_t nb = n_blocks(N);
   const dim3 grid((unsigned)(BH * nb)), blk(256);
 #define SSD_LAUNCH_OUT(BFV, DHV, ORD)                                                           \
   hipLaunchKernelGGL((k_output<BFV, DHV, ORD>), grid, blk, 0, stream, q, k, v, dt, a_cs, BH, N, \
-                     chunk, nb, state, part, P_a, y, den)
+                     chunk, nb, state, part, y, den)
   if (order == 2) {
     SSD_LAUNCH_OUT(true, 64, 2);
   } else if (bf16) {

@@ -14,9 +14,8 @@ __host__ __device__ inline int64_t n_blocks(int64_t N) { return (N + 63) / 64; }
 // per wave, 2 (one value column per wave, 8 columns per workgroup) with
 // >= 32 heads, else 1 (two waves per column, 4 columns per workgroup), so that
 // the grid still covers the chip.  A workgroup holds all 64 values of a, so
-// there is one partial-output slice per head.
+// its outputs are complete inter-block numerators (no partial sums).
 inline int o2_nat(int64_t BH) { return BH >= 32 ? 2 : 1; }
-inline int o2_pa(int64_t) { return 1; }
 
 // The order-2 numerator state scan advances over steps of two blocks
 // (2m, 2m+1); a last step without partner gets an empty second block.
@@ -54,9 +53,9 @@ constexpr int REC_BYTES = 24880;
 //   state  [BH, nblk, DH*DH + DH]     per-block state contributions, then
 //                                     (in place) the state entering each block
 //                                     (order 1: S and z; order 2: Z and unused)
-//   part   [P_a, BH, rows, 64]        order 2 only: inter-block numerator
-//                                     partials of each a-slice (rows =
-//                                     o2_part_rows(N), padded to whole steps)
+//   part   [BH, rows, 64]             order 2 only: inter-block numerators
+//                                     (rows = o2_part_rows(N), padded to
+//                                     whole steps)
 //   rec    [BH, nblk] x REC_BYTES     order 2 only: operand records
 struct WsLayout {
   size_t tb, state, part, rec, total_floats;
@@ -72,7 +71,7 @@ inline WsLayout ws_layout(int64_t B, int64_t H, int64_t N, int64_t DH, int order
   off += (size_t)(BH * nb) * (size_t)(DH * DH + DH);
   off = (off + 63) & ~(size_t)63;
   L.part = off;
-  if (order == 2) off += (size_t)o2_pa(BH) * (size_t)BH * (size_t)o2_part_rows(N) * 64;
+  if (order == 2) off += (size_t)BH * (size_t)o2_part_rows(N) * 64;
   off = (off + 63) & ~(size_t)63;
   L.rec = off;
   if (order == 2) off += (size_t)(BH * nb) * (REC_BYTES / 4);
@@ -97,7 +96,7 @@ hipError_t launch_state_pass(int64_t DH, int64_t BH, int64_t N, const float* tb,
 // Intra-block masked product + inter-block part + normalisation -> y, den.
 hipError_t launch_output(bool bf16, int64_t DH, int order, const void* q, const void* k,
                          const void* v, const float* dt, const float* a_cs, int64_t BH, int64_t N,
-                         int64_t chunk, const float* state, const float* part, int P_a, float* y,
+                         int64_t chunk, const float* state, const float* part, float* y,
                          float* den, hipStream_t stream);
 
 // Order 2, per block (parallel): the normaliser state contribution

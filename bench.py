@@ -18,6 +18,9 @@ bandwidth (8 TB/s).  Algorithmic work per launch (see the design notes):
   decode step: 2 * 4 * (D * d_h + D) bytes per sequence and head.
 cpu_baseline: the fp64 oracle (tests' reference implementation, untuned) on a
 bounded sample of the same workload, on this machine's host cores.
+device_ceilings: what the vendor library reaches on the same GPU (torch's fp16
+GEMM at 8192^3, a 1 GiB copy), measured outside the timed steps, as context
+for the roofline fractions.
 """
 from __future__ import annotations
 
@@ -263,6 +266,46 @@ def cpu_baseline_decode(cfg: I.DecodeConfig, dec, budget_s=10.0):
                       f"extrapolated to {cfg.S} x {cfg.H} per step", "wall_s": el}
 
 
+def device_ceilings(dev):
+    """What the vendor's own library code reaches on this GPU, as context for
+    the roofline fractions (not part of the timed step): torch's fp16 GEMM
+    (hipBLASLt) on 8192^3 and a 1 GiB device-to-device copy."""
+    import torch
+    out = {}
+    M = 8192
+    a = torch.randn(M, M, dtype=torch.float16, device=dev)
+    b = torch.randn(M, M, dtype=torch.float16, device=dev)
+    for _ in range(3):
+        c = a @ b
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    out["torch_fp16_gemm_8192_tflops"] = 2 * M ** 3 / (ms * 1e-3) / 1e12
+    out["torch_fp16_gemm_8192_frac_of_2500"] = out["torch_fp16_gemm_8192_tflops"] / 2500.0
+    del a, b, c
+    n = (1 << 30) // 4
+    src = torch.ones(n, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    out["torch_copy_1gib_gbs"] = 2 * (1 << 30) / (ms * 1e-3) / 1e9  # bytes read + written
+    del src, dst
+    torch.cuda.empty_cache()
+    return out
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -330,6 +373,12 @@ def main():
                 f"roofline frac {r['roofline']['frac']:.3f}")
             extra.append(r)
 
+    ceilings = None
+    if not a.no_extra:
+        ceilings = device_ceilings(dev)
+        log(f"[bench] context: torch fp16 GEMM 8192^3 {ceilings['torch_fp16_gemm_8192_tflops']:.0f} TFLOP/s, "
+            f"1 GiB copy {ceilings['torch_copy_1gib_gbs']:.0f} GB/s")
+
     cpu = None
     if not a.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
@@ -361,6 +410,7 @@ def main():
         "kernels_ms": res.get("kernels_ms"),
         "step_mfma_frac": res.get("step_mfma_frac"),
         "extra": extra,
+        "device_ceilings": ceilings,
         "device": torch.cuda.get_device_name(dev),
     }
     print(json.dumps(out), flush=True)

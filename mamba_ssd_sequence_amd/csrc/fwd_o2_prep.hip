@@ -5,8 +5,9 @@
 // Algorithm 3's A^CS restricted to the block), T = cs_last - cs_start and
 // w_j = exp(T - cs_j):
 //   1. the normaliser state contribution of Algorithm 6's H_down at order 2,
-//      kept as the d_h x d_h matrix Z_blk = sum_j w_j k_j k_j^T (and the unused
-//      sum_j w_j k_j), on bf16 MFMA with w k split into high + low parts;
+//      kept as the d_h x d_h matrix Z_blk = sum_j w_j k_j k_j^T (the first
+//      d_h^2 floats of the block's state slot), on bf16 MFMA with w k split
+//      into high + low parts;
 //   2. the operand record the numerator state scan consumes (layout in
 //      launch.h): fp16 q 2^tau (columns permuted for the MFMA operand), fp16
 //      k^T 2^kap, fp16 X^T 2^xi with X_jc = w_j dt_j v_jc (for the first
@@ -204,11 +205,6 @@ __global__ __launch_bounds__(256) void k_o2_blockprep(const uint16_t* __restrict
       }
       // acc[r] = Z^T[c = 16ct + 4g + r][b = 16bt + n] -> Z[b][c]
       *reinterpret_cast<f32x4*>(&out[(bt * 16 + n) * DH + ct * 16 + 4 * g]) = acc;
-    }
-    if (tid < DH) {
-      float s = 0.f;
-      for (int j = 0; j < BLK; ++j) s += (float)wKT[tid * P + j] + (float)wKL[tid * P + j];
-      out[DH * DH + tid] = s;
     }
   }
   __syncthreads();

@@ -65,8 +65,6 @@ __global__ __launch_bounds__(256) void k_o2_blockprep(const uint16_t* __restrict
                                                       float* __restrict__ tb,
                                                       float* __restrict__ state,
                                                       uint8_t* __restrict__ rec) {
-  __shared__ __attribute__((aligned(16))) __bf16 wKT[DH * P];  // [b][j] high part of w_j k_jb
-  __shared__ __attribute__((aligned(16))) __bf16 wKL[DH * P];  // [b][j] low part
   __shared__ __attribute__((aligned(16))) __bf16 KTb[DH * P];  // [b][j] k_jb
   __shared__ __attribute__((aligned(16))) __bf16 VTb[DH * P];  // [c][j] v_jc
   __shared__ float wv[BLK], wdt[BLK], vrow[BLK];
@@ -128,11 +126,10 @@ __global__ __launch_bounds__(256) void k_o2_blockprep(const uint16_t* __restrict
   if (tid == 0) tb[bh * nblk + blk] = T;
   __syncthreads();
 
-  // pass 1: the q, k, v segments -> maxima, Z operands and v^T; each
-  // transposing LDS store carries the pair of tokens
+  // pass 1: the q, k, v segments -> maxima, k^T and v^T; each transposing
+  // LDS store carries the pair of tokens
   float qm = 0.f, km = 0.f;
   {
-    const float w0 = wv[j0], w1 = wv[j0 + 1];
     float vm0 = 0.f, vm1 = 0.f;
     const uint32_t qw0[4] = {qv0.x, qv0.y, qv0.z, qv0.w}, qw1[4] = {qv1.x, qv1.y, qv1.z, qv1.w};
     const uint32_t kw0[4] = {kv0.x, kv0.y, kv0.z, kv0.w}, kw1[4] = {kv1.x, kv1.y, kv1.z, kv1.w};
@@ -153,12 +150,6 @@ __global__ __launch_bounds__(256) void k_o2_blockprep(const uint16_t* __restrict
         km = fmaxf(km, fmaxf(fabsf(k0), fabsf(k1)));
         vm0 = fmaxf(vm0, fabsf(v0));
         vm1 = fmaxf(vm1, fabsf(v1));
-        const float wk0 = w0 * k0, wk1 = w1 * k1;
-        const __bf16 h0 = (__bf16)wk0, h1 = (__bf16)wk1;
-        const __bf16 pw[2] = {h0, h1};
-        const __bf16 pl[2] = {(__bf16)(wk0 - (float)h0), (__bf16)(wk1 - (float)h1)};
-        *reinterpret_cast<uint32_t*>(&wKT[d * P + j0]) = __builtin_bit_cast(uint32_t, pw);
-        *reinterpret_cast<uint32_t*>(&wKL[d * P + j0]) = __builtin_bit_cast(uint32_t, pl);
         *reinterpret_cast<uint32_t*>(&KTb[d * P + j0]) = kb0 | (kb1 << 16);
         *reinterpret_cast<uint32_t*>(&VTb[d * P + j0]) = vb0 | (vb1 << 16);
       }
@@ -190,18 +181,33 @@ __global__ __launch_bounds__(256) void k_o2_blockprep(const uint16_t* __restrict
     }
   }
 
-  // normaliser contribution Z_blk (bf16 MFMA, w k in high + low parts)
+  // normaliser contribution Z_blk (bf16 MFMA, w k in high + low parts).
+  // Wave wv_ takes the column tile bt = wv_ of every row tile ct; its B
+  // operand, (w k)^T[b][j] for b in tile bt, is formed in registers from the
+  // k^T rows and w (high part bf16(w k), low part bf16(w k - high)).
   {
-    const int n = lane & 15, g = lane >> 4;
+    const int n = lane & 15, g = lane >> 4, bt = wave;
+    bf16x8 bhi[2], blo[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&KTb[(bt * 16 + n) * P + ks * 32 + 8 * g]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float wk = (float)kr[e] * wv[ks * 32 + 8 * g + e];
+        const __bf16 h = (__bf16)wk;
+        bhi[ks][e] = h;
+        blo[ks][e] = (__bf16)(wk - (float)h);
+      }
+    }
     float* out = state + (bh * nblk + blk) * (int64_t)(DH * DH + DH);
-    for (int tile = wave; tile < 16; tile += 4) {
-      const int ct = tile >> 2, bt = tile & 3;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
       f32x4 acc = zero4();
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 a = *reinterpret_cast<const bf16x8*>(&KTb[(ct * 16 + n) * P + ks * 32 + 8 * g]);
-        acc = mfma_bf16(a, *reinterpret_cast<const bf16x8*>(&wKT[(bt * 16 + n) * P + ks * 32 + 8 * g]), acc);
-        acc = mfma_bf16(a, *reinterpret_cast<const bf16x8*>(&wKL[(bt * 16 + n) * P + ks * 32 + 8 * g]), acc);
+        acc = mfma_bf16(a, bhi[ks], acc);
+        acc = mfma_bf16(a, blo[ks], acc);
       }
       // acc[r] = Z^T[c = 16ct + 4g + r][b = 16bt + n] -> Z[b][c]
       *reinterpret_cast<f32x4*>(&out[(bt * 16 + n) * DH + ct * 16 + 4 * g]) = acc;

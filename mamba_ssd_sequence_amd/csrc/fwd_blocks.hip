@@ -216,8 +216,10 @@ hipError_t launch_state_pass(int64_t DH, int64_t BH, int64_t N, const float* tb,
 // ---------------------------------------------------------------------------
 // k_output
 // ---------------------------------------------------------------------------
+// (order 2: registers capped for five waves per SIMD, which its 29 KB of LDS
+// allows; the order-1 variants are bound by LDS)
 template <bool BF, int DH, int ORDER>
-__global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ORDER == 2 ? 5 : 1, 8))) void k_output(const void* __restrict__ qp,
                                                 const void* __restrict__ kp,
                                                 const void* __restrict__ vp,
                                                 const float* __restrict__ dt,
@@ -235,8 +237,10 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
   __shared__ __attribute__((aligned(16))) C Qs[BLK * PQ];   // [i][d]
   __shared__ __attribute__((aligned(16))) C Ks[BLK * PQ];   // [j][d]
   __shared__ __attribute__((aligned(16))) C VT[DH * PJ];    // [c][j]  value operand, transposed
-  __shared__ __attribute__((aligned(16))) C SinT[DH * PQ];  // [c][b]  entering state, transposed
-  __shared__ __attribute__((aligned(16))) C SinL[BF ? DH * PQ : 1];  // bf16: low part of the same
+  // order 1 only: the entering state (order 2 reads its rows into registers)
+  __shared__ __attribute__((aligned(16))) C SinT[ORDER == 1 ? DH * PQ : 1];  // [c][b] transposed
+  __shared__ __attribute__((aligned(16))) C SinL[ORDER == 1 && BF ? DH * PQ : 1];  // bf16: low part
+  __shared__ float dred[ORDER == 2 ? 4 * BLK : 1];  // order 2: per-wave parts of q^T Z q
   __shared__ float zin[DH];
   __shared__ float csl[BLK];
   __shared__ float dtv[BLK];
@@ -302,14 +306,23 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
       }
     }
   }
-  // entering state: DH * DH floats as float4 (element 4 e4 .. of the block
-  // slot for e4 = tid + 256 u), and at order 1 the d_h normaliser entries
+  // entering state: order 1, DH * DH floats as float4 (element 4 e4 .. of
+  // the block slot for e4 = tid + 256 u) and the d_h normaliser entries;
+  // order 2, the normaliser state Z (symmetric): wave it takes the rows c of
+  // column tile it, lane (n, g) the 8 entries 32 ks + 8 g .. of row 16 it + n
+  // (the A operand of (Z Q^T) restricted to those rows)
   const float* st = state + (bh * nblk + blk) * (int64_t)(DH * DH + DH);
   constexpr int NS4 = DH * DH / 4 / 256;
-  static_assert(NS4 * 256 * 4 == DH * DH, "state mapping");
+  static_assert(NS4 * 256 * 4 == DH * DH && (ORDER == 1 || NS4 == 4), "state mapping");
   f32x4 gs[NS4];
+  if constexpr (ORDER == 2) {
 #pragma unroll
-  for (int u = 0; u < NS4; ++u) gs[u] = *reinterpret_cast<const f32x4*>(&st[4 * (tid + 256 * u)]);
+    for (int u = 0; u < NS4; ++u)
+      gs[u] = *reinterpret_cast<const f32x4*>(&st[(it * 16 + n) * DH + (u >> 1) * 32 + 8 * g + 4 * (u & 1)]);
+  } else {
+#pragma unroll
+    for (int u = 0; u < NS4; ++u) gs[u] = *reinterpret_cast<const f32x4*>(&st[4 * (tid + 256 * u)]);
+  }
   float gzin = 0.f;
   if (ORDER == 1 && tid < DH) gzin = st[DH * DH + tid];
   // order 2: the inter-block numerator partials of row il (columns 16 ct +
@@ -382,22 +395,7 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
       }
     }
   }
-  if constexpr (ORDER == 2) {
-    // the normaliser state Z = sum_j w_j k_j k_j^T is symmetric, so its rows
-    // serve as the transposed operand: high + low bf16 parts
-#pragma unroll
-    for (int u = 0; u < NS4; ++u) {
-      const int e = 4 * (tid + 256 * u), c = e / DH, b4 = e % DH;
-      C hi[4], lo[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        hi[r] = (C)gs[u][r];
-        lo[r] = (C)(gs[u][r] - (float)hi[r]);
-      }
-      *reinterpret_cast<uint2*>(&SinT[c * PQ + b4]) = __builtin_bit_cast(uint2, hi);
-      if constexpr (BF) *reinterpret_cast<uint2*>(&SinL[c * PQ + b4]) = __builtin_bit_cast(uint2, lo);
-    }
-  } else {
+  if constexpr (ORDER == 1) {
 #pragma unroll
     for (int u = 0; u < NS4; ++u) {
       const int e = 4 * (tid + 256 * u), b = e / DH, c4 = e % DH;
@@ -430,6 +428,39 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
   }
   __syncthreads();
   const float cs_i = csl[il];
+
+  if constexpr (ORDER == 2) {
+    // q^T Z q for all 64 rows over this wave's 16 columns c: (Z Q^T)[c][i] on
+    // MFMA with Z in high + low bf16 parts (the factored sum can cancel when
+    // q is nearly orthogonal to the keys), then sum_c q_ic (Z Q^T)[c][i]
+    bf16x8 zhi[2], zlo[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float x = gs[2 * ks + (e >> 2)][e & 3];
+        const __bf16 h = (__bf16)x;
+        zhi[ks][e] = h;
+        zlo[ks][e] = (__bf16)(x - (float)h);
+      }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 b = G::ld(Qs, PQ, t * 16 + n, ks, g);
+        acc = mfma_bf16(zhi[ks], b, acc);
+        acc = mfma_bf16(zlo[ks], b, acc);
+      }
+      // acc[r] = (Z Q^T)[c = 16 it + 4 g + r][i = 16 t + n]
+      const bf16x4 qc = *reinterpret_cast<const bf16x4*>(&Qs[(t * 16 + n) * PQ + it * 16 + 4 * g]);
+      float p = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p += (float)qc[r] * acc[r];
+      p = sum_over_groups(p);
+      if (g == 0) dred[it * BLK + t * 16 + n] = p;
+    }
+  }
 
   // scores, transposed: W[jt][r] = w(i = il, j = 16 jt + 4g + r)
   f32x4 W[4];
@@ -569,38 +600,36 @@ __global__ __launch_bounds__(256) void k_output(const void* __restrict__ qp,
    }
   }
 
-  // inter-block part: D[c][i] = sum_b S_in[b][c] Q[i][b].  With bf16
-  // operands the state is split into high + low bf16 parts: the factored sum
-  // over b can cancel (q nearly orthogonal to the keys), so a single bf16
-  // rounding of the state would be amplified.
+  // inter-block part.  Order 1: D[c][i] = sum_b S_in[b][c] Q[i][b] with
+  // the state in high + low bf16 parts (the factored sum over b can cancel
+  // when q is nearly orthogonal to the keys, so a single bf16 rounding of the
+  // state would be amplified) and the normaliser q . z.  Order 2: the
+  // numerators come from the state scan; q^T Z q from the per-wave parts.
   const float eci = exp2_fast(cs_i);
-  f32x4 inter[NT];
-#pragma unroll
-  for (int ct = 0; ct < NT; ++ct) {
-    f32x4 acc = zero4();
-#pragma unroll
-    for (int ks = 0; ks < DH / G::KS; ++ks) {
-      const auto b = G::ld(Qs, PQ, il, ks, g);
-      acc = G::mma(G::ld(SinT, PQ, ct * 16 + n, ks, g), b, acc);
-      if constexpr (BF) acc = G::mma(G::ld(SinL, PQ, ct * 16 + n, ks, g), b, acc);
-    }
-    inter[ct] = acc;
-  }
   float den_x = 0.f;
   if constexpr (ORDER == 1) {
+    f32x4 inter[NT];
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < DH / G::KS; ++ks) {
+        const auto b = G::ld(Qs, PQ, il, ks, g);
+        acc = G::mma(G::ld(SinT, PQ, ct * 16 + n, ks, g), b, acc);
+        if constexpr (BF) acc = G::mma(G::ld(SinL, PQ, ct * 16 + n, ks, g), b, acc);
+      }
+      inter[ct] = acc;
+    }
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) num[ct] += eci * inter[ct];
     for (int b = g * (DH / 4); b < (g + 1) * (DH / 4); ++b) den_x += (float)Qs[il * PQ + b] * zin[b];
+    den_x = sum_over_groups(den_x);
   } else {
-    // q^T Z q: inter[ct][r] = (Q Z)[i][c = 16ct + 4g + r]
-#pragma unroll
-    for (int ct = 0; ct < NT; ++ct)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) den_x += (float)Qs[il * PQ + ct * 16 + 4 * g + r] * inter[ct][r];
+    __syncthreads();  // every wave's part of q^T Z q is in dred
+    den_x = (dred[il] + dred[BLK + il]) + (dred[2 * BLK + il] + dred[3 * BLK + il]);
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) num[ct] += gp[ct];
   }
-  den_x = sum_over_groups(den_x);
   const float dtot = den_l + eci * den_x;
 
   if (il < nvalid) {

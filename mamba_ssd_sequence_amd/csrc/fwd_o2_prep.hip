@@ -56,7 +56,9 @@ typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 
-__global__ __launch_bounds__(256) void k_o2_blockprep(const uint16_t* __restrict__ q,
+// (registers capped at 64 so that eight workgroups fit on a CU: the kernel
+// is latency-bound, and its 19 KB of LDS allows eight)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) void k_o2_blockprep(const uint16_t* __restrict__ q,
                                                       const uint16_t* __restrict__ k,
                                                       const uint16_t* __restrict__ v,
                                                       const float* __restrict__ dt,

@@ -10,8 +10,9 @@ the order-2 (2Mamba) forward at N = 4096 (B 2, H 16, d_h 64, bf16 inputs, fp32
 accumulation).  One JSON line is printed on stdout; progress goes to stderr.
 
 roofline: the dominant kernel of the step, timed with HIP events that the
-library records on its own stream around each of its kernels over the timed
-steps, against MI355X's published dense bf16 MFMA peak (2.5 PFLOP/s) or HBM
+library records on its own stream around each of its kernels over K further
+steps run after the timed ones (events between kernels add launch gaps, so
+the timed steps record none), against MI355X's published dense bf16 MFMA peak (2.5 PFLOP/s) or HBM
 bandwidth (8 TB/s).  Algorithmic work per launch (see the design notes):
   order-2 numerator state scan: 4 * D * d_h flops per token and head
       (2 D d_h for phi(q)^T S, 2 D d_h for the phi(k) (v dt)^T update),
@@ -121,15 +122,22 @@ def bench_forward(cfg: I.Config, steps: int, warmup: int, dev):
 
     for _ in range(warmup):
         step()
-    timers = [ssd.KernelTimer() for _ in range(steps)]
+    # the timed steps (nothing recorded between the kernels) ...
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for i in range(steps):
-        step(timers[i])
+        step()
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
+    # ... then as many steps again with the library's per-kernel events, for
+    # the kernel breakdown (events between kernels add launch gaps, so these
+    # steps are not the timed ones)
+    timers = [ssd.KernelTimer() for _ in range(steps)]
+    for i in range(steps):
+        step(timers[i])
+    torch.cuda.synchronize()
     names = KERNELS_O2 if cfg.order == 2 else KERNELS_O1
     per = np.array([tm.durations_ms() for tm in timers])  # [steps, kernels]
     kern_ms = dict(zip(names, per.mean(axis=0).tolist()))

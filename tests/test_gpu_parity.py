@@ -102,6 +102,10 @@ SMALL = [
     ("o1_bf16_2k", 1, 1, 2, 1, 64), ("o1_bf16_2k", 1, 1, 2, 129, 64), ("o1_bf16_2k", 1, 2, 2, 333, 128),
     ("o2_bf16_4k", 2, 1, 1, 1, 64), ("o2_bf16_4k", 2, 1, 2, 64, 64), ("o2_bf16_4k", 2, 1, 2, 65, 64),
     ("o2_bf16_4k", 2, 2, 1, 257, 128), ("o2_bf16_4k", 2, 1, 3, 700, 64),
+    # 32 heads: the state scan's one-wave-per-column layout and head-to-XCD
+    # mapping (5 blocks: the last step has an empty second block; 3 blocks of a
+    # chunk of 128)
+    ("o2_bf16_4k", 2, 2, 16, 300, 64), ("o2_bf16_4k", 2, 4, 8, 130, 128),
 ]
 
 

@@ -308,17 +308,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ORDER == 2 
   }
   // entering state: order 1, DH * DH floats as float4 (element 4 e4 .. of
   // the block slot for e4 = tid + 256 u) and the d_h normaliser entries;
-  // order 2, the normaliser state Z (symmetric): wave it takes the rows c of
-  // column tile it, lane (n, g) the 8 entries 32 ks + 8 g .. of row 16 it + n
-  // (the A operand of (Z Q^T) restricted to those rows)
+  // order 2, the normaliser state Z (symmetric, upper 16 x 16 tiles stored):
+  // wave it takes the rows b of tile it, lane (n, g) the 8 entries c = 32 ks
+  // + 8 g .. of row 16 it + n, from tile ct = c / 16 when ct >= it (the A
+  // operand of (Z' Q^T) with Z' the upper tiles of Z, off-diagonal ones
+  // doubled: q^T Z' q = q^T Z q); lanes whose tile lies below the diagonal
+  // read the diagonal tile and use 0
   const float* st = state + (bh * nblk + blk) * (int64_t)(DH * DH + DH);
   constexpr int NS4 = DH * DH / 4 / 256;
   static_assert(NS4 * 256 * 4 == DH * DH && (ORDER == 1 || NS4 == 4), "state mapping");
   f32x4 gs[NS4];
   if constexpr (ORDER == 2) {
 #pragma unroll
-    for (int u = 0; u < NS4; ++u)
-      gs[u] = *reinterpret_cast<const f32x4*>(&st[(it * 16 + n) * DH + (u >> 1) * 32 + 8 * g + 4 * (u & 1)]);
+    for (int u = 0; u < NS4; ++u) {
+      const int ct = 2 * (u >> 1) + (g >> 1), col = 8 * (g & 1) + 4 * (u & 1);
+      gs[u] = *reinterpret_cast<const f32x4*>(&st[256 * z_tile(it, ct < it ? it : ct) + 16 * n + col]);
+    }
   } else {
 #pragma unroll
     for (int u = 0; u < NS4; ++u) gs[u] = *reinterpret_cast<const f32x4*>(&st[4 * (tid + 256 * u)]);
@@ -430,29 +435,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ORDER == 2 
   const float cs_i = csl[il];
 
   if constexpr (ORDER == 2) {
-    // q^T Z q for all 64 rows over this wave's 16 columns c: (Z Q^T)[c][i] on
-    // MFMA with Z in high + low bf16 parts (the factored sum can cancel when
-    // q is nearly orthogonal to the keys), then sum_c q_ic (Z Q^T)[c][i]
+    // q^T Z q for all 64 rows over this wave's 16 rows b of Z': (Z' Q^T)[b][i]
+    // on MFMA with Z' in high + low bf16 parts (the factored sum can cancel
+    // when q is nearly orthogonal to the keys), then sum_b q_ib (Z' Q^T)[b][i]
     bf16x8 zhi[2], zlo[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < 2; ++ks) {
+      const int ct = 2 * ks + (g >> 1);
+      const float wz = ct < it ? 0.f : (ct > it ? 2.f : 1.f);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float x = gs[2 * ks + (e >> 2)][e & 3];
+        const float x = gs[2 * ks + (e >> 2)][e & 3] * wz;
         const __bf16 h = (__bf16)x;
         zhi[ks][e] = h;
         zlo[ks][e] = (__bf16)(x - (float)h);
       }
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       f32x4 acc = zero4();
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
+        if (2 * ks + 1 < it) continue;  // both tiles of this k-range lie below the diagonal
         const bf16x8 b = G::ld(Qs, PQ, t * 16 + n, ks, g);
         acc = mfma_bf16(zhi[ks], b, acc);
         acc = mfma_bf16(zlo[ks], b, acc);
       }
-      // acc[r] = (Z Q^T)[c = 16 it + 4 g + r][i = 16 t + n]
+      // acc[r] = (Z' Q^T)[b = 16 it + 4 g + r][i = 16 t + n]
       const bf16x4 qc = *reinterpret_cast<const bf16x4*>(&Qs[(t * 16 + n) * PQ + it * 16 + 4 * g]);
       float p = 0.f;
 #pragma unroll

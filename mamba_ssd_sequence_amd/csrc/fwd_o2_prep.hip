@@ -5,9 +5,9 @@
 // Algorithm 3's A^CS restricted to the block), T = cs_last - cs_start and
 // w_j = exp(T - cs_j):
 //   1. the normaliser state contribution of Algorithm 6's H_down at order 2,
-//      kept as the d_h x d_h matrix Z_blk = sum_j w_j k_j k_j^T (the first
-//      d_h^2 floats of the block's state slot), on bf16 MFMA with w k split
-//      into high + low parts;
+//      kept as the d_h x d_h matrix Z_blk = sum_j w_j k_j k_j^T (symmetric:
+//      its upper 16 x 16 tiles, in the block's state slot), on bf16 MFMA with
+//      w k split into high + low parts;
 //   2. the operand record the numerator state scan consumes (layout in
 //      launch.h): fp16 q 2^tau (columns permuted for the MFMA operand), fp16
 //      k^T 2^kap, fp16 X^T 2^xi with X_jc = w_j dt_j v_jc (for the first
@@ -202,8 +202,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
       }
     }
     float* out = state + (bh * nblk + blk) * (int64_t)(DH * DH + DH);
+    // Z is symmetric: only the tiles ct >= bt are formed and stored
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) {
+      if (ct < bt) continue;
       f32x4 acc = zero4();
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
@@ -211,8 +213,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8, 8))) voi
         acc = mfma_bf16(a, bhi[ks], acc);
         acc = mfma_bf16(a, blo[ks], acc);
       }
-      // acc[r] = Z^T[c = 16ct + 4g + r][b = 16bt + n] -> Z[b][c]
-      *reinterpret_cast<f32x4*>(&out[(bt * 16 + n) * DH + ct * 16 + 4 * g]) = acc;
+      // acc[r] = Z^T[c = 16ct + 4g + r][b = 16bt + n] -> Z[b][c], tile (bt, ct)
+      *reinterpret_cast<f32x4*>(&out[256 * z_tile(bt, ct) + 16 * n + 4 * g]) = acc;
     }
   }
   __syncthreads();

@@ -104,9 +104,11 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
   constexpr int NCS = DH / CWG;          // column slices per head
   constexpr int NXW = CWG * DH / 2;      // 32-bit X^T words per block
   static_assert(NAT == 1 || NAT == 2, "one or two a-tiles per wave");
-  constexpr int ZE = DH * DH / NCS / (NT / 2);  // normaliser entries per compute-first thread
+  constexpr int ZPW = Z_FLOATS / NCS;       // stored normaliser entries per workgroup
+  constexpr int ZE = ZPW >= 320 ? 2 : 1;    // ... per scanning thread
+  constexpr int ZTH = ZPW / ZE;             // scanning threads (compute-first ones)
   static_assert(BLK * DH / 8 == NT && 2 * NXW <= NT, "thread mapping");
-  static_assert(ZE * NCS * (NT / 2) == DH * DH && (ZE == 1 || ZE == 2), "normaliser mapping");
+  static_assert(ZPW * NCS == Z_FLOATS && ZTH * ZE == ZPW && ZTH <= NT / 2, "normaliser mapping");
 
   // staging (by step parity, then block within the step), outputs, and the
   // e^{cs} rows (over three slots, because the write-out of step m-1 may
@@ -234,13 +236,19 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
   // normaliser state Z = sum_j w_j k_j k_j^T (2Mamba2Furious, Algorithm 6:
   // the denominator q_i^T Z q_i), scanned over the blocks in place: the slot
   // of block b holds Z_blk(b) (from the block-prep kernel) and receives Z
-  // entering b, Z_in(b + 1) = e^{T_b} Z_in(b) + Z_blk(b).  Each workgroup
-  // scans its 1 / NCS share of the d_h^2 entries, ZE per compute-first thread,
-  // in the slack of those threads' bookkeeping: the loads are issued after
-  // their MFMA work and consumed before the barrier, so no register is held
-  // across the MFMA work; the running sums stay in LDS.
+  // entering b, Z_in(b + 1) = e^{T_b} Z_in(b) + Z_blk(b).  Only the upper
+  // 16 x 16 tiles of the symmetric Z are stored (Z_FLOATS floats).  Each
+  // workgroup scans its 1 / NCS share of them, ZE per thread on the first ZTH
+  // compute-first threads, in the slack of those threads' bookkeeping: the
+  // loads are issued after their MFMA work and consumed before the barrier,
+  // so no register is held across the MFMA work; the running sums stay in
+  // LDS.  The other threads read a valid entry too (a load under a
+  // lane-divergent branch would be waited for at the branch's end) and do
+  // not store.
   constexpr int64_t ZS = DH * DH + DH;  // floats per block slot
-  float* zp = zst + bh * nblk * ZS + pc * (DH * DH / NCS) + tid * ZE;
+  const bool zact = tid < ZTH;
+  const int zi = (zact ? tid : ZTH - 1) * ZE;  // this thread's first entry in the share
+  float* zp = zst + bh * nblk * ZS + pc * ZPW + zi;
   float2 zd0{}, zd1{};
   float zT0 = 0.f, zT1 = 0.f;
   auto zload = [&](int st) {
@@ -266,12 +274,14 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
       s2.x = zT1 * s1.x + zd1.x;
       s2.y = zT1 * s1.y + zd1.y;
     }
-    if constexpr (ZE == 2) {
-      *reinterpret_cast<float2*>(zp + b0 * ZS) = s;
-      if (b1 < nblk) *reinterpret_cast<float2*>(zp + b1 * ZS) = s1;
-    } else {
-      zp[b0 * ZS] = s.x;
-      if (b1 < nblk) zp[b1 * ZS] = s1.x;
+    if (zact) {
+      if constexpr (ZE == 2) {
+        *reinterpret_cast<float2*>(zp + b0 * ZS) = s;
+        if (b1 < nblk) *reinterpret_cast<float2*>(zp + b1 * ZS) = s1;
+      } else {
+        zp[b0 * ZS] = s.x;
+        if (b1 < nblk) zp[b1 * ZS] = s1.x;
+      }
     }
     zrun[tid][0] = s2.x;
     if constexpr (ZE == 2) zrun[tid][1] = s2.y;
@@ -516,10 +526,19 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
   }
   if (wave < NW / 2) {
     drain(nstep - 1, prv);
-    if (final_norm) {
-      float* fz = final_norm + bh * DH * DH + pc * (DH * DH / NCS) + tid * ZE;
+    if (final_norm && zact) {
+      // the full d_h x d_h Z: an entry of an off-diagonal tile also goes to
+      // its mirror position
+      float* fz = final_norm + bh * DH * DH;
 #pragma unroll
-      for (int e = 0; e < ZE; ++e) fz[e] = zrun[tid][e];
+      for (int e = 0; e < ZE; ++e) {
+        const int E = pc * ZPW + zi + e, t = E >> 8, w = E & 255;
+        const int bt = t < 4 ? 0 : t < 7 ? 1 : t < 9 ? 2 : 3, ct = bt + t - z_tile(bt, bt);
+        const int b = 16 * bt + (w >> 4), c = 16 * ct + (w & 15);
+        const float z = zrun[tid][e];
+        fz[b * DH + c] = z;
+        if (bt != ct) fz[c * DH + b] = z;
+      }
     }
   }
 

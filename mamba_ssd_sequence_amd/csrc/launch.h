@@ -48,11 +48,20 @@ constexpr int SC_T = 0, SC_DELTA = 1, SC_TAU = 2, SC_KAP = 3, SC_XI = 4, SC_ET =
               SC_ETS = 7, SC_XF = 8, SC_SIG_OUT = 9, SC_EPRE = 10;
 constexpr int REC_BYTES = 24880;
 
+// Order-2 normaliser state Z (d_h = 64, symmetric) in a block's state slot:
+// only its upper 16 x 16 tiles (bt <= ct, 10 of 16) are stored, tile (bt, ct)
+// row-major at float offset 256 z_tile(bt, ct), so that Z[b][c] for
+// b in tile bt <= ct and c in tile ct sits at 256 z_tile(bt, ct) + 16 (b % 16)
+// + c % 16.
+constexpr int Z_TILES = 10, Z_FLOATS = 256 * Z_TILES;
+__host__ __device__ constexpr int z_tile(int bt, int ct) { return bt * 4 - bt * (bt - 1) / 2 + (ct - bt); }
+
 // Workspace layout (float offsets), in this order:
 //   tb     [BH, nblk]                 block decay totals
 //   state  [BH, nblk, DH*DH + DH]     per-block state contributions, then
 //                                     (in place) the state entering each block
-//                                     (order 1: S and z; order 2: Z and unused)
+//                                     (order 1: S and z; order 2: the upper
+//                                     tiles of Z, Z_FLOATS floats, rest unused)
 //   part   [BH, rows, 64]             order 2 only: inter-block numerators
 //                                     (rows = o2_part_rows(N), padded to
 //                                     whole steps)

@@ -17,8 +17,15 @@ Stand-ins (2Mamba2Furious, Algorithm 2 "Mamba-2 Setup" and Algorithm 3
   y + log(-expm1(-y)), the numerically safe form of Algorithm 2's
   dt_init + log(1 - exp(-dt_init)).
 
+* A_P stands for the per-token projection h.W_A of the A-mask of Mamba-2S /
+  2Mamba (Algorithms 4 and 5, A = -softplus(h.W_A)); the pages give no
+  distribution for it, and it is drawn as N(-3, 1), so that a typical token
+  decays by e^{-softplus(-3)} ~ 0.95 (per-token decays from ~0.7 to ~0.999
+  within two standard deviations).
+
 Draw order (fixed, numpy PCG64 ``default_rng(seed)``): Q, K, V (each
-[B,H,N,d_h]), dt_P [B,H,N], A_log [H], then the dt_init exponent [H].
+[B,H,N,d_h]), dt_P [B,H,N], A_log [H], the dt_init exponent [H], then A_P
+[B,H,N].
 """
 from __future__ import annotations
 
@@ -132,6 +139,7 @@ class ForwardInputs:
     dt_proj: np.ndarray  # [B,H,N] fp32
     A_log: np.ndarray  # [H] fp32
     dt_bias: np.ndarray  # [H] fp32
+    A_proj: np.ndarray = None  # [B,H,N] fp32 (A-mask projection A_P)
 
     def qkv_f64(self):
         """The stored q, k, v values, exactly, as fp64 (for the oracle)."""
@@ -171,7 +179,8 @@ def make_forward_inputs(cfg: Config, *, B=None, H=None, N=None, seed=None) -> Fo
         arrs.append(_store(x, cfg.dtype))
     dt_proj = rng.standard_normal((B, H, N)).astype(np.float32)
     A_log, dt_bias = draw_head_params(rng, H)
-    return ForwardInputs(cfg, arrs[0], arrs[1], arrs[2], dt_proj, A_log, dt_bias)
+    A_proj = (rng.standard_normal((B, H, N)) - 3.0).astype(np.float32)
+    return ForwardInputs(cfg, arrs[0], arrs[1], arrs[2], dt_proj, A_log, dt_bias, A_proj)
 
 
 @dataclasses.dataclass

@@ -13,6 +13,9 @@ Mongaras & Larson):
   normaliser = row sum of the same masked score matrix, output y / normaliser.
 * Algorithm 3 (Mamba-2 forward pass): A = -exp(A_log), dt = softplus(dt_P +
   dt_bias), V_dt = V * dt, A^CS = cumsum(A * dt).
+* Algorithms 4 and 5, the A-mask of Mamba-2S / 2Mamba: per-token A =
+  -softplus(h W_A), A^CS = cumsum(A) with no dt in it; Algorithm 4 keeps
+  V_dt = V * dt with dt = softplus(h W_dt) (no bias), Algorithm 5 uses plain V.
 * Algorithms 4 and 5 (Mamba-2S, 2Mamba): decay mask A^M_ij = exp(A^CS_i -
   A^CS_j), causal mask M_ij = [i >= j], and for 2Mamba the scores are squared
   and the normaliser is the row sum of the squared, masked scores.
@@ -67,6 +70,41 @@ def discretise(dt_proj, dt_bias, A_log):
     dt = softplus(dt_proj + dt_bias[:, None])
     a = A[:, None] * dt
     return dt, a
+
+
+def discretise_amask(A_proj, dt_proj=None):
+    """Algorithms 4 and 5 (Mamba-2S, 2Mamba): the A-mask A = -softplus(h W_A)
+    per token, with A^CS = cumsum(A) -- no dt in the decay.
+
+    A_proj: [..., H, N], the projection A_P = h W_A.  Returns (dt, a): a = A
+    (always < 0); dt = softplus(dt_P) with no bias (Algorithm 4, value operand
+    V * dt), or None when dt_proj is None (Algorithm 5, plain V).
+    """
+    a = -softplus(A_proj)
+    dt = None if dt_proj is None else softplus(dt_proj)
+    return dt, a
+
+
+def _chunked_cumsum(a, chunk):
+    """Inclusive cumsum of a restarted at every chunk start, and chunk totals."""
+    N = a.shape[-1]
+    n_chunks = -(-N // chunk)
+    a_cs = np.empty_like(a)
+    a_chunk = np.empty(a.shape[:-1] + (n_chunks,), dtype=np.float64)
+    for c in range(n_chunks):
+        seg = a[..., c * chunk:(c + 1) * chunk]
+        cs = np.cumsum(seg, axis=-1)
+        a_cs[..., c * chunk:(c + 1) * chunk] = cs
+        a_chunk[..., c] = cs[..., -1]
+    return a_cs, a_chunk
+
+
+def prep_amask_ref(A_proj, dt_proj, chunk):
+    """What ssd_prep_amask returns, in fp64: (dt or None, a_cs, a_chunk), with
+    a = -softplus(A_P) chunked as in prep_ref."""
+    dt, a = discretise_amask(A_proj, dt_proj)
+    a_cs, a_chunk = _chunked_cumsum(a, chunk)
+    return dt, a_cs, a_chunk
 
 
 def prep_ref(dt_proj, dt_bias, A_log, chunk):
@@ -196,6 +234,20 @@ def forward_ref(q, k, v, dt_proj, dt_bias, A_log, order, rows=None):
     dt, a = discretise(dt_proj, dt_bias, A_log)
     vdt = np.asarray(v, dtype=np.float64) * dt[..., None]
     out = forward_quadratic(q, k, vdt, a, order, rows=rows)
+    out["dt"] = dt
+    out["a"] = a
+    return out
+
+
+def forward_amask_ref(q, k, v, A_proj, dt_proj, order, rows=None):
+    """End-to-end forward with the A-mask of Algorithms 4 and 5: a =
+    -softplus(A_P), A^CS = cumsum(a); value operand V * softplus(dt_P)
+    (Algorithm 4) or plain V when dt_proj is None (Algorithm 5)."""
+    dt, a = discretise_amask(A_proj, dt_proj)
+    vop = np.asarray(v, dtype=np.float64)
+    if dt is not None:
+        vop = vop * dt[..., None]
+    out = forward_quadratic(q, k, vop, a, order, rows=rows)
     out["dt"] = dt
     out["a"] = a
     return out

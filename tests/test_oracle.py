@@ -340,3 +340,52 @@ def test_error_scale_bounds_an_fp32_evaluation(order):
     assert err.max() <= 1e-5
     if order == 1:
         assert ref["kappa"].max() > 50  # the case really contains ill-conditioned rows
+
+
+# ---------------------------------------------------------------------------
+# A-mask of Algorithms 4 and 5 (Mamba-2S, 2Mamba): A = -softplus(h W_A),
+# A^CS = cumsum(A); Algorithm 4's dt = softplus(h W_dt) without bias
+# ---------------------------------------------------------------------------
+
+def test_amask_reduces_to_algorithm3_with_unit_A_and_no_bias():
+    # Algorithm 3 with A_log = 0 (A = -1) and dt_bias = 0 gives a = -softplus(dt_P)
+    # and dt = softplus(dt_P): exactly the A-mask with A_P = dt_P
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((2, 3, 200)) * 2.0
+    zeros = np.zeros(3)
+    for chunk in (64, 128):
+        dt3, cs3, tot3 = O.prep_ref(x, zeros, zeros, chunk)
+        dt4, cs4, tot4 = O.prep_amask_ref(x, x, chunk)
+        np.testing.assert_array_equal(dt4, dt3)
+        np.testing.assert_array_equal(cs4, cs3)
+        np.testing.assert_array_equal(tot4, tot3)
+    dtn, csn, _ = O.prep_amask_ref(x, None, 64)
+    assert dtn is None
+    np.testing.assert_array_equal(csn, O.prep_ref(x, zeros, zeros, 64)[1])
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_amask_two_tokens_hand_worked(order):
+    # A_P = 0 for both tokens: a = -log 2, so token 1 reaches token 2 with weight
+    # 1/2.  q = (1, 2), k = (3, 1), v = (4, 5), d_h = 1:
+    #   order 1: y_2 = (2*3/2*4 + 2*1*5) / (2*3/2 + 2*1) = 22/5
+    #   order 2: y_2 = ((2*3)^2/2*4 + (2*1)^2*5) / ((2*3)^2/2 + (2*1)^2) = 46/11
+    # and y_1 = v_1 = 4.  With dt_P = 0 (dt = log 2) the value operand is V log 2.
+    q = np.array([1.0, 2.0]).reshape(1, 1, 2, 1)
+    k = np.array([3.0, 1.0]).reshape(1, 1, 2, 1)
+    v = np.array([4.0, 5.0]).reshape(1, 1, 2, 1)
+    A_P = np.zeros((1, 1, 2))
+    y2 = float(Fraction(22, 5)) if order == 1 else float(Fraction(46, 11))
+    plain = O.forward_amask_ref(q, k, v, A_P, None, order)["y"][0, 0, :, 0]
+    np.testing.assert_allclose(plain, [4.0, y2], rtol=1e-14)
+    scaled = O.forward_amask_ref(q, k, v, A_P, np.zeros((1, 1, 2)), order)["y"][0, 0, :, 0]
+    np.testing.assert_allclose(scaled, [4.0 * math.log(2), y2 * math.log(2)], rtol=1e-14)
+
+
+def test_amask_decay_negative_and_monotone():
+    x = np.linspace(-30.0, 30.0, 601)
+    _, a = O.discretise_amask(x)
+    assert np.all(a < 0)
+    assert np.all(np.diff(a) < 0)
+    np.testing.assert_allclose(a[300], -math.log(2), rtol=1e-15)  # A_P = 0
+    np.testing.assert_allclose(a[-1], -30.0, rtol=1e-12)           # softplus(x) ~ x for large x

@@ -93,7 +93,9 @@ def to_dev(x, dtype, dev):
 # forward
 # ---------------------------------------------------------------------------
 
-def bench_forward(cfg: I.Config, steps: int, warmup: int, dev):
+def bench_forward(cfg: I.Config, steps: int, warmup: int, dev, amask: bool = False):
+    """amask: the step is ssd_prep_amask (Algorithm 5's A-mask, plain V) and
+    ssd_forward with no dt, instead of ssd_prep (Algorithm 3) and V*dt."""
     import torch
     from mamba_ssd_sequence_amd import ssd
 
@@ -112,11 +114,16 @@ def bench_forward(cfg: I.Config, steps: int, warmup: int, dev):
                                         ssd.SSD_BF16 if cfg.dtype == I.BF16 else ssd.SSD_F32),
                      dtype=torch.uint8, device=dev)
 
+    A_proj = to_dev(inp.A_proj, I.F32, dev)
+
     def step(timer=None):
-        ssd.prep(dtp, bias, alog, cfg.chunk, out=(dt, a_cs, a_chunk))
+        if amask:
+            ssd.prep_amask(A_proj, None, cfg.chunk, out=(None, a_cs, a_chunk))
+        else:
+            ssd.prep(dtp, bias, alog, cfg.chunk, out=(dt, a_cs, a_chunk))
         if timer is not None:
             timer.arm()
-        ssd.forward(q, k, v, dt, a_cs, cfg.order, cfg.chunk, y=y, workspace=ws)
+        ssd.forward(q, k, v, None if amask else dt, a_cs, cfg.order, cfg.chunk, y=y, workspace=ws)
         if timer is not None:
             timer.collect()
 
@@ -143,7 +150,7 @@ def bench_forward(cfg: I.Config, steps: int, warmup: int, dev):
     kern_ms = dict(zip(names, per.mean(axis=0).tolist()))
     assert bool(torch.isfinite(y).all())
     tokens = B * N
-    res = {"workload": cfg.name, "ms_per_step": ms, "tokens_per_s": tokens / (ms * 1e-3),
+    res = {"workload": cfg.name + ("_amask" if amask else ""), "ms_per_step": ms, "tokens_per_s": tokens / (ms * 1e-3),
            "kernels_ms": kern_ms, "B": B, "H": H, "N": N, "d_h": d, "order": cfg.order,
            "chunk": cfg.chunk, "dtype": cfg.dtype}
     if cfg.order == 2:
@@ -368,11 +375,13 @@ def main():
 
     extra = []
     if not a.no_extra:
-        for name in ("o2_bf16_64k", "o1_bf16_2k", "o2_decode"):
+        for name in ("o2_bf16_64k", "o1_bf16_2k", "o2_decode", "o2_bf16_4k_amask"):
             if name == a.workload:
                 continue
             torch.cuda.empty_cache()
-            if name in I.CONFIGS:
+            if name == "o2_bf16_4k_amask":
+                r, _ = bench_forward(I.CONFIGS["o2_bf16_4k"], a.steps, a.warmup, dev, amask=True)
+            elif name in I.CONFIGS:
                 r, _ = bench_forward(I.CONFIGS[name], max(3, a.steps // 4), 2, dev)
             else:
                 c = I.DECODE_CONFIGS[name]

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 1
+#define SSD_ABI_VERSION 2
 
 typedef enum {
   SSD_OK = 0,
@@ -92,6 +92,29 @@ const char* ssd_last_error(void);
 ssd_status ssd_prep(const float* dt_proj, const float* dt_bias, const float* A_log,
                     int64_t B, int64_t H, int64_t N, int64_t chunk,
                     float* dt, float* a_cs, float* a_chunk, hipStream_t stream);
+
+/*
+ * ssd_prep_amask -- the A-mask of Mamba-2S and 2Mamba (Algorithms 4 and 5):
+ * a per-token A = -softplus(A_P) and A^CS = cumsum(A), with no dt in the
+ * decay; Algorithm 4's dt = softplus(dt_P) (no bias) for the value operand
+ * V*dt, or no dt at all (Algorithm 5 multiplies the scores by plain V: pass
+ * dt_proj = dt = NULL here and dt = NULL to ssd_forward).
+ *
+ *   A_proj  [B,H,N] f32   per-token projection A_P = h W_A
+ *   dt_proj [B,H,N] f32   per-token dt logits, or NULL
+ *   chunk           cumsum segment length: 64 or 128
+ *   dt      [B,H,N] f32   out: softplus(dt_P); must be NULL iff dt_proj is NULL
+ *   a_cs    [B,H,N] f32   out: inclusive cumsum of A restarted at every
+ *                         multiple of `chunk`
+ *   a_chunk [B,H,ceil(N/chunk)] f32  out: total of A over each chunk
+ *
+ * All pointers are device pointers owned by the caller; errors as ssd_prep
+ * (SSD_ERR_NULL also when exactly one of dt_proj, dt is NULL).  a_cs and
+ * a_chunk feed ssd_forward exactly as ssd_prep's do.
+ */
+ssd_status ssd_prep_amask(const float* A_proj, const float* dt_proj, int64_t B, int64_t H,
+                          int64_t N, int64_t chunk, float* dt, float* a_cs, float* a_chunk,
+                          hipStream_t stream);
 
 /* Workspace bytes ssd_forward needs for these sizes (0 if none; the same
  * validation as ssd_forward applies, and an invalid combination returns 0). */

@@ -160,6 +160,37 @@ ssd_status ssd_prep(const float* dt_proj, const float* dt_bias, const float* A_l
   }
 }
 
+ssd_status ssd_prep_amask(const float* A_proj, const float* dt_proj, int64_t B, int64_t H,
+                          int64_t N, int64_t chunk, float* dt, float* a_cs, float* a_chunk,
+                          hipStream_t stream) {
+  try {
+    clear_err();
+    if (!A_proj || !a_cs || !a_chunk)
+      return fail(SSD_ERR_NULL, "ssd_prep_amask: a required pointer is NULL");
+    if ((dt_proj == nullptr) != (dt == nullptr))
+      return fail(SSD_ERR_NULL, "ssd_prep_amask: dt_proj and dt must both be given or both be NULL");
+    int64_t BH, BHN;
+    if (!mul_ok(B, H, &BH) || !mul_ok(BH, N, &BHN))
+      return fail(SSD_ERR_SHAPE, "ssd_prep_amask: B, H, N must be >= 1 and must not overflow");
+    if (chunk != 64 && chunk != 128)
+      return fail(SSD_ERR_UNSUPPORTED, "ssd_prep_amask: chunk %lld (64 or 128)", (long long)chunk);
+    const int64_t nc = (N + chunk - 1) / chunk;
+    if ((BH * nc + 3) / 4 > (int64_t)0x7fffffff)
+      return fail(SSD_ERR_SHAPE, "ssd_prep_amask: grid too large");
+    const Range ins[] = {{"A_proj", A_proj, (size_t)BHN * 4}, {"dt_proj", dt_proj, (size_t)BHN * 4}};
+    const Range outs[] = {{"dt", dt, (size_t)BHN * 4},
+                          {"a_cs", a_cs, (size_t)BHN * 4},
+                          {"a_chunk", a_chunk, (size_t)(BH * nc) * 4}};
+    ssd_status s;
+    if ((s = check_aligned(ins, 2)) != SSD_OK || (s = check_aligned(outs, 3)) != SSD_OK) return s;
+    if ((s = check_alias(outs, 3, ins, 2)) != SSD_OK) return s;
+    return hip_status(ssd::launch_prep_amask(A_proj, dt_proj, B, H, N, chunk, dt, a_cs, a_chunk, stream),
+                      "ssd_prep_amask launch");
+  } catch (...) {
+    return fail(SSD_ERR_HIP, "ssd_prep_amask: unexpected exception");
+  }
+}
+
 size_t ssd_forward_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d_h, int order,
                                   int64_t chunk, int dtype) {
   int64_t BH, BHN, BHNd;

@@ -92,6 +92,12 @@ hipError_t launch_prep(const float* dt_proj, const float* dt_bias, const float* 
                        int64_t H, int64_t N, int64_t chunk, float* dt, float* a_cs, float* a_chunk,
                        hipStream_t stream);
 
+// Algorithms 4 / 5 A-mask: a = -softplus(A_proj), dt = softplus(dt_proj) (no
+// bias) if dt_proj is not NULL (dt is then written), chunk-local cumsum.
+hipError_t launch_prep_amask(const float* A_proj, const float* dt_proj, int64_t B, int64_t H,
+                             int64_t N, int64_t chunk, float* dt, float* a_cs, float* a_chunk,
+                             hipStream_t stream);
+
 // Per-block state contributions: state[bh,blk] = sum_j w_j k_j val_j^T and
 // sum_j w_j k_j with w_j = exp(A^CS_last - A^CS_j); val = v*dt (dt != NULL) or v.
 hipError_t launch_chunk_state(bool bf16, int64_t DH, const void* k, const void* v, const float* dt,

@@ -45,6 +45,8 @@ def _declare(lib):
     lib.ssd_last_error.argtypes = []
     lib.ssd_prep.restype = ctypes.c_int
     lib.ssd_prep.argtypes = [fp, fp, fp, i64, i64, i64, i64, fp, fp, fp, vp]
+    lib.ssd_prep_amask.restype = ctypes.c_int
+    lib.ssd_prep_amask.argtypes = [fp, fp, i64, i64, i64, i64, fp, fp, fp, vp]
     lib.ssd_forward_workspace_size.restype = sz
     lib.ssd_forward_workspace_size.argtypes = [i64, i64, i64, i64, i32, i64, i32]
     lib.ssd_forward.restype = ctypes.c_int
@@ -137,6 +139,28 @@ def prep(dt_proj, dt_bias, A_log, chunk: int, out=None):
     dt, a_cs, a_chunk = out
     _check(lib().ssd_prep(_ptr(dt_proj), _ptr(dt_bias), _ptr(A_log), B, H, N, chunk,
                           _ptr(dt), _ptr(a_cs), _ptr(a_chunk), _stream(dev)))
+    return dt, a_cs, a_chunk
+
+
+def prep_amask(A_proj, dt_proj, chunk: int, out=None):
+    """ssd_prep_amask (the A-mask of Algorithms 4 and 5): returns (dt or None,
+    a_cs, a_chunk); dt_proj None means no dt (plain value operand)."""
+    torch = _torch()
+    f32 = torch.float32
+    _require(A_proj, "A_proj", f32)
+    dev = A_proj.device
+    if dt_proj is not None:
+        _require(dt_proj, "dt_proj", f32, dev)
+        if dt_proj.shape != A_proj.shape:
+            raise ValueError("dt_proj must have the shape of A_proj")
+    B, H, N = A_proj.shape
+    nc = -(-N // chunk)
+    if out is None:
+        out = (torch.empty_like(A_proj) if dt_proj is not None else None, torch.empty_like(A_proj),
+               torch.empty((B, H, nc), dtype=f32, device=dev))
+    dt, a_cs, a_chunk = out
+    _check(lib().ssd_prep_amask(_ptr(A_proj), _ptr(dt_proj), B, H, N, chunk, _ptr(dt), _ptr(a_cs),
+                                _ptr(a_chunk), _stream(dev)))
     return dt, a_cs, a_chunk
 
 

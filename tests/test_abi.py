@@ -17,14 +17,15 @@ def lib():
 
 def test_exports_every_header_function(lib):
     names = ssd.header_functions()
-    assert set(names) >= {"ssd_prep", "ssd_forward", "ssd_forward_workspace_size", "ssd_decode_step",
+    assert set(names) >= {"ssd_prep", "ssd_prep_amask", "ssd_forward", "ssd_forward_workspace_size",
+                          "ssd_decode_step",
                           "ssd_abi_version", "ssd_status_str", "ssd_last_error"}
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssd_abi_version() == 1
+    assert lib.ssd_abi_version() == 2
     for i, name in enumerate(ssd.STATUS):
         assert lib.ssd_status_str(i).decode() == name
     assert lib.ssd_status_str(99).decode() == "SSD_ERR_UNKNOWN"
@@ -45,6 +46,24 @@ def test_prep_errors(lib):
     assert prep(lib, ptrs=[A[0] + 4] + A[1:6]) == 4
     assert prep(lib, ptrs=A[:3] + [A[0]] + A[4:6]) == 5  # dt output aliases dt_proj
     assert prep(lib, ptrs=A[:3] + [A[3], A[3] + 16, A[5]]) == 5  # outputs overlap each other
+
+
+def prep_amask(lib, *, ptrs=None, B=1, H=2, N=100, chunk=64):
+    p = [A[0], A[1], A[3], A[4], A[5]] if ptrs is None else ptrs
+    return lib.ssd_prep_amask(p[0], p[1], B, H, N, chunk, p[2], p[3], p[4], None)
+
+
+def test_prep_amask_errors(lib):
+    assert prep_amask(lib, ptrs=[None, A[1], A[3], A[4], A[5]]) == 1
+    assert prep_amask(lib, ptrs=[A[0], None, A[3], A[4], A[5]]) == 1  # dt without dt_proj
+    assert "both" in lib.ssd_last_error().decode()
+    assert prep_amask(lib, ptrs=[A[0], A[1], None, A[4], A[5]]) == 1  # dt_proj without dt
+    assert prep_amask(lib, B=0) == 2
+    assert prep_amask(lib, N=-1) == 2
+    assert prep_amask(lib, chunk=256) == 3
+    assert prep_amask(lib, ptrs=[A[0] + 8, A[1], A[3], A[4], A[5]]) == 4
+    assert prep_amask(lib, ptrs=[A[0], A[1], A[3], A[0], A[5]]) == 5  # a_cs aliases A_proj
+    assert prep_amask(lib, ptrs=[A[0], None, None, A[4], A[4] + 16]) == 5  # outputs overlap
 
 
 def fwd(lib, *, B=1, H=2, N=100, d_h=64, order=1, chunk=64, dtype=1, ws=None, wbytes=None,

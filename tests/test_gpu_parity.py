@@ -192,6 +192,82 @@ def test_forward_full_size(name, n_random):
 
 
 # ---------------------------------------------------------------------------
+# the A-mask of Algorithms 4 and 5 (ssd_prep_amask + the same forward)
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("name", list(I.CONFIGS))
+@pytest.mark.parametrize("with_dt", [True, False])
+def test_prep_amask_full_size(name, with_dt):
+    cfg = I.CONFIGS[name]
+    say("prep amask", name, with_dt)
+    inp = I.make_forward_inputs(cfg)
+    ssd = ssd_mod()
+    dtp = inp.dt_proj if with_dt else None
+    dt, a_cs, a_chunk = ssd.prep_amask(to_dev_f32(inp.A_proj), to_dev_f32(dtp) if with_dt else None,
+                                       cfg.chunk)
+    torch.cuda.synchronize()
+    dt_r, cs_r, tot_r = O.prep_amask_ref(inp.A_proj, dtp, cfg.chunk)
+    if with_dt:
+        np.testing.assert_allclose(dt.cpu().numpy(), dt_r, rtol=2e-6, atol=0)
+    else:
+        assert dt is None
+    err = np.abs(a_cs.cpu().numpy() - cs_r)  # a < 0: as in test_prep_full_size
+    bound = 1e-5 * np.abs(cs_r) + 1e-6
+    assert np.all(err <= bound), float((err / bound).max())
+    np.testing.assert_allclose(a_chunk.cpu().numpy(), tot_r, rtol=2e-6, atol=1e-6)
+
+
+def run_forward_amask(inp, order, chunk, with_dt):
+    ssd = ssd_mod()
+    q, k, v = (to_dev_qkv(x, inp.cfg.dtype) for x in (inp.q, inp.k, inp.v))
+    dt, a_cs, _ = ssd.prep_amask(to_dev_f32(inp.A_proj), to_dev_f32(inp.dt_proj) if with_dt else None,
+                                 chunk)
+    B, H, N, d = q.shape
+    den = torch.empty((B, H, N), device="cuda")
+    y = ssd.forward(q, k, v, dt, a_cs, order, chunk, den=den)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), den.cpu().numpy()
+
+
+# (config, order, B, H, N, chunk, value operand V*dt (Algorithm 4) or plain V (Algorithm 5))
+AMASK = [
+    ("o1_f32_small", 1, 1, 2, 200, 64, True), ("o1_bf16_2k", 1, 2, 2, 333, 128, True),
+    ("o1_bf16_2k", 1, 1, 2, 130, 64, False),
+    ("o2_bf16_4k", 2, 1, 2, 257, 64, False), ("o2_bf16_4k", 2, 2, 16, 300, 64, False),
+    ("o2_bf16_4k", 2, 1, 3, 200, 128, True),
+]
+
+
+@pytest.mark.parametrize("name,order,B,H,N,chunk,with_dt", AMASK)
+def test_forward_amask_small(name, order, B, H, N, chunk, with_dt):
+    say("forward amask", name, order, B, H, N, chunk, with_dt)
+    cfg = I.CONFIGS[name]
+    inp = I.make_forward_inputs(cfg, B=B, H=H, N=N, seed=3 * N + H)
+    y, den = run_forward_amask(inp, order, chunk, with_dt)
+    q, k, v = inp.qkv_f64()
+    ref = O.forward_amask_ref(q, k, v, inp.A_proj, inp.dt_proj if with_dt else None, order)
+    err = row_error(y, ref["y"], ref["scale"])
+    say("  err", err)
+    assert err <= TOL[cfg.dtype]
+    den_err = np.abs(den - ref["den"]) / (ref["kappa"] * np.abs(ref["den"]))
+    assert float(den_err.max()) <= TOL[cfg.dtype]
+
+
+def test_forward_amask_full_size_2mamba():
+    # Algorithm 5 at the order-2 4K workload: plain V, sampled rows
+    cfg = I.CONFIGS["o2_bf16_4k"]
+    say("forward amask full o2_bf16_4k")
+    inp = I.make_forward_inputs(cfg)
+    y, _ = run_forward_amask(inp, 2, cfg.chunk, False)
+    rows = sample_rows(cfg.N, 48, np.random.default_rng(5))
+    q, k, v = inp.qkv_f64()
+    ref = O.forward_amask_ref(q, k, v, inp.A_proj, None, 2, rows=rows)
+    err = row_error(y[:, :, rows], ref["y"], ref["scale"])
+    say("  err", err)
+    assert err <= TOL[cfg.dtype]
+
+
+# ---------------------------------------------------------------------------
 # decode
 # ---------------------------------------------------------------------------
 

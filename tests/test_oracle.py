@@ -389,3 +389,22 @@ def test_amask_decay_negative_and_monotone():
     assert np.all(np.diff(a) < 0)
     np.testing.assert_allclose(a[300], -math.log(2), rtol=1e-15)  # A_P = 0
     np.testing.assert_allclose(a[-1], -30.0, rtol=1e-12)           # softplus(x) ~ x for large x
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_initial_state_continues_the_sequence(order):
+    """Algorithm 6 with a nonzero initial state: the recurrence over a suffix,
+    started from the state a prefix leaves, gives the full sequence's outputs
+    (from the quadratic form) and its final state."""
+    rng = np.random.default_rng(21)
+    q, k, v, a = rand_case(rng, 1, 2, 90, 3, signed=False)
+    full = O.forward_quadratic(q, k, v, a, order)
+    _, _, S_all, z_all = O.forward_recurrent(q, k, v, a, order)
+    for n1 in (1, 37, 64, 89):
+        _, _, S1, z1 = O.forward_recurrent(q[:, :, :n1], k[:, :, :n1], v[:, :, :n1], a[:, :, :n1], order)
+        y2, den2, S2, z2 = O.forward_recurrent(q[:, :, n1:], k[:, :, n1:], v[:, :, n1:], a[:, :, n1:],
+                                               order, S0=S1, z0=z1)
+        assert rel_err(y2, full["y"][:, :, n1:], full["scale"][:, :, n1:]) <= 1e-10
+        np.testing.assert_allclose(den2, full["den"][:, :, n1:], rtol=1e-10)
+        np.testing.assert_allclose(S2, S_all, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(z2, z_all, rtol=1e-10, atol=1e-12)

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 2
+#define SSD_ABI_VERSION 3
 
 typedef enum {
   SSD_OK = 0,
@@ -132,6 +132,13 @@ size_t ssd_forward_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d_h,
  *                        prints it, plain V).
  *   a_cs    [B,H,N] f32  chunk-local cumsum from ssd_prep with the same
  *                        `chunk` (every decay is derived from it alone)
+ *   initial_state [B,H,D,d_h] f32, initial_norm [B,H,D] f32: in, optional
+ *                        (both or neither; NULL = zero): the numerator and
+ *                        normaliser states before token 0 (Algorithm 6 H_up,
+ *                        H_down; the layout of final_state / final_norm,
+ *                        e.g. a previous segment's), decayed from the segment
+ *                        start by the cumsum of this segment's a_cs.  Must not
+ *                        overlap any output.
  *   d_h                  32 or 64 (order 1); 64 (order 2)
  *   order                1 or 2 (order 2 requires SSD_BF16)
  *   chunk                64 or 128 (the a_cs segmentation)
@@ -149,7 +156,8 @@ size_t ssd_forward_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d_h,
  * inf/nan, as the definition does.
  */
 ssd_status ssd_forward(const void* q, const void* k, const void* v, const float* dt,
-                       const float* a_cs, int64_t B, int64_t H, int64_t N, int64_t d_h, int order, int64_t chunk,
+                       const float* a_cs, const float* initial_state, const float* initial_norm,
+                       int64_t B, int64_t H, int64_t N, int64_t d_h, int order, int64_t chunk,
                        int dtype, float* y, float* den, float* final_state, float* final_norm,
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 

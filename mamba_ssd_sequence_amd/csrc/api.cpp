@@ -199,7 +199,8 @@ size_t ssd_forward_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d_h, 
 }
 
 ssd_status ssd_forward(const void* q, const void* k, const void* v, const float* dt,
-                       const float* a_cs, int64_t B, int64_t H, int64_t N, int64_t d_h, int order,
+                       const float* a_cs, const float* initial_state, const float* initial_norm,
+                       int64_t B, int64_t H, int64_t N, int64_t d_h, int order,
                        int64_t chunk, int dtype, float* y, float* den, float* final_state,
                        float* final_norm, void* workspace, size_t workspace_bytes,
                        hipStream_t stream) {
@@ -208,6 +209,8 @@ ssd_status ssd_forward(const void* q, const void* k, const void* v, const float*
     if (!q || !k || !v || !a_cs || !y) return fail(SSD_ERR_NULL, "ssd_forward: a required pointer is NULL");
     if ((final_state == nullptr) != (final_norm == nullptr))
       return fail(SSD_ERR_NULL, "ssd_forward: final_state and final_norm must be given together");
+    if ((initial_state == nullptr) != (initial_norm == nullptr))
+      return fail(SSD_ERR_NULL, "ssd_forward: initial_state and initial_norm must be given together");
     int64_t BH, BHN, BHNd;
     ssd_status s = validate_forward_sizes(B, H, N, d_h, order, chunk, dtype, &BH, &BHN, &BHNd);
     if (s != SSD_OK) return s;
@@ -219,14 +222,16 @@ ssd_status ssd_forward(const void* q, const void* k, const void* v, const float*
                   workspace ? workspace_bytes : (size_t)0);
     const Range ins[] = {{"q", q, (size_t)BHNd * es},  {"k", k, (size_t)BHNd * es},
                          {"v", v, (size_t)BHNd * es},  {"dt", dt, (size_t)BHN * 4},
-                         {"a_cs", a_cs, (size_t)BHN * 4}};
+                         {"a_cs", a_cs, (size_t)BHN * 4},
+                         {"initial_state", initial_state, (size_t)(BH * D * d_h) * 4},
+                         {"initial_norm", initial_norm, (size_t)(BH * D) * 4}};
     const Range outs[] = {{"y", y, (size_t)BHNd * 4},
                           {"den", den, (size_t)BHN * 4},
                           {"final_state", final_state, (size_t)(BH * D * d_h) * 4},
                           {"final_norm", final_norm, (size_t)(BH * D) * 4},
                           {"workspace", workspace, need}};
-    if ((s = check_aligned(ins, 5)) != SSD_OK || (s = check_aligned(outs, 5)) != SSD_OK) return s;
-    if ((s = check_alias(outs, 5, ins, 5)) != SSD_OK) return s;
+    if ((s = check_aligned(ins, 7)) != SSD_OK || (s = check_aligned(outs, 5)) != SSD_OK) return s;
+    if ((s = check_alias(outs, 5, ins, 7)) != SSD_OK) return s;
 
     const bool bf = dtype == SSD_BF16;
     Timer tm(stream);
@@ -239,7 +244,8 @@ ssd_status ssd_forward(const void* q, const void* k, const void* v, const float*
       if ((e = ssd::launch_chunk_state(bf, d_h, k, v, dt, a_cs, BH, N, chunk, tb, st, stream)) != hipSuccess)
         return hip_status(e, "chunk_state launch");
       tm.mark();
-      if ((e = ssd::launch_state_pass(d_h, BH, N, tb, st, final_state, final_norm, stream)) != hipSuccess)
+      if ((e = ssd::launch_state_pass(d_h, BH, N, tb, st, final_state, final_norm, initial_state,
+                                      initial_norm, stream)) != hipSuccess)
         return hip_status(e, "state_pass launch");
       tm.mark();
       e = ssd::launch_output(bf, d_h, 1, q, k, v, dt, a_cs, BH, N, chunk, st, nullptr, y, den, stream);
@@ -254,10 +260,17 @@ ssd_status ssd_forward(const void* q, const void* k, const void* v, const float*
     if ((e = ssd::launch_o2_blockprep(q, k, v, dt, a_cs, BH, N, chunk, tb, st, rec, stream)) != hipSuccess)
       return hip_status(e, "o2_blockprep launch");
     tm.mark();
-    if ((e = ssd::launch_o2_scale_scan(rec, BH, N, stream)) != hipSuccess)
+    float* initmax = nullptr;
+    if (initial_state) {
+      initmax = ws + L.initmax;
+      if ((e = ssd::launch_o2_initmax(initial_state, BH, initmax, stream)) != hipSuccess)
+        return hip_status(e, "o2_initmax launch");
+    }
+    if ((e = ssd::launch_o2_scale_scan(rec, BH, N, initmax, stream)) != hipSuccess)
       return hip_status(e, "o2_scale_scan launch");
     tm.mark();
-    if ((e = ssd::launch_o2_state(rec, BH, N, part, final_state, st, final_norm, stream)) != hipSuccess)
+    if ((e = ssd::launch_o2_state(rec, BH, N, part, final_state, st, final_norm, initial_state,
+                                  initial_norm, stream)) != hipSuccess)
       return hip_status(e, "o2_state launch");
     tm.mark();
     e = ssd::launch_output(true, 64, 2, q, k, v, dt, a_cs, BH, N, chunk, st, part, y, den, stream);

@@ -162,14 +162,19 @@ __global__ __launch_bounds__(256) void k_state_pass(int64_t nblk, int eblocks,
                                                     const float* __restrict__ tb,
                                                     float* __restrict__ state,
                                                     float* __restrict__ fS,
-                                                    float* __restrict__ fz) {
+                                                    float* __restrict__ fz,
+                                                    const float* __restrict__ iS,
+                                                    const float* __restrict__ iz) {
   constexpr int E = DH * DH + DH;
   const int64_t bh = blockIdx.x / eblocks;
   const int e = (int)(blockIdx.x - bh * eblocks) * 256 + threadIdx.x;
   if (e >= E) return;
   float* p = state + bh * nblk * E + e;
   const float* t = tb + bh * nblk;
+  // the state before the first block: zero, or the caller's initial state
+  // (same entry order as the final state: S row-major, then z)
   float s = 0.f;
+  if (iS) s = e < DH * DH ? iS[bh * DH * DH + e] : iz[bh * DH + (e - DH * DH)];
   int64_t b = 0;
   // 32 blocks' loads in flight per thread: the scan is latency-bound
   // otherwise (one state entry per thread, a strided walk over the blocks)
@@ -201,15 +206,18 @@ __global__ __launch_bounds__(256) void k_state_pass(int64_t nblk, int eblocks,
 }
 
 hipError_t launch_state_pass(int64_t DH, int64_t BH, int64_t N, const float* tb, float* state,
-                             float* final_S, float* final_z, hipStream_t stream) {
+                             float* final_S, float* final_z, const float* init_S,
+                             const float* init_z, hipStream_t stream) {
   const int64_t nb = n_blocks(N);
   const int E = (int)(DH * DH + DH);
   const int eblocks = (E + 255) / 256;
   const dim3 grid((unsigned)(BH * eblocks)), blk(256);
   if (DH == 64)
-    hipLaunchKernelGGL(k_state_pass<64>, grid, blk, 0, stream, nb, eblocks, tb, state, final_S, final_z);
+    hipLaunchKernelGGL(k_state_pass<64>, grid, blk, 0, stream, nb, eblocks, tb, state, final_S, final_z,
+                       init_S, init_z);
   else
-    hipLaunchKernelGGL(k_state_pass<32>, grid, blk, 0, stream, nb, eblocks, tb, state, final_S, final_z);
+    hipLaunchKernelGGL(k_state_pass<32>, grid, blk, 0, stream, nb, eblocks, tb, state, final_S, final_z,
+                       init_S, init_z);
   return hipGetLastError();
 }
 

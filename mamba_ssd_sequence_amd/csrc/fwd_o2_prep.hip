@@ -309,9 +309,17 @@ __device__ __forceinline__ int sig_of(float m) {
 }
 }  // namespace
 
-__global__ __launch_bounds__(64) void k_o2_scale_scan(uint8_t* __restrict__ rec, int64_t nblk) {
+__global__ __launch_bounds__(64) void k_o2_scale_scan(uint8_t* __restrict__ rec, int64_t nblk,
+                                                       const float* __restrict__ initmax) {
   const int64_t bh = blockIdx.x;
   const int lane = threadIdx.x;
+  // bound of the state before the first step: max |S0| of an initial state
+  // (the maximum of its partial maxima), else 0
+  float M0 = 0.f;
+  if (initmax) {
+    static_assert(O2_INIT_PARTS == WAVE, "one partial maximum per lane");
+    M0 = wmax(initmax[bh * O2_INIT_PARTS + lane]);
+  }
   const int64_t nstep = (nblk + 1) / 2;
   const int64_t seg = (nstep + WAVE - 1) / WAVE;
   const int64_t s0 = lane * seg, s1 = (s0 + seg < nstep) ? s0 + seg : nstep;
@@ -353,8 +361,9 @@ __global__ __launch_bounds__(64) void k_o2_scale_scan(uint8_t* __restrict__ rec,
       A = A * pA;
     }
   }
-  float M = __shfl_up(B, 1, WAVE);  // bound after the previous lane's run (M_{-1} = 0)
-  if (lane == 0) M = 0.f;
+  // bound after the previous lane's run: that run's map applied to M0
+  float M = __shfl_up(A, 1, WAVE) * M0 + __shfl_up(B, 1, WAVE);
+  if (lane == 0) M = M0;
   for (int64_t c0 = s0; c0 < s1; c0 += 4) {
     float eA[4], E[4], D[4];
 #pragma unroll
@@ -392,9 +401,36 @@ __global__ __launch_bounds__(64) void k_o2_scale_scan(uint8_t* __restrict__ rec,
   }
 }
 
-hipError_t launch_o2_scale_scan(void* rec, int64_t BH, int64_t N, hipStream_t stream) {
+// Partial maxima of |S0| (order-2 initial numerator state, 4096 x 64 floats
+// per head): workgroup (head, part) reduces 4096 consecutive floats.
+__global__ __launch_bounds__(256) void k_o2_initmax(const float* __restrict__ S0,
+                                                    float* __restrict__ initmax) {
+  constexpr int PER = DH * DH * DH / O2_INIT_PARTS;  // floats per workgroup
+  static_assert(PER == 256 * 16, "four float4 per thread");
+  const float* p = S0 + (int64_t)blockIdx.x * PER;
+  float m = 0.f;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(p + 4 * (threadIdx.x + 256 * u));
+    m = fmaxf(m, fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
+  }
+  m = wmax(m);
+  __shared__ float wm[4];
+  if ((threadIdx.x & (WAVE - 1)) == 0) wm[threadIdx.x / WAVE] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) initmax[blockIdx.x] = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+}
+
+hipError_t launch_o2_initmax(const float* S0, int64_t BH, float* initmax, hipStream_t stream) {
+  hipLaunchKernelGGL(k_o2_initmax, dim3((unsigned)(BH * O2_INIT_PARTS)), dim3(256), 0, stream, S0,
+                     initmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_o2_scale_scan(void* rec, int64_t BH, int64_t N, const float* initmax,
+                                hipStream_t stream) {
   hipLaunchKernelGGL(k_o2_scale_scan, dim3((unsigned)BH), dim3(WAVE), 0, stream,
-                     static_cast<uint8_t*>(rec), n_blocks(N));
+                     static_cast<uint8_t*>(rec), n_blocks(N), initmax);
   return hipGetLastError();
 }
 

@@ -92,13 +92,15 @@ __device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f
 }
 }  // namespace
 
-template <int NAT>
+template <int NAT, bool INIT>
 __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ rec, int64_t BH,
                                                   int64_t N, int xcd_map,
                                                   float* __restrict__ part,
                                                   float* __restrict__ final_state,
                                                   float* __restrict__ zst,
-                                                  float* __restrict__ final_norm) {
+                                                  float* __restrict__ final_norm,
+                                                  const float* __restrict__ S0,
+                                                  const float* __restrict__ Z0) {
   constexpr int NW = 8, NT = NW * WAVE;  // waves, threads
   constexpr int CWG = NW * NAT / 2;      // value columns per workgroup
   constexpr int NCS = DH / CWG;          // column slices per head
@@ -479,14 +481,63 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
     }
   };
 
-  // prologue: stage step 0, prefetch step 1
+  // prologue: the initial states (if any), stage step 0, prefetch step 1
   prefetch(0);
-  stage(0);
   cur = nx;
+  if constexpr (INIT) {
+    // initial numerator state, S0[a][b][c] (row (a, b) of H_up, the layout
+    // of final_state): the workgroup's columns c0 .. c0 + CWG - 1 pass through
+    // LDS (the staging buffer of q, not yet in use) in passes of AP values of
+    // a; each lane then takes its accumulator entries, scaled to the first
+    // step's 2^sig_in, and forms the fp16 copy of its first a-tile.  (A kernel
+    // variant of its own: in the common variant the registers are fully used.)
+    constexpr int AP = 16, V4 = CWG / 4;
+    static_assert(AP * DH * CWG * sizeof(float) <= sizeof(Qh), "initial-state staging fits");
+    float* buf = reinterpret_cast<float*>(&Qh[0][0][0]);
+    const float* s0h = S0 + bh * (int64_t)DH * DH * DH;
+    const float sc = ldexpf(1.f, cur.sig_in);
+    for (int pass = 0; pass < DH / AP; ++pass) {
+      for (int e = tid; e < AP * DH * V4; e += NT) {
+        const int row = e / V4, part = e % V4;  // row = (a - AP pass) * 64 + b
+        const int64_t a = AP * pass + row / DH, b = row % DH;
+        *reinterpret_cast<f32x4*>(&buf[row * CWG + 4 * part]) =
+            *reinterpret_cast<const f32x4*>(&s0h[(a * DH + b) * DH + c0 + 4 * part]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int at = 0; at < NAT; ++at) {
+        const int a = 32 * (NAT == 2 ? at : (wave >> 2)) + n32;
+        if (a / AP == pass) {
+#pragma unroll
+          for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int b = bt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+              S[at][bt][r] = buf[((a - AP * pass) * DH + b) * CWG + cl] * sc;
+            }
+        }
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) SA0[kk][e] = (_Float16)S[0][kk >> 1][8 * (kk & 1) + e];
+  }
+  stage(0);
   prefetch(nstep > 1 ? 1 : 0);
   if (wave < NW / 2) {
+    // running normaliser sums: zero, or the initial state's stored entries
 #pragma unroll
-    for (int e = 0; e < ZE; ++e) zrun[tid][e] = 0.f;
+    for (int e = 0; e < ZE; ++e) {
+      float z = 0.f;
+      if (Z0) {
+        const int E = pc * ZPW + zi + e, t = E >> 8, w = E & 255;
+        const int bt = t < 4 ? 0 : t < 7 ? 1 : t < 9 ? 2 : 3, ct = bt + t - z_tile(bt, bt);
+        z = Z0[bh * DH * DH + (16 * bt + (w >> 4)) * DH + 16 * ct + (w & 15)];
+      }
+      zrun[tid][e] = z;
+    }
     zload(0);
     zscan(0);
   }
@@ -560,14 +611,21 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
 }
 
 hipError_t launch_o2_state(const void* rec, int64_t BH, int64_t N, float* part,
-                           float* final_state, float* zstate, float* final_norm,
-                           hipStream_t stream) {
+                           float* final_state, float* zstate, float* final_norm, const float* S0,
+                           const float* Z0, hipStream_t stream) {
   const int xcd_map = (BH % 8) == 0;
   const uint8_t* r = static_cast<const uint8_t*>(rec);
-  if (o2_nat(BH) == 2)
-    hipLaunchKernelGGL((k_o2_state<2>), dim3((unsigned)(BH * 8)), dim3(512), 0, stream, r, BH, N, xcd_map, part, final_state, zstate, final_norm);
-  else
-    hipLaunchKernelGGL((k_o2_state<1>), dim3((unsigned)(BH * 16)), dim3(512), 0, stream, r, BH, N, xcd_map, part, final_state, zstate, final_norm);
+#define SSD_LAUNCH_O2(NATV, INITV, WGS)                                                       \
+  hipLaunchKernelGGL((k_o2_state<NATV, INITV>), dim3((unsigned)(BH * (WGS))), dim3(512), 0,  \
+                     stream, r, BH, N, xcd_map, part, final_state, zstate, final_norm, S0, Z0)
+  if (o2_nat(BH) == 2) {
+    if (S0) SSD_LAUNCH_O2(2, true, 8);
+    else SSD_LAUNCH_O2(2, false, 8);
+  } else {
+    if (S0) SSD_LAUNCH_O2(1, true, 16);
+    else SSD_LAUNCH_O2(1, false, 16);
+  }
+#undef SSD_LAUNCH_O2
   return hipGetLastError();
 }
 

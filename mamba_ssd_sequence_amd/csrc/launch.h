@@ -54,6 +54,10 @@ constexpr int REC_BYTES = 24880;
 // b in tile bt <= ct and c in tile ct sits at 256 z_tile(bt, ct) + 16 (b % 16)
 // + c % 16.
 constexpr int Z_TILES = 10, Z_FLOATS = 256 * Z_TILES;
+
+// An order-2 initial numerator state S0 is reduced to this many partial
+// maxima of |S0| per head (the scale scan's starting bound).
+constexpr int O2_INIT_PARTS = 64;
 __host__ __device__ constexpr int z_tile(int bt, int ct) { return bt * 4 - bt * (bt - 1) / 2 + (ct - bt); }
 
 // Workspace layout (float offsets), in this order:
@@ -66,8 +70,9 @@ __host__ __device__ constexpr int z_tile(int bt, int ct) { return bt * 4 - bt * 
 //                                     (rows = o2_part_rows(N), padded to
 //                                     whole steps)
 //   rec    [BH, nblk] x REC_BYTES     order 2 only: operand records
+//   initmax [BH, O2_INIT_PARTS]       order 2 only: partial maxima of |S0|
 struct WsLayout {
-  size_t tb, state, part, rec, total_floats;
+  size_t tb, state, part, rec, initmax, total_floats;
 };
 
 inline WsLayout ws_layout(int64_t B, int64_t H, int64_t N, int64_t DH, int order) {
@@ -84,6 +89,9 @@ inline WsLayout ws_layout(int64_t B, int64_t H, int64_t N, int64_t DH, int order
   off = (off + 63) & ~(size_t)63;
   L.rec = off;
   if (order == 2) off += (size_t)(BH * nb) * (REC_BYTES / 4);
+  off = (off + 63) & ~(size_t)63;
+  L.initmax = off;
+  if (order == 2) off += (size_t)BH * O2_INIT_PARTS;
   L.total_floats = off;
   return L;
 }
@@ -104,9 +112,11 @@ hipError_t launch_chunk_state(bool bf16, int64_t DH, const void* k, const void* 
                               const float* a_cs, int64_t BH, int64_t N, int64_t chunk, float* tb,
                               float* state, hipStream_t stream);
 
-// In-place exclusive scan over blocks: state[bh,blk] <- state entering blk.
+// In-place exclusive scan over blocks: state[bh,blk] <- state entering blk,
+// starting from (init_S, init_z) when given (else zero).
 hipError_t launch_state_pass(int64_t DH, int64_t BH, int64_t N, const float* tb, float* state,
-                             float* final_S, float* final_z, hipStream_t stream);
+                             float* final_S, float* final_z, const float* init_S,
+                             const float* init_z, hipStream_t stream);
 
 // Intra-block masked product + inter-block part + normalisation -> y, den.
 hipError_t launch_output(bool bf16, int64_t DH, int order, const void* q, const void* k,
@@ -121,17 +131,24 @@ hipError_t launch_o2_blockprep(const void* q, const void* k, const void* v, cons
                                const float* a_cs, int64_t BH, int64_t N, int64_t chunk, float* tb,
                                float* state, void* rec, hipStream_t stream);
 
+// Order-2 initial state: O2_INIT_PARTS partial maxima of |S0| per head.
+hipError_t launch_o2_initmax(const float* S0, int64_t BH, float* initmax, hipStream_t stream);
+
 // Order-2 scale scan: per head, the running bound of the numerator state and
-// the per-block scale exponents of the state scan (record words SC_SIG_IN ..).
-hipError_t launch_o2_scale_scan(void* rec, int64_t BH, int64_t N, hipStream_t stream);
+// the per-block scale exponents of the state scan (record words SC_SIG_IN ..);
+// the bound starts at max |S0| (from initmax, if not NULL) or 0.
+hipError_t launch_o2_scale_scan(void* rec, int64_t BH, int64_t N, const float* initmax,
+                                hipStream_t stream);
 
 // Order-2 inter-block numerator: on-chip state scan over the block records.
 // The same kernel scans the normaliser state in place over the per-block
 // slots of `zstate` (Z_blk -> Z entering the block, as launch_state_pass) and
 // writes the final Z to final_norm (if not NULL).
+// The scans start from (S0, Z0) when given (the initial numerator and
+// normaliser states, the layouts of final_state and final_norm), else zero.
 hipError_t launch_o2_state(const void* rec, int64_t BH, int64_t N, float* part,
-                           float* final_state, float* zstate, float* final_norm,
-                           hipStream_t stream);
+                           float* final_state, float* zstate, float* final_norm, const float* S0,
+                           const float* Z0, hipStream_t stream);
 
 hipError_t launch_decode(bool bf16, int64_t DH, int order, const void* q, const void* k,
                          const void* v, const float* dt_proj, const float* dt_bias,

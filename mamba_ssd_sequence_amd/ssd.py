@@ -50,7 +50,7 @@ def _declare(lib):
     lib.ssd_forward_workspace_size.restype = sz
     lib.ssd_forward_workspace_size.argtypes = [i64, i64, i64, i64, i32, i64, i32]
     lib.ssd_forward.restype = ctypes.c_int
-    lib.ssd_forward.argtypes = [vp, vp, vp, fp, fp, i64, i64, i64, i64, i32, i64, i32,
+    lib.ssd_forward.argtypes = [vp, vp, vp, fp, fp, fp, fp, i64, i64, i64, i64, i32, i64, i32,
                                 fp, fp, fp, fp, vp, sz, vp]
     lib.ssd_set_timing_events.restype = ctypes.c_int
     lib.ssd_set_timing_events.argtypes = [vp, ctypes.c_int]
@@ -169,8 +169,10 @@ def workspace_size(B, H, N, d_h, order, chunk, dtype) -> int:
 
 
 def forward(q, k, v, dt, a_cs, order: int, chunk: int, *, y=None, den=None,
-            final_state=None, final_norm=None, workspace=None):
-    """ssd_forward: y [B,H,N,d_h] fp32 (den and final states optional outputs)."""
+            final_state=None, final_norm=None, workspace=None, initial_state=None,
+            initial_norm=None):
+    """ssd_forward: y [B,H,N,d_h] fp32 (den and final states optional outputs;
+    initial states optional inputs)."""
     torch = _torch()
     _require(q, "q")
     dev = q.device
@@ -185,14 +187,16 @@ def forward(q, k, v, dt, a_cs, order: int, chunk: int, *, y=None, den=None,
     _require(a_cs, "a_cs", torch.float32, dev)
     if y is None:
         y = torch.empty((B, H, N, d_h), dtype=torch.float32, device=dev)
-    for name, t in (("y", y), ("den", den), ("final_state", final_state), ("final_norm", final_norm)):
+    for name, t in (("y", y), ("den", den), ("final_state", final_state), ("final_norm", final_norm),
+                    ("initial_state", initial_state), ("initial_norm", initial_norm)):
         if t is not None:
             _require(t, name, torch.float32, dev)
     need = workspace_size(B, H, N, d_h, order, chunk, dtype)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().ssd_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(dt), _ptr(a_cs), B, H, N, d_h, order,
+    _check(lib().ssd_forward(_ptr(q), _ptr(k), _ptr(v), _ptr(dt), _ptr(a_cs), _ptr(initial_state),
+                             _ptr(initial_norm), B, H, N, d_h, order,
                              chunk, dtype, _ptr(y), _ptr(den), _ptr(final_state), _ptr(final_norm),
                              _ptr(workspace), wbytes, _stream(dev)))
     return y

@@ -25,7 +25,7 @@ def test_exports_every_header_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssd_abi_version() == 2
+    assert lib.ssd_abi_version() == 3
     for i, name in enumerate(ssd.STATUS):
         assert lib.ssd_status_str(i).decode() == name
     assert lib.ssd_status_str(99).decode() == "SSD_ERR_UNKNOWN"
@@ -67,11 +67,11 @@ def test_prep_amask_errors(lib):
 
 
 def fwd(lib, *, B=1, H=2, N=100, d_h=64, order=1, chunk=64, dtype=1, ws=None, wbytes=None,
-        q=A[0], dt=A[3], y=A[10], den=None, fs=None, fn=None):
+        q=A[0], dt=A[3], y=A[10], den=None, fs=None, fn=None, s0=None, z0=None):
     need = lib.ssd_forward_workspace_size(B, H, N, d_h, order, chunk, dtype)
     ws = A[20] if ws is None else ws
     wbytes = need if wbytes is None else wbytes
-    return lib.ssd_forward(q, A[1], A[2], dt, A[4], B, H, N, d_h, order, chunk, dtype,
+    return lib.ssd_forward(q, A[1], A[2], dt, A[4], s0, z0, B, H, N, d_h, order, chunk, dtype,
                            y, den, fs, fn, ws, wbytes, None)
 
 
@@ -90,6 +90,10 @@ def test_forward_errors(lib):
     assert fwd(lib, y=A[1]) == 5  # y aliases k
     assert "output y overlaps input k" in lib.ssd_last_error().decode()
     assert fwd(lib, den=A[10] + 16) == 5  # den overlaps y
+    assert fwd(lib, s0=A[12], z0=None) == 1  # initial_state without initial_norm
+    assert "initial_state" in lib.ssd_last_error().decode()
+    assert fwd(lib, s0=A[12] + 4, z0=A[13]) == 4
+    assert fwd(lib, s0=A[12], z0=A[13], fs=A[12], fn=A[14]) == 5  # final_state aliases initial_state
     assert fwd(lib, wbytes=16) == 6
     assert fwd(lib, ws=0) == 6
 

@@ -161,6 +161,53 @@ def test_final_state_matches_recurrence(name, B, H, N):
     assert np.abs(got["fn"] - z).max() <= tol * np.abs(z).max()
 
 
+def _forward_arrays(cfg, q, k, v, dtp, bias, alog, order, chunk, S0=None, z0=None):
+    """GPU forward over given (sliced) stored inputs; returns y, final S and z."""
+    ssd = ssd_mod()
+    qd, kd, vd = (to_dev_qkv(np.ascontiguousarray(x), cfg.dtype) for x in (q, k, v))
+    dt, a_cs, _ = ssd.prep(to_dev_f32(dtp), to_dev_f32(bias), to_dev_f32(alog), chunk)
+    B, H, N, d = qd.shape
+    D = d ** order
+    fs = torch.empty((B, H, D, d), device="cuda")
+    fn = torch.empty((B, H, D), device="cuda")
+    y = ssd.forward(qd, kd, vd, dt, a_cs, order, chunk, final_state=fs, final_norm=fn,
+                    initial_state=None if S0 is None else to_dev_f32(S0),
+                    initial_norm=None if z0 is None else to_dev_f32(z0))
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), fs.cpu().numpy(), fn.cpu().numpy()
+
+
+# (config, B, H, N, chunk, split point): at order 2, 2 heads use the
+# two-wave-per-column state layout and 32 heads the one-wave layout
+@pytest.mark.parametrize("name,B,H,N,chunk,n1", [
+    ("o1_f32_small", 1, 2, 200, 64, 100), ("o1_bf16_2k", 1, 2, 300, 128, 191),
+    ("o2_bf16_4k", 1, 2, 300, 64, 128), ("o2_bf16_4k", 1, 2, 250, 128, 77),
+    ("o2_bf16_4k", 2, 16, 300, 64, 150)])
+def test_initial_state_continues_the_sequence(name, B, H, N, chunk, n1):
+    """ssd_forward from the states a prefix leaves (Algorithm 6 hand-off) gives
+    the full sequence's outputs for the suffix and its final states."""
+    cfg = I.CONFIGS[name]
+    say("initial state", name, B, H, N, chunk, n1)
+    inp = I.make_forward_inputs(cfg, B=B, H=H, N=N, seed=5 + n1)
+    order = cfg.order
+    pre = lambda x: x[:, :, :n1]
+    suf = lambda x: x[:, :, n1:]
+    _, S1, z1 = _forward_arrays(cfg, pre(inp.q), pre(inp.k), pre(inp.v), pre(inp.dt_proj),
+                                inp.dt_bias, inp.A_log, order, chunk)
+    y2, S2, z2 = _forward_arrays(cfg, suf(inp.q), suf(inp.k), suf(inp.v), suf(inp.dt_proj),
+                                 inp.dt_bias, inp.A_log, order, chunk, S0=S1, z0=z1)
+    ref = oracle_forward(inp, order)
+    err = row_error(y2, ref["y"][:, :, n1:], ref["scale"][:, :, n1:])
+    say("  err", err)
+    assert err <= TOL[cfg.dtype]
+    qf, kf, vf = inp.qkv_f64()
+    dt, a = O.discretise(inp.dt_proj, inp.dt_bias, inp.A_log)
+    _, _, S, z = O.forward_recurrent(qf, kf, vf * dt[..., None], a, order)
+    tol = TOL[cfg.dtype]
+    assert np.abs(S2 - S).max() <= tol * np.abs(S).max()
+    assert np.abs(z2 - z).max() <= tol * np.abs(z).max()
+
+
 def test_deterministic():
     cfg = I.CONFIGS["o2_bf16_4k"]
     inp = I.make_forward_inputs(cfg, B=1, H=2, N=300, seed=2)

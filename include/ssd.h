@@ -34,6 +34,10 @@
  *    the ABI.
  *  - Outputs must not overlap inputs (SSD_ERR_ALIAS), except the decode
  *    state, which is updated in place by design.
+ *  - Sizes B, H, N (decode: S, H) may be 0: an empty input is valid and the
+ *    call does no work (ssd_forward with N = 0 still sets the final states
+ *    to the initial ones, or to zero).  A pointer to an array of zero bytes
+ *    may be NULL.
  */
 #ifndef SSD_H_
 #define SSD_H_

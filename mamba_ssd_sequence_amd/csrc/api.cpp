@@ -48,9 +48,11 @@ void clear_err() { g_err[0] = 0; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // product of positive sizes with overflow detection (limit 2^62)
+// a * b for sizes >= 0 (0 allowed: an empty input), false on a negative size
+// or an overflow past 2^62
 bool mul_ok(int64_t a, int64_t b, int64_t* out) {
-  if (a <= 0 || b <= 0) return false;
-  if (a > ((int64_t)1 << 62) / b) return false;
+  if (a < 0 || b < 0) return false;
+  if (a && b > ((int64_t)1 << 62) / a) return false;
   *out = a * b;
   return true;
 }
@@ -96,7 +98,7 @@ ssd_status validate_forward_sizes(int64_t B, int64_t H, int64_t N, int64_t d_h, 
                                   int64_t chunk, int dtype, int64_t* BH, int64_t* BHN,
                                   int64_t* BHNd) {
   if (!mul_ok(B, H, BH) || !mul_ok(*BH, N, BHN) || !mul_ok(*BHN, d_h, BHNd))
-    return fail(SSD_ERR_SHAPE, "B, H, N, d_h must be >= 1 and their product must not overflow");
+    return fail(SSD_ERR_SHAPE, "B, H, N must be >= 0, d_h >= 1, and their product must not overflow");
   if (dtype != SSD_F32 && dtype != SSD_BF16) return fail(SSD_ERR_UNSUPPORTED, "dtype %d", dtype);
   if (order != 1 && order != 2) return fail(SSD_ERR_UNSUPPORTED, "order %d (1 or 2)", order);
   if (chunk != 64 && chunk != 128) return fail(SSD_ERR_UNSUPPORTED, "chunk %lld (64 or 128)", (long long)chunk);
@@ -135,13 +137,14 @@ ssd_status ssd_prep(const float* dt_proj, const float* dt_bias, const float* A_l
                     hipStream_t stream) {
   try {
     clear_err();
-    if (!dt_proj || !dt_bias || !A_log || !dt || !a_cs || !a_chunk)
-      return fail(SSD_ERR_NULL, "ssd_prep: a required pointer is NULL");
     int64_t BH, BHN;
     if (!mul_ok(B, H, &BH) || !mul_ok(BH, N, &BHN))
-      return fail(SSD_ERR_SHAPE, "ssd_prep: B, H, N must be >= 1 and must not overflow");
+      return fail(SSD_ERR_SHAPE, "ssd_prep: B, H, N must be >= 0 and must not overflow");
     if (chunk != 64 && chunk != 128)
       return fail(SSD_ERR_UNSUPPORTED, "ssd_prep: chunk %lld (64 or 128)", (long long)chunk);
+    if (BHN == 0) return SSD_OK;  // empty input: nothing to compute
+    if (!dt_proj || !dt_bias || !A_log || !dt || !a_cs || !a_chunk)
+      return fail(SSD_ERR_NULL, "ssd_prep: a required pointer is NULL");
     const int64_t nc = (N + chunk - 1) / chunk;
     if ((BH * nc + 3) / 4 > (int64_t)0x7fffffff) return fail(SSD_ERR_SHAPE, "ssd_prep: grid too large");
     const Range ins[] = {{"dt_proj", dt_proj, (size_t)BHN * 4},
@@ -165,15 +168,16 @@ ssd_status ssd_prep_amask(const float* A_proj, const float* dt_proj, int64_t B, 
                           hipStream_t stream) {
   try {
     clear_err();
+    int64_t BH, BHN;
+    if (!mul_ok(B, H, &BH) || !mul_ok(BH, N, &BHN))
+      return fail(SSD_ERR_SHAPE, "ssd_prep_amask: B, H, N must be >= 0 and must not overflow");
+    if (chunk != 64 && chunk != 128)
+      return fail(SSD_ERR_UNSUPPORTED, "ssd_prep_amask: chunk %lld (64 or 128)", (long long)chunk);
+    if (BHN == 0) return SSD_OK;  // empty input: nothing to compute
     if (!A_proj || !a_cs || !a_chunk)
       return fail(SSD_ERR_NULL, "ssd_prep_amask: a required pointer is NULL");
     if ((dt_proj == nullptr) != (dt == nullptr))
       return fail(SSD_ERR_NULL, "ssd_prep_amask: dt_proj and dt must both be given or both be NULL");
-    int64_t BH, BHN;
-    if (!mul_ok(B, H, &BH) || !mul_ok(BH, N, &BHN))
-      return fail(SSD_ERR_SHAPE, "ssd_prep_amask: B, H, N must be >= 1 and must not overflow");
-    if (chunk != 64 && chunk != 128)
-      return fail(SSD_ERR_UNSUPPORTED, "ssd_prep_amask: chunk %lld (64 or 128)", (long long)chunk);
     const int64_t nc = (N + chunk - 1) / chunk;
     if ((BH * nc + 3) / 4 > (int64_t)0x7fffffff)
       return fail(SSD_ERR_SHAPE, "ssd_prep_amask: grid too large");
@@ -195,6 +199,7 @@ size_t ssd_forward_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d_h, 
                                   int64_t chunk, int dtype) {
   int64_t BH, BHN, BHNd;
   if (validate_forward_sizes(B, H, N, d_h, order, chunk, dtype, &BH, &BHN, &BHNd) != SSD_OK) return 0;
+  if (BHN == 0) return 0;  // an empty input needs no workspace
   return ssd::ws_layout(B, H, N, d_h, order).total_floats * sizeof(float);
 }
 
@@ -206,16 +211,30 @@ ssd_status ssd_forward(const void* q, const void* k, const void* v, const float*
                        hipStream_t stream) {
   try {
     clear_err();
-    if (!q || !k || !v || !a_cs || !y) return fail(SSD_ERR_NULL, "ssd_forward: a required pointer is NULL");
+    int64_t BH, BHN, BHNd;
+    ssd_status s = validate_forward_sizes(B, H, N, d_h, order, chunk, dtype, &BH, &BHN, &BHNd);
+    if (s != SSD_OK) return s;
+    if (BH == 0) return SSD_OK;  // no heads: nothing to compute
     if ((final_state == nullptr) != (final_norm == nullptr))
       return fail(SSD_ERR_NULL, "ssd_forward: final_state and final_norm must be given together");
     if ((initial_state == nullptr) != (initial_norm == nullptr))
       return fail(SSD_ERR_NULL, "ssd_forward: initial_state and initial_norm must be given together");
-    int64_t BH, BHN, BHNd;
-    ssd_status s = validate_forward_sizes(B, H, N, d_h, order, chunk, dtype, &BH, &BHN, &BHNd);
-    if (s != SSD_OK) return s;
     const size_t es = dtype == SSD_BF16 ? 2 : 4;
     const int64_t D = order == 1 ? d_h : d_h * d_h;
+    if (BHN == 0) {
+      // an empty segment (N = 0): the final states are the initial ones (or zero)
+      if (!final_state) return SSD_OK;
+      const Range ins0[] = {{"initial_state", initial_state, (size_t)(BH * D * d_h) * 4},
+                            {"initial_norm", initial_norm, (size_t)(BH * D) * 4}};
+      const Range outs0[] = {{"final_state", final_state, (size_t)(BH * D * d_h) * 4},
+                             {"final_norm", final_norm, (size_t)(BH * D) * 4}};
+      if ((s = check_aligned(ins0, 2)) != SSD_OK || (s = check_aligned(outs0, 2)) != SSD_OK) return s;
+      if ((s = check_alias(outs0, 2, ins0, 2)) != SSD_OK) return s;
+      hipError_t e = ssd::launch_copy_or_zero(final_state, initial_state, BH * D * d_h, stream);
+      if (e == hipSuccess) e = ssd::launch_copy_or_zero(final_norm, initial_norm, BH * D, stream);
+      return hip_status(e, "final-state copy launch");
+    }
+    if (!q || !k || !v || !a_cs || !y) return fail(SSD_ERR_NULL, "ssd_forward: a required pointer is NULL");
     const size_t need = ssd::ws_layout(B, H, N, d_h, order).total_floats * sizeof(float);
     if (workspace_bytes < need || (need && !workspace))
       return fail(SSD_ERR_WORKSPACE, "ssd_forward: workspace of %zu bytes needed, %zu given", need,
@@ -297,14 +316,15 @@ ssd_status ssd_decode_step(const void* q, const void* k, const void* v, const fl
                            float* y, hipStream_t stream) {
   try {
     clear_err();
-    if (!q || !k || !v || !dt_proj || !dt_bias || !A_log || !state || !norm_state || !y)
-      return fail(SSD_ERR_NULL, "ssd_decode_step: a required pointer is NULL");
     int64_t SH, SHd;
     if (!mul_ok(S, H, &SH) || !mul_ok(SH, d_h, &SHd))
-      return fail(SSD_ERR_SHAPE, "ssd_decode_step: S, H, d_h must be >= 1 and must not overflow");
+      return fail(SSD_ERR_SHAPE, "ssd_decode_step: S, H must be >= 0 and must not overflow");
     if (dtype != SSD_F32 && dtype != SSD_BF16) return fail(SSD_ERR_UNSUPPORTED, "dtype %d", dtype);
     if (order != 1 && order != 2) return fail(SSD_ERR_UNSUPPORTED, "order %d (1 or 2)", order);
     if (d_h != 32 && d_h != 64) return fail(SSD_ERR_UNSUPPORTED, "d_h %lld (32 or 64)", (long long)d_h);
+    if (SH == 0) return SSD_OK;  // no sequences or heads: nothing to compute
+    if (!q || !k || !v || !dt_proj || !dt_bias || !A_log || !state || !norm_state || !y)
+      return fail(SSD_ERR_NULL, "ssd_decode_step: a required pointer is NULL");
     if (SH > (int64_t)0x7fffffff) return fail(SSD_ERR_SHAPE, "ssd_decode_step: grid too large");
     const int64_t D = order == 1 ? d_h : d_h * d_h;
     int64_t nstate;

@@ -100,6 +100,9 @@ hipError_t launch_prep(const float* dt_proj, const float* dt_bias, const float* 
                        int64_t H, int64_t N, int64_t chunk, float* dt, float* a_cs, float* a_chunk,
                        hipStream_t stream);
 
+// dst[0 .. n) = src (or 0 if src is NULL); n >= 1.
+hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t stream);
+
 // Algorithms 4 / 5 A-mask: a = -softplus(A_proj), dt = softplus(dt_proj) (no
 // bias) if dt_proj is not NULL (dt is then written), chunk-local cumsum.
 hipError_t launch_prep_amask(const float* A_proj, const float* dt_proj, int64_t B, int64_t H,

@@ -113,4 +113,19 @@ hipError_t launch_prep_amask(const float* A_proj, const float* dt_proj, int64_t 
                              a_chunk, stream);
 }
 
+// dst[0 .. n) = src[0 .. n), or 0 where src is NULL (the final states of an
+// empty segment)
+__global__ __launch_bounds__(256) void k_copy_or_zero(float* __restrict__ dst,
+                                                      const float* __restrict__ src, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    dst[i] = src ? src[i] : 0.f;
+}
+
+hipError_t launch_copy_or_zero(float* dst, const float* src, int64_t n, hipStream_t stream) {
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(k_copy_or_zero, dim3((unsigned)(blocks < 4096 ? blocks : 4096)), dim3(256), 0,
+                     stream, dst, src, n);
+  return hipGetLastError();
+}
+
 }  // namespace ssd

@@ -39,7 +39,7 @@ def prep(lib, *, ptrs=None, B=1, H=2, N=100, chunk=64):
 def test_prep_errors(lib):
     assert prep(lib, ptrs=[A[0], None, A[2], A[3], A[4], A[5]]) == 1
     assert "NULL" in lib.ssd_last_error().decode()
-    assert prep(lib, B=0) == 2
+    assert prep(lib, B=-1) == 2
     assert prep(lib, N=-5) == 2
     assert prep(lib, B=1 << 40, H=1 << 40) == 2
     assert prep(lib, chunk=32) == 3
@@ -58,7 +58,7 @@ def test_prep_amask_errors(lib):
     assert prep_amask(lib, ptrs=[A[0], None, A[3], A[4], A[5]]) == 1  # dt without dt_proj
     assert "both" in lib.ssd_last_error().decode()
     assert prep_amask(lib, ptrs=[A[0], A[1], None, A[4], A[5]]) == 1  # dt_proj without dt
-    assert prep_amask(lib, B=0) == 2
+    assert prep_amask(lib, B=-1) == 2
     assert prep_amask(lib, N=-1) == 2
     assert prep_amask(lib, chunk=256) == 3
     assert prep_amask(lib, ptrs=[A[0] + 8, A[1], A[3], A[4], A[5]]) == 4
@@ -79,7 +79,7 @@ def test_forward_errors(lib):
     assert fwd(lib, q=None) == 1
     assert fwd(lib, y=None) == 1
     assert fwd(lib, fs=A[11], fn=None) == 1
-    assert fwd(lib, N=0) == 2
+    assert fwd(lib, N=-1) == 2
     assert fwd(lib, d_h=48) == 3
     assert fwd(lib, order=3) == 3
     assert fwd(lib, chunk=256) == 3
@@ -107,7 +107,8 @@ def test_workspace_size(lib):
     w2 = lib.ssd_forward_workspace_size(B, H, N, d, 2, 64, 1)
     assert w2 > w1 + 4 * B * H * N * 64
     assert lib.ssd_forward_workspace_size(B, H, N, 48, 1, 64, 1) == 0
-    assert lib.ssd_forward_workspace_size(0, H, N, d, 1, 64, 1) == 0
+    assert lib.ssd_forward_workspace_size(-1, H, N, d, 1, 64, 1) == 0
+    assert lib.ssd_forward_workspace_size(B, H, 0, d, 2, 64, 1) == 0  # empty: no workspace
 
 
 def dec(lib, *, S=1, H=1, d_h=64, order=2, dtype=1, q=A[0], state=A[6], norm=A[7], y=A[8]):
@@ -118,7 +119,7 @@ def dec(lib, *, S=1, H=1, d_h=64, order=2, dtype=1, q=A[0], state=A[6], norm=A[7
 def test_decode_errors(lib):
     assert dec(lib, q=None) == 1
     assert dec(lib, state=None) == 1
-    assert dec(lib, S=0) == 2
+    assert dec(lib, S=-1) == 2
     assert dec(lib, d_h=16) == 3
     assert dec(lib, order=0) == 3
     assert dec(lib, dtype=2) == 3
@@ -133,3 +134,21 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 2, 64)
     with pytest.raises(ValueError):
         ssd.prep(x, torch.zeros(2), torch.zeros(2), 64)
+
+
+def test_empty_inputs_are_valid_no_ops(lib):
+    """Sizes of 0 are an empty input: OK with no work, NULL allowed for the
+    zero-byte arrays (no call here reaches a kernel launch)."""
+    assert lib.ssd_prep(None, None, None, 0, 2, 100, 64, None, None, None, None) == 0
+    assert lib.ssd_prep(None, None, None, 1, 2, 0, 64, None, None, None, None) == 0
+    assert lib.ssd_prep(None, None, None, 1, 2, 0, 48, None, None, None, None) == 3  # still validated
+    assert lib.ssd_prep_amask(None, None, 1, 0, 10, 128, None, None, None, None) == 0
+    for order in (1, 2):
+        assert lib.ssd_forward(None, None, None, None, None, None, None, 1, 2, 0, 64, order, 64, 1,
+                               None, None, None, None, None, 0, None) == 0
+        assert lib.ssd_forward(None, None, None, None, None, None, None, 0, 2, 10, 64, order, 64, 1,
+                               None, None, None, None, None, 0, None) == 0
+    assert lib.ssd_forward(None, None, None, None, None, None, None, 1, 2, 0, 48, 1, 64, 1,
+                           None, None, None, None, None, 0, None) == 3
+    assert lib.ssd_decode_step(None, None, None, None, None, None, 0, 4, 64, 2, 1,
+                               None, None, None, None) == 0

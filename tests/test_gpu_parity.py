@@ -420,3 +420,83 @@ def test_prefill_then_decode():
     ref = oracle_forward(inp, 2, rows=np.arange(N, N + T))
     y = np.stack(ys, axis=2)
     assert row_error(y, ref["y"], ref["scale"]) <= TOL[cfg.dtype]
+
+
+# ---------------------------------------------------------------------------
+# empty inputs and the method's degenerate cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_empty_segment(order):
+    """N = 0: nothing to compute; the final states are the initial ones (or 0)."""
+    say("empty segment", order)
+    ssd = ssd_mod()
+    B, H, d = 2, 3, 64
+    D = d ** order
+    q = torch.empty((B, H, 0, d), dtype=torch.bfloat16, device="cuda")
+    dtp = torch.empty((B, H, 0), device="cuda")
+    dt, a_cs, a_chunk = ssd.prep(dtp, torch.zeros(H, device="cuda"), torch.zeros(H, device="cuda"), 64)
+    assert dt.shape == (B, H, 0) and a_chunk.shape == (B, H, 0)
+    fs = torch.full((B, H, D, d), 7.0, device="cuda")
+    fn = torch.full((B, H, D), 7.0, device="cuda")
+    y = ssd.forward(q, q.clone(), q.clone(), dt, a_cs, order, 64, final_state=fs, final_norm=fn)
+    torch.cuda.synchronize()
+    assert y.shape == (B, H, 0, d)
+    assert float(fs.abs().max()) == 0.0 and float(fn.abs().max()) == 0.0
+    s0 = torch.randn((B, H, D, d), device="cuda")
+    z0 = torch.rand((B, H, D), device="cuda")
+    ssd.forward(q, q.clone(), q.clone(), dt, a_cs, order, 64, final_state=fs, final_norm=fn,
+                initial_state=s0, initial_norm=z0)
+    torch.cuda.synchronize()
+    assert torch.equal(fs, s0) and torch.equal(fn, z0)
+
+
+@pytest.mark.parametrize("name", ["o1_bf16_2k", "o2_bf16_4k"])
+def test_no_decay_is_causal_linear_attention(name):
+    """A -> 0 (A_log = -40): the decay mask is all ones and the mixer is plain
+    causal (order-p) linear attention (Algorithm 1 with the causal mask)."""
+    cfg = I.CONFIGS[name]
+    say("no decay", name)
+    inp = I.make_forward_inputs(cfg, B=1, H=4, N=260, seed=31)
+    inp.A_log[:] = -40.0
+    got = run_forward(inp, cfg.order, cfg.chunk)
+    q, k, v = inp.qkv_f64()
+    dt, a = O.discretise(inp.dt_proj, inp.dt_bias, inp.A_log)
+    assert np.abs(a).max() < 1e-15
+    ref = O.forward_quadratic(q, k, v * dt[..., None], np.zeros_like(a), cfg.order)
+    err = row_error(got["y"], ref["y"], ref["scale"])
+    say("  err", err)
+    assert err <= TOL[cfg.dtype]
+
+
+def test_full_decay_keeps_only_the_token_itself():
+    """A dt -> -inf: every earlier token is masked out and y_i = (v dt)_i
+    (order 2: the diagonal score (q_i . k_i)^2 is positive)."""
+    cfg = I.CONFIGS["o2_bf16_4k"]
+    say("full decay")
+    inp = I.make_forward_inputs(cfg, B=1, H=2, N=200, seed=32)
+    inp.A_log[:] = 6.0       # A = -403
+    inp.dt_bias[:] = 5.0     # dt ~ 5: a ~ -2000 per token
+    got = run_forward(inp, 2, 64)
+    q, k, v = inp.qkv_f64()
+    dt, _ = O.discretise(inp.dt_proj, inp.dt_bias, inp.A_log)
+    expect = v * dt[..., None]
+    # the value operand and the scores enter the MFMA as bf16: ~2^-8 relative
+    err = np.abs(got["y"] - expect).max() / np.abs(expect).max()
+    say("  err", err)
+    assert err <= TOL[cfg.dtype]
+
+
+def test_constant_value_gives_the_value():
+    """2Mamba with a constant plain V (dt = NULL): every output row is that V
+    (a convex combination of equal rows, Algorithm 5's weights being >= 0)."""
+    cfg = I.CONFIGS["o2_bf16_4k"]
+    say("constant value")
+    inp = I.make_forward_inputs(cfg, B=1, H=2, N=333, seed=33)
+    row = inp.v[0, 0, 0].copy()
+    inp.v[:] = row
+    got = run_forward(inp, 2, 64, with_dt=False)
+    expect = I.bf16_bits_to_f64(row)
+    err = np.abs(got["y"] - expect).max() / np.abs(expect).max()
+    say("  err", err)
+    assert err <= 2e-2

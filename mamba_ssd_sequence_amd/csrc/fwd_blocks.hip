@@ -256,7 +256,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ORDER == 2 
   const St* q = static_cast<const St*>(qp);
   const St* k = static_cast<const St*>(kp);
   const St* v = static_cast<const St*>(vp);
-  const int64_t bh = blockIdx.x / nblk, blk = blockIdx.x - bh * nblk;
+  int64_t bh, blk;
+  if constexpr (ORDER == 2 && BF) {
+    // the two blocks of a step (2m, 2m + 1) go to workgroups 8 apart, i.e. to
+    // the same XCD (workgroups are dispatched round-robin over the 8 XCDs),
+    // so that the second block's read of the first block's k and v (its
+    // direct term) finds them in that XCD's L2
+    const int64_t np = (nblk + 1) / 2, xcd = blockIdx.x & 7, s8 = blockIdx.x >> 3;
+    const int64_t P = 8 * (s8 >> 1) + xcd;  // (head, step) pair index
+    if (P >= BH * np) return;
+    bh = P / np;
+    blk = 2 * (P - bh * np) + (s8 & 1);
+    if (blk >= nblk) return;  // the empty second block of a last step
+  } else {
+    bh = blockIdx.x / nblk;
+    blk = blockIdx.x - bh * nblk;
+  }
   const int64_t t0 = blk * BLK;
   const int nvalid = (int)((N - t0) < BLK ? (N - t0) : BLK);
   const int64_t row = bh * N;
@@ -668,7 +683,9 @@ hipError_t launch_output(bool bf16, int64_t DH, int order, const void* q, const 
                          int64_t chunk, const float* state, const float* part, float* y,
                          float* den, hipStream_t stream) {
   const int64_t nb = n_blocks(N);
-  const dim3 grid((unsigned)(BH * nb)), blk(256);
+  // order 2: workgroups in groups of 16 (8 step pairs) over the XCDs, see k_output
+  const int64_t g2 = 16 * ((BH * ((nb + 1) / 2) + 7) / 8);
+  const dim3 grid((unsigned)(order == 2 ? g2 : BH * nb)), blk(256);
 #define SSD_LAUNCH_OUT(BFV, DHV, ORD)                                                           \
   hipLaunchKernelGGL((k_output<BFV, DHV, ORD>), grid, blk, 0, stream, q, k, v, dt, a_cs, BH, N, \
                      chunk, nb, state, part, y, den)

@@ -42,6 +42,12 @@ __device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4& c) {
 
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
+// x if c else 0, per component (a select of the whole struct would be
+// lowered through memory)
+__device__ __forceinline__ uint4 keep_if(bool c, const uint4& x) {
+  return make_uint4(c ? x.x : 0u, c ? x.y : 0u, c ? x.z : 0u, c ? x.w : 0u);
+}
+
 // 2^x on the hardware exponential (v_exp_f32, about 1 ulp; results below the
 // smallest normal flush to 0, which only ever happens for decays that are 0
 // to fp32 accuracy anyway); with x = y log2(e) it gives e^y.

@@ -55,8 +55,8 @@ template <> struct Cfg<false> {
 // ---------------------------------------------------------------------------
 // k_chunk_state
 // ---------------------------------------------------------------------------
-template <bool BF, int DH>
-__global__ __launch_bounds__(256) void k_chunk_state(const void* __restrict__ kp,
+template <bool BF, int DH>  // (fp32 inputs; BF is false)
+__global__ __launch_bounds__(256) void k_chunk_state_f32(const void* __restrict__ kp,
                                                      const void* __restrict__ vp,
                                                      const float* __restrict__ dt,
                                                      const float* __restrict__ a_cs, int64_t N,
@@ -138,19 +138,127 @@ __global__ __launch_bounds__(256) void k_chunk_state(const void* __restrict__ kp
   }
 }
 
+// bf16 inputs: one memory round trip (q is not needed; k and v segments of
+// two consecutive tokens per thread are loaded before anything else), k^T and
+// (v dt)^T staged in LDS with transposing 4-byte stores (a token pair per
+// store), and the weighted-key operand (w k)^T formed in registers: wave w
+// takes the column tile b in [16 w, 16 w + 16) of every row tile c, so its
+// operand fragments are those of one b-tile, split into high + low bf16
+// parts; z = sum_j w_j k_j comes from the same fp32 products.
+template <int DH>
+__global__ __launch_bounds__(256) void k_chunk_state_bf16(const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ v,
+                                                          const float* __restrict__ dt,
+                                                          const float* __restrict__ a_cs,
+                                                          int64_t N, int64_t chunk, int64_t nblk,
+                                                          float* __restrict__ tb,
+                                                          float* __restrict__ state) {
+  constexpr int P = BLK + 8;         // LDS row pitch (bf16 elements)
+  constexpr int SEG = DH / 8;        // 16-byte segments per row
+  static_assert(BLK * SEG / 2 == 256 || BLK * SEG / 2 == 128, "segment mapping");
+  constexpr int NT = DH / 16;
+  static_assert(NT <= 4, "one b-tile per wave");
+  __shared__ __attribute__((aligned(16))) __bf16 KT[DH * P];  // [b][j] k_jb
+  __shared__ __attribute__((aligned(16))) __bf16 VT[DH * P];  // [c][j] v_jc dt_j
+  __shared__ float wv[BLK];
+
+  const int64_t bh = blockIdx.x / nblk, blk = blockIdx.x - bh * nblk;
+  const int64_t t0 = blk * BLK;
+  const int nvalid = (int)((N - t0) < BLK ? (N - t0) : BLK);
+  const int64_t row = bh * N;
+  const int tid = threadIdx.x;
+
+  // reads, all issued up front; rows past a ragged block's end read the
+  // last valid row (zeroed below: no load under a lane-divergent branch)
+  const bool act = tid < BLK * SEG / 2;  // thread -> (token pair, segment)
+  const int pr = (tid / SEG) % (BLK / 2), sg = tid % SEG, j0 = 2 * pr;
+  const int r0 = min(j0, nvalid - 1), r1 = min(j0 + 1, nvalid - 1);
+  const uint4 k0 = *reinterpret_cast<const uint4*>(k + (row + t0 + r0) * DH + sg * 8);
+  const uint4 k1 = *reinterpret_cast<const uint4*>(k + (row + t0 + r1) * DH + sg * 8);
+  const uint4 v0 = *reinterpret_cast<const uint4*>(v + (row + t0 + r0) * DH + sg * 8);
+  const uint4 v1 = *reinterpret_cast<const uint4*>(v + (row + t0 + r1) * DH + sg * 8);
+  const float d0 = dt ? dt[row + t0 + r0] : 1.f, d1 = dt ? dt[row + t0 + r1] : 1.f;
+  const int ja = min(tid & (BLK - 1), nvalid - 1);
+  const float acs = a_cs[row + t0 + ja];
+  const float base = (t0 % chunk == 0) ? 0.f : a_cs[row + t0 - 1];
+  const float cs_last = a_cs[row + t0 + nvalid - 1];
+
+  if (tid < BLK) wv[tid] = tid < nvalid ? expf(cs_last - acs) : 0.f;
+  if (tid == 0) tb[bh * nblk + blk] = cs_last - base;
+  if (act) {
+    const bool ok0 = j0 < nvalid, ok1 = j0 + 1 < nvalid;
+    const uint4 ka = keep_if(ok0, k0), kb = keep_if(ok1, k1);
+    const uint4 va = keep_if(ok0, v0), vb = keep_if(ok1, v1);
+    const uint32_t kw0[4] = {ka.x, ka.y, ka.z, ka.w}, kw1[4] = {kb.x, kb.y, kb.z, kb.w};
+    const uint32_t vw0[4] = {va.x, va.y, va.z, va.w}, vw1[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int d = sg * 8 + 2 * u + hh;
+        const uint32_t kb0 = hh ? (kw0[u] >> 16) : (kw0[u] & 0xffffu);
+        const uint32_t kb1 = hh ? (kw1[u] >> 16) : (kw1[u] & 0xffffu);
+        *reinterpret_cast<uint32_t*>(&KT[d * P + j0]) = kb0 | (kb1 << 16);
+        const float a0 = __uint_as_float(hh ? (vw0[u] & 0xffff0000u) : (vw0[u] << 16)) * d0;
+        const float a1 = __uint_as_float(hh ? (vw1[u] & 0xffff0000u) : (vw1[u] << 16)) * d1;
+        const __bf16 pv[2] = {(__bf16)a0, (__bf16)a1};
+        *reinterpret_cast<uint32_t*>(&VT[d * P + j0]) = __builtin_bit_cast(uint32_t, pv);
+      }
+  }
+  __syncthreads();
+
+  const int wave = tid / WAVE, lane = tid & (WAVE - 1), n = lane & 15, g = lane >> 4;
+  float* out = state + (bh * nblk + blk) * (int64_t)(DH * DH + DH);
+  if (wave < NT) {
+    const int bt = wave;
+    // B operand (w k)^T[b = 16 bt + n][j = 32 ks + 8 g ..]: high + low parts;
+    // z_b from the fp32 products
+    bf16x8 bhi[BLK / 32], blo[BLK / 32];
+    float zp = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < BLK / 32; ++ks) {
+      const bf16x8 kr = *reinterpret_cast<const bf16x8*>(&KT[(bt * 16 + n) * P + ks * 32 + 8 * g]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float wk = (float)kr[e] * wv[ks * 32 + 8 * g + e];
+        const __bf16 h = (__bf16)wk;
+        bhi[ks][e] = h;
+        blo[ks][e] = (__bf16)(wk - (float)h);
+        zp += wk;
+      }
+    }
+    zp = sum_over_groups(zp);
+    if (g == 0) out[DH * DH + bt * 16 + n] = zp;
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < BLK / 32; ++ks) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&VT[(ct * 16 + n) * P + ks * 32 + 8 * g]);
+        acc = mfma_bf16(a, bhi[ks], acc);
+        acc = mfma_bf16(a, blo[ks], acc);
+      }
+      // acc[r] = dS^T[c = 16 ct + 4 g + r][b = 16 bt + n] -> dS[b][c]
+      *reinterpret_cast<f32x4*>(&out[(bt * 16 + n) * DH + ct * 16 + 4 * g]) = acc;
+    }
+  }
+}
+
 hipError_t launch_chunk_state(bool bf16, int64_t DH, const void* k, const void* v, const float* dt,
                               const float* a_cs, int64_t BH, int64_t N, int64_t chunk, float* tb,
                               float* state, hipStream_t stream) {
   const int64_t nb = n_blocks(N);
   const dim3 grid((unsigned)(BH * nb)), blk(256);
+  const uint16_t* kb = static_cast<const uint16_t*>(k);
+  const uint16_t* vb = static_cast<const uint16_t*>(v);
   if (bf16 && DH == 64)
-    hipLaunchKernelGGL((k_chunk_state<true, 64>), grid, blk, 0, stream, k, v, dt, a_cs, N, chunk, nb, tb, state);
+    hipLaunchKernelGGL((k_chunk_state_bf16<64>), grid, blk, 0, stream, kb, vb, dt, a_cs, N, chunk, nb, tb, state);
   else if (bf16 && DH == 32)
-    hipLaunchKernelGGL((k_chunk_state<true, 32>), grid, blk, 0, stream, k, v, dt, a_cs, N, chunk, nb, tb, state);
+    hipLaunchKernelGGL((k_chunk_state_bf16<32>), grid, blk, 0, stream, kb, vb, dt, a_cs, N, chunk, nb, tb, state);
   else if (!bf16 && DH == 64)
-    hipLaunchKernelGGL((k_chunk_state<false, 64>), grid, blk, 0, stream, k, v, dt, a_cs, N, chunk, nb, tb, state);
+    hipLaunchKernelGGL((k_chunk_state_f32<false, 64>), grid, blk, 0, stream, k, v, dt, a_cs, N, chunk, nb, tb, state);
   else
-    hipLaunchKernelGGL((k_chunk_state<false, 32>), grid, blk, 0, stream, k, v, dt, a_cs, N, chunk, nb, tb, state);
+    hipLaunchKernelGGL((k_chunk_state_f32<false, 32>), grid, blk, 0, stream, k, v, dt, a_cs, N, chunk, nb, tb, state);
   return hipGetLastError();
 }
 

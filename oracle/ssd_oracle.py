@@ -21,7 +21,11 @@ Mongaras & Larson):
   and the normaliser is the row sum of the squared, masked scores.
 * Algorithm 6 (2Mamba inference, appendix): the recurrent form, with order-2
   features k (x) k and the two states H_up (numerator) and H_down (normaliser)
-  decayed by a_t each step.
+  decayed by a_t each step; as printed, a_t = exp(-softplus(h W_A)) (the
+  A-mask), also provided next to the Mamba-2 discretisation.
+* The symmetric-packed order-2 state (not on the pages; derived from the
+  symmetry of k (x) k in Algorithm 6): only the rows (a, b) with a <= b are
+  stored, and the query contraction counts the off-diagonal rows twice.
 
 Readings where the pages are silent or garbled (each is also listed with its
 reasoning in the design notes):
@@ -312,3 +316,117 @@ def decode_step_ref(state, norm_state, q, k, v, dt_proj, dt_bias, A_log, order):
     vop = np.asarray(v, dtype=np.float64) * dt[..., None]
     S, z, y, den = recurrent_step(state, norm_state, q, k, vop, a, order)
     return y, S, z, den
+
+
+def decode_step_amask_ref(state, norm_state, q, k, v, A_proj, dt_proj, order):
+    """One decode step with the A-mask, as Algorithm 6 prints it: the step's
+    decay factor is exp(-softplus(h W_A)) per sequence and head, with no dt in
+    it; the value operand is v * softplus(dt_P) (Algorithm 4's dt, no bias) or
+    plain v when dt_proj is None (Algorithm 6 and Algorithm 5 use v itself).
+
+    state [S,H,D,d_h], norm_state [S,H,D]; q, k, v [S,H,d_h]; A_proj, dt_proj
+    [S,H].  Returns (y [S,H,d_h], new_state, new_norm, den).
+    """
+    dt, a = discretise_amask(A_proj, dt_proj)
+    vop = np.asarray(v, dtype=np.float64)
+    if dt is not None:
+        vop = vop * dt[..., None]
+    S, z, y, den = recurrent_step(state, norm_state, q, k, vop, a, order)
+    return y, S, z, den
+
+
+# ---------------------------------------------------------------------------
+# Symmetric packing of the order-2 state (derived from Algorithm 6)
+#
+# The order-2 feature k (x) k is symmetric in its two indices, so every state
+# row (a, b) equals row (b, a).  The packed layout keeps the rows a <= b only,
+# D' = d_h (d_h + 1) / 2 of them, in row-major order of the upper triangle; a
+# query's contraction phi(q)^T S then counts each off-diagonal row twice.
+# This layout is not on the pages; it is the same state, stored once.
+# ---------------------------------------------------------------------------
+
+def packed_pairs(d):
+    """The pairs (a, b), a <= b, in packed row order: row p(a, b) = a d -
+    a (a - 1) / 2 + (b - a)."""
+    return [(a, b) for a in range(d) for b in range(a, d)]
+
+
+def _pair_rows(d):
+    pairs = packed_pairs(d)
+    upper = np.array([a * d + b for a, b in pairs])   # full row (a, b)
+    lower = np.array([b * d + a for a, b in pairs])   # full row (b, a)
+    return pairs, upper, lower
+
+
+def pack_state(state, norm_state, d):
+    """Full order-2 states [.., d^2, d_v], [.., d^2] -> packed [.., D', d_v],
+    [.., D'].  Each packed row is the mean of the full rows (a, b) and (b, a):
+    the symmetric part, which is all that phi(q)^T S and phi(q)^T z read, and
+    the rows themselves when the state is symmetric."""
+    _, up, lo = _pair_rows(d)
+    S = np.asarray(state, dtype=np.float64)
+    z = np.asarray(norm_state, dtype=np.float64)
+    return (S[..., up, :] + S[..., lo, :]) / 2.0, (z[..., up] + z[..., lo]) / 2.0
+
+
+def unpack_state(state_p, norm_p, d):
+    """Packed [.., D', d_v], [.., D'] -> full [.., d^2, d_v], [.., d^2]: rows
+    (a, b) and (b, a) both take packed row p(min, max)."""
+    pairs = packed_pairs(d)
+    index = np.empty(d * d, dtype=np.int64)
+    for p, (a, b) in enumerate(pairs):
+        index[a * d + b] = p
+        index[b * d + a] = p
+    Sp = np.asarray(state_p, dtype=np.float64)
+    zp = np.asarray(norm_p, dtype=np.float64)
+    return Sp[..., index, :], zp[..., index]
+
+
+def packed_features(x, weighted):
+    """x_a x_b over the packed pairs; with weighted, the off-diagonal pairs
+    count twice (the query side of phi(q)^T S over the packed rows)."""
+    x = np.asarray(x, dtype=np.float64)
+    pairs = packed_pairs(x.shape[-1])
+    ia = np.array([a for a, _ in pairs])
+    ib = np.array([b for _, b in pairs])
+    f = x[..., ia] * x[..., ib]
+    if weighted:
+        f = f * np.where(ia == ib, 1.0, 2.0)
+    return f
+
+
+def recurrent_step_packed(state_p, norm_p, q, k, vop, a):
+    """recurrent_step at order 2 on packed states: S' <- e^a S' + k_a k_b
+    vop^T, z' <- e^a z' + k_a k_b over the pairs a <= b; y = sum_p w_p q_a q_b
+    S'_p / sum_p w_p q_a q_b z'_p with w_p = 1 on the diagonal, 2 off it.
+    Returns (S', z', y, den)."""
+    alpha = np.exp(np.asarray(a, dtype=np.float64))
+    fk = packed_features(k, False)
+    fq = packed_features(q, True)
+    Sp = alpha[..., None, None] * state_p + fk[..., :, None] * np.asarray(vop, dtype=np.float64)[..., None, :]
+    zp = alpha[..., None] * norm_p + fk
+    num = np.einsum("...d,...dv->...v", fq, Sp)
+    den = np.einsum("...d,...d->...", fq, zp)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = num / den[..., None]
+    return Sp, zp, y, den
+
+
+def decode_step_packed_ref(state_p, norm_p, q, k, v, dt_proj, dt_bias, A_log):
+    """decode_step_ref at order 2 on packed states (same discretisation)."""
+    dt_proj = np.asarray(dt_proj, dtype=np.float64)
+    dt = softplus(dt_proj + np.asarray(dt_bias, dtype=np.float64)[None, :])
+    a = -np.exp(np.asarray(A_log, dtype=np.float64))[None, :] * dt
+    vop = np.asarray(v, dtype=np.float64) * dt[..., None]
+    Sp, zp, y, den = recurrent_step_packed(state_p, norm_p, q, k, vop, a)
+    return y, Sp, zp, den
+
+
+def decode_step_amask_packed_ref(state_p, norm_p, q, k, v, A_proj, dt_proj):
+    """decode_step_amask_ref at order 2 on packed states."""
+    dt, a = discretise_amask(A_proj, dt_proj)
+    vop = np.asarray(v, dtype=np.float64)
+    if dt is not None:
+        vop = vop * dt[..., None]
+    Sp, zp, y, den = recurrent_step_packed(state_p, norm_p, q, k, vop, a)
+    return y, Sp, zp, den

@@ -408,3 +408,127 @@ def test_initial_state_continues_the_sequence(order):
         np.testing.assert_allclose(den2, full["den"][:, :, n1:], rtol=1e-10)
         np.testing.assert_allclose(S2, S_all, rtol=1e-10, atol=1e-12)
         np.testing.assert_allclose(z2, z_all, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Algorithm 6 with the A-mask as printed: decay exp(-softplus(h W_A)) per step
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("order", [1, 2])
+@pytest.mark.parametrize("with_dt", [False, True])
+def test_amask_decode_steps_equal_forward(order, with_dt):
+    # the recurrence fed step by step against the A-mask quadratic form
+    rng = np.random.default_rng(51)
+    S, H, T, d = 2, 3, 19, 3
+    qs, ks, vs = (rng.standard_normal((T, S, H, d)) for _ in range(3))
+    A_P = rng.standard_normal((T, S, H)) - 1.0
+    dt_P = rng.standard_normal((T, S, H)) if with_dt else None
+    D = d ** order
+    st, nz = np.zeros((S, H, D, d)), np.zeros((S, H, D))
+    ys = []
+    for t in range(T):
+        y, st, nz, _ = O.decode_step_amask_ref(st, nz, qs[t], ks[t], vs[t], A_P[t],
+                                               None if dt_P is None else dt_P[t], order)
+        ys.append(y)
+    ys = np.stack(ys, axis=2)
+    tr = lambda x: None if x is None else np.moveaxis(x, 0, 2)
+    fwd = O.forward_amask_ref(tr(qs), tr(ks), tr(vs), tr(A_P), tr(dt_P), order)
+    assert rel_err(ys, fwd["y"], fwd["scale"]) <= 1e-10
+
+
+def test_amask_decode_strong_decay_keeps_the_token():
+    # A_P = 45: the factor exp(-softplus(45)) ~ 3e-20 wipes the history, so y_t
+    # is the step's own value operand (v * softplus(dt_P))
+    rng = np.random.default_rng(52)
+    S, H, d = 2, 2, 4
+    st, nz = np.zeros((S, H, d * d, d)), np.zeros((S, H, d * d))
+    for t in range(5):
+        q, k, v = (np.abs(rng.standard_normal((S, H, d))) + 0.1 for _ in range(3))
+        dtp = rng.standard_normal((S, H))
+        y, st, nz, _ = O.decode_step_amask_ref(st, nz, q, k, v, np.full((S, H), 45.0), dtp, 2)
+        np.testing.assert_allclose(y, v * O.softplus(dtp)[..., None], rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Symmetric packing of the order-2 state (derived from Algorithm 6's k (x) k)
+# ---------------------------------------------------------------------------
+
+def test_packed_pairs_layout():
+    assert O.packed_pairs(3) == [(0, 0), (0, 1), (0, 2), (1, 1), (1, 2), (2, 2)]
+    for d in (1, 2, 5, 32, 64):
+        pairs = O.packed_pairs(d)
+        assert len(pairs) == d * (d + 1) // 2
+        for p, (a, b) in enumerate(pairs):
+            assert 0 <= a <= b < d
+            assert p == a * d - a * (a - 1) // 2 + (b - a)
+
+
+def test_pack_unpack_roundtrip_and_symmetric_part():
+    rng = np.random.default_rng(53)
+    d, dv = 4, 3
+    X = rng.standard_normal((2, d, d, dv))
+    sym = (X + X.transpose(0, 2, 1, 3)) / 2  # rows (a, b) and (b, a) equal
+    S = sym.reshape(2, d * d, dv)
+    zm = rng.standard_normal((2, d, d))
+    z = ((zm + zm.transpose(0, 2, 1)) / 2).reshape(2, d * d)
+    Sp, zp = O.pack_state(S, z, d)
+    assert Sp.shape == (2, d * (d + 1) // 2, dv) and zp.shape == (2, d * (d + 1) // 2)
+    S2, z2 = O.unpack_state(Sp, zp, d)
+    np.testing.assert_array_equal(S2, S)
+    np.testing.assert_array_equal(z2, z)
+    Sp2, zp2 = O.pack_state(S2, z2, d)
+    np.testing.assert_array_equal(Sp2, Sp)
+    # an asymmetric state packs to its symmetric part: the packed row (a, b)
+    # is the mean of the two full rows
+    A = X.reshape(2, d * d, dv)
+    Ap, _ = O.pack_state(A, z, d)
+    for p, (a, b) in enumerate(O.packed_pairs(d)):
+        np.testing.assert_allclose(Ap[:, p], (X[:, a, b] + X[:, b, a]) / 2, rtol=1e-15)
+
+
+def test_weighted_packed_contraction_brute_force():
+    # sum over all (a, b) of q_a q_b M_ab, by a plain double loop, equals the
+    # packed contraction with weight 2 off the diagonal, for any M (the packed
+    # rows hold M's symmetric part)
+    rng = np.random.default_rng(54)
+    d = 3
+    q = rng.standard_normal(d)
+    M = rng.standard_normal((d, d))
+    brute = 0.0
+    for a in range(d):
+        for b in range(d):
+            brute += q[a] * q[b] * M[a, b]
+    _, Mp = O.pack_state(np.zeros((d * d, 1)), M.reshape(d * d), d)
+    packed = float(O.packed_features(q, True) @ Mp)
+    assert abs(packed - brute) <= 1e-14 * (1 + abs(brute))
+    # the unweighted k side is the upper triangle of k k^T
+    k = rng.standard_normal(d)
+    np.testing.assert_array_equal(O.packed_features(k, False),
+                                  [k[a] * k[b] for a, b in O.packed_pairs(d)])
+
+
+@pytest.mark.parametrize("amask", [False, True])
+def test_packed_decode_equals_full_decode(amask):
+    # the packed recurrence gives the full recurrence's outputs, and its states
+    # are the packed full states, step after step
+    rng = np.random.default_rng(55)
+    S, H, T, d = 2, 2, 12, 4
+    A_log = np.log(rng.uniform(1, 16, H))
+    bias = rng.standard_normal(H) - 2.0
+    st, nz = np.zeros((S, H, d * d, d)), np.zeros((S, H, d * d))
+    sp, zp = O.pack_state(st, nz, d)
+    for t in range(T):
+        q, k, v = (rng.standard_normal((S, H, d)) for _ in range(3))
+        dtp = rng.standard_normal((S, H))
+        if amask:
+            A_P = rng.standard_normal((S, H))
+            y, st, nz, den = O.decode_step_amask_ref(st, nz, q, k, v, A_P, dtp, 2)
+            yp, sp, zp, denp = O.decode_step_amask_packed_ref(sp, zp, q, k, v, A_P, dtp)
+        else:
+            y, st, nz, den = O.decode_step_ref(st, nz, q, k, v, dtp, bias, A_log, 2)
+            yp, sp, zp, denp = O.decode_step_packed_ref(sp, zp, q, k, v, dtp, bias, A_log)
+        np.testing.assert_allclose(denp, den, rtol=1e-12)
+        np.testing.assert_allclose(yp * den[..., None], y * den[..., None], rtol=1e-10, atol=1e-12)
+        want_s, want_z = O.pack_state(st, nz, d)
+        np.testing.assert_allclose(sp, want_s, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(zp, want_z, rtol=1e-12, atol=1e-14)

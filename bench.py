@@ -16,7 +16,8 @@ the timed steps record none), against MI355X's published dense bf16 MFMA peak (2
 bandwidth (8 TB/s).  Algorithmic work per launch (see the design notes):
   order-2 numerator state scan: 4 * D * d_h flops per token and head
       (2 D d_h for phi(q)^T S, 2 D d_h for the phi(k) (v dt)^T update),
-  decode step: 2 * 4 * (D * d_h + D) bytes per sequence and head.
+  decode step: 2 * 4 * (D * d_h + D) bytes per sequence and head (D = d_h^2 rows,
+      or d_h (d_h + 1) / 2 in the packed layout).
 cpu_baseline: the fp64 oracle (tests' reference implementation, untuned) on a
 bounded sample of the same workload, on this machine's host cores.
 device_ceilings: what the vendor library reaches on the same GPU (torch's fp16
@@ -219,7 +220,9 @@ def cpu_baseline_forward(cfg: I.Config, inp, budget_s=12.0):
 # decode
 # ---------------------------------------------------------------------------
 
-def bench_decode(cfg: I.DecodeConfig, steps: int, warmup: int, dev):
+def bench_decode(cfg: I.DecodeConfig, steps: int, warmup: int, dev, packed=False):
+    """Decode steps; packed: the order-2 states in the packed layout (rows
+    a <= b, D' = d_h (d_h + 1) / 2), whose algorithmic bytes are counted with D'."""
     import torch
     from mamba_ssd_sequence_amd import ssd
 
@@ -228,20 +231,20 @@ def bench_decode(cfg: I.DecodeConfig, steps: int, warmup: int, dev):
     toks = [tuple(to_dev(x, cfg.dtype, dev) for x in s[:3]) + (to_dev(s[3], I.F32, dev),)
             for s in dec.steps()]
     log(f"[bench] {cfg.name}: inputs drawn in {time.time() - t:.1f}s")
-    D = cfg.d_h ** cfg.order
+    D = cfg.d_h ** cfg.order if not packed else cfg.d_h * (cfg.d_h + 1) // 2
     state = torch.zeros((cfg.S, cfg.H, D, cfg.d_h), device=dev)
     norm = torch.zeros((cfg.S, cfg.H, D), device=dev)
     y = torch.empty((cfg.S, cfg.H, cfg.d_h), device=dev)
     bias, alog = to_dev(dec.dt_bias, I.F32, dev), to_dev(dec.A_log, I.F32, dev)
     for i in range(warmup):
         q, k, v, dtp = toks[i]
-        ssd.decode_step(q, k, v, dtp, bias, alog, state, norm, cfg.order, y=y)
+        ssd.decode_step(q, k, v, dtp, bias, alog, state, norm, cfg.order, y=y, packed=packed)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     for i in range(steps):
         q, k, v, dtp = toks[warmup + i]
         ev[i].record()
-        ssd.decode_step(q, k, v, dtp, bias, alog, state, norm, cfg.order, y=y)
+        ssd.decode_step(q, k, v, dtp, bias, alog, state, norm, cfg.order, y=y, packed=packed)
     ev[steps].record()
     torch.cuda.synchronize()
     per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
@@ -249,11 +252,13 @@ def bench_decode(cfg: I.DecodeConfig, steps: int, warmup: int, dev):
     by = 2.0 * 4 * (D * cfg.d_h + D) * cfg.S * cfg.H
     t_ms = float(np.mean(per))
     ach = by / (t_ms * 1e-3) / 1e9
-    return {"workload": cfg.name, "ms_per_step": ms, "tokens_per_s": cfg.S / (ms * 1e-3),
+    name = cfg.name + ("_packed" if packed else "")
+    return {"workload": name, "ms_per_step": ms, "tokens_per_s": cfg.S / (ms * 1e-3),
             "S": cfg.S, "H": cfg.H, "d_h": cfg.d_h, "order": cfg.order, "steps": steps,
+            "state_layout": "packed" if packed else "full", "state_rows": D,
             "roofline": {"kernel": "k_decode", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                         "traffic": measured_traffic("k_decode", cfg.name),
+                         "traffic": measured_traffic("k_decode", name),
                          "alg_bytes_per_launch": by, "avg_launch_ms": t_ms}}, dec
 
 
@@ -337,7 +342,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="o2_bf16_4k",
-                    choices=list(I.CONFIGS) + list(I.DECODE_CONFIGS))
+                    choices=list(I.CONFIGS) + list(I.DECODE_CONFIGS) + ["o2_decode_packed"])
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (64K forward, decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -368,14 +373,15 @@ def main():
         cfg = I.CONFIGS[a.workload]
         res, inp = bench_forward(cfg, a.steps, a.warmup, dev)
     else:
-        cfg = I.DECODE_CONFIGS[a.workload]
-        res, inp = bench_decode(cfg, a.steps, a.warmup, dev)
+        packed = a.workload.endswith("_packed")
+        cfg = I.DECODE_CONFIGS[a.workload[:-len("_packed")] if packed else a.workload]
+        res, inp = bench_decode(cfg, a.steps, a.warmup, dev, packed=packed)
     log(f"[bench] {a.workload}: {res['ms_per_step']:.4f} ms/step, {res['tokens_per_s']:.4g} tokens/s, "
         f"roofline frac {res['roofline']['frac']:.3f}")
 
     extra = []
     if not a.no_extra:
-        for name in ("o2_bf16_64k", "o1_bf16_2k", "o2_decode", "o2_bf16_4k_amask"):
+        for name in ("o2_bf16_64k", "o1_bf16_2k", "o2_decode", "o2_decode_packed", "o2_bf16_4k_amask"):
             if name == a.workload:
                 continue
             torch.cuda.empty_cache()
@@ -383,6 +389,9 @@ def main():
                 r, _ = bench_forward(I.CONFIGS["o2_bf16_4k"], a.steps, a.warmup, dev, amask=True)
             elif name in I.CONFIGS:
                 r, _ = bench_forward(I.CONFIGS[name], max(3, a.steps // 4), 2, dev)
+            elif name == "o2_decode_packed":
+                c = I.DECODE_CONFIGS["o2_decode"]
+                r, _ = bench_decode(c, c.steps, 3, dev, packed=True)
             else:
                 c = I.DECODE_CONFIGS[name]
                 r, _ = bench_decode(c, c.steps, 3, dev)

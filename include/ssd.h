@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 3
+#define SSD_ABI_VERSION 4
 
 typedef enum {
   SSD_OK = 0,
@@ -65,6 +65,15 @@ typedef enum {
 } ssd_status;
 
 typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+/* Layout of the decode states.  SSD_STATE_FULL: D = d_h^p rows, the layout of
+ * ssd_forward's states.  SSD_STATE_PACKED (order 2 only): the order-2 feature
+ * k (x) k is symmetric in its two indices (Algorithm 6), so state rows (a, b)
+ * and (b, a) are equal; the packed layout keeps the rows a <= b only,
+ * D' = d_h (d_h + 1) / 2 of them, row-major over the upper triangle (row
+ * a d_h - a (a - 1) / 2 + b - a).  Not on the pages: the same state in about
+ * half the bytes, which is what a decode step streams. */
+typedef enum { SSD_STATE_FULL = 0, SSD_STATE_PACKED = 1 } ssd_state_layout;
 
 /* ABI version of the loaded library (SSD_ABI_VERSION). */
 int ssd_abi_version(void);
@@ -166,20 +175,6 @@ ssd_status ssd_forward(const void* q, const void* k, const void* v, const float*
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
- * ssd_decode_step -- one recurrent token step (Algorithm 6), in place.
- *
- *   q, k, v    [S,H,d_h] dtype      this step's token for S sequences
- *   dt_proj    [S,H] f32; dt_bias, A_log [H] f32
- *   state      [S,H,D,d_h] f32 in/out  numerator state H_up
- *   norm_state [S,H,D] f32 in/out      normaliser state H_down
- *   y          [S,H,d_h] f32 out
- *
- * dt = softplus(dt_P + dt_bias); alpha = exp(-exp(A_log) dt);
- * state <- alpha state + phi(k) (v dt)^T; norm_state <- alpha norm_state + phi(k);
- * y = phi(q)^T state / phi(q)^T norm_state, using the updated states.
- * d_h is 32 or 64; order 1 or 2.
- */
-/*
  * ssd_set_timing_events -- optional per-kernel timing of the next ssd_forward
  * call on the calling thread (used by the benchmark; not part of the math).
  *
@@ -198,10 +193,64 @@ ssd_status ssd_set_timing_events(hipEvent_t* events, int n);
 /* Number of kernels the last ssd_forward on this thread timed (0 if none). */
 int ssd_timing_count(void);
 
+/*
+ * ssd_decode_step -- one recurrent token step (Algorithm 6), in place, with
+ * the Mamba-2 discretisation of Algorithm 3.
+ *
+ *   q, k, v    [S,H,d_h] dtype      this step's token for S sequences
+ *   dt_proj    [S,H] f32; dt_bias, A_log [H] f32
+ *   layout     ssd_state_layout (SSD_STATE_PACKED requires order 2)
+ *   state      [S,H,D,d_h] f32 in/out  numerator state H_up
+ *   norm_state [S,H,D] f32 in/out      normaliser state H_down
+ *   y          [S,H,d_h] f32 out
+ *
+ * D = d_h^p (full layout) or d_h (d_h + 1) / 2 (packed).
+ * dt = softplus(dt_P + dt_bias); alpha = exp(-exp(A_log) dt);
+ * state <- alpha state + phi(k) (v dt)^T; norm_state <- alpha norm_state + phi(k);
+ * y = phi(q)^T state / phi(q)^T norm_state, using the updated states (packed:
+ * the off-diagonal rows count twice).  d_h is 32 or 64; order 1 or 2.
+ */
 ssd_status ssd_decode_step(const void* q, const void* k, const void* v,
                            const float* dt_proj, const float* dt_bias, const float* A_log,
-                           int64_t S, int64_t H, int64_t d_h, int order, int dtype,
+                           int64_t S, int64_t H, int64_t d_h, int order, int dtype, int layout,
                            float* state, float* norm_state, float* y, hipStream_t stream);
+
+/*
+ * ssd_decode_step_amask -- the decode step as Algorithm 6 prints it: the
+ * step's decay factor is a_t = exp(-softplus(h_t W_A)), per sequence and
+ * head, with no dt in it (the A-mask of Algorithms 4 and 5, whose prefill is
+ * ssd_prep_amask + ssd_forward).
+ *
+ *   A_proj     [S,H] f32   the projection A_P = h W_A
+ *   dt_proj    [S,H] f32 or NULL: the value operand is v softplus(dt_P)
+ *              (Algorithm 4's dt, no bias), or plain v when NULL (Algorithms
+ *              5 and 6)
+ *   everything else as ssd_decode_step.
+ */
+ssd_status ssd_decode_step_amask(const void* q, const void* k, const void* v,
+                                 const float* A_proj, const float* dt_proj, int64_t S,
+                                 int64_t H, int64_t d_h, int order, int dtype, int layout,
+                                 float* state, float* norm_state, float* y, hipStream_t stream);
+
+/*
+ * ssd_state_pack / ssd_state_unpack -- convert order-2 states between the
+ * full layout (ssd_forward's final_state / final_norm and initial_state /
+ * initial_norm) and the packed one (SSD_STATE_PACKED), for BH (sequence,
+ * head) pairs.
+ *
+ *   full:   state [BH, d_h^2, d_h] f32, norm [BH, d_h^2] f32
+ *   packed: state [BH, d_h (d_h + 1) / 2, d_h] f32, norm [BH, d_h (d_h + 1) / 2] f32
+ *
+ * Packing stores, for every a <= b, the mean of the full rows (a, b) and
+ * (b, a): the symmetric part of the state, which is all that phi(q)^T H
+ * reads, and exactly the rows themselves when they are equal.  Unpacking
+ * writes packed row (min(a,b), max(a,b)) to both full rows.  d_h is 32 or
+ * 64; source and destination must not overlap.  Errors as the other calls.
+ */
+ssd_status ssd_state_pack(const float* state, const float* norm_state, int64_t BH, int64_t d_h,
+                          float* state_p, float* norm_p, hipStream_t stream);
+ssd_status ssd_state_unpack(const float* state_p, const float* norm_p, int64_t BH, int64_t d_h,
+                            float* state, float* norm_state, hipStream_t stream);
 
 #ifdef __cplusplus
 }

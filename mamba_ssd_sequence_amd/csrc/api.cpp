@@ -310,40 +310,133 @@ ssd_status ssd_set_timing_events(hipEvent_t* events, int n) {
 
 int ssd_timing_count(void) { return g_timed; }
 
+// Shared by both decode entry points: sizes, parameters, pointers, alignment
+// and overlap; `params` are the per-token / per-head decay inputs.
+static ssd_status decode_common(const char* fn, const void* q, const void* k, const void* v,
+                         const Range* params, int n_params, int64_t S, int64_t H, int64_t d_h,
+                         int order, int dtype, int layout, float* state, float* norm_state,
+                         float* y, bool* empty) {
+  int64_t SH, SHd;
+  *empty = false;
+  if (!mul_ok(S, H, &SH) || !mul_ok(SH, d_h, &SHd))
+    return fail(SSD_ERR_SHAPE, "%s: S, H must be >= 0 and must not overflow", fn);
+  if (dtype != SSD_F32 && dtype != SSD_BF16) return fail(SSD_ERR_UNSUPPORTED, "dtype %d", dtype);
+  if (order != 1 && order != 2) return fail(SSD_ERR_UNSUPPORTED, "order %d (1 or 2)", order);
+  if (d_h != 32 && d_h != 64) return fail(SSD_ERR_UNSUPPORTED, "d_h %lld (32 or 64)", (long long)d_h);
+  if (layout != SSD_STATE_FULL && layout != SSD_STATE_PACKED)
+    return fail(SSD_ERR_UNSUPPORTED, "%s: layout %d", fn, layout);
+  if (layout == SSD_STATE_PACKED && order != 2)
+    return fail(SSD_ERR_UNSUPPORTED, "%s: the packed layout is for order 2", fn);
+  if (SH == 0) {  // no sequences or heads: nothing to compute
+    *empty = true;
+    return SSD_OK;
+  }
+  if (!q || !k || !v || !state || !norm_state || !y)
+    return fail(SSD_ERR_NULL, "%s: a required pointer is NULL", fn);
+  if (SH > (int64_t)0x7fffffff) return fail(SSD_ERR_SHAPE, "%s: grid too large", fn);
+  const int64_t D = order == 1 ? d_h : (layout == SSD_STATE_PACKED ? d_h * (d_h + 1) / 2 : d_h * d_h);
+  int64_t nstate;
+  if (!mul_ok(SH, D * d_h, &nstate)) return fail(SSD_ERR_SHAPE, "%s: state too large", fn);
+  const size_t es = dtype == SSD_BF16 ? 2 : 4;
+  Range ins[8] = {{"q", q, (size_t)SHd * es}, {"k", k, (size_t)SHd * es}, {"v", v, (size_t)SHd * es}};
+  for (int i = 0; i < n_params; ++i) ins[3 + i] = params[i];
+  const Range outs[] = {{"state", state, (size_t)nstate * 4},
+                        {"norm_state", norm_state, (size_t)(SH * D) * 4},
+                        {"y", y, (size_t)SHd * 4}};
+  ssd_status s;
+  if ((s = check_aligned(ins, 3 + n_params)) != SSD_OK || (s = check_aligned(outs, 3)) != SSD_OK)
+    return s;
+  return check_alias(outs, 3, ins, 3 + n_params);
+}
+
 ssd_status ssd_decode_step(const void* q, const void* k, const void* v, const float* dt_proj,
                            const float* dt_bias, const float* A_log, int64_t S, int64_t H,
-                           int64_t d_h, int order, int dtype, float* state, float* norm_state,
-                           float* y, hipStream_t stream) {
+                           int64_t d_h, int order, int dtype, int layout, float* state,
+                           float* norm_state, float* y, hipStream_t stream) {
   try {
     clear_err();
-    int64_t SH, SHd;
-    if (!mul_ok(S, H, &SH) || !mul_ok(SH, d_h, &SHd))
-      return fail(SSD_ERR_SHAPE, "ssd_decode_step: S, H must be >= 0 and must not overflow");
-    if (dtype != SSD_F32 && dtype != SSD_BF16) return fail(SSD_ERR_UNSUPPORTED, "dtype %d", dtype);
-    if (order != 1 && order != 2) return fail(SSD_ERR_UNSUPPORTED, "order %d (1 or 2)", order);
-    if (d_h != 32 && d_h != 64) return fail(SSD_ERR_UNSUPPORTED, "d_h %lld (32 or 64)", (long long)d_h);
-    if (SH == 0) return SSD_OK;  // no sequences or heads: nothing to compute
-    if (!q || !k || !v || !dt_proj || !dt_bias || !A_log || !state || !norm_state || !y)
+    int64_t SH = 0;
+    (void)mul_ok(S, H, &SH);
+    const Range params[] = {{"dt_proj", dt_proj, (size_t)SH * 4},
+                            {"dt_bias", dt_bias, (size_t)(H > 0 ? H : 0) * 4},
+                            {"A_log", A_log, (size_t)(H > 0 ? H : 0) * 4}};
+    bool empty;
+    ssd_status s = decode_common("ssd_decode_step", q, k, v, params, 3, S, H, d_h, order, dtype,
+                                 layout, state, norm_state, y, &empty);
+    if (s != SSD_OK || empty) return s;
+    if (!dt_proj || !dt_bias || !A_log)
       return fail(SSD_ERR_NULL, "ssd_decode_step: a required pointer is NULL");
-    if (SH > (int64_t)0x7fffffff) return fail(SSD_ERR_SHAPE, "ssd_decode_step: grid too large");
-    const int64_t D = order == 1 ? d_h : d_h * d_h;
-    int64_t nstate;
-    if (!mul_ok(SH, D * d_h, &nstate)) return fail(SSD_ERR_SHAPE, "ssd_decode_step: state too large");
-    const size_t es = dtype == SSD_BF16 ? 2 : 4;
-    const Range ins[] = {{"q", q, (size_t)SHd * es},          {"k", k, (size_t)SHd * es},
-                         {"v", v, (size_t)SHd * es},          {"dt_proj", dt_proj, (size_t)SH * 4},
-                         {"dt_bias", dt_bias, (size_t)H * 4}, {"A_log", A_log, (size_t)H * 4}};
-    const Range outs[] = {{"state", state, (size_t)nstate * 4},
-                          {"norm_state", norm_state, (size_t)(SH * D) * 4},
-                          {"y", y, (size_t)SHd * 4}};
-    ssd_status s;
-    if ((s = check_aligned(ins, 6)) != SSD_OK || (s = check_aligned(outs, 3)) != SSD_OK) return s;
-    if ((s = check_alias(outs, 3, ins, 6)) != SSD_OK) return s;
-    return hip_status(ssd::launch_decode(dtype == SSD_BF16, d_h, order, q, k, v, dt_proj, dt_bias, A_log,
-                                         S, H, state, norm_state, y, stream),
+    return hip_status(ssd::launch_decode(dtype == SSD_BF16, d_h, order, layout == SSD_STATE_PACKED, q, k,
+                                         v, dt_proj, dt_bias, A_log, nullptr, S, H, state, norm_state,
+                                         y, stream),
                       "decode launch");
   } catch (...) {
     return fail(SSD_ERR_HIP, "ssd_decode_step: unexpected exception");
+  }
+}
+
+ssd_status ssd_decode_step_amask(const void* q, const void* k, const void* v, const float* A_proj,
+                                 const float* dt_proj, int64_t S, int64_t H, int64_t d_h,
+                                 int order, int dtype, int layout, float* state,
+                                 float* norm_state, float* y, hipStream_t stream) {
+  try {
+    clear_err();
+    int64_t SH = 0;
+    (void)mul_ok(S, H, &SH);
+    const Range params[] = {{"A_proj", A_proj, (size_t)SH * 4}, {"dt_proj", dt_proj, (size_t)SH * 4}};
+    bool empty;
+    ssd_status s = decode_common("ssd_decode_step_amask", q, k, v, params, 2, S, H, d_h, order, dtype,
+                                 layout, state, norm_state, y, &empty);
+    if (s != SSD_OK || empty) return s;
+    if (!A_proj) return fail(SSD_ERR_NULL, "ssd_decode_step_amask: A_proj is NULL");
+    return hip_status(ssd::launch_decode(dtype == SSD_BF16, d_h, order, layout == SSD_STATE_PACKED, q, k,
+                                         v, dt_proj, nullptr, nullptr, A_proj, S, H, state,
+                                         norm_state, y, stream),
+                      "decode launch");
+  } catch (...) {
+    return fail(SSD_ERR_HIP, "ssd_decode_step_amask: unexpected exception");
+  }
+}
+
+// ssd_state_pack / ssd_state_unpack
+static ssd_status state_layout(const char* fn, bool to_packed, const float* src_S, const float* src_z,
+                               int64_t BH, int64_t d_h, float* dst_S, float* dst_z,
+                               hipStream_t stream) {
+  clear_err();
+  if (BH < 0) return fail(SSD_ERR_SHAPE, "%s: BH must be >= 0", fn);
+  if (d_h != 32 && d_h != 64) return fail(SSD_ERR_UNSUPPORTED, "d_h %lld (32 or 64)", (long long)d_h);
+  if (BH == 0) return SSD_OK;
+  if (!src_S || !src_z || !dst_S || !dst_z) return fail(SSD_ERR_NULL, "%s: a required pointer is NULL", fn);
+  const int64_t Df = d_h * d_h, Dp = d_h * (d_h + 1) / 2;
+  int64_t nf, np_;
+  if (!mul_ok(BH, Df * d_h, &nf) || !mul_ok(BH, Dp * d_h, &np_) || BH * d_h > (int64_t)0x7fffffff)
+    return fail(SSD_ERR_SHAPE, "%s: state too large", fn);
+  const int64_t ns = to_packed ? nf : np_, nd = to_packed ? np_ : nf;
+  const int64_t zs = (to_packed ? Df : Dp) * BH, zd = (to_packed ? Dp : Df) * BH;
+  const Range ins[] = {{"source state", src_S, (size_t)ns * 4}, {"source norm", src_z, (size_t)zs * 4}};
+  const Range outs[] = {{"state", dst_S, (size_t)nd * 4}, {"norm", dst_z, (size_t)zd * 4}};
+  ssd_status s;
+  if ((s = check_aligned(ins, 2)) != SSD_OK || (s = check_aligned(outs, 2)) != SSD_OK) return s;
+  if ((s = check_alias(outs, 2, ins, 2)) != SSD_OK) return s;
+  return hip_status(ssd::launch_state_layout(to_packed, d_h, BH, src_S, src_z, dst_S, dst_z, stream),
+                    "state layout launch");
+}
+
+ssd_status ssd_state_pack(const float* state, const float* norm_state, int64_t BH, int64_t d_h,
+                          float* state_p, float* norm_p, hipStream_t stream) {
+  try {
+    return state_layout("ssd_state_pack", true, state, norm_state, BH, d_h, state_p, norm_p, stream);
+  } catch (...) {
+    return fail(SSD_ERR_HIP, "ssd_state_pack: unexpected exception");
+  }
+}
+
+ssd_status ssd_state_unpack(const float* state_p, const float* norm_p, int64_t BH, int64_t d_h,
+                            float* state, float* norm_state, hipStream_t stream) {
+  try {
+    return state_layout("ssd_state_unpack", false, state_p, norm_p, BH, d_h, state, norm_state, stream);
+  } catch (...) {
+    return fail(SSD_ERR_HIP, "ssd_state_unpack: unexpected exception");
   }
 }
 

@@ -153,9 +153,18 @@ hipError_t launch_o2_state(const void* rec, int64_t BH, int64_t N, float* part,
                            float* final_state, float* zstate, float* final_norm, const float* S0,
                            const float* Z0, hipStream_t stream);
 
-hipError_t launch_decode(bool bf16, int64_t DH, int order, const void* q, const void* k,
-                         const void* v, const float* dt_proj, const float* dt_bias,
-                         const float* A_log, int64_t S, int64_t H, float* state, float* norm_state,
-                         float* y, hipStream_t stream);
+// One decode step.  A_proj == NULL: the Mamba-2 discretisation (dt_proj,
+// dt_bias, A_log); else the A-mask (A_proj, optional dt_proj).  packed: the
+// order-2 states in the packed layout (rows a <= b).
+hipError_t launch_decode(bool bf16, int64_t DH, int order, bool packed, const void* q,
+                         const void* k, const void* v, const float* dt_proj, const float* dt_bias,
+                         const float* A_log, const float* A_proj, int64_t S, int64_t H,
+                         float* state, float* norm_state, float* y, hipStream_t stream);
+
+// Order-2 state layout conversion over BH (sequence, head) pairs: full ->
+// packed (the symmetric part) when to_packed, else packed -> full.
+hipError_t launch_state_layout(bool to_packed, int64_t DH, int64_t BH, const float* src_S,
+                               const float* src_z, float* dst_S, float* dst_z,
+                               hipStream_t stream);
 
 }  // namespace ssd

@@ -190,8 +190,10 @@ class DecodeInputs:
     dt_bias: np.ndarray  # [H] fp32
     _rng_state: dict
 
-    def steps(self, n_steps=None, S=None):
-        """Yield (q, k, v, dt_proj) per step, step-major, sequences [0:S)."""
+    def steps(self, n_steps=None, S=None, with_A=False):
+        """Yield (q, k, v, dt_proj) per step, step-major, sequences [0:S); with
+        with_A also the A-mask projection A_P [S,H] ~ N(-3, 1), drawn after
+        dt_proj (the other draws are unchanged)."""
         rng = np.random.default_rng()
         rng.bit_generator.state = self._rng_state
         c = self.cfg
@@ -200,10 +202,12 @@ class DecodeInputs:
             shape = (c.S, c.H, c.d_h)
             qkv = [_store(silu(rng.standard_normal(shape)), c.dtype) for _ in range(3)]
             dt_proj = rng.standard_normal((c.S, c.H)).astype(np.float32)
+            out = qkv + [dt_proj]
+            if with_A:
+                out.append((rng.standard_normal((c.S, c.H)) - 3.0).astype(np.float32))
             if S is not None:
-                qkv = [x[:S] for x in qkv]
-                dt_proj = dt_proj[:S]
-            yield qkv[0], qkv[1], qkv[2], dt_proj
+                out = [x[:S] for x in out]
+            yield tuple(out)
 
 
 def make_decode_inputs(cfg: DecodeConfig, *, S=None, H=None, steps=None, seed=None) -> DecodeInputs:

@@ -8,6 +8,8 @@ call fails, an exception is raised.
     dt, a_cs, a_chunk = prep(dt_proj, dt_bias, A_log, chunk)
     y = forward(q, k, v, dt, a_cs, order=2, chunk=64)
     y = decode_step(q, k, v, dt_proj, dt_bias, A_log, state, norm_state, order=2)
+    y = decode_step_amask(q, k, v, A_proj, dt_proj, state, norm_state, order=2)
+    state_p, norm_p = state_pack(state, norm_state)
 """
 from __future__ import annotations
 
@@ -22,6 +24,8 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "ssd.h")
 SSD_OK = 0
 SSD_F32 = 0
 SSD_BF16 = 1
+SSD_STATE_FULL = 0
+SSD_STATE_PACKED = 1
 STATUS = ["SSD_OK", "SSD_ERR_NULL", "SSD_ERR_SHAPE", "SSD_ERR_UNSUPPORTED", "SSD_ERR_ALIGN",
           "SSD_ERR_ALIAS", "SSD_ERR_WORKSPACE", "SSD_ERR_HIP"]
 
@@ -57,7 +61,13 @@ def _declare(lib):
     lib.ssd_timing_count.restype = ctypes.c_int
     lib.ssd_timing_count.argtypes = []
     lib.ssd_decode_step.restype = ctypes.c_int
-    lib.ssd_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, i64, i64, i64, i32, i32, fp, fp, fp, vp]
+    lib.ssd_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, i64, i64, i64, i32, i32, i32, fp, fp, fp, vp]
+    lib.ssd_decode_step_amask.restype = ctypes.c_int
+    lib.ssd_decode_step_amask.argtypes = [vp, vp, vp, fp, fp, i64, i64, i64, i32, i32, i32, fp, fp, fp, vp]
+    lib.ssd_state_pack.restype = ctypes.c_int
+    lib.ssd_state_pack.argtypes = [fp, fp, i64, i64, fp, fp, vp]
+    lib.ssd_state_unpack.restype = ctypes.c_int
+    lib.ssd_state_unpack.argtypes = [fp, fp, i64, i64, fp, fp, vp]
     return lib
 
 
@@ -228,8 +238,7 @@ class KernelTimer:
         return [self.events[i].elapsed_time(self.events[i + 1]) for i in range(self.count)]
 
 
-def decode_step(q, k, v, dt_proj, dt_bias, A_log, state, norm_state, order: int, *, y=None):
-    """ssd_decode_step: updates state/norm_state in place, returns y [S,H,d_h] fp32."""
+def _decode_common(q, k, v, params, state, norm_state, order, y, packed):
     torch = _torch()
     _require(q, "q")
     dev = q.device
@@ -237,12 +246,69 @@ def decode_step(q, k, v, dt_proj, dt_bias, A_log, state, norm_state, order: int,
     for name, t in (("k", k), ("v", v)):
         _require(t, name, q.dtype, dev)
     S, H, d_h = q.shape
-    for name, t in (("dt_proj", dt_proj), ("dt_bias", dt_bias), ("A_log", A_log),
-                    ("state", state), ("norm_state", norm_state)):
-        _require(t, name, torch.float32, dev)
+    for name, t in params + (("state", state), ("norm_state", norm_state)):
+        if t is not None:
+            _require(t, name, torch.float32, dev)
     if y is None:
         y = torch.empty((S, H, d_h), dtype=torch.float32, device=dev)
+    layout = SSD_STATE_PACKED if packed else SSD_STATE_FULL
+    return dev, dtype, S, H, d_h, layout, y
+
+
+def decode_step(q, k, v, dt_proj, dt_bias, A_log, state, norm_state, order: int, *, y=None,
+                packed=False):
+    """ssd_decode_step: updates state/norm_state in place, returns y [S,H,d_h] fp32.
+    packed: the order-2 states are in the packed layout (rows a <= b)."""
+    dev, dtype, S, H, d_h, layout, y = _decode_common(
+        q, k, v, (("dt_proj", dt_proj), ("dt_bias", dt_bias), ("A_log", A_log)), state, norm_state,
+        order, y, packed)
     _check(lib().ssd_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(dt_proj), _ptr(dt_bias), _ptr(A_log),
-                                 S, H, d_h, order, dtype, _ptr(state), _ptr(norm_state), _ptr(y),
+                                 S, H, d_h, order, dtype, layout, _ptr(state), _ptr(norm_state), _ptr(y),
                                  _stream(dev)))
     return y
+
+
+def decode_step_amask(q, k, v, A_proj, dt_proj, state, norm_state, order: int, *, y=None,
+                      packed=False):
+    """ssd_decode_step_amask (Algorithm 6 as printed): decay exp(-softplus(A_P));
+    value operand v softplus(dt_P), or plain v when dt_proj is None."""
+    dev, dtype, S, H, d_h, layout, y = _decode_common(
+        q, k, v, (("A_proj", A_proj), ("dt_proj", dt_proj)), state, norm_state, order, y, packed)
+    _check(lib().ssd_decode_step_amask(_ptr(q), _ptr(k), _ptr(v), _ptr(A_proj),
+                                       _ptr(dt_proj) if dt_proj is not None else None,
+                                       S, H, d_h, order, dtype, layout, _ptr(state), _ptr(norm_state),
+                                       _ptr(y), _stream(dev)))
+    return y
+
+
+def _state_layout(fn, src_S, src_z, to_packed, out):
+    torch = _torch()
+    _require(src_S, "state", torch.float32)
+    dev = src_S.device
+    _require(src_z, "norm", torch.float32, dev)
+    lead = src_S.shape[:-2]
+    d_h = src_S.shape[-1]
+    BH = 1
+    for n in lead:
+        BH *= n
+    src_rows = d_h * d_h if to_packed else d_h * (d_h + 1) // 2
+    if src_S.shape[-2] != src_rows or tuple(src_z.shape) != tuple(lead) + (src_rows,):
+        raise ValueError(f"state shape {tuple(src_S.shape)} / norm shape {tuple(src_z.shape)} "
+                         f"do not match {src_rows} rows of width {d_h}")
+    rows = d_h * (d_h + 1) // 2 if to_packed else d_h * d_h
+    if out is None:
+        out = (torch.empty(lead + (rows, d_h), dtype=torch.float32, device=dev),
+               torch.empty(lead + (rows,), dtype=torch.float32, device=dev))
+    _check(fn(_ptr(src_S), _ptr(src_z), BH, d_h, _ptr(out[0]), _ptr(out[1]), _stream(dev)))
+    return out
+
+
+def state_pack(state, norm_state, out=None):
+    """ssd_state_pack: full order-2 states [..., d_h^2, d_h], [..., d_h^2] ->
+    packed [..., d_h(d_h+1)/2, d_h], [..., d_h(d_h+1)/2]."""
+    return _state_layout(lib().ssd_state_pack, state, norm_state, True, out)
+
+
+def state_unpack(state_p, norm_p, out=None):
+    """ssd_state_unpack: packed order-2 states -> the full layout."""
+    return _state_layout(lib().ssd_state_unpack, state_p, norm_p, False, out)

@@ -18,14 +18,15 @@ def lib():
 def test_exports_every_header_function(lib):
     names = ssd.header_functions()
     assert set(names) >= {"ssd_prep", "ssd_prep_amask", "ssd_forward", "ssd_forward_workspace_size",
-                          "ssd_decode_step",
+                          "ssd_decode_step", "ssd_decode_step_amask", "ssd_state_pack",
+                          "ssd_state_unpack",
                           "ssd_abi_version", "ssd_status_str", "ssd_last_error"}
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssd_abi_version() == 3
+    assert lib.ssd_abi_version() == 4
     for i, name in enumerate(ssd.STATUS):
         assert lib.ssd_status_str(i).decode() == name
     assert lib.ssd_status_str(99).decode() == "SSD_ERR_UNKNOWN"
@@ -111,9 +112,14 @@ def test_workspace_size(lib):
     assert lib.ssd_forward_workspace_size(B, H, 0, d, 2, 64, 1) == 0  # empty: no workspace
 
 
-def dec(lib, *, S=1, H=1, d_h=64, order=2, dtype=1, q=A[0], state=A[6], norm=A[7], y=A[8]):
-    return lib.ssd_decode_step(q, A[1], A[2], A[3], A[4], A[5], S, H, d_h, order, dtype,
+def dec(lib, *, S=1, H=1, d_h=64, order=2, dtype=1, layout=0, q=A[0], state=A[6], norm=A[7], y=A[8]):
+    return lib.ssd_decode_step(q, A[1], A[2], A[3], A[4], A[5], S, H, d_h, order, dtype, layout,
                                state, norm, y, None)
+
+
+def dec_amask(lib, *, S=1, H=1, d_h=64, order=2, layout=0, A_proj=A[3], dt_proj=A[4], norm=A[7]):
+    return lib.ssd_decode_step_amask(A[0], A[1], A[2], A_proj, dt_proj, S, H, d_h, order, 1, layout,
+                                     A[6], norm, A[8], None)
 
 
 def test_decode_errors(lib):
@@ -127,6 +133,28 @@ def test_decode_errors(lib):
     assert dec(lib, y=A[0]) == 5
     assert "y" in lib.ssd_last_error().decode() and "q" in lib.ssd_last_error().decode()
     assert dec(lib, norm=A[6] + 64) == 5  # norm_state inside state
+    assert dec(lib, layout=2) == 3
+    assert dec(lib, layout=1, order=1) == 3  # packing is for order 2
+
+
+def test_decode_amask_errors(lib):
+    assert dec_amask(lib, A_proj=None) == 1
+    assert dec_amask(lib, A_proj=A[3] + 4) == 4
+    assert dec_amask(lib, dt_proj=A[6]) == 5       # dt_proj inside the state output
+    assert dec_amask(lib, norm=A[3]) == 5          # an output over A_proj
+    assert dec_amask(lib, layout=1, order=1) == 3
+    assert dec_amask(lib, d_h=48) == 3
+    assert dec_amask(lib, S=-2) == 2
+
+
+def test_state_layout_errors(lib):
+    for fn in (lib.ssd_state_pack, lib.ssd_state_unpack):
+        assert fn(None, A[1], 2, 64, A[2], A[3], None) == 1
+        assert fn(A[0], A[1], 2, 48, A[2], A[3], None) == 3
+        assert fn(A[0], A[1], -1, 64, A[2], A[3], None) == 2
+        assert fn(A[0], A[1], 2, 64, A[2] + 4, A[3], None) == 4
+        assert fn(A[0], A[1], 2, 64, A[0], A[3], None) == 5  # destination over the source
+        assert fn(None, None, 0, 64, None, None, None) == 0   # empty
 
 
 def test_binding_refuses_cpu_tensors():
@@ -150,5 +178,7 @@ def test_empty_inputs_are_valid_no_ops(lib):
                                None, None, None, None, None, 0, None) == 0
     assert lib.ssd_forward(None, None, None, None, None, None, None, 1, 2, 0, 48, 1, 64, 1,
                            None, None, None, None, None, 0, None) == 3
-    assert lib.ssd_decode_step(None, None, None, None, None, None, 0, 4, 64, 2, 1,
+    assert lib.ssd_decode_step(None, None, None, None, None, None, 0, 4, 64, 2, 1, 0,
                                None, None, None, None) == 0
+    assert lib.ssd_decode_step_amask(None, None, None, None, None, 3, 0, 64, 2, 1, 1,
+                                     None, None, None, None) == 0

@@ -423,6 +423,182 @@ def test_prefill_then_decode():
 
 
 # ---------------------------------------------------------------------------
+# decode: the A-mask as Algorithm 6 prints it, and the packed order-2 layout
+# ---------------------------------------------------------------------------
+
+def run_decode_variant(dec, order, steps, *, amask, with_dt=True, packed=False, check_heads=None):
+    """Decode `steps` steps from a zero state with the A-mask and/or the packed
+    layout; returns per-step y, the step inputs, and the final states (all
+    heads, or check_heads only)."""
+    ssd = ssd_mod()
+    c = dec.cfg
+    d = c.d_h
+    D = d if order == 1 else (d * (d + 1) // 2 if packed else d * d)
+    state = torch.zeros((c.S, c.H, D, d), device="cuda")
+    norm = torch.zeros((c.S, c.H, D), device="cuda")
+    bias, alog = to_dev_f32(dec.dt_bias), to_dev_f32(dec.A_log)
+    ys, ins = [], []
+    for (q, k, v, dtp, A_P) in dec.steps(steps, with_A=True):
+        qd, kd, vd = (to_dev_qkv(x, c.dtype) for x in (q, k, v))
+        if amask:
+            y = ssd.decode_step_amask(qd, kd, vd, to_dev_f32(A_P), to_dev_f32(dtp) if with_dt else None,
+                                      state, norm, order, packed=packed)
+        else:
+            y = ssd.decode_step(qd, kd, vd, to_dev_f32(dtp), bias, alog, state, norm, order, packed=packed)
+        if check_heads is None:
+            ys.append(y.cpu().numpy())
+            ins.append((q, k, v, dtp, A_P))
+        else:
+            s_idx, h_idx = check_heads
+            ys.append(y[s_idx, h_idx].cpu().numpy())
+            ins.append(tuple(x[s_idx, h_idx] for x in (q, k, v, dtp, A_P)))
+    torch.cuda.synchronize()
+    if check_heads is None:
+        return ys, ins, state.cpu().numpy(), norm.cpu().numpy()
+    s_idx, h_idx = check_heads
+    return ys, ins, state[s_idx, h_idx].cpu().numpy(), norm[s_idx, h_idx].cpu().numpy()
+
+
+def decode_variant_reference(ins, dtype, dec, order, *, amask, with_dt, h_idx=None):
+    """The oracle for run_decode_variant: the quadratic form over the steps
+    (outputs and their error scale) and the recurrence's final full states."""
+    up = I.bf16_bits_to_f64 if dtype == I.BF16 else (lambda x: x.astype(np.float64))
+    A_log, dt_bias = dec.A_log.astype(np.float64), dec.dt_bias.astype(np.float64)
+    if h_idx is not None:
+        A_log, dt_bias = A_log[h_idx], dt_bias[h_idx]
+    S = None
+    for (q, k, v, dtp, A_P) in ins:
+        q, k, v = up(q), up(k), up(v)
+        if S is None:
+            D = q.shape[-1] ** order
+            S = np.zeros(q.shape[:-1] + (D, q.shape[-1]))
+            z = np.zeros(q.shape[:-1] + (D,))
+        if amask:
+            _, S, z, _ = O.decode_step_amask_ref(S, z, q, k, v, A_P, dtp if with_dt else None, order)
+        elif h_idx is None:
+            _, S, z, _ = O.decode_step_ref(S, z, q, k, v, dtp, dt_bias, A_log, order)
+        else:  # per-row head parameters: rows of (s, h) pairs as S = 1, H = M
+            _, S1, z1, _ = O.decode_step_ref(S[None], z[None], q[None], k[None], v[None], dtp[None],
+                                             dt_bias, A_log, order)
+            S, z = S1[0], z1[0]
+    stack = lambda j: np.stack([up(x[j]) if j < 3 else x[j].astype(np.float64) for x in ins], axis=-2 if j < 3 else -1)
+    qs, ks, vs, dtp, A_P = (stack(j) for j in range(5))
+    if h_idx is not None:
+        qs, ks, vs, dtp, A_P = (x[None] for x in (qs, ks, vs, dtp, A_P))
+    if amask:
+        ref = O.forward_amask_ref(qs, ks, vs, A_P, dtp if with_dt else None, order)
+    else:
+        ref = O.forward_ref(qs, ks, vs, dtp, dt_bias, A_log, order)
+    return ref, S, z
+
+
+# (order, d_h, dtype, A-mask, value operand v*dt, packed layout)
+DECODE_VARIANTS = [
+    (2, 64, I.BF16, False, True, True), (2, 32, I.BF16, False, True, True), (2, 64, I.F32, False, True, True),
+    (2, 64, I.BF16, True, False, False), (2, 64, I.BF16, True, True, True), (2, 32, I.F32, True, False, True),
+    (1, 64, I.BF16, True, True, False), (1, 32, I.F32, True, False, False),
+]
+
+
+@pytest.mark.parametrize("order,d_h,dtype,amask,with_dt,packed", DECODE_VARIANTS)
+def test_decode_variants_small(order, d_h, dtype, amask, with_dt, packed):
+    say("decode variant", order, d_h, dtype, "amask" if amask else "mamba2", with_dt, "packed" if packed else "full")
+    cfg = I.DecodeConfig("t", S=3, H=2, d_h=d_h, order=order, steps=17, dtype=dtype, seed=70 + d_h + order)
+    dec = I.make_decode_inputs(cfg)
+    ys, ins, st, nz = run_decode_variant(dec, order, cfg.steps, amask=amask, with_dt=with_dt, packed=packed)
+    ref, Sx, zx = decode_variant_reference(ins, dtype, dec, order, amask=amask, with_dt=with_dt)
+    y = np.stack(ys, axis=2)  # [S,H,T,d]
+    err = row_error(y, ref["y"], ref["scale"])
+    say("  err", err)
+    assert err <= TOL[dtype]
+    if packed:
+        Sx, zx = O.pack_state(Sx, zx, d_h)
+    assert st.shape == Sx.shape and nz.shape == zx.shape
+    assert np.abs(st - Sx).max() <= 1e-5 * np.abs(Sx).max()
+    assert np.abs(nz - zx).max() <= 1e-5 * np.abs(zx).max()
+
+
+def test_decode_packed_full_size_sampled():
+    """The order-2 decode workload (256 x 32 heads, 128 steps) in the packed
+    layout; 16 (sequence, head) pairs are checked at every step and at the end."""
+    cfg = I.DECODE_CONFIGS["o2_decode"]
+    say("decode packed full")
+    dec = I.make_decode_inputs(cfg)
+    rng = np.random.default_rng(6)
+    s_idx = rng.integers(0, cfg.S, 16)
+    h_idx = rng.integers(0, cfg.H, 16)
+    ys, ins, st, nz = run_decode_variant(dec, 2, cfg.steps, amask=False, packed=True,
+                                         check_heads=(s_idx, h_idx))
+    ref, Sx, zx = decode_variant_reference(ins, cfg.dtype, dec, 2, amask=False, with_dt=True, h_idx=h_idx)
+    y = np.stack(ys, axis=1)[None]  # [1,M,T,d]
+    err = row_error(y, ref["y"], ref["scale"])
+    say("  err", err)
+    assert err <= TOL[cfg.dtype]
+    Sp, zp = O.pack_state(Sx, zx, cfg.d_h)
+    assert np.abs(st - Sp).max() <= 1e-5 * np.abs(Sp).max()
+    assert np.abs(nz - zp).max() <= 1e-5 * np.abs(zp).max()
+
+
+@pytest.mark.parametrize("d_h", [32, 64])
+def test_state_pack_unpack(d_h):
+    """Packing keeps the rows a <= b (bit-exact for symmetric states), unpacking
+    restores the full layout; an asymmetric state packs to its symmetric part."""
+    ssd = ssd_mod()
+    say("state pack/unpack", d_h)
+    rng = np.random.default_rng(60 + d_h)
+    X = rng.standard_normal((2, 3, d_h, d_h, d_h)).astype(np.float32)
+    sym = (X + X.transpose(0, 1, 3, 2, 4)) * np.float32(0.5)  # rows (a,b) and (b,a) identical
+    S = np.ascontiguousarray(sym.reshape(2, 3, d_h * d_h, d_h))
+    zm = rng.standard_normal((2, 3, d_h, d_h)).astype(np.float32)
+    z = np.ascontiguousarray(((zm + zm.transpose(0, 1, 3, 2)) * np.float32(0.5)).reshape(2, 3, d_h * d_h))
+    Sp, zp = ssd.state_pack(to_dev_f32(S), to_dev_f32(z))
+    want_S, want_z = O.pack_state(S, z, d_h)
+    np.testing.assert_array_equal(Sp.cpu().numpy(), want_S)
+    np.testing.assert_array_equal(zp.cpu().numpy(), want_z)
+    S2, z2 = ssd.state_unpack(Sp, zp)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(S2.cpu().numpy(), S)
+    np.testing.assert_array_equal(z2.cpu().numpy(), z)
+    # asymmetric: the mean of the two rows, within one rounding of the fp32 sum
+    A = np.ascontiguousarray(X.reshape(2, 3, d_h * d_h, d_h))
+    Az = np.ascontiguousarray(zm.reshape(2, 3, d_h * d_h))
+    Ap, Azp = ssd.state_pack(to_dev_f32(A), to_dev_f32(Az))
+    want_A, want_Az = O.pack_state(A, Az, d_h)
+    assert np.all(np.abs(Ap.cpu().numpy() - want_A) <= 2.0 ** -24 * np.abs(want_A))
+    assert np.all(np.abs(Azp.cpu().numpy() - want_Az) <= 2.0 ** -24 * np.abs(want_Az))
+
+
+def test_prefill_then_decode_amask_packed():
+    """2Mamba inference as Algorithm 6 prints it: an A-mask prefill (plain V)
+    hands its final states, packed, to the A-mask decode step; continuing for T
+    tokens equals the oracle over N + T tokens."""
+    ssd = ssd_mod()
+    cfg = I.CONFIGS["o2_bf16_4k"]
+    N, T = 130, 6
+    inp = I.make_forward_inputs(cfg, B=2, H=2, N=N + T, seed=23)
+    say("prefill amask -> packed decode")
+    q, k, v = (to_dev_qkv(np.ascontiguousarray(x[:, :, :N]), cfg.dtype) for x in (inp.q, inp.k, inp.v))
+    _, a_cs, _ = ssd.prep_amask(to_dev_f32(np.ascontiguousarray(inp.A_proj[:, :, :N])), None, 64)
+    D = 64 * 64
+    fs = torch.empty((2, 2, D, 64), device="cuda")
+    fn = torch.empty((2, 2, D), device="cuda")
+    ssd.forward(q, k, v, None, a_cs, 2, 64, final_state=fs, final_norm=fn)
+    state, norm = ssd.state_pack(fs, fn)
+    ys = []
+    for t in range(N, N + T):
+        qt, kt, vt = (to_dev_qkv(np.ascontiguousarray(x[:, :, t]), cfg.dtype) for x in (inp.q, inp.k, inp.v))
+        y = ssd.decode_step_amask(qt, kt, vt, to_dev_f32(np.ascontiguousarray(inp.A_proj[:, :, t])), None,
+                                  state, norm, 2, packed=True)
+        ys.append(y.cpu().numpy())
+    qf, kf, vf = inp.qkv_f64()
+    ref = O.forward_amask_ref(qf, kf, vf, inp.A_proj, None, 2, rows=np.arange(N, N + T))
+    y = np.stack(ys, axis=2)
+    err = row_error(y, ref["y"], ref["scale"])
+    say("  err", err)
+    assert err <= TOL[cfg.dtype]
+
+
+# ---------------------------------------------------------------------------
 # empty inputs and the method's degenerate cases
 # ---------------------------------------------------------------------------
 

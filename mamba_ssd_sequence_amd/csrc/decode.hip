@@ -20,16 +20,14 @@
 //
 // The step is pure streaming: every state element is read once and written
 // once (order 2, d_h 64: 1 MiB + 16 KiB per sequence and head, 520 KiB
-// packed), so the kernel is HBM-bound.  One workgroup per (sequence, head) --
-// 1024 threads for the large order-2 states, 256 for the small ones; the
-// per-row features phi(k)_r and (weighted) phi(q)_r are tabulated in LDS
+// packed), so the kernel is HBM-bound.  One workgroup per (sequence, head);
+// the per-row features phi(k)_r and (weighted) phi(q)_r are tabulated in LDS
 // first; each thread owns one 16-byte column group of the state rows it
 // visits, keeps several row loads in flight (non-temporal: the state has no
 // reuse within a step), fuses the update with the output contraction, and the
-// partial outputs are reduced across lanes and waves at the end.  (A sweep of
-// rows in flight x workgroup size on the 256 x 32-head, d_h 64 order-2 step
-// favoured 4 rows x 1024 threads: 71.5% of the HBM peak against 67.6% for 8
-// rows x 256 threads.)
+// partial outputs are reduced across lanes and waves at the end.  Workgroup
+// size and rows in flight per layout: see launch_decode.  (Issuing the first
+// row loads before the set-up, to hide it, was measured slower.)
 #include "common.h"
 #include "launch.h"
 
@@ -45,7 +43,7 @@ __device__ __forceinline__ int packed_row(int a, int b, int dh) {
   return a * dh - a * (a - 1) / 2 + (b - a);
 }
 
-template <typename St, int DH, int ORDER, int NTH, bool PACKED>
+template <typename St, int DH, int ORDER, int NTH, int UR, bool PACKED>
 __global__ __launch_bounds__(NTH) void k_decode(const St* __restrict__ q, const St* __restrict__ k,
                                                 const St* __restrict__ v,
                                                 const float* __restrict__ dt_proj,
@@ -57,10 +55,9 @@ __global__ __launch_bounds__(NTH) void k_decode(const St* __restrict__ q, const 
   constexpr int R = Rows<DH, ORDER, PACKED>::value;
   constexpr int CG = DH / 4;         // 16-byte column groups per state row
   constexpr int RPP = NTH / CG;      // rows per pass of the workgroup
-  constexpr int UMAX = NTH >= 1024 ? 4 : 8;
-  constexpr int U = (R / RPP) < UMAX ? (R / RPP) : UMAX;  // rows in flight per thread
+  constexpr int U = (R / RPP) < UR ? (R / RPP) : UR;  // rows in flight per thread
   constexpr int STEP = RPP * U;
-  constexpr int RMAIN = (R / STEP) * STEP;  // rows of the unrolled loop; the rest one by one
+  constexpr int RMAIN = (R / STEP) * STEP;  // rows of the unrolled loop (>= STEP); the rest one by one
   constexpr int NWV = NTH / WAVE;
   constexpr int RT = ORDER == 2 ? R : 1;
   static_assert(U >= 1, "workgroup too large for the state");
@@ -80,10 +77,13 @@ __global__ __launch_bounds__(NTH) void k_decode(const St* __restrict__ q, const 
     dtv = softplus_f(dt_proj[sh] + dt_bias[h]);
     alpha = expf(-expf(A_log[h]) * dtv);
   }
+  const int tq = tid < DH ? tid : 0;
+  const float lq = Elem<St>::ld(q, sh * DH + tq), lk = Elem<St>::ld(k, sh * DH + tq),
+              lv = Elem<St>::ld(v, sh * DH + tq);
   if (tid < DH) {
-    qs[tid] = Elem<St>::ld(q, sh * DH + tid);
-    ks[tid] = Elem<St>::ld(k, sh * DH + tid);
-    vs[tid] = Elem<St>::ld(v, sh * DH + tid) * dtv;
+    qs[tid] = lq;
+    ks[tid] = lk;
+    vs[tid] = lv * dtv;
   }
   __syncthreads();
   if constexpr (ORDER == 2) {
@@ -104,9 +104,9 @@ __global__ __launch_bounds__(NTH) void k_decode(const St* __restrict__ q, const 
   const float* fq = ORDER == 2 ? fqT : qs;
 
   const int cg = tid % CG, r0 = tid / CG;
+  float* Sp = state + sh * (int64_t)R * DH + 4 * cg;
   const f32x4 vd = {vs[4 * cg], vs[4 * cg + 1], vs[4 * cg + 2], vs[4 * cg + 3]};
   f32x4 acc = zero4();
-  float* Sp = state + sh * (int64_t)R * DH + 4 * cg;
   for (int rb = r0; rb < RMAIN; rb += STEP) {
     f32x4 s[U];
 #pragma unroll
@@ -120,10 +120,10 @@ __global__ __launch_bounds__(NTH) void k_decode(const St* __restrict__ q, const 
       acc += fq[rw] * ns;
     }
   }
-  if constexpr (RMAIN < R) {  // the packed layout's last rows
+  if constexpr (RMAIN < R) {  // the last rows when the passes do not tile the state
     for (int rw = RMAIN + r0; rw < R; rw += RPP) {
-      const f32x4 s = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sp + (int64_t)rw * DH));
-      const f32x4 ns = alpha * s + fk[rw] * vd;
+      const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(Sp + (int64_t)rw * DH));
+      const f32x4 ns = alpha * t + fk[rw] * vd;
       __builtin_nontemporal_store(ns, reinterpret_cast<f32x4*>(Sp + (int64_t)rw * DH));
       acc += fq[rw] * ns;
     }
@@ -167,10 +167,14 @@ hipError_t launch_decode(bool bf16, int64_t DH, int order, bool packed, const vo
                          const float* A_log, const float* A_proj, int64_t S, int64_t H,
                          float* state, float* norm_state, float* y, hipStream_t stream) {
   const dim3 grid((unsigned)(S * H));
-  // order-2 states stream with 1024-thread workgroups, order-1 with 256
+  // workgroup size x rows in flight per thread: order 2 full 1024 x 4 (71.7%
+  // of the HBM peak on the 256 x 32-head step), packed 512 x 8 (68.5%, against
+  // 66.9% at 1024 x 4), order 1 256 x 8
+#define DEC_NTH(ORD, PK) (ORD == 1 ? 256 : (PK ? 512 : 1024))
+#define DEC_ROWS(ORD, PK) (ORD == 1 ? 8 : (PK ? 8 : 4))
 #define SSD_LAUNCH_DEC(ST, DHV, ORD, PK)                                                         \
-  hipLaunchKernelGGL((k_decode<ST, DHV, ORD, ORD == 2 ? 1024 : 256, PK>), grid,                \
-                     dim3(ORD == 2 ? 1024 : 256), 0, stream, static_cast<const ST*>(q),         \
+  hipLaunchKernelGGL((k_decode<ST, DHV, ORD, DEC_NTH(ORD, PK), DEC_ROWS(ORD, PK), PK>), grid,   \
+                     dim3(DEC_NTH(ORD, PK)), 0, stream, static_cast<const ST*>(q),               \
                      static_cast<const ST*>(k), static_cast<const ST*>(v), dt_proj, dt_bias,   \
                      A_log, A_proj, H, state, norm_state, y)
 #define SSD_DEC_ORDERS(ST, DHV)                      \
@@ -192,6 +196,8 @@ hipError_t launch_decode(bool bf16, int64_t DH, int order, bool packed, const vo
   }
 #undef SSD_DEC_ORDERS
 #undef SSD_LAUNCH_DEC
+#undef DEC_ROWS
+#undef DEC_NTH
   return hipGetLastError();
 }
 

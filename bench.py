@@ -342,7 +342,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="o2_bf16_4k",
-                    choices=list(I.CONFIGS) + list(I.DECODE_CONFIGS) + ["o2_decode_packed"])
+                    choices=list(I.ALL_CONFIGS) + list(I.DECODE_CONFIGS) + ["o2_decode_packed"])
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (64K forward, decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -369,8 +369,8 @@ def main():
     from mamba_ssd_sequence_amd import ssd
     ssd.lib()
 
-    if a.workload in I.CONFIGS:
-        cfg = I.CONFIGS[a.workload]
+    if a.workload in I.ALL_CONFIGS:
+        cfg = I.ALL_CONFIGS[a.workload]
         res, inp = bench_forward(cfg, a.steps, a.warmup, dev)
     else:
         packed = a.workload.endswith("_packed")
@@ -381,14 +381,15 @@ def main():
 
     extra = []
     if not a.no_extra:
-        for name in ("o2_bf16_64k", "o1_bf16_2k", "o2_decode", "o2_decode_packed", "o2_bf16_4k_amask"):
+        for name in ("o2_bf16_64k", "o1_bf16_2k", "o1_bf16_4k", "o1_bf16_64k", "o2_decode",
+                     "o2_decode_packed", "o2_bf16_4k_amask"):
             if name == a.workload:
                 continue
             torch.cuda.empty_cache()
             if name == "o2_bf16_4k_amask":
                 r, _ = bench_forward(I.CONFIGS["o2_bf16_4k"], a.steps, a.warmup, dev, amask=True)
-            elif name in I.CONFIGS:
-                r, _ = bench_forward(I.CONFIGS[name], max(3, a.steps // 4), 2, dev)
+            elif name in I.ALL_CONFIGS:
+                r, _ = bench_forward(I.ALL_CONFIGS[name], max(3, a.steps // 4), 2, dev)
             elif name == "o2_decode_packed":
                 c = I.DECODE_CONFIGS["o2_decode"]
                 r, _ = bench_decode(c, c.steps, 3, dev, packed=True)
@@ -408,7 +409,7 @@ def main():
     cpu = None
     if not a.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
-        if a.workload in I.CONFIGS:
+        if a.workload in I.ALL_CONFIGS:
             cpu = cpu_baseline_forward(cfg, inp)
         else:
             cpu = cpu_baseline_decode(cfg, inp)

@@ -332,10 +332,11 @@ hipError_t launch_state_pass(int64_t DH, int64_t BH, int64_t N, const float* tb,
 // ---------------------------------------------------------------------------
 // k_output
 // ---------------------------------------------------------------------------
-// (order 2: registers capped for five waves per SIMD, which its 29 KB of LDS
-// allows; the order-1 variants are bound by LDS)
+// (registers capped for five waves per SIMD where the LDS allows five
+// workgroups per CU: order 2 (29 KB) and order 1 with bf16 inputs (28 KB);
+// the fp32 variants are bound by LDS)
 template <bool BF, int DH, int ORDER>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ORDER == 2 ? 5 : 1, 8))) void k_output(const void* __restrict__ qp,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF ? 5 : 1, 8))) void k_output(const void* __restrict__ qp,
                                                 const void* __restrict__ kp,
                                                 const void* __restrict__ vp,
                                                 const float* __restrict__ dt,
@@ -350,12 +351,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ORDER == 2 
   constexpr int PQ = DH + G::PAD;   // pitch of rows indexed by feature
   constexpr int PJ = BLK + G::PAD;  // pitch of rows indexed by token
   constexpr int NT = DH / 16;
+  // Order 1 with bf16 inputs (SPLIT): the entering state, in high and low
+  // bf16 parts, is staged first in the space that k and v take afterwards
+  // (the inter-block product runs in between), which keeps the workgroup at
+  // 28 KB of LDS; fp32 inputs stage it in an array of its own; order 2 reads
+  // its rows into registers.
+  constexpr bool SPLIT = ORDER == 1 && BF;
+  static_assert(!SPLIT || 2 * DH * PQ <= BLK * PQ + DH * PJ, "state fits the k / v space");
   __shared__ __attribute__((aligned(16))) C Qs[BLK * PQ];   // [i][d]
-  __shared__ __attribute__((aligned(16))) C Ks[BLK * PQ];   // [j][d]
-  __shared__ __attribute__((aligned(16))) C VT[DH * PJ];    // [c][j]  value operand, transposed
-  // order 1 only: the entering state (order 2 reads its rows into registers)
-  __shared__ __attribute__((aligned(16))) C SinT[ORDER == 1 ? DH * PQ : 1];  // [c][b] transposed
-  __shared__ __attribute__((aligned(16))) C SinL[ORDER == 1 && BF ? DH * PQ : 1];  // bf16: low part
+  __shared__ __attribute__((aligned(16))) C KV[BLK * PQ + DH * PJ];
+  __shared__ __attribute__((aligned(16))) C SinX[ORDER == 1 && !SPLIT ? DH * PQ : 1];
+  C* const Ks = KV;               // [j][d]
+  C* const VT = KV + BLK * PQ;    // [c][j]  value operand, transposed
+  C* const SinT = SPLIT ? KV : SinX;  // [c][b] the entering state, transposed (bf16: high part)
+  C* const SinL = KV + DH * PQ;   // [c][b] SPLIT: low part
   __shared__ float dred[ORDER == 2 ? 4 * BLK : 1];  // order 2: per-wave parts of q^T Z q
   __shared__ float zin[DH];
   __shared__ float csl[BLK];
@@ -504,18 +513,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ORDER == 2 
     csl[tid] = c_own;
     dtv[tid] = d_own;
   }
-  if constexpr (BF) {
+  // bf16: k rows and the value operand v dt, transposed (each LDS store
+  // carries a token pair)
+  auto stage_kv = [&]() {
+   if constexpr (BF) {
     {
       const int j = tid / SEG, sg = tid % SEG;
-      *reinterpret_cast<uint4*>(&Qs[j * PQ + sg * 8]) = gq0;
       *reinterpret_cast<uint4*>(&Ks[j * PQ + sg * 8]) = gk0;
     }
     if constexpr (NQ == 2) {
       const int j = (tid + 256) / SEG, sg = tid % SEG;
-      *reinterpret_cast<uint4*>(&Qs[j * PQ + sg * 8]) = gq1;
       *reinterpret_cast<uint4*>(&Ks[j * PQ + sg * 8]) = gk1;
     }
-    // value operand v dt, transposed: each LDS store carries the token pair
     if (tid < (BLK / 2) * SEG) {
       const int j0 = 2 * (tid / SEG), sg = tid % SEG;
       const uint32_t w0[4] = {gv0.x, gv0.y, gv0.z, gv0.w}, w1[4] = {gv1.x, gv1.y, gv1.z, gv1.w};
@@ -530,6 +539,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ORDER == 2 
         }
       }
     }
+   }
+  };
+  if constexpr (BF) {
+    {
+      const int j = tid / SEG, sg = tid % SEG;
+      *reinterpret_cast<uint4*>(&Qs[j * PQ + sg * 8]) = gq0;
+    }
+    if constexpr (NQ == 2) {
+      const int j = (tid + 256) / SEG, sg = tid % SEG;
+      *reinterpret_cast<uint4*>(&Qs[j * PQ + sg * 8]) = gq1;
+    }
+    if constexpr (!SPLIT) stage_kv();
   }
   if constexpr (ORDER == 1) {
 #pragma unroll
@@ -564,6 +585,34 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ORDER == 2 
   }
   __syncthreads();
   const float cs_i = csl[il];
+
+  // order 1: the inter-block product D[c][i] = sum_b S_in[b][c] Q[i][b], with
+  // the state in high + low bf16 parts (the factored sum over b can cancel
+  // when q is nearly orthogonal to the keys, so a single bf16 rounding of the
+  // state would be amplified), and the normaliser part q . z
+  f32x4 inter[NT];
+  float den_x = 0.f;
+  auto inter_product = [&]() {
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) {
+      f32x4 acc = zero4();
+#pragma unroll
+      for (int ks = 0; ks < DH / G::KS; ++ks) {
+        const auto b = G::ld(Qs, PQ, il, ks, g);
+        acc = G::mma(G::ld(SinT, PQ, ct * 16 + n, ks, g), b, acc);
+        if constexpr (BF) acc = G::mma(G::ld(SinL, PQ, ct * 16 + n, ks, g), b, acc);
+      }
+      inter[ct] = acc;
+    }
+    for (int b = g * (DH / 4); b < (g + 1) * (DH / 4); ++b) den_x += (float)Qs[il * PQ + b] * zin[b];
+    den_x = sum_over_groups(den_x);
+  };
+  if constexpr (SPLIT) {
+    inter_product();
+    __syncthreads();  // the state's space is free: stage k and v there
+    stage_kv();
+    __syncthreads();
+  }
 
   if constexpr (ORDER == 2) {
     // q^T Z q for all 64 rows over this wave's 16 rows b of Z': (Z' Q^T)[b][i]
@@ -740,30 +789,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(ORDER == 2 
    }
   }
 
-  // inter-block part.  Order 1: D[c][i] = sum_b S_in[b][c] Q[i][b] with
-  // the state in high + low bf16 parts (the factored sum over b can cancel
-  // when q is nearly orthogonal to the keys, so a single bf16 rounding of the
-  // state would be amplified) and the normaliser q . z.  Order 2: the
-  // numerators come from the state scan; q^T Z q from the per-wave parts.
+  // inter-block part, decayed from the block start.  Order 1: the product
+  // above.  Order 2: the numerators come from the state scan; q^T Z q from
+  // the per-wave parts.
   const float eci = exp2_fast(cs_i);
-  float den_x = 0.f;
   if constexpr (ORDER == 1) {
-    f32x4 inter[NT];
-#pragma unroll
-    for (int ct = 0; ct < NT; ++ct) {
-      f32x4 acc = zero4();
-#pragma unroll
-      for (int ks = 0; ks < DH / G::KS; ++ks) {
-        const auto b = G::ld(Qs, PQ, il, ks, g);
-        acc = G::mma(G::ld(SinT, PQ, ct * 16 + n, ks, g), b, acc);
-        if constexpr (BF) acc = G::mma(G::ld(SinL, PQ, ct * 16 + n, ks, g), b, acc);
-      }
-      inter[ct] = acc;
-    }
+    if constexpr (!SPLIT) inter_product();
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) num[ct] += eci * inter[ct];
-    for (int b = g * (DH / 4); b < (g + 1) * (DH / 4); ++b) den_x += (float)Qs[il * PQ + b] * zin[b];
-    den_x = sum_over_groups(den_x);
   } else {
     __syncthreads();  // every wave's part of q^T Z q is in dred
     den_x = (dred[il] + dred[BLK + il]) + (dred[2 * BLK + il] + dred[3 * BLK + il]);

@@ -123,6 +123,16 @@ CONFIGS = {
     "o2_bf16_64k": Config("o2_bf16_64k", B=1, H=16, N=65536, d_h=64, chunk=128, order=2, dtype=BF16,
                           qkv_scale=1.0 / math.sqrt(64)),
 }
+# Order 1 at the order-2 shapes (the metric names both orders at 4K and 64K):
+# supplementary, measured and parity-tested next to the five workloads.
+SUPPLEMENTARY = {
+    "o1_bf16_4k": Config("o1_bf16_4k", B=2, H=16, N=4096, d_h=64, chunk=64, order=1, dtype=BF16,
+                         qkv_scale=1.0 / math.sqrt(64)),
+    "o1_bf16_64k": Config("o1_bf16_64k", B=1, H=16, N=65536, d_h=64, chunk=128, order=1, dtype=BF16,
+                          qkv_scale=1.0 / math.sqrt(64)),
+}
+ALL_CONFIGS = {**CONFIGS, **SUPPLEMENTARY}
+
 DECODE_CONFIGS = {
     "o2_decode": DecodeConfig("o2_decode", S=256, H=32, d_h=64, order=2, steps=128),
 }

@@ -221,9 +221,10 @@ def test_deterministic():
 # ---------------------------------------------------------------------------
 
 @pytest.mark.parametrize("name,n_random", [("o1_f32_small", None), ("o1_bf16_2k", 48),
-                                            ("o2_bf16_4k", 48), ("o2_bf16_64k", 24)])
+                                            ("o2_bf16_4k", 48), ("o2_bf16_64k", 24),
+                                            ("o1_bf16_4k", 32), ("o1_bf16_64k", 16)])
 def test_forward_full_size(name, n_random):
-    cfg = I.CONFIGS[name]
+    cfg = I.ALL_CONFIGS[name]
     say("forward full", name)
     inp = I.make_forward_inputs(cfg)
     got = run_forward(inp, cfg.order, cfg.chunk, want_den=True)

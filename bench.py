@@ -67,10 +67,10 @@ def measured_traffic(kernel: str, workload: str):
     kernel's sources changed since the counters were taken."""
     try:
         with open(TRAFFIC_JSON) as f:
-            t = json.load(f).get(kernel)
+            t = json.load(f).get(f"{kernel}@{workload}")
     except (OSError, ValueError):
         return None
-    if not t or t.get("workload") != workload or t.get("source_sha256") != kernel_source_sha(kernel):
+    if not t or t.get("source_sha256") != kernel_source_sha(kernel):
         return None
     return t["traffic_bytes"]
 PEAK_BF16_TFLOPS = 2500.0

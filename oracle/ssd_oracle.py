@@ -23,6 +23,9 @@ Mongaras & Larson):
   features k (x) k and the two states H_up (numerator) and H_down (normaliser)
   decayed by a_t each step; as printed, a_t = exp(-softplus(h W_A)) (the
   A-mask), also provided next to the Mamba-2 discretisation.
+* The backward pass (the pages train these models but print no gradients):
+  the chain rule applied to the quadratic form and to Algorithm 3's
+  discretisation, written out step by step.
 * The symmetric-packed order-2 state (not on the pages; derived from the
   symmetry of k (x) k in Algorithm 6): only the rows (a, b) with a <= b are
   stored, and the query contraction counts the off-diagonal rows twice.
@@ -430,3 +433,87 @@ def decode_step_amask_packed_ref(state_p, norm_p, q, k, v, A_proj, dt_proj):
         vop = vop * dt[..., None]
     Sp, zp, y, den = recurrent_step_packed(state_p, norm_p, q, k, vop, a)
     return y, Sp, zp, den
+
+
+# ---------------------------------------------------------------------------
+# Backward pass (gradients of the forward definitions above; the pages train
+# these models, but print no backward pass: this is the chain rule applied to
+# the quadratic form and the Algorithm 3 discretisation, step by step)
+# ---------------------------------------------------------------------------
+
+def _head_backward(q, k, vop, a, order, dy):
+    """One head.  Forward: s = q k^T, W = s^p * D with D_ij = exp(cs_i - cs_j)
+    (j <= i), cs = cumsum(a); num = W vop, den = W 1, y = num / den.
+    Returns dq, dk, dvop, da for the upstream gradient dy."""
+    cs = np.cumsum(a)
+    s = q @ k.T
+    causal = np.tril(np.ones(s.shape, dtype=bool))
+    D = np.exp(np.where(causal, cs[:, None] - cs[None, :], -np.inf))
+    W = s ** order * D
+    num = W @ vop
+    den = W.sum(axis=1)
+    y = num / den[:, None]
+    # y = num / den
+    dnum = dy / den[:, None]
+    dden = -(dy * y).sum(axis=1) / den
+    # num = W vop, den = W 1
+    dW = (dnum @ vop.T + dden[:, None]) * causal
+    dvop = W.T @ dnum
+    # W = s^p D
+    ds = dW * D * order * s ** (order - 1)
+    dq = ds @ k
+    dk = ds.T @ q
+    # D_ij = exp(cs_i - cs_j): d/dcs_i = +W_ij, d/dcs_j = -W_ij
+    P = dW * W
+    dcs = P.sum(axis=1) - P.sum(axis=0)
+    # cs = cumsum(a): da_t = sum_{s >= t} dcs_s
+    da = np.cumsum(dcs[::-1])[::-1]
+    return dq, dk, dvop, da
+
+
+def backward_quadratic(q, k, vop, a, order, dy):
+    """Gradients of the masked quadratic form (forward_quadratic's y) with
+    respect to its operands, over [B,H,N,.] arrays, for upstream gradient dy
+    [B,H,N,d_v].  Returns dict dq, dk, dvop, da (da: per-token log-decay)."""
+    q, k, vop, a, dy = (np.asarray(x, dtype=np.float64) for x in (q, k, vop, a, dy))
+    B, H = q.shape[:2]
+    out = {"dq": np.empty_like(q), "dk": np.empty_like(k), "dvop": np.empty_like(vop), "da": np.empty_like(a)}
+    for b in range(B):
+        for h in range(H):
+            r = _head_backward(q[b, h], k[b, h], vop[b, h], a[b, h], order, dy[b, h])
+            for name, x in zip(("dq", "dk", "dvop", "da"), r):
+                out[name][b, h] = x
+    return out
+
+
+def prep_backward_ref(dt_proj, dt_bias, A_log, da, ddt):
+    """Chain rule through Algorithm 3's discretisation: a = A dt with A =
+    -exp(A_log), dt = softplus(dt_P + dt_bias).  da: gradient w.r.t. a
+    [B,H,N]; ddt: gradient w.r.t. dt from other uses (the value operand
+    v * dt), [B,H,N].  Returns d_dt_proj [B,H,N], d_dt_bias [H], d_A_log [H]."""
+    dt_proj = np.asarray(dt_proj, dtype=np.float64)
+    x = dt_proj + np.asarray(dt_bias, dtype=np.float64)[:, None]
+    A = -np.exp(np.asarray(A_log, dtype=np.float64))
+    dt = softplus(x)
+    da = np.asarray(da, dtype=np.float64)
+    g_dt = np.asarray(ddt, dtype=np.float64) + da * A[:, None]
+    sig = 1.0 / (1.0 + np.exp(-x))  # softplus' = logistic
+    d_dt_proj = g_dt * sig
+    d_dt_bias = d_dt_proj.sum(axis=(0, 2))
+    d_A_log = (da * dt).sum(axis=(0, 2)) * A  # dA/dA_log = A
+    return d_dt_proj, d_dt_bias, d_A_log
+
+
+def backward_ref(q, k, v, dt_proj, dt_bias, A_log, order, dy):
+    """End-to-end gradients of forward_ref's y: dq, dk, dv, and through the
+    discretisation d_dt_proj, d_dt_bias, d_A_log; also the intermediate
+    gradients da (w.r.t. a = A dt) and ddt_v (w.r.t. dt through V * dt)."""
+    dt, a = discretise(dt_proj, dt_bias, A_log)
+    v = np.asarray(v, dtype=np.float64)
+    vdt = v * dt[..., None]
+    g = backward_quadratic(q, k, vdt, a, order, dy)
+    dv = g["dvop"] * dt[..., None]
+    ddt_v = (g["dvop"] * v).sum(axis=-1)
+    d_dt_proj, d_dt_bias, d_A_log = prep_backward_ref(dt_proj, dt_bias, A_log, g["da"], ddt_v)
+    return {"dq": g["dq"], "dk": g["dk"], "dv": dv, "da": g["da"], "ddt_v": ddt_v,
+            "d_dt_proj": d_dt_proj, "d_dt_bias": d_dt_bias, "d_A_log": d_A_log}

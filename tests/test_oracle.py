@@ -532,3 +532,93 @@ def test_packed_decode_equals_full_decode(amask):
         want_s, want_z = O.pack_state(st, nz, d)
         np.testing.assert_allclose(sp, want_s, rtol=1e-12, atol=1e-14)
         np.testing.assert_allclose(zp, want_z, rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Backward pass: gradients of the forward definitions, pinned by central
+# finite differences, closed forms and invariances of the mathematics
+# ---------------------------------------------------------------------------
+
+def _loss(q, k, vop, a, order, dy):
+    return float((O.forward_quadratic(q, k, vop, a, order)["y"] * dy).sum())
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_backward_matches_finite_differences(order):
+    rng = np.random.default_rng(61)
+    q, k, v, a = rand_case(rng, 1, 2, 9, 3, signed=False)
+    q, k = q + 0.2, k + 0.2  # keep every normaliser well away from zero
+    dy = rng.standard_normal(v.shape)
+    g = O.backward_quadratic(q, k, v, a, order, dy)
+    h = 1e-6
+    for name, x in (("dq", q), ("dk", k), ("dvop", v), ("da", a)):
+        num = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args = {"dq": (xp, k, v, a), "dk": (q, xp, v, a), "dvop": (q, k, xp, a), "da": (q, k, v, xp)}
+            argm = {"dq": (xm, k, v, a), "dk": (q, xm, v, a), "dvop": (q, k, xm, a), "da": (q, k, v, xm)}
+            num[idx] = (_loss(*args[name], order, dy) - _loss(*argm[name], order, dy)) / (2 * h)
+        np.testing.assert_allclose(g[name], num, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_backward_end_to_end_matches_finite_differences(order):
+    rng = np.random.default_rng(62)
+    B, H, N, d = 1, 2, 7, 3
+    q = np.abs(rng.standard_normal((B, H, N, d))) + 0.2
+    k = np.abs(rng.standard_normal((B, H, N, d))) + 0.2
+    v = rng.standard_normal((B, H, N, d))
+    dt_proj = rng.standard_normal((B, H, N))
+    dt_bias = rng.standard_normal(H) - 1.0
+    A_log = np.log(rng.uniform(1, 4, H))
+    dy = rng.standard_normal((B, H, N, d))
+    g = O.backward_ref(q, k, v, dt_proj, dt_bias, A_log, order, dy)
+
+    def loss(v_, dtp_, bias_, alog_):
+        return float((O.forward_ref(q, k, v_, dtp_, bias_, alog_, order)["y"] * dy).sum())
+
+    h = 1e-6
+    for name, x, pos in (("dv", v, 0), ("d_dt_proj", dt_proj, 1), ("d_dt_bias", dt_bias, 2),
+                         ("d_A_log", A_log, 3)):
+        num = np.empty_like(x)
+        for idx in np.ndindex(x.shape):
+            xs = [v, dt_proj, dt_bias, A_log]
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            num[idx] = (loss(*(xp if i == pos else xs[i] for i in range(4)))
+                        - loss(*(xm if i == pos else xs[i] for i in range(4)))) / (2 * h)
+        np.testing.assert_allclose(g[name], num, rtol=1e-6, atol=1e-8, err_msg=name)
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_backward_single_token_closed_form(order):
+    # N = 1: y_0 = vop_0 exactly, so dvop = dy and nothing else has a gradient
+    rng = np.random.default_rng(63)
+    q, k, v, a = rand_case(rng, 1, 1, 1, 4)
+    dy = rng.standard_normal(v.shape)
+    g = O.backward_quadratic(q, k, v, a, order, dy)
+    np.testing.assert_allclose(g["dvop"], dy, rtol=1e-14)
+    for name in ("dq", "dk", "da"):
+        assert np.abs(g[name]).max() <= 1e-14 * (1 + np.abs(dy).max())
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_backward_invariances(order):
+    """Consequences of the definition, exact for any input:
+    - y_i is homogeneous of degree 0 in q_i, so sum_c q_ic dq_ic = 0 per row;
+    - y is homogeneous of degree 0 in k (all rows), so sum k . dk = 0;
+    - a_0 shifts every cumsum equally and cancels in every difference: da_0 = 0;
+    - a constant added to every value operand row adds it to every y_i, so
+      sum_j dvop_j = sum_i dy_i."""
+    rng = np.random.default_rng(64)
+    q, k, v, a = rand_case(rng, 1, 2, 40, 5, signed=False)
+    dy = rng.standard_normal(v.shape)
+    g = O.backward_quadratic(q, k, v, a, order, dy)
+    scale = np.abs(g["dq"]).max() * np.abs(q).max()
+    assert np.abs((q * g["dq"]).sum(axis=-1)).max() <= 1e-10 * scale
+    assert abs((k * g["dk"]).sum()) <= 1e-10 * np.abs(k * g["dk"]).sum()
+    assert np.abs(g["da"][..., 0]).max() <= 1e-10 * np.abs(g["da"]).max()
+    np.testing.assert_allclose(g["dvop"].sum(axis=2), dy.sum(axis=2), rtol=1e-10)

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 4
+#define SSD_ABI_VERSION 5
 
 typedef enum {
   SSD_OK = 0,
@@ -251,6 +251,63 @@ ssd_status ssd_state_pack(const float* state, const float* norm_state, int64_t B
                           float* state_p, float* norm_p, hipStream_t stream);
 ssd_status ssd_state_unpack(const float* state_p, const float* norm_p, int64_t BH, int64_t d_h,
                             float* state, float* norm_state, hipStream_t stream);
+
+/*
+ * ssd_backward -- gradients of ssd_forward's y (order 1), for training.
+ * The pages train these models but print no backward pass: this is the chain
+ * rule through the same definitions (Algorithm 1's masked product and row-sum
+ * normaliser, Algorithm 4's decay mask), on the same 64-token blocks: the
+ * states entering each block are recomputed, the gradient of the state
+ * leaving each block is scanned in reverse, and each block then forms its
+ * gradients from its own tokens and those two states.  All arithmetic is
+ * fp32.
+ *
+ *   q, k, v, dt, a_cs, B..dtype   exactly as given to ssd_forward (dt may be NULL)
+ *   y, den    [B,H,N,d_h], [B,H,N] f32   ssd_forward's outputs (den is required)
+ *   dy        [B,H,N,d_h] f32            gradient of the loss with respect to y
+ *   dq, dk, dv [B,H,N,d_h] f32   out: gradients with respect to q, k, v
+ *   ddt       [B,H,N] f32        out: gradient with respect to dt through the
+ *                                value operand v dt (sum_c dL/d(v dt)_c v_c);
+ *                                NULL iff dt is NULL
+ *   da        [B,H,N] f32        out: gradient with respect to the per-token
+ *                                log-decay a (A dt, or the A-mask's
+ *                                -softplus(A_P)) whose chunk-local cumsum is a_cs
+ *   workspace  >= ssd_backward_workspace_size bytes
+ *
+ * order must be 1 (SSD_ERR_UNSUPPORTED otherwise); d_h 32 or 64; fp32 or
+ * bf16 inputs; no initial state.  Feed (da, ddt) to ssd_prep_backward or
+ * ssd_prep_amask_backward for the parameter gradients.
+ */
+size_t ssd_backward_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d_h, int order,
+                                   int64_t chunk, int dtype);
+ssd_status ssd_backward(const void* q, const void* k, const void* v, const float* dt,
+                        const float* a_cs, const float* y, const float* den, const float* dy,
+                        int64_t B, int64_t H, int64_t N, int64_t d_h, int order, int64_t chunk,
+                        int dtype, float* dq, float* dk, float* dv, float* ddt, float* da,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * ssd_prep_backward -- chain rule through Algorithm 3's discretisation
+ * (a = A dt, A = -exp(A_log), dt = softplus(dt_P + dt_bias)):
+ *   d_dt_proj = (ddt + da A) sigmoid(dt_P + dt_bias)      [B,H,N]
+ *   d_dt_bias[h] = sum over b, n of d_dt_proj              [H]
+ *   d_A_log[h] = A_h sum over b, n of da dt                [H]
+ * ddt may be NULL (no value-operand use of dt).  The per-head sums are
+ * taken in a fixed order (deterministic).
+ */
+ssd_status ssd_prep_backward(const float* dt_proj, const float* dt_bias, const float* A_log,
+                             const float* da, const float* ddt, int64_t B, int64_t H, int64_t N,
+                             float* d_dt_proj, float* d_dt_bias, float* d_A_log, hipStream_t stream);
+
+/*
+ * ssd_prep_amask_backward -- chain rule through the A-mask of Algorithms 4
+ * and 5 (a = -softplus(A_P); dt = softplus(dt_P)):
+ *   d_A_proj = -da sigmoid(A_P);  d_dt_proj = ddt sigmoid(dt_P)
+ * dt_proj, ddt and d_dt_proj are all given or all NULL.
+ */
+ssd_status ssd_prep_amask_backward(const float* A_proj, const float* dt_proj, const float* da,
+                                   const float* ddt, int64_t B, int64_t H, int64_t N,
+                                   float* d_A_proj, float* d_dt_proj, hipStream_t stream);
 
 #ifdef __cplusplus
 }

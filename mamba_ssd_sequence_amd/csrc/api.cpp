@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include "bwd.h"
 #include "launch.h"
 
 namespace {
@@ -437,6 +438,117 @@ ssd_status ssd_state_unpack(const float* state_p, const float* norm_p, int64_t B
     return state_layout("ssd_state_unpack", false, state_p, norm_p, BH, d_h, state, norm_state, stream);
   } catch (...) {
     return fail(SSD_ERR_HIP, "ssd_state_unpack: unexpected exception");
+  }
+}
+
+size_t ssd_backward_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d_h, int order,
+                                   int64_t chunk, int dtype) {
+  int64_t BH, BHN, BHNd;
+  if (validate_forward_sizes(B, H, N, d_h, order, chunk, dtype, &BH, &BHN, &BHNd) != SSD_OK) return 0;
+  if (order != 1 || BHN == 0) return 0;
+  return ssd::bwd_layout(BH, N, d_h).total_floats * sizeof(float);
+}
+
+ssd_status ssd_backward(const void* q, const void* k, const void* v, const float* dt,
+                        const float* a_cs, const float* y, const float* den, const float* dy,
+                        int64_t B, int64_t H, int64_t N, int64_t d_h, int order, int64_t chunk,
+                        int dtype, float* dq, float* dk, float* dv, float* ddt, float* da,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  try {
+    clear_err();
+    int64_t BH, BHN, BHNd;
+    ssd_status s = validate_forward_sizes(B, H, N, d_h, order, chunk, dtype, &BH, &BHN, &BHNd);
+    if (s != SSD_OK) return s;
+    if (order != 1)
+      return fail(SSD_ERR_UNSUPPORTED, "ssd_backward: order %d (this build has the order-1 backward)", order);
+    if (BHN == 0) return SSD_OK;  // nothing to differentiate
+    if (!q || !k || !v || !a_cs || !y || !den || !dy || !dq || !dk || !dv || !da)
+      return fail(SSD_ERR_NULL, "ssd_backward: a required pointer is NULL");
+    if ((dt == nullptr) != (ddt == nullptr))
+      return fail(SSD_ERR_NULL, "ssd_backward: dt and ddt must be given together");
+    const size_t need = ssd::bwd_layout(BH, N, d_h).total_floats * sizeof(float);
+    if (workspace_bytes < need || !workspace)
+      return fail(SSD_ERR_WORKSPACE, "ssd_backward: workspace of %zu bytes needed, %zu given", need,
+                  workspace ? workspace_bytes : (size_t)0);
+    const size_t es = dtype == SSD_BF16 ? 2 : 4;
+    const Range ins[] = {{"q", q, (size_t)BHNd * es},  {"k", k, (size_t)BHNd * es},
+                         {"v", v, (size_t)BHNd * es},  {"dt", dt, (size_t)BHN * 4},
+                         {"a_cs", a_cs, (size_t)BHN * 4}, {"y", y, (size_t)BHNd * 4},
+                         {"den", den, (size_t)BHN * 4}, {"dy", dy, (size_t)BHNd * 4}};
+    const Range outs[] = {{"dq", dq, (size_t)BHNd * 4}, {"dk", dk, (size_t)BHNd * 4},
+                          {"dv", dv, (size_t)BHNd * 4}, {"ddt", ddt, (size_t)BHN * 4},
+                          {"da", da, (size_t)BHN * 4},  {"workspace", workspace, need}};
+    if ((s = check_aligned(ins, 8)) != SSD_OK || (s = check_aligned(outs, 6)) != SSD_OK) return s;
+    if ((s = check_alias(outs, 6, ins, 8)) != SSD_OK) return s;
+    return hip_status(ssd::launch_backward_o1(dtype == SSD_BF16, d_h, q, k, v, dt, a_cs, y, den, dy, BH, N,
+                                              chunk, dq, dk, dv, ddt, da, static_cast<float*>(workspace),
+                                              stream),
+                      "backward launch");
+  } catch (...) {
+    return fail(SSD_ERR_HIP, "ssd_backward: unexpected exception");
+  }
+}
+
+// shared size validation of the two discretisation backward calls
+static ssd_status prep_bwd_sizes(const char* fn, int64_t B, int64_t H, int64_t N, int64_t* BHN) {
+  int64_t BH;
+  if (!mul_ok(B, H, &BH) || !mul_ok(BH, N, BHN))
+    return fail(SSD_ERR_SHAPE, "%s: B, H, N must be >= 0 and must not overflow", fn);
+  if (H > (int64_t)0x7fffffff) return fail(SSD_ERR_SHAPE, "%s: H too large", fn);
+  return SSD_OK;
+}
+
+ssd_status ssd_prep_backward(const float* dt_proj, const float* dt_bias, const float* A_log,
+                             const float* da, const float* ddt, int64_t B, int64_t H, int64_t N,
+                             float* d_dt_proj, float* d_dt_bias, float* d_A_log, hipStream_t stream) {
+  try {
+    clear_err();
+    int64_t BHN;
+    ssd_status s = prep_bwd_sizes("ssd_prep_backward", B, H, N, &BHN);
+    if (s != SSD_OK) return s;
+    if (H == 0) return SSD_OK;
+    if (!dt_bias || !A_log || !d_dt_bias || !d_A_log || (BHN && (!dt_proj || !da || !d_dt_proj)))
+      return fail(SSD_ERR_NULL, "ssd_prep_backward: a required pointer is NULL");
+    const Range ins[] = {{"dt_proj", dt_proj, (size_t)BHN * 4}, {"dt_bias", dt_bias, (size_t)H * 4},
+                         {"A_log", A_log, (size_t)H * 4},       {"da", da, (size_t)BHN * 4},
+                         {"ddt", ddt, (size_t)BHN * 4}};
+    const Range outs[] = {{"d_dt_proj", d_dt_proj, (size_t)BHN * 4},
+                          {"d_dt_bias", d_dt_bias, (size_t)H * 4},
+                          {"d_A_log", d_A_log, (size_t)H * 4}};
+    if ((s = check_aligned(ins, 5)) != SSD_OK || (s = check_aligned(outs, 3)) != SSD_OK) return s;
+    if ((s = check_alias(outs, 3, ins, 5)) != SSD_OK) return s;
+    return hip_status(ssd::launch_prep_backward(dt_proj, dt_bias, A_log, da, ddt, B, H, N, d_dt_proj,
+                                                d_dt_bias, d_A_log, stream),
+                      "prep backward launch");
+  } catch (...) {
+    return fail(SSD_ERR_HIP, "ssd_prep_backward: unexpected exception");
+  }
+}
+
+ssd_status ssd_prep_amask_backward(const float* A_proj, const float* dt_proj, const float* da,
+                                   const float* ddt, int64_t B, int64_t H, int64_t N,
+                                   float* d_A_proj, float* d_dt_proj, hipStream_t stream) {
+  try {
+    clear_err();
+    int64_t BHN;
+    ssd_status s = prep_bwd_sizes("ssd_prep_amask_backward", B, H, N, &BHN);
+    if (s != SSD_OK) return s;
+    if (BHN == 0) return SSD_OK;
+    if (!A_proj || !da || !d_A_proj)
+      return fail(SSD_ERR_NULL, "ssd_prep_amask_backward: a required pointer is NULL");
+    if ((dt_proj == nullptr) != (ddt == nullptr) || (dt_proj == nullptr) != (d_dt_proj == nullptr))
+      return fail(SSD_ERR_NULL, "ssd_prep_amask_backward: dt_proj, ddt and d_dt_proj go together");
+    const Range ins[] = {{"A_proj", A_proj, (size_t)BHN * 4}, {"dt_proj", dt_proj, (size_t)BHN * 4},
+                         {"da", da, (size_t)BHN * 4},         {"ddt", ddt, (size_t)BHN * 4}};
+    const Range outs[] = {{"d_A_proj", d_A_proj, (size_t)BHN * 4},
+                          {"d_dt_proj", d_dt_proj, (size_t)BHN * 4}};
+    if ((s = check_aligned(ins, 4)) != SSD_OK || (s = check_aligned(outs, 2)) != SSD_OK) return s;
+    if ((s = check_alias(outs, 2, ins, 4)) != SSD_OK) return s;
+    return hip_status(ssd::launch_prep_amask_backward(A_proj, dt_proj, da, ddt, B, H, N, d_A_proj,
+                                                      d_dt_proj, stream),
+                      "prep amask backward launch");
+  } catch (...) {
+    return fail(SSD_ERR_HIP, "ssd_prep_amask_backward: unexpected exception");
   }
 }
 

@@ -1,0 +1,65 @@
+// Internal launchers and workspace layout of the backward pass (bwd.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "launch.h"
+
+namespace ssd {
+
+// Backward workspace (float offsets), blocks of 64 tokens, E = d_h^2 + d_h:
+//   tb   [BH, nblk]          block decay totals
+//   sst  [BH, nblk, E]       forward increments, then (in place) the state
+//                            entering each block, S_c and z_c (recomputed)
+//   gst  [BH, nblk, E]       R_c, r_c, then (in place) the gradient of the
+//                            state leaving each block, G_{c+1} and g_{c+1}
+//   dnum [BH, nblk, 64, d_h] dy / den;  dden [BH, nblk, 64]
+//   w, c [BH, nblk, 64, 64]  the block's W_ij and C_ij = dW_ij e^{cs_i - cs_j}
+//   rowp, colp [BH, nblk, 64] the row and column parts of dcs
+struct BwdLayout {
+  size_t tb, sst, gst, dnum, dden, w, c, rowp, colp, total_floats;
+};
+
+inline BwdLayout bwd_layout(int64_t BH, int64_t N, int64_t DH) {
+  const size_t nbk = (size_t)(BH * n_blocks(N));
+  auto up = [](size_t x) { return (x + 63) & ~(size_t)63; };
+  BwdLayout L;
+  size_t off = 0;
+  L.tb = off;   off = up(off + nbk);
+  L.sst = off;  off = up(off + nbk * (size_t)(DH * DH + DH));
+  L.gst = off;  off = up(off + nbk * (size_t)(DH * DH + DH));
+  L.dnum = off; off = up(off + nbk * 64 * (size_t)DH);
+  L.dden = off; off = up(off + nbk * 64);
+  L.w = off;    off = up(off + nbk * 64 * 64);
+  L.c = off;    off = up(off + nbk * 64 * 64);
+  L.rowp = off; off = up(off + nbk * 64);
+  L.colp = off; off = up(off + nbk * 64);
+  L.total_floats = off;
+  return L;
+}
+
+// Order-1 backward: gradients with respect to q, k, v, dt (through the value
+// operand v dt) and the per-token log-decay a.  dt may be NULL (v is the
+// value operand; ddt is then NULL too).
+hipError_t launch_backward_o1(bool bf16, int64_t DH, const void* q, const void* k, const void* v,
+                              const float* dt, const float* a_cs, const float* y, const float* den,
+                              const float* dy, int64_t BH, int64_t N, int64_t chunk, float* dq,
+                              float* dk, float* dv, float* ddt, float* da, float* ws,
+                              hipStream_t stream);
+
+// Chain rule through Algorithm 3's discretisation (per-head sums in d_dt_bias
+// and d_A_log); ddt may be NULL (no value-operand gradient).
+hipError_t launch_prep_backward(const float* dt_proj, const float* dt_bias, const float* A_log,
+                                const float* da, const float* ddt, int64_t B, int64_t H, int64_t N,
+                                float* d_dt_proj, float* d_dt_bias, float* d_A_log,
+                                hipStream_t stream);
+
+// Chain rule through the A-mask: d_A_proj from da; d_dt_proj from ddt when
+// dt_proj is given.
+hipError_t launch_prep_amask_backward(const float* A_proj, const float* dt_proj, const float* da,
+                                      const float* ddt, int64_t B, int64_t H, int64_t N,
+                                      float* d_A_proj, float* d_dt_proj, hipStream_t stream);
+
+}  // namespace ssd

@@ -68,6 +68,15 @@ def _declare(lib):
     lib.ssd_state_pack.argtypes = [fp, fp, i64, i64, fp, fp, vp]
     lib.ssd_state_unpack.restype = ctypes.c_int
     lib.ssd_state_unpack.argtypes = [fp, fp, i64, i64, fp, fp, vp]
+    lib.ssd_backward_workspace_size.restype = sz
+    lib.ssd_backward_workspace_size.argtypes = [i64, i64, i64, i64, i32, i64, i32]
+    lib.ssd_backward.restype = ctypes.c_int
+    lib.ssd_backward.argtypes = [vp, vp, vp, fp, fp, fp, fp, fp, i64, i64, i64, i64, i32, i64, i32,
+                                 fp, fp, fp, fp, fp, vp, sz, vp]
+    lib.ssd_prep_backward.restype = ctypes.c_int
+    lib.ssd_prep_backward.argtypes = [fp, fp, fp, fp, fp, i64, i64, i64, fp, fp, fp, vp]
+    lib.ssd_prep_amask_backward.restype = ctypes.c_int
+    lib.ssd_prep_amask_backward.argtypes = [fp, fp, fp, fp, i64, i64, i64, fp, fp, vp]
     return lib
 
 
@@ -312,3 +321,66 @@ def state_pack(state, norm_state, out=None):
 def state_unpack(state_p, norm_p, out=None):
     """ssd_state_unpack: packed order-2 states -> the full layout."""
     return _state_layout(lib().ssd_state_unpack, state_p, norm_p, False, out)
+
+
+def backward(q, k, v, dt, a_cs, y, den, dy, order: int, chunk: int, *, workspace=None):
+    """ssd_backward: returns dq, dk, dv, ddt (None when dt is None), da."""
+    torch = _torch()
+    _require(q, "q")
+    dev = q.device
+    dtype = _qkv_dtype(q)
+    for name, t in (("k", k), ("v", v)):
+        _require(t, name, q.dtype, dev)
+    B, H, N, d_h = q.shape
+    for name, t in (("a_cs", a_cs), ("y", y), ("den", den), ("dy", dy)) + ((("dt", dt),) if dt is not None else ()):
+        _require(t, name, torch.float32, dev)
+    dq, dk, dv = (torch.empty((B, H, N, d_h), dtype=torch.float32, device=dev) for _ in range(3))
+    da = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    ddt = torch.empty((B, H, N), dtype=torch.float32, device=dev) if dt is not None else None
+    need = lib().ssd_backward_workspace_size(B, H, N, d_h, order, chunk, dtype)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wptr = _ptr(workspace) if workspace is not None else None
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    opt = lambda t: _ptr(t) if t is not None else None
+    _check(lib().ssd_backward(_ptr(q), _ptr(k), _ptr(v), opt(dt), _ptr(a_cs), _ptr(y), _ptr(den), _ptr(dy),
+                              B, H, N, d_h, order, chunk, dtype, _ptr(dq), _ptr(dk), _ptr(dv), opt(ddt),
+                              _ptr(da), wptr, wbytes, _stream(dev)))
+    return dq, dk, dv, ddt, da
+
+
+def prep_backward(dt_proj, dt_bias, A_log, da, ddt=None):
+    """ssd_prep_backward: returns d_dt_proj [B,H,N], d_dt_bias [H], d_A_log [H]."""
+    torch = _torch()
+    _require(dt_proj, "dt_proj", torch.float32)
+    dev = dt_proj.device
+    for name, t in (("dt_bias", dt_bias), ("A_log", A_log), ("da", da)) + ((("ddt", ddt),) if ddt is not None else ()):
+        _require(t, name, torch.float32, dev)
+    B, H, N = dt_proj.shape
+    d_dt_proj = torch.empty_like(dt_proj)
+    d_bias = torch.empty((H,), dtype=torch.float32, device=dev)
+    d_alog = torch.empty((H,), dtype=torch.float32, device=dev)
+    _check(lib().ssd_prep_backward(_ptr(dt_proj), _ptr(dt_bias), _ptr(A_log), _ptr(da),
+                                   _ptr(ddt) if ddt is not None else None, B, H, N, _ptr(d_dt_proj),
+                                   _ptr(d_bias), _ptr(d_alog), _stream(dev)))
+    return d_dt_proj, d_bias, d_alog
+
+
+def prep_amask_backward(A_proj, dt_proj, da, ddt=None):
+    """ssd_prep_amask_backward: returns d_A_proj and d_dt_proj (None without dt_proj)."""
+    torch = _torch()
+    _require(A_proj, "A_proj", torch.float32)
+    dev = A_proj.device
+    _require(da, "da", torch.float32, dev)
+    if (dt_proj is None) != (ddt is None):
+        raise ValueError("dt_proj and ddt go together")
+    if dt_proj is not None:
+        _require(dt_proj, "dt_proj", torch.float32, dev)
+        _require(ddt, "ddt", torch.float32, dev)
+    B, H, N = A_proj.shape
+    d_A = torch.empty_like(A_proj)
+    d_dt = torch.empty_like(A_proj) if dt_proj is not None else None
+    opt = lambda t: _ptr(t) if t is not None else None
+    _check(lib().ssd_prep_amask_backward(_ptr(A_proj), opt(dt_proj), _ptr(da), opt(ddt), B, H, N,
+                                         _ptr(d_A), opt(d_dt), _stream(dev)))
+    return d_A, d_dt

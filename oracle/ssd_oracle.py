@@ -471,6 +471,52 @@ def _head_backward(q, k, vop, a, order, dy):
     return dq, dk, dvop, da
 
 
+def _head_backward_scale(q, k, vop, a, order, dy):
+    """Per-element first-order rounding bounds of the gradients of one head,
+    divided by the unit roundoff: every gradient is a sum of products, and a
+    floating-point evaluation with relative accuracy eps in each of its terms
+    is off by at most about eps times the sum of the terms' absolute values
+    (with dnum and dden taken at their own bounds).
+    Returns the scales of dq, dk, dvop, da (the parity metric of the backward
+    tests, as the forward's `scale`)."""
+    cs = np.cumsum(a)
+    s = q @ k.T
+    causal = np.tril(np.ones(s.shape, dtype=bool))
+    D = np.exp(np.where(causal, cs[:, None] - cs[None, :], -np.inf))
+    W = s ** order * D
+    num = W @ vop
+    den = W.sum(axis=1)
+    y = num / den[:, None]
+    # dnum = dy / den and dden = -dy . y / den inherit the rounding of the
+    # normaliser and of y, amplified by the normaliser's condition kappa =
+    # sum|W| / |den| (the forward's error scale of y covers the latter)
+    aW = np.abs(W)
+    kappa = aW.sum(axis=1) / np.abs(den)
+    yscale = (aW @ np.abs(vop) + np.abs(y) * aW.sum(axis=1)[:, None]) / np.abs(den)[:, None]
+    amp = (1.0 + kappa)[:, None]
+    adn = np.abs(dy) / np.abs(den)[:, None] * amp
+    add = (np.abs(dy) * (np.abs(y) + yscale)).sum(axis=1) / np.abs(den) * amp[:, 0]
+    adW = (adn @ np.abs(vop).T + add[:, None]) * causal
+    ads = adW * D * order * np.abs(s) ** (order - 1)
+    aP = adW * aW
+    dcs = aP.sum(axis=1) + aP.sum(axis=0)
+    return ads @ np.abs(k), ads.T @ np.abs(q), aW.T @ adn, np.cumsum(dcs[::-1])[::-1]
+
+
+def backward_error_scale(q, k, vop, a, order, dy):
+    """backward_quadratic's per-element error scales over [B,H,N,.] arrays:
+    dict dq, dk, dvop, da (see _head_backward_scale)."""
+    q, k, vop, a, dy = (np.asarray(x, dtype=np.float64) for x in (q, k, vop, a, dy))
+    B, H = q.shape[:2]
+    out = {"dq": np.empty_like(q), "dk": np.empty_like(k), "dvop": np.empty_like(vop), "da": np.empty_like(a)}
+    for b in range(B):
+        for h in range(H):
+            r = _head_backward_scale(q[b, h], k[b, h], vop[b, h], a[b, h], order, dy[b, h])
+            for name, x in zip(("dq", "dk", "dvop", "da"), r):
+                out[name][b, h] = x
+    return out
+
+
 def backward_quadratic(q, k, vop, a, order, dy):
     """Gradients of the masked quadratic form (forward_quadratic's y) with
     respect to its operands, over [B,H,N,.] arrays, for upstream gradient dy
@@ -502,6 +548,18 @@ def prep_backward_ref(dt_proj, dt_bias, A_log, da, ddt):
     d_dt_bias = d_dt_proj.sum(axis=(0, 2))
     d_A_log = (da * dt).sum(axis=(0, 2)) * A  # dA/dA_log = A
     return d_dt_proj, d_dt_bias, d_A_log
+
+
+def prep_amask_backward_ref(A_proj, dt_proj, da, ddt):
+    """Chain rule through the A-mask of Algorithms 4 and 5: a = -softplus(A_P),
+    dt = softplus(dt_P).  Returns d_A_proj and d_dt_proj (None without
+    dt_proj)."""
+    A_proj = np.asarray(A_proj, dtype=np.float64)
+    d_A = -np.asarray(da, dtype=np.float64) / (1.0 + np.exp(-A_proj))
+    if dt_proj is None:
+        return d_A, None
+    dt_proj = np.asarray(dt_proj, dtype=np.float64)
+    return d_A, np.asarray(ddt, dtype=np.float64) / (1.0 + np.exp(-dt_proj))
 
 
 def backward_ref(q, k, v, dt_proj, dt_bias, A_log, order, dy):

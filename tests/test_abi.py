@@ -19,14 +19,15 @@ def test_exports_every_header_function(lib):
     names = ssd.header_functions()
     assert set(names) >= {"ssd_prep", "ssd_prep_amask", "ssd_forward", "ssd_forward_workspace_size",
                           "ssd_decode_step", "ssd_decode_step_amask", "ssd_state_pack",
-                          "ssd_state_unpack",
+                          "ssd_state_unpack", "ssd_backward", "ssd_backward_workspace_size",
+                          "ssd_prep_backward", "ssd_prep_amask_backward",
                           "ssd_abi_version", "ssd_status_str", "ssd_last_error"}
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssd_abi_version() == 4
+    assert lib.ssd_abi_version() == 5
     for i, name in enumerate(ssd.STATUS):
         assert lib.ssd_status_str(i).decode() == name
     assert lib.ssd_status_str(99).decode() == "SSD_ERR_UNKNOWN"
@@ -182,3 +183,34 @@ def test_empty_inputs_are_valid_no_ops(lib):
                                None, None, None, None) == 0
     assert lib.ssd_decode_step_amask(None, None, None, None, None, 3, 0, 64, 2, 1, 1,
                                      None, None, None, None) == 0
+
+
+def bwd(lib, *, order=1, d_h=64, dt=A[3], ddt=A[12], dq=A[9], ws=A[15], wsb=1 << 40, N=100):
+    return lib.ssd_backward(A[0], A[1], A[2], dt, A[4], A[5], A[6], A[7], 1, 2, N, d_h, order, 64, 1,
+                            dq, A[10], A[11], ddt, A[13], ws, wsb, None)
+
+
+def test_backward_errors(lib):
+    assert bwd(lib, order=2) == 3                       # order-1 backward only
+    assert bwd(lib, d_h=48) == 3
+    assert bwd(lib, dq=None) == 1
+    assert bwd(lib, ddt=None) == 1                      # dt given without ddt
+    assert bwd(lib, dt=None) == 1                       # ddt given without dt
+    assert bwd(lib, ws=None, wsb=0) == 6
+    assert bwd(lib, wsb=16) == 6
+    assert bwd(lib, dq=A[9] + 4) == 4
+    assert bwd(lib, dq=A[0]) == 5                       # dq over q
+    assert bwd(lib, N=0) == 0                           # empty: nothing to do
+    need = lib.ssd_backward_workspace_size(1, 2, 100, 64, 1, 64, 1)
+    assert need >= 4 * 2 * 2 * (64 * 64 + 64)
+    assert lib.ssd_backward_workspace_size(1, 2, 100, 64, 2, 64, 1) == 0
+
+
+def test_prep_backward_errors(lib):
+    assert lib.ssd_prep_backward(A[0], None, A[2], A[3], A[4], 1, 2, 10, A[5], A[6], A[7], None) == 1
+    assert lib.ssd_prep_backward(A[0], A[1], A[2], A[3], A[4], -1, 2, 10, A[5], A[6], A[7], None) == 2
+    assert lib.ssd_prep_backward(A[0], A[1], A[2], A[3], A[4], 1, 2, 10, A[0], A[6], A[7], None) == 5
+    assert lib.ssd_prep_amask_backward(A[0], A[1], A[2], None, 1, 2, 10, A[5], A[6], None) == 1
+    assert lib.ssd_prep_amask_backward(None, None, A[2], None, 1, 2, 10, A[5], None, None) == 1
+    assert lib.ssd_prep_amask_backward(A[0], None, A[2], None, 1, 2, 10, A[2], None, None) == 5
+    assert lib.ssd_prep_amask_backward(None, None, None, None, 1, 2, 0, None, None, None) == 0

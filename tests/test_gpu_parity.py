@@ -677,3 +677,167 @@ def test_constant_value_gives_the_value():
     err = np.abs(got["y"] - expect).max() / np.abs(expect).max()
     say("  err", err)
     assert err <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# backward (order 1): the GPU gradients against the oracle's, with the
+# oracle's y and den as the saved forward outputs (so that only the backward
+# is measured)
+# ---------------------------------------------------------------------------
+
+def run_backward(q, k, v, dt, a_cs, y, den, dy, chunk):
+    ssd = ssd_mod()
+    out = ssd.backward(q, k, v, dt, a_cs, y, den, dy, 1, chunk)
+    torch.cuda.synchronize()
+    return [None if x is None else x.cpu().numpy() for x in out]
+
+
+def backward_case(cfg, B, H, N, seed, positive, with_dt, chunk):
+    """Inputs of the workload's generator (positive: |x| + 0.05 for q and k,
+    normalisers bounded away from 0), the oracle's forward and backward, and
+    the GPU backward on the same values."""
+    inp = I.make_forward_inputs(cfg, B=B, H=H, N=N, seed=seed)
+    qf, kf, vf = inp.qkv_f64()
+    if positive:
+        qf, kf = np.abs(qf) + 0.05, np.abs(kf) + 0.05
+        store = lambda x: I._store(x, cfg.dtype)
+        qs, ks = store(qf), store(kf)
+        up = I.bf16_bits_to_f64 if cfg.dtype == I.BF16 else (lambda x: x.astype(np.float64))
+        qf, kf = up(qs), up(ks)
+    else:
+        qs, ks = inp.q, inp.k
+    dt, a = O.discretise(inp.dt_proj, inp.dt_bias, inp.A_log)
+    vop = vf * dt[..., None] if with_dt else vf
+    ref_f = O.forward_quadratic(qf, kf, vop, a, 1)
+    dy = np.random.default_rng(seed + 1).standard_normal(vf.shape)
+    dy = dy.astype(np.float32).astype(np.float64)
+    ref = O.backward_quadratic(qf, kf, vop, a, 1, dy)
+    ssd = ssd_mod()
+    dt_d, a_cs, _ = ssd.prep(to_dev_f32(inp.dt_proj), to_dev_f32(inp.dt_bias), to_dev_f32(inp.A_log), chunk)
+    got = run_backward(to_dev_qkv(qs, cfg.dtype), to_dev_qkv(ks, cfg.dtype), to_dev_qkv(inp.v, cfg.dtype),
+                       dt_d if with_dt else None, a_cs, to_dev_f32(ref_f["y"]), to_dev_f32(ref_f["den"]),
+                       to_dev_f32(dy), chunk)
+    dq, dk, dv, ddt, da = got
+    # the oracle's gradients of v and dt through the value operand v dt
+    if with_dt:
+        ref_dv = ref["dvop"] * dt[..., None]
+        ref_ddt = (ref["dvop"] * vf).sum(axis=-1)
+    else:
+        ref_dv, ref_ddt = ref["dvop"], None
+    return {"dq": (dq, ref["dq"]), "dk": (dk, ref["dk"]), "dv": (dv, ref_dv), "da": (da, ref["da"]),
+            "ddt": (ddt, ref_ddt)}, (qf, kf, vop, a, dy)
+
+
+def rel_to_max(got, ref):
+    return float(np.abs(got - ref).max() / np.abs(ref).max())
+
+
+# (config, B, H, N, chunk, value operand v*dt)
+BWD = [
+    ("o1_f32_small", 1, 2, 1, 64, True), ("o1_f32_small", 1, 2, 63, 64, True),
+    ("o1_f32_small", 2, 1, 200, 128, True), ("o1_f32_small", 1, 2, 130, 64, False),
+    ("o1_bf16_2k", 1, 2, 64, 64, True), ("o1_bf16_2k", 2, 2, 333, 128, True),
+    ("o1_bf16_2k", 1, 3, 700, 64, False),
+]
+
+
+@pytest.mark.parametrize("name,B,H,N,chunk,with_dt", BWD)
+def test_backward_small(name, B, H, N, chunk, with_dt):
+    """Well-conditioned inputs (positive features): every gradient within
+    1e-4 of the largest reference element of its tensor (fp32 arithmetic)."""
+    cfg = I.CONFIGS[name]
+    say("backward", name, B, H, N, chunk, with_dt)
+    res, _ = backward_case(cfg, B, H, N, seed=5 * N + H, positive=True, with_dt=with_dt, chunk=chunk)
+    dv_max = float(np.abs(res["dv"][1]).max())
+    for n, (g, r) in res.items():
+        if r is None:
+            assert g is None
+            continue
+        # a gradient that is exactly 0 (N = 1: y_0 is the value operand) is
+        # measured against the value gradient's size
+        denom = float(np.abs(r).max())
+        if denom <= 1e-8 * dv_max:
+            denom = dv_max
+        err = float(np.abs(g - r).max()) / denom
+        say("  ", n, err)
+        assert err <= 1e-4, n
+
+
+@pytest.mark.parametrize("name,N", [("o1_f32_small", 256), ("o1_bf16_2k", 320)])
+def test_backward_workload_inputs(name, N):
+    """The workload's own inputs (signed features, some normalisers near 0):
+    every element within 1e-4 of its first-order error scale (the oracle's
+    backward_error_scale), and the tensors' norm-wise errors small."""
+    cfg = I.CONFIGS[name]
+    say("backward workload inputs", name, N)
+    res, (qf, kf, vop, a, dy) = backward_case(cfg, 1, 2, N, seed=17, positive=False, with_dt=True,
+                                              chunk=cfg.chunk)
+    sc = O.backward_error_scale(qf, kf, vop, a, 1, dy)
+    for n in ("dq", "dk", "da"):
+        g, r = res[n]
+        err = float((np.abs(g - r) / sc[n]).max())
+        nrm = float(np.linalg.norm(g - r) / np.linalg.norm(r))
+        say("  ", n, err, nrm)
+        assert err <= 1e-4 and nrm <= 1e-3, n
+    assert all(np.all(np.isfinite(res[n][0])) for n in res if res[n][0] is not None)
+
+
+def test_backward_full_size_sampled_heads():
+    """The order-1 2K workload (4 x 16 heads, N 2048) through the backward at
+    full size, in the launch the library uses; two heads checked against the
+    oracle (positive features)."""
+    cfg = I.CONFIGS["o1_bf16_2k"]
+    say("backward full size")
+    inp = I.make_forward_inputs(cfg)
+    store = lambda x: I._store(x, cfg.dtype)
+    qf, kf = (I.bf16_bits_to_f64(store(np.abs(I.bf16_bits_to_f64(x)) + 0.05)) for x in (inp.q, inp.k))
+    qs, ks = store(qf), store(kf)
+    dt, a = O.discretise(inp.dt_proj, inp.dt_bias, inp.A_log)
+    vop = I.bf16_bits_to_f64(inp.v) * dt[..., None]
+    heads = [(0, 3), (3, 14)]
+    dy = np.random.default_rng(8).standard_normal(vop.shape).astype(np.float32)
+    # y and den for every head (the kernels read all of them): the GPU forward
+    # on the same inputs; the checked heads' y and den are the oracle's
+    ssd = ssd_mod()
+    dt_d, a_cs, _ = ssd.prep(to_dev_f32(inp.dt_proj), to_dev_f32(inp.dt_bias), to_dev_f32(inp.A_log), cfg.chunk)
+    q_d, k_d, v_d = to_dev_qkv(qs, cfg.dtype), to_dev_qkv(ks, cfg.dtype), to_dev_qkv(inp.v, cfg.dtype)
+    den_d = torch.empty(inp.dt_proj.shape, device="cuda")
+    y_d = ssd.forward(q_d, k_d, v_d, dt_d, a_cs, 1, cfg.chunk, den=den_d)
+    refs = {}
+    for (b, h) in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rf = O.forward_quadratic(qf[sl], kf[sl], vop[sl], a[sl], 1)
+        y_d[b, h] = torch.from_numpy(rf["y"][0, 0].astype(np.float32)).cuda()
+        den_d[b, h] = torch.from_numpy(rf["den"][0, 0].astype(np.float32)).cuda()
+        refs[(b, h)] = O.backward_quadratic(qf[sl], kf[sl], vop[sl], a[sl], 1, dy[sl].astype(np.float64))
+    dq, dk, dv, ddt, da = run_backward(q_d, k_d, v_d, dt_d, a_cs, y_d, den_d, to_dev_f32(dy), cfg.chunk)
+    for (b, h), ref in refs.items():
+        for n, g in (("dq", dq), ("dk", dk), ("da", da)):
+            err = rel_to_max(g[b, h], ref[n][0, 0])
+            say("  head", b, h, n, err)
+            assert err <= 1e-4, (b, h, n)
+        err = rel_to_max(dv[b, h], ref["dvop"][0, 0] * dt[b, h][:, None])
+        assert err <= 1e-4, (b, h, "dv")
+
+
+@pytest.mark.parametrize("amask", [False, True])
+def test_prep_backward(amask):
+    """The discretisation's chain rule against the oracle's."""
+    ssd = ssd_mod()
+    cfg = I.CONFIGS["o1_bf16_2k"]
+    inp = I.make_forward_inputs(cfg, B=2, H=3, N=200, seed=31)
+    rng = np.random.default_rng(32)
+    da = rng.standard_normal(inp.dt_proj.shape).astype(np.float32)
+    ddt = rng.standard_normal(inp.dt_proj.shape).astype(np.float32)
+    if not amask:
+        g = ssd.prep_backward(to_dev_f32(inp.dt_proj), to_dev_f32(inp.dt_bias), to_dev_f32(inp.A_log),
+                              to_dev_f32(da), to_dev_f32(ddt))
+        ref = O.prep_backward_ref(inp.dt_proj, inp.dt_bias, inp.A_log, da, ddt)
+        for x, r in zip(g, ref):
+            np.testing.assert_allclose(x.cpu().numpy(), r, rtol=1e-4, atol=1e-5 * np.abs(r).max())
+    else:
+        dA, ddtp = ssd.prep_amask_backward(to_dev_f32(inp.A_proj), to_dev_f32(inp.dt_proj), to_dev_f32(da),
+                                           to_dev_f32(ddt))
+        rA, rdt = O.prep_amask_backward_ref(inp.A_proj, inp.dt_proj, da, ddt)
+        np.testing.assert_allclose(dA.cpu().numpy(), rA, rtol=1e-5, atol=1e-7)
+        np.testing.assert_allclose(ddtp.cpu().numpy(), rdt, rtol=1e-5, atol=1e-7)

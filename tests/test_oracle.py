@@ -622,3 +622,68 @@ def test_backward_invariances(order):
     assert abs((k * g["dk"]).sum()) <= 1e-10 * np.abs(k * g["dk"]).sum()
     assert np.abs(g["da"][..., 0]).max() <= 1e-10 * np.abs(g["da"]).max()
     np.testing.assert_allclose(g["dvop"].sum(axis=2), dy.sum(axis=2), rtol=1e-10)
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_backward_error_scale_bounds_an_fp32_evaluation(order):
+    """The gradients' error scales bound an fp32 evaluation of the same
+    formulas (signed features, so order-1 normalisers nearly cancel on some
+    rows): every element stays within a small multiple of fp32's unit
+    roundoff times its scale."""
+    rng = np.random.default_rng(65)
+    q, k, v, a = rand_case(rng, 1, 2, 96, 6, a_scale=0.3)
+    dy = rng.standard_normal(v.shape)
+    ref = O.backward_quadratic(q, k, v, a, order, dy)
+    sc = O.backward_error_scale(q, k, v, a, order, dy)
+    f32 = O.backward_quadratic(*(x.astype(np.float32).astype(np.float64) for x in (q, k, v, a)), order,
+                               dy.astype(np.float32).astype(np.float64))
+    # an evaluation whose every product and sum is rounded to fp32
+    lo = {n: np.empty_like(x) for n, x in ref.items()}
+    for h in range(2):
+        q32, k32, v32, dy32 = (x[0, h].astype(np.float32) for x in (q, k, v, dy))
+        cs = np.cumsum(a[0, h]).astype(np.float32)
+        s32 = q32 @ k32.T
+        causal = np.tril(np.ones(s32.shape, bool))
+        D = np.exp(np.where(causal, cs[:, None] - cs[None, :], -np.inf)).astype(np.float32)
+        W = (s32 ** order * D).astype(np.float32)
+        den = W.sum(axis=1, dtype=np.float32)
+        y = (W @ v32) / den[:, None]
+        dnum = dy32 / den[:, None]
+        dden = -(dy32 * y).sum(axis=1, dtype=np.float32) / den
+        dW = ((dnum @ v32.T + dden[:, None]) * causal).astype(np.float32)
+        ds = (dW * D * np.float32(order) * s32 ** (order - 1)).astype(np.float32)
+        P = dW * W
+        dcs = P.sum(axis=1, dtype=np.float32) - P.sum(axis=0, dtype=np.float32)
+        lo["dq"][0, h] = ds @ k32
+        lo["dk"][0, h] = ds.T @ q32
+        lo["dvop"][0, h] = W.T @ dnum
+        lo["da"][0, h] = np.cumsum(dcs[::-1], dtype=np.float32)[::-1]
+    for n in ("dq", "dk", "dvop", "da"):
+        err = np.abs(lo[n] - ref[n]) / sc[n]
+        assert err.max() <= 1e-5, (n, err.max())
+    del f32
+
+
+def test_prep_amask_backward_matches_finite_differences():
+    rng = np.random.default_rng(66)
+    A_P = rng.standard_normal((1, 2, 6)) * 3
+    dt_P = rng.standard_normal((1, 2, 6)) * 3
+    da = rng.standard_normal(A_P.shape)
+    ddt = rng.standard_normal(A_P.shape)
+    gA, gdt = O.prep_amask_backward_ref(A_P, dt_P, da, ddt)
+
+    def loss(ap, dp):
+        dt, a = O.discretise_amask(ap, dp)
+        return float((a * da).sum() + (dt * ddt).sum())
+
+    h = 1e-6
+    for g, pos in ((gA, 0), (gdt, 1)):
+        num = np.empty_like(g)
+        for idx in np.ndindex(g.shape):
+            xs = [A_P.copy(), dt_P.copy()]
+            xs[pos][idx] += h
+            lp = loss(*xs)
+            xs[pos][idx] -= 2 * h
+            num[idx] = (lp - loss(*xs)) / (2 * h)
+        np.testing.assert_allclose(g, num, rtol=1e-7, atol=1e-9)
+    assert O.prep_amask_backward_ref(A_P, None, da, None)[1] is None

@@ -180,6 +180,51 @@ def bench_forward(cfg: I.Config, steps: int, warmup: int, dev, amask: bool = Fal
     return res, inp
 
 
+def bench_backward(cfg: I.Config, steps: int, warmup: int, dev):
+    """Order-1 training step's mixer gradients: ssd_backward + ssd_prep_backward
+    on the workload's inputs, with the forward's y and den (computed once,
+    outside the timed steps) as the saved activations and a random dy."""
+    import torch
+    from mamba_ssd_sequence_amd import ssd
+
+    inp = I.make_forward_inputs(cfg)
+    q, k, v = (to_dev(x, cfg.dtype, dev) for x in (inp.q, inp.k, inp.v))
+    dtp, bias, alog = (to_dev(x, I.F32, dev) for x in (inp.dt_proj, inp.dt_bias, inp.A_log))
+    B, H, N, d = q.shape
+    dt, a_cs, _ = ssd.prep(dtp, bias, alog, cfg.chunk)
+    den = torch.empty((B, H, N), device=dev)
+    y = ssd.forward(q, k, v, dt, a_cs, 1, cfg.chunk, den=den)
+    dy = torch.randn((B, H, N, d), generator=torch.Generator(device=dev).manual_seed(0), device=dev)
+    ws = torch.empty(ssd.lib().ssd_backward_workspace_size(B, H, N, d, 1, cfg.chunk,
+                                                           ssd.SSD_BF16 if cfg.dtype == I.BF16 else ssd.SSD_F32),
+                     dtype=torch.uint8, device=dev)
+
+    def step():
+        _, _, _, ddt, da = ssd.backward(q, k, v, dt, a_cs, y, den, dy, 1, cfg.chunk, workspace=ws)
+        ssd.prep_backward(dtp, bias, alog, da, ddt)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    # algorithmic bytes: q, k, v read, dt, a_cs, den read, y and dy read
+    # (fp32), dq, dk, dv written (fp32), ddt, da and the prep gradients
+    es = 2 if cfg.dtype == I.BF16 else 4
+    by = B * H * N * (3 * d * es + 2 * 4 * d + 3 * 4 * d + 4 * 4 + 2 * 4)
+    ach = by / (ms * 1e-3) / 1e9
+    return {"workload": cfg.name + "_backward", "ms_per_step": ms, "tokens_per_s": B * N / (ms * 1e-3),
+            "B": B, "H": H, "N": N, "d_h": d, "order": 1, "chunk": cfg.chunk,
+            "roofline": {"kernel": "step", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None,
+                         "alg_bytes_per_launch": by, "avg_launch_ms": ms}}
+
+
 def cpu_baseline_forward(cfg: I.Config, inp, budget_s=12.0):
     """Oracle throughput on a bounded sample: whole heads (quadratic form) when
     they fit the budget, else uniformly sampled rows of one head, extrapolated."""
@@ -382,7 +427,7 @@ def main():
     extra = []
     if not a.no_extra:
         for name in ("o2_bf16_64k", "o1_bf16_2k", "o1_bf16_4k", "o1_bf16_64k", "o2_decode",
-                     "o2_decode_packed", "o2_bf16_4k_amask"):
+                     "o2_decode_packed", "o2_bf16_4k_amask", "o1_bf16_2k_backward"):
             if name == a.workload:
                 continue
             torch.cuda.empty_cache()
@@ -390,6 +435,8 @@ def main():
                 r, _ = bench_forward(I.CONFIGS["o2_bf16_4k"], a.steps, a.warmup, dev, amask=True)
             elif name in I.ALL_CONFIGS:
                 r, _ = bench_forward(I.ALL_CONFIGS[name], max(3, a.steps // 4), 2, dev)
+            elif name == "o1_bf16_2k_backward":
+                r = bench_backward(I.CONFIGS["o1_bf16_2k"], a.steps, a.warmup, dev)
             elif name == "o2_decode_packed":
                 c = I.DECODE_CONFIGS["o2_decode"]
                 r, _ = bench_decode(c, c.steps, 3, dev, packed=True)

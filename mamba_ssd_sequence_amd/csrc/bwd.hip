@@ -29,7 +29,8 @@
 //   da_t = sum_{i >= t in the block} dcs_i (cs is the cumsum of a from the
 //   block start); dv = dvop dt, ddt = sum_c dvop_c v_c.
 //
-// Everything is computed in fp32 (the inputs are exact in fp32).  Kernels:
+// Everything is computed in fp32 (the inputs are exact in fp32); the block
+// products run on the fp32 matrix cores (v_mfma_f32_16x16x4_f32).  Kernels:
 //   k_bwd_outer  (x2)  per block, sum_i wgt_i x_i y_i^T and sum_i wgt_i zw_i x_i:
 //                      the block's state increment (forward states, recomputed)
 //                      and R_c, r_c; the latter also writes dnum and dden
@@ -79,6 +80,19 @@ __device__ __forceinline__ void load_row(const St* p, const BlockGeo& g, int r, 
   }
 }
 
+// acc[nt] += (16-row strip of A starting at m0) x (column tile nt of B) on
+// fp32 MFMA (16x16x4): lane (n, gq) supplies A[m0 + n][k + gq] and
+// B[k + gq][16 nt + n]; acc[nt][q4] = out[m0 + 4 gq + q4][16 nt + n].
+template <int NT, int K, class FA, class FB>
+__device__ __forceinline__ void mm_strip(f32x4 (&acc)[NT], int m0, int n, int gq, FA A, FB B) {
+#pragma unroll 4
+  for (int kk = 0; kk < K; kk += 4) {
+    const float a = A(m0 + n, kk + gq);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_f32(a, B(kk + gq, 16 * nt + n), acc[nt]);
+  }
+}
+
 // sum over the 4 consecutive lanes of a row (lanes 4r .. 4r + 3)
 __device__ __forceinline__ float sum4(float x) {
   x += __shfl_xor(x, 1, WAVE);
@@ -94,8 +108,8 @@ __device__ __forceinline__ float sum4(float x) {
 // MODE 0 (forward increment): x = k, y = v dt, wgt_j = e^{T - cs_j}, zw = 1;
 // also writes the block total T.  MODE 1 (R_c, r_c): x = q, y = dnum,
 // wgt_i = e^{cs_i}, zw = dden; also writes dnum and dden.
-// Thread t: row r = t / 4 (staging) / state row b = t / 4 (products), and a
-// quarter of the columns.
+// Staging: row r = t / 4, a quarter of the columns; the product on fp32
+// MFMA, wave w computing state rows 16 w .. 16 w + 15.
 // ---------------------------------------------------------------------------
 template <typename St, int DH, int MODE>
 __global__ __launch_bounds__(256) void k_bwd_outer(const St* __restrict__ xs, const St* __restrict__ vs,
@@ -111,6 +125,7 @@ __global__ __launch_bounds__(256) void k_bwd_outer(const St* __restrict__ xs, co
                                                    float* __restrict__ dden_out) {
   constexpr int QC = DH / 4;
   constexpr int E = DH * DH + DH;
+  constexpr int NTD = DH / 16;
   __shared__ float X[BLK * PF], Y[BLK * PF], wz[BLK];
   const BlockGeo g = block_geo(nblk, N, chunk, a_cs);
   const int tid = threadIdx.x, r = tid >> 2, c0 = (tid & 3) * QC;
@@ -160,23 +175,24 @@ __global__ __launch_bounds__(256) void k_bwd_outer(const St* __restrict__ xs, co
   if ((tid & 3) == 0) wz[r] = zw;
   __syncthreads();
 
-  // state row b = tid / 4 (DH rows), columns c0 ..
-  const int b = tid >> 2;
-  if (b < DH) {
-    float acc[QC], az = 0.f;
+  const int wave = tid >> 6, lane = tid & 63, n = lane & 15, gq = lane >> 4;
+  if (16 * wave < DH) {
+    f32x4 acc[NTD];
 #pragma unroll
-    for (int u = 0; u < QC; ++u) acc[u] = 0.f;
-#pragma unroll 4
-    for (int i = 0; i < BLK; ++i) {
-      const float xb = X[i * PF + b];
-#pragma unroll
-      for (int u = 0; u < QC; ++u) acc[u] += xb * Y[i * PF + c0 + u];
-      az += xb * wz[i];
-    }
+    for (int nt = 0; nt < NTD; ++nt) acc[nt] = zero4();
+    mm_strip<NTD, BLK>(acc, 16 * wave, n, gq, [&](int m, int k) { return X[k * PF + m]; },
+                       [&](int k, int c) { return Y[k * PF + c]; });
     float* o = out + slot * (int64_t)E;
 #pragma unroll
-    for (int u = 0; u < QC; ++u) o[b * DH + c0 + u] = acc[u];
-    if ((tid & 3) == 0) o[DH * DH + b] = az;
+    for (int nt = 0; nt < NTD; ++nt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) o[(16 * wave + 4 * gq + q4) * DH + 16 * nt + n] = acc[nt][q4];
+    // normaliser part: state row b = 16 wave + n, tokens 16 gq .. 16 gq + 15
+    float az = 0.f;
+#pragma unroll
+    for (int i = 16 * gq; i < 16 * gq + 16; ++i) az += X[i * PF + 16 * wave + n] * wz[i];
+    az = sum_over_groups(az);
+    if (gq == 0) o[DH * DH + 16 * wave + n] = az;
   }
 }
 
@@ -222,9 +238,10 @@ __global__ __launch_bounds__(256) void k_bwd_rev_pass(int64_t nblk, int eblocks,
 // ---------------------------------------------------------------------------
 // k_bwd_rows: the pair products of a block and everything indexed by the
 // query row: W and C (to the workspace, for k_bwd_cols), the row and column
-// sums of dW W, dq (intra + inter), and the row part of dcs.
-// Pair tile of thread t: rows 4 (t / 16) .., columns 4 (t % 16) ..; row
-// mapping of the contractions: row t / 4, a quarter of the columns.
+// sums of dW W, dq (intra + inter), and the row part of dcs.  All products
+// on fp32 MFMA; wave w owns query rows i = 16 w .. 16 w + 15, and its
+// results sit at rows 16 w + 4 gq + q4, columns 16 nt + n (gq = lane / 16,
+// n = lane % 16).
 // ---------------------------------------------------------------------------
 template <typename St, int DH>
 __global__ __launch_bounds__(256) void k_bwd_rows(const St* __restrict__ q, const St* __restrict__ k,
@@ -241,190 +258,163 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const St* __restrict__ q, cons
                                                   float* __restrict__ dq) {
   constexpr int QC = DH / 4;
   constexpr int E = DH * DH + DH;
-  __shared__ float A[BLK * PF], Bm[BLK * PF];
-  __shared__ float csl[BLK], ddl[BLK], rowl[BLK], zl[DH], colw[4][BLK];
+  constexpr int NTD = DH / 16;
+  __shared__ float X0[BLK * PF], X1[BLK * PF], X2[BLK * PF];
+  __shared__ float csl[BLK], ddl[BLK], zl[DH], colw[4][BLK];
   const BlockGeo g = block_geo(nblk, N, chunk, a_cs);
   const int tid = threadIdx.x, r = tid >> 2, c0 = (tid & 3) * QC;
+  const int wave = tid >> 6, lane = tid & 63, n = lane & 15, gq = lane >> 4;
   const int64_t slot = g.bh * nblk + g.blk;
   const float* st = sst + slot * (int64_t)E;
 
-  // phase 1: s = Q K^T on the pair tile
-  float qr[QC], kr[QC];
-  load_row<St, QC>(q, g, r, c0, qr);
-  load_row<St, QC>(k, g, r, c0, kr);
+  // X0 = Q, X1 = K: s = Q K^T
+  {
+    float qr[QC], kr[QC];
+    load_row<St, QC>(q, g, r, c0, qr);
+    load_row<St, QC>(k, g, r, c0, kr);
 #pragma unroll
-  for (int u = 0; u < QC; ++u) {
-    A[r * PF + c0 + u] = qr[u];
-    Bm[r * PF + c0 + u] = kr[u];
+    for (int u = 0; u < QC; ++u) {
+      X0[r * PF + c0 + u] = qr[u];
+      X1[r * PF + c0 + u] = kr[u];
+    }
   }
   if (tid < BLK) {
-    const bool ok = tid < g.nvalid;
-    csl[tid] = ok ? a_cs[g.row + g.t0 + tid] - g.base : 0.f;
+    csl[tid] = tid < g.nvalid ? a_cs[g.row + g.t0 + tid] - g.base : 0.f;
     ddl[tid] = ddw[slot * BLK + tid];
   }
   if (tid < DH) zl[tid] = st[DH * DH + tid];
   __syncthreads();
-  const int ti = tid >> 4, tj = tid & 15;
-  float s[4][4], a[4][4];
+  f32x4 sa[4];
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) s[x][u] = a[x][u] = 0.f;
-#pragma unroll 4
-  for (int b = 0; b < DH; ++b) {
-    float qa[4], kb[4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      qa[x] = A[(4 * ti + x) * PF + b];
-      kb[x] = Bm[(4 * tj + x) * PF + b];
-    }
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) s[x][u] += qa[x] * kb[u];
-  }
+  for (int nt = 0; nt < 4; ++nt) sa[nt] = zero4();
+  mm_strip<4, DH>(sa, 16 * wave, n, gq, [&](int m, int kk) { return X0[m * PF + kk]; },
+                  [&](int kk, int j) { return X1[j * PF + kk]; });
   __syncthreads();
 
-  // phase 2: dnum . vop on the pair tile
-  float dn[QC], vr[QC];
+  // X2 = dnum, X1 = v dt: a = dnum vop^T
   {
     const float* dp = dnw + slot * (BLK * DH) + r * DH + c0;
-#pragma unroll
-    for (int u = 0; u < QC; ++u) dn[u] = dp[u];
+    float vr[QC];
     load_row<St, QC>(v, g, r, c0, vr);
     const float d = r < g.nvalid ? (dt ? dt[g.row + g.t0 + r] : 1.f) : 0.f;
 #pragma unroll
     for (int u = 0; u < QC; ++u) {
-      A[r * PF + c0 + u] = dn[u];
-      Bm[r * PF + c0 + u] = vr[u] * d;
+      X2[r * PF + c0 + u] = dp[u];
+      X1[r * PF + c0 + u] = vr[u] * d;
     }
   }
   __syncthreads();
-#pragma unroll 4
-  for (int c = 0; c < DH; ++c) {
-    float da_[4], vb[4];
+  f32x4 aa[4];
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-      da_[x] = A[(4 * ti + x) * PF + c];
-      vb[x] = Bm[(4 * tj + x) * PF + c];
-    }
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int u = 0; u < 4; ++u) a[x][u] += da_[x] * vb[u];
-  }
+  for (int nt = 0; nt < 4; ++nt) aa[nt] = zero4();
+  mm_strip<4, DH>(aa, 16 * wave, n, gq, [&](int m, int c) { return X2[m * PF + c]; },
+                  [&](int c, int j) { return X1[j * PF + c]; });
 
   // pair quantities: W, C = dW D, P = dW W (zero outside j <= i < nvalid)
   float rowP[4] = {0.f, 0.f, 0.f, 0.f}, colP[4] = {0.f, 0.f, 0.f, 0.f};
-  float Cq[4][4];
+  f32x4 Cr[4];
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int i = 4 * ti + x;
-    f32x4 Wv, Cv;
+  for (int nt = 0; nt < 4; ++nt) {
+    const int j = 16 * nt + n;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = 4 * tj + u;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int i = 16 * wave + 4 * gq + q4;
       const bool ok = j <= i && i < g.nvalid;
       const float D = ok ? expf(csl[i] - csl[j]) : 0.f;
-      const float W = s[x][u] * D;
-      const float dW = ok ? a[x][u] + ddl[i] : 0.f;
+      const float W = sa[nt][q4] * D;
+      const float dW = ok ? aa[nt][q4] + ddl[i] : 0.f;
       const float C = dW * D;
       const float P = dW * W;
-      Wv[u] = W;
-      Cv[u] = C;
-      Cq[x][u] = C;
-      rowP[x] += P;
-      colP[u] += P;
+      Cr[nt][q4] = C;
+      rowP[q4] += P;
+      colP[nt] += P;
+      ww[slot * (BLK * BLK) + i * BLK + j] = W;
+      cw[slot * (BLK * BLK) + i * BLK + j] = C;
     }
-    *reinterpret_cast<f32x4*>(&ww[slot * (BLK * BLK) + i * BLK + 4 * tj]) = Wv;
-    *reinterpret_cast<f32x4*>(&cw[slot * (BLK * BLK) + i * BLK + 4 * tj]) = Cv;
   }
-  // row sums over the 16 lanes of a tile row (lanes 16 ti .. 16 ti + 15)
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    float p = rowP[x];
+  for (int q4 = 0; q4 < 4; ++q4) {  // over the 16 lanes n of a row
+    float p = rowP[q4];
     p += __shfl_xor(p, 1, WAVE);
     p += __shfl_xor(p, 2, WAVE);
     p += __shfl_xor(p, 4, WAVE);
     p += __shfl_xor(p, 8, WAVE);
-    rowP[x] = p;
+    rowP[q4] = p;
   }
-  // column sums: over the 4 tile rows of a wave (lanes xor 16, 32), then waves
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    float p = colP[u];
-    p += __shfl_xor(p, 16, WAVE);
-    p += __shfl_xor(p, 32, WAVE);
-    colP[u] = p;
+  for (int nt = 0; nt < 4; ++nt) colP[nt] = sum_over_groups(colP[nt]);
+  if (gq == 0) {
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) colw[wave][16 * nt + n] = colP[nt];
   }
-  __syncthreads();  // phase-2 operands no longer needed
-  if (tj == 0) {
-#pragma unroll
-    for (int x = 0; x < 4; ++x) rowl[4 * ti + x] = rowP[x];
-  }
-  if ((tid & 63) < 16) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) colw[tid >> 6][4 * tj + u] = colP[u];
-  }
-  // phase 3: dq_intra = C K
-#pragma unroll
-  for (int x = 0; x < 4; ++x)
-#pragma unroll
-    for (int u = 0; u < 4; ++u) A[(4 * ti + x) * PF + 4 * tj + u] = Cq[x][u];
-#pragma unroll
-  for (int u = 0; u < QC; ++u) Bm[r * PF + c0 + u] = kr[u];
+  __syncthreads();  // every wave is done with X1 (v dt)
+
+  // X1 = S_c ([b][c]): u = dnum S^T, dq_inter = e_i (u + dden_i z_c)
+  for (int e = tid; e < DH * DH; e += 256) X1[(e / DH) * PF + (e % DH)] = st[e];
   __syncthreads();
+  f32x4 ua[NTD];
+#pragma unroll
+  for (int nt = 0; nt < NTD; ++nt) ua[nt] = zero4();
+  mm_strip<NTD, DH>(ua, 16 * wave, n, gq, [&](int m, int c) { return X2[m * PF + c]; },
+                    [&](int c, int b) { return X1[b * PF + c]; });
+  float dcs_inter[4] = {0.f, 0.f, 0.f, 0.f};
+  f32x4 dqo[NTD];
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int i = 16 * wave + 4 * gq + q4;
+    const float ei = i < g.nvalid ? expf(csl[i]) : 0.f;
+#pragma unroll
+    for (int nt = 0; nt < NTD; ++nt) {
+      const int b = 16 * nt + n;
+      const float inter = ei * (ua[nt][q4] + ddl[i] * zl[b]);
+      dqo[nt][q4] = inter;
+      dcs_inter[q4] += X0[i * PF + b] * inter;
+    }
+  }
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    float p = dcs_inter[q4];
+    p += __shfl_xor(p, 1, WAVE);
+    p += __shfl_xor(p, 2, WAVE);
+    p += __shfl_xor(p, 4, WAVE);
+    p += __shfl_xor(p, 8, WAVE);
+    dcs_inter[q4] = p;
+  }
+  __syncthreads();  // X0 (Q) and X2 (dnum) are free
+
+  // X0 = C, X2 = K: dq_intra = C K
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) X0[(16 * wave + 4 * gq + q4) * PF + 16 * nt + n] = Cr[nt][q4];
+  {
+    float kr[QC];
+    load_row<St, QC>(k, g, r, c0, kr);
+#pragma unroll
+    for (int u = 0; u < QC; ++u) X2[r * PF + c0 + u] = kr[u];
+  }
+  __syncthreads();
+  mm_strip<NTD, BLK>(dqo, 16 * wave, n, gq, [&](int m, int j) { return X0[m * PF + j]; },
+                     [&](int j, int b) { return X2[j * PF + b]; });
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int i = 16 * wave + 4 * gq + q4;
+    if (i < g.nvalid) {
+      float* o = dq + (g.row + g.t0 + i) * DH;
+#pragma unroll
+      for (int nt = 0; nt < NTD; ++nt) o[16 * nt + n] = dqo[nt][q4];
+      if (n == 0) rowp[slot * BLK + i] = rowP[q4] + dcs_inter[q4];
+    }
+  }
   if (tid < BLK)
     colp[slot * BLK + tid] = (colw[0][tid] + colw[1][tid]) + (colw[2][tid] + colw[3][tid]);
-  float dqi[QC];
-#pragma unroll
-  for (int u = 0; u < QC; ++u) dqi[u] = 0.f;
-#pragma unroll 4
-  for (int j = 0; j < BLK; ++j) {
-    const float cij = A[r * PF + j];
-#pragma unroll
-    for (int u = 0; u < QC; ++u) dqi[u] += cij * Bm[j * PF + c0 + u];
-  }
-  __syncthreads();
-
-  // phase 4: inter part, u_ib = sum_c S_c[b][c] dnum_ic for this row's b
-  // range; dq_inter = e_i (u_i + dden_i z_c)
-  for (int e = tid; e < DH * DH; e += 256) Bm[(e / DH) * PF + (e % DH)] = st[e];
-#pragma unroll
-  for (int u = 0; u < QC; ++u) A[r * PF + c0 + u] = dn[u];
-  __syncthreads();
-  const float ei = r < g.nvalid ? expf(csl[r]) : 0.f;
-  float acc[QC];
-#pragma unroll
-  for (int u = 0; u < QC; ++u) acc[u] = 0.f;
-#pragma unroll 4
-  for (int c = 0; c < DH; ++c) {
-    const float dnc = A[r * PF + c];
-#pragma unroll
-    for (int u = 0; u < QC; ++u) acc[u] += Bm[(c0 + u) * PF + c] * dnc;
-  }
-  float dcs_inter = 0.f;
-  float dqo[QC];
-#pragma unroll
-  for (int u = 0; u < QC; ++u) {
-    const float inter = ei * (acc[u] + ddl[r] * zl[c0 + u]);
-    dcs_inter += qr[u] * inter;
-    dqo[u] = dqi[u] + inter;
-  }
-  dcs_inter = sum4(dcs_inter);
-  if (r < g.nvalid) {
-    float* o = dq + (g.row + g.t0 + r) * DH + c0;
-#pragma unroll
-    for (int u = 0; u < QC; ++u) o[u] = dqo[u];
-    if ((tid & 3) == 0) rowp[slot * BLK + r] = rowl[r] + dcs_inter;
-  }
 }
 
 // ---------------------------------------------------------------------------
 // k_bwd_cols: everything indexed by the key row j: dk (intra + state), dvop
 // (intra + state) -> dv and ddt, dcs (row part from k_bwd_rows, column part,
-// state part, dT at the last token) -> da.  Thread t: row j = t / 4, a
-// quarter of the columns.
+// state part, dT at the last token) -> da.  fp32 MFMA; wave w owns key rows
+// j = 16 w .. 16 w + 15 (layout as in k_bwd_rows).
 // ---------------------------------------------------------------------------
 template <typename St, int DH>
 __global__ __launch_bounds__(256) void k_bwd_cols(const St* __restrict__ q, const St* __restrict__ k,
@@ -444,136 +434,141 @@ __global__ __launch_bounds__(256) void k_bwd_cols(const St* __restrict__ q, cons
                                                   float* __restrict__ da) {
   constexpr int QC = DH / 4;
   constexpr int E = DH * DH + DH;
-  __shared__ float A[BLK * PF], Bm[BLK * PF], Cm[BLK * PF];
-  __shared__ float gl[DH], dcl[BLK], red[4];
+  constexpr int NTD = DH / 16;
+  __shared__ float X0[BLK * PF], X1[BLK * PF], X2[BLK * PF];
+  __shared__ float gl[DH], csl[BLK], dtl[BLK], dcl[BLK], red[4];
   const BlockGeo g = block_geo(nblk, N, chunk, a_cs);
-  const int tid = threadIdx.x, j = tid >> 2, c0 = (tid & 3) * QC;
+  const int tid = threadIdx.x, r = tid >> 2, c0 = (tid & 3) * QC;
+  const int wave = tid >> 6, lane = tid & 63, n = lane & 15, gq = lane >> 4;
   const int64_t slot = g.bh * nblk + g.blk;
   const float* st = sst + slot * (int64_t)E;
   const float* gs = gst + slot * (int64_t)E;
-  const bool ok = j < g.nvalid;
-  const float cs = ok ? a_cs[g.row + g.t0 + j] - g.base : 0.f;
   const float T = a_cs[g.row + g.t0 + g.nvalid - 1] - g.base;
-  const float wj = ok ? expf(T - cs) : 0.f;
-  const float dtj = ok ? (dt ? dt[g.row + g.t0 + j] : 1.f) : 0.f;
 
-  // phase 1: dk_intra[j] = sum_i C[i][j] q_i
-  float qr[QC], kr[QC], vr[QC];
-  load_row<St, QC>(q, g, j, c0, qr);
-  load_row<St, QC>(k, g, j, c0, kr);
-  load_row<St, QC>(v, g, j, c0, vr);
+  // X0 = C ([i][j]), X1 = Q: dk_intra = C^T Q
   const float* cb = cw + slot * (BLK * BLK);
-  for (int e = tid; e < BLK * BLK; e += 256) A[(e / BLK) * PF + (e % BLK)] = cb[e];
-#pragma unroll
-  for (int u = 0; u < QC; ++u) Bm[j * PF + c0 + u] = qr[u];
-  __syncthreads();
-  float dkj[QC];
-#pragma unroll
-  for (int u = 0; u < QC; ++u) dkj[u] = 0.f;
-#pragma unroll 4
-  for (int i = 0; i < BLK; ++i) {
-    const float cij = A[i * PF + j];
-#pragma unroll
-    for (int u = 0; u < QC; ++u) dkj[u] += cij * Bm[i * PF + c0 + u];
-  }
-  __syncthreads();
-
-  // phase 2: dvop_intra[j] = sum_i W[i][j] dnum_i
-  const float* wb = ww + slot * (BLK * BLK);
-  for (int e = tid; e < BLK * BLK; e += 256) A[(e / BLK) * PF + (e % BLK)] = wb[e];
+  for (int e = tid; e < BLK * BLK; e += 256) X0[(e / BLK) * PF + (e % BLK)] = cb[e];
   {
-    const float* dp = dnw + slot * (BLK * DH) + j * DH + c0;
+    float qr[QC];
+    load_row<St, QC>(q, g, r, c0, qr);
 #pragma unroll
-    for (int u = 0; u < QC; ++u) Bm[j * PF + c0 + u] = dp[u];
+    for (int u = 0; u < QC; ++u) X1[r * PF + c0 + u] = qr[u];
+  }
+  if (tid < BLK) {
+    const bool ok = tid < g.nvalid;
+    csl[tid] = ok ? a_cs[g.row + g.t0 + tid] - g.base : 0.f;
+    dtl[tid] = ok ? (dt ? dt[g.row + g.t0 + tid] : 1.f) : 0.f;
   }
   __syncthreads();
-  float dvj[QC];
+  f32x4 dka[NTD], dva[NTD];
 #pragma unroll
-  for (int u = 0; u < QC; ++u) dvj[u] = 0.f;
-#pragma unroll 4
-  for (int i = 0; i < BLK; ++i) {
-    const float wij = A[i * PF + j];
-#pragma unroll
-    for (int u = 0; u < QC; ++u) dvj[u] += wij * Bm[i * PF + c0 + u];
-  }
+  for (int nt = 0; nt < NTD; ++nt) dka[nt] = dva[nt] = zero4();
+  mm_strip<NTD, BLK>(dka, 16 * wave, n, gq, [&](int m, int i) { return X0[i * PF + m]; },
+                     [&](int i, int b) { return X1[i * PF + b]; });
   __syncthreads();
 
-  // phase 3: the state terms with G = G_{c+1}: t_j = G vop_j + g,
-  // dk_j += w_j t_j, dvop_j += w_j G^T k_j, k_j . t_j
-  for (int e = tid; e < DH * DH; e += 256) A[(e / DH) * PF + (e % DH)] = gs[e];
-  if (tid < DH) gl[tid] = gs[DH * DH + tid];
+  // X0 = W, X1 = dnum: dvop_intra = W^T dnum
+  const float* wb = ww + slot * (BLK * BLK);
+  for (int e = tid; e < BLK * BLK; e += 256) X0[(e / BLK) * PF + (e % BLK)] = wb[e];
+  {
+    const float* dp = dnw + slot * (BLK * DH) + r * DH + c0;
 #pragma unroll
-  for (int u = 0; u < QC; ++u) {
-    Bm[j * PF + c0 + u] = vr[u] * dtj;  // vop
-    Cm[j * PF + c0 + u] = kr[u];
+    for (int u = 0; u < QC; ++u) X1[r * PF + c0 + u] = dp[u];
   }
   __syncthreads();
-  float tj[QC], gk[QC];
+  mm_strip<NTD, BLK>(dva, 16 * wave, n, gq, [&](int m, int i) { return X0[i * PF + m]; },
+                     [&](int i, int c) { return X1[i * PF + c]; });
+  __syncthreads();
+
+  // X0 = G ([b][c]), X1 = v (raw), X2 = K: t = (v dt) G^T, gk = K G
+  for (int e = tid; e < DH * DH; e += 256) X0[(e / DH) * PF + (e % DH)] = gs[e];
+  if (tid < DH) gl[tid] = gs[DH * DH + tid];
+  {
+    float vr[QC], kr[QC];
+    load_row<St, QC>(v, g, r, c0, vr);
+    load_row<St, QC>(k, g, r, c0, kr);
 #pragma unroll
-  for (int u = 0; u < QC; ++u) {
-    tj[u] = gl[c0 + u];
-    gk[u] = 0.f;
+    for (int u = 0; u < QC; ++u) {
+      X1[r * PF + c0 + u] = vr[u];
+      X2[r * PF + c0 + u] = kr[u];
+    }
   }
-#pragma unroll 4
-  for (int c = 0; c < DH; ++c) {
-    const float vc = Bm[j * PF + c];  // t_b = g_b + sum_c G[b][c] vop_jc, b in this quarter
+  __syncthreads();
+  f32x4 ta[NTD], gka[NTD];
 #pragma unroll
-    for (int u = 0; u < QC; ++u) tj[u] += A[(c0 + u) * PF + c] * vc;
-  }
-#pragma unroll 4
-  for (int b = 0; b < DH; ++b) {
-    const float kb = Cm[j * PF + b];  // (G^T k_j)_c, c in this quarter
+  for (int nt = 0; nt < NTD; ++nt) ta[nt] = gka[nt] = zero4();
+  mm_strip<NTD, DH>(ta, 16 * wave, n, gq, [&](int m, int c) { return X1[m * PF + c] * dtl[m]; },
+                    [&](int c, int b) { return X0[b * PF + c]; });
+  mm_strip<NTD, DH>(gka, 16 * wave, n, gq, [&](int m, int b) { return X2[m * PF + b]; },
+                    [&](int b, int c) { return X0[b * PF + c]; });
+
+  float kt[4] = {0.f, 0.f, 0.f, 0.f}, dd[4] = {0.f, 0.f, 0.f, 0.f}, wjr[4];
 #pragma unroll
-    for (int u = 0; u < QC; ++u) gk[u] += A[b * PF + c0 + u] * kb;
-  }
-  float kt = 0.f;
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int j = 16 * wave + 4 * gq + q4;
+    const bool ok = j < g.nvalid;
+    const float wj = ok ? expf(T - csl[j]) : 0.f;
+    wjr[q4] = wj;
 #pragma unroll
-  for (int u = 0; u < QC; ++u) {
-    dkj[u] += wj * tj[u];
-    kt += kr[u] * tj[u];
-    dvj[u] += wj * gk[u];
+    for (int nt = 0; nt < NTD; ++nt) {
+      const int b = 16 * nt + n;  // also the value column c
+      const float t = ta[nt][q4] + gl[b];
+      dka[nt][q4] += wj * t;
+      kt[q4] += X2[j * PF + b] * t;
+      dva[nt][q4] += wj * gka[nt][q4];
+      dd[q4] += dva[nt][q4] * X1[j * PF + b];
+    }
   }
-  kt = sum4(kt);
-  // <G, S_c> + <g, z_c> over the block's state slots
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+      kt[q4] += __shfl_xor(kt[q4], off, WAVE);
+      dd[q4] += __shfl_xor(dd[q4], off, WAVE);
+    }
+  }
+  // dT = sum_j w_j k_j . t_j + e^T (<G, S_c> + <g, z_c>)
   float gsd = 0.f;
   for (int e = tid; e < E; e += 256) gsd += gs[e] * st[e];
-  for (int off = 1; off < WAVE; off <<= 1) gsd += __shfl_xor(gsd, off, WAVE);
-  // sum_j w_j k_j . t_j over the block (one lane per row)
-  float wkt = ((tid & 3) == 0) ? wj * kt : 0.f;
-  for (int off = 1; off < WAVE; off <<= 1) wkt += __shfl_xor(wkt, off, WAVE);
-  if ((tid & 63) == 0) red[tid >> 6] = wkt + expf(T) * gsd;
+  float wkt = 0.f;
+  if (n == 0) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) wkt += wjr[q4] * kt[q4];
+  }
+  float part = wkt + expf(T) * gsd;
+  for (int off = 1; off < WAVE; off <<= 1) part += __shfl_xor(part, off, WAVE);
+  if (lane == 0) red[wave] = part;
   __syncthreads();
   const float dT = (red[0] + red[1]) + (red[2] + red[3]);
 
-  // outputs of row j
-  float ddtj = 0.f;
 #pragma unroll
-  for (int u = 0; u < QC; ++u) ddtj += dvj[u] * vr[u];
-  ddtj = sum4(ddtj);
-  if (ok) {
-    const int64_t o = (g.row + g.t0 + j) * DH + c0;
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int j = 16 * wave + 4 * gq + q4;
+    if (j < g.nvalid) {
+      const int64_t o = (g.row + g.t0 + j) * DH;
 #pragma unroll
-    for (int u = 0; u < QC; ++u) {
-      dk[o + u] = dkj[u];
-      dv[o + u] = dvj[u] * dtj;
+      for (int nt = 0; nt < NTD; ++nt) {
+        dk[o + 16 * nt + n] = dka[nt][q4];
+        dv[o + 16 * nt + n] = dva[nt][q4] * dtl[j];
+      }
     }
-  }
-  if ((tid & 3) == 0) {
-    float dcs = 0.f;
-    if (ok) {
-      dcs = rowp[slot * BLK + j] - colp[slot * BLK + j] - wj * kt;
-      if (j == g.nvalid - 1) dcs += dT;
-      if (ddt) ddt[g.row + g.t0 + j] = ddtj;
+    if (n == 0) {
+      float dcs = 0.f;
+      if (j < g.nvalid) {
+        dcs = rowp[slot * BLK + j] - colp[slot * BLK + j] - wjr[q4] * kt[q4];
+        if (j == g.nvalid - 1) dcs += dT;
+        if (ddt) ddt[g.row + g.t0 + j] = dd[q4];
+      }
+      dcl[j] = dcs;
     }
-    dcl[j] = dcs;
   }
   __syncthreads();
   // da_t = sum_{s >= t} dcs_s within the block: a reverse scan by wave 0
   if (tid < BLK) {
     float x = dcl[BLK - 1 - tid];  // lane l holds dcs of token 63 - l
     for (int off = 1; off < WAVE; off <<= 1) {
-      const float y = __shfl_up(x, off, WAVE);
-      if (tid >= off) x += y;
+      const float yv = __shfl_up(x, off, WAVE);
+      if (tid >= off) x += yv;
     }
     const int t = BLK - 1 - tid;
     if (t < g.nvalid) da[g.row + g.t0 + t] = x;
@@ -592,17 +587,19 @@ __global__ __launch_bounds__(256) void k_bwd_cols(const St* __restrict__ q, cons
 __device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
 
 template <int MODE>
-__global__ __launch_bounds__(256) void k_prep_bwd(const float* __restrict__ p0,
-                                                  const float* __restrict__ p1,
-                                                  const float* __restrict__ A_log,
-                                                  const float* __restrict__ da,
-                                                  const float* __restrict__ ddt, int64_t B,
-                                                  int64_t H, int64_t N, float* __restrict__ o0,
-                                                  float* __restrict__ o1,
-                                                  float* __restrict__ o2) {
-  // one workgroup per head h, looping over the batch and the tokens
+__global__ __launch_bounds__(1024) void k_prep_bwd(const float* __restrict__ p0,
+                                                   const float* __restrict__ p1,
+                                                   const float* __restrict__ A_log,
+                                                   const float* __restrict__ da,
+                                                   const float* __restrict__ ddt, int64_t B,
+                                                   int64_t H, int64_t N, float* __restrict__ o0,
+                                                   float* __restrict__ o1,
+                                                   float* __restrict__ o2) {
+  // one workgroup of 1024 threads per head h, looping over the batch and the
+  // tokens (4 tokens in flight per thread)
+  constexpr int NTH = 1024, U = 4;
   const int64_t h = blockIdx.x;
-  __shared__ float red[2][4];
+  __shared__ float red[2][NTH / WAVE];
   float sb = 0.f, sa = 0.f;
   float A = 0.f, bias = 0.f;
   if (MODE == 0) {
@@ -611,19 +608,24 @@ __global__ __launch_bounds__(256) void k_prep_bwd(const float* __restrict__ p0,
   }
   for (int64_t b = 0; b < B; ++b) {
     const int64_t base = (b * H + h) * N;
-    for (int64_t n = threadIdx.x; n < N; n += 256) {
-      const int64_t i = base + n;
-      if (MODE == 0) {
-        const float x = p0[i] + bias;
-        const float dtv = softplus_f(x);
-        const float gdt = (ddt ? ddt[i] : 0.f) + da[i] * A;
-        const float d = gdt * sigmoid_f(x);
-        o0[i] = d;
-        sb += d;
-        sa += da[i] * dtv;
-      } else {
-        o0[i] = -da[i] * sigmoid_f(p0[i]);
-        if (p1) o1[i] = ddt[i] * sigmoid_f(p1[i]);
+    for (int64_t n0 = 0; n0 < N; n0 += NTH * U) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t n = n0 + u * NTH + threadIdx.x;
+        if (n >= N) continue;
+        const int64_t i = base + n;
+        if (MODE == 0) {
+          const float x = p0[i] + bias;
+          const float dtv = softplus_f(x);
+          const float gdt = (ddt ? ddt[i] : 0.f) + da[i] * A;
+          const float d = gdt * sigmoid_f(x);
+          o0[i] = d;
+          sb += d;
+          sa += da[i] * dtv;
+        } else {
+          o0[i] = -da[i] * sigmoid_f(p0[i]);
+          if (p1) o1[i] = ddt[i] * sigmoid_f(p1[i]);
+        }
       }
     }
   }
@@ -638,8 +640,13 @@ __global__ __launch_bounds__(256) void k_prep_bwd(const float* __restrict__ p0,
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-      o1[h] = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
-      o2[h] = A * ((red[1][0] + red[1][1]) + (red[1][2] + red[1][3]));
+      float tb = 0.f, ta = 0.f;
+      for (int w = 0; w < NTH / WAVE; ++w) {
+        tb += red[0][w];
+        ta += red[1][w];
+      }
+      o1[h] = tb;
+      o2[h] = A * ta;
     }
   }
 }
@@ -705,7 +712,7 @@ hipError_t launch_prep_backward(const float* dt_proj, const float* dt_bias, cons
                                 const float* da, const float* ddt, int64_t B, int64_t H, int64_t N,
                                 float* d_dt_proj, float* d_dt_bias, float* d_A_log,
                                 hipStream_t stream) {
-  hipLaunchKernelGGL(k_prep_bwd<0>, dim3((unsigned)H), dim3(256), 0, stream, dt_proj, dt_bias, A_log, da,
+  hipLaunchKernelGGL(k_prep_bwd<0>, dim3((unsigned)H), dim3(1024), 0, stream, dt_proj, dt_bias, A_log, da,
                      ddt, B, H, N, d_dt_proj, d_dt_bias, d_A_log);
   return hipGetLastError();
 }
@@ -713,7 +720,7 @@ hipError_t launch_prep_backward(const float* dt_proj, const float* dt_bias, cons
 hipError_t launch_prep_amask_backward(const float* A_proj, const float* dt_proj, const float* da,
                                       const float* ddt, int64_t B, int64_t H, int64_t N,
                                       float* d_A_proj, float* d_dt_proj, hipStream_t stream) {
-  hipLaunchKernelGGL(k_prep_bwd<1>, dim3((unsigned)H), dim3(256), 0, stream, A_proj, dt_proj, nullptr, da,
+  hipLaunchKernelGGL(k_prep_bwd<1>, dim3((unsigned)H), dim3(1024), 0, stream, A_proj, dt_proj, nullptr, da,
                      ddt, B, H, N, d_A_proj, d_dt_proj, nullptr);
   return hipGetLastError();
 }

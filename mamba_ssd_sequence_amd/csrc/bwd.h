@@ -16,10 +16,8 @@ namespace ssd {
 //   gst  [BH, nblk, E]       R_c, r_c, then (in place) the gradient of the
 //                            state leaving each block, G_{c+1} and g_{c+1}
 //   dnum [BH, nblk, 64, d_h] dy / den;  dden [BH, nblk, 64]
-//   w, c [BH, nblk, 64, 64]  the block's W_ij and C_ij = dW_ij e^{cs_i - cs_j}
-//   rowp, colp [BH, nblk, 64] the row and column parts of dcs
 struct BwdLayout {
-  size_t tb, sst, gst, dnum, dden, w, c, rowp, colp, total_floats;
+  size_t tb, sst, gst, dnum, dden, total_floats;
 };
 
 inline BwdLayout bwd_layout(int64_t BH, int64_t N, int64_t DH) {
@@ -32,10 +30,6 @@ inline BwdLayout bwd_layout(int64_t BH, int64_t N, int64_t DH) {
   L.gst = off;  off = up(off + nbk * (size_t)(DH * DH + DH));
   L.dnum = off; off = up(off + nbk * 64 * (size_t)DH);
   L.dden = off; off = up(off + nbk * 64);
-  L.w = off;    off = up(off + nbk * 64 * 64);
-  L.c = off;    off = up(off + nbk * 64 * 64);
-  L.rowp = off; off = up(off + nbk * 64);
-  L.colp = off; off = up(off + nbk * 64);
   L.total_floats = off;
   return L;
 }

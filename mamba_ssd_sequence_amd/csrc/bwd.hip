@@ -36,9 +36,8 @@
 //                      and R_c, r_c; the latter also writes dnum and dden
 //   k_state_pass       forward scan of the increments -> S_c (shared with the forward)
 //   k_bwd_rev_pass     reverse scan of R_c -> G_{c+1}
-//   k_bwd_rows         pair products (W, C, the two sums of dW W), dq, and the row
-//                      parts of dcs
-//   k_bwd_cols         dk, dvop -> dv, ddt, the column and state parts of dcs, da
+//   k_bwd_block        per block, every gradient: the pair products (W, C, the
+//                      two sums of dW W), dq, dk, dvop -> dv and ddt, dcs -> da
 #include "common.h"
 #include "launch.h"
 #include "bwd.h"
@@ -236,53 +235,70 @@ __global__ __launch_bounds__(256) void k_bwd_rev_pass(int64_t nblk, int eblocks,
 }
 
 // ---------------------------------------------------------------------------
-// k_bwd_rows: the pair products of a block and everything indexed by the
-// query row: W and C (to the workspace, for k_bwd_cols), the row and column
-// sums of dW W, dq (intra + inter), and the row part of dcs.  All products
-// on fp32 MFMA; wave w owns query rows i = 16 w .. 16 w + 15, and its
-// results sit at rows 16 w + 4 gq + q4, columns 16 nt + n (gq = lane / 16,
-// n = lane % 16).
+// k_bwd_block: every gradient of one block from its own tokens, the state
+// entering it (S_c, z_c) and the gradient of the state leaving it (G, g):
+// the pair products (s = Q K^T, dnum vop^T -> W, C = dW D, P = dW W), dq
+// (intra C K + inter), dk (intra C^T Q + state), dvop (intra W^T dnum +
+// state) -> dv and ddt, and dcs (row and column sums of P, the inter and
+// state parts, dT at the last token) -> da.  All products on fp32 MFMA in
+// three LDS buffers that each phase restages; wave w owns rows 16 w ..
+// 16 w + 15 of every product, its results at rows 16 w + 4 gq + q4, columns
+// 16 nt + n (gq = lane / 16, n = lane % 16).
 // ---------------------------------------------------------------------------
 template <typename St, int DH>
-__global__ __launch_bounds__(256) void k_bwd_rows(const St* __restrict__ q, const St* __restrict__ k,
-                                                  const St* __restrict__ v,
-                                                  const float* __restrict__ dt,
-                                                  const float* __restrict__ a_cs, int64_t N,
-                                                  int64_t chunk, int64_t nblk,
-                                                  const float* __restrict__ sst,
-                                                  const float* __restrict__ dnw,
-                                                  const float* __restrict__ ddw,
-                                                  float* __restrict__ ww, float* __restrict__ cw,
-                                                  float* __restrict__ rowp,
-                                                  float* __restrict__ colp,
-                                                  float* __restrict__ dq) {
+__global__ __launch_bounds__(256) void k_bwd_block(const St* __restrict__ q, const St* __restrict__ k,
+                                                   const St* __restrict__ v,
+                                                   const float* __restrict__ dt,
+                                                   const float* __restrict__ a_cs, int64_t N,
+                                                   int64_t chunk, int64_t nblk,
+                                                   const float* __restrict__ sst,
+                                                   const float* __restrict__ gst,
+                                                   const float* __restrict__ dnw,
+                                                   const float* __restrict__ ddw,
+                                                   float* __restrict__ dq, float* __restrict__ dk,
+                                                   float* __restrict__ dv, float* __restrict__ ddt,
+                                                   float* __restrict__ da) {
   constexpr int QC = DH / 4;
   constexpr int E = DH * DH + DH;
   constexpr int NTD = DH / 16;
   __shared__ float X0[BLK * PF], X1[BLK * PF], X2[BLK * PF];
-  __shared__ float csl[BLK], ddl[BLK], zl[DH], colw[4][BLK];
+  __shared__ float csl[BLK], ddl[BLK], dtl[BLK], zl[DH], gl[DH], rowl[BLK], colw[4][BLK], dcl[BLK];
+  __shared__ float red[4];
   const BlockGeo g = block_geo(nblk, N, chunk, a_cs);
   const int tid = threadIdx.x, r = tid >> 2, c0 = (tid & 3) * QC;
   const int wave = tid >> 6, lane = tid & 63, n = lane & 15, gq = lane >> 4;
   const int64_t slot = g.bh * nblk + g.blk;
   const float* st = sst + slot * (int64_t)E;
-
-  // X0 = Q, X1 = K: s = Q K^T
-  {
-    float qr[QC], kr[QC];
-    load_row<St, QC>(q, g, r, c0, qr);
-    load_row<St, QC>(k, g, r, c0, kr);
+  const float* gs = gst + slot * (int64_t)E;
+  const float* dnb = dnw + slot * (BLK * DH);
+  const float T = a_cs[g.row + g.t0 + g.nvalid - 1] - g.base;
+  auto stage_rows = [&](float* X, const St* p) {
+    float x[QC];
+    load_row<St, QC>(p, g, r, c0, x);
 #pragma unroll
-    for (int u = 0; u < QC; ++u) {
-      X0[r * PF + c0 + u] = qr[u];
-      X1[r * PF + c0 + u] = kr[u];
-    }
-  }
+    for (int u = 0; u < QC; ++u) X[r * PF + c0 + u] = x[u];
+  };
+  auto stage_dnum = [&](float* X) {
+#pragma unroll
+    for (int u = 0; u < QC; ++u) X[r * PF + c0 + u] = dnb[r * DH + c0 + u];
+  };
+  auto stage_state = [&](float* X, const float* src) {
+    for (int e = tid; e < DH * DH; e += 256) X[(e / DH) * PF + (e % DH)] = src[e];
+  };
+
+  // phase 1: X0 = Q, X1 = K: s = Q K^T
+  stage_rows(X0, q);
+  stage_rows(X1, k);
   if (tid < BLK) {
-    csl[tid] = tid < g.nvalid ? a_cs[g.row + g.t0 + tid] - g.base : 0.f;
+    const bool ok = tid < g.nvalid;
+    csl[tid] = ok ? a_cs[g.row + g.t0 + tid] - g.base : 0.f;
     ddl[tid] = ddw[slot * BLK + tid];
+    dtl[tid] = ok ? (dt ? dt[g.row + g.t0 + tid] : 1.f) : 0.f;
   }
-  if (tid < DH) zl[tid] = st[DH * DH + tid];
+  if (tid < DH) {
+    zl[tid] = st[DH * DH + tid];
+    gl[tid] = gs[DH * DH + tid];
+  }
   __syncthreads();
   f32x4 sa[4];
 #pragma unroll
@@ -291,28 +307,17 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const St* __restrict__ q, cons
                   [&](int kk, int j) { return X1[j * PF + kk]; });
   __syncthreads();
 
-  // X2 = dnum, X1 = v dt: a = dnum vop^T
-  {
-    const float* dp = dnw + slot * (BLK * DH) + r * DH + c0;
-    float vr[QC];
-    load_row<St, QC>(v, g, r, c0, vr);
-    const float d = r < g.nvalid ? (dt ? dt[g.row + g.t0 + r] : 1.f) : 0.f;
-#pragma unroll
-    for (int u = 0; u < QC; ++u) {
-      X2[r * PF + c0 + u] = dp[u];
-      X1[r * PF + c0 + u] = vr[u] * d;
-    }
-  }
+  // phase 2: X2 = dnum, X1 = v: a = dnum (v dt)^T; the pair quantities
+  stage_dnum(X2);
+  stage_rows(X1, v);
   __syncthreads();
   f32x4 aa[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) aa[nt] = zero4();
   mm_strip<4, DH>(aa, 16 * wave, n, gq, [&](int m, int c) { return X2[m * PF + c]; },
-                  [&](int c, int j) { return X1[j * PF + c]; });
-
-  // pair quantities: W, C = dW D, P = dW W (zero outside j <= i < nvalid)
+                  [&](int c, int j) { return X1[j * PF + c] * dtl[j]; });
   float rowP[4] = {0.f, 0.f, 0.f, 0.f}, colP[4] = {0.f, 0.f, 0.f, 0.f};
-  f32x4 Cr[4];
+  f32x4 Cr[4], Wr[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) {
     const int j = 16 * nt + n;
@@ -323,23 +328,17 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const St* __restrict__ q, cons
       const float D = ok ? expf(csl[i] - csl[j]) : 0.f;
       const float W = sa[nt][q4] * D;
       const float dW = ok ? aa[nt][q4] + ddl[i] : 0.f;
-      const float C = dW * D;
       const float P = dW * W;
-      Cr[nt][q4] = C;
+      Cr[nt][q4] = dW * D;
+      Wr[nt][q4] = W;
       rowP[q4] += P;
       colP[nt] += P;
-      ww[slot * (BLK * BLK) + i * BLK + j] = W;
-      cw[slot * (BLK * BLK) + i * BLK + j] = C;
     }
   }
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {  // over the 16 lanes n of a row
-    float p = rowP[q4];
-    p += __shfl_xor(p, 1, WAVE);
-    p += __shfl_xor(p, 2, WAVE);
-    p += __shfl_xor(p, 4, WAVE);
-    p += __shfl_xor(p, 8, WAVE);
-    rowP[q4] = p;
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) rowP[q4] += __shfl_xor(rowP[q4], off, WAVE);
   }
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) colP[nt] = sum_over_groups(colP[nt]);
@@ -347,18 +346,18 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const St* __restrict__ q, cons
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) colw[wave][16 * nt + n] = colP[nt];
   }
-  __syncthreads();  // every wave is done with X1 (v dt)
-
-  // X1 = S_c ([b][c]): u = dnum S^T, dq_inter = e_i (u + dden_i z_c)
-  for (int e = tid; e < DH * DH; e += 256) X1[(e / DH) * PF + (e % DH)] = st[e];
   __syncthreads();
-  f32x4 ua[NTD];
-#pragma unroll
-  for (int nt = 0; nt < NTD; ++nt) ua[nt] = zero4();
-  mm_strip<NTD, DH>(ua, 16 * wave, n, gq, [&](int m, int c) { return X2[m * PF + c]; },
-                    [&](int c, int b) { return X1[b * PF + c]; });
-  float dcs_inter[4] = {0.f, 0.f, 0.f, 0.f};
+
+  // phase 3: X1 = S_c: u = dnum S_c^T, dq_inter = e_i (u + dden_i z_c),
+  // dcs_inter_i = q_i . dq_inter_i
+  stage_state(X1, st);
+  __syncthreads();
   f32x4 dqo[NTD];
+#pragma unroll
+  for (int nt = 0; nt < NTD; ++nt) dqo[nt] = zero4();
+  mm_strip<NTD, DH>(dqo, 16 * wave, n, gq, [&](int m, int c) { return X2[m * PF + c]; },
+                    [&](int c, int b) { return X1[b * PF + c]; });
+  float dci[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
     const int i = 16 * wave + 4 * gq + q4;
@@ -366,36 +365,31 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const St* __restrict__ q, cons
 #pragma unroll
     for (int nt = 0; nt < NTD; ++nt) {
       const int b = 16 * nt + n;
-      const float inter = ei * (ua[nt][q4] + ddl[i] * zl[b]);
+      const float inter = ei * (dqo[nt][q4] + ddl[i] * zl[b]);
       dqo[nt][q4] = inter;
-      dcs_inter[q4] += X0[i * PF + b] * inter;
+      dci[q4] += X0[i * PF + b] * inter;
     }
-  }
 #pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
-    float p = dcs_inter[q4];
-    p += __shfl_xor(p, 1, WAVE);
-    p += __shfl_xor(p, 2, WAVE);
-    p += __shfl_xor(p, 4, WAVE);
-    p += __shfl_xor(p, 8, WAVE);
-    dcs_inter[q4] = p;
+    for (int off = 1; off < 16; off <<= 1) dci[q4] += __shfl_xor(dci[q4], off, WAVE);
+    if (n == 0) rowl[i] = rowP[q4] + dci[q4];
   }
-  __syncthreads();  // X0 (Q) and X2 (dnum) are free
+  __syncthreads();
 
-  // X0 = C, X2 = K: dq_intra = C K
+  // phase 4: X0 = C, X1 = K, X2 = Q: dq += C K, dk_intra = C^T Q
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) X0[(16 * wave + 4 * gq + q4) * PF + 16 * nt + n] = Cr[nt][q4];
-  {
-    float kr[QC];
-    load_row<St, QC>(k, g, r, c0, kr);
-#pragma unroll
-    for (int u = 0; u < QC; ++u) X2[r * PF + c0 + u] = kr[u];
-  }
+  stage_rows(X1, k);
+  stage_rows(X2, q);
   __syncthreads();
   mm_strip<NTD, BLK>(dqo, 16 * wave, n, gq, [&](int m, int j) { return X0[m * PF + j]; },
-                     [&](int j, int b) { return X2[j * PF + b]; });
+                     [&](int j, int b) { return X1[j * PF + b]; });
+  f32x4 dka[NTD];
+#pragma unroll
+  for (int nt = 0; nt < NTD; ++nt) dka[nt] = zero4();
+  mm_strip<NTD, BLK>(dka, 16 * wave, n, gq, [&](int m, int i) { return X0[i * PF + m]; },
+                     [&](int i, int b) { return X2[i * PF + b]; });
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
     const int i = 16 * wave + 4 * gq + q4;
@@ -403,96 +397,29 @@ __global__ __launch_bounds__(256) void k_bwd_rows(const St* __restrict__ q, cons
       float* o = dq + (g.row + g.t0 + i) * DH;
 #pragma unroll
       for (int nt = 0; nt < NTD; ++nt) o[16 * nt + n] = dqo[nt][q4];
-      if (n == 0) rowp[slot * BLK + i] = rowP[q4] + dcs_inter[q4];
     }
   }
-  if (tid < BLK)
-    colp[slot * BLK + tid] = (colw[0][tid] + colw[1][tid]) + (colw[2][tid] + colw[3][tid]);
-}
-
-// ---------------------------------------------------------------------------
-// k_bwd_cols: everything indexed by the key row j: dk (intra + state), dvop
-// (intra + state) -> dv and ddt, dcs (row part from k_bwd_rows, column part,
-// state part, dT at the last token) -> da.  fp32 MFMA; wave w owns key rows
-// j = 16 w .. 16 w + 15 (layout as in k_bwd_rows).
-// ---------------------------------------------------------------------------
-template <typename St, int DH>
-__global__ __launch_bounds__(256) void k_bwd_cols(const St* __restrict__ q, const St* __restrict__ k,
-                                                  const St* __restrict__ v,
-                                                  const float* __restrict__ dt,
-                                                  const float* __restrict__ a_cs, int64_t N,
-                                                  int64_t chunk, int64_t nblk,
-                                                  const float* __restrict__ sst,
-                                                  const float* __restrict__ gst,
-                                                  const float* __restrict__ dnw,
-                                                  const float* __restrict__ ww,
-                                                  const float* __restrict__ cw,
-                                                  const float* __restrict__ rowp,
-                                                  const float* __restrict__ colp,
-                                                  float* __restrict__ dk, float* __restrict__ dv,
-                                                  float* __restrict__ ddt,
-                                                  float* __restrict__ da) {
-  constexpr int QC = DH / 4;
-  constexpr int E = DH * DH + DH;
-  constexpr int NTD = DH / 16;
-  __shared__ float X0[BLK * PF], X1[BLK * PF], X2[BLK * PF];
-  __shared__ float gl[DH], csl[BLK], dtl[BLK], dcl[BLK], red[4];
-  const BlockGeo g = block_geo(nblk, N, chunk, a_cs);
-  const int tid = threadIdx.x, r = tid >> 2, c0 = (tid & 3) * QC;
-  const int wave = tid >> 6, lane = tid & 63, n = lane & 15, gq = lane >> 4;
-  const int64_t slot = g.bh * nblk + g.blk;
-  const float* st = sst + slot * (int64_t)E;
-  const float* gs = gst + slot * (int64_t)E;
-  const float T = a_cs[g.row + g.t0 + g.nvalid - 1] - g.base;
-
-  // X0 = C ([i][j]), X1 = Q: dk_intra = C^T Q
-  const float* cb = cw + slot * (BLK * BLK);
-  for (int e = tid; e < BLK * BLK; e += 256) X0[(e / BLK) * PF + (e % BLK)] = cb[e];
-  {
-    float qr[QC];
-    load_row<St, QC>(q, g, r, c0, qr);
-#pragma unroll
-    for (int u = 0; u < QC; ++u) X1[r * PF + c0 + u] = qr[u];
-  }
-  if (tid < BLK) {
-    const bool ok = tid < g.nvalid;
-    csl[tid] = ok ? a_cs[g.row + g.t0 + tid] - g.base : 0.f;
-    dtl[tid] = ok ? (dt ? dt[g.row + g.t0 + tid] : 1.f) : 0.f;
-  }
-  __syncthreads();
-  f32x4 dka[NTD], dva[NTD];
-#pragma unroll
-  for (int nt = 0; nt < NTD; ++nt) dka[nt] = dva[nt] = zero4();
-  mm_strip<NTD, BLK>(dka, 16 * wave, n, gq, [&](int m, int i) { return X0[i * PF + m]; },
-                     [&](int i, int b) { return X1[i * PF + b]; });
   __syncthreads();
 
-  // X0 = W, X1 = dnum: dvop_intra = W^T dnum
-  const float* wb = ww + slot * (BLK * BLK);
-  for (int e = tid; e < BLK * BLK; e += 256) X0[(e / BLK) * PF + (e % BLK)] = wb[e];
-  {
-    const float* dp = dnw + slot * (BLK * DH) + r * DH + c0;
+  // phase 5: X0 = W, X2 = dnum: dvop_intra = W^T dnum
 #pragma unroll
-    for (int u = 0; u < QC; ++u) X1[r * PF + c0 + u] = dp[u];
-  }
+  for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) X0[(16 * wave + 4 * gq + q4) * PF + 16 * nt + n] = Wr[nt][q4];
+  stage_dnum(X2);
   __syncthreads();
+  f32x4 dva[NTD];
+#pragma unroll
+  for (int nt = 0; nt < NTD; ++nt) dva[nt] = zero4();
   mm_strip<NTD, BLK>(dva, 16 * wave, n, gq, [&](int m, int i) { return X0[i * PF + m]; },
-                     [&](int i, int c) { return X1[i * PF + c]; });
+                     [&](int i, int c) { return X2[i * PF + c]; });
   __syncthreads();
 
-  // X0 = G ([b][c]), X1 = v (raw), X2 = K: t = (v dt) G^T, gk = K G
-  for (int e = tid; e < DH * DH; e += 256) X0[(e / DH) * PF + (e % DH)] = gs[e];
-  if (tid < DH) gl[tid] = gs[DH * DH + tid];
-  {
-    float vr[QC], kr[QC];
-    load_row<St, QC>(v, g, r, c0, vr);
-    load_row<St, QC>(k, g, r, c0, kr);
-#pragma unroll
-    for (int u = 0; u < QC; ++u) {
-      X1[r * PF + c0 + u] = vr[u];
-      X2[r * PF + c0 + u] = kr[u];
-    }
-  }
+  // phase 6: X0 = G, X1 = v, X2 = K: t = (v dt) G^T + g, gk = K G; the
+  // state terms
+  stage_state(X0, gs);
+  stage_rows(X1, v);
+  stage_rows(X2, k);
   __syncthreads();
   f32x4 ta[NTD], gka[NTD];
 #pragma unroll
@@ -501,13 +428,11 @@ __global__ __launch_bounds__(256) void k_bwd_cols(const St* __restrict__ q, cons
                     [&](int c, int b) { return X0[b * PF + c]; });
   mm_strip<NTD, DH>(gka, 16 * wave, n, gq, [&](int m, int b) { return X2[m * PF + b]; },
                     [&](int b, int c) { return X0[b * PF + c]; });
-
   float kt[4] = {0.f, 0.f, 0.f, 0.f}, dd[4] = {0.f, 0.f, 0.f, 0.f}, wjr[4];
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
     const int j = 16 * wave + 4 * gq + q4;
-    const bool ok = j < g.nvalid;
-    const float wj = ok ? expf(T - csl[j]) : 0.f;
+    const float wj = j < g.nvalid ? expf(T - csl[j]) : 0.f;
     wjr[q4] = wj;
 #pragma unroll
     for (int nt = 0; nt < NTD; ++nt) {
@@ -518,9 +443,6 @@ __global__ __launch_bounds__(256) void k_bwd_cols(const St* __restrict__ q, cons
       dva[nt][q4] += wj * gka[nt][q4];
       dd[q4] += dva[nt][q4] * X1[j * PF + b];
     }
-  }
-#pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) {
       kt[q4] += __shfl_xor(kt[q4], off, WAVE);
@@ -529,13 +451,13 @@ __global__ __launch_bounds__(256) void k_bwd_cols(const St* __restrict__ q, cons
   }
   // dT = sum_j w_j k_j . t_j + e^T (<G, S_c> + <g, z_c>)
   float gsd = 0.f;
-  for (int e = tid; e < E; e += 256) gsd += gs[e] * st[e];
-  float wkt = 0.f;
+  for (int e = tid; e < DH * DH; e += 256) gsd += X0[(e / DH) * PF + (e % DH)] * st[e];
+  if (tid < DH) gsd += gl[tid] * zl[tid];
+  float part = expf(T) * gsd;
   if (n == 0) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) wkt += wjr[q4] * kt[q4];
+    for (int q4 = 0; q4 < 4; ++q4) part += wjr[q4] * kt[q4];
   }
-  float part = wkt + expf(T) * gsd;
   for (int off = 1; off < WAVE; off <<= 1) part += __shfl_xor(part, off, WAVE);
   if (lane == 0) red[wave] = part;
   __syncthreads();
@@ -555,7 +477,8 @@ __global__ __launch_bounds__(256) void k_bwd_cols(const St* __restrict__ q, cons
     if (n == 0) {
       float dcs = 0.f;
       if (j < g.nvalid) {
-        dcs = rowp[slot * BLK + j] - colp[slot * BLK + j] - wjr[q4] * kt[q4];
+        const float cp = (colw[0][j] + colw[1][j]) + (colw[2][j] + colw[3][j]);
+        dcs = rowl[j] - cp - wjr[q4] * kt[q4];
         if (j == g.nvalid - 1) dcs += dT;
         if (ddt) ddt[g.row + g.t0 + j] = dd[q4];
       }
@@ -670,10 +593,6 @@ static hipError_t bwd_o1_typed(const void* q, const void* k, const void* v, cons
   float* gst = ws + L.gst;
   float* dnw = ws + L.dnum;
   float* ddw = ws + L.dden;
-  float* wwp = ws + L.w;
-  float* cwp = ws + L.c;
-  float* rowp = ws + L.rowp;
-  float* colp = ws + L.colp;
   constexpr int E = DH * DH + DH;
   const int eblocks = (E + 255) / 256;
   // forward states S_c (recomputed in fp32) and the gradients R_c
@@ -685,10 +604,8 @@ static hipError_t bwd_o1_typed(const void* q, const void* k, const void* v, cons
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_bwd_rev_pass<DH>, dim3((unsigned)(BH * eblocks)), blk, 0, stream, nb, eblocks,
                      tb, gst);
-  hipLaunchKernelGGL((k_bwd_rows<St, DH>), grid, blk, 0, stream, qs, ks, vs, dt, a_cs, N, chunk, nb,
-                     sst, dnw, ddw, wwp, cwp, rowp, colp, dq);
-  hipLaunchKernelGGL((k_bwd_cols<St, DH>), grid, blk, 0, stream, qs, ks, vs, dt, a_cs, N, chunk, nb,
-                     sst, gst, dnw, wwp, cwp, rowp, colp, dk, dv, ddt, da);
+  hipLaunchKernelGGL((k_bwd_block<St, DH>), grid, blk, 0, stream, qs, ks, vs, dt, a_cs, N, chunk, nb,
+                     sst, gst, dnw, ddw, dq, dk, dv, ddt, da);
   return hipGetLastError();
 }
 

@@ -216,6 +216,52 @@ def test_deterministic():
     assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("name,order", [("o1_bf16_2k", 1), ("o2_bf16_4k", 2)])
+def test_graph_capture_replays_match_eager(name, order):
+    """ssd_prep + ssd_forward captured in a HIP graph (no memset nodes: the
+    library launches kernels only) and replayed several times, with other
+    eager work and synchronisations between the replays: every replay
+    reproduces the eager result bit for bit."""
+    ssd = ssd_mod()
+    cfg = I.CONFIGS[name]
+    say("graph capture", name)
+    inp = I.make_forward_inputs(cfg, B=1, H=4, N=333, seed=12)
+    other = I.make_forward_inputs(cfg, B=1, H=4, N=333, seed=13)
+    dev = [to_dev_qkv(x, cfg.dtype) for x in (inp.q, inp.k, inp.v)] + \
+          [to_dev_f32(x) for x in (inp.dt_proj, inp.dt_bias, inp.A_log)]
+    odev = [to_dev_qkv(x, cfg.dtype) for x in (other.q, other.k, other.v)] + \
+           [to_dev_f32(x) for x in (other.dt_proj, other.dt_bias, other.A_log)]
+    B, H, N, d = dev[0].shape
+    ws = torch.empty(ssd.workspace_size(B, H, N, d, order, cfg.chunk, 1 if cfg.dtype == I.BF16 else 0),
+                     dtype=torch.uint8, device="cuda")
+    dt, a_cs, a_chunk = (torch.empty((B, H, n), device="cuda") for n in (N, N, -(-N // cfg.chunk)))
+    y = torch.empty((B, H, N, d), device="cuda")
+
+    def step(t, out):
+        ssd.prep(t[3], t[4], t[5], cfg.chunk, out=(dt, a_cs, a_chunk))
+        ssd.forward(t[0], t[1], t[2], dt, a_cs, order, cfg.chunk, y=out, workspace=ws)
+
+    step(dev, y)
+    torch.cuda.synchronize()
+    want = y.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step(dev, y)
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step(dev, y)
+    y_other = torch.empty_like(y)
+    for rep in range(3):
+        y.zero_()
+        step(odev, y_other)  # eager work on other inputs in between
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, want), rep
+
+
 # ---------------------------------------------------------------------------
 # forward: the full-size workloads, sampled rows
 # ---------------------------------------------------------------------------

@@ -181,8 +181,8 @@ def bench_forward(cfg: I.Config, steps: int, warmup: int, dev, amask: bool = Fal
 
 
 def bench_backward(cfg: I.Config, steps: int, warmup: int, dev):
-    """Order-1 training step's mixer gradients: ssd_backward + ssd_prep_backward
-    on the workload's inputs, with the forward's y and den (computed once,
+    """A training step's mixer gradients: ssd_backward + ssd_prep_backward on
+    the workload's inputs, with the forward's y and den (computed once,
     outside the timed steps) as the saved activations and a random dy."""
     import torch
     from mamba_ssd_sequence_amd import ssd
@@ -193,14 +193,14 @@ def bench_backward(cfg: I.Config, steps: int, warmup: int, dev):
     B, H, N, d = q.shape
     dt, a_cs, _ = ssd.prep(dtp, bias, alog, cfg.chunk)
     den = torch.empty((B, H, N), device=dev)
-    y = ssd.forward(q, k, v, dt, a_cs, 1, cfg.chunk, den=den)
+    y = ssd.forward(q, k, v, dt, a_cs, cfg.order, cfg.chunk, den=den)
     dy = torch.randn((B, H, N, d), generator=torch.Generator(device=dev).manual_seed(0), device=dev)
-    ws = torch.empty(ssd.lib().ssd_backward_workspace_size(B, H, N, d, 1, cfg.chunk,
+    ws = torch.empty(ssd.lib().ssd_backward_workspace_size(B, H, N, d, cfg.order, cfg.chunk,
                                                            ssd.SSD_BF16 if cfg.dtype == I.BF16 else ssd.SSD_F32),
                      dtype=torch.uint8, device=dev)
 
     def step():
-        _, _, _, ddt, da = ssd.backward(q, k, v, dt, a_cs, y, den, dy, 1, cfg.chunk, workspace=ws)
+        _, _, _, ddt, da = ssd.backward(q, k, v, dt, a_cs, y, den, dy, cfg.order, cfg.chunk, workspace=ws)
         ssd.prep_backward(dtp, bias, alog, da, ddt)
 
     for _ in range(warmup):
@@ -219,7 +219,7 @@ def bench_backward(cfg: I.Config, steps: int, warmup: int, dev):
     by = B * H * N * (3 * d * es + 2 * 4 * d + 3 * 4 * d + 4 * 4 + 2 * 4)
     ach = by / (ms * 1e-3) / 1e9
     return {"workload": cfg.name + "_backward", "ms_per_step": ms, "tokens_per_s": B * N / (ms * 1e-3),
-            "B": B, "H": H, "N": N, "d_h": d, "order": 1, "chunk": cfg.chunk,
+            "B": B, "H": H, "N": N, "d_h": d, "order": cfg.order, "chunk": cfg.chunk,
             "roofline": {"kernel": "step", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None,
                          "alg_bytes_per_launch": by, "avg_launch_ms": ms}}
@@ -427,7 +427,8 @@ def main():
     extra = []
     if not a.no_extra:
         for name in ("o2_bf16_64k", "o1_bf16_2k", "o1_bf16_4k", "o1_bf16_64k", "o2_decode",
-                     "o2_decode_packed", "o2_bf16_4k_amask", "o1_bf16_2k_backward"):
+                     "o2_decode_packed", "o2_bf16_4k_amask", "o1_bf16_2k_backward",
+                     "o2_bf16_4k_backward"):
             if name == a.workload:
                 continue
             torch.cuda.empty_cache()
@@ -435,8 +436,8 @@ def main():
                 r, _ = bench_forward(I.CONFIGS["o2_bf16_4k"], a.steps, a.warmup, dev, amask=True)
             elif name in I.ALL_CONFIGS:
                 r, _ = bench_forward(I.ALL_CONFIGS[name], max(3, a.steps // 4), 2, dev)
-            elif name == "o1_bf16_2k_backward":
-                r = bench_backward(I.CONFIGS["o1_bf16_2k"], a.steps, a.warmup, dev)
+            elif name.endswith("_backward"):
+                r = bench_backward(I.CONFIGS[name[:-len("_backward")]], max(3, a.steps // 4), 2, dev)
             elif name == "o2_decode_packed":
                 c = I.DECODE_CONFIGS["o2_decode"]
                 r, _ = bench_decode(c, c.steps, 3, dev, packed=True)

@@ -253,14 +253,15 @@ ssd_status ssd_state_unpack(const float* state_p, const float* norm_p, int64_t B
                             float* state, float* norm_state, hipStream_t stream);
 
 /*
- * ssd_backward -- gradients of ssd_forward's y (order 1), for training.
+ * ssd_backward -- gradients of ssd_forward's y, for training.
  * The pages train these models but print no backward pass: this is the chain
  * rule through the same definitions (Algorithm 1's masked product and row-sum
- * normaliser, Algorithm 4's decay mask), on the same 64-token blocks: the
- * states entering each block are recomputed, the gradient of the state
- * leaving each block is scanned in reverse, and each block then forms its
- * gradients from its own tokens and those two states.  All arithmetic is
- * fp32.
+ * normaliser, Algorithm 4's decay mask, Algorithm 5's squared scores at order
+ * 2), on the same 64-token blocks: the states entering each block are
+ * recomputed, the gradient of the state leaving each block is scanned in
+ * reverse, and each block then forms its gradients from its own tokens and
+ * those two states (at order 2 the d_h^2-row states go through HBM, one
+ * 1 MiB slot per block and head each).  All arithmetic is fp32.
  *
  *   q, k, v, dt, a_cs, B..dtype   exactly as given to ssd_forward (dt may be NULL)
  *   y, den    [B,H,N,d_h], [B,H,N] f32   ssd_forward's outputs (den is required)
@@ -274,9 +275,9 @@ ssd_status ssd_state_unpack(const float* state_p, const float* norm_p, int64_t B
  *                                -softplus(A_P)) whose chunk-local cumsum is a_cs
  *   workspace  >= ssd_backward_workspace_size bytes
  *
- * order must be 1 (SSD_ERR_UNSUPPORTED otherwise); d_h 32 or 64; fp32 or
- * bf16 inputs; no initial state.  Feed (da, ddt) to ssd_prep_backward or
- * ssd_prep_amask_backward for the parameter gradients.
+ * Orders and sizes as ssd_forward (order 1: d_h 32 or 64, fp32 or bf16;
+ * order 2: d_h 64, bf16); no initial state.  Feed (da, ddt) to
+ * ssd_prep_backward or ssd_prep_amask_backward for the parameter gradients.
  */
 size_t ssd_backward_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d_h, int order,
                                    int64_t chunk, int dtype);

@@ -445,8 +445,8 @@ size_t ssd_backward_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d_h,
                                    int64_t chunk, int dtype) {
   int64_t BH, BHN, BHNd;
   if (validate_forward_sizes(B, H, N, d_h, order, chunk, dtype, &BH, &BHN, &BHNd) != SSD_OK) return 0;
-  if (order != 1 || BHN == 0) return 0;
-  return ssd::bwd_layout(BH, N, d_h).total_floats * sizeof(float);
+  if (BHN == 0) return 0;
+  return ssd::bwd_layout(BH, N, d_h, order).total_floats * sizeof(float);
 }
 
 ssd_status ssd_backward(const void* q, const void* k, const void* v, const float* dt,
@@ -459,14 +459,12 @@ ssd_status ssd_backward(const void* q, const void* k, const void* v, const float
     int64_t BH, BHN, BHNd;
     ssd_status s = validate_forward_sizes(B, H, N, d_h, order, chunk, dtype, &BH, &BHN, &BHNd);
     if (s != SSD_OK) return s;
-    if (order != 1)
-      return fail(SSD_ERR_UNSUPPORTED, "ssd_backward: order %d (this build has the order-1 backward)", order);
     if (BHN == 0) return SSD_OK;  // nothing to differentiate
     if (!q || !k || !v || !a_cs || !y || !den || !dy || !dq || !dk || !dv || !da)
       return fail(SSD_ERR_NULL, "ssd_backward: a required pointer is NULL");
     if ((dt == nullptr) != (ddt == nullptr))
       return fail(SSD_ERR_NULL, "ssd_backward: dt and ddt must be given together");
-    const size_t need = ssd::bwd_layout(BH, N, d_h).total_floats * sizeof(float);
+    const size_t need = ssd::bwd_layout(BH, N, d_h, order).total_floats * sizeof(float);
     if (workspace_bytes < need || !workspace)
       return fail(SSD_ERR_WORKSPACE, "ssd_backward: workspace of %zu bytes needed, %zu given", need,
                   workspace ? workspace_bytes : (size_t)0);
@@ -480,9 +478,9 @@ ssd_status ssd_backward(const void* q, const void* k, const void* v, const float
                           {"da", da, (size_t)BHN * 4},  {"workspace", workspace, need}};
     if ((s = check_aligned(ins, 8)) != SSD_OK || (s = check_aligned(outs, 6)) != SSD_OK) return s;
     if ((s = check_alias(outs, 6, ins, 8)) != SSD_OK) return s;
-    return hip_status(ssd::launch_backward_o1(dtype == SSD_BF16, d_h, q, k, v, dt, a_cs, y, den, dy, BH, N,
-                                              chunk, dq, dk, dv, ddt, da, static_cast<float*>(workspace),
-                                              stream),
+    return hip_status(ssd::launch_backward(order, dtype == SSD_BF16, d_h, q, k, v, dt, a_cs, y, den, dy, BH,
+                                           N, chunk, dq, dk, dv, ddt, da, static_cast<float*>(workspace),
+                                           stream),
                       "backward launch");
   } catch (...) {
     return fail(SSD_ERR_HIP, "ssd_backward: unexpected exception");

@@ -9,7 +9,8 @@
 
 namespace ssd {
 
-// Backward workspace (float offsets), blocks of 64 tokens, E = d_h^2 + d_h:
+// Backward workspace (float offsets), blocks of 64 tokens, E = D d_h + D with
+// D = d_h^order:
 //   tb   [BH, nblk]          block decay totals
 //   sst  [BH, nblk, E]       forward increments, then (in place) the state
 //                            entering each block, S_c and z_c (recomputed)
@@ -20,23 +21,31 @@ struct BwdLayout {
   size_t tb, sst, gst, dnum, dden, total_floats;
 };
 
-inline BwdLayout bwd_layout(int64_t BH, int64_t N, int64_t DH) {
+inline BwdLayout bwd_layout(int64_t BH, int64_t N, int64_t DH, int order) {
   const size_t nbk = (size_t)(BH * n_blocks(N));
+  const size_t D = order == 1 ? (size_t)DH : (size_t)(DH * DH);
+  const size_t E = D * (size_t)DH + D;
   auto up = [](size_t x) { return (x + 63) & ~(size_t)63; };
   BwdLayout L;
   size_t off = 0;
   L.tb = off;   off = up(off + nbk);
-  L.sst = off;  off = up(off + nbk * (size_t)(DH * DH + DH));
-  L.gst = off;  off = up(off + nbk * (size_t)(DH * DH + DH));
+  L.sst = off;  off = up(off + nbk * E);
+  L.gst = off;  off = up(off + nbk * E);
   L.dnum = off; off = up(off + nbk * 64 * (size_t)DH);
   L.dden = off; off = up(off + nbk * 64);
   L.total_floats = off;
   return L;
 }
 
-// Order-1 backward: gradients with respect to q, k, v, dt (through the value
-// operand v dt) and the per-token log-decay a.  dt may be NULL (v is the
-// value operand; ddt is then NULL too).
+// Backward of the order-1 or order-2 mixer (order 2: bf16 inputs, d_h 64):
+// gradients with respect to q, k, v, dt (through the value operand v dt) and
+// the per-token log-decay a.  dt may be NULL (v is the value operand; ddt is
+// then NULL too).
+hipError_t launch_backward(int order, bool bf16, int64_t DH, const void* q, const void* k,
+                           const void* v, const float* dt, const float* a_cs, const float* y,
+                           const float* den, const float* dy, int64_t BH, int64_t N, int64_t chunk,
+                           float* dq, float* dk, float* dv, float* ddt, float* da, float* ws,
+                           hipStream_t stream);
 hipError_t launch_backward_o1(bool bf16, int64_t DH, const void* q, const void* k, const void* v,
                               const float* dt, const float* a_cs, const float* y, const float* den,
                               const float* dy, int64_t BH, int64_t N, int64_t chunk, float* dq,

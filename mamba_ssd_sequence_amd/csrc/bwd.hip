@@ -196,6 +196,154 @@ __global__ __launch_bounds__(256) void k_bwd_outer(const St* __restrict__ xs, co
 }
 
 // ---------------------------------------------------------------------------
+// k_bwd_phi_outer (order 2, d_h 64): per block, out[(a, b)][c] = sum_t wgt_t
+// x_ta x_tb y_tc and out[64^3 + (a, b)] = sum_t wgt_t zw_t x_ta x_tb, the
+// order-2 state-slot layout; MODE as k_bwd_outer.  Workgroup (block, a
+// range of 64 / AS values of a); per a a 64 x 64 x 64 product on fp32 MFMA
+// with the feature x_ta x_tb formed from the staged rows.
+// ---------------------------------------------------------------------------
+template <typename St, int MODE, int AS>
+__global__ __launch_bounds__(256) void k_bwd_phi_outer(const St* __restrict__ xs,
+                                                       const St* __restrict__ vs,
+                                                       const float* __restrict__ dt,
+                                                       const float* __restrict__ y,
+                                                       const float* __restrict__ den,
+                                                       const float* __restrict__ dy,
+                                                       const float* __restrict__ a_cs, int64_t N,
+                                                       int64_t chunk, int64_t nblk,
+                                                       float* __restrict__ tb,
+                                                       float* __restrict__ out,
+                                                       float* __restrict__ dnum_out,
+                                                       float* __restrict__ dden_out) {
+  constexpr int DH = 64, QC = DH / 4, NTD = DH / 16, AP = DH / AS;
+  constexpr int64_t E = (int64_t)DH * DH * DH + DH * DH;
+  __shared__ float X[BLK * PF], Y[BLK * PF], wl[BLK], wz[BLK];
+  // block geometry of blockIdx.x / AS
+  const int64_t bid = blockIdx.x / AS;
+  const int as = (int)(blockIdx.x - bid * AS);
+  BlockGeo g;
+  g.bh = bid / nblk;
+  g.blk = bid - g.bh * nblk;
+  g.t0 = g.blk * BLK;
+  g.row = g.bh * N;
+  g.nvalid = (int)((N - g.t0) < BLK ? (N - g.t0) : BLK);
+  g.base = (g.t0 % chunk == 0) ? 0.f : a_cs[g.row + g.t0 - 1];
+  const int tid = threadIdx.x, r = tid >> 2, c0 = (tid & 3) * QC;
+  const int64_t slot = g.bh * nblk + g.blk;
+  const bool ok = r < g.nvalid;
+  const float cs = ok ? a_cs[g.row + g.t0 + r] - g.base : 0.f;
+  const float T = a_cs[g.row + g.t0 + g.nvalid - 1] - g.base;
+
+  float xr[QC], yr[QC];
+  load_row<St, QC>(xs, g, r, c0, xr);
+  float wgt, zw;
+  if constexpr (MODE == 0) {
+    load_row<St, QC>(vs, g, r, c0, yr);
+    const float d = ok ? (dt ? dt[g.row + g.t0 + r] : 1.f) : 0.f;
+#pragma unroll
+    for (int u = 0; u < QC; ++u) yr[u] *= d;
+    wgt = ok ? expf(T - cs) : 0.f;
+    zw = 1.f;
+    if (tid == 0 && as == 0) tb[slot] = T;
+  } else {
+    const int64_t ro = g.row + g.t0 + (ok ? r : 0);
+    const float dn = den[ro];
+    float dot = 0.f, dd[QC];
+#pragma unroll
+    for (int u = 0; u < QC; ++u) {
+      dd[u] = dy[ro * DH + c0 + u];
+      dot += y[ro * DH + c0 + u] * dd[u];
+    }
+    dot = sum4(dot);
+    const float rd = 1.f / dn;
+#pragma unroll
+    for (int u = 0; u < QC; ++u) yr[u] = ok ? dd[u] * rd : 0.f;
+    zw = ok ? -dot * rd : 0.f;
+    wgt = ok ? expf(cs) : 0.f;
+    if (as == 0) {
+      float* dno = dnum_out + slot * (BLK * DH) + r * DH + c0;
+#pragma unroll
+      for (int u = 0; u < QC; ++u) dno[u] = yr[u];
+      if ((tid & 3) == 0) dden_out[slot * BLK + r] = zw;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < QC; ++u) {
+    X[r * PF + c0 + u] = xr[u];
+    Y[r * PF + c0 + u] = yr[u];
+  }
+  if ((tid & 3) == 0) {
+    wl[r] = wgt;
+    wz[r] = wgt * zw;
+  }
+  __syncthreads();
+
+  const int wave = tid >> 6, lane = tid & 63, n = lane & 15, gq = lane >> 4;
+  float* o = out + slot * E;
+  for (int a = as * AP; a < as * AP + AP; ++a) {
+    // rows (a, b = 16 wave ..): A[b][t] = wgt_t x_ta x_tb
+    f32x4 acc[NTD];
+#pragma unroll
+    for (int nt = 0; nt < NTD; ++nt) acc[nt] = zero4();
+    mm_strip<NTD, BLK>(acc, 16 * wave, n, gq,
+                       [&](int m, int t) { return X[t * PF + m] * X[t * PF + a] * wl[t]; },
+                       [&](int t, int c) { return Y[t * PF + c]; });
+#pragma unroll
+    for (int nt = 0; nt < NTD; ++nt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        o[((int64_t)a * DH + 16 * wave + 4 * gq + q4) * DH + 16 * nt + n] = acc[nt][q4];
+    // normaliser: state row (a, b = 16 wave + n), tokens 16 gq .. 16 gq + 15
+    float az = 0.f;
+#pragma unroll
+    for (int t = 16 * gq; t < 16 * gq + 16; ++t) az += X[t * PF + 16 * wave + n] * X[t * PF + a] * wz[t];
+    az = sum_over_groups(az);
+    if (gq == 0) o[(int64_t)DH * DH * DH + a * DH + 16 * wave + n] = az;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_bwd_scan: the scans over the blocks of a head for any slot size E, one
+// entry per thread.  REV false (forward states): slot c <- the running sum
+// before c, then run = e^{T_c} run + slot c.  REV true (state gradients):
+// the same from the last block down.
+// ---------------------------------------------------------------------------
+template <bool REV>
+__global__ __launch_bounds__(256) void k_bwd_scan(int64_t nblk, int64_t E, int64_t eblocks,
+                                                  const float* __restrict__ tb,
+                                                  float* __restrict__ state) {
+  const int64_t bh = blockIdx.x / eblocks;
+  const int64_t e = (blockIdx.x - bh * eblocks) * 256 + threadIdx.x;
+  if (e >= E) return;
+  float* p = state + bh * nblk * E + e;
+  const float* t = tb + bh * nblk;
+  float run = 0.f;
+  constexpr int U = 16;
+  int64_t done = 0;
+  for (; done + U <= nblk; done += U) {
+    float d[U], T[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = REV ? nblk - 1 - (done + u) : done + u;
+      d[u] = p[c * E];
+      T[u] = t[c];
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = REV ? nblk - 1 - (done + u) : done + u;
+      p[c * E] = run;
+      run = expf(T[u]) * run + d[u];
+    }
+  }
+  for (; done < nblk; ++done) {
+    const int64_t c = REV ? nblk - 1 - done : done;
+    const float d = p[c * E];
+    p[c * E] = run;
+    run = expf(t[c]) * run + d;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // k_bwd_rev_pass: in place, slot c <- sum over c' > c of the increments of
 // c', decayed: acc = 0; for c = last .. 0: (slot c, acc) <- (acc, e^{T_c} acc
 // + slot c).  One state entry per thread, all blocks of the head.
@@ -245,7 +393,7 @@ __global__ __launch_bounds__(256) void k_bwd_rev_pass(int64_t nblk, int eblocks,
 // 16 w + 15 of every product, its results at rows 16 w + 4 gq + q4, columns
 // 16 nt + n (gq = lane / 16, n = lane % 16).
 // ---------------------------------------------------------------------------
-template <typename St, int DH>
+template <typename St, int DH, int ORDER>
 __global__ __launch_bounds__(256) void k_bwd_block(const St* __restrict__ q, const St* __restrict__ k,
                                                    const St* __restrict__ v,
                                                    const float* __restrict__ dt,
@@ -259,8 +407,10 @@ __global__ __launch_bounds__(256) void k_bwd_block(const St* __restrict__ q, con
                                                    float* __restrict__ dv, float* __restrict__ ddt,
                                                    float* __restrict__ da) {
   constexpr int QC = DH / 4;
-  constexpr int E = DH * DH + DH;
+  constexpr int D = ORDER == 1 ? DH : DH * DH;  // state rows
+  constexpr int E = D * DH + D;
   constexpr int NTD = DH / 16;
+  static_assert(ORDER == 1 || DH == 64, "order 2: d_h 64");
   __shared__ float X0[BLK * PF], X1[BLK * PF], X2[BLK * PF];
   __shared__ float csl[BLK], ddl[BLK], dtl[BLK], zl[DH], gl[DH], rowl[BLK], colw[4][BLK], dcl[BLK];
   __shared__ float red[4];
@@ -295,7 +445,7 @@ __global__ __launch_bounds__(256) void k_bwd_block(const St* __restrict__ q, con
     ddl[tid] = ddw[slot * BLK + tid];
     dtl[tid] = ok ? (dt ? dt[g.row + g.t0 + tid] : 1.f) : 0.f;
   }
-  if (tid < DH) {
+  if (ORDER == 1 && tid < DH) {
     zl[tid] = st[DH * DH + tid];
     gl[tid] = gs[DH * DH + tid];
   }
@@ -325,11 +475,13 @@ __global__ __launch_bounds__(256) void k_bwd_block(const St* __restrict__ q, con
     for (int q4 = 0; q4 < 4; ++q4) {
       const int i = 16 * wave + 4 * gq + q4;
       const bool ok = j <= i && i < g.nvalid;
-      const float D = ok ? expf(csl[i] - csl[j]) : 0.f;
-      const float W = sa[nt][q4] * D;
+      const float Dm = ok ? expf(csl[i] - csl[j]) : 0.f;
+      const float sv = sa[nt][q4];
+      const float W = (ORDER == 2 ? sv * sv : sv) * Dm;
       const float dW = ok ? aa[nt][q4] + ddl[i] : 0.f;
       const float P = dW * W;
-      Cr[nt][q4] = dW * D;
+      // dW / ds (times the decay): C = dW D p s^{p-1}
+      Cr[nt][q4] = ORDER == 2 ? 2.f * sv * dW * Dm : dW * Dm;
       Wr[nt][q4] = W;
       rowP[q4] += P;
       colP[nt] += P;
@@ -348,27 +500,86 @@ __global__ __launch_bounds__(256) void k_bwd_block(const St* __restrict__ q, con
   }
   __syncthreads();
 
-  // phase 3: X1 = S_c: u = dnum S_c^T, dq_inter = e_i (u + dden_i z_c),
-  // dcs_inter_i = q_i . dq_inter_i
-  stage_state(X1, st);
-  __syncthreads();
   f32x4 dqo[NTD];
 #pragma unroll
   for (int nt = 0; nt < NTD; ++nt) dqo[nt] = zero4();
-  mm_strip<NTD, DH>(dqo, 16 * wave, n, gq, [&](int m, int c) { return X2[m * PF + c]; },
-                    [&](int c, int b) { return X1[b * PF + c]; });
   float dci[4] = {0.f, 0.f, 0.f, 0.f};
+  float eir[4];
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
     const int i = 16 * wave + 4 * gq + q4;
-    const float ei = i < g.nvalid ? expf(csl[i]) : 0.f;
+    eir[q4] = i < g.nvalid ? expf(csl[i]) : 0.f;
+  }
+  if constexpr (ORDER == 1) {
+    // phase 3: X1 = S_c: u = dnum S_c^T, dq_inter = e_i (u + dden_i z_c),
+    // dcs_inter_i = q_i . dq_inter_i
+    stage_state(X1, st);
+    __syncthreads();
+    mm_strip<NTD, DH>(dqo, 16 * wave, n, gq, [&](int m, int c) { return X2[m * PF + c]; },
+                      [&](int c, int b) { return X1[b * PF + c]; });
 #pragma unroll
-    for (int nt = 0; nt < NTD; ++nt) {
-      const int b = 16 * nt + n;
-      const float inter = ei * (dqo[nt][q4] + ddl[i] * zl[b]);
-      dqo[nt][q4] = inter;
-      dci[q4] += X0[i * PF + b] * inter;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int i = 16 * wave + 4 * gq + q4;
+#pragma unroll
+      for (int nt = 0; nt < NTD; ++nt) {
+        const int b = 16 * nt + n;
+        const float inter = eir[q4] * (dqo[nt][q4] + ddl[i] * zl[b]);
+        dqo[nt][q4] = inter;
+        dci[q4] += X0[i * PF + b] * inter;
+      }
     }
+  } else {
+    // phase 3, order 2: the state rows (a, b) and the features q_a q_b.
+    // With U_i[a][b] = sum_c S_c[(a, b)][c] dnum_ic (symmetric in a, b, as
+    // S_c is): phi(q_i)^T S_c dnum_i = q_i^T U_i q_i, so dq_i += 2 e_i U_i q_i
+    // and dcs_i += e_i q_i^T U_i q_i; the normaliser adds 2 e_i dden_i Z q_i
+    // and e_i dden_i q_i^T Z q_i (Z = z_c as a d_h x d_h matrix).  One state
+    // tile a (rows (a, 0 .. 63)) per pass: X1 = tile a, X2 = dnum, X0 = Q.
+    for (int a = 0; a <= DH; ++a) {
+      // a < DH: tile a of S_c; a == DH: Z
+      stage_state(X1, a < DH ? st + (int64_t)a * DH * DH : st + (int64_t)DH * DH * DH);
+      __syncthreads();
+      f32x4 ta[NTD];
+#pragma unroll
+      for (int nt = 0; nt < NTD; ++nt) ta[nt] = zero4();
+      if (a < DH) {  // T[i][b] = U_i[a][b]
+        mm_strip<NTD, DH>(ta, 16 * wave, n, gq, [&](int m, int c) { return X2[m * PF + c]; },
+                          [&](int c, int b) { return X1[b * PF + c]; });
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int i = 16 * wave + 4 * gq + q4;
+          float rd = 0.f;  // (U_i q_i)_a
+#pragma unroll
+          for (int nt = 0; nt < NTD; ++nt) rd += ta[nt][q4] * X0[i * PF + 16 * nt + n];
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) rd += __shfl_xor(rd, off, WAVE);
+          if (n == (a & 15)) {
+#pragma unroll
+            for (int nt = 0; nt < NTD; ++nt)
+              if (nt == (a >> 4)) dqo[nt][q4] += 2.f * eir[q4] * rd;
+          }
+          if (n == 0) dci[q4] += eir[q4] * X0[i * PF + a] * rd;  // reduced over n below
+        }
+      } else {  // (Q Z)[i][a']
+        mm_strip<NTD, DH>(ta, 16 * wave, n, gq, [&](int m, int b) { return X0[m * PF + b]; },
+                          [&](int b, int c) { return X1[b * PF + c]; });
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int i = 16 * wave + 4 * gq + q4;
+          const float f = eir[q4] * ddl[i];
+#pragma unroll
+          for (int nt = 0; nt < NTD; ++nt) {
+            dqo[nt][q4] += 2.f * f * ta[nt][q4];
+            dci[q4] += f * X0[i * PF + 16 * nt + n] * ta[nt][q4];
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int i = 16 * wave + 4 * gq + q4;
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) dci[q4] += __shfl_xor(dci[q4], off, WAVE);
     if (n == 0) rowl[i] = rowP[q4] + dci[q4];
@@ -415,44 +626,113 @@ __global__ __launch_bounds__(256) void k_bwd_block(const St* __restrict__ q, con
                      [&](int i, int c) { return X2[i * PF + c]; });
   __syncthreads();
 
-  // phase 6: X0 = G, X1 = v, X2 = K: t = (v dt) G^T + g, gk = K G; the
-  // state terms
-  stage_state(X0, gs);
+  // phase 6: the state terms, with X1 = v and X2 = K.  Order 1: X0 = G:
+  // t = (v dt) G^T + g, dk_j += w_j t_j, dvop_j += w_j G^T k_j, kt_j = k_j . t_j.
+  // Order 2 (tile a of G per pass, rows (a, 0 .. 63); G symmetric in a, b):
+  // with V_j[a][b] = sum_c G[(a, b)][c] vop_jc, dk_j += 2 w_j (V_j + g) k_j,
+  // dvop_j += w_j sum_{a,b} k_ja k_jb G[(a, b)], kt_j = k_j^T (V_j + g) k_j.
   stage_rows(X1, v);
   stage_rows(X2, k);
-  __syncthreads();
-  f32x4 ta[NTD], gka[NTD];
-#pragma unroll
-  for (int nt = 0; nt < NTD; ++nt) ta[nt] = gka[nt] = zero4();
-  mm_strip<NTD, DH>(ta, 16 * wave, n, gq, [&](int m, int c) { return X1[m * PF + c] * dtl[m]; },
-                    [&](int c, int b) { return X0[b * PF + c]; });
-  mm_strip<NTD, DH>(gka, 16 * wave, n, gq, [&](int m, int b) { return X2[m * PF + b]; },
-                    [&](int b, int c) { return X0[b * PF + c]; });
   float kt[4] = {0.f, 0.f, 0.f, 0.f}, dd[4] = {0.f, 0.f, 0.f, 0.f}, wjr[4];
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
     const int j = 16 * wave + 4 * gq + q4;
-    const float wj = j < g.nvalid ? expf(T - csl[j]) : 0.f;
-    wjr[q4] = wj;
+    wjr[q4] = j < g.nvalid ? expf(T - csl[j]) : 0.f;
+  }
+  float gsd = 0.f;  // <G, S_c> + <g, z_c> (this thread's share)
+  if constexpr (ORDER == 1) {
+    stage_state(X0, gs);
+    __syncthreads();
+    f32x4 ta[NTD], gka[NTD];
 #pragma unroll
-    for (int nt = 0; nt < NTD; ++nt) {
-      const int b = 16 * nt + n;  // also the value column c
-      const float t = ta[nt][q4] + gl[b];
-      dka[nt][q4] += wj * t;
-      kt[q4] += X2[j * PF + b] * t;
-      dva[nt][q4] += wj * gka[nt][q4];
-      dd[q4] += dva[nt][q4] * X1[j * PF + b];
+    for (int nt = 0; nt < NTD; ++nt) ta[nt] = gka[nt] = zero4();
+    mm_strip<NTD, DH>(ta, 16 * wave, n, gq, [&](int m, int c) { return X1[m * PF + c] * dtl[m]; },
+                      [&](int c, int b) { return X0[b * PF + c]; });
+    mm_strip<NTD, DH>(gka, 16 * wave, n, gq, [&](int m, int b) { return X2[m * PF + b]; },
+                      [&](int b, int c) { return X0[b * PF + c]; });
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int j = 16 * wave + 4 * gq + q4;
+#pragma unroll
+      for (int nt = 0; nt < NTD; ++nt) {
+        const int b = 16 * nt + n;
+        const float t = ta[nt][q4] + gl[b];
+        dka[nt][q4] += wjr[q4] * t;
+        kt[q4] += X2[j * PF + b] * t;
+        dva[nt][q4] += wjr[q4] * gka[nt][q4];
+      }
     }
+    for (int e = tid; e < DH * DH; e += 256) gsd += X0[(e / DH) * PF + (e % DH)] * st[e];
+    if (tid < DH) gsd += gl[tid] * zl[tid];
+  } else {
+    for (int a = 0; a <= DH; ++a) {
+      // a < DH: tile a of G; a == DH: g (as a d_h x d_h matrix)
+      const int64_t toff = a < DH ? (int64_t)a * DH * DH : (int64_t)DH * DH * DH;
+      stage_state(X0, gs + toff);
+      __syncthreads();
+      for (int e = tid; e < DH * DH; e += 256) gsd += X0[(e / DH) * PF + (e % DH)] * st[toff + e];
+      f32x4 va[NTD];
+#pragma unroll
+      for (int nt = 0; nt < NTD; ++nt) va[nt] = zero4();
+      if (a < DH) {
+        // V[j][b] = V_j[a][b]; (V_j k_j)_a
+        mm_strip<NTD, DH>(va, 16 * wave, n, gq, [&](int m, int c) { return X1[m * PF + c] * dtl[m]; },
+                          [&](int c, int b) { return X0[b * PF + c]; });
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int j = 16 * wave + 4 * gq + q4;
+          float rd = 0.f;
+#pragma unroll
+          for (int nt = 0; nt < NTD; ++nt) rd += va[nt][q4] * X2[j * PF + 16 * nt + n];
+#pragma unroll
+          for (int off = 1; off < 16; off <<= 1) rd += __shfl_xor(rd, off, WAVE);
+          if (n == (a & 15)) {
+#pragma unroll
+            for (int nt = 0; nt < NTD; ++nt)
+              if (nt == (a >> 4)) dka[nt][q4] += 2.f * wjr[q4] * rd;
+          }
+          if (n == 0) kt[q4] += X2[j * PF + a] * rd;  // reduced over n below
+        }
+        // dvop_j += w_j sum_b k_ja k_jb G[(a, b)]
+        f32x4 pa[NTD];
+#pragma unroll
+        for (int nt = 0; nt < NTD; ++nt) pa[nt] = zero4();
+        mm_strip<NTD, DH>(pa, 16 * wave, n, gq,
+                          [&](int m, int b) { return X2[m * PF + b] * X2[m * PF + a]; },
+                          [&](int b, int c) { return X0[b * PF + c]; });
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+#pragma unroll
+          for (int nt = 0; nt < NTD; ++nt) dva[nt][q4] += wjr[q4] * pa[nt][q4];
+      } else {
+        // (K g)[j][a']: dk_j += 2 w_j g k_j, kt_j += k_j^T g k_j
+        mm_strip<NTD, DH>(va, 16 * wave, n, gq, [&](int m, int b) { return X2[m * PF + b]; },
+                          [&](int b, int c) { return X0[b * PF + c]; });
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int j = 16 * wave + 4 * gq + q4;
+#pragma unroll
+          for (int nt = 0; nt < NTD; ++nt) {
+            dka[nt][q4] += 2.f * wjr[q4] * va[nt][q4];
+            kt[q4] += X2[j * PF + 16 * nt + n] * va[nt][q4];
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {
+    const int j = 16 * wave + 4 * gq + q4;
+#pragma unroll
+    for (int nt = 0; nt < NTD; ++nt) dd[q4] += dva[nt][q4] * X1[j * PF + 16 * nt + n];
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) {
       kt[q4] += __shfl_xor(kt[q4], off, WAVE);
       dd[q4] += __shfl_xor(dd[q4], off, WAVE);
     }
   }
-  // dT = sum_j w_j k_j . t_j + e^T (<G, S_c> + <g, z_c>)
-  float gsd = 0.f;
-  for (int e = tid; e < DH * DH; e += 256) gsd += X0[(e / DH) * PF + (e % DH)] * st[e];
-  if (tid < DH) gsd += gl[tid] * zl[tid];
+  // dT = sum_j w_j kt_j + e^T (<G, S_c> + <g, z_c>)
   float part = expf(T) * gsd;
   if (n == 0) {
 #pragma unroll
@@ -604,9 +884,53 @@ static hipError_t bwd_o1_typed(const void* q, const void* k, const void* v, cons
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_bwd_rev_pass<DH>, dim3((unsigned)(BH * eblocks)), blk, 0, stream, nb, eblocks,
                      tb, gst);
-  hipLaunchKernelGGL((k_bwd_block<St, DH>), grid, blk, 0, stream, qs, ks, vs, dt, a_cs, N, chunk, nb,
+  hipLaunchKernelGGL((k_bwd_block<St, DH, 1>), grid, blk, 0, stream, qs, ks, vs, dt, a_cs, N, chunk, nb,
                      sst, gst, dnw, ddw, dq, dk, dv, ddt, da);
   return hipGetLastError();
+}
+
+static hipError_t bwd_o2(const void* q, const void* k, const void* v, const float* dt,
+                         const float* a_cs, const float* y, const float* den, const float* dy,
+                         int64_t BH, int64_t N, int64_t chunk, float* dq, float* dk, float* dv,
+                         float* ddt, float* da, const BwdLayout& L, float* ws, hipStream_t stream) {
+  using St = uint16_t;
+  constexpr int DH = 64, AS = 4;
+  const int64_t nb = n_blocks(N);
+  const dim3 grid((unsigned)(BH * nb)), blk(256);
+  const St* qs = static_cast<const St*>(q);
+  const St* ks = static_cast<const St*>(k);
+  const St* vs = static_cast<const St*>(v);
+  float* tb = ws + L.tb;
+  float* sst = ws + L.sst;
+  float* gst = ws + L.gst;
+  float* dnw = ws + L.dnum;
+  float* ddw = ws + L.dden;
+  const int64_t E = (int64_t)DH * DH * DH + DH * DH;
+  const int64_t eblocks = (E + 255) / 256;
+  hipLaunchKernelGGL((k_bwd_phi_outer<St, 0, AS>), dim3((unsigned)(BH * nb * AS)), blk, 0, stream, ks, vs,
+                     dt, nullptr, nullptr, nullptr, a_cs, N, chunk, nb, tb, sst, nullptr, nullptr);
+  hipLaunchKernelGGL((k_bwd_phi_outer<St, 1, AS>), dim3((unsigned)(BH * nb * AS)), blk, 0, stream, qs,
+                     nullptr, nullptr, y, den, dy, a_cs, N, chunk, nb, nullptr, gst, dnw, ddw);
+  hipLaunchKernelGGL(k_bwd_scan<false>, dim3((unsigned)(BH * eblocks)), blk, 0, stream, nb, E, eblocks, tb,
+                     sst);
+  hipLaunchKernelGGL(k_bwd_scan<true>, dim3((unsigned)(BH * eblocks)), blk, 0, stream, nb, E, eblocks, tb,
+                     gst);
+  hipLaunchKernelGGL((k_bwd_block<St, DH, 2>), grid, blk, 0, stream, qs, ks, vs, dt, a_cs, N, chunk, nb,
+                     sst, gst, dnw, ddw, dq, dk, dv, ddt, da);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(int order, bool bf16, int64_t DH, const void* q, const void* k,
+                           const void* v, const float* dt, const float* a_cs, const float* y,
+                           const float* den, const float* dy, int64_t BH, int64_t N, int64_t chunk,
+                           float* dq, float* dk, float* dv, float* ddt, float* da, float* ws,
+                           hipStream_t stream) {
+  if (order == 2) {
+    const BwdLayout L = bwd_layout(BH, N, DH, 2);
+    return bwd_o2(q, k, v, dt, a_cs, y, den, dy, BH, N, chunk, dq, dk, dv, ddt, da, L, ws, stream);
+  }
+  return launch_backward_o1(bf16, DH, q, k, v, dt, a_cs, y, den, dy, BH, N, chunk, dq, dk, dv, ddt, da,
+                            ws, stream);
 }
 
 hipError_t launch_backward_o1(bool bf16, int64_t DH, const void* q, const void* k, const void* v,
@@ -614,7 +938,7 @@ hipError_t launch_backward_o1(bool bf16, int64_t DH, const void* q, const void* 
                               const float* dy, int64_t BH, int64_t N, int64_t chunk, float* dq,
                               float* dk, float* dv, float* ddt, float* da, float* ws,
                               hipStream_t stream) {
-  const BwdLayout L = bwd_layout(BH, N, DH);
+  const BwdLayout L = bwd_layout(BH, N, DH, 1);
   if (bf16) {
     if (DH == 64)
       return bwd_o1_typed<uint16_t, 64>(q, k, v, dt, a_cs, y, den, dy, BH, N, chunk, dq, dk, dv, ddt, da, L, ws, stream);

@@ -191,7 +191,8 @@ def bwd(lib, *, order=1, d_h=64, dt=A[3], ddt=A[12], dq=A[9], ws=A[15], wsb=1 <<
 
 
 def test_backward_errors(lib):
-    assert bwd(lib, order=2) == 3                       # order-1 backward only
+    assert bwd(lib, order=2, d_h=32) == 3               # order 2: d_h 64 only
+    assert bwd(lib, order=3) == 3
     assert bwd(lib, d_h=48) == 3
     assert bwd(lib, dq=None) == 1
     assert bwd(lib, ddt=None) == 1                      # dt given without ddt
@@ -203,7 +204,8 @@ def test_backward_errors(lib):
     assert bwd(lib, N=0) == 0                           # empty: nothing to do
     need = lib.ssd_backward_workspace_size(1, 2, 100, 64, 1, 64, 1)
     assert need >= 4 * 2 * 2 * (64 * 64 + 64)
-    assert lib.ssd_backward_workspace_size(1, 2, 100, 64, 2, 64, 1) == 0
+    assert lib.ssd_backward_workspace_size(1, 2, 100, 64, 2, 64, 1) >= 4 * 2 * 2 * (64 ** 3 + 64 ** 2)
+    assert lib.ssd_backward_workspace_size(1, 2, 100, 64, 2, 64, 0) == 0  # order 2 needs bf16
 
 
 def test_prep_backward_errors(lib):

@@ -731,14 +731,14 @@ def test_constant_value_gives_the_value():
 # is measured)
 # ---------------------------------------------------------------------------
 
-def run_backward(q, k, v, dt, a_cs, y, den, dy, chunk):
+def run_backward(q, k, v, dt, a_cs, y, den, dy, chunk, order=1):
     ssd = ssd_mod()
-    out = ssd.backward(q, k, v, dt, a_cs, y, den, dy, 1, chunk)
+    out = ssd.backward(q, k, v, dt, a_cs, y, den, dy, order, chunk)
     torch.cuda.synchronize()
     return [None if x is None else x.cpu().numpy() for x in out]
 
 
-def backward_case(cfg, B, H, N, seed, positive, with_dt, chunk):
+def backward_case(cfg, B, H, N, seed, positive, with_dt, chunk, order=1):
     """Inputs of the workload's generator (positive: |x| + 0.05 for q and k,
     normalisers bounded away from 0), the oracle's forward and backward, and
     the GPU backward on the same values."""
@@ -754,15 +754,15 @@ def backward_case(cfg, B, H, N, seed, positive, with_dt, chunk):
         qs, ks = inp.q, inp.k
     dt, a = O.discretise(inp.dt_proj, inp.dt_bias, inp.A_log)
     vop = vf * dt[..., None] if with_dt else vf
-    ref_f = O.forward_quadratic(qf, kf, vop, a, 1)
+    ref_f = O.forward_quadratic(qf, kf, vop, a, order)
     dy = np.random.default_rng(seed + 1).standard_normal(vf.shape)
     dy = dy.astype(np.float32).astype(np.float64)
-    ref = O.backward_quadratic(qf, kf, vop, a, 1, dy)
+    ref = O.backward_quadratic(qf, kf, vop, a, order, dy)
     ssd = ssd_mod()
     dt_d, a_cs, _ = ssd.prep(to_dev_f32(inp.dt_proj), to_dev_f32(inp.dt_bias), to_dev_f32(inp.A_log), chunk)
     got = run_backward(to_dev_qkv(qs, cfg.dtype), to_dev_qkv(ks, cfg.dtype), to_dev_qkv(inp.v, cfg.dtype),
                        dt_d if with_dt else None, a_cs, to_dev_f32(ref_f["y"]), to_dev_f32(ref_f["den"]),
-                       to_dev_f32(dy), chunk)
+                       to_dev_f32(dy), chunk, order)
     dq, dk, dv, ddt, da = got
     # the oracle's gradients of v and dt through the value operand v dt
     if with_dt:
@@ -778,22 +778,25 @@ def rel_to_max(got, ref):
     return float(np.abs(got - ref).max() / np.abs(ref).max())
 
 
-# (config, B, H, N, chunk, value operand v*dt)
+# (config, order, B, H, N, chunk, value operand v*dt)
 BWD = [
-    ("o1_f32_small", 1, 2, 1, 64, True), ("o1_f32_small", 1, 2, 63, 64, True),
-    ("o1_f32_small", 2, 1, 200, 128, True), ("o1_f32_small", 1, 2, 130, 64, False),
-    ("o1_bf16_2k", 1, 2, 64, 64, True), ("o1_bf16_2k", 2, 2, 333, 128, True),
-    ("o1_bf16_2k", 1, 3, 700, 64, False),
+    ("o1_f32_small", 1, 1, 2, 1, 64, True), ("o1_f32_small", 1, 1, 2, 63, 64, True),
+    ("o1_f32_small", 1, 2, 1, 200, 128, True), ("o1_f32_small", 1, 1, 2, 130, 64, False),
+    ("o1_bf16_2k", 1, 1, 2, 64, 64, True), ("o1_bf16_2k", 1, 2, 2, 333, 128, True),
+    ("o1_bf16_2k", 1, 1, 3, 700, 64, False),
+    ("o2_bf16_4k", 2, 1, 2, 1, 64, True), ("o2_bf16_4k", 2, 1, 2, 65, 64, True),
+    ("o2_bf16_4k", 2, 2, 1, 200, 128, False), ("o2_bf16_4k", 2, 1, 3, 333, 64, True),
 ]
 
 
-@pytest.mark.parametrize("name,B,H,N,chunk,with_dt", BWD)
-def test_backward_small(name, B, H, N, chunk, with_dt):
+@pytest.mark.parametrize("name,order,B,H,N,chunk,with_dt", BWD)
+def test_backward_small(name, order, B, H, N, chunk, with_dt):
     """Well-conditioned inputs (positive features): every gradient within
     1e-4 of the largest reference element of its tensor (fp32 arithmetic)."""
     cfg = I.CONFIGS[name]
-    say("backward", name, B, H, N, chunk, with_dt)
-    res, _ = backward_case(cfg, B, H, N, seed=5 * N + H, positive=True, with_dt=with_dt, chunk=chunk)
+    say("backward", name, order, B, H, N, chunk, with_dt)
+    res, _ = backward_case(cfg, B, H, N, seed=5 * N + H, positive=True, with_dt=with_dt, chunk=chunk,
+                           order=order)
     dv_max = float(np.abs(res["dv"][1]).max())
     for n, (g, r) in res.items():
         if r is None:
@@ -809,7 +812,7 @@ def test_backward_small(name, B, H, N, chunk, with_dt):
         assert err <= 1e-4, n
 
 
-@pytest.mark.parametrize("name,N", [("o1_f32_small", 256), ("o1_bf16_2k", 320)])
+@pytest.mark.parametrize("name,N", [("o1_f32_small", 256), ("o1_bf16_2k", 320), ("o2_bf16_4k", 200)])
 def test_backward_workload_inputs(name, N):
     """The workload's own inputs (signed features, some normalisers near 0):
     every element within 1e-4 of its first-order error scale (the oracle's
@@ -817,8 +820,8 @@ def test_backward_workload_inputs(name, N):
     cfg = I.CONFIGS[name]
     say("backward workload inputs", name, N)
     res, (qf, kf, vop, a, dy) = backward_case(cfg, 1, 2, N, seed=17, positive=False, with_dt=True,
-                                              chunk=cfg.chunk)
-    sc = O.backward_error_scale(qf, kf, vop, a, 1, dy)
+                                              chunk=cfg.chunk, order=cfg.order)
+    sc = O.backward_error_scale(qf, kf, vop, a, cfg.order, dy)
     for n in ("dq", "dk", "da"):
         g, r = res[n]
         err = float((np.abs(g - r) / sc[n]).max())
@@ -857,6 +860,41 @@ def test_backward_full_size_sampled_heads():
         den_d[b, h] = torch.from_numpy(rf["den"][0, 0].astype(np.float32)).cuda()
         refs[(b, h)] = O.backward_quadratic(qf[sl], kf[sl], vop[sl], a[sl], 1, dy[sl].astype(np.float64))
     dq, dk, dv, ddt, da = run_backward(q_d, k_d, v_d, dt_d, a_cs, y_d, den_d, to_dev_f32(dy), cfg.chunk)
+    for (b, h), ref in refs.items():
+        for n, g in (("dq", dq), ("dk", dk), ("da", da)):
+            err = rel_to_max(g[b, h], ref[n][0, 0])
+            say("  head", b, h, n, err)
+            assert err <= 1e-4, (b, h, n)
+        err = rel_to_max(dv[b, h], ref["dvop"][0, 0] * dt[b, h][:, None])
+        assert err <= 1e-4, (b, h, "dv")
+
+
+def test_backward_order2_full_size_sampled_heads():
+    """The order-2 4K workload (2 x 16 heads, N 4096) through the backward at
+    full size; two heads checked against the oracle (positive features)."""
+    cfg = I.CONFIGS["o2_bf16_4k"]
+    say("backward order 2 full size")
+    inp = I.make_forward_inputs(cfg)
+    store = lambda x: I._store(x, cfg.dtype)
+    qf, kf = (I.bf16_bits_to_f64(store(np.abs(I.bf16_bits_to_f64(x)) + 0.05)) for x in (inp.q, inp.k))
+    qs, ks = store(qf), store(kf)
+    dt, a = O.discretise(inp.dt_proj, inp.dt_bias, inp.A_log)
+    vop = I.bf16_bits_to_f64(inp.v) * dt[..., None]
+    heads = [(0, 5), (1, 12)]
+    dy = np.random.default_rng(9).standard_normal(vop.shape).astype(np.float32)
+    ssd = ssd_mod()
+    dt_d, a_cs, _ = ssd.prep(to_dev_f32(inp.dt_proj), to_dev_f32(inp.dt_bias), to_dev_f32(inp.A_log), cfg.chunk)
+    q_d, k_d, v_d = to_dev_qkv(qs, cfg.dtype), to_dev_qkv(ks, cfg.dtype), to_dev_qkv(inp.v, cfg.dtype)
+    den_d = torch.empty(inp.dt_proj.shape, device="cuda")
+    y_d = ssd.forward(q_d, k_d, v_d, dt_d, a_cs, 2, cfg.chunk, den=den_d)
+    refs = {}
+    for (b, h) in heads:
+        sl = (slice(b, b + 1), slice(h, h + 1))
+        rf = O.forward_quadratic(qf[sl], kf[sl], vop[sl], a[sl], 2)
+        y_d[b, h] = torch.from_numpy(rf["y"][0, 0].astype(np.float32)).cuda()
+        den_d[b, h] = torch.from_numpy(rf["den"][0, 0].astype(np.float32)).cuda()
+        refs[(b, h)] = O.backward_quadratic(qf[sl], kf[sl], vop[sl], a[sl], 2, dy[sl].astype(np.float64))
+    dq, dk, dv, ddt, da = run_backward(q_d, k_d, v_d, dt_d, a_cs, y_d, den_d, to_dev_f32(dy), cfg.chunk, 2)
     for (b, h), ref in refs.items():
         for n, g in (("dq", dq), ("dk", dk), ("da", da)):
             err = rel_to_max(g[b, h], ref[n][0, 0])

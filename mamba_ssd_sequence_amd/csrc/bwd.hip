@@ -394,7 +394,7 @@ __global__ __launch_bounds__(256) void k_bwd_rev_pass(int64_t nblk, int eblocks,
 // 16 nt + n (gq = lane / 16, n = lane % 16).
 // ---------------------------------------------------------------------------
 template <typename St, int DH, int ORDER>
-__global__ __launch_bounds__(256) void k_bwd_block(const St* __restrict__ q, const St* __restrict__ k,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_bwd_block(const St* __restrict__ q, const St* __restrict__ k,
                                                    const St* __restrict__ v,
                                                    const float* __restrict__ dt,
                                                    const float* __restrict__ a_cs, int64_t N,
@@ -535,10 +535,22 @@ __global__ __launch_bounds__(256) void k_bwd_block(const St* __restrict__ q, con
     // and dcs_i += e_i q_i^T U_i q_i; the normaliser adds 2 e_i dden_i Z q_i
     // and e_i dden_i q_i^T Z q_i (Z = z_c as a d_h x d_h matrix).  One state
     // tile a (rows (a, 0 .. 63)) per pass: X1 = tile a, X2 = dnum, X0 = Q.
+    // the next tile's loads are issued before this tile's product
+    float pre[DH * DH / 256];
+#pragma unroll
+    for (int u = 0; u < DH * DH / 256; ++u) pre[u] = st[tid + 256 * u];
     for (int a = 0; a <= DH; ++a) {
       // a < DH: tile a of S_c; a == DH: Z
-      stage_state(X1, a < DH ? st + (int64_t)a * DH * DH : st + (int64_t)DH * DH * DH);
+#pragma unroll
+      for (int u = 0; u < DH * DH / 256; ++u) {
+        const int e = tid + 256 * u;
+        X1[(e / DH) * PF + (e % DH)] = pre[u];
+      }
       __syncthreads();
+      if (a < DH) {  // a + 1 == DH: Z
+#pragma unroll
+        for (int u = 0; u < DH * DH / 256; ++u) pre[u] = st[(int64_t)(a + 1) * DH * DH + tid + 256 * u];
+      }
       f32x4 ta[NTD];
 #pragma unroll
       for (int nt = 0; nt < NTD; ++nt) ta[nt] = zero4();
@@ -665,11 +677,22 @@ __global__ __launch_bounds__(256) void k_bwd_block(const St* __restrict__ q, con
     for (int e = tid; e < DH * DH; e += 256) gsd += X0[(e / DH) * PF + (e % DH)] * st[e];
     if (tid < DH) gsd += gl[tid] * zl[tid];
   } else {
+    float pre[DH * DH / 256];  // the next tile of G, loaded during this tile's products
+#pragma unroll
+    for (int u = 0; u < DH * DH / 256; ++u) pre[u] = gs[tid + 256 * u];
     for (int a = 0; a <= DH; ++a) {
       // a < DH: tile a of G; a == DH: g (as a d_h x d_h matrix)
-      const int64_t toff = a < DH ? (int64_t)a * DH * DH : (int64_t)DH * DH * DH;
-      stage_state(X0, gs + toff);
+      const int64_t toff = (int64_t)a * DH * DH;  // a == DH: the normaliser part
+#pragma unroll
+      for (int u = 0; u < DH * DH / 256; ++u) {
+        const int e = tid + 256 * u;
+        X0[(e / DH) * PF + (e % DH)] = pre[u];
+      }
       __syncthreads();
+      if (a < DH) {
+#pragma unroll
+        for (int u = 0; u < DH * DH / 256; ++u) pre[u] = gs[toff + DH * DH + tid + 256 * u];
+      }
       for (int e = tid; e < DH * DH; e += 256) gsd += X0[(e / DH) * PF + (e % DH)] * st[toff + e];
       f32x4 va[NTD];
 #pragma unroll

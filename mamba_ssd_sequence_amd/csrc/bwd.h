@@ -11,7 +11,7 @@ namespace ssd {
 
 // Backward workspace (float offsets), blocks of 64 tokens, E = D d_h + D with
 // D = d_h^order:
-//   tb   [BH, nblk]          block decay totals
+//   tb   [BH, nblk]          block decay totals (order 1)
 //   sst  [BH, nblk, E]       forward increments, then (in place) the state
 //                            entering each block, S_c and z_c (recomputed)
 //   gst  [BH, nblk, E]       R_c, r_c, then (in place) the gradient of the

@@ -38,6 +38,12 @@
 //   k_bwd_rev_pass     reverse scan of R_c -> G_{c+1}
 //   k_bwd_block        per block, every gradient: the pair products (W, C, the
 //                      two sums of dW W), dq, dk, dvop -> dv and ddt, dcs -> da
+// and at order 2 (states of d_h^2 rows, one 1 MiB slot per block and head):
+//   k_bwd_dnum         dnum and dden per block
+//   k_bwd_phi_scan     per (head, first feature index a), sequential over the
+//                      blocks: the state tile a entering each block (forward)
+//                      and the gradient tile a of the state leaving it (reverse)
+//   k_bwd_block<2>     as above, with the state contractions per tile a
 #include "common.h"
 #include "launch.h"
 #include "bwd.h"
@@ -196,150 +202,122 @@ __global__ __launch_bounds__(256) void k_bwd_outer(const St* __restrict__ xs, co
 }
 
 // ---------------------------------------------------------------------------
-// k_bwd_phi_outer (order 2, d_h 64): per block, out[(a, b)][c] = sum_t wgt_t
-// x_ta x_tb y_tc and out[64^3 + (a, b)] = sum_t wgt_t zw_t x_ta x_tb, the
-// order-2 state-slot layout; MODE as k_bwd_outer.  Workgroup (block, a
-// range of 64 / AS values of a); per a a 64 x 64 x 64 product on fp32 MFMA
-// with the feature x_ta x_tb formed from the staged rows.
+// k_bwd_dnum: per block, dnum = dy / den and dden = -dy . y / den (order 2's
+// inputs of the state-gradient scan).  Row r = t / 4, a quarter of the columns.
 // ---------------------------------------------------------------------------
-template <typename St, int MODE, int AS>
-__global__ __launch_bounds__(256) void k_bwd_phi_outer(const St* __restrict__ xs,
-                                                       const St* __restrict__ vs,
-                                                       const float* __restrict__ dt,
-                                                       const float* __restrict__ y,
-                                                       const float* __restrict__ den,
-                                                       const float* __restrict__ dy,
-                                                       const float* __restrict__ a_cs, int64_t N,
-                                                       int64_t chunk, int64_t nblk,
-                                                       float* __restrict__ tb,
-                                                       float* __restrict__ out,
-                                                       float* __restrict__ dnum_out,
-                                                       float* __restrict__ dden_out) {
-  constexpr int DH = 64, QC = DH / 4, NTD = DH / 16, AP = DH / AS;
-  constexpr int64_t E = (int64_t)DH * DH * DH + DH * DH;
-  __shared__ float X[BLK * PF], Y[BLK * PF], wl[BLK], wz[BLK];
-  // block geometry of blockIdx.x / AS
-  const int64_t bid = blockIdx.x / AS;
-  const int as = (int)(blockIdx.x - bid * AS);
-  BlockGeo g;
-  g.bh = bid / nblk;
-  g.blk = bid - g.bh * nblk;
-  g.t0 = g.blk * BLK;
-  g.row = g.bh * N;
-  g.nvalid = (int)((N - g.t0) < BLK ? (N - g.t0) : BLK);
-  g.base = (g.t0 % chunk == 0) ? 0.f : a_cs[g.row + g.t0 - 1];
+template <int DH>
+__global__ __launch_bounds__(256) void k_bwd_dnum(const float* __restrict__ y,
+                                                  const float* __restrict__ den,
+                                                  const float* __restrict__ dy,
+                                                  const float* __restrict__ a_cs, int64_t N,
+                                                  int64_t chunk, int64_t nblk,
+                                                  float* __restrict__ dnum_out,
+                                                  float* __restrict__ dden_out) {
+  constexpr int QC = DH / 4;
+  const BlockGeo g = block_geo(nblk, N, chunk, a_cs);
   const int tid = threadIdx.x, r = tid >> 2, c0 = (tid & 3) * QC;
   const int64_t slot = g.bh * nblk + g.blk;
   const bool ok = r < g.nvalid;
-  const float cs = ok ? a_cs[g.row + g.t0 + r] - g.base : 0.f;
-  const float T = a_cs[g.row + g.t0 + g.nvalid - 1] - g.base;
-
-  float xr[QC], yr[QC];
-  load_row<St, QC>(xs, g, r, c0, xr);
-  float wgt, zw;
-  if constexpr (MODE == 0) {
-    load_row<St, QC>(vs, g, r, c0, yr);
-    const float d = ok ? (dt ? dt[g.row + g.t0 + r] : 1.f) : 0.f;
-#pragma unroll
-    for (int u = 0; u < QC; ++u) yr[u] *= d;
-    wgt = ok ? expf(T - cs) : 0.f;
-    zw = 1.f;
-    if (tid == 0 && as == 0) tb[slot] = T;
-  } else {
-    const int64_t ro = g.row + g.t0 + (ok ? r : 0);
-    const float dn = den[ro];
-    float dot = 0.f, dd[QC];
-#pragma unroll
-    for (int u = 0; u < QC; ++u) {
-      dd[u] = dy[ro * DH + c0 + u];
-      dot += y[ro * DH + c0 + u] * dd[u];
-    }
-    dot = sum4(dot);
-    const float rd = 1.f / dn;
-#pragma unroll
-    for (int u = 0; u < QC; ++u) yr[u] = ok ? dd[u] * rd : 0.f;
-    zw = ok ? -dot * rd : 0.f;
-    wgt = ok ? expf(cs) : 0.f;
-    if (as == 0) {
-      float* dno = dnum_out + slot * (BLK * DH) + r * DH + c0;
-#pragma unroll
-      for (int u = 0; u < QC; ++u) dno[u] = yr[u];
-      if ((tid & 3) == 0) dden_out[slot * BLK + r] = zw;
-    }
-  }
+  const int64_t ro = g.row + g.t0 + (ok ? r : 0);
+  const float rd = 1.f / den[ro];
+  float dd[QC], dot = 0.f;
 #pragma unroll
   for (int u = 0; u < QC; ++u) {
-    X[r * PF + c0 + u] = xr[u];
-    Y[r * PF + c0 + u] = yr[u];
+    dd[u] = dy[ro * DH + c0 + u];
+    dot += y[ro * DH + c0 + u] * dd[u];
   }
-  if ((tid & 3) == 0) {
-    wl[r] = wgt;
-    wz[r] = wgt * zw;
-  }
-  __syncthreads();
-
-  const int wave = tid >> 6, lane = tid & 63, n = lane & 15, gq = lane >> 4;
-  float* o = out + slot * E;
-  for (int a = as * AP; a < as * AP + AP; ++a) {
-    // rows (a, b = 16 wave ..): A[b][t] = wgt_t x_ta x_tb
-    f32x4 acc[NTD];
+  dot = sum4(dot);
+  float* dno = dnum_out + slot * (BLK * DH) + r * DH + c0;
 #pragma unroll
-    for (int nt = 0; nt < NTD; ++nt) acc[nt] = zero4();
-    mm_strip<NTD, BLK>(acc, 16 * wave, n, gq,
-                       [&](int m, int t) { return X[t * PF + m] * X[t * PF + a] * wl[t]; },
-                       [&](int t, int c) { return Y[t * PF + c]; });
+  for (int u = 0; u < QC; ++u) dno[u] = ok ? dd[u] * rd : 0.f;
+  if ((tid & 3) == 0) dden_out[slot * BLK + r] = ok ? -dot * rd : 0.f;
+}
+
+// ---------------------------------------------------------------------------
+// k_bwd_phi_scan (order 2, d_h 64): the state slots of one head and one first
+// feature index a, scanned over the blocks in one workgroup (the state tile
+// stays in registers): slot c <- the running tile, then running = e^{T_c}
+// running + the block's increment sum_t wgt_t x_ta x_tb y_tc (and the
+// normaliser row sum_t wgt_t zw_t x_ta x_tb).  MODE 0: forward over the
+// blocks, x = k, y = v dt, wgt = e^{T - cs}, zw = 1 (the states S_c, z_c
+// entering each block).  MODE 1: in reverse, x = q, y = dnum, wgt = e^{cs},
+// zw = dden (the gradients G_{c+1}, g_{c+1} of the state leaving each block).
+// ---------------------------------------------------------------------------
+template <typename St, int MODE>
+__global__ __launch_bounds__(256) void k_bwd_phi_scan(const St* __restrict__ xs,
+                                                      const St* __restrict__ vs,
+                                                      const float* __restrict__ dt,
+                                                      const float* __restrict__ dnw,
+                                                      const float* __restrict__ ddw,
+                                                      const float* __restrict__ a_cs, int64_t N,
+                                                      int64_t chunk, int64_t nblk,
+                                                      float* __restrict__ out) {
+  constexpr int DH = 64, QC = DH / 4, NTD = DH / 16;
+  constexpr int64_t E = (int64_t)DH * DH * DH + DH * DH;
+  __shared__ float X[BLK * PF], Y[BLK * PF], wl[BLK], wz[BLK];
+  const int64_t bh = blockIdx.x / DH;
+  const int a = (int)(blockIdx.x - bh * DH);
+  const int tid = threadIdx.x, r = tid >> 2, c0 = (tid & 3) * QC;
+  const int wave = tid >> 6, lane = tid & 63, n = lane & 15, gq = lane >> 4;
+  const int64_t row = bh * N;
+  f32x4 run[NTD];  // running tile: rows (a, b = 16 wave + 4 gq + q4), columns 16 nt + n
+#pragma unroll
+  for (int nt = 0; nt < NTD; ++nt) run[nt] = zero4();
+  float runz = 0.f;  // running normaliser entry (a, b = 16 wave + n) (lanes gq == 0)
+  for (int64_t step = 0; step < nblk; ++step) {
+    const int64_t blk = MODE == 0 ? step : nblk - 1 - step;
+    const int64_t t0 = blk * BLK;
+    const int nvalid = (int)((N - t0) < BLK ? (N - t0) : BLK);
+    const float base = (t0 % chunk == 0) ? 0.f : a_cs[row + t0 - 1];
+    const float T = a_cs[row + t0 + nvalid - 1] - base;
+    // the slot of this block gets the running tile
+    float* o = out + (bh * nblk + blk) * E;
 #pragma unroll
     for (int nt = 0; nt < NTD; ++nt)
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4)
-        o[((int64_t)a * DH + 16 * wave + 4 * gq + q4) * DH + 16 * nt + n] = acc[nt][q4];
-    // normaliser: state row (a, b = 16 wave + n), tokens 16 gq .. 16 gq + 15
+        o[((int64_t)a * DH + 16 * wave + 4 * gq + q4) * DH + 16 * nt + n] = run[nt][q4];
+    if (gq == 0) o[(int64_t)DH * DH * DH + a * DH + 16 * wave + n] = runz;
+    // stage the block: X = x rows, Y = y rows, per-token weights
+    const bool ok = r < nvalid;
+    const int64_t rr = row + t0 + (ok ? r : 0);
+    const float cs = ok ? a_cs[rr] - base : 0.f;
+#pragma unroll
+    for (int u = 0; u < QC; ++u) {
+      const float xv = Elem<St>::ld(xs, rr * DH + c0 + u);
+      X[r * PF + c0 + u] = ok ? xv : 0.f;
+    }
+    if constexpr (MODE == 0) {
+      const float d = ok ? (dt ? dt[rr] : 1.f) : 0.f;
+#pragma unroll
+      for (int u = 0; u < QC; ++u) Y[r * PF + c0 + u] = Elem<St>::ld(vs, rr * DH + c0 + u) * d;
+      if ((tid & 3) == 0) {
+        wl[r] = ok ? expf(T - cs) : 0.f;
+        wz[r] = wl[r];
+      }
+    } else {
+      const float* dp = dnw + (bh * nblk + blk) * (BLK * DH) + r * DH + c0;
+#pragma unroll
+      for (int u = 0; u < QC; ++u) Y[r * PF + c0 + u] = dp[u];
+      if ((tid & 3) == 0) {
+        const float e = ok ? expf(cs) : 0.f;
+        wl[r] = e;
+        wz[r] = e * ddw[(bh * nblk + blk) * BLK + r];
+      }
+    }
+    __syncthreads();
+    const float eT = expf(T);
+#pragma unroll
+    for (int nt = 0; nt < NTD; ++nt) run[nt] = eT * run[nt];
+    mm_strip<NTD, BLK>(run, 16 * wave, n, gq,
+                       [&](int m, int t) { return X[t * PF + m] * X[t * PF + a] * wl[t]; },
+                       [&](int t, int c) { return Y[t * PF + c]; });
     float az = 0.f;
 #pragma unroll
     for (int t = 16 * gq; t < 16 * gq + 16; ++t) az += X[t * PF + 16 * wave + n] * X[t * PF + a] * wz[t];
     az = sum_over_groups(az);
-    if (gq == 0) o[(int64_t)DH * DH * DH + a * DH + 16 * wave + n] = az;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// k_bwd_scan: the scans over the blocks of a head for any slot size E, one
-// entry per thread.  REV false (forward states): slot c <- the running sum
-// before c, then run = e^{T_c} run + slot c.  REV true (state gradients):
-// the same from the last block down.
-// ---------------------------------------------------------------------------
-template <bool REV>
-__global__ __launch_bounds__(256) void k_bwd_scan(int64_t nblk, int64_t E, int64_t eblocks,
-                                                  const float* __restrict__ tb,
-                                                  float* __restrict__ state) {
-  const int64_t bh = blockIdx.x / eblocks;
-  const int64_t e = (blockIdx.x - bh * eblocks) * 256 + threadIdx.x;
-  if (e >= E) return;
-  float* p = state + bh * nblk * E + e;
-  const float* t = tb + bh * nblk;
-  float run = 0.f;
-  constexpr int U = 16;
-  int64_t done = 0;
-  for (; done + U <= nblk; done += U) {
-    float d[U], T[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = REV ? nblk - 1 - (done + u) : done + u;
-      d[u] = p[c * E];
-      T[u] = t[c];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int64_t c = REV ? nblk - 1 - (done + u) : done + u;
-      p[c * E] = run;
-      run = expf(T[u]) * run + d[u];
-    }
-  }
-  for (; done < nblk; ++done) {
-    const int64_t c = REV ? nblk - 1 - done : done;
-    const float d = p[c * E];
-    p[c * E] = run;
-    run = expf(t[c]) * run + d;
+    runz = eT * runz + az;
+    __syncthreads();
   }
 }
 
@@ -917,27 +895,24 @@ static hipError_t bwd_o2(const void* q, const void* k, const void* v, const floa
                          int64_t BH, int64_t N, int64_t chunk, float* dq, float* dk, float* dv,
                          float* ddt, float* da, const BwdLayout& L, float* ws, hipStream_t stream) {
   using St = uint16_t;
-  constexpr int DH = 64, AS = 4;
+  constexpr int DH = 64;
   const int64_t nb = n_blocks(N);
   const dim3 grid((unsigned)(BH * nb)), blk(256);
   const St* qs = static_cast<const St*>(q);
   const St* ks = static_cast<const St*>(k);
   const St* vs = static_cast<const St*>(v);
-  float* tb = ws + L.tb;
   float* sst = ws + L.sst;
   float* gst = ws + L.gst;
   float* dnw = ws + L.dnum;
   float* ddw = ws + L.dden;
-  const int64_t E = (int64_t)DH * DH * DH + DH * DH;
-  const int64_t eblocks = (E + 255) / 256;
-  hipLaunchKernelGGL((k_bwd_phi_outer<St, 0, AS>), dim3((unsigned)(BH * nb * AS)), blk, 0, stream, ks, vs,
-                     dt, nullptr, nullptr, nullptr, a_cs, N, chunk, nb, tb, sst, nullptr, nullptr);
-  hipLaunchKernelGGL((k_bwd_phi_outer<St, 1, AS>), dim3((unsigned)(BH * nb * AS)), blk, 0, stream, qs,
-                     nullptr, nullptr, y, den, dy, a_cs, N, chunk, nb, nullptr, gst, dnw, ddw);
-  hipLaunchKernelGGL(k_bwd_scan<false>, dim3((unsigned)(BH * eblocks)), blk, 0, stream, nb, E, eblocks, tb,
-                     sst);
-  hipLaunchKernelGGL(k_bwd_scan<true>, dim3((unsigned)(BH * eblocks)), blk, 0, stream, nb, E, eblocks, tb,
-                     gst);
+  // the states entering each block, and the gradients of the states leaving
+  // them: one workgroup per (head, first feature index), sequential over the
+  // blocks
+  hipLaunchKernelGGL(k_bwd_dnum<DH>, grid, blk, 0, stream, y, den, dy, a_cs, N, chunk, nb, dnw, ddw);
+  hipLaunchKernelGGL((k_bwd_phi_scan<St, 0>), dim3((unsigned)(BH * DH)), blk, 0, stream, ks, vs, dt,
+                     nullptr, nullptr, a_cs, N, chunk, nb, sst);
+  hipLaunchKernelGGL((k_bwd_phi_scan<St, 1>), dim3((unsigned)(BH * DH)), blk, 0, stream, qs, nullptr,
+                     nullptr, dnw, ddw, a_cs, N, chunk, nb, gst);
   hipLaunchKernelGGL((k_bwd_block<St, DH, 2>), grid, blk, 0, stream, qs, ks, vs, dt, a_cs, N, chunk, nb,
                      sst, gst, dnw, ddw, dq, dk, dv, ddt, da);
   return hipGetLastError();

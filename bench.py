@@ -387,7 +387,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="o2_bf16_4k",
-                    choices=list(I.ALL_CONFIGS) + list(I.DECODE_CONFIGS) + ["o2_decode_packed"])
+                    choices=list(I.ALL_CONFIGS) + list(I.DECODE_CONFIGS) + ["o2_decode_packed"]
+                    + ["o1_bf16_2k_backward", "o2_bf16_4k_backward"])
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (64K forward, decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -414,7 +415,10 @@ def main():
     from mamba_ssd_sequence_amd import ssd
     ssd.lib()
 
-    if a.workload in I.ALL_CONFIGS:
+    if a.workload.endswith("_backward"):
+        cfg = I.ALL_CONFIGS[a.workload[:-len("_backward")]]
+        res, inp = bench_backward(cfg, a.steps, a.warmup, dev), None
+    elif a.workload in I.ALL_CONFIGS:
         cfg = I.ALL_CONFIGS[a.workload]
         res, inp = bench_forward(cfg, a.steps, a.warmup, dev)
     else:
@@ -455,7 +459,7 @@ def main():
             f"1 GiB copy {ceilings['torch_copy_1gib_gbs']:.0f} GB/s")
 
     cpu = None
-    if not a.no_cpu_baseline:
+    if not a.no_cpu_baseline and inp is not None:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         if a.workload in I.ALL_CONFIGS:
             cpu = cpu_baseline_forward(cfg, inp)

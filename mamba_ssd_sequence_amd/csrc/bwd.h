@@ -17,8 +17,9 @@ namespace ssd {
 //   gst  [BH, nblk, E]       R_c, r_c, then (in place) the gradient of the
 //                            state leaving each block, G_{c+1} and g_{c+1}
 //   dnum [BH, nblk, 64, d_h] dy / den;  dden [BH, nblk, 64]
+//   gsd  [BH, nblk, 64]      order 2: <G_{c+1}, S_c> + <g_{c+1}, z_c> per state tile
 struct BwdLayout {
-  size_t tb, sst, gst, dnum, dden, total_floats;
+  size_t tb, sst, gst, dnum, dden, gsd, total_floats;
 };
 
 inline BwdLayout bwd_layout(int64_t BH, int64_t N, int64_t DH, int order) {
@@ -33,6 +34,7 @@ inline BwdLayout bwd_layout(int64_t BH, int64_t N, int64_t DH, int order) {
   L.gst = off;  off = up(off + nbk * E);
   L.dnum = off; off = up(off + nbk * 64 * (size_t)DH);
   L.dden = off; off = up(off + nbk * 64);
+  L.gsd = off;  off = up(off + (order == 2 ? nbk * 64 : 0));
   L.total_floats = off;
   return L;
 }

@@ -251,10 +251,12 @@ __global__ __launch_bounds__(256) void k_bwd_phi_scan(const St* __restrict__ xs,
                                                       const float* __restrict__ ddw,
                                                       const float* __restrict__ a_cs, int64_t N,
                                                       int64_t chunk, int64_t nblk,
-                                                      float* __restrict__ out) {
+                                                      float* __restrict__ out,
+                                                      const float* __restrict__ sst,
+                                                      float* __restrict__ gsdp) {
   constexpr int DH = 64, QC = DH / 4, NTD = DH / 16;
   constexpr int64_t E = (int64_t)DH * DH * DH + DH * DH;
-  __shared__ float X[BLK * PF], Y[BLK * PF], wl[BLK], wz[BLK];
+  __shared__ float X[BLK * PF], Y[BLK * PF], wl[BLK], wz[BLK], red[4];
   const int64_t bh = blockIdx.x / DH;
   const int a = (int)(blockIdx.x - bh * DH);
   const int tid = threadIdx.x, r = tid >> 2, c0 = (tid & 3) * QC;
@@ -278,6 +280,19 @@ __global__ __launch_bounds__(256) void k_bwd_phi_scan(const St* __restrict__ xs,
       for (int q4 = 0; q4 < 4; ++q4)
         o[((int64_t)a * DH + 16 * wave + 4 * gq + q4) * DH + 16 * nt + n] = run[nt][q4];
     if (gq == 0) o[(int64_t)DH * DH * DH + a * DH + 16 * wave + n] = runz;
+    if constexpr (MODE == 1) {
+      // <G_{c+1}, S_c> + <g_{c+1}, z_c> over this tile, for the block's dT
+      const float* so = sst + (bh * nblk + blk) * E;
+      float d = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NTD; ++nt)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          d += run[nt][q4] * so[((int64_t)a * DH + 16 * wave + 4 * gq + q4) * DH + 16 * nt + n];
+      if (gq == 0) d += runz * so[(int64_t)DH * DH * DH + a * DH + 16 * wave + n];
+      for (int off = 1; off < WAVE; off <<= 1) d += __shfl_xor(d, off, WAVE);
+      if (lane == 0) red[wave] = d;
+    }
     // stage the block: X = x rows, Y = y rows, per-token weights
     const bool ok = r < nvalid;
     const int64_t rr = row + t0 + (ok ? r : 0);
@@ -306,6 +321,7 @@ __global__ __launch_bounds__(256) void k_bwd_phi_scan(const St* __restrict__ xs,
       }
     }
     __syncthreads();
+    if (MODE == 1 && tid == 0) gsdp[(bh * nblk + blk) * DH + a] = (red[0] + red[1]) + (red[2] + red[3]);
     const float eT = expf(T);
 #pragma unroll
     for (int nt = 0; nt < NTD; ++nt) run[nt] = eT * run[nt];
@@ -379,6 +395,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                                                    int64_t chunk, int64_t nblk,
                                                    const float* __restrict__ sst,
                                                    const float* __restrict__ gst,
+                                                   const float* __restrict__ gsdp,
                                                    const float* __restrict__ dnw,
                                                    const float* __restrict__ ddw,
                                                    float* __restrict__ dq, float* __restrict__ dk,
@@ -671,7 +688,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
 #pragma unroll
         for (int u = 0; u < DH * DH / 256; ++u) pre[u] = gs[toff + DH * DH + tid + 256 * u];
       }
-      for (int e = tid; e < DH * DH; e += 256) gsd += X0[(e / DH) * PF + (e % DH)] * st[toff + e];
       f32x4 va[NTD];
 #pragma unroll
       for (int nt = 0; nt < NTD; ++nt) va[nt] = zero4();
@@ -721,6 +737,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
       }
       __syncthreads();
     }
+    // <G_{c+1}, S_c> + <g_{c+1}, z_c>: the reverse scan's per-tile parts
+    if (tid < DH) gsd = gsdp[slot * DH + tid];
   }
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
@@ -886,7 +904,7 @@ static hipError_t bwd_o1_typed(const void* q, const void* k, const void* v, cons
   hipLaunchKernelGGL(k_bwd_rev_pass<DH>, dim3((unsigned)(BH * eblocks)), blk, 0, stream, nb, eblocks,
                      tb, gst);
   hipLaunchKernelGGL((k_bwd_block<St, DH, 1>), grid, blk, 0, stream, qs, ks, vs, dt, a_cs, N, chunk, nb,
-                     sst, gst, dnw, ddw, dq, dk, dv, ddt, da);
+                     sst, gst, nullptr, dnw, ddw, dq, dk, dv, ddt, da);
   return hipGetLastError();
 }
 
@@ -909,12 +927,13 @@ static hipError_t bwd_o2(const void* q, const void* k, const void* v, const floa
   // them: one workgroup per (head, first feature index), sequential over the
   // blocks
   hipLaunchKernelGGL(k_bwd_dnum<DH>, grid, blk, 0, stream, y, den, dy, a_cs, N, chunk, nb, dnw, ddw);
+  float* gsdp = ws + L.gsd;
   hipLaunchKernelGGL((k_bwd_phi_scan<St, 0>), dim3((unsigned)(BH * DH)), blk, 0, stream, ks, vs, dt,
-                     nullptr, nullptr, a_cs, N, chunk, nb, sst);
+                     nullptr, nullptr, a_cs, N, chunk, nb, sst, nullptr, nullptr);
   hipLaunchKernelGGL((k_bwd_phi_scan<St, 1>), dim3((unsigned)(BH * DH)), blk, 0, stream, qs, nullptr,
-                     nullptr, dnw, ddw, a_cs, N, chunk, nb, gst);
+                     nullptr, dnw, ddw, a_cs, N, chunk, nb, gst, sst, gsdp);
   hipLaunchKernelGGL((k_bwd_block<St, DH, 2>), grid, blk, 0, stream, qs, ks, vs, dt, a_cs, N, chunk, nb,
-                     sst, gst, dnw, ddw, dq, dk, dv, ddt, da);
+                     sst, gst, gsdp, dnw, ddw, dq, dk, dv, ddt, da);
   return hipGetLastError();
 }
 

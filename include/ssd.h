@@ -273,7 +273,9 @@ ssd_status ssd_state_unpack(const float* state_p, const float* norm_p, int64_t B
  *   da        [B,H,N] f32        out: gradient with respect to the per-token
  *                                log-decay a (A dt, or the A-mask's
  *                                -softplus(A_P)) whose chunk-local cumsum is a_cs
- *   workspace  >= ssd_backward_workspace_size bytes
+ *   workspace  >= ssd_backward_workspace_size bytes (order 1: ~17 KB per
+ *              64-token block and head; order 2: ~2.1 MB per block and head,
+ *              the states and state gradients of every block)
  *
  * Orders and sizes as ssd_forward (order 1: d_h 32 or 64, fp32 or bf16;
  * order 2: d_h 64, bf16); no initial state.  Feed (da, ddt) to

@@ -98,6 +98,38 @@ __device__ __forceinline__ void mm_strip(f32x4 (&acc)[NT], int m0, int n, int gq
   }
 }
 
+// mm_strip over the column tiles nt >= NT0 and the k >= k0 only (k0 a
+// multiple of 4)
+template <int NT0, int NT, int K, class FA, class FB>
+__device__ __forceinline__ void mm_strip_tiles(f32x4 (&acc)[NT], int m0, int n, int gq, int k0, FA A, FB B) {
+#pragma unroll 4
+  for (int kk = k0; kk < K; kk += 4) {
+    const float a = A(m0 + n, kk + gq);
+#pragma unroll
+    for (int nt = NT0; nt < NT; ++nt) acc[nt] = mfma_f32(a, B(kk + gq, 16 * nt + n), acc[nt]);
+  }
+}
+
+// the same with the first column tile nt0 uniform at run time (0 .. 3)
+template <int NT, int K, class FA, class FB>
+__device__ __forceinline__ void mm_strip_from(f32x4 (&acc)[NT], int m0, int n, int gq, int nt0, int k0,
+                                              FA A, FB B) {
+  static_assert(NT == 4, "four column tiles");
+  switch (nt0) {
+    case 0: mm_strip_tiles<0, NT, K>(acc, m0, n, gq, k0, A, B); break;
+    case 1: mm_strip_tiles<1, NT, K>(acc, m0, n, gq, k0, A, B); break;
+    case 2: mm_strip_tiles<2, NT, K>(acc, m0, n, gq, k0, A, B); break;
+    default: mm_strip_tiles<3, NT, K>(acc, m0, n, gq, k0, A, B); break;
+  }
+}
+
+// sum over the 16 lanes n of a lane group (lanes 16 gq .. 16 gq + 15)
+__device__ __forceinline__ float sum16(float x) {
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) x += __shfl_xor(x, off, WAVE);
+  return x;
+}
+
 // sum over the 4 consecutive lanes of a row (lanes 4r .. 4r + 3)
 __device__ __forceinline__ float sum4(float x) {
   x += __shfl_xor(x, 1, WAVE);
@@ -278,16 +310,20 @@ __global__ __launch_bounds__(256) void k_bwd_phi_scan(const St* __restrict__ xs,
     const int nvalid = (int)((N - t0) < BLK ? (N - t0) : BLK);
     const float base = (t0 % chunk == 0) ? 0.f : a_cs[row + t0 - 1];
     const float T = a_cs[row + t0 + nvalid - 1] - base;
-    // the slot of this block gets the running tiles
+    // the slot of this block gets the running tiles: rows (a, b) of the
+    // strips that hold some b >= a only (the state is symmetric in a, b; the
+    // readers take rows b >= a), and every normaliser entry
     float* o = out + (bh * nblk + blk) * E;
 #pragma unroll
     for (int ai = 0; ai < AP; ++ai) {
       const int a = a0 + ai;
+      if (16 * wave + 15 >= a) {
 #pragma unroll
-      for (int nt = 0; nt < NTD; ++nt)
+        for (int nt = 0; nt < NTD; ++nt)
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          o[((int64_t)a * DH + 16 * wave + 4 * gq + q4) * DH + 16 * nt + n] = run[ai][nt][q4];
+          for (int q4 = 0; q4 < 4; ++q4)
+            o[((int64_t)a * DH + 16 * wave + 4 * gq + q4) * DH + 16 * nt + n] = run[ai][nt][q4];
+      }
       if (gq == 0) o[(int64_t)DH * DH * DH + a * DH + 16 * wave + n] = runz[ai];
     }
     if constexpr (MODE == 1) {
@@ -296,13 +332,25 @@ __global__ __launch_bounds__(256) void k_bwd_phi_scan(const St* __restrict__ xs,
 #pragma unroll
       for (int ai = 0; ai < AP; ++ai) {
         const int a = a0 + ai;
+        // each pair (a, b), b > a, stands for (a, b) and (b, a)
         float d = 0.f;
+        if (16 * wave + 15 >= a) {
 #pragma unroll
-        for (int nt = 0; nt < NTD; ++nt)
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int b = 16 * wave + 4 * gq + q4;
+            const float wgt = b > a ? 2.f : (b == a ? 1.f : 0.f);
+            float e = 0.f;
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            d += run[ai][nt][q4] * so[((int64_t)a * DH + 16 * wave + 4 * gq + q4) * DH + 16 * nt + n];
-        if (gq == 0) d += runz[ai] * so[(int64_t)DH * DH * DH + a * DH + 16 * wave + n];
+            for (int nt = 0; nt < NTD; ++nt)
+              e += run[ai][nt][q4] * so[((int64_t)a * DH + b) * DH + 16 * nt + n];
+            d += wgt * e;
+          }
+        }
+        if (gq == 0) {
+          const int b = 16 * wave + n;
+          const float wgt = b > a ? 2.f : (b == a ? 1.f : 0.f);
+          d += wgt * runz[ai] * so[(int64_t)DH * DH * DH + a * DH + b];
+        }
         for (int off = 1; off < WAVE; off <<= 1) d += __shfl_xor(d, off, WAVE);
         if (lane == 0) red[ai][wave] = d;
       }
@@ -343,9 +391,10 @@ __global__ __launch_bounds__(256) void k_bwd_phi_scan(const St* __restrict__ xs,
       const int a = a0 + ai;
 #pragma unroll
       for (int nt = 0; nt < NTD; ++nt) run[ai][nt] = eT * run[ai][nt];
-      mm_strip<NTD, BLK>(run[ai], 16 * wave, n, gq,
-                         [&](int m, int t) { return X[t * PF + m] * X[t * PF + a] * wl[t]; },
-                         [&](int t, int c) { return Y[t * PF + c]; });
+      if (16 * wave + 15 >= a)  // strips entirely below a are never read
+        mm_strip<NTD, BLK>(run[ai], 16 * wave, n, gq,
+                           [&](int m, int t) { return X[t * PF + m] * X[t * PF + a] * wl[t]; },
+                           [&](int t, int c) { return Y[t * PF + c]; });
       float az = 0.f;
 #pragma unroll
       for (int t = 16 * gq; t < 16 * gq + 16; ++t) az += X[t * PF + 16 * wave + n] * X[t * PF + a] * wz[t];
@@ -549,10 +598,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     // and dcs_i += e_i q_i^T U_i q_i; the normaliser adds 2 e_i dden_i Z q_i
     // and e_i dden_i q_i^T Z q_i (Z = z_c as a d_h x d_h matrix).  One state
     // tile a (rows (a, 0 .. 63)) per pass: X1 = tile a, X2 = dnum, X0 = Q.
-    // the next tile's loads are issued before this tile's product
+    // Only the rows b >= a of tile a are used (U_i is symmetric): tile a
+    // adds 2 e_i sum_{b >= a} U_i[a][b] q_ib to dq_ia and 2 e_i U_i[a][b] q_ia to
+    // dq_ib (b > a), and e_i q_ia (U_i[a][a] q_ia + 2 sum_{b > a} U_i[a][b] q_ib)
+    // to dcs_i.  The next tile's rows are loaded during this tile's product.
     float pre[DH * DH / 256];
+    auto load_pre = [&](int an) {  // tile an (an == DH: Z, all rows)
+      const int rmin = an < DH ? 16 * (an >> 4) : 0;
 #pragma unroll
-    for (int u = 0; u < DH * DH / 256; ++u) pre[u] = st[tid + 256 * u];
+      for (int u = 0; u < DH * DH / 256; ++u) {
+        const int e = tid + 256 * u;  // row e / DH = 4 u + wave: uniform in the wave
+        if (e / DH >= rmin) pre[u] = st[(int64_t)an * DH * DH + e];
+      }
+    };
+    load_pre(0);
     for (int a = 0; a <= DH; ++a) {
       // a < DH: tile a of S_c; a == DH: Z
 #pragma unroll
@@ -561,30 +620,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         X1[(e / DH) * PF + (e % DH)] = pre[u];
       }
       __syncthreads();
-      if (a < DH) {  // a + 1 == DH: Z
-#pragma unroll
-        for (int u = 0; u < DH * DH / 256; ++u) pre[u] = st[(int64_t)(a + 1) * DH * DH + tid + 256 * u];
-      }
+      if (a < DH) load_pre(a + 1);
       f32x4 ta[NTD];
 #pragma unroll
       for (int nt = 0; nt < NTD; ++nt) ta[nt] = zero4();
-      if (a < DH) {  // T[i][b] = U_i[a][b]
-        mm_strip<NTD, DH>(ta, 16 * wave, n, gq, [&](int m, int c) { return X2[m * PF + c]; },
-                          [&](int c, int b) { return X1[b * PF + c]; });
+      if (a < DH) {  // T[i][b] = U_i[a][b], column tiles holding some b >= a
+        mm_strip_from<NTD, DH>(ta, 16 * wave, n, gq, a >> 4, 0,
+                               [&](int m, int c) { return X2[m * PF + c]; },
+                               [&](int c, int b) { return X1[b * PF + c]; });
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int i = 16 * wave + 4 * gq + q4;
-          float rd = 0.f;  // (U_i q_i)_a
+          const float qa = X0[i * PF + a];
+          float r1 = 0.f, r2 = 0.f;
 #pragma unroll
-          for (int nt = 0; nt < NTD; ++nt) rd += ta[nt][q4] * X0[i * PF + 16 * nt + n];
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) rd += __shfl_xor(rd, off, WAVE);
+          for (int nt = 0; nt < NTD; ++nt) {
+            const int b = 16 * nt + n;
+            const float tq = ta[nt][q4] * X0[i * PF + b];
+            if (b >= a) r1 += tq;
+            r2 += b > a ? 2.f * tq : (b == a ? tq : 0.f);
+            if (b > a) dqo[nt][q4] += 2.f * eir[q4] * qa * ta[nt][q4];
+          }
+          r1 = sum16(r1);
+          r2 = sum16(r2);
           if (n == (a & 15)) {
 #pragma unroll
             for (int nt = 0; nt < NTD; ++nt)
-              if (nt == (a >> 4)) dqo[nt][q4] += 2.f * eir[q4] * rd;
+              if (nt == (a >> 4)) dqo[nt][q4] += 2.f * eir[q4] * r1;
           }
-          if (n == 0) dci[q4] += eir[q4] * X0[i * PF + a] * rd;  // reduced over n below
+          if (n == 0) dci[q4] += eir[q4] * qa * r2;  // reduced over n below
         }
       } else {  // (Q Z)[i][a']
         mm_strip<NTD, DH>(ta, 16 * wave, n, gq, [&](int m, int b) { return X0[m * PF + b]; },
@@ -691,51 +755,67 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     for (int e = tid; e < DH * DH; e += 256) gsd += X0[(e / DH) * PF + (e % DH)] * st[e];
     if (tid < DH) gsd += gl[tid] * zl[tid];
   } else {
-    float pre[DH * DH / 256];  // the next tile of G, loaded during this tile's products
+    // rows b >= a of each tile, as in phase 3; the next tile's rows are
+    // loaded during this tile's products
+    float pre[DH * DH / 256];
+    auto load_pre = [&](int an) {  // tile an (an == DH: g, all rows)
+      const int rmin = an < DH ? 16 * (an >> 4) : 0;
 #pragma unroll
-    for (int u = 0; u < DH * DH / 256; ++u) pre[u] = gs[tid + 256 * u];
+      for (int u = 0; u < DH * DH / 256; ++u) {
+        const int e = tid + 256 * u;
+        if (e / DH >= rmin) pre[u] = gs[(int64_t)an * DH * DH + e];
+      }
+    };
+    load_pre(0);
     for (int a = 0; a <= DH; ++a) {
       // a < DH: tile a of G; a == DH: g (as a d_h x d_h matrix)
-      const int64_t toff = (int64_t)a * DH * DH;  // a == DH: the normaliser part
 #pragma unroll
       for (int u = 0; u < DH * DH / 256; ++u) {
         const int e = tid + 256 * u;
         X0[(e / DH) * PF + (e % DH)] = pre[u];
       }
       __syncthreads();
-      if (a < DH) {
-#pragma unroll
-        for (int u = 0; u < DH * DH / 256; ++u) pre[u] = gs[toff + DH * DH + tid + 256 * u];
-      }
+      if (a < DH) load_pre(a + 1);
       f32x4 va[NTD];
 #pragma unroll
       for (int nt = 0; nt < NTD; ++nt) va[nt] = zero4();
       if (a < DH) {
-        // V[j][b] = V_j[a][b]; (V_j k_j)_a
-        mm_strip<NTD, DH>(va, 16 * wave, n, gq, [&](int m, int c) { return X1[m * PF + c] * dtl[m]; },
-                          [&](int c, int b) { return X0[b * PF + c]; });
+        // V[j][b] = V_j[a][b] for b >= a
+        mm_strip_from<NTD, DH>(va, 16 * wave, n, gq, a >> 4, 0,
+                               [&](int m, int c) { return X1[m * PF + c] * dtl[m]; },
+                               [&](int c, int b) { return X0[b * PF + c]; });
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int j = 16 * wave + 4 * gq + q4;
-          float rd = 0.f;
+          const float ka = X2[j * PF + a];
+          float r1 = 0.f, r2 = 0.f;
 #pragma unroll
-          for (int nt = 0; nt < NTD; ++nt) rd += va[nt][q4] * X2[j * PF + 16 * nt + n];
-#pragma unroll
-          for (int off = 1; off < 16; off <<= 1) rd += __shfl_xor(rd, off, WAVE);
+          for (int nt = 0; nt < NTD; ++nt) {
+            const int b = 16 * nt + n;
+            const float vk = va[nt][q4] * X2[j * PF + b];
+            if (b >= a) r1 += vk;
+            r2 += b > a ? 2.f * vk : (b == a ? vk : 0.f);
+            if (b > a) dka[nt][q4] += 2.f * wjr[q4] * ka * va[nt][q4];
+          }
+          r1 = sum16(r1);
+          r2 = sum16(r2);
           if (n == (a & 15)) {
 #pragma unroll
             for (int nt = 0; nt < NTD; ++nt)
-              if (nt == (a >> 4)) dka[nt][q4] += 2.f * wjr[q4] * rd;
+              if (nt == (a >> 4)) dka[nt][q4] += 2.f * wjr[q4] * r1;
           }
-          if (n == 0) kt[q4] += X2[j * PF + a] * rd;  // reduced over n below
+          if (n == 0) kt[q4] += ka * r2;  // reduced over n below
         }
-        // dvop_j += w_j sum_b k_ja k_jb G[(a, b)]
+        // dvop_j += w_j sum_{b >= a} (2 if b > a) k_ja k_jb G[(a, b)]
         f32x4 pa[NTD];
 #pragma unroll
         for (int nt = 0; nt < NTD; ++nt) pa[nt] = zero4();
-        mm_strip<NTD, DH>(pa, 16 * wave, n, gq,
-                          [&](int m, int b) { return X2[m * PF + b] * X2[m * PF + a]; },
-                          [&](int b, int c) { return X0[b * PF + c]; });
+        mm_strip_from<NTD, DH>(pa, 16 * wave, n, gq, 0, a & ~3,
+                               [&](int m, int b) {
+                                 const float w = b > a ? 2.f : (b == a ? 1.f : 0.f);
+                                 return w * X2[m * PF + b] * X2[m * PF + a];
+                               },
+                               [&](int b, int c) { return X0[b * PF + c]; });
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4)
 #pragma unroll

@@ -13,7 +13,9 @@
  * forward pass), the decay and causal masks of Algorithms 4 and 5, the
  * squared scores of 2Mamba at order 2 (Algorithm 5) and the row-sum
  * normaliser of Algorithm 1.  The recurrent decode step is the order-p
- * state update of Algorithm 6 (2Mamba inference).
+ * state update of Algorithm 6 (2Mamba inference).  The backward pass (for
+ * training; not printed on the pages) is the chain rule through the same
+ * definitions.
  *
  * Conventions shared by every entry point
  * ---------------------------------------

@@ -10,6 +10,8 @@ call fails, an exception is raised.
     y = decode_step(q, k, v, dt_proj, dt_bias, A_log, state, norm_state, order=2)
     y = decode_step_amask(q, k, v, A_proj, dt_proj, state, norm_state, order=2)
     state_p, norm_p = state_pack(state, norm_state)
+    dq, dk, dv, ddt, da = backward(q, k, v, dt, a_cs, y, den, dy, order=2, chunk=64)
+    d_dt_proj, d_dt_bias, d_A_log = prep_backward(dt_proj, dt_bias, A_log, da, ddt)
 """
 from __future__ import annotations
 

@@ -30,7 +30,10 @@
 //   block start); dv = dvop dt, ddt = sum_c dvop_c v_c.
 //
 // Everything is computed in fp32 (the inputs are exact in fp32); the block
-// products run on the fp32 matrix cores (v_mfma_f32_16x16x4_f32).  Kernels:
+// products run on the bf16 matrix cores with every fp32 operand split into
+// a high and a low bf16 part (mm_strip_tiles: at most 3 2^-16 of each
+// product's magnitude, against 2^-24 for fp32 arithmetic, and 3 bf16 MFMAs in
+// place of 8 fp32 ones per 32 k).  Kernels:
 //   k_bwd_outer  (x2)  per block, sum_i wgt_i x_i y_i^T and sum_i wgt_i zw_i x_i:
 //                      the block's state increment (forward states, recomputed)
 //                      and R_c, r_c; the latter also writes dnum and dden
@@ -85,29 +88,48 @@ __device__ __forceinline__ void load_row(const St* p, const BlockGeo& g, int r, 
   }
 }
 
-// acc[nt] += (16-row strip of A starting at m0) x (column tile nt of B) on
-// fp32 MFMA (16x16x4): lane (n, gq) supplies A[m0 + n][k + gq] and
-// B[k + gq][16 nt + n]; acc[nt][q4] = out[m0 + 4 gq + q4][16 nt + n].
-template <int NT, int K, class FA, class FB>
-__device__ __forceinline__ void mm_strip(f32x4 (&acc)[NT], int m0, int n, int gq, FA A, FB B) {
-#pragma unroll 4
-  for (int kk = 0; kk < K; kk += 4) {
-    const float a = A(m0 + n, kk + gq);
+// An fp32 value as a high bf16 part (rounded to nearest) and a low bf16 part
+// (the rounded remainder): x = hi + lo within 2^-16 |x|.
+__device__ __forceinline__ void split_bf16(float x, bf16x8& hi, bf16x8& lo, int e) {
+  const __bf16 h = (__bf16)x;
+  hi[e] = h;
+  lo[e] = (__bf16)(x - (float)h);
+}
+
+// acc[nt] += (16-row strip of A starting at m0) x (column tile nt of B), for
+// the column tiles nt >= NT0 and k from k0 rounded down to a multiple of 32
+// (the accessors must give zero products below k0).  fp32 operands on the
+// bf16 matrix cores (v_mfma_f32_16x16x32_bf16): each operand split into high
+// and low parts, three products hi*hi + lo*hi + hi*lo, fp32 accumulation;
+// the dropped lo*lo and the rounding of the low parts leave at most 3 2^-16
+// of each product |a_k b_k|.  Lane (n, gq) supplies A[m0 + n][k] and B[k][16 nt
+// + n] for k = kk + gq + 4 e in its operand slot e (the same slots for both
+// operands, so each k is summed once); acc[nt][q4] = out[m0 + 4 gq + q4][16 nt
+// + n] as for every 16x16 MFMA.
+template <int NT0, int NT, int K, class FA, class FB>
+__device__ __forceinline__ void mm_strip_tiles(f32x4 (&acc)[NT], int m0, int n, int gq, int k0, FA A, FB B) {
+  static_assert(K % 32 == 0, "k in steps of 32");
+#pragma unroll 1
+  for (int kk = k0 & ~31; kk < K; kk += 32) {
+    bf16x8 ah, al;
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) acc[nt] = mfma_f32(a, B(kk + gq, 16 * nt + n), acc[nt]);
+    for (int e = 0; e < 8; ++e) split_bf16(A(m0 + n, kk + gq + 4 * e), ah, al, e);
+#pragma unroll
+    for (int nt = NT0; nt < NT; ++nt) {
+      bf16x8 bh, bl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) split_bf16(B(kk + gq + 4 * e, 16 * nt + n), bh, bl, e);
+      acc[nt] = mfma_bf16(ah, bh, acc[nt]);
+      acc[nt] = mfma_bf16(al, bh, acc[nt]);
+      acc[nt] = mfma_bf16(ah, bl, acc[nt]);
+    }
   }
 }
 
-// mm_strip over the column tiles nt >= NT0 and the k >= k0 only (k0 a
-// multiple of 4)
-template <int NT0, int NT, int K, class FA, class FB>
-__device__ __forceinline__ void mm_strip_tiles(f32x4 (&acc)[NT], int m0, int n, int gq, int k0, FA A, FB B) {
-#pragma unroll 4
-  for (int kk = k0; kk < K; kk += 4) {
-    const float a = A(m0 + n, kk + gq);
-#pragma unroll
-    for (int nt = NT0; nt < NT; ++nt) acc[nt] = mfma_f32(a, B(kk + gq, 16 * nt + n), acc[nt]);
-  }
+// all column tiles and all k
+template <int NT, int K, class FA, class FB>
+__device__ __forceinline__ void mm_strip(f32x4 (&acc)[NT], int m0, int n, int gq, FA A, FB B) {
+  mm_strip_tiles<0, NT, K>(acc, m0, n, gq, 0, A, B);
 }
 
 // the same with the first column tile nt0 uniform at run time (0 .. 3)
@@ -450,8 +472,8 @@ __global__ __launch_bounds__(256) void k_bwd_rev_pass(int64_t nblk, int eblocks,
 // the pair products (s = Q K^T, dnum vop^T -> W, C = dW D, P = dW W), dq
 // (intra C K + inter), dk (intra C^T Q + state), dvop (intra W^T dnum +
 // state) -> dv and ddt, and dcs (row and column sums of P, the inter and
-// state parts, dT at the last token) -> da.  All products on fp32 MFMA in
-// three LDS buffers that each phase restages; wave w owns rows 16 w ..
+// state parts, dT at the last token) -> da.  All products by mm_strip_tiles
+// (split-bf16 MFMA) from three LDS buffers that each phase restages; wave w owns rows 16 w ..
 // 16 w + 15 of every product, its results at rows 16 w + 4 gq + q4, columns
 // 16 nt + n (gq = lane / 16, n = lane % 16).
 // ---------------------------------------------------------------------------

@@ -792,7 +792,8 @@ BWD = [
 @pytest.mark.parametrize("name,order,B,H,N,chunk,with_dt", BWD)
 def test_backward_small(name, order, B, H, N, chunk, with_dt):
     """Well-conditioned inputs (positive features): every gradient within
-    1e-4 of the largest reference element of its tensor (fp32 arithmetic)."""
+    1e-4 of the largest reference element of its tensor (fp32 arithmetic,
+    products on split-bf16 operands: at most 3 2^-16 of each term)."""
     cfg = I.CONFIGS[name]
     say("backward", name, order, B, H, N, chunk, with_dt)
     res, _ = backward_case(cfg, B, H, N, seed=5 * N + H, positive=True, with_dt=with_dt, chunk=chunk,

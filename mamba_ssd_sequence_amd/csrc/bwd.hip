@@ -473,9 +473,9 @@ __global__ __launch_bounds__(256) void k_bwd_rev_pass(int64_t nblk, int eblocks,
 // (intra C K + inter), dk (intra C^T Q + state), dvop (intra W^T dnum +
 // state) -> dv and ddt, and dcs (row and column sums of P, the inter and
 // state parts, dT at the last token) -> da.  All products by mm_strip_tiles
-// (split-bf16 MFMA) from three LDS buffers that each phase restages; wave w owns rows 16 w ..
-// 16 w + 15 of every product, its results at rows 16 w + 4 gq + q4, columns
-// 16 nt + n (gq = lane / 16, n = lane % 16).
+// (split-bf16 MFMA) from three LDS buffers that each phase restages; wave w
+// owns rows 16 w .. 16 w + 15 of every product, its results at rows 16 w +
+// 4 gq + q4, columns 16 nt + n (gq = lane / 16, n = lane % 16).
 // ---------------------------------------------------------------------------
 template <typename St, int DH, int ORDER>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) void k_bwd_block(const St* __restrict__ q, const St* __restrict__ k,

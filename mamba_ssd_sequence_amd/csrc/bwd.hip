@@ -167,8 +167,8 @@ __device__ __forceinline__ float sum4(float x) {
 // MODE 0 (forward increment): x = k, y = v dt, wgt_j = e^{T - cs_j}, zw = 1;
 // also writes the block total T.  MODE 1 (R_c, r_c): x = q, y = dnum,
 // wgt_i = e^{cs_i}, zw = dden; also writes dnum and dden.
-// Staging: row r = t / 4, a quarter of the columns; the product on fp32
-// MFMA, wave w computing state rows 16 w .. 16 w + 15.
+// Staging: row r = t / 4, a quarter of the columns; the product by mm_strip
+// (split-bf16 MFMA), wave w computing state rows 16 w .. 16 w + 15.
 // ---------------------------------------------------------------------------
 template <typename St, int DH, int MODE>
 __global__ __launch_bounds__(256) void k_bwd_outer(const St* __restrict__ xs, const St* __restrict__ vs,

@@ -176,20 +176,28 @@ def _head_quadratic(q, k, vop, a, order, rows):
         abs_sum = absW.sum(axis=1)
         abs_num = absW @ np.abs(vop)
     else:
+        # the same definition for the requested rows only, a batch of rows at
+        # a time: row i uses the tokens j <= i (mask first, then exponentiate
+        # the kept, non-positive differences)
+        rows = np.asarray(rows, dtype=np.int64)
         R = len(rows)
         dv = vop.shape[1]
         num = np.empty((R, dv))
         den = np.empty(R)
         abs_sum = np.empty(R)
         abs_num = np.empty((R, dv))
-        for r, i in enumerate(rows):
-            g = k[: i + 1] @ q[i]
-            w = (g ** order) * np.exp(cs[i] - cs[: i + 1])
-            num[r] = w @ vop[: i + 1]
-            den[r] = w.sum()
+        avop = np.abs(vop)
+        for r0 in range(0, R, 128):
+            rb = rows[r0:r0 + 128]
+            n = int(rb.max()) + 1
+            g = q[rb] @ k[:n].T
+            keep = np.arange(n)[None, :] <= rb[:, None]
+            w = (g ** order) * np.exp(np.where(keep, cs[rb][:, None] - cs[None, :n], -np.inf))
+            num[r0:r0 + len(rb)] = w @ vop[:n]
+            den[r0:r0 + len(rb)] = w.sum(axis=1)
             aw = np.abs(w)
-            abs_sum[r] = aw.sum()
-            abs_num[r] = aw @ np.abs(vop[: i + 1])
+            abs_sum[r0:r0 + len(rb)] = aw.sum(axis=1)
+            abs_num[r0:r0 + len(rb)] = aw @ avop[:n]
     with np.errstate(divide="ignore", invalid="ignore"):
         kappa = abs_sum / np.abs(den)
         y = num / den[:, None]

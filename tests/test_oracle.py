@@ -54,9 +54,13 @@ def load_golden():
 
 
 @pytest.mark.parametrize("order", [1, 2])
-@pytest.mark.parametrize("name", ["kernel_level_dh1", "order2_state_dh2"])
+@pytest.mark.parametrize("name", ["kernel_level_dh1", "order2_state_dh2", "signed_dh1"])
 def test_golden_kernel_level(name, order):
-    """Algorithms 1, 4, 5 on exact hand-worked values (inclusive A^CS)."""
+    """Algorithms 1, 4, 5 on exact hand-worked values (inclusive A^CS).  Where
+    the fixture gives them, also the parity metric's error scale and the
+    normaliser's condition, worked by hand from their definitions: any factor
+    other than 1 in either (a scale twice or half as large, a dropped term, a
+    missing absolute value on the signed case) fails here."""
     c = load_golden()[name]
     q = np.array(c["q"], float)[None, None]
     k = np.array(c["k"], float)[None, None]
@@ -66,6 +70,13 @@ def test_golden_kernel_level(name, order):
     out = O.forward_quadratic(q, k, vop, a, order)
     np.testing.assert_allclose(out["y"][0, 0], fracs(exp["y"]), rtol=1e-14, atol=1e-14)
     np.testing.assert_allclose(out["den"][0, 0], fracs(exp["den"]), rtol=1e-14)
+    if "scale" in exp:
+        np.testing.assert_allclose(out["scale"][0, 0], fracs(exp["scale"]), rtol=1e-14)
+        np.testing.assert_allclose(out["kappa"][0, 0], fracs(exp["kappa"]), rtol=1e-14)
+        # the sampled-row evaluation gives the same diagnostics
+        rows = O.forward_quadratic(q, k, vop, a, order, rows=np.arange(q.shape[2]))
+        np.testing.assert_allclose(rows["scale"][0, 0], fracs(exp["scale"]), rtol=1e-14)
+        np.testing.assert_allclose(rows["kappa"][0, 0], fracs(exp["kappa"]), rtol=1e-14)
     y, den, S, z = O.forward_recurrent(q, k, vop, a, order)
     np.testing.assert_allclose(y[0, 0], fracs(exp["y"]), rtol=1e-14, atol=1e-14)
     np.testing.assert_allclose(den[0, 0], fracs(exp["den"]), rtol=1e-14)
@@ -117,14 +128,18 @@ def test_quadratic_equals_recurrence(order, N, d):
     np.testing.assert_allclose(z, np.einsum("bhn,bhnd->bhd", w, fk), rtol=1e-10, atol=1e-12)
 
 
-def test_sampled_rows_equal_full():
+@pytest.mark.parametrize("order", [1, 2])
+def test_sampled_rows_equal_full(order):
+    """The sampled-row evaluation (rows taken in batches) equals the full
+    quadratic form on those rows: a few rows, and more rows than one batch in
+    an unsorted order."""
     rng = np.random.default_rng(7)
-    q, k, v, a = rand_case(rng, 1, 2, 200, 4)
-    full = O.forward_quadratic(q, k, v, a, 2)
-    rows = np.array([0, 1, 63, 64, 65, 199])
-    part = O.forward_quadratic(q, k, v, a, 2, rows=rows)
-    for key in ("y", "den", "scale", "kappa"):
-        np.testing.assert_allclose(part[key], full[key][:, :, rows], rtol=1e-12)
+    q, k, v, a = rand_case(rng, 1, 2, 300, 4)
+    full = O.forward_quadratic(q, k, v, a, order)
+    for rows in (np.array([0, 1, 63, 64, 65, 299]), rng.permutation(300)[:200]):
+        part = O.forward_quadratic(q, k, v, a, order, rows=rows)
+        for key in ("y", "den", "scale", "kappa"):
+            np.testing.assert_allclose(part[key], full[key][:, :, rows], rtol=1e-12)
 
 
 # ---------------------------------------------------------------------------
@@ -622,6 +637,24 @@ def test_backward_invariances(order):
     assert abs((k * g["dk"]).sum()) <= 1e-10 * np.abs(k * g["dk"]).sum()
     assert np.abs(g["da"][..., 0]).max() <= 1e-10 * np.abs(g["da"]).max()
     np.testing.assert_allclose(g["dvop"].sum(axis=2), dy.sum(axis=2), rtol=1e-10)
+
+
+@pytest.mark.parametrize("order", [1, 2])
+@pytest.mark.parametrize("case", ["one_token", "two_tokens"])
+def test_golden_backward_error_scale(case, order):
+    """The gradients' error scales (the backward parity metric) against values
+    worked by hand from their definition (tests/golden/hand_worked.json): a
+    scale off by any factor, a dropped term or a row / column sum swapped
+    fails here."""
+    c = load_golden()["backward_error_scale_dh1"][case]
+    col = lambda x: np.array(x, float)[None, None, :, None]
+    q, k, vop, dy = col(c["q"]), col(c["k"]), col(c["vop"]), col(c["dy"])
+    a = np.log(np.array(c.get("exp_a", [0.5] * len(c["q"])), float))[None, None]
+    sc = O.backward_error_scale(q, k, vop, a, order, dy)
+    exp = c["expected"][str(order)]
+    for name in ("dq", "dk", "dvop"):
+        np.testing.assert_allclose(sc[name][0, 0, :, 0], fracs(exp[name]), rtol=1e-14, err_msg=name)
+    np.testing.assert_allclose(sc["da"][0, 0], fracs(exp["da"]), rtol=1e-14)
 
 
 @pytest.mark.parametrize("order", [1, 2])

@@ -314,6 +314,36 @@ def forward_recurrent(q, k, vop, a, order, S0=None, z0=None):
     return y, den, S, z
 
 
+def final_state_closed_form(k, vop, a, order, S0=None, z0=None, block=2048):
+    """The states after the last token, from the recurrence unrolled
+    (Algorithm 6: each step decays the states by e^{a_t} and adds phi(k_t)
+    vop_t^T, phi(k_t)):
+        S_N = e^{A^CS_N} S0 + sum_j e^{A^CS_N - A^CS_j} phi(k_j) vop_j^T,
+        z_N = e^{A^CS_N} z0 + sum_j e^{A^CS_N - A^CS_j} phi(k_j),
+    with A^CS the inclusive cumsum of a (so the decay from token j to the end
+    applies a_{j+1} .. a_N).  Over [B,H,N,.] arrays; the sum is taken over
+    blocks of tokens (phi(k) of one block at a time).
+    Returns (S_N [B,H,D,d_v], z_N [B,H,D])."""
+    k = np.asarray(k, dtype=np.float64)
+    vop = np.asarray(vop, dtype=np.float64)
+    a = np.asarray(a, dtype=np.float64)
+    B, H, N, d = k.shape
+    D = d ** order
+    cs = np.cumsum(a, axis=-1)
+    tot = cs[..., -1] if N else np.zeros((B, H))
+    S = np.zeros((B, H, D, vop.shape[-1])) if S0 is None else np.exp(tot)[..., None, None] * S0
+    z = np.zeros((B, H, D)) if z0 is None else np.exp(tot)[..., None] * z0
+    for b in range(B):
+        for h in range(H):
+            for j0 in range(0, N, block):
+                sl = slice(j0, j0 + block)
+                w = np.exp(tot[b, h] - cs[b, h, sl])
+                fk = features(k[b, h, sl], order) * w[:, None]
+                S[b, h] += fk.T @ vop[b, h, sl]
+                z[b, h] += fk.sum(axis=0)
+    return S, z
+
+
 def decode_step_ref(state, norm_state, q, k, v, dt_proj, dt_bias, A_log, order):
     """One decode step for S sequences x H heads (what ssd_decode_step computes).
 
@@ -344,6 +374,64 @@ def decode_step_amask_ref(state, norm_state, q, k, v, A_proj, dt_proj, order):
         vop = vop * dt[..., None]
     S, z, y, den = recurrent_step(state, norm_state, q, k, vop, a, order)
     return y, S, z, den
+
+
+# ---------------------------------------------------------------------------
+# The short convolution of Algorithm 6 (window 2), one decode step
+#
+# Algorithm 6 forms q^c_t, k^c_t, v^c_t = conv_1d(q_t, k_t, v_t, q_{t-1},
+# k_{t-1}, v_{t-1}, window_size = 2) before the order-2 features.  The pages
+# do not spell conv_1d out; read here as the depthwise causal convolution of
+# the q, k, v channels that Algorithms 3-5 apply over the whole sequence
+# (d_conv = 3 d_ssm channels, Algorithm 2), restricted to one step: per
+# channel, x^c_t = w0 x_{t-1} + w1 x_t (+ a bias), with x_{-1} = 0.
+# Algorithm 6 applies no activation after it; Algorithm 3 applies sigma
+# (SiLU), offered as an option.
+# ---------------------------------------------------------------------------
+
+def silu(x):
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def conv_window2(x, x_prev, w, b=None, act=None):
+    """One step of the window-2 depthwise convolution: x^c = w[..., 0] x_prev
+    + w[..., 1] x (+ b), then SiLU if act == "silu".  x, x_prev: [..., C];
+    w: [C, 2] (broadcast over the leading dims); b: [C] or None."""
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    y = w[..., 0] * np.asarray(x_prev, dtype=np.float64) + w[..., 1] * x
+    if b is not None:
+        y = y + np.asarray(b, dtype=np.float64)
+    if act == "silu":
+        y = silu(y)
+    elif act is not None:
+        raise ValueError("act must be None or 'silu'")
+    return y
+
+
+def decode_step_conv_ref(state, norm_state, conv_state, q, k, v, conv_w, conv_b, act, order,
+                         A_proj=None, dt_proj=None, dt_bias=None, A_log=None):
+    """One decode step of Algorithm 6 with its window-2 convolution.
+
+    conv_state [S,3,H,d_h]: the previous step's raw q, k, v (zero before the
+    first token); conv_w [3,H,d_h,2], conv_b [3,H,d_h] or None; q, k, v
+    [S,H,d_h] this step's raw projections.  The convolved q^c, k^c, v^c then
+    go through the step: with A_proj given, the A-mask as Algorithm 6 prints
+    it (decode_step_amask_ref: a_t = exp(-softplus(A_P)), value v^c, or v^c
+    softplus(dt_P) with dt_proj); else the Mamba-2 discretisation
+    (decode_step_ref with dt_proj, dt_bias, A_log).
+    Returns (y, new_state, new_norm, new_conv_state, den); the new conv state
+    holds this step's raw q, k, v."""
+    cs = np.asarray(conv_state, dtype=np.float64)
+    b = [None] * 3 if conv_b is None else [conv_b[i] for i in range(3)]
+    qc, kc, vc = (conv_window2(x, cs[:, i], conv_w[i], b[i], act) for i, x in enumerate((q, k, v)))
+    if A_proj is not None:
+        y, S, z, den = decode_step_amask_ref(state, norm_state, qc, kc, vc, A_proj, dt_proj, order)
+    else:
+        y, S, z, den = decode_step_ref(state, norm_state, qc, kc, vc, dt_proj, dt_bias, A_log, order)
+    new_cs = np.stack([np.asarray(x, dtype=np.float64) for x in (q, k, v)], axis=1)
+    return y, S, z, new_cs, den
 
 
 # ---------------------------------------------------------------------------

@@ -129,6 +129,26 @@ def test_quadratic_equals_recurrence(order, N, d):
 
 
 @pytest.mark.parametrize("order", [1, 2])
+@pytest.mark.parametrize("N,block", [(1, 4), (37, 8), (130, 64), (130, 1000)])
+def test_final_state_closed_form_equals_recurrence(order, N, block):
+    """The unrolled state (a sum over tokens, taken in blocks) equals the
+    token-by-token recurrence of Algorithm 6, from zero and from an initial
+    state."""
+    rng = np.random.default_rng(40 + N + order)
+    q, k, v, a = rand_case(rng, 2, 2, N, 3, dv=4, a_scale=0.7)
+    _, _, S, z = O.forward_recurrent(q, k, v, a, order)
+    Sc, zc = O.final_state_closed_form(k, v, a, order, block=block)
+    np.testing.assert_allclose(Sc, S, rtol=1e-11, atol=1e-12 * np.abs(S).max())
+    np.testing.assert_allclose(zc, z, rtol=1e-11, atol=1e-12 * np.abs(z).max())
+    S0 = rng.standard_normal(S.shape)
+    z0 = rng.standard_normal(z.shape)
+    _, _, S, z = O.forward_recurrent(q, k, v, a, order, S0=S0, z0=z0)
+    Sc, zc = O.final_state_closed_form(k, v, a, order, S0=S0, z0=z0, block=block)
+    np.testing.assert_allclose(Sc, S, rtol=1e-11, atol=1e-12 * np.abs(S).max())
+    np.testing.assert_allclose(zc, z, rtol=1e-11, atol=1e-12 * np.abs(z).max())
+
+
+@pytest.mark.parametrize("order", [1, 2])
 def test_sampled_rows_equal_full(order):
     """The sampled-row evaluation (rows taken in batches) equals the full
     quadratic form on those rows: a few rows, and more rows than one batch in
@@ -720,3 +740,94 @@ def test_prep_amask_backward_matches_finite_differences():
             num[idx] = (lp - loss(*xs)) / (2 * h)
         np.testing.assert_allclose(g, num, rtol=1e-7, atol=1e-9)
     assert O.prep_amask_backward_ref(A_P, None, da, None)[1] is None
+
+
+# ---------------------------------------------------------------------------
+# Algorithm 6's window-2 convolution on the decode path
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_decode_conv_hand_worked(order):
+    c = load_golden()["decode_conv_dh1"]
+    w = np.array(c["conv_w"], float).reshape(3, 1, 1, 2)
+    b = np.array(c["conv_b"], float).reshape(3, 1, 1)
+    S = np.zeros((1, 1, 1, 1))
+    z = np.zeros((1, 1, 1))
+    cs = np.zeros((1, 3, 1, 1))
+    ys = []
+    for st in c["steps"]:
+        x = [np.full((1, 1, 1), float(st[n])) for n in ("q", "k", "v")]
+        y, S, z, cs, _ = O.decode_step_conv_ref(S, z, cs, *x, w, b, None, order,
+                                                A_proj=np.full((1, 1), c["A_proj"]))
+        ys.append(float(y[0, 0, 0]))
+    exp = c["expected"][str(order)]
+    np.testing.assert_allclose(ys, fracs(exp["y"]), rtol=1e-14)
+    np.testing.assert_allclose(S[0, 0, 0, 0], frac(exp["S_final"]), rtol=1e-14)
+    np.testing.assert_allclose(z[0, 0, 0], frac(exp["z_final"]), rtol=1e-14)
+    np.testing.assert_array_equal(cs[0, :, 0, 0], c["expected"]["conv_state_final"])
+
+
+@pytest.mark.parametrize("order", [1, 2])
+@pytest.mark.parametrize("amask,act,bias", [(True, None, True), (False, "silu", False), (True, "silu", True)])
+def test_decode_conv_steps_equal_sequence_conv_and_forward(order, amask, act, bias):
+    """T decode steps with the convolution, from zero, equal the causal
+    depthwise convolution of the whole sequence (numpy.convolve per channel,
+    zero before the first token; SiLU as x * scipy.special.expit(x)) followed
+    by the masked quadratic form on the convolved q, k, v."""
+    from scipy.special import expit
+    rng = np.random.default_rng(80 + order)
+    Sq, H, d, T = 2, 3, 3, 9
+    raw = [rng.standard_normal((T, Sq, H, d)) for _ in range(3)]
+    w = rng.standard_normal((3, H, d, 2))
+    b = rng.standard_normal((3, H, d)) if bias else None
+    A_P = rng.standard_normal((T, Sq, H)) - 1.0
+    dt_P = rng.standard_normal((T, Sq, H))
+    dt_bias = rng.standard_normal(H) - 2.0
+    A_log = rng.uniform(0, 1, H)
+    D = d ** order
+    S, z = np.zeros((Sq, H, D, d)), np.zeros((Sq, H, D))
+    cs = np.zeros((Sq, 3, H, d))
+    ys = []
+    for t in range(T):
+        kw = dict(A_proj=A_P[t], dt_proj=dt_P[t]) if amask else dict(dt_proj=dt_P[t], dt_bias=dt_bias, A_log=A_log)
+        y, S, z, cs, _ = O.decode_step_conv_ref(S, z, cs, raw[0][t], raw[1][t], raw[2][t], w, b, act, order, **kw)
+        ys.append(y)
+    ys = np.stack(ys, axis=2)  # [S,H,T,d]
+    # the whole sequences convolved channel by channel
+    conv = []
+    for i in range(3):
+        x = np.moveaxis(raw[i], 0, -1)  # [S,H,d,T]
+        out = np.empty_like(x)
+        for idx in np.ndindex(x.shape[:-1]):
+            hh, cc = idx[1], idx[2]
+            out[idx] = np.convolve(x[idx], [w[i, hh, cc, 1], w[i, hh, cc, 0]])[:T]
+            if b is not None:
+                out[idx] += b[i, hh, cc]
+        if act == "silu":
+            out = out * expit(out)
+        conv.append(np.moveaxis(out, -1, 2))  # [S,H,T,d]
+    tr = lambda x: np.moveaxis(x, 0, -1)  # [T,S,H] -> [S,H,T]
+    if amask:
+        fwd = O.forward_amask_ref(*conv, tr(A_P), tr(dt_P), order)
+    else:
+        fwd = O.forward_ref(*conv, tr(dt_P), dt_bias, A_log, order)
+    assert rel_err(ys, fwd["y"], fwd["scale"]) <= 1e-10
+    np.testing.assert_array_equal(cs, np.stack([r[-1] for r in raw], axis=1))
+
+
+def test_decode_conv_identity_is_the_plain_step():
+    """Weights (0, 1), no bias, no activation: the convolution passes the raw
+    q, k, v through, and the step is exactly the plain decode step."""
+    rng = np.random.default_rng(90)
+    Sq, H, d = 2, 2, 4
+    q, k, v = (rng.standard_normal((Sq, H, d)) for _ in range(3))
+    S0, z0 = rng.standard_normal((Sq, H, d * d, d)), rng.uniform(0, 1, (Sq, H, d * d))
+    cs = rng.standard_normal((Sq, 3, H, d))
+    w = np.zeros((3, H, d, 2))
+    w[..., 1] = 1.0
+    A_P = rng.standard_normal((Sq, H))
+    y, S, z, _, _ = O.decode_step_conv_ref(S0, z0, cs, q, k, v, w, None, None, 2, A_proj=A_P)
+    y2, S2, z2, _ = O.decode_step_amask_ref(S0, z0, q, k, v, A_P, None, 2)
+    np.testing.assert_array_equal(y, y2)
+    np.testing.assert_array_equal(S, S2)
+    np.testing.assert_array_equal(z, z2)

@@ -16,8 +16,20 @@ the timed steps record none), against MI355X's published dense bf16 MFMA peak (2
 bandwidth (8 TB/s).  Algorithmic work per launch (see the design notes):
   order-2 numerator state scan: 4 * D * d_h flops per token and head
       (2 D d_h for phi(q)^T S, 2 D d_h for the phi(k) (v dt)^T update),
+  order-1 output kernel: q, k, v, dt, a_cs read and y written per token and
+      head (3 d_h s_in + 8 + 4 d_h bytes); the whole order-1 step is also
+      reported against its algorithmic bytes (3 d_h s_in + 4 + 4 d_h: q, k, v
+      and dt_P read, y written),
   decode step: 2 * 4 * (D * d_h + D) bytes per sequence and head (D = d_h^2 rows,
-      or d_h (d_h + 1) / 2 in the packed layout).
+      or d_h (d_h + 1) / 2 in the packed layout),
+  backward step: 10 D d_h flops per token and head for the state parts (the
+      states and state gradients rebuilt, and the three products with them:
+      dq from S, dk and dv from the state gradient) plus 5 * 2 * 64^2 * d_h
+      per 64-token block for the block-local products, against the bf16 peak
+      (the backward's products run on bf16 matrix cores),
+  prep sweep: 12 bytes per token and head (dt_P read, dt and a_cs written).
+step_mfma_frac (order 2): the whole step against the chunked form's count,
+  n_c [L(L+1)/2 (4 d_h + 2) + 2 (2 L D d_h + 2 L D) + 2 (D d_h + D)] per head.
 cpu_baseline: the fp64 oracle (tests' reference implementation, untuned) on a
 bounded sample of the same workload, on this machine's host cores.
 device_ceilings: what the vendor library reaches on the same GPU (torch's fp16
@@ -47,8 +59,10 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 # version of a kernel is reported only while these files are unchanged
 KERNEL_SOURCES = {
     "k_o2_state": ["fwd_o2_state.hip", "launch.h", "common.h"],
+    "k_o2_blockprep": ["fwd_o2_prep.hip", "launch.h", "common.h"],
     "k_output": ["fwd_blocks.hip", "launch.h", "common.h"],
     "k_decode": ["decode.hip", "launch.h", "common.h"],
+    "k_prep": ["prep.hip", "launch.h", "common.h"],
 }
 
 
@@ -164,19 +178,31 @@ def bench_forward(cfg: I.Config, steps: int, warmup: int, dev, amask: bool = Fal
                            "frac": ach / PEAK_BF16_TFLOPS,
                            "traffic": measured_traffic("k_o2_state", cfg.name),
                            "alg_flops_per_launch": flops, "avg_launch_ms": t_ms}
-        # whole-step MFMA fraction of the method's chunked work (SURVEY-style count)
-        res["step_mfma_frac"] = flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+        # whole-step MFMA fraction of the method's chunked work: every flop of
+        # the chunked form per head, n_c [L(L+1)/2 (4 d_h + 2) + 2 (2 L D d_h +
+        # 2 L D) + 2 (D d_h + D)] with L the chunk, D = d_h^2
+        L = cfg.chunk
+        n_c = -(-N // L)
+        F = B * H * n_c * (L * (L + 1) / 2 * (4 * d + 2) + 2 * (2 * L * D * d + 2 * L * D)
+                           + 2 * (D * d + D))
+        res["step_alg_flops"] = F
+        res["step_mfma_frac"] = F / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
     else:
         es = 2 if cfg.dtype == I.BF16 else 4
-        nb = -(-N // 64)
-        # output kernel: q,k,v + dt + a_cs read, entering states read, y written
-        by = B * H * (N * (3 * d * es + 8 + 4 * d) + nb * (d * d + d) * 4)
+        # output kernel: q, k, v, dt and a_cs read, y written (the entering
+        # states it also reads are the implementation's, not the method's)
+        by = B * H * N * (3 * d * es + 8 + 4 * d)
         t_ms = kern_ms["output"]
         ach = by / (t_ms * 1e-3) / 1e9
         res["roofline"] = {"kernel": "k_output", "bound": "hbm", "achieved": ach,
                            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
                            "traffic": measured_traffic("k_output", cfg.name),
                            "alg_bytes_per_launch": by, "avg_launch_ms": t_ms}
+        # the whole step (prep + forward) against the method's bytes: q, k, v
+        # and dt_P read, y written
+        step_by = B * H * N * (3 * d * es + 4 + 4 * d)
+        res["step_alg_bytes"] = step_by
+        res["step_hbm_frac"] = step_by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS
     return res, inp
 
 
@@ -213,15 +239,58 @@ def bench_backward(cfg: I.Config, steps: int, warmup: int, dev):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
-    # algorithmic bytes: q, k, v read, dt, a_cs, den read, y and dy read
-    # (fp32), dq, dk, dv written (fp32), ddt, da and the prep gradients
+    # algorithmic flops: per token and head 10 D d_h for the state parts (the
+    # states S and state gradients G rebuilt, 2 D d_h each; dq from S dnum,
+    # dk and dv from G, 2 D d_h each), per 64-token block and head five
+    # 64 x 64 x d_h products (scores, dnum vop^T, the scores' gradient times
+    # K and times Q, W^T dnum)
+    D = d ** cfg.order
+    nb = -(-N // 64)
+    flops = B * H * (N * 10.0 * D * d + nb * 5 * 2.0 * 64 * 64 * d)
+    ach = flops / (ms * 1e-3) / 1e12
+    # algorithmic bytes (context): q, k, v read, dt, a_cs, den read, y and dy
+    # read (fp32), dq, dk, dv written (fp32), ddt, da and the prep gradients
     es = 2 if cfg.dtype == I.BF16 else 4
     by = B * H * N * (3 * d * es + 2 * 4 * d + 3 * 4 * d + 4 * 4 + 2 * 4)
-    ach = by / (ms * 1e-3) / 1e9
     return {"workload": cfg.name + "_backward", "ms_per_step": ms, "tokens_per_s": B * N / (ms * 1e-3),
             "B": B, "H": H, "N": N, "d_h": d, "order": cfg.order, "chunk": cfg.chunk,
-            "roofline": {"kernel": "step", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None,
+            "roofline": {"kernel": "step", "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                         "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                         "alg_flops_per_launch": flops, "avg_launch_ms": ms},
+            "alg_bytes": by, "hbm_frac_of_alg_bytes": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+
+
+def bench_prep_sweep(steps: int, warmup: int, dev, B=4, H=32, N=1 << 21, chunk=64):
+    """ssd_prep alone on B * H * N = 2^28 tokens x heads (dt_P from torch's
+    seeded generator on the device), against the HBM peak: 4 bytes read and
+    8 written per token and head."""
+    import torch
+    from mamba_ssd_sequence_amd import ssd
+    g = torch.Generator(device=dev).manual_seed(0)
+    dtp = torch.randn((B, H, N), generator=g, device=dev)
+    bias = torch.full((H,), -3.0, device=dev)
+    alog = torch.zeros((H,), device=dev)
+    nc = -(-N // chunk)
+    out = (torch.empty((B, H, N), device=dev), torch.empty((B, H, N), device=dev),
+           torch.empty((B, H, nc), device=dev))
+    for _ in range(warmup):
+        ssd.prep(dtp, bias, alog, chunk, out=out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        ssd.prep(dtp, bias, alog, chunk, out=out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    by = B * H * N * 12 + B * H * nc * 4
+    ach = by / (ms * 1e-3) / 1e9
+    del dtp, out
+    return {"workload": "prep_sweep_2^28", "ms_per_step": ms, "tokens_per_s": B * N / (ms * 1e-3),
+            "B": B, "H": H, "N": N, "chunk": chunk,
+            "roofline": {"kernel": "k_prep", "bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
+                         "traffic": measured_traffic("k_prep", "prep_sweep_2^28"),
                          "alg_bytes_per_launch": by, "avg_launch_ms": ms}}
 
 
@@ -388,7 +457,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="o2_bf16_4k",
                     choices=list(I.ALL_CONFIGS) + list(I.DECODE_CONFIGS) + ["o2_decode_packed"]
-                    + ["o1_bf16_2k_backward", "o2_bf16_4k_backward"])
+                    + ["o1_bf16_2k_backward", "o2_bf16_4k_backward", "prep_sweep_2^28"])
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (64K forward, decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -415,7 +484,9 @@ def main():
     from mamba_ssd_sequence_amd import ssd
     ssd.lib()
 
-    if a.workload.endswith("_backward"):
+    if a.workload == "prep_sweep_2^28":
+        cfg, res, inp = None, bench_prep_sweep(a.steps, a.warmup, dev), None
+    elif a.workload.endswith("_backward"):
         cfg = I.ALL_CONFIGS[a.workload[:-len("_backward")]]
         res, inp = bench_backward(cfg, a.steps, a.warmup, dev), None
     elif a.workload in I.ALL_CONFIGS:
@@ -432,11 +503,13 @@ def main():
     if not a.no_extra:
         for name in ("o2_bf16_64k", "o1_bf16_2k", "o1_bf16_4k", "o1_bf16_64k", "o2_decode",
                      "o2_decode_packed", "o2_bf16_4k_amask", "o1_bf16_2k_backward",
-                     "o2_bf16_4k_backward"):
+                     "o2_bf16_4k_backward", "prep_sweep_2^28"):
             if name == a.workload:
                 continue
             torch.cuda.empty_cache()
-            if name == "o2_bf16_4k_amask":
+            if name == "prep_sweep_2^28":
+                r = bench_prep_sweep(max(3, a.steps // 4), 2, dev)
+            elif name == "o2_bf16_4k_amask":
                 r, _ = bench_forward(I.CONFIGS["o2_bf16_4k"], a.steps, a.warmup, dev, amask=True)
             elif name in I.ALL_CONFIGS:
                 r, _ = bench_forward(I.ALL_CONFIGS[name], max(3, a.steps // 4), 2, dev)
@@ -488,6 +561,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels_ms": res.get("kernels_ms"),
         "step_mfma_frac": res.get("step_mfma_frac"),
+        "step_hbm_frac": res.get("step_hbm_frac"),
         "extra": extra,
         "device_ceilings": ceilings,
         "device": torch.cuda.get_device_name(dev),

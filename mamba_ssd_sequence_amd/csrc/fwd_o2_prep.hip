@@ -304,8 +304,15 @@ hipError_t launch_o2_blockprep(const void* q, const void* k, const void* v, cons
 // the second block).
 // ---------------------------------------------------------------------------
 namespace {
+// The state's scale exponent keeps max |S| 2^sig in [2^12, 2^13).  Its range
+// is wider than the per-block exponents': the state of a long run of tokens
+// that add nothing (zero keys or values) keeps decaying, and its fp16 copy
+// must follow it down as far as fp32 (the normaliser's arithmetic) reaches.
+// Every use of sig is an fp32 ldexp.
 __device__ __forceinline__ int sig_of(float m) {
-  return (m > 0.f && isfinite(m)) ? clamp64(13 - exp_ceil(m)) : 0;
+  if (!(m > 0.f) || !isfinite(m)) return 0;
+  const int s = 13 - exp_ceil(m);
+  return s < -100 ? -100 : (s > 100 ? 100 : s);
 }
 }  // namespace
 
@@ -384,14 +391,22 @@ __global__ __launch_bounds__(64) void k_o2_scale_scan(uint8_t* __restrict__ rec,
             si[SC_SIG_OUT] = sout;
             sc[SC_ETS] = ets;
             sc[SC_EPRE] = hb ? eA[u] : 1.f;
-            // X 2^xi -> X 2^(sig - 2 kap): exact power-of-two factors (d <= 2
-            // since max X 2^xi >= 2^13; below 2^-48 the terms are negligible
-            // and dropped)
-            const int d = sout - 2 * si[SC_KAP] - si[SC_XI];
+            // X 2^xi -> X 2^(sig - 2 kap): exact power-of-two factors.  When
+            // the block adds to the state (delta > 0), d <= 1: sig keeps the
+            // bound M >= delta = max|k|^2 sum_j max_c |X_jc| below 2^13, kap
+            // puts max|k| 2^kap in [1/2, 1) and xi puts max|X| 2^xi in
+            // [2^13, 2^14); the cap at 15 only guards exponents clamped at
+            // their limits.  A block whose keys or values are all zero
+            // (delta = 0) adds nothing: its factors are 0, so that its X is
+            // never scaled by a factor that overflows fp16.  Below 2^-48
+            // the terms are negligible and dropped.
+            const int d0 = sout - 2 * si[SC_KAP] - si[SC_XI];
+            const int d = d0 > 15 ? 15 : d0;
             const int d1 = d >= -14 ? d : d / 2, d2 = d >= -14 ? 0 : d - d / 2;
+            const bool adds = sc[SC_DELTA] > 0.f;
             h16x2 xf;
-            xf[0] = d < -48 ? (_Float16)0.f : (_Float16)ldexpf(1.f, d1);
-            xf[1] = (_Float16)ldexpf(1.f, d2);
+            xf[0] = (!adds || d < -48) ? (_Float16)0.f : (_Float16)ldexpf(1.f, d1);
+            xf[1] = adds ? (_Float16)ldexpf(1.f, d2) : (_Float16)0.f;
             *reinterpret_cast<h16x2*>(&sc[SC_XF]) = xf;
           }
         }

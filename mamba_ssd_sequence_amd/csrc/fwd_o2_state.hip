@@ -221,16 +221,18 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const float* yr = &yo[st & 1][hb][i * RP];
-      const float f = st_ecs[st % 3][hb][i] * (hb ? p.epre1 : p.epre0) *
-                      ldexpf(ldexpf(1.f, -p.sig_in), -2 * (hb ? p.tau1 : p.tau0));
+      // the power of two is applied last (one ldexp of the product), so that
+      // no intermediate factor leaves the fp32 range
+      const float f = st_ecs[st % 3][hb][i] * (hb ? p.epre1 : p.epre0);
+      const int sh = -p.sig_in - 2 * (hb ? p.tau1 : p.tau0);
       float* dst = &part[(bh * Np + (int64_t)(2 * st + hb) * BLK + i) * DH + c0];
       if constexpr (NAT == 2) {
         float2 o;
-        o.x = yr[2 * q4] * f;
-        o.y = yr[2 * q4 + 1] * f;
+        o.x = ldexpf(yr[2 * q4] * f, sh);
+        o.y = ldexpf(yr[2 * q4 + 1] * f, sh);
         *reinterpret_cast<float2*>(dst + 2 * q4) = o;
       } else {
-        dst[q4] = (yr[2 * q4] + yr[2 * q4 + 1]) * f;
+        dst[q4] = ldexpf((yr[2 * q4] + yr[2 * q4 + 1]) * f, sh);
       }
     }
   };

@@ -41,10 +41,24 @@ def row_error(y_gpu: np.ndarray, y_ref: np.ndarray, scale: np.ndarray) -> float:
     return float(d.max()) if d.size else 0.0
 
 
-def sample_rows(N: int, n_random: int, rng: np.random.Generator, block: int = 64) -> np.ndarray:
-    """First and last block, every block boundary +-1 (up to a cap), and random rows."""
+def sample_rows(N: int, n_random: int, rng: np.random.Generator, block: int = 64,
+                boundaries: bool = True) -> np.ndarray:
+    """First and last `block` rows, every block boundary +-1 over the whole
+    sequence (if `boundaries`), and `n_random` random rows."""
     s = set(range(min(N, block))) | set(range(max(0, N - block), N))
-    for b in range(block, N, block)[:64]:
-        s.update((b - 1, b, b + 1))
+    if boundaries:
+        for b in range(block, N, block):
+            s.update((b - 1, b, b + 1))
     s.update(rng.integers(0, N, size=n_random).tolist())
     return np.array(sorted(x for x in s if 0 <= x < N), dtype=np.int64)
+
+
+def worst(y_gpu: np.ndarray, y_ref: np.ndarray, scale: np.ndarray, rows=None) -> str:
+    """Where the largest scaled error sits: (b, h, token, column) and its value."""
+    d = np.abs(np.asarray(y_gpu, np.float64) - y_ref) / scale
+    if d.size == 0:
+        return "empty"
+    d = np.where(np.isfinite(d), d, np.inf)
+    b, h, r, c = np.unravel_index(int(np.argmax(d)), d.shape)
+    tok = r if rows is None else int(rows[r])
+    return f"max err {d[b, h, r, c]:.3e} at (b={b}, h={h}, token={tok}, col={c})"

@@ -175,6 +175,10 @@ def _head_quadratic(q, k, vop, a, order, rows):
         absW = np.abs(W)
         abs_sum = absW.sum(axis=1)
         abs_num = absW @ np.abs(vop)
+        # the state form's magnitudes: (sum_a |q_ia||k_ja|)^p in place of |q_i . k_j|^p
+        Wst = (np.abs(q) @ np.abs(k).T) ** order * decay
+        st_sum = Wst.sum(axis=1)
+        st_num = Wst @ np.abs(vop)
     else:
         # the same definition for the requested rows only, a batch of rows at
         # a time: row i uses the tokens j <= i (mask first, then exponentiate
@@ -186,25 +190,36 @@ def _head_quadratic(q, k, vop, a, order, rows):
         den = np.empty(R)
         abs_sum = np.empty(R)
         abs_num = np.empty((R, dv))
-        avop = np.abs(vop)
+        st_sum = np.empty(R)
+        st_num = np.empty((R, dv))
+        avop, aq, ak = np.abs(vop), np.abs(q), np.abs(k)
         for r0 in range(0, R, 128):
             rb = rows[r0:r0 + 128]
             n = int(rb.max()) + 1
             g = q[rb] @ k[:n].T
             keep = np.arange(n)[None, :] <= rb[:, None]
-            w = (g ** order) * np.exp(np.where(keep, cs[rb][:, None] - cs[None, :n], -np.inf))
+            decay = np.exp(np.where(keep, cs[rb][:, None] - cs[None, :n], -np.inf))
+            w = (g ** order) * decay
             num[r0:r0 + len(rb)] = w @ vop[:n]
             den[r0:r0 + len(rb)] = w.sum(axis=1)
             aw = np.abs(w)
             abs_sum[r0:r0 + len(rb)] = aw.sum(axis=1)
             abs_num[r0:r0 + len(rb)] = aw @ avop[:n]
+            wst = (aq[rb] @ ak[:n].T) ** order * decay
+            st_sum[r0:r0 + len(rb)] = wst.sum(axis=1)
+            st_num[r0:r0 + len(rb)] = wst @ avop[:n]
     with np.errstate(divide="ignore", invalid="ignore"):
         kappa = abs_sum / np.abs(den)
         y = num / den[:, None]
         # first-order rounding bound of a quotient of two sums:
         # |d(n/d)| <= (|dn| + |n/d| |dd|) / |d|, |dn| <= eps sum|w||v|, |dd| <= eps sum|w|
         scale = (abs_num + np.abs(y) * abs_sum[:, None]) / np.abs(den)[:, None]
-    return num, den, kappa, scale
+        # the same bound for the state form (Algorithm 6), y = phi(q)^T S /
+        # phi(q)^T z with S, z sums over tokens of phi(k) terms: its sums run
+        # over the D feature products q_a.. k_a.., so their rounding is
+        # bounded by (sum_a |q_ia||k_ja|)^p per token instead of |q_i . k_j|^p
+        scale_state = (st_num + np.abs(y) * st_sum[:, None]) / np.abs(den)[:, None]
+    return num, den, kappa, scale, scale_state
 
 
 def forward_quadratic(q, k, vop, a, order, rows=None):
@@ -220,6 +235,11 @@ def forward_quadratic(q, k, vop, a, order, rows=None):
     the first-order rounding-error bound of y_ic = num_ic / den_i divided by
     the unit roundoff: a floating-point evaluation of y_ic with relative
     accuracy eps in its sums is off by at most about eps * scale[i, c].
+    scale_state[i, c]: the same bound for an evaluation through the states of
+    Algorithm 6 (y = phi(q)^T S / phi(q)^T z), whose sums run over the
+    feature products: (sum_a |q_ia||k_ja|)^order replaces |q_i . k_j|^order.
+    It equals scale when no feature product cancels (d_h = 1, or q and k
+    with equal signs per component).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -231,13 +251,15 @@ def forward_quadratic(q, k, vop, a, order, rows=None):
     out = {n: np.empty((B, H, R, dv)) for n in ("num",)}
     out.update({n: np.empty((B, H, R)) for n in ("den", "kappa")})
     out["scale"] = np.empty((B, H, R, dv))
+    out["scale_state"] = np.empty((B, H, R, dv))
     for b in range(B):
         for h in range(H):
-            num, den, kap, sc = _head_quadratic(q[b, h], k[b, h], vop[b, h], a[b, h], order, rows)
+            num, den, kap, sc, scs = _head_quadratic(q[b, h], k[b, h], vop[b, h], a[b, h], order, rows)
             out["num"][b, h] = num
             out["den"][b, h] = den
             out["kappa"][b, h] = kap
             out["scale"][b, h] = sc
+            out["scale_state"][b, h] = scs
     with np.errstate(divide="ignore", invalid="ignore"):
         out["y"] = out["num"] / out["den"][..., None]
     return out

@@ -11,6 +11,11 @@ unit roundoff, so eps-accurate sums give err ~ eps on every row, including the
 order-1 rows whose normaliser nearly cancels (there |y| and sum|w|/|den| are
 both large).  At order 2 all weights are >= 0 and scale is the weighted mean of
 |vop| plus |y|, i.e. a relative error on every row.
+
+The decode step evaluates the state form of Algorithm 6, y = phi(q)^T S /
+phi(q)^T z, whose sums run over the feature products; its tests use the
+oracle's scale_state, the same bound with (sum_a |q_ia||k_ja|)^p in place of
+|q_i . k_j|^p (equal to scale when no feature product cancels).
 """
 from __future__ import annotations
 

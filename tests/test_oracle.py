@@ -54,7 +54,7 @@ def load_golden():
 
 
 @pytest.mark.parametrize("order", [1, 2])
-@pytest.mark.parametrize("name", ["kernel_level_dh1", "order2_state_dh2", "signed_dh1"])
+@pytest.mark.parametrize("name", ["kernel_level_dh1", "order2_state_dh2", "signed_dh1", "signed_dh2_state_scale"])
 def test_golden_kernel_level(name, order):
     """Algorithms 1, 4, 5 on exact hand-worked values (inclusive A^CS).  Where
     the fixture gives them, also the parity metric's error scale and the
@@ -77,6 +77,12 @@ def test_golden_kernel_level(name, order):
         rows = O.forward_quadratic(q, k, vop, a, order, rows=np.arange(q.shape[2]))
         np.testing.assert_allclose(rows["scale"][0, 0], fracs(exp["scale"]), rtol=1e-14)
         np.testing.assert_allclose(rows["kappa"][0, 0], fracs(exp["kappa"]), rtol=1e-14)
+    if "scale_state" in exp:
+        for o in (out, O.forward_quadratic(q, k, vop, a, order, rows=np.arange(q.shape[2]))):
+            np.testing.assert_allclose(o["scale_state"][0, 0], fracs(exp["scale_state"]), rtol=1e-14)
+    if q.shape[-1] == 1 or (np.all(q >= 0) and np.all(k >= 0)):
+        # no feature product can cancel: the state form's scale is the scale
+        np.testing.assert_allclose(out["scale_state"], out["scale"], rtol=1e-14)
     y, den, S, z = O.forward_recurrent(q, k, vop, a, order)
     np.testing.assert_allclose(y[0, 0], fracs(exp["y"]), rtol=1e-14, atol=1e-14)
     np.testing.assert_allclose(den[0, 0], fracs(exp["den"]), rtol=1e-14)
@@ -375,6 +381,34 @@ def test_error_scale_bounds_an_fp32_evaluation(order):
     assert err.max() <= 1e-5
     if order == 1:
         assert ref["kappa"].max() > 50  # the case really contains ill-conditioned rows
+
+
+@pytest.mark.parametrize("order", [1, 2])
+def test_state_scale_bounds_an_fp32_recurrent_evaluation(order):
+    """An fp32 evaluation through Algorithm 6's states (S, z updated token by
+    token, y = phi(q)^T S / phi(q)^T z, every operation rounded to fp32)
+    stays within a small multiple of fp32's unit roundoff times scale_state on
+    every element (scale_state >= scale everywhere; the hand-worked fixture
+    signed_dh2_state_scale pins its value)."""
+    rng = np.random.default_rng(16)
+    q, k, v, a = rand_case(rng, 1, 2, 120, 6, a_scale=0.3)
+    ref = O.forward_quadratic(q, k, v, a, order)
+    D = 6 ** order
+    S = np.zeros((2, D, 6), np.float32)
+    z = np.zeros((2, D), np.float32)
+    y32 = np.empty((2, 120, 6))
+    for t in range(120):
+        al = np.exp(a[0, :, t]).astype(np.float32)
+        fk = O.features(k[0, :, t], order).astype(np.float32)
+        fq = O.features(q[0, :, t], order).astype(np.float32)
+        S = (al[:, None, None] * S + fk[:, :, None] * v[0, :, t].astype(np.float32)[:, None, :]).astype(np.float32)
+        z = (al[:, None] * z + fk).astype(np.float32)
+        num = np.einsum("hr,hrc->hc", fq, S).astype(np.float32)
+        den = np.einsum("hr,hr->h", fq, z).astype(np.float32)
+        y32[:, t] = num / den[:, None]
+    eps = 2.0 ** -24
+    assert (np.abs(y32 - ref["y"][0]) / ref["scale_state"][0]).max() <= 64 * eps
+    assert np.all(ref["scale_state"] >= ref["scale"] * (1 - 1e-12))
 
 
 # ---------------------------------------------------------------------------

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SSD_ABI_VERSION 5
+#define SSD_ABI_VERSION 6
 
 typedef enum {
   SSD_OK = 0,
@@ -233,6 +233,43 @@ ssd_status ssd_decode_step_amask(const void* q, const void* k, const void* v,
                                  const float* A_proj, const float* dt_proj, int64_t S,
                                  int64_t H, int64_t d_h, int order, int dtype, int layout,
                                  float* state, float* norm_state, float* y, hipStream_t stream);
+
+/*
+ * ssd_decode_step_conv -- the decode step with Algorithm 6's short
+ * convolution in front of it: q^c_t, k^c_t, v^c_t = conv_1d(q_t, k_t, v_t,
+ * q_{t-1}, k_{t-1}, v_{t-1}, window_size = 2).  The pages name conv_1d
+ * without spelling it out; it is taken as the depthwise causal convolution
+ * of the q, k, v channels (the d_conv = 3 d_ssm channels of Algorithm 2) that
+ * Algorithms 3-5 apply over a whole sequence, one step of it:
+ *     x^c = conv_w[.., 0] x_{t-1} + conv_w[.., 1] x_t (+ conv_b), per channel,
+ * then SiLU if conv_act = 1 (Algorithm 3 applies sigma after its conv;
+ * Algorithm 6 none: conv_act = 0).  The convolved q^c, k^c, v^c (fp32, not
+ * rounded to the input type) then take the step of ssd_decode_step_amask
+ * (A_proj given: a_t = exp(-softplus(A_P)), value v^c or v^c softplus(dt_P))
+ * or of ssd_decode_step (A_proj NULL: dt_proj, dt_bias and A_log required).
+ *
+ *   q, k, v    [S,H,d_h] dtype   this step's raw projections h_t W_QKV
+ *   conv_w     [3,H,d_h,2] f32   per channel (q, k, v planes): the weight of
+ *                                the previous token, then of this token
+ *   conv_b     [3,H,d_h] f32 or NULL (no bias)
+ *   conv_act   0 (none) or 1 (SiLU)
+ *   conv_state [S,3,H,d_h] dtype, in/out: the previous step's raw q, k, v
+ *              (zeros before a sequence's first token); replaced by this
+ *              step's raw q, k, v.  Must not overlap any other argument.
+ *   A_proj, dt_proj, dt_bias, A_log: the decay, as described above (with
+ *              A_proj, dt_bias and A_log must be NULL)
+ *   everything else as ssd_decode_step (state, norm_state in place; y out).
+ *
+ * Errors as ssd_decode_step; SSD_ERR_NULL when conv_w or conv_state is NULL,
+ * SSD_ERR_UNSUPPORTED for another conv_act or for dt_bias / A_log given with
+ * A_proj, SSD_ERR_ALIAS when conv_state overlaps another argument.
+ */
+ssd_status ssd_decode_step_conv(const void* q, const void* k, const void* v, const float* conv_w,
+                                const float* conv_b, int conv_act, void* conv_state,
+                                const float* A_proj, const float* dt_proj, const float* dt_bias,
+                                const float* A_log, int64_t S, int64_t H, int64_t d_h, int order,
+                                int dtype, int layout, float* state, float* norm_state, float* y,
+                                hipStream_t stream);
 
 /*
  * ssd_state_pack / ssd_state_unpack -- convert order-2 states between the

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+
 #include "bwd.h"
 #include "launch.h"
 
@@ -339,7 +340,10 @@ static ssd_status decode_common(const char* fn, const void* q, const void* k, co
   int64_t nstate;
   if (!mul_ok(SH, D * d_h, &nstate)) return fail(SSD_ERR_SHAPE, "%s: state too large", fn);
   const size_t es = dtype == SSD_BF16 ? 2 : 4;
-  Range ins[8] = {{"q", q, (size_t)SHd * es}, {"k", k, (size_t)SHd * es}, {"v", v, (size_t)SHd * es}};
+  constexpr int MAX_PARAMS = 8;
+  if (n_params > MAX_PARAMS) return fail(SSD_ERR_HIP, "%s: internal: too many parameter ranges", fn);
+  Range ins[3 + MAX_PARAMS] = {{"q", q, (size_t)SHd * es}, {"k", k, (size_t)SHd * es},
+                               {"v", v, (size_t)SHd * es}};
   for (int i = 0; i < n_params; ++i) ins[3 + i] = params[i];
   const Range outs[] = {{"state", state, (size_t)nstate * 4},
                         {"norm_state", norm_state, (size_t)(SH * D) * 4},
@@ -396,6 +400,59 @@ ssd_status ssd_decode_step_amask(const void* q, const void* k, const void* v, co
                       "decode launch");
   } catch (...) {
     return fail(SSD_ERR_HIP, "ssd_decode_step_amask: unexpected exception");
+  }
+}
+
+ssd_status ssd_decode_step_conv(const void* q, const void* k, const void* v, const float* conv_w,
+                                const float* conv_b, int conv_act, void* conv_state,
+                                const float* A_proj, const float* dt_proj, const float* dt_bias,
+                                const float* A_log, int64_t S, int64_t H, int64_t d_h, int order,
+                                int dtype, int layout, float* state, float* norm_state, float* y,
+                                hipStream_t stream) {
+  try {
+    clear_err();
+    const char* fn = "ssd_decode_step_conv";
+    int64_t SH = 0, SHd = 0;
+    (void)mul_ok(S, H, &SH);
+    (void)mul_ok(SH, d_h, &SHd);
+    const int64_t Hd = (H > 0 ? H : 0) * (d_h > 0 ? d_h : 0);
+    const size_t es = dtype == SSD_BF16 ? 2 : 4;
+    const Range params[] = {{"A_proj", A_proj, (size_t)SH * 4},
+                            {"dt_proj", dt_proj, (size_t)SH * 4},
+                            {"dt_bias", dt_bias, (size_t)(H > 0 ? H : 0) * 4},
+                            {"A_log", A_log, (size_t)(H > 0 ? H : 0) * 4},
+                            {"conv_w", conv_w, (size_t)(3 * Hd * 2) * 4},
+                            {"conv_b", conv_b, (size_t)(3 * Hd) * 4}};
+    bool empty;
+    ssd_status s = decode_common(fn, q, k, v, params, 6, S, H, d_h, order, dtype, layout, state,
+                                 norm_state, y, &empty);
+    if (s != SSD_OK || empty) return s;
+    if (conv_act != 0 && conv_act != 1) return fail(SSD_ERR_UNSUPPORTED, "%s: conv_act %d (0 or 1)", fn, conv_act);
+    if (!conv_w || !conv_state) return fail(SSD_ERR_NULL, "%s: conv_w and conv_state are required", fn);
+    if (A_proj) {
+      if (dt_bias || A_log)
+        return fail(SSD_ERR_UNSUPPORTED, "%s: with A_proj (the A-mask) dt_bias and A_log must be NULL", fn);
+    } else if (!dt_proj || !dt_bias || !A_log) {
+      return fail(SSD_ERR_NULL, "%s: without A_proj, dt_proj, dt_bias and A_log are required", fn);
+    }
+    // the conv state is read and written in place: it must not overlap any
+    // other argument
+    const Range cs{"conv_state", conv_state, (size_t)(3 * SHd) * es};
+    if (!aligned16(conv_state)) return fail(SSD_ERR_ALIGN, "%s: conv_state is not 16-byte aligned", fn);
+    const Range others[] = {{"q", q, (size_t)SHd * es}, {"k", k, (size_t)SHd * es},
+                            {"v", v, (size_t)SHd * es}, params[0], params[1], params[2], params[3],
+                            params[4], params[5]};
+    if ((s = check_alias(&cs, 1, others, 9)) != SSD_OK) return s;
+    int64_t D = order == 1 ? d_h : (layout == SSD_STATE_PACKED ? d_h * (d_h + 1) / 2 : d_h * d_h);
+    const Range outs[] = {{"state", state, (size_t)(SH * D * d_h) * 4},
+                          {"norm_state", norm_state, (size_t)(SH * D) * 4}, {"y", y, (size_t)SHd * 4}};
+    if ((s = check_alias(outs, 3, &cs, 1)) != SSD_OK) return s;
+    return hip_status(ssd::launch_decode(dtype == SSD_BF16, d_h, order, layout == SSD_STATE_PACKED, q, k, v,
+                                         dt_proj, dt_bias, A_log, A_proj, S, H, state, norm_state, y, stream,
+                                         ssd::DecodeConv{conv_w, conv_b, conv_state, conv_act}),
+                      "decode launch");
+  } catch (...) {
+    return fail(SSD_ERR_HIP, "ssd_decode_step_conv: unexpected exception");
   }
 }
 

@@ -51,7 +51,8 @@ __global__ __launch_bounds__(NTH) void k_decode(const St* __restrict__ q, const 
                                                 const float* __restrict__ A_log,
                                                 const float* __restrict__ A_proj, int64_t H,
                                                 float* __restrict__ state,
-                                                float* __restrict__ norm, float* __restrict__ y) {
+                                                float* __restrict__ norm, float* __restrict__ y,
+                                                DecodeConv conv) {
   constexpr int R = Rows<DH, ORDER, PACKED>::value;
   constexpr int CG = DH / 4;         // 16-byte column groups per state row
   constexpr int RPP = NTH / CG;      // rows per pass of the workgroup
@@ -78,8 +79,32 @@ __global__ __launch_bounds__(NTH) void k_decode(const St* __restrict__ q, const 
     alpha = expf(-expf(A_log[h]) * dtv);
   }
   const int tq = tid < DH ? tid : 0;
-  const float lq = Elem<St>::ld(q, sh * DH + tq), lk = Elem<St>::ld(k, sh * DH + tq),
-              lv = Elem<St>::ld(v, sh * DH + tq);
+  float lq = Elem<St>::ld(q, sh * DH + tq), lk = Elem<St>::ld(k, sh * DH + tq),
+        lv = Elem<St>::ld(v, sh * DH + tq);
+  if (conv.w && tid < DH) {
+    // Algorithm 6's window-2 convolution of channel (., h, tid) of q, k, v:
+    // the previous raw token from the conv state, then this step's raw token
+    // stored in its place (each workgroup owns its (sequence, head) slice;
+    // the read precedes the write in this thread)
+    St* cst = static_cast<St*>(conv.state);
+    const int64_t s = sh / H;
+    float x[3] = {lq, lk, lv};
+    const St raw[3] = {q[sh * DH + tid], k[sh * DH + tid], v[sh * DH + tid]};
+#pragma unroll
+    for (int i = 0; i < 3; ++i) {
+      const int64_t ci = ((s * 3 + i) * H + h) * DH + tid;
+      const int64_t wi = ((int64_t)i * H + h) * DH + tid;
+      const float prev = Elem<St>::ld(cst, ci);
+      float c = conv.w[2 * wi] * prev + conv.w[2 * wi + 1] * x[i];
+      if (conv.b) c += conv.b[wi];
+      if (conv.act) c = c / (1.f + expf(-c));
+      x[i] = c;
+      cst[ci] = raw[i];
+    }
+    lq = x[0];
+    lk = x[1];
+    lv = x[2];
+  }
   if (tid < DH) {
     qs[tid] = lq;
     ks[tid] = lk;
@@ -165,7 +190,8 @@ __global__ __launch_bounds__(NTH) void k_decode(const St* __restrict__ q, const 
 hipError_t launch_decode(bool bf16, int64_t DH, int order, bool packed, const void* q,
                          const void* k, const void* v, const float* dt_proj, const float* dt_bias,
                          const float* A_log, const float* A_proj, int64_t S, int64_t H,
-                         float* state, float* norm_state, float* y, hipStream_t stream) {
+                         float* state, float* norm_state, float* y, hipStream_t stream,
+                         DecodeConv conv) {
   const dim3 grid((unsigned)(S * H));
   // workgroup size x rows in flight per thread: order 2 full 1024 x 4 (71.7%
   // of the HBM peak on the 256 x 32-head step), packed 512 x 8 (68.5%, against
@@ -176,7 +202,7 @@ hipError_t launch_decode(bool bf16, int64_t DH, int order, bool packed, const vo
   hipLaunchKernelGGL((k_decode<ST, DHV, ORD, DEC_NTH(ORD, PK), DEC_ROWS(ORD, PK), PK>), grid,   \
                      dim3(DEC_NTH(ORD, PK)), 0, stream, static_cast<const ST*>(q),               \
                      static_cast<const ST*>(k), static_cast<const ST*>(v), dt_proj, dt_bias,   \
-                     A_log, A_proj, H, state, norm_state, y)
+                     A_log, A_proj, H, state, norm_state, y, conv)
 #define SSD_DEC_ORDERS(ST, DHV)                      \
   if (order == 1) SSD_LAUNCH_DEC(ST, DHV, 1, false); \
   else if (packed) SSD_LAUNCH_DEC(ST, DHV, 2, true); \

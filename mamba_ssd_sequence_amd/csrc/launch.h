@@ -153,13 +153,25 @@ hipError_t launch_o2_state(const void* rec, int64_t BH, int64_t N, float* part,
                            float* final_state, float* zstate, float* final_norm, const float* S0,
                            const float* Z0, hipStream_t stream);
 
+// The window-2 short convolution of Algorithm 6 on the decode path: per
+// channel x^c = w[.., 0] x_prev + w[.., 1] x (+ b), optional SiLU; the conv
+// state holds the previous step's raw q, k, v and receives this step's.
+struct DecodeConv {
+  const float* w;  // [3, H, d_h, 2] (q, k, v channels) or NULL: no convolution
+  const float* b;  // [3, H, d_h] or NULL
+  void* state;     // [S, 3, H, d_h], the q/k/v element type, in/out
+  int act;         // 0: none (Algorithm 6), 1: SiLU (Algorithm 3's sigma)
+};
+
 // One decode step.  A_proj == NULL: the Mamba-2 discretisation (dt_proj,
 // dt_bias, A_log); else the A-mask (A_proj, optional dt_proj).  packed: the
-// order-2 states in the packed layout (rows a <= b).
+// order-2 states in the packed layout (rows a <= b).  conv.w == NULL: q, k, v
+// are used as given.
 hipError_t launch_decode(bool bf16, int64_t DH, int order, bool packed, const void* q,
                          const void* k, const void* v, const float* dt_proj, const float* dt_bias,
                          const float* A_log, const float* A_proj, int64_t S, int64_t H,
-                         float* state, float* norm_state, float* y, hipStream_t stream);
+                         float* state, float* norm_state, float* y, hipStream_t stream,
+                         DecodeConv conv = DecodeConv{nullptr, nullptr, nullptr, 0});
 
 // Order-2 state layout conversion over BH (sequence, head) pairs: full ->
 // packed (the symmetric part) when to_packed, else packed -> full.

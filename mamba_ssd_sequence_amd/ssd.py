@@ -9,6 +9,7 @@ call fails, an exception is raised.
     y = forward(q, k, v, dt, a_cs, order=2, chunk=64)
     y = decode_step(q, k, v, dt_proj, dt_bias, A_log, state, norm_state, order=2)
     y = decode_step_amask(q, k, v, A_proj, dt_proj, state, norm_state, order=2)
+    y = decode_step_conv(q, k, v, conv_w, conv_b, conv_state, state, norm_state, order=2, A_proj=A_proj)
     state_p, norm_p = state_pack(state, norm_state)
     dq, dk, dv, ddt, da = backward(q, k, v, dt, a_cs, y, den, dy, order=2, chunk=64)
     d_dt_proj, d_dt_bias, d_A_log = prep_backward(dt_proj, dt_bias, A_log, da, ddt)
@@ -66,6 +67,9 @@ def _declare(lib):
     lib.ssd_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, i64, i64, i64, i32, i32, i32, fp, fp, fp, vp]
     lib.ssd_decode_step_amask.restype = ctypes.c_int
     lib.ssd_decode_step_amask.argtypes = [vp, vp, vp, fp, fp, i64, i64, i64, i32, i32, i32, fp, fp, fp, vp]
+    lib.ssd_decode_step_conv.restype = ctypes.c_int
+    lib.ssd_decode_step_conv.argtypes = [vp, vp, vp, fp, fp, i32, vp, fp, fp, fp, fp, i64, i64, i64, i32,
+                                         i32, i32, fp, fp, fp, vp]
     lib.ssd_state_pack.restype = ctypes.c_int
     lib.ssd_state_pack.argtypes = [fp, fp, i64, i64, fp, fp, vp]
     lib.ssd_state_unpack.restype = ctypes.c_int
@@ -289,6 +293,30 @@ def decode_step_amask(q, k, v, A_proj, dt_proj, state, norm_state, order: int, *
                                        _ptr(dt_proj) if dt_proj is not None else None,
                                        S, H, d_h, order, dtype, layout, _ptr(state), _ptr(norm_state),
                                        _ptr(y), _stream(dev)))
+    return y
+
+
+def decode_step_conv(q, k, v, conv_w, conv_b, conv_state, state, norm_state, order: int, *,
+                     A_proj=None, dt_proj=None, dt_bias=None, A_log=None, act=False, y=None,
+                     packed=False):
+    """ssd_decode_step_conv: Algorithm 6's window-2 convolution of the raw q, k,
+    v [S,H,d_h] (conv_w [3,H,d_h,2], conv_b [3,H,d_h] or None, SiLU if act)
+    with the previous raw token held in conv_state [S,3,H,d_h] (updated in
+    place), then the decode step: the A-mask with A_proj (optional dt_proj),
+    else the Mamba-2 discretisation (dt_proj, dt_bias, A_log)."""
+    dev, dtype, S, H, d_h, layout, y = _decode_common(
+        q, k, v, (("A_proj", A_proj), ("dt_proj", dt_proj), ("dt_bias", dt_bias), ("A_log", A_log),
+                  ("conv_w", conv_w), ("conv_b", conv_b)), state, norm_state, order, y, packed)
+    _require(conv_state, "conv_state", q.dtype, dev)
+    if tuple(conv_state.shape) != (S, 3, H, d_h) or tuple(conv_w.shape) != (3, H, d_h, 2):
+        raise ValueError(f"conv_state {tuple(conv_state.shape)} / conv_w {tuple(conv_w.shape)} do not match "
+                         f"[{S},3,{H},{d_h}] / [3,{H},{d_h},2]")
+    if conv_b is not None and tuple(conv_b.shape) != (3, H, d_h):
+        raise ValueError(f"conv_b {tuple(conv_b.shape)} does not match [3,{H},{d_h}]")
+    _check(lib().ssd_decode_step_conv(_ptr(q), _ptr(k), _ptr(v), _ptr(conv_w), _ptr(conv_b), 1 if act else 0,
+                                      _ptr(conv_state), _ptr(A_proj), _ptr(dt_proj), _ptr(dt_bias),
+                                      _ptr(A_log), S, H, d_h, order, dtype, layout, _ptr(state),
+                                      _ptr(norm_state), _ptr(y), _stream(dev)))
     return y
 
 

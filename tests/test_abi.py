@@ -18,7 +18,8 @@ def lib():
 def test_exports_every_header_function(lib):
     names = ssd.header_functions()
     assert set(names) >= {"ssd_prep", "ssd_prep_amask", "ssd_forward", "ssd_forward_workspace_size",
-                          "ssd_decode_step", "ssd_decode_step_amask", "ssd_state_pack",
+                          "ssd_decode_step", "ssd_decode_step_amask", "ssd_decode_step_conv",
+                          "ssd_state_pack",
                           "ssd_state_unpack", "ssd_backward", "ssd_backward_workspace_size",
                           "ssd_prep_backward", "ssd_prep_amask_backward",
                           "ssd_abi_version", "ssd_status_str", "ssd_last_error"}
@@ -27,7 +28,7 @@ def test_exports_every_header_function(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.ssd_abi_version() == 5
+    assert lib.ssd_abi_version() == 6
     for i, name in enumerate(ssd.STATUS):
         assert lib.ssd_status_str(i).decode() == name
     assert lib.ssd_status_str(99).decode() == "SSD_ERR_UNKNOWN"
@@ -146,6 +147,31 @@ def test_decode_amask_errors(lib):
     assert dec_amask(lib, layout=1, order=1) == 3
     assert dec_amask(lib, d_h=48) == 3
     assert dec_amask(lib, S=-2) == 2
+
+
+def dec_conv(lib, *, S=1, H=1, d_h=64, order=2, layout=0, conv_w=A[9], conv_b=A[10], act=0, cst=A[11],
+             A_proj=A[3], dt_proj=A[4], dt_bias=None, A_log=None, norm=A[7]):
+    return lib.ssd_decode_step_conv(A[0], A[1], A[2], conv_w, conv_b, act, cst, A_proj, dt_proj, dt_bias,
+                                    A_log, S, H, d_h, order, 1, layout, A[6], norm, A[8], None)
+
+
+def test_decode_conv_errors(lib):
+    # every call here is rejected before any HIP call (none is valid)
+    assert dec_conv(lib, conv_w=None) == 1
+    assert dec_conv(lib, cst=None) == 1
+    assert dec_conv(lib, act=2) == 3
+    assert dec_conv(lib, dt_bias=A[12]) == 3                  # A-mask with Mamba-2 parameters
+    assert dec_conv(lib, A_proj=None, dt_bias=None) == 1      # Mamba-2 without its parameters
+    assert dec_conv(lib, cst=A[11] + 8) == 4
+    assert dec_conv(lib, conv_w=A[9] + 4) == 4
+    assert dec_conv(lib, cst=A[0]) == 5                        # conv state over q
+    assert "conv_state" in lib.ssd_last_error().decode()
+    assert dec_conv(lib, cst=A[6]) == 5                        # conv state inside the state output
+    assert dec_conv(lib, cst=A[9] + 128) == 5                  # conv state over the weights
+    assert dec_conv(lib, norm=A[9]) == 5                       # an output over the weights
+    assert dec_conv(lib, d_h=48) == 3
+    assert dec_conv(lib, S=-1) == 2
+    assert dec_conv(lib, S=0, conv_w=None) == 0                # empty: nothing to do
 
 
 def test_state_layout_errors(lib):

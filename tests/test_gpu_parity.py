@@ -439,7 +439,9 @@ def test_forward_amask_full_size_2mamba():
 
 
 # ---------------------------------------------------------------------------
-# decode
+# decode: the step evaluates Algorithm 6's state form (phi(q)^T S / phi(q)^T z),
+# so its outputs are measured with the state form's error scale
+# (scale_state: sums over the feature products q_a.. k_a..)
 # ---------------------------------------------------------------------------
 
 def run_decode_steps(dec, order, steps, S=None, check_heads=None):
@@ -493,7 +495,7 @@ def test_decode_small(order, d_h, dtype):
     ys, ins, st, nz = run_decode_steps(dec, order, cfg.steps)
     ref = decode_reference(ins, dtype, dec.A_log.astype(np.float64), dec.dt_bias.astype(np.float64), order)
     y = np.stack(ys, axis=2)  # [S,H,T,d]
-    assert row_error(y, ref["y"], ref["scale"]) <= TOL[dtype]
+    assert row_error(y, ref["y"], ref["scale_state"]) <= TOL[dtype]
     # final state against the token recurrence
     up = I.bf16_bits_to_f64 if dtype == I.BF16 else (lambda x: x.astype(np.float64))
     Sx = np.zeros((cfg.S, cfg.H, d_h ** order, d_h))
@@ -539,8 +541,8 @@ def test_decode_full_size_sampled():
     ref = decode_reference(ins, cfg.dtype, dec.A_log.astype(np.float64), dec.dt_bias.astype(np.float64),
                            cfg.order, h_idx=h_idx)
     y = np.stack(ys, axis=1)[None]  # [1,M,T,d]
-    err = row_error(y, ref["y"], ref["scale"])
-    say("  ", worst(y, ref["y"], ref["scale"]))
+    err = row_error(y, ref["y"], ref["scale_state"])
+    say("  ", worst(y, ref["y"], ref["scale_state"]))
     assert err <= TOL[cfg.dtype]
     S, z = decode_final_state_ref(ins, dec, h_idx, cfg.dtype, cfg.order)
     fs_err = np.abs(st - S).max() / np.abs(S).max()
@@ -570,7 +572,7 @@ def test_prefill_then_decode():
         ys.append(y.cpu().numpy())
     ref = oracle_forward(inp, 2, rows=np.arange(N, N + T))
     y = np.stack(ys, axis=2)
-    assert row_error(y, ref["y"], ref["scale"]) <= TOL[cfg.dtype]
+    assert row_error(y, ref["y"], ref["scale_state"]) <= TOL[cfg.dtype]
 
 
 # ---------------------------------------------------------------------------
@@ -660,7 +662,7 @@ def test_decode_variants_small(order, d_h, dtype, amask, with_dt, packed):
     ys, ins, st, nz = run_decode_variant(dec, order, cfg.steps, amask=amask, with_dt=with_dt, packed=packed)
     ref, Sx, zx = decode_variant_reference(ins, dtype, dec, order, amask=amask, with_dt=with_dt)
     y = np.stack(ys, axis=2)  # [S,H,T,d]
-    err = row_error(y, ref["y"], ref["scale"])
+    err = row_error(y, ref["y"], ref["scale_state"])
     say("  err", err)
     assert err <= TOL[dtype]
     if packed:
@@ -682,8 +684,8 @@ def test_decode_packed_full_size_sampled():
     ref = decode_variant_reference(ins, cfg.dtype, dec, 2, amask=False, with_dt=True, h_idx=h_idx,
                                    states=False)[0]
     y = np.stack(ys, axis=1)[None]  # [1,M,T,d]
-    err = row_error(y, ref["y"], ref["scale"])
-    say("  ", worst(y, ref["y"], ref["scale"]))
+    err = row_error(y, ref["y"], ref["scale_state"])
+    say("  ", worst(y, ref["y"], ref["scale_state"]))
     assert err <= TOL[cfg.dtype]
     S, z = decode_final_state_ref(ins, dec, h_idx, cfg.dtype, 2)
     Sp, zp = O.pack_state(S, z, cfg.d_h)
@@ -745,9 +747,85 @@ def test_prefill_then_decode_amask_packed():
     qf, kf, vf = inp.qkv_f64()
     ref = O.forward_amask_ref(qf, kf, vf, inp.A_proj, None, 2, rows=np.arange(N, N + T))
     y = np.stack(ys, axis=2)
-    err = row_error(y, ref["y"], ref["scale"])
+    err = row_error(y, ref["y"], ref["scale_state"])
     say("  err", err)
     assert err <= TOL[cfg.dtype]
+
+
+# ---------------------------------------------------------------------------
+# decode with Algorithm 6's window-2 convolution
+# ---------------------------------------------------------------------------
+
+# (order, d_h, dtype, A-mask decay (else Mamba-2), conv bias, SiLU, packed layout)
+DECODE_CONV = [(2, 64, I.BF16, True, True, False, False), (2, 64, I.BF16, True, False, False, True),
+               (2, 32, I.F32, False, True, True, False), (1, 64, I.BF16, True, True, True, False),
+               (1, 32, I.F32, False, False, False, False)]
+
+
+@pytest.mark.parametrize("order,d_h,dtype,amask,bias,act,packed", DECODE_CONV)
+def test_decode_conv_small(order, d_h, dtype, amask, bias, act, packed):
+    """T decode steps with the window-2 convolution from zero states and a
+    zero conv state: each step's y against the oracle (the masked quadratic
+    form over the convolved sequence, row-scaled metric), the final states
+    against the oracle's steps, and the conv state, which must hold the last
+    raw token bit for bit."""
+    ssd = ssd_mod()
+    say("decode conv", order, d_h, dtype, "amask" if amask else "mamba2", bias, act, packed)
+    cfg = I.DecodeConfig("t", S=3, H=2, d_h=d_h, order=order, steps=13, dtype=dtype, seed=90 + d_h + order)
+    dec = I.make_decode_inputs(cfg)
+    rng = np.random.default_rng(91 + order)
+    w = np.stack([rng.uniform(-0.5, 0.5, (3, cfg.H, d_h)), rng.uniform(0.5, 1.5, (3, cfg.H, d_h))],
+                 axis=-1).astype(np.float32)
+    b = rng.normal(0.0, 0.1, (3, cfg.H, d_h)).astype(np.float32) if bias else None
+    D = d_h if order == 1 else (d_h * (d_h + 1) // 2 if packed else d_h * d_h)
+    state = torch.zeros((cfg.S, cfg.H, D, d_h), device="cuda")
+    norm = torch.zeros((cfg.S, cfg.H, D), device="cuda")
+    tdt = torch.bfloat16 if dtype == I.BF16 else torch.float32
+    cst = torch.zeros((cfg.S, 3, cfg.H, d_h), dtype=tdt, device="cuda")
+    wd, bd = to_dev_f32(w), (to_dev_f32(b) if bias else None)
+    bias_d, alog_d = to_dev_f32(dec.dt_bias), to_dev_f32(dec.A_log)
+    up = I.bf16_bits_to_f64 if dtype == I.BF16 else (lambda x: x.astype(np.float64))
+    Sx = np.zeros((cfg.S, cfg.H, d_h ** order, d_h))
+    zx = np.zeros((cfg.S, cfg.H, d_h ** order))
+    cx = np.zeros((cfg.S, 3, cfg.H, d_h))
+    ys, conv = [], [[], [], []]
+    act_s = "silu" if act else None
+    for (q, k, v, dtp, A_P) in dec.steps(cfg.steps, with_A=True):
+        qd, kd, vd = (to_dev_qkv(x, dtype) for x in (q, k, v))
+        if amask:
+            y = ssd.decode_step_conv(qd, kd, vd, wd, bd, cst, state, norm, order, A_proj=to_dev_f32(A_P),
+                                     dt_proj=to_dev_f32(dtp), act=act, packed=packed)
+            kw = dict(A_proj=A_P, dt_proj=dtp)
+        else:
+            y = ssd.decode_step_conv(qd, kd, vd, wd, bd, cst, state, norm, order, dt_proj=to_dev_f32(dtp),
+                                     dt_bias=bias_d, A_log=alog_d, act=act, packed=packed)
+            kw = dict(dt_proj=dtp, dt_bias=dec.dt_bias, A_log=dec.A_log)
+        ys.append(y.cpu().numpy())
+        for i, x in enumerate((q, k, v)):
+            conv[i].append(O.conv_window2(up(x), cx[:, i], w[i], None if b is None else b[i], act_s))
+        _, Sx, zx, cx, _ = O.decode_step_conv_ref(Sx, zx, cx, up(q), up(k), up(v), w, b, act_s, order, **kw)
+    torch.cuda.synchronize()
+    y = np.stack(ys, axis=2)  # [S,H,T,d]
+    qc, kc, vc = (np.stack(c, axis=2) for c in conv)
+    A_Ps = np.stack([s_[4] for s_ in dec.steps(cfg.steps, with_A=True)], axis=-1).astype(np.float64)
+    dtps = np.stack([s_[3] for s_ in dec.steps(cfg.steps, with_A=True)], axis=-1).astype(np.float64)
+    if amask:
+        ref = O.forward_amask_ref(qc, kc, vc, A_Ps, dtps, order)
+    else:
+        ref = O.forward_ref(qc, kc, vc, dtps, dec.dt_bias, dec.A_log, order)
+    err = row_error(y, ref["y"], ref["scale_state"])
+    say("  ", worst(y, ref["y"], ref["scale_state"]))
+    assert err <= TOL[dtype]
+    st, nz = state.cpu().numpy(), norm.cpu().numpy()
+    if packed:
+        Sx, zx = O.pack_state(Sx, zx, d_h)
+    assert np.abs(st - Sx).max() <= 1e-5 * np.abs(Sx).max()
+    assert np.abs(nz - zx).max() <= 1e-5 * np.abs(zx).max()
+    last = [x for x in dec.steps(cfg.steps, with_A=True)][-1]
+    want = np.stack([np.ascontiguousarray(x) for x in last[:3]], axis=1)  # [S,3,H,d] stored values
+    got_cs = cst.cpu()
+    got_cs = (got_cs.view(torch.int16).numpy().view(np.uint16) if dtype == I.BF16 else got_cs.numpy())
+    assert np.array_equal(got_cs, want.astype(got_cs.dtype) if dtype != I.BF16 else want)
 
 
 # ---------------------------------------------------------------------------

@@ -177,6 +177,35 @@ ssd_status ssd_forward(const void* q, const void* k, const void* v, const float*
                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * ssd_forward_noalloc -- ssd_forward for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same computation and kernels, with no workspace
+ * argument.  Its scratch is a device array inside the library, of
+ * SSD_NOALLOC_SCRATCH_BYTES per GPU, held from the library's first use on
+ * that GPU until the process ends; the call itself allocates nothing.
+ *
+ *   arguments      exactly those of ssd_forward without workspace and
+ *                  workspace_bytes
+ *   sizes          those whose ssd_forward_workspace_size exceeds
+ *                  SSD_NOALLOC_SCRATCH_BYTES are rejected with
+ *                  SSD_ERR_WORKSPACE (use ssd_forward with a workspace)
+ *   concurrency    every call on one GPU uses that GPU's one scratch array:
+ *                  calls that overlap in time on one GPU (other streams,
+ *                  other threads) race and give wrong results; calls queued
+ *                  on one stream are ordered and safe.  No call needs the
+ *                  scratch cleared (every byte read is written first in the
+ *                  same call).
+ * Errors as ssd_forward.
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ssd_status ssd_forward_noalloc(const void* q, const void* k, const void* v, const float* dt,
+                               const float* a_cs, const float* initial_state,
+                               const float* initial_norm, int64_t B, int64_t H, int64_t N,
+                               int64_t d_h, int order, int64_t chunk, int dtype, float* y,
+                               float* den, float* final_state, float* final_norm,
+                               hipStream_t stream);
+
+/*
  * ssd_set_timing_events -- optional per-kernel timing of the next ssd_forward
  * call on the calling thread (used by the benchmark; not part of the math).
  *

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 
 #include "bwd.h"
 #include "launch.h"
@@ -205,6 +206,146 @@ size_t ssd_forward_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d_h, 
   return ssd::ws_layout(B, H, N, d_h, order).total_floats * sizeof(float);
 }
 
+}  // extern "C"
+
+namespace {
+
+// Scratch memory of ssd_forward_noalloc: a file-scope device array (each GPU
+// the library runs on holds its own copy until the process ends).  Host code
+// never uses the array's name as an address: the device address comes from
+// hipGetSymbolAddress, taken once per device on that device's first call.
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
+ssd_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "ssd_forward_noalloc: hipGetDevice");
+  if (dev < 0 || dev >= MAX_DEVICES)
+    return fail(SSD_ERR_HIP, "ssd_forward_noalloc: device %d beyond the %d supported", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "ssd_forward_noalloc: hipGetSymbolAddress(scratch)");
+    if (!p) return fail(SSD_ERR_HIP, "ssd_forward_noalloc: hipGetSymbolAddress returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SSD_OK;
+}
+
+// ssd_forward and ssd_forward_noalloc: every argument check, then (noalloc)
+// the device's scratch array in place of the caller's workspace, then the
+// launches.
+ssd_status forward_core(const char* fn, bool noalloc, const void* q, const void* k, const void* v,
+                        const float* dt, const float* a_cs, const float* initial_state,
+                        const float* initial_norm, int64_t B, int64_t H, int64_t N, int64_t d_h,
+                        int order, int64_t chunk, int dtype, float* y, float* den,
+                        float* final_state, float* final_norm, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
+  int64_t BH, BHN, BHNd;
+  ssd_status s = validate_forward_sizes(B, H, N, d_h, order, chunk, dtype, &BH, &BHN, &BHNd);
+  if (s != SSD_OK) return s;
+  if (BH == 0) return SSD_OK;  // no heads: nothing to compute
+  if ((final_state == nullptr) != (final_norm == nullptr))
+    return fail(SSD_ERR_NULL, "%s: final_state and final_norm must be given together", fn);
+  if ((initial_state == nullptr) != (initial_norm == nullptr))
+    return fail(SSD_ERR_NULL, "%s: initial_state and initial_norm must be given together", fn);
+  const size_t es = dtype == SSD_BF16 ? 2 : 4;
+  const int64_t D = order == 1 ? d_h : d_h * d_h;
+  if (BHN == 0) {
+    // an empty segment (N = 0): the final states are the initial ones (or zero)
+    if (!final_state) return SSD_OK;
+    const Range ins0[] = {{"initial_state", initial_state, (size_t)(BH * D * d_h) * 4},
+                          {"initial_norm", initial_norm, (size_t)(BH * D) * 4}};
+    const Range outs0[] = {{"final_state", final_state, (size_t)(BH * D * d_h) * 4},
+                           {"final_norm", final_norm, (size_t)(BH * D) * 4}};
+    if ((s = check_aligned(ins0, 2)) != SSD_OK || (s = check_aligned(outs0, 2)) != SSD_OK) return s;
+    if ((s = check_alias(outs0, 2, ins0, 2)) != SSD_OK) return s;
+    hipError_t e = ssd::launch_copy_or_zero(final_state, initial_state, BH * D * d_h, stream);
+    if (e == hipSuccess) e = ssd::launch_copy_or_zero(final_norm, initial_norm, BH * D, stream);
+    return hip_status(e, "final-state copy launch");
+  }
+  if (!q || !k || !v || !a_cs || !y) return fail(SSD_ERR_NULL, "%s: a required pointer is NULL", fn);
+  const size_t need = ssd::ws_layout(B, H, N, d_h, order).total_floats * sizeof(float);
+  if (noalloc) {
+    if (need > (size_t)SSD_NOALLOC_SCRATCH_BYTES)
+      return fail(SSD_ERR_WORKSPACE,
+                  "%s: these sizes need %zu bytes of scratch, more than the %zu bytes this entry point "
+                  "holds per device; call ssd_forward with a workspace instead",
+                  fn, need, (size_t)SSD_NOALLOC_SCRATCH_BYTES);
+  } else if (workspace_bytes < need || (need && !workspace)) {
+    return fail(SSD_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                workspace ? workspace_bytes : (size_t)0);
+  }
+  const Range ins[] = {{"q", q, (size_t)BHNd * es},  {"k", k, (size_t)BHNd * es},
+                       {"v", v, (size_t)BHNd * es},  {"dt", dt, (size_t)BHN * 4},
+                       {"a_cs", a_cs, (size_t)BHN * 4},
+                       {"initial_state", initial_state, (size_t)(BH * D * d_h) * 4},
+                       {"initial_norm", initial_norm, (size_t)(BH * D) * 4}};
+  const Range outs[] = {{"y", y, (size_t)BHNd * 4},
+                        {"den", den, (size_t)BHN * 4},
+                        {"final_state", final_state, (size_t)(BH * D * d_h) * 4},
+                        {"final_norm", final_norm, (size_t)(BH * D) * 4},
+                        {"workspace", noalloc ? nullptr : workspace, need}};
+  if ((s = check_aligned(ins, 7)) != SSD_OK || (s = check_aligned(outs, 5)) != SSD_OK) return s;
+  if ((s = check_alias(outs, 5, ins, 7)) != SSD_OK) return s;
+  // every check done: only now the first HIP call
+  if (noalloc && (s = scratch_of_current_device(&workspace)) != SSD_OK) return s;
+
+  const bool bf = dtype == SSD_BF16;
+  Timer tm(stream);
+  const ssd::WsLayout L = ssd::ws_layout(B, H, N, d_h, order);
+  float* ws = static_cast<float*>(workspace);
+  float* tb = ws + L.tb;
+  float* st = ws + L.state;
+  hipError_t e;
+  if (order == 1) {
+    if ((e = ssd::launch_chunk_state(bf, d_h, k, v, dt, a_cs, BH, N, chunk, tb, st, stream)) != hipSuccess)
+      return hip_status(e, "chunk_state launch");
+    tm.mark();
+    if ((e = ssd::launch_state_pass(d_h, BH, N, tb, st, final_state, final_norm, initial_state,
+                                    initial_norm, stream)) != hipSuccess)
+      return hip_status(e, "state_pass launch");
+    tm.mark();
+    e = ssd::launch_output(bf, d_h, 1, q, k, v, dt, a_cs, BH, N, chunk, st, nullptr, y, den, stream);
+    tm.mark();
+    return hip_status(e, "output launch");
+  }
+  // order 2: per-block preparation (normaliser contributions Z_blk and the
+  // numerator operand records), the scale scan, the on-chip numerator scan
+  // (which also scans Z), and the output kernel.
+  float* part = ws + L.part;
+  void* rec = ws + L.rec;
+  if ((e = ssd::launch_o2_blockprep(q, k, v, dt, a_cs, BH, N, chunk, tb, st, rec, stream)) != hipSuccess)
+    return hip_status(e, "o2_blockprep launch");
+  tm.mark();
+  float* initmax = nullptr;
+  if (initial_state) {
+    initmax = ws + L.initmax;
+    if ((e = ssd::launch_o2_initmax(initial_state, BH, initmax, stream)) != hipSuccess)
+      return hip_status(e, "o2_initmax launch");
+  }
+  if ((e = ssd::launch_o2_scale_scan(rec, BH, N, initmax, stream)) != hipSuccess)
+    return hip_status(e, "o2_scale_scan launch");
+  tm.mark();
+  if ((e = ssd::launch_o2_state(rec, BH, N, part, final_state, st, final_norm, initial_state,
+                                initial_norm, stream)) != hipSuccess)
+    return hip_status(e, "o2_state launch");
+  tm.mark();
+  e = ssd::launch_output(true, 64, 2, q, k, v, dt, a_cs, BH, N, chunk, st, part, y, den, stream);
+  tm.mark();
+  return hip_status(e, "output launch");
+}
+
+}  // namespace
+
+extern "C" {
+
 ssd_status ssd_forward(const void* q, const void* k, const void* v, const float* dt,
                        const float* a_cs, const float* initial_state, const float* initial_norm,
                        int64_t B, int64_t H, int64_t N, int64_t d_h, int order,
@@ -213,92 +354,27 @@ ssd_status ssd_forward(const void* q, const void* k, const void* v, const float*
                        hipStream_t stream) {
   try {
     clear_err();
-    int64_t BH, BHN, BHNd;
-    ssd_status s = validate_forward_sizes(B, H, N, d_h, order, chunk, dtype, &BH, &BHN, &BHNd);
-    if (s != SSD_OK) return s;
-    if (BH == 0) return SSD_OK;  // no heads: nothing to compute
-    if ((final_state == nullptr) != (final_norm == nullptr))
-      return fail(SSD_ERR_NULL, "ssd_forward: final_state and final_norm must be given together");
-    if ((initial_state == nullptr) != (initial_norm == nullptr))
-      return fail(SSD_ERR_NULL, "ssd_forward: initial_state and initial_norm must be given together");
-    const size_t es = dtype == SSD_BF16 ? 2 : 4;
-    const int64_t D = order == 1 ? d_h : d_h * d_h;
-    if (BHN == 0) {
-      // an empty segment (N = 0): the final states are the initial ones (or zero)
-      if (!final_state) return SSD_OK;
-      const Range ins0[] = {{"initial_state", initial_state, (size_t)(BH * D * d_h) * 4},
-                            {"initial_norm", initial_norm, (size_t)(BH * D) * 4}};
-      const Range outs0[] = {{"final_state", final_state, (size_t)(BH * D * d_h) * 4},
-                             {"final_norm", final_norm, (size_t)(BH * D) * 4}};
-      if ((s = check_aligned(ins0, 2)) != SSD_OK || (s = check_aligned(outs0, 2)) != SSD_OK) return s;
-      if ((s = check_alias(outs0, 2, ins0, 2)) != SSD_OK) return s;
-      hipError_t e = ssd::launch_copy_or_zero(final_state, initial_state, BH * D * d_h, stream);
-      if (e == hipSuccess) e = ssd::launch_copy_or_zero(final_norm, initial_norm, BH * D, stream);
-      return hip_status(e, "final-state copy launch");
-    }
-    if (!q || !k || !v || !a_cs || !y) return fail(SSD_ERR_NULL, "ssd_forward: a required pointer is NULL");
-    const size_t need = ssd::ws_layout(B, H, N, d_h, order).total_floats * sizeof(float);
-    if (workspace_bytes < need || (need && !workspace))
-      return fail(SSD_ERR_WORKSPACE, "ssd_forward: workspace of %zu bytes needed, %zu given", need,
-                  workspace ? workspace_bytes : (size_t)0);
-    const Range ins[] = {{"q", q, (size_t)BHNd * es},  {"k", k, (size_t)BHNd * es},
-                         {"v", v, (size_t)BHNd * es},  {"dt", dt, (size_t)BHN * 4},
-                         {"a_cs", a_cs, (size_t)BHN * 4},
-                         {"initial_state", initial_state, (size_t)(BH * D * d_h) * 4},
-                         {"initial_norm", initial_norm, (size_t)(BH * D) * 4}};
-    const Range outs[] = {{"y", y, (size_t)BHNd * 4},
-                          {"den", den, (size_t)BHN * 4},
-                          {"final_state", final_state, (size_t)(BH * D * d_h) * 4},
-                          {"final_norm", final_norm, (size_t)(BH * D) * 4},
-                          {"workspace", workspace, need}};
-    if ((s = check_aligned(ins, 7)) != SSD_OK || (s = check_aligned(outs, 5)) != SSD_OK) return s;
-    if ((s = check_alias(outs, 5, ins, 7)) != SSD_OK) return s;
-
-    const bool bf = dtype == SSD_BF16;
-    Timer tm(stream);
-    const ssd::WsLayout L = ssd::ws_layout(B, H, N, d_h, order);
-    float* ws = static_cast<float*>(workspace);
-    float* tb = ws + L.tb;
-    float* st = ws + L.state;
-    hipError_t e;
-    if (order == 1) {
-      if ((e = ssd::launch_chunk_state(bf, d_h, k, v, dt, a_cs, BH, N, chunk, tb, st, stream)) != hipSuccess)
-        return hip_status(e, "chunk_state launch");
-      tm.mark();
-      if ((e = ssd::launch_state_pass(d_h, BH, N, tb, st, final_state, final_norm, initial_state,
-                                      initial_norm, stream)) != hipSuccess)
-        return hip_status(e, "state_pass launch");
-      tm.mark();
-      e = ssd::launch_output(bf, d_h, 1, q, k, v, dt, a_cs, BH, N, chunk, st, nullptr, y, den, stream);
-      tm.mark();
-      return hip_status(e, "output launch");
-    }
-    // order 2: per-block preparation (normaliser contributions Z_blk and the
-    // numerator operand records), the scale scan, the on-chip numerator scan
-    // (which also scans Z), and the output kernel.
-    float* part = ws + L.part;
-    void* rec = ws + L.rec;
-    if ((e = ssd::launch_o2_blockprep(q, k, v, dt, a_cs, BH, N, chunk, tb, st, rec, stream)) != hipSuccess)
-      return hip_status(e, "o2_blockprep launch");
-    tm.mark();
-    float* initmax = nullptr;
-    if (initial_state) {
-      initmax = ws + L.initmax;
-      if ((e = ssd::launch_o2_initmax(initial_state, BH, initmax, stream)) != hipSuccess)
-        return hip_status(e, "o2_initmax launch");
-    }
-    if ((e = ssd::launch_o2_scale_scan(rec, BH, N, initmax, stream)) != hipSuccess)
-      return hip_status(e, "o2_scale_scan launch");
-    tm.mark();
-    if ((e = ssd::launch_o2_state(rec, BH, N, part, final_state, st, final_norm, initial_state,
-                                  initial_norm, stream)) != hipSuccess)
-      return hip_status(e, "o2_state launch");
-    tm.mark();
-    e = ssd::launch_output(true, 64, 2, q, k, v, dt, a_cs, BH, N, chunk, st, part, y, den, stream);
-    tm.mark();
-    return hip_status(e, "output launch");
+    return forward_core("ssd_forward", false, q, k, v, dt, a_cs, initial_state, initial_norm, B, H, N,
+                        d_h, order, chunk, dtype, y, den, final_state, final_norm, workspace,
+                        workspace_bytes, stream);
   } catch (...) {
     return fail(SSD_ERR_HIP, "ssd_forward: unexpected exception");
+  }
+}
+
+ssd_status ssd_forward_noalloc(const void* q, const void* k, const void* v, const float* dt,
+                               const float* a_cs, const float* initial_state,
+                               const float* initial_norm, int64_t B, int64_t H, int64_t N,
+                               int64_t d_h, int order, int64_t chunk, int dtype, float* y,
+                               float* den, float* final_state, float* final_norm,
+                               hipStream_t stream) {
+  try {
+    clear_err();
+    return forward_core("ssd_forward_noalloc", true, q, k, v, dt, a_cs, initial_state, initial_norm, B,
+                        H, N, d_h, order, chunk, dtype, y, den, final_state, final_norm, nullptr, 0,
+                        stream);
+  } catch (...) {
+    return fail(SSD_ERR_HIP, "ssd_forward_noalloc: unexpected exception");
   }
 }
 

@@ -29,6 +29,7 @@ SSD_F32 = 0
 SSD_BF16 = 1
 SSD_STATE_FULL = 0
 SSD_STATE_PACKED = 1
+SSD_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/ssd.h
 STATUS = ["SSD_OK", "SSD_ERR_NULL", "SSD_ERR_SHAPE", "SSD_ERR_UNSUPPORTED", "SSD_ERR_ALIGN",
           "SSD_ERR_ALIAS", "SSD_ERR_WORKSPACE", "SSD_ERR_HIP"]
 
@@ -59,6 +60,9 @@ def _declare(lib):
     lib.ssd_forward.restype = ctypes.c_int
     lib.ssd_forward.argtypes = [vp, vp, vp, fp, fp, fp, fp, i64, i64, i64, i64, i32, i64, i32,
                                 fp, fp, fp, fp, vp, sz, vp]
+    lib.ssd_forward_noalloc.restype = ctypes.c_int
+    lib.ssd_forward_noalloc.argtypes = [vp, vp, vp, fp, fp, fp, fp, i64, i64, i64, i64, i32, i64, i32,
+                                        fp, fp, fp, fp, vp]
     lib.ssd_set_timing_events.restype = ctypes.c_int
     lib.ssd_set_timing_events.argtypes = [vp, ctypes.c_int]
     lib.ssd_timing_count.restype = ctypes.c_int
@@ -197,7 +201,9 @@ def forward(q, k, v, dt, a_cs, order: int, chunk: int, *, y=None, den=None,
             final_state=None, final_norm=None, workspace=None, initial_state=None,
             initial_norm=None):
     """ssd_forward: y [B,H,N,d_h] fp32 (den and final states optional outputs;
-    initial states optional inputs)."""
+    initial states optional inputs).  workspace: a uint8 device tensor, None
+    (one is allocated), or "noalloc" for ssd_forward_noalloc (the library's
+    per-device scratch; sizes up to SSD_NOALLOC_SCRATCH_BYTES of workspace)."""
     torch = _torch()
     _require(q, "q")
     dev = q.device
@@ -216,6 +222,12 @@ def forward(q, k, v, dt, a_cs, order: int, chunk: int, *, y=None, den=None,
                     ("initial_state", initial_state), ("initial_norm", initial_norm)):
         if t is not None:
             _require(t, name, torch.float32, dev)
+    if workspace == "noalloc":
+        # ssd_forward_noalloc: the library's own per-device scratch, no workspace
+        _check(lib().ssd_forward_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(dt), _ptr(a_cs), _ptr(initial_state),
+                                         _ptr(initial_norm), B, H, N, d_h, order, chunk, dtype, _ptr(y),
+                                         _ptr(den), _ptr(final_state), _ptr(final_norm), _stream(dev)))
+        return y
     need = workspace_size(B, H, N, d_h, order, chunk, dtype)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)

@@ -18,7 +18,8 @@ def lib():
 def test_exports_every_header_function(lib):
     names = ssd.header_functions()
     assert set(names) >= {"ssd_prep", "ssd_prep_amask", "ssd_forward", "ssd_forward_workspace_size",
-                          "ssd_decode_step", "ssd_decode_step_amask", "ssd_decode_step_conv",
+                          "ssd_forward_noalloc", "ssd_decode_step", "ssd_decode_step_amask",
+                          "ssd_decode_step_conv",
                           "ssd_state_pack",
                           "ssd_state_unpack", "ssd_backward", "ssd_backward_workspace_size",
                           "ssd_prep_backward", "ssd_prep_amask_backward",
@@ -99,6 +100,24 @@ def test_forward_errors(lib):
     assert fwd(lib, s0=A[12], z0=A[13], fs=A[12], fn=A[14]) == 5  # final_state aliases initial_state
     assert fwd(lib, wbytes=16) == 6
     assert fwd(lib, ws=0) == 6
+
+
+def fwd_noalloc(lib, *, B=1, H=2, N=100, d_h=64, order=1, q=A[0], y=A[10]):
+    return lib.ssd_forward_noalloc(q, A[1], A[2], A[3], A[4], None, None, B, H, N, d_h, order, 64, 1,
+                                   y, None, None, None, None)
+
+
+def test_forward_noalloc_errors(lib):
+    # sizes whose workspace exceeds the library's per-device scratch are
+    # rejected before any HIP call (every call here is invalid)
+    assert lib.ssd_forward_workspace_size(2, 16, 4096, 64, 2, 64, 1) > ssd.SSD_NOALLOC_SCRATCH_BYTES
+    assert fwd_noalloc(lib, B=2, H=16, N=4096, order=2) == 6
+    msg = lib.ssd_last_error().decode()
+    assert "scratch" in msg and str(ssd.SSD_NOALLOC_SCRATCH_BYTES) in msg
+    assert fwd_noalloc(lib, q=None) == 1
+    assert fwd_noalloc(lib, d_h=48) == 3
+    assert fwd_noalloc(lib, y=A[1]) == 5  # y aliases k
+    assert fwd_noalloc(lib, B=0) == 0     # empty: nothing to do
 
 
 def test_workspace_size(lib):

@@ -329,7 +329,11 @@ ssd_status ssd_state_unpack(const float* state_p, const float* norm_p, int64_t B
  * recomputed, the gradient of the state leaving each block is scanned in
  * reverse, and each block then forms its gradients from its own tokens and
  * those two states (at order 2 the d_h^2-row states go through HBM, one
- * 1 MiB slot per block and head each).  All arithmetic is fp32.
+ * 1 MiB slot per block and head each).  Sums, scans and pair quantities are
+ * fp32; the matrix products run on the bf16 matrix cores with each fp32
+ * operand split into a high and a low bf16 part (three products per pair of
+ * operands), so every product term carries up to about 3 * 2^-16 of its
+ * magnitude instead of fp32's 2^-24, for fp32 and bf16 inputs alike.
  *
  *   q, k, v, dt, a_cs, B..dtype   exactly as given to ssd_forward (dt may be NULL)
  *   y, den    [B,H,N,d_h], [B,H,N] f32   ssd_forward's outputs (den is required)

@@ -1,5 +1,8 @@
-// Backward pass of the order-1 chunked mixer (ssd_backward) and of the
-// discretisations (ssd_prep_backward, ssd_prep_amask_backward).
+// Backward pass of the chunked mixer, orders 1 and 2 (ssd_backward), and of
+// the discretisations (ssd_prep_backward, ssd_prep_amask_backward).  The
+// derivation below is written for order 1; order 2 (the squared scores of
+// Algorithm 5, the d_h^2-row states of Algorithm 6) follows it with the
+// order-2 features and is described at its kernels further down.
 //
 // The pages train these models but print no gradients; what is computed here
 // is the chain rule applied to the same definitions as the forward pass

@@ -60,6 +60,7 @@ TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "k_o2_state": ["fwd_o2_state.hip", "launch.h", "common.h"],
     "k_o2_blockprep": ["fwd_o2_prep.hip", "launch.h", "common.h"],
+    "k_o2_scale_scan": ["fwd_o2_prep.hip", "launch.h", "common.h"],
     "k_output": ["fwd_blocks.hip", "launch.h", "common.h"],
     "k_decode": ["decode.hip", "launch.h", "common.h"],
     "k_prep": ["prep.hip", "launch.h", "common.h"],
@@ -187,6 +188,11 @@ def bench_forward(cfg: I.Config, steps: int, warmup: int, dev, amask: bool = Fal
                            + 2 * (D * d + D))
         res["step_alg_flops"] = F
         res["step_mfma_frac"] = F / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+        # measured HBM bytes per launch of every kernel of the step (rocprofv3
+        # counters in profiles/traffic.json; null where the sources changed)
+        res["kernel_traffic_bytes"] = {k: measured_traffic(k, cfg.name) for k in
+                                       ("k_prep", "k_o2_blockprep", "k_o2_scale_scan", "k_o2_state", "k_output")}
+        res["step_alg_bytes"] = B * H * N * (3 * d * 2 + 4 + 4 * d)
     else:
         es = 2 if cfg.dtype == I.BF16 else 4
         # output kernel: q, k, v, dt and a_cs read, y written (the entering

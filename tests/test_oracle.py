@@ -694,6 +694,25 @@ def test_backward_invariances(order):
 
 
 @pytest.mark.parametrize("order", [1, 2])
+def test_backward_decay_gradient_from_key_gradients(order):
+    """An identity of the definition, derived independently of the pair sums
+    the oracle uses for da: with W_ij = (q_i . k_j)^p e^{cs_i - cs_j},
+    sum_j dW_ij W_ij = (q_i . dq_i) / p and sum_i dW_ij W_ij = (k_j . dk_j) / p,
+    so dcs_t = (q_t . dq_t - k_t . dk_t) / p; the first term vanishes (y_t is
+    homogeneous of degree 0 in q_t), hence da_t = -(1/p) sum_{s >= t} k_s . dk_s
+    over the whole sequence.  A slip in the oracle's decay gradient (a sign, a
+    row/column sum, the direction of the cumsum, the decay factor of the
+    pairs) breaks it."""
+    rng = np.random.default_rng(67)
+    q, k, v, a = rand_case(rng, 2, 2, 70, 5, a_scale=0.6)
+    dy = rng.standard_normal(v.shape)
+    g = O.backward_quadratic(q, k, v, a, order, dy)
+    kdk = (k * g["dk"]).sum(axis=-1)
+    da = -np.cumsum(kdk[..., ::-1], axis=-1)[..., ::-1] / order
+    np.testing.assert_allclose(g["da"], da, rtol=1e-9, atol=1e-12 * np.abs(g["da"]).max())
+
+
+@pytest.mark.parametrize("order", [1, 2])
 @pytest.mark.parametrize("case", ["one_token", "two_tokens"])
 def test_golden_backward_error_scale(case, order):
     """The gradients' error scales (the backward parity metric) against values

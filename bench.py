@@ -16,7 +16,7 @@ the timed steps record none), against MI355X's published dense bf16 MFMA peak (2
 bandwidth (8 TB/s).  Algorithmic work per launch (see the design notes):
   order-2 numerator state scan: 4 * D * d_h flops per token and head
       (2 D d_h for phi(q)^T S, 2 D d_h for the phi(k) (v dt)^T update),
-  order-1 output kernel: q, k, v, dt, a_cs read and y written per token and
+  order-1 scan kernel (bf16): q, k, v, dt, a_cs read and y written per token and
       head (3 d_h s_in + 8 + 4 d_h bytes); the whole order-1 step is also
       reported against its algorithmic bytes (3 d_h s_in + 4 + 4 d_h: q, k, v
       and dt_P read, y written),
@@ -62,6 +62,7 @@ KERNEL_SOURCES = {
     "k_o2_blockprep": ["fwd_o2_prep.hip", "launch.h", "common.h"],
     "k_o2_scale_scan": ["fwd_o2_prep.hip", "launch.h", "common.h"],
     "k_output": ["fwd_blocks.hip", "launch.h", "common.h"],
+    "k_o1_scan": ["fwd_o1_scan.hip", "launch.h", "common.h"],
     "k_decode": ["decode.hip", "launch.h", "common.h"],
     "k_prep": ["prep.hip", "launch.h", "common.h"],
 }
@@ -90,7 +91,9 @@ def measured_traffic(kernel: str, workload: str):
     return t["traffic_bytes"]
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
-KERNELS_O1 = ["block_state", "state_pass", "output"]
+# order 1 with bf16 inputs: the segment aggregates (none when the sequence is
+# one segment) and the scan itself
+KERNELS_O1 = ["segment_aggregates", "o1_scan"]
 KERNELS_O2 = ["block_prep", "scale_and_norm_scans", "o2_state_scan", "output"]
 
 
@@ -195,14 +198,14 @@ def bench_forward(cfg: I.Config, steps: int, warmup: int, dev, amask: bool = Fal
         res["step_alg_bytes"] = B * H * N * (3 * d * 2 + 4 + 4 * d)
     else:
         es = 2 if cfg.dtype == I.BF16 else 4
-        # output kernel: q, k, v, dt and a_cs read, y written (the entering
-        # states it also reads are the implementation's, not the method's)
+        # the scan kernel: q, k, v, dt and a_cs read, y written (the segment
+        # aggregates it also reads are the implementation's, not the method's)
         by = B * H * N * (3 * d * es + 8 + 4 * d)
-        t_ms = kern_ms["output"]
+        t_ms = kern_ms["o1_scan"]
         ach = by / (t_ms * 1e-3) / 1e9
-        res["roofline"] = {"kernel": "k_output", "bound": "hbm", "achieved": ach,
+        res["roofline"] = {"kernel": "k_o1_scan", "bound": "hbm", "achieved": ach,
                            "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                           "traffic": measured_traffic("k_output", cfg.name),
+                           "traffic": measured_traffic("k_o1_scan", cfg.name),
                            "alg_bytes_per_launch": by, "avg_launch_ms": t_ms}
         # the whole step (prep + forward) against the method's bytes: q, k, v
         # and dt_P read, y written

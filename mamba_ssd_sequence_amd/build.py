@@ -22,7 +22,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libssd.so")
 
 ARCH = "gfx950"
-SOURCES = ["api.cpp", "prep.hip", "fwd_blocks.hip", "fwd_o2_prep.hip", "fwd_o2_state.hip", "decode.hip",
+SOURCES = ["api.cpp", "prep.hip", "fwd_blocks.hip", "fwd_o1_scan.hip", "fwd_o2_prep.hip", "fwd_o2_state.hip", "decode.hip",
            "bwd.hip"]
 
 # Packed fp32 VALU ops are disabled for all device code: the kernels use plain

@@ -304,6 +304,24 @@ ssd_status forward_core(const char* fn, bool noalloc, const void* q, const void*
   float* tb = ws + L.tb;
   float* st = ws + L.state;
   hipError_t e;
+  if (order == 1 && bf && ssd::o1_scan_supported(BH, d_h, N)) {
+    // bf16 inputs: the sequential scan per (head, segment); the segment
+    // aggregates (when the sequence is cut into segments) go to the state
+    // region of the workspace
+    float* agg = st;
+    const size_t na = (ssd::o1_scan_agg_floats(BH, d_h, N) + 63) & ~(size_t)63;
+    float* sink = st + na;
+    if (na + 64 > L.part - L.state)
+      return fail(SSD_ERR_WORKSPACE, "%s: internal: segment aggregates exceed the workspace", fn);
+    if ((e = ssd::launch_o1_scan(true, d_h, q, k, v, dt, a_cs, BH, N, chunk, nullptr, nullptr, agg,
+                                 nullptr, nullptr, nullptr, nullptr, sink, stream)) != hipSuccess)
+      return hip_status(e, "o1_scan aggregate launch");
+    tm.mark();
+    e = ssd::launch_o1_scan(false, d_h, q, k, v, dt, a_cs, BH, N, chunk, initial_state, initial_norm,
+                            agg, y, den, final_state, final_norm, sink, stream);
+    tm.mark();
+    return hip_status(e, "o1_scan launch");
+  }
   if (order == 1) {
     if ((e = ssd::launch_chunk_state(bf, d_h, k, v, dt, a_cs, BH, N, chunk, tb, st, stream)) != hipSuccess)
       return hip_status(e, "chunk_state launch");

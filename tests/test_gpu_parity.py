@@ -8,6 +8,8 @@ configuration the benchmark times and checked on sampled rows (first and last
 block, block boundaries +-1, random rows), which the oracle evaluates one by
 one.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -25,6 +27,12 @@ def _gpu():
         pytest.skip("no GPU")
     from mamba_ssd_sequence_amd import ssd
     ssd.lib()
+
+
+# the workloads, plus order 1 with bf16 inputs at d_h 32 (two 16-column
+# slices per head in the order-1 scan)
+TEST_CONFIGS = {**I.ALL_CONFIGS,
+                "o1_bf16_d32": dataclasses.replace(I.CONFIGS["o1_bf16_2k"], name="o1_bf16_d32", d_h=32)}
 
 
 def ssd_mod():
@@ -100,6 +108,9 @@ SMALL = [
     ("o1_f32_small", 1, 1, 2, 1, 64), ("o1_f32_small", 1, 1, 2, 63, 64), ("o1_f32_small", 1, 1, 2, 65, 128),
     ("o1_f32_small", 1, 2, 1, 200, 64), ("o1_f32_small", 1, 1, 1, 300, 128),
     ("o1_bf16_2k", 1, 1, 2, 1, 64), ("o1_bf16_2k", 1, 1, 2, 129, 64), ("o1_bf16_2k", 1, 2, 2, 333, 128),
+    # order 1, bf16: d_h 32; sequences cut into 2 and 3 segments (a ragged last
+    # block, chunk 64 and 128)
+    ("o1_bf16_d32", 1, 1, 2, 129, 64), ("o1_bf16_d32", 1, 2, 1, 1100, 128), ("o1_bf16_2k", 1, 1, 3, 1500, 64),
     ("o2_bf16_4k", 2, 1, 1, 1, 64), ("o2_bf16_4k", 2, 1, 2, 64, 64), ("o2_bf16_4k", 2, 1, 2, 65, 64),
     ("o2_bf16_4k", 2, 2, 1, 257, 128), ("o2_bf16_4k", 2, 1, 3, 700, 64),
     # 32 heads: the state scan's one-wave-per-column layout and head-to-XCD
@@ -112,7 +123,7 @@ SMALL = [
 @pytest.mark.parametrize("name,order,B,H,N,chunk", SMALL)
 def test_forward_small(name, order, B, H, N, chunk):
     say("forward small", name, order, B, H, N, chunk)
-    cfg = I.CONFIGS[name]
+    cfg = TEST_CONFIGS[name]
     inp = I.make_forward_inputs(cfg, B=B, H=H, N=N, seed=N + 7 * H)
     got = run_forward(inp, order, chunk, want_den=True)
     ref = oracle_forward(inp, order)
@@ -147,9 +158,10 @@ def test_chunk_size_invariance(name):
 # (B, H, N): at order 2, 2 heads use the two-wave-per-column state layout and
 # 32 heads the one-wave layout; N = 300 ends on a step with one block
 @pytest.mark.parametrize("name,B,H,N", [("o1_f32_small", 1, 2, 200), ("o1_bf16_2k", 1, 2, 200),
+                                        ("o1_bf16_2k", 1, 2, 1500), ("o1_bf16_d32", 2, 1, 1300),
                                         ("o2_bf16_4k", 1, 2, 200), ("o2_bf16_4k", 2, 16, 300)])
 def test_final_state_matches_recurrence(name, B, H, N):
-    cfg = I.CONFIGS[name]
+    cfg = TEST_CONFIGS[name]
     say("final state", name, B, H, N)
     inp = I.make_forward_inputs(cfg, B=B, H=H, N=N, seed=11)
     got = run_forward(inp, cfg.order, cfg.chunk, want_final=True)
@@ -181,12 +193,14 @@ def _forward_arrays(cfg, q, k, v, dtp, bias, alog, order, chunk, S0=None, z0=Non
 # two-wave-per-column state layout and 32 heads the one-wave layout
 @pytest.mark.parametrize("name,B,H,N,chunk,n1", [
     ("o1_f32_small", 1, 2, 200, 64, 100), ("o1_bf16_2k", 1, 2, 300, 128, 191),
+    ("o1_bf16_2k", 1, 2, 3000, 128, 1000), ("o1_bf16_d32", 1, 1, 2300, 64, 700),
     ("o2_bf16_4k", 1, 2, 300, 64, 128), ("o2_bf16_4k", 1, 2, 250, 128, 77),
     ("o2_bf16_4k", 2, 16, 300, 64, 150)])
 def test_initial_state_continues_the_sequence(name, B, H, N, chunk, n1):
     """ssd_forward from the states a prefix leaves (Algorithm 6 hand-off) gives
-    the full sequence's outputs for the suffix and its final states."""
-    cfg = I.CONFIGS[name]
+    the full sequence's outputs for the suffix and its final states (order 1
+    with bf16 inputs: prefix and suffix are cut into segments)."""
+    cfg = TEST_CONFIGS[name]
     say("initial state", name, B, H, N, chunk, n1)
     inp = I.make_forward_inputs(cfg, B=B, H=H, N=N, seed=5 + n1)
     order = cfg.order

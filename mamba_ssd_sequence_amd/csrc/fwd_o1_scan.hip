@@ -10,11 +10,10 @@
 // is a non-positive difference of chunk-local cumsums).
 //
 // Segments: the sequence is cut into nseg segments of whole blocks so that
-// the heads times segments cover the CUs.  An aggregate pass (AGG) runs the
-// same loop over segments 0 .. nseg-2 with the state update only, from a zero
-// state, and writes each segment's state contribution and total log-decay;
-// the full pass of segment s starts from the initial state carried through
-// those aggregates (S <- 2^{T_s'} S + A_s' for s' < s).
+// the heads times segments cover the CUs twice.  An aggregate pass
+// (k_o1_segagg) writes the state contribution and total log-decay of each
+// segment but the last; the scan of segment s starts from the initial state
+// carried through those aggregates (S <- 2^{T_s'} S + A_s' for s' < s).
 //
 // Per block, wave w owns query rows 16 w .. 16 w + 15 and (for the update)
 // state rows b = 16 w .. 16 w + 15 (d_h 32: waves 0, 1), every value column.
@@ -43,11 +42,11 @@ namespace ssd {
 
 namespace {
 
-template <int DH, bool AGG>
+template <int DH>
 struct alignas(16) O1Set {
   static constexpr int PQ = DH + 8;   // pitch (elements) of rows indexed by feature
   static constexpr int PJ = BLK + 8;  // pitch of rows indexed by token
-  __bf16 K[AGG ? 8 : BLK * PQ];  // [j][d]
+  __bf16 K[BLK * PQ];   // [j][d]
   __bf16 KT[DH * PJ];   // [d][j]
   __bf16 VT[DH * PJ];   // [c][j]
   float cs[BLK];        // block-relative cumsum, log2 units
@@ -75,7 +74,7 @@ struct O1Regs {
 
 }  // namespace
 
-template <int DH, bool AGG>
+template <int DH>
 __global__ __launch_bounds__(256) void k_o1_scan(const uint16_t* __restrict__ q,
                                                  const uint16_t* __restrict__ k,
                                                  const uint16_t* __restrict__ v,
@@ -92,7 +91,7 @@ __global__ __launch_bounds__(256) void k_o1_scan(const uint16_t* __restrict__ q,
   constexpr int NKP = (BLK / 2) * SEG;  // threads staging k and v as token pairs
   constexpr int NSW = DH / 16;          // waves that hold state rows
   constexpr int AGGF = DH * DH + DH + 1;  // floats per aggregate
-  using Set = O1Set<DH, AGG>;
+  using Set = O1Set<DH>;
   using Stt = O1State<DH>;
   constexpr int PQ = Set::PQ, PJ = Set::PJ, PS = Stt::PS;
   constexpr int NKS = DH / 32;          // 32-wide steps over d
@@ -100,10 +99,9 @@ __global__ __launch_bounds__(256) void k_o1_scan(const uint16_t* __restrict__ q,
   __shared__ __attribute__((aligned(16))) Set sets[2];
   __shared__ __attribute__((aligned(16))) Stt sts[1];
 
-  const int nps = AGG ? nseg - 1 : nseg;  // segments this pass covers per head
   const int p = blockIdx.x;
-  if (p >= BH * nps) return;
-  const int bh = p / nps, seg = p - bh * nps;
+  if (p >= BH * nseg) return;
+  const int bh = p / nseg, seg = p - bh * nseg;
   const int nblk = (N + BLK - 1) / BLK;
   const int b0 = seg * nbs, b1 = b0 + nbs < nblk ? b0 + nbs : nblk;
   // per-head bases; offsets within a head are 32-bit
@@ -145,10 +143,8 @@ __global__ __launch_bounds__(256) void k_o1_scan(const uint16_t* __restrict__ q,
   auto stage_block = [&](int b, const O1Regs& R, Set& S) {
     const int nv = N - b * BLK < BLK ? N - b * BLK : BLK;
     if (tid < NKP) {
-      if (!AGG) {
-        *reinterpret_cast<uint4*>(&S.K[jp * PQ + sgp * 8]) = R.k0;
-        *reinterpret_cast<uint4*>(&S.K[(jp + 1) * PQ + sgp * 8]) = R.k1;
-      }
+      *reinterpret_cast<uint4*>(&S.K[jp * PQ + sgp * 8]) = R.k0;
+      *reinterpret_cast<uint4*>(&S.K[(jp + 1) * PQ + sgp * 8]) = R.k1;
       // transposed: the token pair (jp, jp + 1) of one feature / column per store
       const uint32_t a[4] = {R.k0.x, R.k0.y, R.k0.z, R.k0.w};
       const uint32_t c[4] = {R.k1.x, R.k1.y, R.k1.z, R.k1.w};
@@ -189,7 +185,7 @@ __global__ __launch_bounds__(256) void k_o1_scan(const uint16_t* __restrict__ q,
   for (int ct = 0; ct < NCT; ++ct) st[ct] = zero4();
   float zs = 0.f;
   const int sb = 16 * wv + 4 * g;  // first state row of this lane
-  if (sw && !AGG) {
+  if (sw) {
     if (S0) {
       const float* s0 = S0 + (int64_t)bh * DH * DH;
 #pragma unroll
@@ -239,40 +235,35 @@ __global__ __launch_bounds__(256) void k_o1_scan(const uint16_t* __restrict__ q,
       if (g == 0) S.z[bs] = zs;
     }
   };
-  if (!AGG) write_state(sts[0]);
+  write_state(sts[0]);
 
   if (b0 % chunk_blocks != 0) prev_raw = csh[b0 * BLK - 1];
   O1Regs R;
   bf16x8 qc[NKS], qn[NKS];
-  if (!AGG) load_q(b0, qn);
+  load_q(b0, qn);
   load_block(b0, R);
   stage_block(b0, R, sets[0]);
   load_block(b0 + 1 < b1 ? b0 + 1 : b1 - 1, R);
-  if (!AGG) {
-    // stores to the sink, as the loop body issues after its loads: the
-    // compiler's count of memory operations in flight at the loop head then
-    // agrees on both ways in
+  // stores to the sink, as the loop body issues after its loads: the
+  // compiler's count of memory operations in flight at the loop head then
+  // agrees on both ways in
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) *reinterpret_cast<f32x4*>(sink + 4 * g) = st[ct];
-    sink[16] = zs;
-  }
+  for (int ct = 0; ct < NCT; ++ct) *reinterpret_cast<f32x4*>(sink + 4 * g) = st[ct];
+  sink[16] = zs;
   __syncthreads();
 
-  float Tsum = 0.f;  // AGG: the segment's total log-decay (log2 units)
   for (int b = b0; b < b1; ++b) {
     const int cur = (b - b0) & 1;
     Set& S = sets[cur];
     if (b + 1 < b1) stage_block(b + 1, R, sets[cur ^ 1]);
-    if (!AGG) {
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) qc[ks] = qn[ks];
-      load_q(b + 1 < b1 ? b + 1 : b1 - 1, qn);
-    }
+    for (int ks = 0; ks < NKS; ++ks) qc[ks] = qn[ks];
+    load_q(b + 1 < b1 ? b + 1 : b1 - 1, qn);
     load_block(b + 2 < b1 ? b + 2 : b1 - 1, R);  // (a repeat of the last block at the end)
     const int t0 = b * BLK;
     const int nv = N - t0 < BLK ? N - t0 : BLK;
 
-    if constexpr (!AGG) {
+    {
       const Stt& SI = sts[0];
       const float cs_i = S.cs[il];
       // scores s(i = il, j = 16 jt + 4 g + r) for the key tiles jt <= wv,
@@ -368,7 +359,6 @@ __global__ __launch_bounds__(256) void k_o1_scan(const uint16_t* __restrict__ q,
     // state update to the end of the block: S[b][c] = e^T S[b][c] +
     // sum_j (k_jb dw_j) v_jc, the operand k dw split once for every column tile
     const float T = S.T;
-    if (AGG) Tsum += T;
     if (sw) {
       const float eT = exp2_fast(T);
       bf16x8 ah[2], al[2];
@@ -406,24 +396,14 @@ __global__ __launch_bounds__(256) void k_o1_scan(const uint16_t* __restrict__ q,
       }
       zs = eT * zs + sum_over_groups(zp);
     }
-    if (!AGG && b + 1 < b1) {
+    if (b + 1 < b1) {
       __syncthreads();  // every wave is done with the state entering block b
       write_state(sts[0]);
     }
     __syncthreads();
   }
 
-  if constexpr (AGG) {
-    float* a = agg + ((int64_t)bh * (nseg - 1) + seg) * AGGF;
-    if (sw) {
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) a[(sb + r) * DH + 16 * ct + n] = st[ct][r];
-      if (g == 0) a[DH * DH + bs] = zs;
-    }
-    if (tid == 0) a[DH * DH + DH] = Tsum;
-  } else {
+  {
     if (Sf && seg == nseg - 1 && sw) {
       float* sf = Sf + (int64_t)bh * DH * DH;
 #pragma unroll
@@ -433,6 +413,186 @@ __global__ __launch_bounds__(256) void k_o1_scan(const uint16_t* __restrict__ q,
       if (g == 0) zf[(int64_t)bh * DH + bs] = zs;
     }
   }
+}
+
+// Segment aggregates (the scan forms each segment's entering state from them)
+// with the four waves of a
+// workgroup on four contiguous quarters of the segment at once: each wave
+// runs its quarter's blocks with no barrier, A_w <- 2^T A_w + C_blk with
+// C_blk = sum_j (k_j dw_j) (v_j)^T and z_w likewise, in its own LDS buffers;
+// then A = sum_w 2^{T after quarter w} A_w, and the same for z.  The products
+// are those of the scan's update (16x16x32 bf16, the operand k dw in high +
+// low parts); z_b = sum_j w_j k_jb is summed alongside the split.
+template <int DH>
+__global__ __launch_bounds__(256) void k_o1_segagg(const uint16_t* __restrict__ k,
+                                                   const uint16_t* __restrict__ v,
+                                                   const float* __restrict__ dt,
+                                                   const float* __restrict__ a_cs, int BH, int N,
+                                                   int chunk_blocks, int nseg, int nbs,
+                                                   float* __restrict__ agg) {
+  constexpr int NT = DH / 16;            // 16-wide tiles of the state rows and columns
+  constexpr int SEG = DH / 8;            // 16-byte segments per row
+  constexpr int NIT = (BLK / 2) * SEG / WAVE;  // (token pair, segment) items per lane
+  constexpr int PJ = BLK + 8;
+  constexpr int AGGF = DH * DH + DH + 1;
+  struct alignas(16) WaveBuf {
+    __bf16 KT[DH * PJ];  // [d][j]
+    __bf16 VT[DH * PJ];  // [c][j]
+    float w[BLK];        // 2^{T - cs_j}, 0 past the block's end
+    float dw[BLK];       // w_j dt_j
+  };
+  static_assert(sizeof(WaveBuf) >= (DH * DH + DH) * sizeof(float), "partials fit a wave's buffer");
+  __shared__ __attribute__((aligned(16))) WaveBuf wb[4];
+  __shared__ float wT[4];
+
+  const int p = blockIdx.x;
+  if (p >= BH * (nseg - 1)) return;
+  const int bh = p / (nseg - 1), seg = p - bh * (nseg - 1);
+  const int nblk = (N + BLK - 1) / BLK;
+  const int b0 = seg * nbs, b1 = b0 + nbs < nblk ? b0 + nbs : nblk;
+  const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, n = lane & 15, g = lane >> 4;
+  const int qr = (b1 - b0 + 3) / 4;  // blocks per quarter
+  const int bw0 = b0 + wv * qr < b1 ? b0 + wv * qr : b1;
+  const int bw1 = bw0 + qr < b1 ? bw0 + qr : b1;
+  const uint16_t* kh = k + (int64_t)bh * N * DH;
+  const uint16_t* vh = v + (int64_t)bh * N * DH;
+  const float* csh = a_cs + (int64_t)bh * N;
+  const float* dth = (dt ? dt : a_cs) + (int64_t)bh * N;
+  WaveBuf& B = wb[wv];
+
+  // acc[bt][ct][r] = A_w[b = 16 bt + 4 g + r][c = 16 ct + n]; zacc[bt]: z_w[16 bt + n]
+  f32x4 acc[NT][NT];
+#pragma unroll
+  for (int bt = 0; bt < NT; ++bt)
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct) acc[bt][ct] = zero4();
+  float zacc[NT];
+#pragma unroll
+  for (int bt = 0; bt < NT; ++bt) zacc[bt] = 0.f;
+  float Tw = 0.f;
+
+  uint4 rk0[NIT], rk1[NIT], rv0[NIT], rv1[NIT];
+  float rcs = 0.f, rdt = 0.f;
+  auto load = [&](int b) {
+    const int t0 = b * BLK;
+    const int last = (N - t0 < BLK ? N - t0 : BLK) - 1;
+#pragma unroll
+    for (int u = 0; u < NIT; ++u) {
+      const int it = lane + WAVE * u, jp = 2 * (it / SEG), sg = it % SEG;
+      const int ja = t0 + (jp < last ? jp : last), jb = t0 + (jp + 1 < last ? jp + 1 : last);
+      rk0[u] = *reinterpret_cast<const uint4*>(kh + ja * DH + sg * 8);
+      rk1[u] = *reinterpret_cast<const uint4*>(kh + jb * DH + sg * 8);
+      rv0[u] = *reinterpret_cast<const uint4*>(vh + ja * DH + sg * 8);
+      rv1[u] = *reinterpret_cast<const uint4*>(vh + jb * DH + sg * 8);
+    }
+    const int tl = t0 + (lane < last ? lane : last);
+    rcs = csh[tl];
+    rdt = dth[tl];
+  };
+  float prev_raw = 0.f;
+  if (bw0 < bw1 && bw0 % chunk_blocks != 0) prev_raw = csh[bw0 * BLK - 1];
+  for (int b = bw0; b < bw1; ++b) {
+    const int nv = N - b * BLK < BLK ? N - b * BLK : BLK;
+    load(b);
+    // stage this block (transposed token pairs)
+#pragma unroll
+    for (int u = 0; u < NIT; ++u) {
+      const int it = lane + WAVE * u, jp = 2 * (it / SEG), sg = it % SEG;
+      const uint32_t a[4] = {rk0[u].x, rk0[u].y, rk0[u].z, rk0[u].w};
+      const uint32_t c[4] = {rk1[u].x, rk1[u].y, rk1[u].z, rk1[u].w};
+      const uint32_t e[4] = {rv0[u].x, rv0[u].y, rv0[u].z, rv0[u].w};
+      const uint32_t f[4] = {rv1[u].x, rv1[u].y, rv1[u].z, rv1[u].w};
+#pragma unroll
+      for (int uu = 0; uu < 4; ++uu) {
+        const int d = sg * 8 + 2 * uu;
+        *reinterpret_cast<uint32_t*>(&B.KT[d * PJ + jp]) = (a[uu] & 0xffffu) | (c[uu] << 16);
+        *reinterpret_cast<uint32_t*>(&B.KT[(d + 1) * PJ + jp]) = (a[uu] >> 16) | (c[uu] & 0xffff0000u);
+        *reinterpret_cast<uint32_t*>(&B.VT[d * PJ + jp]) = (e[uu] & 0xffffu) | (f[uu] << 16);
+        *reinterpret_cast<uint32_t*>(&B.VT[(d + 1) * PJ + jp]) = (e[uu] >> 16) | (f[uu] & 0xffff0000u);
+      }
+    }
+    const float lastv = __shfl(rcs, nv - 1, WAVE);
+    const float base = (b % chunk_blocks == 0) ? 0.f : prev_raw;
+    prev_raw = lastv;
+    const float T = (lastv - base) * LOG2E;
+    {
+      const bool ok = lane < nv;
+      const float cs = ok ? (rcs - base) * LOG2E : T;
+      const float w = ok ? exp2_fast(T - cs) : 0.f;
+      B.w[lane] = w;
+      B.dw[lane] = w * (ok ? (dt ? rdt : 1.f) : 0.f);
+    }
+    __builtin_amdgcn_wave_barrier();  // (the wave's own LDS writes precede its reads)
+
+    const float eT = exp2_fast(T);
+    Tw += T;
+#pragma unroll
+    for (int bt = 0; bt < NT; ++bt) {
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct) acc[bt][ct] *= eT;
+    }
+    float zp[NT];
+#pragma unroll
+    for (int bt = 0; bt < NT; ++bt) zp[bt] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(&B.dw[32 * ks + 8 * g]);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(&B.dw[32 * ks + 8 * g + 4]);
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(&B.w[32 * ks + 8 * g]);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(&B.w[32 * ks + 8 * g + 4]);
+      bf16x8 bv[NT];
+#pragma unroll
+      for (int ct = 0; ct < NT; ++ct)
+        bv[ct] = *reinterpret_cast<const bf16x8*>(&B.VT[(16 * ct + n) * PJ + 32 * ks + 8 * g]);
+#pragma unroll
+      for (int bt = 0; bt < NT; ++bt) {
+        const bf16x8 kt = *reinterpret_cast<const bf16x8*>(&B.KT[(16 * bt + n) * PJ + 32 * ks + 8 * g]);
+        bf16x8 ah, al;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float kv = (float)kt[e];
+          const float x = kv * (e < 4 ? d0[e] : d1[e - 4]);
+          zp[bt] += kv * (e < 4 ? w0[e] : w1[e - 4]);
+          const __bf16 h = (__bf16)x;
+          ah[e] = h;
+          al[e] = (__bf16)(x - (float)h);
+        }
+#pragma unroll
+        for (int ct = 0; ct < NT; ++ct) {
+          acc[bt][ct] = mfma_bf16(ah, bv[ct], acc[bt][ct]);
+          acc[bt][ct] = mfma_bf16(al, bv[ct], acc[bt][ct]);
+        }
+      }
+    }
+#pragma unroll
+    for (int bt = 0; bt < NT; ++bt) zacc[bt] = eT * zacc[bt] + sum_over_groups(zp[bt]);
+    __builtin_amdgcn_wave_barrier();  // (reads of this block before the next staging)
+  }
+
+  // combine the quarters: A = sum_w 2^{T_{w+1} + .. + T_3} A_w
+  if (lane == 0) wT[wv] = Tw;
+  __syncthreads();
+  float after = 0.f;
+  for (int w2 = wv + 1; w2 < 4; ++w2) after += wT[w2];
+  const float f = exp2_fast(after);
+  float* part = reinterpret_cast<float*>(&B);  // [b][c] then z[b]
+#pragma unroll
+  for (int bt = 0; bt < NT; ++bt) {
+#pragma unroll
+    for (int ct = 0; ct < NT; ++ct)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) part[(16 * bt + 4 * g + r) * DH + 16 * ct + n] = f * acc[bt][ct][r];
+    if (g == 0) part[DH * DH + 16 * bt + n] = f * zacc[bt];
+  }
+  __syncthreads();
+  float* a = agg + ((int64_t)bh * (nseg - 1) + seg) * AGGF;
+  for (int e = tid; e < DH * DH + DH; e += 256) {
+    float x = 0.f;
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) x += reinterpret_cast<const float*>(&wb[w2])[e];
+    a[e] = x;
+  }
+  if (tid == 0) a[DH * DH + DH] = (wT[0] + wT[1]) + (wT[2] + wT[3]);
 }
 
 // Segments: enough workgroups for two per CU where the sequence allows,
@@ -474,15 +634,19 @@ hipError_t launch_o1_scan(bool agg_pass, int64_t DH, const void* q, const void* 
   const uint16_t* kk = static_cast<const uint16_t*>(k);
   const uint16_t* vv = static_cast<const uint16_t*>(v);
   const int cb = (int)(chunk / BLK);
-#define SSD_O1_SCAN(DHV, AG)                                                                    \
-  hipLaunchKernelGGL((k_o1_scan<DHV, AG>), grid, blk, 0, stream, qq, kk, vv, dt, a_cs, (int)BH, \
+#define SSD_O1_SCAN(DHV)                                                                    \
+  hipLaunchKernelGGL((k_o1_scan<DHV>), grid, blk, 0, stream, qq, kk, vv, dt, a_cs, (int)BH, \
                      (int)N, cb, nseg, nbs, S0, z0, agg, y, den, Sf, zf, sink)
   if (agg_pass) {
-    if (DH == 64) SSD_O1_SCAN(64, true);
-    else SSD_O1_SCAN(32, true);
+    if (DH == 64)
+      hipLaunchKernelGGL((k_o1_segagg<64>), grid, blk, 0, stream, kk, vv, dt, a_cs, (int)BH, (int)N, cb,
+                         nseg, nbs, agg);
+    else
+      hipLaunchKernelGGL((k_o1_segagg<32>), grid, blk, 0, stream, kk, vv, dt, a_cs, (int)BH, (int)N, cb,
+                         nseg, nbs, agg);
   } else {
-    if (DH == 64) SSD_O1_SCAN(64, false);
-    else SSD_O1_SCAN(32, false);
+    if (DH == 64) SSD_O1_SCAN(64);
+    else SSD_O1_SCAN(32);
   }
 #undef SSD_O1_SCAN
   return hipGetLastError();

@@ -63,6 +63,7 @@ KERNEL_SOURCES = {
     "k_o2_scale_scan": ["fwd_o2_prep.hip", "launch.h", "common.h"],
     "k_output": ["fwd_blocks.hip", "launch.h", "common.h"],
     "k_o1_scan": ["fwd_o1_scan.hip", "launch.h", "common.h"],
+    "k_o1_segagg": ["fwd_o1_scan.hip", "launch.h", "common.h"],
     "k_decode": ["decode.hip", "launch.h", "common.h"],
     "k_prep": ["prep.hip", "launch.h", "common.h"],
 }

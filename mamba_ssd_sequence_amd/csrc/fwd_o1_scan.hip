@@ -281,12 +281,22 @@ __global__ __launch_bounds__(256) void k_o1_scan(const uint16_t* __restrict__ q,
                             qc[ks], acc);
           const f32x4 csj = *reinterpret_cast<const f32x4*>(&S.cs[16 * jt + 4 * g]);
           const f32x4 dtj = *reinterpret_cast<const f32x4*>(&S.dt[16 * jt + 4 * g]);
+          if (jt < wv && nv == BLK) {
+            // a key tile wholly before the wave's rows of a full block: no mask
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int j = 16 * jt + 4 * g + r;
-            const float w = (j <= il && j < nv) ? acc[r] * exp2_fast(cs_i - csj[r]) : 0.f;
-            den_l += w;
-            Wd[jt][r] = w * dtj[r];
+            for (int r = 0; r < 4; ++r) {
+              const float w = acc[r] * exp2_fast(cs_i - csj[r]);
+              den_l += w;
+              Wd[jt][r] = w * dtj[r];
+            }
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int j = 16 * jt + 4 * g + r;
+              const float w = (j <= il && j < nv) ? acc[r] * exp2_fast(cs_i - csj[r]) : 0.f;
+              den_l += w;
+              Wd[jt][r] = w * dtj[r];
+            }
           }
         }
       }
@@ -361,15 +371,21 @@ __global__ __launch_bounds__(256) void k_o1_scan(const uint16_t* __restrict__ q,
     const float T = S.T;
     if (sw) {
       const float eT = exp2_fast(T);
+      // (z_b = sum_j w_j k_jb is summed over the same 16 tokens of this lane)
       bf16x8 ah[2], al[2];
+      float zp = 0.f;
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 kt = *reinterpret_cast<const bf16x8*>(&S.KT[bs * PJ + 32 * ks + 8 * g]);
         const f32x4 d0 = *reinterpret_cast<const f32x4*>(&S.dw[32 * ks + 8 * g]);
         const f32x4 d1 = *reinterpret_cast<const f32x4*>(&S.dw[32 * ks + 8 * g + 4]);
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(&S.w[32 * ks + 8 * g]);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(&S.w[32 * ks + 8 * g + 4]);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float x = (float)kt[e] * (e < 4 ? d0[e] : d1[e - 4]);
+          const float kv = (float)kt[e];
+          const float x = kv * (e < 4 ? d0[e] : d1[e - 4]);
+          zp += kv * (e < 4 ? w0[e] : w1[e - 4]);
           const __bf16 h = (__bf16)x;
           ah[ks][e] = h;
           al[ks][e] = (__bf16)(x - (float)h);
@@ -384,15 +400,6 @@ __global__ __launch_bounds__(256) void k_o1_scan(const uint16_t* __restrict__ q,
           st[ct] = mfma_bf16(ah[ks], bv, st[ct]);
           st[ct] = mfma_bf16(al[ks], bv, st[ct]);
         }
-      }
-      float zp = 0.f;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const bf16x8 kt = *reinterpret_cast<const bf16x8*>(&S.KT[bs * PJ + 16 * g + 8 * u]);
-        const f32x4 wa = *reinterpret_cast<const f32x4*>(&S.w[16 * g + 8 * u]);
-        const f32x4 wb = *reinterpret_cast<const f32x4*>(&S.w[16 * g + 8 * u + 4]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) zp += (float)kt[e] * wa[e] + (float)kt[4 + e] * wb[e];
       }
       zs = eT * zs + sum_over_groups(zp);
     }

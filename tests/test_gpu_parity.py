@@ -280,11 +280,12 @@ def test_graph_capture_replays_match_eager(name, order):
 # forward: the full-size workloads, sampled rows
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("name", ["o1_f32_small", "o1_bf16_2k", "o2_bf16_4k", "o1_bf16_4k"])
+@pytest.mark.parametrize("name", ["o1_f32_small", "o1_bf16_2k", "o2_bf16_4k", "o1_bf16_4k", "o1_bf16_d32"])
 def test_forward_full_size_all_rows(name):
     """The workloads up to N = 4096 at full size, in the benchmark's launch,
-    against the oracle on every row of every head."""
-    cfg = I.ALL_CONFIGS[name]
+    against the oracle on every row of every head (and order 1 at d_h 32 at
+    the 2K shape)."""
+    cfg = TEST_CONFIGS[name]
     say("forward full, all rows", name)
     inp = I.make_forward_inputs(cfg)
     got = run_forward(inp, cfg.order, cfg.chunk, want_den=True)
@@ -418,6 +419,8 @@ def run_forward_amask(inp, order, chunk, with_dt):
 AMASK = [
     ("o1_f32_small", 1, 1, 2, 200, 64, True), ("o1_bf16_2k", 1, 2, 2, 333, 128, True),
     ("o1_bf16_2k", 1, 1, 2, 130, 64, False),
+    # order 1, bf16: sequences cut into segments (the A-mask's decays through the segment pass)
+    ("o1_bf16_2k", 1, 1, 2, 1500, 64, True), ("o1_bf16_d32", 1, 1, 1, 1100, 128, False),
     ("o2_bf16_4k", 2, 1, 2, 257, 64, False), ("o2_bf16_4k", 2, 2, 16, 300, 64, False),
     ("o2_bf16_4k", 2, 1, 3, 200, 128, True),
 ]
@@ -426,7 +429,7 @@ AMASK = [
 @pytest.mark.parametrize("name,order,B,H,N,chunk,with_dt", AMASK)
 def test_forward_amask_small(name, order, B, H, N, chunk, with_dt):
     say("forward amask", name, order, B, H, N, chunk, with_dt)
-    cfg = I.CONFIGS[name]
+    cfg = TEST_CONFIGS[name]
     inp = I.make_forward_inputs(cfg, B=B, H=H, N=N, seed=3 * N + H)
     y, den = run_forward_amask(inp, order, chunk, with_dt)
     q, k, v = inp.qkv_f64()
@@ -889,37 +892,41 @@ def test_no_decay_is_causal_linear_attention(name):
     assert err <= TOL[cfg.dtype]
 
 
-def test_full_decay_keeps_only_the_token_itself():
-    """A dt -> -inf: every earlier token is masked out and y_i = (v dt)_i
-    (order 2: the diagonal score (q_i . k_i)^2 is positive).  Checked element
-    by element against the oracle (whose error scale is then 2 |(v dt)_ic|:
-    a relative error per element)."""
-    cfg = I.CONFIGS["o2_bf16_4k"]
-    say("full decay")
-    inp = I.make_forward_inputs(cfg, B=1, H=2, N=200, seed=32)
+@pytest.mark.parametrize("name,order,N", [("o2_bf16_4k", 2, 200), ("o1_bf16_2k", 1, 1500)])
+def test_full_decay_keeps_only_the_token_itself(name, order, N):
+    """A dt -> -inf: every earlier token is masked out and y_i = (v dt)_i (the
+    diagonal score cancels; order 2: it is positive).  Checked element by
+    element against the oracle (whose error scale is then 2 |(v dt)_ic|: a
+    relative error per element).  Order 1 at N = 1500 runs through six
+    segments: every state and segment aggregate decays to zero."""
+    cfg = TEST_CONFIGS[name]
+    say("full decay", name, order, N)
+    inp = I.make_forward_inputs(cfg, B=1, H=2, N=N, seed=32)
     inp.A_log[:] = 6.0       # A = -403
     inp.dt_bias[:] = 5.0     # dt ~ 5: a ~ -2000 per token
-    got = run_forward(inp, 2, 64)
+    got = run_forward(inp, order, 64)
     q, k, v = inp.qkv_f64()
     dt, _ = O.discretise(inp.dt_proj, inp.dt_bias, inp.A_log)
-    ref = oracle_forward(inp, 2)
+    ref = oracle_forward(inp, order)
     np.testing.assert_allclose(ref["y"], v * dt[..., None], rtol=1e-12, atol=0)
     err = row_error(got["y"], ref["y"], ref["scale"])
     say("  ", worst(got["y"], ref["y"], ref["scale"]))
     assert err <= TOL[cfg.dtype]
 
 
-def test_constant_value_gives_the_value():
-    """2Mamba with a constant plain V (dt = NULL): every output row is that V
-    (a convex combination of equal rows, Algorithm 5's weights being >= 0).
-    Checked element by element (the oracle's error scale is 2 |V_c| there)."""
-    cfg = I.CONFIGS["o2_bf16_4k"]
-    say("constant value")
-    inp = I.make_forward_inputs(cfg, B=1, H=2, N=333, seed=33)
+@pytest.mark.parametrize("name,order,N", [("o2_bf16_4k", 2, 333), ("o1_bf16_2k", 1, 1500)])
+def test_constant_value_gives_the_value(name, order, N):
+    """A constant plain V (dt = NULL): every output row is that V (a
+    combination of equal rows whose weights sum to one; Algorithm 5's are
+    >= 0).  Checked element by element (the oracle's error scale is 2 |V_c|
+    there at order 2; at order 1 it also carries the normaliser's condition)."""
+    cfg = TEST_CONFIGS[name]
+    say("constant value", name, order, N)
+    inp = I.make_forward_inputs(cfg, B=1, H=2, N=N, seed=33)
     row = inp.v[0, 0, 0].copy()
     inp.v[:] = row
-    got = run_forward(inp, 2, 64, with_dt=False)
-    ref = oracle_forward(inp, 2, with_dt=False)
+    got = run_forward(inp, order, 64, with_dt=False)
+    ref = oracle_forward(inp, order, with_dt=False)
     expect = np.broadcast_to(I.bf16_bits_to_f64(row), ref["y"].shape)
     np.testing.assert_allclose(ref["y"], expect, rtol=1e-12, atol=0)
     err = row_error(got["y"], ref["y"], ref["scale"])

@@ -108,43 +108,51 @@ __device__ __forceinline__ void split_bf16(float x, bf16x8& hi, bf16x8& lo, int 
 // of each product |a_k b_k|.  Lane (n, gq) supplies A[m0 + n][k] and B[k][16 nt
 // + n] for k = kk + gq + 4 e in its operand slot e (the same slots for both
 // operands, so each k is summed once); acc[nt][q4] = out[m0 + 4 gq + q4][16 nt
-// + n] as for every 16x16 MFMA.
-template <int NT0, int NT, int K, class FA, class FB>
+// + n] as for every 16x16 MFMA.  AX / BX: the A / B values are exact in bf16
+// (q, k, v of bf16 inputs): that operand is not split, and its low-part
+// product is skipped (two MFMAs per pair of operands, one if both are exact).
+template <int NT0, int NT, int K, bool AX = false, bool BX = false, class FA, class FB>
 __device__ __forceinline__ void mm_strip_tiles(f32x4 (&acc)[NT], int m0, int n, int gq, int k0, FA A, FB B) {
   static_assert(K % 32 == 0, "k in steps of 32");
 #pragma unroll 1
   for (int kk = k0 & ~31; kk < K; kk += 32) {
     bf16x8 ah, al;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) split_bf16(A(m0 + n, kk + gq + 4 * e), ah, al, e);
+    for (int e = 0; e < 8; ++e) {
+      if constexpr (AX) ah[e] = (__bf16)A(m0 + n, kk + gq + 4 * e);
+      else split_bf16(A(m0 + n, kk + gq + 4 * e), ah, al, e);
+    }
 #pragma unroll
     for (int nt = NT0; nt < NT; ++nt) {
       bf16x8 bh, bl;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) split_bf16(B(kk + gq + 4 * e, 16 * nt + n), bh, bl, e);
+      for (int e = 0; e < 8; ++e) {
+        if constexpr (BX) bh[e] = (__bf16)B(kk + gq + 4 * e, 16 * nt + n);
+        else split_bf16(B(kk + gq + 4 * e, 16 * nt + n), bh, bl, e);
+      }
       acc[nt] = mfma_bf16(ah, bh, acc[nt]);
-      acc[nt] = mfma_bf16(al, bh, acc[nt]);
-      acc[nt] = mfma_bf16(ah, bl, acc[nt]);
+      if constexpr (!AX) acc[nt] = mfma_bf16(al, bh, acc[nt]);
+      if constexpr (!BX) acc[nt] = mfma_bf16(ah, bl, acc[nt]);
     }
   }
 }
 
 // all column tiles and all k
-template <int NT, int K, class FA, class FB>
+template <int NT, int K, bool AX = false, bool BX = false, class FA, class FB>
 __device__ __forceinline__ void mm_strip(f32x4 (&acc)[NT], int m0, int n, int gq, FA A, FB B) {
-  mm_strip_tiles<0, NT, K>(acc, m0, n, gq, 0, A, B);
+  mm_strip_tiles<0, NT, K, AX, BX>(acc, m0, n, gq, 0, A, B);
 }
 
 // the same with the first column tile nt0 uniform at run time (0 .. 3)
-template <int NT, int K, class FA, class FB>
+template <int NT, int K, bool AX = false, bool BX = false, class FA, class FB>
 __device__ __forceinline__ void mm_strip_from(f32x4 (&acc)[NT], int m0, int n, int gq, int nt0, int k0,
                                               FA A, FB B) {
   static_assert(NT == 4, "four column tiles");
   switch (nt0) {
-    case 0: mm_strip_tiles<0, NT, K>(acc, m0, n, gq, k0, A, B); break;
-    case 1: mm_strip_tiles<1, NT, K>(acc, m0, n, gq, k0, A, B); break;
-    case 2: mm_strip_tiles<2, NT, K>(acc, m0, n, gq, k0, A, B); break;
-    default: mm_strip_tiles<3, NT, K>(acc, m0, n, gq, k0, A, B); break;
+    case 0: mm_strip_tiles<0, NT, K, AX, BX>(acc, m0, n, gq, k0, A, B); break;
+    case 1: mm_strip_tiles<1, NT, K, AX, BX>(acc, m0, n, gq, k0, A, B); break;
+    case 2: mm_strip_tiles<2, NT, K, AX, BX>(acc, m0, n, gq, k0, A, B); break;
+    default: mm_strip_tiles<3, NT, K, AX, BX>(acc, m0, n, gq, k0, A, B); break;
   }
 }
 
@@ -229,12 +237,14 @@ __global__ __launch_bounds__(256) void k_bwd_outer(const St* __restrict__ xs, co
     for (int u = 0; u < QC; ++u) dno[u] = yr[u];
     if ((tid & 3) == 0) dden_out[slot * BLK + r] = zw;
   }
+  // the token weight goes with the second operand, so that x (q or k, exact
+  // in bf16 for bf16 inputs) needs no split
 #pragma unroll
   for (int u = 0; u < QC; ++u) {
-    X[r * PF + c0 + u] = wgt * xr[u];
-    Y[r * PF + c0 + u] = yr[u];
+    X[r * PF + c0 + u] = xr[u];
+    Y[r * PF + c0 + u] = wgt * yr[u];
   }
-  if ((tid & 3) == 0) wz[r] = zw;
+  if ((tid & 3) == 0) wz[r] = wgt * zw;
   __syncthreads();
 
   const int wave = tid >> 6, lane = tid & 63, n = lane & 15, gq = lane >> 4;
@@ -242,8 +252,9 @@ __global__ __launch_bounds__(256) void k_bwd_outer(const St* __restrict__ xs, co
     f32x4 acc[NTD];
 #pragma unroll
     for (int nt = 0; nt < NTD; ++nt) acc[nt] = zero4();
-    mm_strip<NTD, BLK>(acc, 16 * wave, n, gq, [&](int m, int k) { return X[k * PF + m]; },
-                       [&](int k, int c) { return Y[k * PF + c]; });
+    constexpr bool EX = sizeof(St) == 2;  // bf16 inputs
+    mm_strip<NTD, BLK, EX, false>(acc, 16 * wave, n, gq, [&](int m, int k) { return X[k * PF + m]; },
+                                  [&](int k, int c) { return Y[k * PF + c]; });
     float* o = out + slot * (int64_t)E;
 #pragma unroll
     for (int nt = 0; nt < NTD; ++nt)
@@ -541,8 +552,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   f32x4 sa[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) sa[nt] = zero4();
-  mm_strip<4, DH>(sa, 16 * wave, n, gq, [&](int m, int kk) { return X0[m * PF + kk]; },
-                  [&](int kk, int j) { return X1[j * PF + kk]; });
+  constexpr bool EX = sizeof(St) == 2;  // q, k, v exact in bf16 (bf16 inputs)
+  mm_strip<4, DH, EX, EX>(sa, 16 * wave, n, gq, [&](int m, int kk) { return X0[m * PF + kk]; },
+                          [&](int kk, int j) { return X1[j * PF + kk]; });
   __syncthreads();
 
   // phase 2: X2 = dnum, X1 = v: a = dnum (v dt)^T; the pair quantities
@@ -552,8 +564,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   f32x4 aa[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) aa[nt] = zero4();
-  mm_strip<4, DH>(aa, 16 * wave, n, gq, [&](int m, int c) { return X2[m * PF + c]; },
-                  [&](int c, int j) { return X1[j * PF + c] * dtl[j]; });
+  // dnum v^T, then each column j times dt_j (v stays exact for bf16 inputs)
+  mm_strip<4, DH, false, EX>(aa, 16 * wave, n, gq, [&](int m, int c) { return X2[m * PF + c]; },
+                             [&](int c, int j) { return X1[j * PF + c]; });
+#pragma unroll
+  for (int nt = 0; nt < 4; ++nt) aa[nt] *= dtl[16 * nt + n];
   float rowP[4] = {0.f, 0.f, 0.f, 0.f}, colP[4] = {0.f, 0.f, 0.f, 0.f};
   f32x4 Cr[4], Wr[4];
 #pragma unroll
@@ -676,8 +691,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
           if (n == 0) dci[q4] += eir[q4] * qa * r2;  // reduced over n below
         }
       } else {  // (Q Z)[i][a']
-        mm_strip<NTD, DH>(ta, 16 * wave, n, gq, [&](int m, int b) { return X0[m * PF + b]; },
-                          [&](int b, int c) { return X1[b * PF + c]; });
+        mm_strip<NTD, DH, EX, false>(ta, 16 * wave, n, gq, [&](int m, int b) { return X0[m * PF + b]; },
+                                     [&](int b, int c) { return X1[b * PF + c]; });
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int i = 16 * wave + 4 * gq + q4;
@@ -709,13 +724,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   stage_rows(X1, k);
   stage_rows(X2, q);
   __syncthreads();
-  mm_strip<NTD, BLK>(dqo, 16 * wave, n, gq, [&](int m, int j) { return X0[m * PF + j]; },
-                     [&](int j, int b) { return X1[j * PF + b]; });
+  mm_strip<NTD, BLK, false, EX>(dqo, 16 * wave, n, gq, [&](int m, int j) { return X0[m * PF + j]; },
+                                [&](int j, int b) { return X1[j * PF + b]; });
   f32x4 dka[NTD];
 #pragma unroll
   for (int nt = 0; nt < NTD; ++nt) dka[nt] = zero4();
-  mm_strip<NTD, BLK>(dka, 16 * wave, n, gq, [&](int m, int i) { return X0[i * PF + m]; },
-                     [&](int i, int b) { return X2[i * PF + b]; });
+  mm_strip<NTD, BLK, false, EX>(dka, 16 * wave, n, gq, [&](int m, int i) { return X0[i * PF + m]; },
+                                [&](int i, int b) { return X2[i * PF + b]; });
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
     const int i = 16 * wave + 4 * gq + q4;
@@ -761,10 +776,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     f32x4 ta[NTD], gka[NTD];
 #pragma unroll
     for (int nt = 0; nt < NTD; ++nt) ta[nt] = gka[nt] = zero4();
-    mm_strip<NTD, DH>(ta, 16 * wave, n, gq, [&](int m, int c) { return X1[m * PF + c] * dtl[m]; },
-                      [&](int c, int b) { return X0[b * PF + c]; });
-    mm_strip<NTD, DH>(gka, 16 * wave, n, gq, [&](int m, int b) { return X2[m * PF + b]; },
-                      [&](int b, int c) { return X0[b * PF + c]; });
+    // v G^T, then each row j times dt_j
+    mm_strip<NTD, DH, EX, false>(ta, 16 * wave, n, gq, [&](int m, int c) { return X1[m * PF + c]; },
+                                 [&](int c, int b) { return X0[b * PF + c]; });
+#pragma unroll
+    for (int nt = 0; nt < NTD; ++nt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) ta[nt][q4] *= dtl[16 * wave + 4 * gq + q4];
+    mm_strip<NTD, DH, EX, false>(gka, 16 * wave, n, gq, [&](int m, int b) { return X2[m * PF + b]; },
+                                 [&](int b, int c) { return X0[b * PF + c]; });
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
       const int j = 16 * wave + 4 * gq + q4;
@@ -806,9 +826,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
       for (int nt = 0; nt < NTD; ++nt) va[nt] = zero4();
       if (a < DH) {
         // V[j][b] = V_j[a][b] for b >= a
-        mm_strip_from<NTD, DH>(va, 16 * wave, n, gq, a >> 4, 0,
-                               [&](int m, int c) { return X1[m * PF + c] * dtl[m]; },
-                               [&](int c, int b) { return X0[b * PF + c]; });
+        mm_strip_from<NTD, DH, EX, false>(va, 16 * wave, n, gq, a >> 4, 0,
+                                          [&](int m, int c) { return X1[m * PF + c]; },
+                                          [&](int c, int b) { return X0[b * PF + c]; });
+#pragma unroll
+        for (int nt = 0; nt < NTD; ++nt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) va[nt][q4] *= dtl[16 * wave + 4 * gq + q4];
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int j = 16 * wave + 4 * gq + q4;
@@ -847,8 +871,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
           for (int nt = 0; nt < NTD; ++nt) dva[nt][q4] += wjr[q4] * pa[nt][q4];
       } else {
         // (K g)[j][a']: dk_j += 2 w_j g k_j, kt_j += k_j^T g k_j
-        mm_strip<NTD, DH>(va, 16 * wave, n, gq, [&](int m, int b) { return X2[m * PF + b]; },
-                          [&](int b, int c) { return X0[b * PF + c]; });
+        mm_strip<NTD, DH, EX, false>(va, 16 * wave, n, gq, [&](int m, int b) { return X2[m * PF + b]; },
+                                     [&](int b, int c) { return X0[b * PF + c]; });
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int j = 16 * wave + 4 * gq + q4;

@@ -486,46 +486,6 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
   // prologue: the initial states (if any), stage step 0, prefetch step 1
   prefetch(0);
   cur = nx;
-  if constexpr (INIT) {
-    // initial numerator state, S0[a][b][c] (row (a, b) of H_up, the layout
-    // of final_state): the workgroup's columns c0 .. c0 + CWG - 1 pass through
-    // LDS (the staging buffer of q, not yet in use) in passes of AP values of
-    // a; each lane then takes its accumulator entries, scaled to the first
-    // step's 2^sig_in, and forms the fp16 copy of its first a-tile.  (A kernel
-    // variant of its own: in the common variant the registers are fully used.)
-    constexpr int AP = 16, V4 = CWG / 4;
-    static_assert(AP * DH * CWG * sizeof(float) <= sizeof(Qh), "initial-state staging fits");
-    float* buf = reinterpret_cast<float*>(&Qh[0][0][0]);
-    const float* s0h = S0 + bh * (int64_t)DH * DH * DH;
-    const float sc = ldexpf(1.f, cur.sig_in);
-    for (int pass = 0; pass < DH / AP; ++pass) {
-      for (int e = tid; e < AP * DH * V4; e += NT) {
-        const int row = e / V4, part = e % V4;  // row = (a - AP pass) * 64 + b
-        const int64_t a = AP * pass + row / DH, b = row % DH;
-        *reinterpret_cast<f32x4*>(&buf[row * CWG + 4 * part]) =
-            *reinterpret_cast<const f32x4*>(&s0h[(a * DH + b) * DH + c0 + 4 * part]);
-      }
-      __syncthreads();
-#pragma unroll
-      for (int at = 0; at < NAT; ++at) {
-        const int a = 32 * (NAT == 2 ? at : (wave >> 2)) + n32;
-        if (a / AP == pass) {
-#pragma unroll
-          for (int bt = 0; bt < 2; ++bt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int b = bt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-              S[at][bt][r] = buf[((a - AP * pass) * DH + b) * CWG + cl] * sc;
-            }
-        }
-      }
-      __syncthreads();
-    }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) SA0[kk][e] = (_Float16)S[0][kk >> 1][8 * (kk & 1) + e];
-  }
   stage(0);
   prefetch(nstep > 1 ? 1 : 0);
   if (wave < NW / 2) {
@@ -545,6 +505,52 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
   }
   __syncthreads();
 
+  // initial numerator state, S0[a][b][c] (row (a, b) of H_up, the layout of
+  // final_state), taken at the top of the first step: the workgroup's
+  // columns c0 .. c0 + CWG - 1 pass through LDS (q's second staging slot,
+  // not written before the first step's staging) in passes of AP values of
+  // a; each lane then takes its accumulator entries, scaled to the first
+  // step's 2^sig_in, and forms the fp16 copy of its first a-tile.  (Loaded
+  // before the loop instead, the accumulators' longer live range makes the
+  // register allocator spill inside the loop.)
+  auto load_initial_state = [&] {
+    // AS: floats per value of a, padded so that the lanes of a pass (eight
+    // consecutive a) read distinct LDS banks
+    constexpr int AP = 8, V4 = CWG / 4, AS = DH * CWG + 4;
+    static_assert(AP * AS * sizeof(float) <= sizeof(Qh[1]), "initial-state staging fits");
+    float* buf = reinterpret_cast<float*>(&Qh[1][0][0]);
+    const float* s0h = S0 + bh * (int64_t)DH * DH * DH;
+    const float sc = ldexpf(1.f, cur.sig_in);
+#pragma unroll 1
+    for (int pass = 0; pass < DH / AP; ++pass) {
+      for (int e = tid; e < AP * DH * V4; e += NT) {
+        const int row = e / V4, part = e % V4;  // row = (a - AP pass) * 64 + b
+        const int64_t a = AP * pass + row / DH, b = row % DH;
+        *reinterpret_cast<f32x4*>(&buf[(row / DH) * AS + (row % DH) * CWG + 4 * part]) =
+            *reinterpret_cast<const f32x4*>(&s0h[(a * DH + b) * DH + c0 + 4 * part]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int at = 0; at < NAT; ++at) {
+        const int a = 32 * (NAT == 2 ? at : (wave >> 2)) + n32;
+        if (a / AP == pass) {
+#pragma unroll
+          for (int bt = 0; bt < 2; ++bt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int b = bt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+              S[at][bt][r] = buf[(a - AP * pass) * AS + b * CWG + cl] * sc;
+            }
+        }
+      }
+      __syncthreads();
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) SA0[kk][e] = (_Float16)S[0][kk >> 1][8 * (kk & 1) + e];
+  };
+
   // Per step m: MFMA work of m, write-out of m-1 (compute-first waves),
   // staging of m+1, loads of m+2, one barrier.  With two waves per SIMD the first four waves run the
   // MFMA work first and the other four the bookkeeping first; each group has
@@ -555,6 +561,8 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
   if (wave < NW / 2) {
     for (int st = 0; st < nstep; ++st) {
       const Stp nxt = nx;  // scales of step st + 1 (prefetched)
+      if constexpr (INIT)
+        if (st == 0) load_initial_state();
       compute(st, std::integral_constant<int, 0>{});
       const bool zs = st + 1 < nstep;
       if (zs) zload(st + 1);
@@ -569,6 +577,8 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
   } else {
     for (int st = 0; st < nstep; ++st) {
       const Stp nxt = nx;
+      if constexpr (INIT)
+        if (st == 0) load_initial_state();
       stage(st + 1);
       prefetch(st + 2 < nstep ? st + 2 : nstep - 1);
       compute(st, std::integral_constant<int, NAT == 2 ? 0 : 1>{});

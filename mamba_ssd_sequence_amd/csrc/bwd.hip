@@ -156,6 +156,79 @@ __device__ __forceinline__ void mm_strip_from(f32x4 (&acc)[NT], int m0, int n, i
   }
 }
 
+// bf16 row pitch of the pre-split operands (elements: 144 bytes, so that the
+// 16-byte fragment reads of 16 consecutive rows hit distinct LDS banks)
+constexpr int PH = 72;
+
+// acc[nt] += A (16 rows from m0) x B (column tiles NT0 .. NT - 1), k from k0
+// rounded down to a multiple of 32 up to K, with both operands already in
+// LDS as bf16, k contiguous: A as [m][k], B as [n][k] (row pitch PH), each
+// as a high part and, unless exact in bf16 (ALO / BLO false), a low part;
+// products hi*hi + lo*hi + hi*lo as in mm_strip_tiles, one 16-byte read per
+// operand part and k-step.  A values with k <= kz count as zero.  Lane (n,
+// gq) supplies the k = kk + 8 gq + e of its slot e for both operands.
+template <int NT0, int NT, int K, bool ALO, bool BLO>
+__device__ __forceinline__ void mm_pre_tiles(f32x4 (&acc)[NT], const __bf16* Ah, const __bf16* Al,
+                                             const __bf16* Bh, const __bf16* Bl, int m0, int n,
+                                             int gq, int k0, int kz) {
+  static_assert(K % 32 == 0, "k in steps of 32");
+#pragma unroll 1
+  for (int kk = k0 & ~31; kk < K; kk += 32) {
+    const int ko = kk + 8 * gq;
+    bf16x8 ah = *reinterpret_cast<const bf16x8*>(&Ah[(m0 + n) * PH + ko]);
+    bf16x8 al;
+    if constexpr (ALO) al = *reinterpret_cast<const bf16x8*>(&Al[(m0 + n) * PH + ko]);
+    if (kz >= kk) {  // uniform
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (ko + e <= kz) {
+          ah[e] = (__bf16)0.f;
+          if constexpr (ALO) al[e] = (__bf16)0.f;
+        }
+    }
+#pragma unroll
+    for (int nt = NT0; nt < NT; ++nt) {
+      const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&Bh[(16 * nt + n) * PH + ko]);
+      acc[nt] = mfma_bf16(ah, bh, acc[nt]);
+      if constexpr (ALO) acc[nt] = mfma_bf16(al, bh, acc[nt]);
+      if constexpr (BLO) {
+        const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&Bl[(16 * nt + n) * PH + ko]);
+        acc[nt] = mfma_bf16(ah, bl, acc[nt]);
+      }
+    }
+  }
+}
+
+// the same with the first column tile nt0 uniform at run time (0 .. 3)
+template <int NT, int K, bool ALO, bool BLO>
+__device__ __forceinline__ void mm_pre_from(f32x4 (&acc)[NT], const __bf16* Ah, const __bf16* Al,
+                                            const __bf16* Bh, const __bf16* Bl, int m0, int n,
+                                            int gq, int nt0) {
+  static_assert(NT == 4, "four column tiles");
+  switch (nt0) {
+    case 0: mm_pre_tiles<0, NT, K, ALO, BLO>(acc, Ah, Al, Bh, Bl, m0, n, gq, 0, -1); break;
+    case 1: mm_pre_tiles<1, NT, K, ALO, BLO>(acc, Ah, Al, Bh, Bl, m0, n, gq, 0, -1); break;
+    case 2: mm_pre_tiles<2, NT, K, ALO, BLO>(acc, Ah, Al, Bh, Bl, m0, n, gq, 0, -1); break;
+    default: mm_pre_tiles<3, NT, K, ALO, BLO>(acc, Ah, Al, Bh, Bl, m0, n, gq, 0, -1); break;
+  }
+}
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// 16 fp32 values -> 16 consecutive bf16 of a high and a low row (16-byte aligned)
+__device__ __forceinline__ void split16(const f32x16& x, __bf16* hi, __bf16* lo) {
+  bf16x8 h0, l0, h1, l1;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    split_bf16(x[e], h0, l0, e);
+    split_bf16(x[8 + e], h1, l1, e);
+  }
+  *reinterpret_cast<bf16x8*>(hi) = h0;
+  *reinterpret_cast<bf16x8*>(hi + 8) = h1;
+  *reinterpret_cast<bf16x8*>(lo) = l0;
+  *reinterpret_cast<bf16x8*>(lo + 8) = l1;
+}
+
 // sum over the 16 lanes n of a lane group (lanes 16 gq .. 16 gq + 15)
 __device__ __forceinline__ float sum16(float x) {
 #pragma unroll
@@ -510,7 +583,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   constexpr int E = D * DH + D;
   constexpr int NTD = DH / 16;
   static_assert(ORDER == 1 || DH == 64, "order 2: d_h 64");
-  __shared__ float X0[BLK * PF], X1[BLK * PF], X2[BLK * PF];
+  // three fp32 staging buffers X0, X1, X2; at order 2 the state-tile passes
+  // reuse their memory (and a little more) for pre-split bf16 operands of TB
+  // elements each
+  constexpr int XF = BLK * PF;        // floats per fp32 buffer
+  constexpr int TB = BLK * PH;        // bf16 elements per pre-split operand part
+  constexpr int POOL = ORDER == 2 ? 6 * TB / 2 : 3 * XF;  // floats
+  static_assert(ORDER == 1 || (2 * XF + 4 * TB <= 2 * POOL && 3 * XF <= POOL), "pool layout");
+  __shared__ __attribute__((aligned(16))) float pool[POOL];
+  float* const X0 = pool;
+  float* const X1 = pool + XF;
+  float* const X2 = pool + 2 * XF;
+  __bf16* const P16 = reinterpret_cast<__bf16*>(pool);
   __shared__ float csl[BLK], ddl[BLK], dtl[BLK], zl[DH], gl[DH], rowl[BLK], colw[4][BLK], dcl[BLK];
   __shared__ float red[4];
   const BlockGeo g = block_geo(nblk, N, chunk, a_cs);
@@ -642,32 +726,54 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     // adds 2 e_i sum_{b >= a} U_i[a][b] q_ib to dq_ia and 2 e_i U_i[a][b] q_ia to
     // dq_ib (b > a), and e_i q_ia (U_i[a][a] q_ia + 2 sum_{b > a} U_i[a][b] q_ib)
     // to dcs_i.  The next tile's rows are loaded during this tile's product.
-    float pre[DH * DH / 256];
-    auto load_pre = [&](int an) {  // tile an (an == DH: Z, all rows)
-      const int rmin = an < DH ? 16 * (an >> 4) : 0;
+    // Operands pre-split once (bf16 high and low parts, k contiguous): Dh/Dl
+    // = dnum [i][c] for the block, Sh/Sl = the state tile [b][c] per pass,
+    // after X0 (Q, fp32, read by the contractions).  Thread t stages row
+    // sr = t / 4, columns sc .. sc + 15 of a 64 x 64 operand.
+    __bf16* const Dh = P16 + 2 * XF;
+    __bf16* const Dl = Dh + TB;
+    __bf16* const Sh = Dh + 2 * TB;
+    __bf16* const Sl = Dh + 3 * TB;
+    const int sr = tid >> 2, sc = (tid & 3) * 16;
+    {
+      f32x16 x;
 #pragma unroll
-      for (int u = 0; u < DH * DH / 256; ++u) {
-        const int e = tid + 256 * u;  // row e / DH = 4 u + wave: uniform in the wave
-        if (e / DH >= rmin) pre[u] = st[(int64_t)an * DH * DH + e];
+      for (int u = 0; u < 16; ++u) x[u] = dnb[sr * DH + sc + u];
+      split16(x, &Dh[sr * PH + sc], &Dl[sr * PH + sc]);
+    }
+    // rows b >= 16 (an / 16) of tile an (an == DH: Z, all rows); the row
+    // test is uniform in a wave (rows 16 wave .. 16 wave + 15).  Two register
+    // sets: the loads of tile a + 2 are issued as tile a is staged, two
+    // passes ahead of their use.
+    f32x16 preA, preB;
+    auto rmin = [](int an) { return an < DH ? 16 * (an >> 4) : 0; };
+    auto load_pre = [&](f32x16& pre, int an) {
+      if (sr >= rmin(an)) {
+        const float* src = st + (int64_t)an * DH * DH + sr * DH + sc;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(src + 4 * u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pre[4 * u + e] = x[e];
+        }
       }
     };
-    load_pre(0);
-    for (int a = 0; a <= DH; ++a) {
-      // a < DH: tile a of S_c; a == DH: Z
+    auto pass = [&](int a, f32x16& pre) {
+      // a < DH: tile a of S_c (pre-split); a == DH: Z (fp32, in X1's place:
+      // the dnum parts are not read by that pass)
+      if (a < DH) {
+        if (sr >= rmin(a)) split16(pre, &Sh[sr * PH + sc], &Sl[sr * PH + sc]);
+      } else {
 #pragma unroll
-      for (int u = 0; u < DH * DH / 256; ++u) {
-        const int e = tid + 256 * u;
-        X1[(e / DH) * PF + (e % DH)] = pre[u];
+        for (int u = 0; u < 16; ++u) X1[sr * PF + sc + u] = pre[u];
       }
       __syncthreads();
-      if (a < DH) load_pre(a + 1);
+      if (a + 2 <= DH) load_pre(pre, a + 2);
       f32x4 ta[NTD];
 #pragma unroll
       for (int nt = 0; nt < NTD; ++nt) ta[nt] = zero4();
       if (a < DH) {  // T[i][b] = U_i[a][b], column tiles holding some b >= a
-        mm_strip_from<NTD, DH>(ta, 16 * wave, n, gq, a >> 4, 0,
-                               [&](int m, int c) { return X2[m * PF + c]; },
-                               [&](int c, int b) { return X1[b * PF + c]; });
+        mm_pre_from<NTD, DH, true, true>(ta, Dh, Dl, Sh, Sl, 16 * wave, n, gq, a >> 4);
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int i = 16 * wave + 4 * gq + q4;
@@ -683,11 +789,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
           }
           r1 = sum16(r1);
           r2 = sum16(r2);
-          if (n == (a & 15)) {
+          // (every tile gets an add, zero but for tile a / 16: a store under
+          // a test of the tile index would become a dynamically indexed array)
+          const float add = n == (a & 15) ? 2.f * eir[q4] * r1 : 0.f;
 #pragma unroll
-            for (int nt = 0; nt < NTD; ++nt)
-              if (nt == (a >> 4)) dqo[nt][q4] += 2.f * eir[q4] * r1;
-          }
+          for (int nt = 0; nt < NTD; ++nt) dqo[nt][q4] += nt == (a >> 4) ? add : 0.f;
           if (n == 0) dci[q4] += eir[q4] * qa * r2;  // reduced over n below
         }
       } else {  // (Q Z)[i][a']
@@ -705,6 +811,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         }
       }
       __syncthreads();
+    };
+    load_pre(preA, 0);
+    load_pre(preB, 1);
+    for (int a = 0; a <= DH; a += 2) {
+      pass(a, preA);
+      if (a + 1 <= DH) pass(a + 1, preB);
     }
   }
 #pragma unroll
@@ -761,8 +873,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   // Order 2 (tile a of G per pass, rows (a, 0 .. 63); G symmetric in a, b):
   // with V_j[a][b] = sum_c G[(a, b)][c] vop_jc, dk_j += 2 w_j (V_j + g) k_j,
   // dvop_j += w_j sum_{a,b} k_ja k_jb G[(a, b)], kt_j = k_j^T (V_j + g) k_j.
-  stage_rows(X1, v);
-  stage_rows(X2, k);
+  // k and v: fp32 in X2 and X1 (order 1), or bf16 (exact for bf16 inputs)
+  // in the pool's first two operand slots (order 2)
+  __bf16* const Kh = P16;
+  __bf16* const Vh = P16 + TB;
+  if constexpr (ORDER == 1) {
+    stage_rows(X1, v);
+    stage_rows(X2, k);
+  } else {
+    const int sr = tid >> 2, sc = (tid & 3) * 16;
+    float x[QC];
+    load_row<St, QC>(k, g, sr, sc, x);
+    bf16x8 h0, h1;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      h0[e] = (__bf16)x[e];
+      h1[e] = (__bf16)x[8 + e];
+    }
+    *reinterpret_cast<bf16x8*>(&Kh[sr * PH + sc]) = h0;
+    *reinterpret_cast<bf16x8*>(&Kh[sr * PH + sc + 8]) = h1;
+    load_row<St, QC>(v, g, sr, sc, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      h0[e] = (__bf16)x[e];
+      h1[e] = (__bf16)x[8 + e];
+    }
+    *reinterpret_cast<bf16x8*>(&Vh[sr * PH + sc]) = h0;
+    *reinterpret_cast<bf16x8*>(&Vh[sr * PH + sc + 8]) = h1;
+  }
+  auto kval = [&](int j, int b) -> float {
+    if constexpr (ORDER == 1) return X2[j * PF + b];
+    else return (float)Kh[j * PH + b];
+  };
+  auto vval = [&](int j, int c) -> float {
+    if constexpr (ORDER == 1) return X1[j * PF + c];
+    else return (float)Vh[j * PH + c];
+  };
   float kt[4] = {0.f, 0.f, 0.f, 0.f}, dd[4] = {0.f, 0.f, 0.f, 0.f}, wjr[4];
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
@@ -800,35 +946,55 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     for (int e = tid; e < DH * DH; e += 256) gsd += X0[(e / DH) * PF + (e % DH)] * st[e];
     if (tid < DH) gsd += gl[tid] * zl[tid];
   } else {
-    // rows b >= a of each tile, as in phase 3; the next tile's rows are
+    // rows b >= a of each tile, as in phase 3, pre-split: Gh/Gl = tile a as
+    // [b][c] (the V product contracts over c) and GTh/GTl = its transpose
+    // [c][b] (the dvop product contracts over b); the next tile's rows are
     // loaded during this tile's products
-    float pre[DH * DH / 256];
-    auto load_pre = [&](int an) {  // tile an (an == DH: g, all rows)
-      const int rmin = an < DH ? 16 * (an >> 4) : 0;
+    __bf16* const Gh = P16 + 2 * TB;
+    __bf16* const Gl = P16 + 3 * TB;
+    __bf16* const GTh = P16 + 4 * TB;
+    __bf16* const GTl = P16 + 5 * TB;
+    float* const Xg = reinterpret_cast<float*>(Gh);  // g (fp32) for the last pass
+    const int sr = tid >> 2, sc = (tid & 3) * 16;
+    // two register sets, loads two passes ahead (as in phase 3)
+    f32x16 preA, preB;
+    auto rmin = [](int an) { return an < DH ? 16 * (an >> 4) : 0; };
+    auto load_pre = [&](f32x16& pre, int an) {  // tile an (an == DH: g, all rows)
+      if (sr >= rmin(an)) {
+        const float* src = gs + (int64_t)an * DH * DH + sr * DH + sc;
 #pragma unroll
-      for (int u = 0; u < DH * DH / 256; ++u) {
-        const int e = tid + 256 * u;
-        if (e / DH >= rmin) pre[u] = gs[(int64_t)an * DH * DH + e];
+        for (int u = 0; u < 4; ++u) {
+          const f32x4 x = *reinterpret_cast<const f32x4*>(src + 4 * u);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pre[4 * u + e] = x[e];
+        }
       }
     };
-    load_pre(0);
-    for (int a = 0; a <= DH; ++a) {
-      // a < DH: tile a of G; a == DH: g (as a d_h x d_h matrix)
+    auto pass = [&](int a, f32x16& pre) {
+      // a < DH: tile a of G (pre-split, both layouts); a == DH: g (as a
+      // d_h x d_h matrix, fp32)
+      if (a < DH) {
+        if (sr >= rmin(a)) {
+          split16(pre, &Gh[sr * PH + sc], &Gl[sr * PH + sc]);
 #pragma unroll
-      for (int u = 0; u < DH * DH / 256; ++u) {
-        const int e = tid + 256 * u;
-        X0[(e / DH) * PF + (e % DH)] = pre[u];
+          for (int u = 0; u < 16; ++u) {
+            const __bf16 h = (__bf16)pre[u];
+            GTh[(sc + u) * PH + sr] = h;
+            GTl[(sc + u) * PH + sr] = (__bf16)(pre[u] - (float)h);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) Xg[sr * PF + sc + u] = pre[u];
       }
       __syncthreads();
-      if (a < DH) load_pre(a + 1);
+      if (a + 2 <= DH) load_pre(pre, a + 2);
       f32x4 va[NTD];
 #pragma unroll
       for (int nt = 0; nt < NTD; ++nt) va[nt] = zero4();
       if (a < DH) {
-        // V[j][b] = V_j[a][b] for b >= a
-        mm_strip_from<NTD, DH, EX, false>(va, 16 * wave, n, gq, a >> 4, 0,
-                                          [&](int m, int c) { return X1[m * PF + c]; },
-                                          [&](int c, int b) { return X0[b * PF + c]; });
+        // V[j][b] = V_j[a][b] for b >= a (v exact in bf16)
+        mm_pre_from<NTD, DH, false, true>(va, Vh, nullptr, Gh, Gl, 16 * wave, n, gq, a >> 4);
 #pragma unroll
         for (int nt = 0; nt < NTD; ++nt)
 #pragma unroll
@@ -836,54 +1002,60 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int j = 16 * wave + 4 * gq + q4;
-          const float ka = X2[j * PF + a];
+          const float ka = kval(j, a);
           float r1 = 0.f, r2 = 0.f;
 #pragma unroll
           for (int nt = 0; nt < NTD; ++nt) {
             const int b = 16 * nt + n;
-            const float vk = va[nt][q4] * X2[j * PF + b];
+            const float vk = va[nt][q4] * kval(j, b);
             if (b >= a) r1 += vk;
             r2 += b > a ? 2.f * vk : (b == a ? vk : 0.f);
             if (b > a) dka[nt][q4] += 2.f * wjr[q4] * ka * va[nt][q4];
           }
           r1 = sum16(r1);
           r2 = sum16(r2);
-          if (n == (a & 15)) {
+          const float add = n == (a & 15) ? 2.f * wjr[q4] * r1 : 0.f;  // as in phase 3
 #pragma unroll
-            for (int nt = 0; nt < NTD; ++nt)
-              if (nt == (a >> 4)) dka[nt][q4] += 2.f * wjr[q4] * r1;
-          }
+          for (int nt = 0; nt < NTD; ++nt) dka[nt][q4] += nt == (a >> 4) ? add : 0.f;
           if (n == 0) kt[q4] += ka * r2;  // reduced over n below
         }
-        // dvop_j += w_j sum_{b >= a} (2 if b > a) k_ja k_jb G[(a, b)]
+        // dvop_j += w_j k_ja (2 sum_{b > a} k_jb G[(a, b)] + k_ja G[(a, a)])
+        // (k exact in bf16; the entries b <= a of its operand count as zero)
         f32x4 pa[NTD];
 #pragma unroll
         for (int nt = 0; nt < NTD; ++nt) pa[nt] = zero4();
-        mm_strip_from<NTD, DH>(pa, 16 * wave, n, gq, 0, a & ~3,
-                               [&](int m, int b) {
-                                 const float w = b > a ? 2.f : (b == a ? 1.f : 0.f);
-                                 return w * X2[m * PF + b] * X2[m * PF + a];
-                               },
-                               [&](int b, int c) { return X0[b * PF + c]; });
+        mm_pre_tiles<0, NTD, DH, false, true>(pa, Kh, nullptr, GTh, GTl, 16 * wave, n, gq, a + 1, a);
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const float ka = kval(16 * wave + 4 * gq + q4, a);
 #pragma unroll
-          for (int nt = 0; nt < NTD; ++nt) dva[nt][q4] += wjr[q4] * pa[nt][q4];
+          for (int nt = 0; nt < NTD; ++nt) {
+            const int c = 16 * nt + n;
+            const float gaa = (float)Gh[a * PH + c] + (float)Gl[a * PH + c];
+            dva[nt][q4] += wjr[q4] * ka * (2.f * pa[nt][q4] + ka * gaa);
+          }
+        }
       } else {
         // (K g)[j][a']: dk_j += 2 w_j g k_j, kt_j += k_j^T g k_j
-        mm_strip<NTD, DH, EX, false>(va, 16 * wave, n, gq, [&](int m, int b) { return X2[m * PF + b]; },
-                                     [&](int b, int c) { return X0[b * PF + c]; });
+        mm_strip<NTD, DH, EX, false>(va, 16 * wave, n, gq, [&](int m, int b) { return kval(m, b); },
+                                     [&](int b, int c) { return Xg[b * PF + c]; });
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int j = 16 * wave + 4 * gq + q4;
 #pragma unroll
           for (int nt = 0; nt < NTD; ++nt) {
             dka[nt][q4] += 2.f * wjr[q4] * va[nt][q4];
-            kt[q4] += X2[j * PF + 16 * nt + n] * va[nt][q4];
+            kt[q4] += kval(j, 16 * nt + n) * va[nt][q4];
           }
         }
       }
       __syncthreads();
+    };
+    load_pre(preA, 0);
+    load_pre(preB, 1);
+    for (int a = 0; a <= DH; a += 2) {
+      pass(a, preA);
+      if (a + 1 <= DH) pass(a + 1, preB);
     }
     // <G_{c+1}, S_c> + <g_{c+1}, z_c>: the reverse scan's per-tile parts
     if (tid < DH) gsd = gsdp[slot * DH + tid];
@@ -892,7 +1064,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   for (int q4 = 0; q4 < 4; ++q4) {
     const int j = 16 * wave + 4 * gq + q4;
 #pragma unroll
-    for (int nt = 0; nt < NTD; ++nt) dd[q4] += dva[nt][q4] * X1[j * PF + 16 * nt + n];
+    for (int nt = 0; nt < NTD; ++nt) dd[q4] += dva[nt][q4] * vval(j, 16 * nt + n);
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) {
       kt[q4] += __shfl_xor(kt[q4], off, WAVE);

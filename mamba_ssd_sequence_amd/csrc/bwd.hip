@@ -49,7 +49,11 @@
 //   k_bwd_phi_scan     per (head, first feature index a), sequential over the
 //                      blocks: the state tile a entering each block (forward)
 //                      and the gradient tile a of the state leaving it (reverse)
-//   k_bwd_block<2>     as above, with the state contractions per tile a
+//   k_bwd_block<2>     as above, with the state contractions per tile a, and
+//                      da from the keys' gradients alone (no state dot):
+//                      da_t = -(1/2) sum_{s >= t} k_s . dk_s over the sequence,
+//                      the in-block part here
+//   k_bwd_da_tail      ... and the later blocks' totals
 #include "common.h"
 #include "launch.h"
 #include "bwd.h"
@@ -392,13 +396,11 @@ __global__ __launch_bounds__(256) void k_bwd_phi_scan(const St* __restrict__ xs,
                                                       const float* __restrict__ ddw,
                                                       const float* __restrict__ a_cs, int64_t N,
                                                       int64_t chunk, int64_t nblk,
-                                                      float* __restrict__ out,
-                                                      const float* __restrict__ sst,
-                                                      float* __restrict__ gsdp) {
+                                                      float* __restrict__ out) {
   constexpr int DH = 64, QC = DH / 4, NTD = DH / 16;
   constexpr int64_t E = (int64_t)DH * DH * DH + DH * DH;
   constexpr int NA = DH / AP;  // workgroups per head
-  __shared__ float X[BLK * PF], Y[BLK * PF], wl[BLK], wz[BLK], red[AP][4];
+  __shared__ float X[BLK * PF], Y[BLK * PF], wl[BLK], wz[BLK];
   const int64_t bh = blockIdx.x / NA;
   const int a0 = (int)(blockIdx.x - bh * NA) * AP;
   const int tid = threadIdx.x, r = tid >> 2, c0 = (tid & 3) * QC;
@@ -435,35 +437,6 @@ __global__ __launch_bounds__(256) void k_bwd_phi_scan(const St* __restrict__ xs,
       }
       if (gq == 0) o[(int64_t)DH * DH * DH + a * DH + 16 * wave + n] = runz[ai];
     }
-    if constexpr (MODE == 1) {
-      // <G_{c+1}, S_c> + <g_{c+1}, z_c> over these tiles, for the block's dT
-      const float* so = sst + (bh * nblk + blk) * E;
-#pragma unroll
-      for (int ai = 0; ai < AP; ++ai) {
-        const int a = a0 + ai;
-        // each pair (a, b), b > a, stands for (a, b) and (b, a)
-        float d = 0.f;
-        if (16 * wave + 15 >= a) {
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int b = 16 * wave + 4 * gq + q4;
-            const float wgt = b > a ? 2.f : (b == a ? 1.f : 0.f);
-            float e = 0.f;
-#pragma unroll
-            for (int nt = 0; nt < NTD; ++nt)
-              e += run[ai][nt][q4] * so[((int64_t)a * DH + b) * DH + 16 * nt + n];
-            d += wgt * e;
-          }
-        }
-        if (gq == 0) {
-          const int b = 16 * wave + n;
-          const float wgt = b > a ? 2.f : (b == a ? 1.f : 0.f);
-          d += wgt * runz[ai] * so[(int64_t)DH * DH * DH + a * DH + b];
-        }
-        for (int off = 1; off < WAVE; off <<= 1) d += __shfl_xor(d, off, WAVE);
-        if (lane == 0) red[ai][wave] = d;
-      }
-    }
     // stage the block: X = x rows, Y = y rows, per-token weights
     const bool ok = r < nvalid;
     const int64_t rr = row + t0 + (ok ? r : 0);
@@ -492,8 +465,6 @@ __global__ __launch_bounds__(256) void k_bwd_phi_scan(const St* __restrict__ xs,
       }
     }
     __syncthreads();
-    if (MODE == 1 && tid < AP)
-      gsdp[(bh * nblk + blk) * DH + a0 + tid] = (red[tid][0] + red[tid][1]) + (red[tid][2] + red[tid][3]);
     const float eT = expf(T);
 #pragma unroll
     for (int ai = 0; ai < AP; ++ai) {
@@ -572,7 +543,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
                                                    int64_t chunk, int64_t nblk,
                                                    const float* __restrict__ sst,
                                                    const float* __restrict__ gst,
-                                                   const float* __restrict__ gsdp,
+                                                   float* __restrict__ btot,
                                                    const float* __restrict__ dnw,
                                                    const float* __restrict__ ddw,
                                                    float* __restrict__ dq, float* __restrict__ dk,
@@ -1057,8 +1028,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
       pass(a, preA);
       if (a + 1 <= DH) pass(a + 1, preB);
     }
-    // <G_{c+1}, S_c> + <g_{c+1}, z_c>: the reverse scan's per-tile parts
-    if (tid < DH) gsd = gsdp[slot * DH + tid];
   }
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
@@ -1071,16 +1040,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
       dd[q4] += __shfl_xor(dd[q4], off, WAVE);
     }
   }
-  // dT = sum_j w_j kt_j + e^T (<G, S_c> + <g, z_c>)
-  float part = expf(T) * gsd;
-  if (n == 0) {
+  // order 1: dT = sum_j w_j kt_j + e^T (<G, S_c> + <g, z_c>).  Order 2: the
+  // decay gradient from the keys' gradients alone, da_t = -(1/2) sum over
+  // s >= t (whole sequence) of k_s . dk_s (the scores depend on the decay
+  // only through e^{A_i - A_j} = (e^{A_i / 2} e^{-A_j / 2})^2, so
+  // dA_t = (q_t . dq_t - k_t . dk_t) / 2, and q_t . dq_t = 0 since y_t is
+  // homogeneous of degree 0 in q_t): no state dot is needed
+  float dT = 0.f, kdk[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (ORDER == 1) {
+    float part = expf(T) * gsd;
+    if (n == 0) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) part += wjr[q4] * kt[q4];
+      for (int q4 = 0; q4 < 4; ++q4) part += wjr[q4] * kt[q4];
+    }
+    for (int off = 1; off < WAVE; off <<= 1) part += __shfl_xor(part, off, WAVE);
+    if (lane == 0) red[wave] = part;
+    __syncthreads();
+    dT = (red[0] + red[1]) + (red[2] + red[3]);
+  } else {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int j = 16 * wave + 4 * gq + q4;
+#pragma unroll
+      for (int nt = 0; nt < NTD; ++nt) kdk[q4] += dka[nt][q4] * kval(j, 16 * nt + n);
+      kdk[q4] = sum16(kdk[q4]);
+    }
   }
-  for (int off = 1; off < WAVE; off <<= 1) part += __shfl_xor(part, off, WAVE);
-  if (lane == 0) red[wave] = part;
-  __syncthreads();
-  const float dT = (red[0] + red[1]) + (red[2] + red[3]);
 
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {
@@ -1096,9 +1081,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     if (n == 0) {
       float dcs = 0.f;
       if (j < g.nvalid) {
-        const float cp = (colw[0][j] + colw[1][j]) + (colw[2][j] + colw[3][j]);
-        dcs = rowl[j] - cp - wjr[q4] * kt[q4];
-        if (j == g.nvalid - 1) dcs += dT;
+        if constexpr (ORDER == 1) {
+          const float cp = (colw[0][j] + colw[1][j]) + (colw[2][j] + colw[3][j]);
+          dcs = rowl[j] - cp - wjr[q4] * kt[q4];
+          if (j == g.nvalid - 1) dcs += dT;
+        } else {
+          dcs = -0.5f * kdk[q4];
+        }
         if (ddt) ddt[g.row + g.t0 + j] = dd[q4];
       }
       dcl[j] = dcs;
@@ -1106,6 +1095,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   }
   __syncthreads();
   // da_t = sum_{s >= t} dcs_s within the block: a reverse scan by wave 0
+  // (order 2: the block's total goes to btot; k_bwd_da_tail then adds the
+  // totals of the later blocks)
   if (tid < BLK) {
     float x = dcl[BLK - 1 - tid];  // lane l holds dcs of token 63 - l
     for (int off = 1; off < WAVE; off <<= 1) {
@@ -1114,6 +1105,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     }
     const int t = BLK - 1 - tid;
     if (t < g.nvalid) da[g.row + g.t0 + t] = x;
+    if (ORDER == 2 && tid == BLK - 1) btot[slot] = x;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_bwd_da_tail (order 2): da_t += the totals of every later block of the
+// head (the block kernel wrote each block's in-block reverse cumsum and its
+// total).  One workgroup per head: the blocks in chunks of 256 from the
+// last, a reverse scan of the chunk's totals in LDS and the running suffix of
+// the later chunks, both in fp64; then the chunk's tokens, coalesced.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_bwd_da_tail(const float* __restrict__ btot, int64_t N,
+                                                     int64_t nblk, float* __restrict__ da) {
+  constexpr int NT = 256;
+  __shared__ double sh[NT];
+  __shared__ float suf[NT];
+  const int64_t bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  double carry = 0.0;  // totals of the blocks after the current chunk
+  for (int64_t ch = (nblk - 1) / NT; ch >= 0; --ch) {
+    const int64_t c = ch * NT + tid;
+    const double x = c < nblk ? (double)btot[bh * nblk + c] : 0.0;
+    sh[tid] = x;
+    __syncthreads();
+    for (int off = 1; off < NT; off <<= 1) {  // sh[t] <- sum over t' >= t
+      const double y = tid + off < NT ? sh[tid + off] : 0.0;
+      __syncthreads();
+      sh[tid] += y;
+      __syncthreads();
+    }
+    suf[tid] = (float)(carry + (sh[tid] - x));  // blocks after c
+    carry += sh[0];
+    __syncthreads();
+    const int64_t t0 = ch * NT * BLK, t1 = (ch + 1) * NT * BLK < N ? (ch + 1) * NT * BLK : N;
+    for (int64_t t = t0 + tid; t < t1; t += NT) da[bh * N + t] += suf[(t - t0) / BLK];
+    __syncthreads();
   }
 }
 
@@ -1247,16 +1274,17 @@ static hipError_t bwd_o2(const void* q, const void* k, const void* v, const floa
   // them: one workgroup per (head, first feature index), sequential over the
   // blocks
   hipLaunchKernelGGL(k_bwd_dnum<DH>, grid, blk, 0, stream, y, den, dy, a_cs, N, chunk, nb, dnw, ddw);
-  float* gsdp = ws + L.gsd;
+  float* btot = ws + L.btot;
   // first feature indices per scan workgroup (measured on the 4K step: 1 tile
   // 5.02 ms, 2 tiles 5.34 ms, 4 tiles 5.12 ms)
   constexpr int AP = 1;
   hipLaunchKernelGGL((k_bwd_phi_scan<St, 0, AP>), dim3((unsigned)(BH * DH / AP)), blk, 0, stream, ks, vs,
-                     dt, nullptr, nullptr, a_cs, N, chunk, nb, sst, nullptr, nullptr);
+                     dt, nullptr, nullptr, a_cs, N, chunk, nb, sst);
   hipLaunchKernelGGL((k_bwd_phi_scan<St, 1, AP>), dim3((unsigned)(BH * DH / AP)), blk, 0, stream, qs,
-                     nullptr, nullptr, dnw, ddw, a_cs, N, chunk, nb, gst, sst, gsdp);
+                     nullptr, nullptr, dnw, ddw, a_cs, N, chunk, nb, gst);
   hipLaunchKernelGGL((k_bwd_block<St, DH, 2>), grid, blk, 0, stream, qs, ks, vs, dt, a_cs, N, chunk, nb,
-                     sst, gst, gsdp, dnw, ddw, dq, dk, dv, ddt, da);
+                     sst, gst, btot, dnw, ddw, dq, dk, dv, ddt, da);
+  hipLaunchKernelGGL(k_bwd_da_tail, dim3((unsigned)BH), dim3(256), 0, stream, btot, N, nb, da);
   return hipGetLastError();
 }
 

@@ -379,107 +379,137 @@ __global__ __launch_bounds__(256) void k_bwd_dnum(const float* __restrict__ y,
 }
 
 // ---------------------------------------------------------------------------
-// k_bwd_phi_scan (order 2, d_h 64): the state slots of one head and AP first
-// feature indices a, scanned over the blocks in one workgroup (the state
-// tiles stay in registers): slot c <- the running tile, then running = e^{T_c}
-// running + the block's increment sum_t wgt_t x_ta x_tb y_tc (and the
-// normaliser row sum_t wgt_t zw_t x_ta x_tb).  MODE 0: forward over the
-// blocks, x = k, y = v dt, wgt = e^{T - cs}, zw = 1 (the states S_c, z_c
+// k_bwd_phi_scan (order 2, d_h 64, bf16 inputs): the state slots of one head
+// and one first feature index a, scanned over the blocks in one workgroup
+// (the state tile stays in registers): slot c <- the running tile, then
+// running = e^{T_c} running + the block's increment sum_t wgt_t x_ta x_tb y_tc
+// (and the normaliser row sum_t wgt_t zw_t x_ta x_tb).  MODE 0: forward over
+// the blocks, x = k, y = v dt, wgt = e^{T - cs}, zw = 1 (the states S_c, z_c
 // entering each block).  MODE 1: in reverse, x = q, y = dnum, wgt = e^{cs},
 // zw = dden (the gradients G_{c+1}, g_{c+1} of the state leaving each block).
+// Each block is staged transposed (token index contiguous) as bf16: XT[b][t]
+// = x_tb (exact for bf16 inputs) and the high and low parts YH, YL[c][t] of
+// s_t y_tc, s_t = x_ta wgt_t (the factor of this a goes with y, so x needs no
+// split); lane t of wave w stages features 16 w .. 16 w + 15 of token t, so
+// the transposing stores are free of bank conflicts.  The update is then a
+// product over the block's tokens with one 16-byte read per operand part
+// and two bf16 MFMAs per pair of fragments.  Wave w holds rows b = 16 w +
+// 4 gq + q4 of the tile (all 64 columns c = 16 nt + n).
 // ---------------------------------------------------------------------------
-template <typename St, int MODE, int AP>
-__global__ __launch_bounds__(256) void k_bwd_phi_scan(const St* __restrict__ xs,
-                                                      const St* __restrict__ vs,
+template <int MODE>
+__global__ __launch_bounds__(256) void k_bwd_phi_scan(const uint16_t* __restrict__ xs,
+                                                      const uint16_t* __restrict__ vs,
                                                       const float* __restrict__ dt,
                                                       const float* __restrict__ dnw,
                                                       const float* __restrict__ ddw,
                                                       const float* __restrict__ a_cs, int64_t N,
                                                       int64_t chunk, int64_t nblk,
                                                       float* __restrict__ out) {
-  constexpr int DH = 64, QC = DH / 4, NTD = DH / 16;
+  constexpr int DH = 64, NTD = DH / 16;
   constexpr int64_t E = (int64_t)DH * DH * DH + DH * DH;
-  constexpr int NA = DH / AP;  // workgroups per head
-  __shared__ float X[BLK * PF], Y[BLK * PF], wl[BLK], wz[BLK];
-  const int64_t bh = blockIdx.x / NA;
-  const int a0 = (int)(blockIdx.x - bh * NA) * AP;
-  const int tid = threadIdx.x, r = tid >> 2, c0 = (tid & 3) * QC;
+  __shared__ __attribute__((aligned(16))) __bf16 XT[DH * PH], YH[DH * PH], YL[DH * PH];
+  __shared__ __attribute__((aligned(16))) float sz[BLK];  // x_ta wgt_t zw_t
+  const int64_t bh = blockIdx.x / DH;
+  const int a = (int)(blockIdx.x - bh * DH);
+  const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, n = lane & 15, gq = lane >> 4;
   const int64_t row = bh * N;
-  // running tiles: rows (a0 + ai, b = 16 wave + 4 gq + q4), columns 16 nt + n
-  f32x4 run[AP][NTD];
-  float runz[AP];  // running normaliser entries (a0 + ai, b = 16 wave + n) (lanes gq == 0)
+  f32x4 run[NTD];   // rows (a, b = 16 wave + 4 gq + q4), columns 16 nt + n
+  float runz = 0.f;  // normaliser entry (a, b = 16 wave + n) (lanes gq == 0)
 #pragma unroll
-  for (int ai = 0; ai < AP; ++ai) {
-#pragma unroll
-    for (int nt = 0; nt < NTD; ++nt) run[ai][nt] = zero4();
-    runz[ai] = 0.f;
-  }
+  for (int nt = 0; nt < NTD; ++nt) run[nt] = zero4();
+  const bool active = 16 * wave + 15 >= a;  // strips entirely below a are never read
   for (int64_t step = 0; step < nblk; ++step) {
     const int64_t blk = MODE == 0 ? step : nblk - 1 - step;
     const int64_t t0 = blk * BLK;
     const int nvalid = (int)((N - t0) < BLK ? (N - t0) : BLK);
     const float base = (t0 % chunk == 0) ? 0.f : a_cs[row + t0 - 1];
     const float T = a_cs[row + t0 + nvalid - 1] - base;
-    // the slot of this block gets the running tiles: rows (a, b) of the
+    // the slot of this block gets the running tile: rows (a, b) of the
     // strips that hold some b >= a only (the state is symmetric in a, b; the
     // readers take rows b >= a), and every normaliser entry
     float* o = out + (bh * nblk + blk) * E;
+    if (active) {
 #pragma unroll
-    for (int ai = 0; ai < AP; ++ai) {
-      const int a = a0 + ai;
-      if (16 * wave + 15 >= a) {
+      for (int nt = 0; nt < NTD; ++nt)
 #pragma unroll
-        for (int nt = 0; nt < NTD; ++nt)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            o[((int64_t)a * DH + 16 * wave + 4 * gq + q4) * DH + 16 * nt + n] = run[ai][nt][q4];
-      }
-      if (gq == 0) o[(int64_t)DH * DH * DH + a * DH + 16 * wave + n] = runz[ai];
+        for (int q4 = 0; q4 < 4; ++q4)
+          o[((int64_t)a * DH + 16 * wave + 4 * gq + q4) * DH + 16 * nt + n] = run[nt][q4];
     }
-    // stage the block: X = x rows, Y = y rows, per-token weights
-    const bool ok = r < nvalid;
-    const int64_t rr = row + t0 + (ok ? r : 0);
+    if (gq == 0) o[(int64_t)DH * DH * DH + a * DH + 16 * wave + n] = runz;
+    // stage token t = lane, features 16 wave .. 16 wave + 15
+    const int t = lane;
+    const bool ok = t < nvalid;
+    const int64_t rr = row + t0 + (ok ? t : 0);
+    const int f0 = 16 * wave;
     const float cs = ok ? a_cs[rr] - base : 0.f;
-#pragma unroll
-    for (int u = 0; u < QC; ++u) {
-      const float xv = Elem<St>::ld(xs, rr * DH + c0 + u);
-      X[r * PF + c0 + u] = ok ? xv : 0.f;
-    }
+    bf16x8 x0 = *reinterpret_cast<const bf16x8*>(xs + rr * DH + f0);
+    bf16x8 x1 = *reinterpret_cast<const bf16x8*>(xs + rr * DH + f0 + 8);
+    const float xa = ok ? __uint_as_float((uint32_t)xs[rr * DH + a] << 16) : 0.f;
+    float y[16], wgt, zw;
     if constexpr (MODE == 0) {
-      const float d = ok ? (dt ? dt[rr] : 1.f) : 0.f;
+      const float d = dt ? dt[rr] : 1.f;
+      const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(vs + rr * DH + f0);
+      const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(vs + rr * DH + f0 + 8);
 #pragma unroll
-      for (int u = 0; u < QC; ++u) Y[r * PF + c0 + u] = Elem<St>::ld(vs, rr * DH + c0 + u) * d;
-      if ((tid & 3) == 0) {
-        wl[r] = ok ? expf(T - cs) : 0.f;
-        wz[r] = wl[r];
+      for (int e = 0; e < 8; ++e) {
+        y[e] = (float)v0[e] * d;
+        y[8 + e] = (float)v1[e] * d;
       }
+      wgt = ok ? expf(T - cs) : 0.f;
+      zw = 1.f;
     } else {
-      const float* dp = dnw + (bh * nblk + blk) * (BLK * DH) + r * DH + c0;
+      const float* dp = dnw + (bh * nblk + blk) * (BLK * DH) + t * DH + f0;
 #pragma unroll
-      for (int u = 0; u < QC; ++u) Y[r * PF + c0 + u] = dp[u];
-      if ((tid & 3) == 0) {
-        const float e = ok ? expf(cs) : 0.f;
-        wl[r] = e;
-        wz[r] = e * ddw[(bh * nblk + blk) * BLK + r];
+      for (int u = 0; u < 4; ++u) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dp + 4 * u);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[4 * u + e] = d4[e];
       }
+      wgt = ok ? expf(cs) : 0.f;
+      zw = ddw[(bh * nblk + blk) * BLK + t];
     }
+    if (!ok) {
+      x0 = bf16x8{};
+      x1 = bf16x8{};
+    }
+    const float sx = xa * wgt;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      XT[(f0 + u) * PH + t] = u < 8 ? x0[u] : x1[u - 8];
+      const float yv = sx * y[u];
+      const __bf16 h = (__bf16)yv;
+      YH[(f0 + u) * PH + t] = h;
+      YL[(f0 + u) * PH + t] = (__bf16)(yv - (float)h);
+    }
+    if (wave == 0) sz[t] = sx * zw;
     __syncthreads();
     const float eT = expf(T);
 #pragma unroll
-    for (int ai = 0; ai < AP; ++ai) {
-      const int a = a0 + ai;
+    for (int nt = 0; nt < NTD; ++nt) run[nt] = eT * run[nt];
+    if (active) {
 #pragma unroll
-      for (int nt = 0; nt < NTD; ++nt) run[ai][nt] = eT * run[ai][nt];
-      if (16 * wave + 15 >= a)  // strips entirely below a are never read
-        mm_strip<NTD, BLK>(run[ai], 16 * wave, n, gq,
-                           [&](int m, int t) { return X[t * PF + m] * X[t * PF + a] * wl[t]; },
-                           [&](int t, int c) { return Y[t * PF + c]; });
+      for (int kk = 0; kk < BLK; kk += 32) {
+        const int ko = kk + 8 * gq;
+        const bf16x8 ah = *reinterpret_cast<const bf16x8*>(&XT[(16 * wave + n) * PH + ko]);
+#pragma unroll
+        for (int nt = 0; nt < NTD; ++nt) {
+          const bf16x8 bh = *reinterpret_cast<const bf16x8*>(&YH[(16 * nt + n) * PH + ko]);
+          const bf16x8 bl = *reinterpret_cast<const bf16x8*>(&YL[(16 * nt + n) * PH + ko]);
+          run[nt] = mfma_bf16(ah, bh, run[nt]);
+          run[nt] = mfma_bf16(ah, bl, run[nt]);
+        }
+      }
+    }
+    // normaliser row b = 16 wave + n over tokens 16 gq .. 16 gq + 15
+    {
+      const bf16x8 p0 = *reinterpret_cast<const bf16x8*>(&XT[(16 * wave + n) * PH + 16 * gq]);
+      const bf16x8 p1 = *reinterpret_cast<const bf16x8*>(&XT[(16 * wave + n) * PH + 16 * gq + 8]);
       float az = 0.f;
 #pragma unroll
-      for (int t = 16 * gq; t < 16 * gq + 16; ++t) az += X[t * PF + 16 * wave + n] * X[t * PF + a] * wz[t];
+      for (int e = 0; e < 8; ++e) az += (float)p0[e] * sz[16 * gq + e] + (float)p1[e] * sz[16 * gq + 8 + e];
       az = sum_over_groups(az);
-      runz[ai] = eT * runz[ai] + az;
+      runz = eT * runz + az;
     }
     __syncthreads();
   }
@@ -1275,13 +1305,11 @@ static hipError_t bwd_o2(const void* q, const void* k, const void* v, const floa
   // blocks
   hipLaunchKernelGGL(k_bwd_dnum<DH>, grid, blk, 0, stream, y, den, dy, a_cs, N, chunk, nb, dnw, ddw);
   float* btot = ws + L.btot;
-  // first feature indices per scan workgroup (measured on the 4K step: 1 tile
-  // 5.02 ms, 2 tiles 5.34 ms, 4 tiles 5.12 ms)
-  constexpr int AP = 1;
-  hipLaunchKernelGGL((k_bwd_phi_scan<St, 0, AP>), dim3((unsigned)(BH * DH / AP)), blk, 0, stream, ks, vs,
-                     dt, nullptr, nullptr, a_cs, N, chunk, nb, sst);
-  hipLaunchKernelGGL((k_bwd_phi_scan<St, 1, AP>), dim3((unsigned)(BH * DH / AP)), blk, 0, stream, qs,
-                     nullptr, nullptr, dnw, ddw, a_cs, N, chunk, nb, gst);
+  // one workgroup per (head, first feature index)
+  hipLaunchKernelGGL((k_bwd_phi_scan<0>), dim3((unsigned)(BH * DH)), blk, 0, stream, ks, vs, dt, nullptr,
+                     nullptr, a_cs, N, chunk, nb, sst);
+  hipLaunchKernelGGL((k_bwd_phi_scan<1>), dim3((unsigned)(BH * DH)), blk, 0, stream, qs, nullptr, nullptr,
+                     dnw, ddw, a_cs, N, chunk, nb, gst);
   hipLaunchKernelGGL((k_bwd_block<St, DH, 2>), grid, blk, 0, stream, qs, ks, vs, dt, a_cs, N, chunk, nb,
                      sst, gst, btot, dnw, ddw, dq, dk, dv, ddt, da);
   hipLaunchKernelGGL(k_bwd_da_tail, dim3((unsigned)BH), dim3(256), 0, stream, btot, N, nb, da);

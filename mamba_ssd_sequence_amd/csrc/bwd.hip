@@ -682,7 +682,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
   }
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) colP[nt] = sum_over_groups(colP[nt]);
-  if (gq == 0) {
+  if (ORDER == 1 && gq == 0) {  // (order 2 takes da from the keys' gradients)
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) colw[wave][16 * nt + n] = colP[nt];
   }
@@ -779,23 +779,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         for (int q4 = 0; q4 < 4; ++q4) {
           const int i = 16 * wave + 4 * gq + q4;
           const float qa = X0[i * PF + a];
-          float r1 = 0.f, r2 = 0.f;
+          const float c2 = 2.f * eir[q4] * qa;
+          // the entries b < a of the first column tile taken as zero: r1 =
+          // sum_{b >= a} U_i[a][b] q_ib, and dq_ib += 2 e_i q_ia U_i[a][b] for
+          // b >= a, the diagonal's share (tdiag) taken back below
+          float r1 = 0.f, tdiag = 0.f;
 #pragma unroll
           for (int nt = 0; nt < NTD; ++nt) {
             const int b = 16 * nt + n;
-            const float tq = ta[nt][q4] * X0[i * PF + b];
-            if (b >= a) r1 += tq;
-            r2 += b > a ? 2.f * tq : (b == a ? tq : 0.f);
-            if (b > a) dqo[nt][q4] += 2.f * eir[q4] * qa * ta[nt][q4];
+            const float t = b >= a ? ta[nt][q4] : 0.f;
+            r1 = fmaf(t, X0[i * PF + b], r1);
+            dqo[nt][q4] = fmaf(c2, t, dqo[nt][q4]);
+            tdiag = b == a ? t : tdiag;
           }
           r1 = sum16(r1);
-          r2 = sum16(r2);
           // (every tile gets an add, zero but for tile a / 16: a store under
           // a test of the tile index would become a dynamically indexed array)
-          const float add = n == (a & 15) ? 2.f * eir[q4] * r1 : 0.f;
+          const float add = n == (a & 15) ? 2.f * eir[q4] * r1 - c2 * tdiag : 0.f;
 #pragma unroll
           for (int nt = 0; nt < NTD; ++nt) dqo[nt][q4] += nt == (a >> 4) ? add : 0.f;
-          if (n == 0) dci[q4] += eir[q4] * qa * r2;  // reduced over n below
         }
       } else {  // (Q Z)[i][a']
         mm_strip<NTD, DH, EX, false>(ta, 16 * wave, n, gq, [&](int m, int b) { return X0[m * PF + b]; },
@@ -805,10 +807,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
           const int i = 16 * wave + 4 * gq + q4;
           const float f = eir[q4] * ddl[i];
 #pragma unroll
-          for (int nt = 0; nt < NTD; ++nt) {
-            dqo[nt][q4] += 2.f * f * ta[nt][q4];
-            dci[q4] += f * X0[i * PF + 16 * nt + n] * ta[nt][q4];
-          }
+          for (int nt = 0; nt < NTD; ++nt) dqo[nt][q4] += 2.f * f * ta[nt][q4];
         }
       }
       __syncthreads();
@@ -825,7 +824,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
     const int i = 16 * wave + 4 * gq + q4;
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) dci[q4] += __shfl_xor(dci[q4], off, WAVE);
-    if (n == 0) rowl[i] = rowP[q4] + dci[q4];
+    if (ORDER == 1 && n == 0) rowl[i] = rowP[q4] + dci[q4];
   }
   __syncthreads();
 
@@ -1004,21 +1003,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
         for (int q4 = 0; q4 < 4; ++q4) {
           const int j = 16 * wave + 4 * gq + q4;
           const float ka = kval(j, a);
-          float r1 = 0.f, r2 = 0.f;
+          const float c2 = 2.f * wjr[q4] * ka;
+          float r1 = 0.f, tdiag = 0.f;  // as in phase 3
 #pragma unroll
           for (int nt = 0; nt < NTD; ++nt) {
             const int b = 16 * nt + n;
-            const float vk = va[nt][q4] * kval(j, b);
-            if (b >= a) r1 += vk;
-            r2 += b > a ? 2.f * vk : (b == a ? vk : 0.f);
-            if (b > a) dka[nt][q4] += 2.f * wjr[q4] * ka * va[nt][q4];
+            const float t = b >= a ? va[nt][q4] : 0.f;
+            r1 = fmaf(t, kval(j, b), r1);
+            dka[nt][q4] = fmaf(c2, t, dka[nt][q4]);
+            tdiag = b == a ? t : tdiag;
           }
           r1 = sum16(r1);
-          r2 = sum16(r2);
-          const float add = n == (a & 15) ? 2.f * wjr[q4] * r1 : 0.f;  // as in phase 3
+          const float add = n == (a & 15) ? 2.f * wjr[q4] * r1 - c2 * tdiag : 0.f;
 #pragma unroll
           for (int nt = 0; nt < NTD; ++nt) dka[nt][q4] += nt == (a >> 4) ? add : 0.f;
-          if (n == 0) kt[q4] += ka * r2;  // reduced over n below
         }
         // dvop_j += w_j k_ja (2 sum_{b > a} k_jb G[(a, b)] + k_ja G[(a, a)])
         // (k exact in bf16; the entries b <= a of its operand count as zero)

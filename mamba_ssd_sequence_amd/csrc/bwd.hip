@@ -425,16 +425,19 @@ __global__ __launch_bounds__(256) void k_bwd_phi_scan(const uint16_t* __restrict
     const int nvalid = (int)((N - t0) < BLK ? (N - t0) : BLK);
     const float base = (t0 % chunk == 0) ? 0.f : a_cs[row + t0 - 1];
     const float T = a_cs[row + t0 + nvalid - 1] - base;
-    // the slot of this block gets the running tile: rows (a, b) of the
-    // strips that hold some b >= a only (the state is symmetric in a, b; the
-    // readers take rows b >= a), and every normaliser entry
+    // the slot of this block gets the running tile: rows (a, b), b >= a
+    // only (the state is symmetric in a, b; the readers take rows b >= a and
+    // zero the others of the strips they load), and every normaliser entry
     float* o = out + (bh * nblk + blk) * E;
     if (active) {
 #pragma unroll
-      for (int nt = 0; nt < NTD; ++nt)
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int b = 16 * wave + 4 * gq + q4;
+        if (b >= a) {
 #pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          o[((int64_t)a * DH + 16 * wave + 4 * gq + q4) * DH + 16 * nt + n] = run[nt][q4];
+          for (int nt = 0; nt < NTD; ++nt) o[((int64_t)a * DH + b) * DH + 16 * nt + n] = run[nt][q4];
+        }
+      }
     }
     if (gq == 0) o[(int64_t)DH * DH * DH + a * DH + 16 * wave + n] = runz;
     // stage token t = lane, features 16 wave .. 16 wave + 15
@@ -763,7 +766,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
       // a < DH: tile a of S_c (pre-split); a == DH: Z (fp32, in X1's place:
       // the dnum parts are not read by that pass)
       if (a < DH) {
-        if (sr >= rmin(a)) split16(pre, &Sh[sr * PH + sc], &Sl[sr * PH + sc]);
+        if (sr >= rmin(a)) {
+          // rows b < a of the strip are not written by the scan: zero
+          const f32x16 x = sr >= a ? pre : f32x16{};
+          split16(x, &Sh[sr * PH + sc], &Sl[sr * PH + sc]);
+        }
       } else {
 #pragma unroll
         for (int u = 0; u < 16; ++u) X1[sr * PF + sc + u] = pre[u];
@@ -975,12 +982,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 8))) voi
       // d_h x d_h matrix, fp32)
       if (a < DH) {
         if (sr >= rmin(a)) {
-          split16(pre, &Gh[sr * PH + sc], &Gl[sr * PH + sc]);
+          const f32x16 x = sr >= a ? pre : f32x16{};  // as in phase 3
+          split16(x, &Gh[sr * PH + sc], &Gl[sr * PH + sc]);
 #pragma unroll
           for (int u = 0; u < 16; ++u) {
-            const __bf16 h = (__bf16)pre[u];
+            const __bf16 h = (__bf16)x[u];
             GTh[(sc + u) * PH + sr] = h;
-            GTl[(sc + u) * PH + sr] = (__bf16)(pre[u] - (float)h);
+            GTl[(sc + u) * PH + sr] = (__bf16)(x[u] - (float)h);
           }
         }
       } else {

@@ -1114,6 +1114,36 @@ def test_backward_order2_full_size_sampled_heads():
         assert err <= 1e-4, (b, h, "dv")
 
 
+def test_backward_order2_long_sequence_decay_gradient():
+    """Order 2 beyond 256 blocks (N 17100: 268 blocks, the last one ragged),
+    where the decay gradient's suffix over later blocks runs in two chunks:
+    da against -(1/2) sum_{s >= t} k_s . dk_s formed in fp64 from the same
+    run's k and dk (an identity of the definition, pinned on the oracle by
+    test_backward_decay_gradient_from_key_gradients; it holds at any size),
+    and every gradient finite.  The tolerance is relative to the same sum of
+    the terms' magnitudes."""
+    cfg = I.CONFIGS["o2_bf16_4k"]
+    N = 17100
+    say("backward order 2 long sequence", N)
+    inp = I.make_forward_inputs(cfg, B=1, H=1, N=N, seed=41)
+    ssd = ssd_mod()
+    dt_d, a_cs, _ = ssd.prep(to_dev_f32(inp.dt_proj), to_dev_f32(inp.dt_bias), to_dev_f32(inp.A_log), cfg.chunk)
+    q_d, k_d, v_d = (to_dev_qkv(x, cfg.dtype) for x in (inp.q, inp.k, inp.v))
+    den_d = torch.empty(inp.dt_proj.shape, device="cuda")
+    y_d = ssd.forward(q_d, k_d, v_d, dt_d, a_cs, 2, cfg.chunk, den=den_d)
+    dy = np.random.default_rng(42).standard_normal(y_d.shape).astype(np.float32)
+    dq, dk, dv, ddt, da = run_backward(q_d, k_d, v_d, dt_d, a_cs, y_d, den_d, to_dev_f32(dy), cfg.chunk, 2)
+    for name, g in (("dq", dq), ("dk", dk), ("dv", dv), ("ddt", ddt), ("da", da)):
+        assert np.isfinite(g).all(), name
+    kf = I.bf16_bits_to_f64(inp.k)
+    term = -0.5 * (kf * dk.astype(np.float64)).sum(axis=-1)  # [1, 1, N]
+    ref = np.cumsum(term[..., ::-1], axis=-1)[..., ::-1]
+    mag = np.cumsum(np.abs(term)[..., ::-1], axis=-1)[..., ::-1]
+    err = float((np.abs(da - ref) / (mag + 1e-30)).max())
+    say("  da against the key-gradient identity", err)
+    assert err <= 1e-5
+
+
 @pytest.mark.parametrize("amask", [False, True])
 def test_prep_backward(amask):
     """The discretisation's chain rule against the oracle's."""

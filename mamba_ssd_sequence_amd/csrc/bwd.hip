@@ -1200,9 +1200,10 @@ __global__ __launch_bounds__(1024) void k_prep_bwd(const float* __restrict__ p0,
                                                    int64_t H, int64_t N, float* __restrict__ o0,
                                                    float* __restrict__ o1,
                                                    float* __restrict__ o2) {
-  // one workgroup of 1024 threads per head h, looping over the batch and the
-  // tokens (4 tokens in flight per thread)
-  constexpr int NTH = 1024, U = 4;
+  // one workgroup of 1024 threads per head h over the head's B x N tokens,
+  // U per thread in flight: every load of a pass is issued before any is used
+  // (indices past the end read the head's first token and store nothing)
+  constexpr int NTH = 1024, U = 8;
   const int64_t h = blockIdx.x;
   __shared__ float red[2][NTH / WAVE];
   float sb = 0.f, sa = 0.f;
@@ -1211,26 +1212,35 @@ __global__ __launch_bounds__(1024) void k_prep_bwd(const float* __restrict__ p0,
     A = -expf(A_log[h]);
     bias = p1[h];
   }
-  for (int64_t b = 0; b < B; ++b) {
-    const int64_t base = (b * H + h) * N;
-    for (int64_t n0 = 0; n0 < N; n0 += NTH * U) {
+  const int64_t total = B * N;
+  for (int64_t k0 = 0; k0 < total; k0 += NTH * U) {
+    int64_t idx[U];
+    bool ok[U];
+    float x[U], dav[U], g[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t n = n0 + u * NTH + threadIdx.x;
-        if (n >= N) continue;
-        const int64_t i = base + n;
-        if (MODE == 0) {
-          const float x = p0[i] + bias;
-          const float dtv = softplus_f(x);
-          const float gdt = (ddt ? ddt[i] : 0.f) + da[i] * A;
-          const float d = gdt * sigmoid_f(x);
-          o0[i] = d;
+    for (int u = 0; u < U; ++u) {
+      const int64_t k = k0 + u * NTH + threadIdx.x;
+      ok[u] = k < total;
+      const int64_t b = ok[u] ? k / N : 0, n = ok[u] ? k - b * N : 0;
+      idx[u] = (b * H + h) * N + n;
+      x[u] = p0[idx[u]];
+      dav[u] = da[idx[u]];
+      g[u] = MODE == 0 ? (ddt ? ddt[idx[u]] : 0.f) : (p1 ? ddt[idx[u]] : 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (MODE == 0) {
+        const float xv = x[u] + bias;
+        const float dtv = softplus_f(xv);
+        const float d = (g[u] + dav[u] * A) * sigmoid_f(xv);
+        if (ok[u]) {
+          o0[idx[u]] = d;
           sb += d;
-          sa += da[i] * dtv;
-        } else {
-          o0[i] = -da[i] * sigmoid_f(p0[i]);
-          if (p1) o1[i] = ddt[i] * sigmoid_f(p1[i]);
+          sa += dav[u] * dtv;
         }
+      } else if (ok[u]) {
+        o0[idx[u]] = -dav[u] * sigmoid_f(x[u]);
+        if (p1) o1[idx[u]] = g[u] * sigmoid_f(p1[idx[u]]);
       }
     }
   }

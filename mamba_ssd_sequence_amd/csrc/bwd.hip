@@ -36,7 +36,9 @@
 // products run on the bf16 matrix cores with every fp32 operand split into
 // a high and a low bf16 part (mm_strip_tiles: at most 3 2^-16 of each
 // product's magnitude, against 2^-24 for fp32 arithmetic, and 3 bf16 MFMAs in
-// place of 8 fp32 ones per 32 k).  Kernels:
+// place of 8 fp32 ones per 32 k; the order-2 state-tile products and scans
+// split their operands once into LDS instead, mm_pre_tiles, and an operand
+// exact in bf16 keeps one part).  Kernels:
 //   k_bwd_outer  (x2)  per block, sum_i wgt_i x_i y_i^T and sum_i wgt_i zw_i x_i:
 //                      the block's state increment (forward states, recomputed)
 //                      and R_c, r_c; the latter also writes dnum and dden

@@ -112,29 +112,32 @@ __device__ __forceinline__ void split_bf16(float x, bf16x8& hi, bf16x8& lo, int 
 // and low parts, three products hi*hi + lo*hi + hi*lo, fp32 accumulation;
 // the dropped lo*lo and the rounding of the low parts leave at most 3 2^-16
 // of each product |a_k b_k|.  Lane (n, gq) supplies A[m0 + n][k] and B[k][16 nt
-// + n] for k = kk + gq + 4 e in its operand slot e (the same slots for both
-// operands, so each k is summed once); acc[nt][q4] = out[m0 + 4 gq + q4][16 nt
-// + n] as for every 16x16 MFMA.  AX / BX: the A / B values are exact in bf16
+// + n] for k = kk + ko(gq) + e in its operand slot e, ko = 0, 16, 8, 24 for gq
+// = 0 .. 3 (the same slots for both operands, so each k is summed once; with
+// the odd row pitch the 32 lanes of a half-wave, gq 0 and 1 or 2 and 3, read
+// 32 distinct LDS banks); acc[nt][q4] = out[m0 + 4 gq + q4][16 nt + n] as for
+// every 16x16 MFMA.  AX / BX: the A / B values are exact in bf16
 // (q, k, v of bf16 inputs): that operand is not split, and its low-part
 // product is skipped (two MFMAs per pair of operands, one if both are exact).
 template <int NT0, int NT, int K, bool AX = false, bool BX = false, class FA, class FB>
 __device__ __forceinline__ void mm_strip_tiles(f32x4 (&acc)[NT], int m0, int n, int gq, int k0, FA A, FB B) {
   static_assert(K % 32 == 0, "k in steps of 32");
+  const int ko = 16 * (gq & 1) + 8 * (gq >> 1);
 #pragma unroll 1
   for (int kk = k0 & ~31; kk < K; kk += 32) {
     bf16x8 ah, al;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      if constexpr (AX) ah[e] = (__bf16)A(m0 + n, kk + gq + 4 * e);
-      else split_bf16(A(m0 + n, kk + gq + 4 * e), ah, al, e);
+      if constexpr (AX) ah[e] = (__bf16)A(m0 + n, kk + ko + e);
+      else split_bf16(A(m0 + n, kk + ko + e), ah, al, e);
     }
 #pragma unroll
     for (int nt = NT0; nt < NT; ++nt) {
       bf16x8 bh, bl;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        if constexpr (BX) bh[e] = (__bf16)B(kk + gq + 4 * e, 16 * nt + n);
-        else split_bf16(B(kk + gq + 4 * e, 16 * nt + n), bh, bl, e);
+        if constexpr (BX) bh[e] = (__bf16)B(kk + ko + e, 16 * nt + n);
+        else split_bf16(B(kk + ko + e, 16 * nt + n), bh, bl, e);
       }
       acc[nt] = mfma_bf16(ah, bh, acc[nt]);
       if constexpr (!AX) acc[nt] = mfma_bf16(al, bh, acc[nt]);

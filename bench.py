@@ -1,7 +1,7 @@
 """Throughput of the SSD / 2Mamba sequence mixer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-extra]
-                    [--no-cpu-baseline]
+                    [--no-cpu-baseline] [--settle SECONDS]
 
 A step is one pass of the whole hot path over one batch of synthetic inputs
 already resident in HBM: ssd_prep (softplus, A*dt, chunk-local cumsum) followed
@@ -102,6 +102,31 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+# seconds of GPU load run before each workload's warm-up steps (--settle)
+SETTLE_S = 0.25
+
+
+def settle_clocks(dev):
+    """Keep the GPU busy with fp16 GEMMs (torch, hipBLASLt) for SETTLE_S
+    seconds, right before a workload's warm-up steps.  Drawing a workload's
+    inputs on the host leaves the GPU idle for up to seconds, and an idle GPU
+    drops to low clocks: without this the warm-up and the first few dozen
+    timed steps would run while the clocks ramp back up (the 4K order-2 step
+    takes ~0.20 ms over its first 25 steps and ~0.18 ms once settled), so
+    the figure would describe a cold start rather than a running job."""
+    import torch
+    if SETTLE_S <= 0:
+        return
+    a = torch.randn(4096, 4096, dtype=torch.float16, device=dev)
+    b = torch.randn(4096, 4096, dtype=torch.float16, device=dev)
+    t = time.time()
+    while time.time() - t < SETTLE_S:
+        for _ in range(8):
+            c = a @ b
+        torch.cuda.synchronize()
+    del a, b, c
+
+
 def to_dev(x, dtype, dev):
     import torch
     if dtype == I.BF16:
@@ -147,6 +172,7 @@ def bench_forward(cfg: I.Config, steps: int, warmup: int, dev, amask: bool = Fal
         if timer is not None:
             timer.collect()
 
+    settle_clocks(dev)
     for _ in range(warmup):
         step()
     # the timed steps (nothing recorded between the kernels) ...
@@ -239,6 +265,7 @@ def bench_backward(cfg: I.Config, steps: int, warmup: int, dev):
         _, _, _, ddt, da = ssd.backward(q, k, v, dt, a_cs, y, den, dy, cfg.order, cfg.chunk, workspace=ws)
         ssd.prep_backward(dtp, bias, alog, da, ddt)
 
+    settle_clocks(dev)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -283,6 +310,7 @@ def bench_prep_sweep(steps: int, warmup: int, dev, B=4, H=32, N=1 << 21, chunk=6
     nc = -(-N // chunk)
     out = (torch.empty((B, H, N), device=dev), torch.empty((B, H, N), device=dev),
            torch.empty((B, H, nc), device=dev))
+    settle_clocks(dev)
     for _ in range(warmup):
         ssd.prep(dtp, bias, alog, chunk, out=out)
     torch.cuda.synchronize()
@@ -360,6 +388,7 @@ def bench_decode(cfg: I.DecodeConfig, steps: int, warmup: int, dev, packed=False
     norm = torch.zeros((cfg.S, cfg.H, D), device=dev)
     y = torch.empty((cfg.S, cfg.H, cfg.d_h), device=dev)
     bias, alog = to_dev(dec.dt_bias, I.F32, dev), to_dev(dec.A_log, I.F32, dev)
+    settle_clocks(dev)
     for i in range(warmup):
         q, k, v, dtp = toks[i]
         ssd.decode_step(q, k, v, dtp, bias, alog, state, norm, cfg.order, y=y, packed=packed)
@@ -461,6 +490,7 @@ def blas_threads():
 
 
 def main():
+    global SETTLE_S
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
@@ -471,9 +501,13 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the secondary workloads (64K forward, decode)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--settle", type=float, default=SETTLE_S, metavar="SECONDS",
+                    help="GPU load (fp16 GEMMs) before each workload's warm-up steps, so that "
+                         "the clocks have left their idle state (0: none, a cold start)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a device-to-device copy of MIB MiB (reference for HBM counters)")
     a = ap.parse_args()
+    SETTLE_S = a.settle
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the mixer's workloads are per-head independent "
               "and this build has no multi-GPU path; run with --gpus 1.", file=sys.stderr)
@@ -575,6 +609,7 @@ def main():
         "extra": extra,
         "device_ceilings": ceilings,
         "device": torch.cuda.get_device_name(dev),
+        "clock_settle_s": SETTLE_S,
     }
     print(json.dumps(out), flush=True)
 

@@ -341,6 +341,58 @@ def test_forward_full_size_64k(name):
     assert np.all(np.isfinite(got["y"]))
 
 
+@pytest.mark.parametrize("name", ["o2_bf16_64k", "o1_bf16_64k"])
+def test_forward_offsets_past_2e31_elements(name):
+    """Tensors of more than 2^31 elements: 17 distinct heads of the 64K
+    workload, tiled 32 times over H = 544 (q, k, v, y: 2.28e9 elements each;
+    heads 512 and up start past element 2^31 of y, and the order-2 workspace
+    spans 32 GB).  Every copy of a head must reproduce its source head (the
+    copy at the lowest offset) bit for bit in y, den and the final states,
+    which an index that wrapped at 32 bits anywhere would break; two source
+    heads are checked against the oracle on sampled rows (at 544 heads the
+    order-2 state scan runs its one-wave-per-column layout on 64K tokens)."""
+    ssd = ssd_mod()
+    cfg = I.ALL_CONFIGS[name]
+    HS, REP = 17, 32
+    H = HS * REP
+    say("offsets past 2^31", name, "H", H)
+    src = I.make_forward_inputs(cfg, H=HS)
+    assert H * cfg.N * cfg.d_h > 2 ** 31
+    q, k, v = (to_dev_qkv(x, cfg.dtype).repeat(1, REP, 1, 1) for x in (src.q, src.k, src.v))
+    dtp = to_dev_f32(src.dt_proj).repeat(1, REP, 1)
+    bias, alog = to_dev_f32(src.dt_bias).repeat(REP), to_dev_f32(src.A_log).repeat(REP)
+    dt, a_cs, _ = ssd.prep(dtp, bias, alog, cfg.chunk)
+    D = cfg.d_h ** cfg.order
+    den = torch.empty((1, H, cfg.N), device="cuda")
+    fs = torch.empty((1, H, D, cfg.d_h), device="cuda")
+    fn = torch.empty((1, H, D), device="cuda")
+    say("   forward")
+    y = ssd.forward(q, k, v, dt, a_cs, cfg.order, cfg.chunk, den=den, final_state=fs, final_norm=fn)
+    torch.cuda.synchronize()
+    del q, k, v, dtp, dt, a_cs
+    say("   copies against their sources")
+    for t, nm in ((y, "y"), (den, "den"), (fs, "final_state"), (fn, "final_norm")):
+        base = t[:, :HS]
+        for r in range(1, REP):
+            assert torch.equal(t[:, r * HS:(r + 1) * HS], base), (nm, r)
+    assert bool(torch.isfinite(y[:, :HS]).all())
+    qs, ks, vs = src.qkv_f64()
+    dts, a = O.discretise(src.dt_proj, src.dt_bias, src.A_log)
+    vop = vs * dts[..., None]
+    rng = np.random.default_rng(7)
+    for h in (2, 13):
+        rows = sample_rows(cfg.N, 256, rng, block=cfg.chunk, boundaries=False)
+        sl = (slice(0, 1), slice(h, h + 1))
+        ref = O.forward_quadratic(qs[sl], ks[sl], vop[sl], a[sl], cfg.order, rows=rows)
+        got = y[:, h:h + 1, rows].cpu().numpy()
+        err = row_error(got, ref["y"], ref["scale"])
+        say(f"   head {h} (and its copies up to head {h + (REP - 1) * HS}): {len(rows)} rows, "
+            f"{worst(got, ref['y'], ref['scale'], rows)}")
+        assert err <= TOL[cfg.dtype], h
+    del y, den, fs, fn
+    torch.cuda.empty_cache()
+
+
 # (B, H, decay per token): H = 3 runs the order-2 state scan's
 # two-wave-per-column layout and B*H = 32 the one-wave layout; at 0.1 per
 # token the 640 tail tokens decay the state by e^-64 (its scale exponent

@@ -623,6 +623,48 @@ def test_decode_full_size_sampled():
     assert fs_err <= 1e-5 and fn_err <= 1e-5
 
 
+@pytest.mark.parametrize("packed", [False, True])
+def test_decode_offsets_past_2e31_elements(packed):
+    """Order-2 decode states of more than 2^31 elements: 16 distinct
+    sequences of 32 heads tiled 32 times (S = 512; 2.1e9 state entries in the
+    packed layout, 4.3e9 in the full one, so every sequence from 256 on
+    starts past element 2^31 of the full state).  Over 4 steps every copy
+    must reproduce its source sequence bit for bit in y and both states, and
+    one source sequence (all heads) is checked against the oracle."""
+    ssd = ssd_mod()
+    SS, REP, T = 16, 32, 4
+    cfg = I.DecodeConfig("big", S=SS, H=32, d_h=64, order=2, steps=T, dtype=I.BF16, seed=5)
+    say("decode offsets past 2^31, packed" if packed else "decode offsets past 2^31, full layout")
+    dec = I.make_decode_inputs(cfg)
+    D = cfg.d_h * (cfg.d_h + 1) // 2 if packed else cfg.d_h ** 2
+    S = SS * REP
+    assert S * cfg.H * D * cfg.d_h > 2 ** 31
+    state = torch.zeros((S, cfg.H, D, cfg.d_h), device="cuda")
+    norm = torch.zeros((S, cfg.H, D), device="cuda")
+    bias, alog = to_dev_f32(dec.dt_bias), to_dev_f32(dec.A_log)
+    ys, ins = [], []
+    for (q, k, v, dtp) in dec.steps(T):
+        y = ssd.decode_step(*(to_dev_qkv(x, cfg.dtype).repeat(REP, 1, 1) for x in (q, k, v)),
+                            to_dev_f32(dtp).repeat(REP, 1), bias, alog, state, norm, 2, packed=packed)
+        for r in range(1, REP):
+            assert torch.equal(y[r * SS:(r + 1) * SS], y[:SS]), ("y", r)
+        ys.append(y[:SS].cpu().numpy())
+        ins.append((q, k, v, dtp))
+    torch.cuda.synchronize()
+    for t, nm in ((state, "state"), (norm, "norm")):
+        for r in range(1, REP):
+            assert torch.equal(t[r * SS:(r + 1) * SS], t[:SS]), (nm, r)
+    del state, norm
+    torch.cuda.empty_cache()
+    s0 = 5
+    ref = decode_reference([tuple(x[s0:s0 + 1] for x in st) for st in ins], cfg.dtype,
+                           dec.A_log.astype(np.float64), dec.dt_bias.astype(np.float64), 2)
+    y = np.stack([x[s0:s0 + 1] for x in ys], axis=2)  # [1,H,T,d]
+    err = row_error(y, ref["y"], ref["scale_state"])
+    say(f"   sequence {s0} (and its copies up to {s0 + (REP - 1) * SS}), all heads: max err {err:.3e}")
+    assert err <= TOL[cfg.dtype]
+
+
 def test_prefill_then_decode():
     """Forward over N tokens hands its final states to decode; continuing for T
     tokens equals the oracle over N + T tokens."""

@@ -27,10 +27,14 @@ SOURCES = ["api.cpp", "prep.hip", "fwd_blocks.hip", "fwd_o1_scan.hip", "fwd_o2_p
 
 # Packed fp32 VALU ops are disabled for all device code: the kernels use plain
 # fp32 arithmetic only.  hipcc's host pass warns that it does not know the
-# feature; that warning is expected.
+# feature; that warning is expected.  MFMA accumulators are kept in the
+# architectural VGPRs (-amdgpu-mfma-vgpr-form): otherwise the compiler places
+# some of them in AGPRs, and every VALU use of such a result (decays, splits,
+# the output arithmetic) costs an extra v_accvgpr_read/write.
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", INCLUDE, "-I", CSRC,
     "-Wall", "-Wno-unused-function",
 ]

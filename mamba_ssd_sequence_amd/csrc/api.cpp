@@ -306,15 +306,15 @@ ssd_status forward_core(const char* fn, bool noalloc, const void* q, const void*
   hipError_t e;
   if (order == 1 && bf && ssd::o1_scan_supported(BH, d_h, N)) {
     // bf16 inputs: the sequential scan per (head, segment); the segment
-    // aggregates (when the sequence is cut into segments) go to the state
-    // region of the workspace
+    // aggregates and their prefixes (when the sequence is cut into segments)
+    // go to the state region of the workspace
     float* agg = st;
     const size_t na = (ssd::o1_scan_agg_floats(BH, d_h, N) + 63) & ~(size_t)63;
     float* sink = st + na;
     if (na + 64 > L.part - L.state)
       return fail(SSD_ERR_WORKSPACE, "%s: internal: segment aggregates exceed the workspace", fn);
-    if ((e = ssd::launch_o1_scan(true, d_h, q, k, v, dt, a_cs, BH, N, chunk, nullptr, nullptr, agg,
-                                 nullptr, nullptr, nullptr, nullptr, sink, stream)) != hipSuccess)
+    if ((e = ssd::launch_o1_scan(true, d_h, q, k, v, dt, a_cs, BH, N, chunk, initial_state, initial_norm,
+                                 agg, nullptr, nullptr, nullptr, nullptr, sink, stream)) != hipSuccess)
       return hip_status(e, "o1_scan aggregate launch");
     tm.mark();
     e = ssd::launch_o1_scan(false, d_h, q, k, v, dt, a_cs, BH, N, chunk, initial_state, initial_norm,

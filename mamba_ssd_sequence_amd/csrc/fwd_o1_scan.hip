@@ -12,8 +12,10 @@
 // Segments: the sequence is cut into nseg segments of whole blocks so that
 // the heads times segments cover the CUs twice.  An aggregate pass
 // (k_o1_segagg) writes the state contribution and total log-decay of each
-// segment but the last; the scan of segment s starts from the initial state
-// carried through those aggregates (S <- 2^{T_s'} S + A_s' for s' < s).
+// segment but the last, a prefix pass (k_o1_segprefix) turns them in place
+// into the state entering each following segment (the initial state carried
+// through S <- 2^{T_s'} S + A_s' for s' < s), and the scan of segment s
+// starts from that one slot.
 //
 // Per block, wave w owns query rows 16 w .. 16 w + 15 and (for the update)
 // state rows b = 16 w .. 16 w + 15 (d_h 32: waves 0, 1), every value column.
@@ -185,28 +187,6 @@ __global__ __launch_bounds__(256) void k_o1_scan(const uint16_t* __restrict__ q,
   for (int ct = 0; ct < NCT; ++ct) st[ct] = zero4();
   float zs = 0.f;
   const int sb = 16 * wv + 4 * g;  // first state row of this lane
-  if (sw) {
-    if (S0) {
-      const float* s0 = S0 + (int64_t)bh * DH * DH;
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st[ct][r] = s0[(sb + r) * DH + 16 * ct + n];
-      zs = z0[(int64_t)bh * DH + bs];
-    }
-    // the preceding segments' aggregates, in order (loads issued four
-    // segments at a time)
-#pragma unroll 4
-    for (int s2 = 0; s2 < seg; ++s2) {
-      const float* a = agg + ((int64_t)bh * (nseg - 1) + s2) * AGGF;
-      const float f = exp2_fast(a[DH * DH + DH]);
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st[ct][r] = f * st[ct][r] + a[(sb + r) * DH + 16 * ct + n];
-      zs = f * zs + a[DH * DH + bs];
-    }
-  }
   // this lane's query fragments q[il][32 ks + 8 g .. + 7] (the B operand of
   // the scores and of the inter product), one block ahead
   auto load_q = [&](int b, bf16x8 (&qf)[NKS]) {
@@ -235,13 +215,33 @@ __global__ __launch_bounds__(256) void k_o1_scan(const uint16_t* __restrict__ q,
       if (g == 0) S.z[bs] = zs;
     }
   };
-  write_state(sts[0]);
-
   if (b0 % chunk_blocks != 0) prev_raw = csh[b0 * BLK - 1];
   O1Regs R;
   bf16x8 qc[NKS], qn[NKS];
   load_q(b0, qn);
   load_block(b0, R);
+  // the state entering the segment, read while the first block's loads are
+  // in flight: the initial state for the first segment, else the prefix
+  // that k_o1_segprefix left in the previous segment's aggregate slot
+  if (sw) {
+    const float* sp = nullptr;
+    const float* zp0 = nullptr;
+    if (seg > 0) {
+      sp = agg + ((int64_t)bh * (nseg - 1) + seg - 1) * AGGF;
+      zp0 = sp + DH * DH;
+    } else if (S0) {
+      sp = S0 + (int64_t)bh * DH * DH;
+      zp0 = z0 + (int64_t)bh * DH;
+    }
+    if (sp) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[ct][r] = sp[(sb + r) * DH + 16 * ct + n];
+      zs = zp0[bs];
+    }
+  }
+  write_state(sts[0]);
   stage_block(b0, R, sets[0]);
   load_block(b0 + 1 < b1 ? b0 + 1 : b1 - 1, R);
   // stores to the sink, as the loop body issues after its loads: the
@@ -430,8 +430,11 @@ __global__ __launch_bounds__(256) void k_o1_scan(const uint16_t* __restrict__ q,
 // then A = sum_w 2^{T after quarter w} A_w, and the same for z.  The products
 // are those of the scan's update (16x16x32 bf16, the operand k dw in high +
 // low parts); z_b = sum_j w_j k_jb is summed alongside the split.
+// (LDS admits two workgroups per CU at d_h 64, four at d_h 32; the
+// waves-per-EU bound keeps the registers within what that many waves per SIMD
+// allow)
 template <int DH>
-__global__ __launch_bounds__(256) void k_o1_segagg(const uint16_t* __restrict__ k,
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(128 / DH))) void k_o1_segagg(const uint16_t* __restrict__ k,
                                                    const uint16_t* __restrict__ v,
                                                    const float* __restrict__ dt,
                                                    const float* __restrict__ a_cs, int BH, int N,
@@ -602,6 +605,45 @@ __global__ __launch_bounds__(256) void k_o1_segagg(const uint16_t* __restrict__ 
   if (tid == 0) a[DH * DH + DH] = (wT[0] + wT[1]) + (wT[2] + wT[3]);
 }
 
+// Prefix of the segment aggregates, in place: slot s (segment s's state
+// contribution A_s, z contribution and log2 decay total T_s, from
+// k_o1_segagg) becomes the state entering segment s + 1,
+//   P_{s+1} = 2^{T_s} P_s + A_s,  P_0 = the initial state (or 0),
+// for the d_h^2 state and d_h z entries (T_s is left as it is).  One thread
+// per entry of a head's slot, its slots read eight at a time so that their
+// loads are in flight together; the chain itself is the scan's former
+// per-workgroup composition, done once per head instead of once per segment.
+template <int DH>
+__global__ __launch_bounds__(256) void k_o1_segprefix(int BH, int nseg, const float* __restrict__ S0,
+                                                      const float* __restrict__ z0,
+                                                      float* __restrict__ agg) {
+  constexpr int NE = DH * DH + DH;  // state and z entries of a slot
+  constexpr int AGGF = NE + 1;
+  constexpr int PER = (NE + 255) / 256;  // workgroups per head
+  const int bh = blockIdx.x / PER;
+  const int e = (blockIdx.x - bh * PER) * 256 + threadIdx.x;
+  if (bh >= BH || e >= NE) return;
+  float* a = agg + (int64_t)bh * (nseg - 1) * AGGF;
+  float p = 0.f;
+  if (S0) p = e < DH * DH ? S0[(int64_t)bh * DH * DH + e] : z0[(int64_t)bh * DH + (e - DH * DH)];
+  for (int s0 = 0; s0 < nseg - 1; s0 += 8) {
+    float x[8], t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int s = s0 + u < nseg - 1 ? s0 + u : nseg - 2;
+      x[u] = a[(int64_t)s * AGGF + e];
+      t[u] = a[(int64_t)s * AGGF + NE];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (s0 + u < nseg - 1) {
+        p = exp2_fast(t[u]) * p + x[u];
+        a[(int64_t)(s0 + u) * AGGF + e] = p;
+      }
+    }
+  }
+}
+
 // Segments: enough workgroups for two per CU where the sequence allows,
 // each segment at least 4 blocks.
 void o1_scan_segments(int64_t BH, int64_t DH, int64_t N, int* nseg, int* nbs) {
@@ -645,12 +687,17 @@ hipError_t launch_o1_scan(bool agg_pass, int64_t DH, const void* q, const void* 
   hipLaunchKernelGGL((k_o1_scan<DHV>), grid, blk, 0, stream, qq, kk, vv, dt, a_cs, (int)BH, \
                      (int)N, cb, nseg, nbs, S0, z0, agg, y, den, Sf, zf, sink)
   if (agg_pass) {
-    if (DH == 64)
+    const int64_t ne = DH * DH + DH;
+    const dim3 gp((unsigned)(BH * ((ne + 255) / 256)));
+    if (DH == 64) {
       hipLaunchKernelGGL((k_o1_segagg<64>), grid, blk, 0, stream, kk, vv, dt, a_cs, (int)BH, (int)N, cb,
                          nseg, nbs, agg);
-    else
+      hipLaunchKernelGGL((k_o1_segprefix<64>), gp, blk, 0, stream, (int)BH, nseg, S0, z0, agg);
+    } else {
       hipLaunchKernelGGL((k_o1_segagg<32>), grid, blk, 0, stream, kk, vv, dt, a_cs, (int)BH, (int)N, cb,
                          nseg, nbs, agg);
+      hipLaunchKernelGGL((k_o1_segprefix<32>), gp, blk, 0, stream, (int)BH, nseg, S0, z0, agg);
+    }
   } else {
     if (DH == 64) SSD_O1_SCAN(64);
     else SSD_O1_SCAN(32);

@@ -127,11 +127,13 @@ hipError_t launch_output(bool bf16, int64_t DH, int order, const void* q, const 
                          int64_t chunk, const float* state, const float* part, float* y,
                          float* den, hipStream_t stream);
 
-// Order 1 with bf16 inputs: the sequential scan per (head, 16-column slice,
-// segment).  agg_pass: the segment aggregates (nothing when the sequence is
-// one segment); otherwise the outputs, starting from S0, z0 (or zero) carried
-// through the aggregates, and the final states when Sf is given.  sink: 32
-// floats of scratch that take the stores of rows past a ragged end.
+// Order 1 with bf16 inputs: the sequential scan per (head, segment).
+// agg_pass: the segment aggregates and, in place, their prefixes from S0, z0
+// (or zero): the state entering each segment but the first (nothing when the
+// sequence is one segment); otherwise the outputs, each segment starting from
+// its prefix (the first from S0, z0 or zero), and the final states when Sf is
+// given.  sink: 32 floats of scratch that take the stores of rows past a
+// ragged end.
 void o1_scan_segments(int64_t BH, int64_t DH, int64_t N, int* nseg, int* nbs);
 size_t o1_scan_agg_floats(int64_t BH, int64_t DH, int64_t N);
 bool o1_scan_supported(int64_t BH, int64_t DH, int64_t N);  // d_h 32/64, N d_h < 2^31

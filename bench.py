@@ -64,6 +64,7 @@ KERNEL_SOURCES = {
     "k_output": ["fwd_blocks.hip", "launch.h", "common.h"],
     "k_o1_scan": ["fwd_o1_scan.hip", "launch.h", "common.h"],
     "k_o1_segagg": ["fwd_o1_scan.hip", "launch.h", "common.h"],
+    "k_o1_segprefix": ["fwd_o1_scan.hip", "launch.h", "common.h"],
     "k_decode": ["decode.hip", "launch.h", "common.h"],
     "k_prep": ["prep.hip", "launch.h", "common.h"],
 }

@@ -33,8 +33,9 @@ step_mfma_frac (order 2): the whole step against the chunked form's count,
 cpu_baseline: the fp64 oracle (tests' reference implementation, untuned) on a
 bounded sample of the same workload, on this machine's host cores.
 device_ceilings: what the vendor library reaches on the same GPU (torch's fp16
-GEMM at 8192^3, a 1 GiB copy), measured outside the timed steps, as context
-for the roofline fractions.
+GEMM at 8192^3 and at 4096^3, whose 1.374e11 flops equal the 4K state scan's
+algorithmic count, and a 1 GiB copy), measured outside the timed steps, as
+context for the roofline fractions.
 """
 from __future__ import annotations
 
@@ -443,25 +444,29 @@ def cpu_baseline_decode(cfg: I.DecodeConfig, dec, budget_s=10.0):
 def device_ceilings(dev):
     """What the vendor's own library code reaches on this GPU, as context for
     the roofline fractions (not part of the timed step): torch's fp16 GEMM
-    (hipBLASLt) on 8192^3 and a 1 GiB device-to-device copy."""
+    (hipBLASLt) on 8192^3 and on 4096^3 (1.374e11 flops: the order-2 state
+    scan's algorithmic count on the 4K workload, so the two times compare
+    directly), and a 1 GiB device-to-device copy."""
     import torch
     out = {}
-    M = 8192
-    a = torch.randn(M, M, dtype=torch.float16, device=dev)
-    b = torch.randn(M, M, dtype=torch.float16, device=dev)
-    for _ in range(3):
-        c = a @ b
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(10):
-        c = a @ b
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 10
-    out["torch_fp16_gemm_8192_tflops"] = 2 * M ** 3 / (ms * 1e-3) / 1e12
-    out["torch_fp16_gemm_8192_frac_of_2500"] = out["torch_fp16_gemm_8192_tflops"] / 2500.0
-    del a, b, c
+    for M, reps in ((8192, 10), (4096, 40)):
+        a = torch.randn(M, M, dtype=torch.float16, device=dev)
+        b = torch.randn(M, M, dtype=torch.float16, device=dev)
+        for _ in range(3):
+            c = a @ b
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            c = a @ b
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[f"torch_fp16_gemm_{M}_tflops"] = 2 * M ** 3 / (ms * 1e-3) / 1e12
+        out[f"torch_fp16_gemm_{M}_frac_of_2500"] = out[f"torch_fp16_gemm_{M}_tflops"] / 2500.0
+        if M == 4096:
+            out["torch_fp16_gemm_4096_us"] = ms * 1e3
+        del a, b, c
     n = (1 << 30) // 4
     src = torch.ones(n, device=dev)
     dst = torch.empty_like(src)
@@ -574,6 +579,7 @@ def main():
     if not a.no_extra:
         ceilings = device_ceilings(dev)
         log(f"[bench] context: torch fp16 GEMM 8192^3 {ceilings['torch_fp16_gemm_8192_tflops']:.0f} TFLOP/s, "
+            f"4096^3 {ceilings['torch_fp16_gemm_4096_us']:.1f} us, "
             f"1 GiB copy {ceilings['torch_copy_1gib_gbs']:.0f} GB/s")
 
     cpu = None

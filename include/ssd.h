@@ -152,8 +152,12 @@ size_t ssd_forward_workspace_size(int64_t B, int64_t H, int64_t N, int64_t d_h,
  *                        normaliser states before token 0 (Algorithm 6 H_up,
  *                        H_down; the layout of final_state / final_norm,
  *                        e.g. a previous segment's), decayed from the segment
- *                        start by the cumsum of this segment's a_cs.  Must not
- *                        overlap any output.
+ *                        start by the cumsum of this segment's a_cs.  At
+ *                        order 2 they must be symmetric in (a, b) as
+ *                        Algorithm 6's states are (rows (a, b) and (b, a)
+ *                        equal; those of ssd_forward, ssd_decode_step and
+ *                        ssd_state_unpack are): the forward may read either
+ *                        row of such a pair.  Must not overlap any output.
  *   d_h                  32 or 64 (order 1); 64 (order 2)
  *   order                1 or 2 (order 2 requires SSD_BF16)
  *   chunk                64 or 128 (the a_cs segmentation)

@@ -21,11 +21,17 @@
 //
 // Decomposition.  The 1 MiB state never leaves the chip: each wave holds
 // S_c for one value column c as 32 x 32 MFMA accumulator tiles (fp32; rows
-// b, columns a) across the whole sequence: all four tiles with >= 32 heads
-// (NAT = 2 a-tiles, eight columns per workgroup), or the two tiles of one
-// a-half with fewer heads (NAT = 1, two waves per column, four columns per
-// workgroup, so that the grid still covers the chip; the compute-first waves
-// hold a-tile 0, the others a-tile 1).  In this layout the
+// b, columns a) across the whole sequence.  With >= 32 heads (NAT = 2
+// a-tiles, eight columns per workgroup) a wave holds three of the four
+// tiles: S_c is symmetric in (a, b) (k (x) k is), so the tile (a-tile 0,
+// b-tile 1) is the transpose of (a-tile 1, b-tile 0); it is neither updated
+// nor held, and its share of the output, equal to that of its transpose, is
+// taken as twice the latter's (in exact high + low fp16 parts, so that the
+// pair's one rounding is not doubled), which saves a quarter of the update
+// MFMAs and of the decay.  With fewer heads a wave holds the two tiles of one
+// a-half (NAT = 1, two waves per column, four columns per workgroup, so that
+// the grid still covers the chip; the compute-first waves hold a-tile 0, the
+// others a-tile 1).  In this layout the
 // update's per-column factor k_ja comes from the same K^T operand fragment
 // the product itself uses (a and b index the same keys), and the output's
 // per-row factor q_ia from the Q operand fragment, so besides q, k^T and X
@@ -79,6 +85,7 @@ namespace ssd {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 namespace {
 constexpr int DH = 64;
@@ -295,6 +302,7 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
   // (b) x (a = 32 at + n32), value column c0 + cl; lane (n32, h) holds the
   // rows b = 32 bt + 8 q + 4 h + s in register 4 q + s
   f32x16 S[NAT][2];
+  constexpr int A1 = NAT - 1;  // the second a-tile (used with NAT = 2 only)
 #pragma unroll
   for (int p = 0; p < NAT; ++p)
 #pragma unroll
@@ -355,6 +363,30 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
 #pragma unroll
       for (int e = 0; e < 4; ++e) S[at][bt][4 * g + e] *= eT;
     };
+    // two a-tiles per wave: the state is symmetric in (a, b), so the tile of
+    // a-tile 0 and b-tile 1 is the transpose of S[1][0] and is not held; its
+    // share of the output, sum_{a in 0, b in 1} q_a q_b S[b][a], equals that
+    // of S[1][0], so the second a-tile's chain takes twice S[1][0] (over
+    // kk = 0, 1) in high and low fp16 parts (the one fp16 copy then carries
+    // no rounding that the missing tile would have averaged out), then
+    // S[1][1] (kk = 2, 3); the first a-tile's chain takes S[0][0] alone
+    f16x8 SH[2], SL[2];
+    auto cvh = [&](int kk, int p) {
+      const f32x2 x = {S[A1][0][8 * kk + 2 * p], S[A1][0][8 * kk + 2 * p + 1]};
+      f16x2 hh = __builtin_convertvector(x, f16x2);
+      f16x2 ll = __builtin_convertvector(x - __builtin_convertvector(hh, f32x2), f16x2);
+      hh = hh + hh;  // (exact: powers of two, |2 S 2^sig| < 2^14)
+      ll = ll + ll;
+      SH[kk][2 * p] = hh[0];
+      SH[kk][2 * p + 1] = hh[1];
+      SL[kk][2 * p] = ll[0];
+      SL[kk][2 * p + 1] = ll[1];
+    };
+    auto outp = [&](int t, int j) {
+      const f16x8& A = j < 2 ? SH[j] : j < 4 ? SL[j - 2] : SA1[j - 2];
+      const int kk = j < 4 ? (j & 1) : j - 2;
+      T[A1][t] = mfma32(A, Qf[t][kk], j == 0 ? f32x16{} : T[A1][t]);
+    };
     // rows 8 m + 4 h + s of T: a = 32 (AT + at) + 8 m + 4 h + s, whose q value
     // is element 4 (m % 2) + s of the lane's Q fragment 2 (AT + at) + m / 2
     auto fy = [&](int at, int t, int m) {
@@ -377,67 +409,59 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
 
     if constexpr (NAT == 2) {
       // -- generated schedule, 2 a-tiles per wave --
-      rdQ(0, 0); rdQ(0, 1); rdQ(0, 2); rdQ(0, 3); rdQ(1, 0); cvt(SA1, 1, 0); cvt(SA1, 1, 1); SB();
-      out(0, 0, 0); cvt(SA1, 1, 2); rdQ(1, 1); SB();
-      out(0, 0, 1); cvt(SA1, 1, 3); mul(0, 0, 0); rdQ(1, 2); SB();
-      out(0, 0, 2); mul(0, 0, 1); rdQ(1, 3); SB();
-      out(0, 0, 3); mul(0, 0, 2); mul(0, 0, 3); SB();
-      out(1, 0, 0); mul(0, 1, 0); SB();
-      out(1, 0, 1); mul(0, 1, 1); mul(0, 1, 2); SB();
-      out(1, 0, 2); fy(0, 0, 0); SB();
-      out(1, 0, 3); fy(0, 0, 1); fy(0, 0, 2); rdQ(2, 0); SB();
-      out(0, 1, 0); fy(0, 0, 3); rdQ(2, 1); SB();
-      out(0, 1, 1); mul(0, 1, 3); mul(1, 0, 0); rdQ(2, 2); SB();
-      out(0, 1, 2); fy(1, 0, 0); rdQ(2, 3); SB();
-      out(0, 1, 3); fy(1, 0, 1); fy(1, 0, 2); SB();
-      out(1, 1, 0); fy(1, 0, 3); SB();
-      out(1, 1, 1); mul(1, 0, 1); mul(1, 0, 2); SB();
-      out(1, 1, 2); fy(0, 1, 0); SB();
-      out(1, 1, 3); fy(0, 1, 1); fy(0, 1, 2); rdQ(3, 0); SB();
-      out(0, 2, 0); fy(0, 1, 3); rdQ(3, 1); SB();
-      out(0, 2, 1); mul(1, 0, 3); mul(1, 1, 0); rdQ(3, 2); SB();
-      out(0, 2, 2); fy(1, 1, 0); rdQ(3, 3); SB();
-      out(0, 2, 3); fy(1, 1, 1); fy(1, 1, 2); SB();
-      out(1, 2, 0); fy(1, 1, 3); rdK(0, 0, 0); SB();
-      out(1, 2, 1); mul(1, 1, 1); mul(1, 1, 2); rdK(1, 0, 0); SB();
-      out(1, 2, 2); fy(0, 2, 0); rdX(0, 0); SB();
-      out(1, 2, 3); fy(0, 2, 1); fy(0, 2, 2); rdK(0, 0, 1); SB();
-      out(0, 3, 0); fy(0, 2, 3); rdK(1, 0, 1); SB();
-      out(0, 3, 1); bu(0, 0, 0); bu(1, 0, 0); rdX(0, 1); SB();
-      out(0, 3, 2); fy(1, 2, 0); rdK(0, 0, 2); SB();
-      out(0, 3, 3); fy(1, 2, 1); fy(1, 2, 2); rdK(1, 0, 2); SB();
-      out(1, 3, 0); bu(0, 0, 1); rdX(0, 2); SB();
-      out(1, 3, 1); fy(1, 2, 3); bu(1, 0, 1); rdK(0, 0, 3); SB();
-      out(1, 3, 2); fy(0, 3, 0); rdK(1, 0, 3); SB();
-      out(1, 3, 3); bu(0, 0, 2); fy(0, 3, 1); rdX(0, 3); SB();
-      upd(0, 0, 0, 0); fy(0, 3, 2); SB();
-      upd(0, 0, 0, 1); fy(0, 3, 3); SB();
-      upd(0, 0, 0, 2); bu(0, 0, 3); SB();
-      upd(0, 0, 0, 3); fy(1, 3, 0); SB();
-      upd(0, 1, 0, 0); fy(1, 3, 1); rdK(0, 1, 0); SB();
-      upd(0, 1, 0, 1); fy(1, 3, 2); rdK(1, 1, 0); SB();
-      upd(0, 1, 0, 2); fy(1, 3, 3); rdX(1, 0); SB();
-      upd(0, 1, 0, 3); bu(1, 0, 2); rdK(0, 1, 1); wr(); SB();
-      upd(1, 0, 0, 0); bu(1, 0, 3); rdK(1, 1, 1); SB();
-      upd(1, 0, 0, 1); mul(1, 1, 3); rdX(1, 1); SB();
-      upd(1, 0, 0, 2); bu(0, 1, 0); rdK(0, 1, 2); SB();
-      upd(1, 0, 0, 3); bu(1, 1, 0); rdK(1, 1, 2); SB();
-      upd(1, 1, 0, 0); bu(0, 1, 1); rdX(1, 2); SB();
-      upd(1, 1, 0, 1); bu(1, 1, 1); rdK(0, 1, 3); SB();
-      upd(1, 1, 0, 2); rdK(1, 1, 3); SB();
-      upd(1, 1, 0, 3); bu(0, 1, 2); rdX(1, 3); SB();
-      upd(0, 0, 1, 0); bu(1, 1, 2); SB();
-      upd(0, 0, 1, 1); SB();
+      rdQ(0, 0); rdQ(0, 1); rdQ(0, 2); rdQ(0, 3); rdQ(1, 0); rdQ(1, 1); cvh(0, 0); cvh(0, 1); SB();
+      out(0, 0, 0); cvh(0, 2); SB();
+      out(0, 0, 1); cvh(0, 3); cvh(1, 0); SB();
+      out(0, 1, 0); cvh(1, 1); SB();
+      out(0, 1, 1); cvh(1, 2); cvh(1, 3); SB();
+      outp(0, 0); cvt(SA1, 1, 2); SB();
+      outp(0, 1); cvt(SA1, 1, 3); fy(0, 0, 0); rdQ(1, 2); SB();
+      outp(0, 2); fy(0, 0, 1); rdQ(1, 3); SB();
+      outp(0, 3); fy(0, 0, 2); fy(0, 0, 3); rdQ(2, 0); SB();
+      outp(0, 4); fy(0, 1, 0); rdQ(2, 1); SB();
+      outp(0, 5); fy(0, 1, 1); fy(0, 1, 2); rdQ(3, 0); SB();
+      outp(1, 0); fy(0, 1, 3); rdQ(3, 1); SB();
+      outp(1, 1); mul(0, 0, 0); mul(0, 0, 1); SB();
+      outp(1, 2); fy(1, 0, 0); SB();
+      outp(1, 3); fy(1, 0, 1); fy(1, 0, 2); SB();
+      outp(1, 4); fy(1, 0, 3); SB();
+      outp(1, 5); mul(0, 0, 2); mul(0, 0, 3); rdQ(2, 2); SB();
+      out(0, 2, 0); mul(1, 0, 0); rdQ(2, 3); SB();
+      out(0, 2, 1); mul(1, 0, 1); mul(1, 0, 2); SB();
+      out(0, 3, 0); fy(1, 1, 0); SB();
+      out(0, 3, 1); fy(1, 1, 1); fy(1, 1, 2); SB();
+      outp(2, 0); fy(1, 1, 3); rdK(0, 0, 0); SB();
+      outp(2, 1); fy(0, 2, 0); fy(0, 2, 1); rdQ(3, 2); SB();
+      outp(2, 2); fy(0, 2, 2); rdQ(3, 3); SB();
+      outp(2, 3); fy(0, 2, 3); fy(0, 3, 0); rdK(1, 0, 0); SB();
+      outp(2, 4); fy(0, 3, 1); rdX(0, 0); SB();
+      outp(2, 5); fy(0, 3, 2); fy(0, 3, 3); rdK(0, 0, 1); SB();
+      outp(3, 0); mul(1, 0, 3); rdK(1, 0, 1); SB();
+      outp(3, 1); bu(0, 0, 0); bu(1, 0, 0); rdX(0, 1); SB();
+      outp(3, 2); fy(1, 2, 0); rdK(0, 0, 2); SB();
+      outp(3, 3); fy(1, 2, 1); rdK(1, 0, 2); SB();
+      outp(3, 4); bu(0, 0, 1); rdX(0, 2); rdK(0, 0, 3); SB();
+      outp(3, 5); fy(1, 2, 2); rdK(1, 0, 3); rdX(0, 3); SB();
+      upd(0, 0, 0, 0); fy(1, 2, 3); rdK(0, 1, 0); SB();
+      upd(0, 0, 0, 1); bu(0, 0, 2); rdK(1, 1, 0); SB();
+      upd(0, 0, 0, 2); bu(0, 0, 3); rdX(1, 0); SB();
+      upd(0, 0, 0, 3); bu(1, 0, 1); rdK(0, 1, 1); SB();
+      upd(1, 0, 0, 0); bu(1, 0, 2); rdK(1, 1, 1); SB();
+      upd(1, 0, 0, 1); bu(1, 0, 3); rdX(1, 1); SB();
+      upd(1, 0, 0, 2); mul(1, 1, 0); mul(1, 1, 1); rdK(0, 1, 2); SB();
+      upd(1, 0, 0, 3); mul(1, 1, 2); mul(1, 1, 3); rdK(1, 1, 2); SB();
+      upd(1, 1, 0, 0); fy(1, 3, 0); fy(1, 3, 1); rdX(1, 2); SB();
+      upd(1, 1, 0, 1); fy(1, 3, 2); fy(1, 3, 3); rdK(0, 1, 3); SB();
+      upd(1, 1, 0, 2); bu(0, 1, 0); rdK(1, 1, 3); wr(); SB();
+      upd(1, 1, 0, 3); bu(0, 1, 1); rdX(1, 3); SB();
+      upd(0, 0, 1, 0); bu(0, 1, 2); SB();
+      upd(0, 0, 1, 1); bu(1, 1, 0); SB();
       upd(0, 0, 1, 2); bu(0, 1, 3); SB();
-      upd(0, 0, 1, 3); bu(1, 1, 3); SB();
-      upd(0, 1, 1, 0); SB();
-      upd(0, 1, 1, 1); SB();
-      upd(0, 1, 1, 2); cvt(SA0, 0, 0); SB();
-      upd(0, 1, 1, 3); cvt(SA0, 0, 1); SB();
-      upd(1, 0, 1, 0); SB();
-      upd(1, 0, 1, 1); SB();
-      upd(1, 0, 1, 2); cvt(SA0, 0, 2); SB();
-      upd(1, 0, 1, 3); cvt(SA0, 0, 3); SB();
+      upd(0, 0, 1, 3); bu(1, 1, 1); SB();
+      upd(1, 0, 1, 0); bu(1, 1, 2); SB();
+      upd(1, 0, 1, 1); bu(1, 1, 3); SB();
+      upd(1, 0, 1, 2); cvt(SA0, 0, 0); SB();
+      upd(1, 0, 1, 3); cvt(SA0, 0, 1); SB();
       upd(1, 1, 1, 0); SB();
       upd(1, 1, 1, 1); SB();
       upd(1, 1, 1, 2); SB();
@@ -535,18 +559,22 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
         const int a = 32 * (NAT == 2 ? at : (wave >> 2)) + n32;
         if (a / AP == pass) {
 #pragma unroll
-          for (int bt = 0; bt < 2; ++bt)
+          for (int bt = 0; bt < 2; ++bt) {
+            // (the state is symmetric in (a, b): with two a-tiles per wave the
+            // rows (a, b), a >= 32 > b, stand for their mirrors (b, a) too)
+            if (NAT == 2 && at == 0 && bt == 1) continue;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const int b = bt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
               S[at][bt][r] = buf[(a - AP * pass) * AS + b * CWG + cl] * sc;
             }
+          }
         }
       }
       __syncthreads();
     }
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    for (int kk = 0; kk < (NAT == 2 ? 2 : 4); ++kk)
 #pragma unroll
       for (int e = 0; e < 8; ++e) SA0[kk][e] = (_Float16)S[0][kk >> 1][8 * (kk & 1) + e];
   };
@@ -612,12 +640,16 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
     for (int at = 0; at < NAT; ++at) {
       const int a = 32 * (NAT == 2 ? at : (wave >> 2)) + n32;
 #pragma unroll
-      for (int bt = 0; bt < 2; ++bt)
+      for (int bt = 0; bt < 2; ++bt) {
+        if (NAT == 2 && at == 0 && bt == 1) continue;  // written as the mirror of S[1][0]
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int b = bt * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          final_state[((bh * DH + a) * DH + b) * DH + c] = S[at][bt][r] * f;
+          const float x = S[at][bt][r] * f;
+          final_state[((bh * DH + a) * DH + b) * DH + c] = x;
+          if (NAT == 2 && at == 1 && bt == 0) final_state[((bh * DH + b) * DH + a) * DH + c] = x;
         }
+      }
     }
   }
 }

@@ -22,6 +22,8 @@ VALU units:
                    always before the outputs are written
   bu(at, hb, kk)   update operand, three slots after its reads
 LDS reads: rdQ(t, kk), rdK(bt, hb, kk), rdX(hb, kk), a few slots before use.
+One a-tile per wave (NAT = 1) uses these chains; two a-tiles per wave use
+schedule_sym (three state tiles, the state being symmetric in (a, b)).
 """
 import heapq
 import os
@@ -135,8 +137,86 @@ def schedule(nat, order, lq=3, lk=4, fd=7, front=True):
     return ["      " + re.sub(r"\s+", " ", l).strip() for l in lines]
 
 
+def schedule_sym(lq=3, lk=4, fd=7):
+    """Two a-tiles per wave with the state's symmetry: the tiles (b-tile 0,
+    a-tile 0), (0, 1) and (1, 1) are held; (1, 0) is the transpose of (0, 1).
+    Output chains: out(0, t, kk) over kk = 0, 1 (tile (0, 0)); outp(t, j),
+    j = 0..5, the hi and lo parts of twice tile (0, 1) over kk = 0, 1, then
+    tile (1, 1) over kk = 2, 3.  Updates: upd(at, bt, hb, kk) for the three
+    tiles.  VALU units: cvh(kk, p), the hi / lo parts of twice tile (0, 1)
+    (two of the eight values of k-step kk per unit); cvt(SA1, 1, kk), kk =
+    2, 3; mul for the three tiles; fy and bu as above; cvt(SA0, 0, kk), kk =
+    0, 1, after the last update of tile (0, 0)."""
+    chains = []
+    for t2 in (0, 2):
+        chains += [("C0", t2), ("C0", t2 + 1), ("C1", t2), ("C1", t2 + 1)]
+    for hb in range(2):
+        chains += [("U", 0, 0, hb), ("U", 1, 0, hb), ("U", 1, 1, hb)]
+    length = {"C0": 2, "C1": 6, "U": 4}
+    start, s0 = {}, 0
+    for c in chains:
+        start[c] = s0
+        s0 += length[c[0]]
+    ns = s0
+    mf = []
+    for c in chains:
+        if c[0] == "C0":
+            mf += [f"out(0, {c[1]}, {kk});" for kk in range(2)]
+        elif c[0] == "C1":
+            mf += [f"outp({c[1]}, {j});" for j in range(6)]
+        else:
+            mf += [f"upd({c[1]}, {c[2]}, {c[3]}, {kk});" for kk in range(4)]
+    # first use of Q fragment (t, kk): kk 0, 1 by out(0, t, kk), kk 2, 3 by outp(t, 4 + kk - 2)
+    first_u = {hb: start[("U", 0, 0, hb)] for hb in range(2)}
+    reads = []
+    for t in range(1, 4):
+        for kk in range(4):
+            need = start[("C0", t)] + kk if kk < 2 else start[("C1", t)] + 4 + kk - 2
+            reads.append((f"rdQ({t}, {kk});", need - lq - 6, need - lq, 0))
+    for hb in range(2):
+        for kk in range(4):
+            d = first_u[hb] - lk + kk
+            reads += [(f"rdK({bt}, {hb}, {kk});", d - 8, d, 1) for bt in range(2)]
+            reads.append((f"rdX({hb}, {kk});", d - 8, d, 1))
+    rplaced, rtail = edf(reads, ns, {-1: 4}, -1, 2)
+    assert not rtail
+    rslot = {n: s for s, v in rplaced.items() for n in v}
+    c1 = start[("C1", 0)]
+    units = []
+    units += [(f"cvh({kk}, {p});", -1, c1 + kk - 1, 2) for kk in range(2) for p in range(4)]
+    units += [(f"cvt(SA1, 1, {kk});", -1, c1 + 4 + kk - 2 - 1, 2) for kk in (2, 3)]
+    for t in range(4):
+        r = start[("C0", t)] + length["C0"] + 2
+        units += [(f"fy(0, {t}, {m});", r, min(r + fd, ns - 2), 0) for m in range(4)]
+        r = start[("C1", t)] + length["C1"] + 2
+        units += [(f"fy(1, {t}, {m});", r, min(r + fd, ns - 2), 0) for m in range(4)]
+    for (at, bt, r) in ((0, 0, 0), (1, 0, c1), (1, 1, c1 + 6)):
+        units += [(f"mul({at}, {bt}, {g});", r, start[("U", at, bt, 0)] - 1, 1) for g in range(4)]
+    for hb in range(2):
+        for at in range(2):
+            for kk in range(4):
+                r = max(rslot[f"rdK({at}, {hb}, {kk});"], rslot[f"rdX({hb}, {kk});"]) + 3
+                units.append((f"bu({at}, {hb}, {kk});", r, start[("U", at, 0, hb)] + kk - 1, 3))
+    for kk in range(2):
+        units.append((f"cvt(SA0, 0, {kk});", start[("U", 0, 0, 1)] + 6, 10 ** 6, 4))
+    cap = {-1: 2}
+    for x in range(0, ns // 2, 2):
+        cap[x + 1] = 2
+    placed, tail = edf(units, ns, cap, -1, 3)
+    assert all(u.startswith("cvt(SA0") for u in tail), tail
+    lastfy = max(s for s, v in placed.items() if any(u.startswith("fy(") for u in v))
+    assert lastfy < ns - 1
+    lines = ["rdQ(0, 0); rdQ(0, 1); rdQ(0, 2); rdQ(0, 3); " + " ".join(rplaced.get(-1, []) + placed[-1]) + " SB();"]
+    for s in range(ns):
+        w = ["wr();"] if s == lastfy + 1 else []
+        lines.append(" ".join([mf[s]] + placed[s] + rplaced.get(s, []) + w) + " SB();")
+    if tail:
+        lines.append(" ".join(tail) + " SB();")
+    return ["      " + re.sub(r"\s+", " ", l).strip() for l in lines]
+
+
 def main():
-    blocks = {2: schedule(2, "split", front=True), 1: schedule(1, "inter", front=False)}
+    blocks = {2: schedule_sym(), 1: schedule(1, "inter", front=False)}
     if "--print" in sys.argv:
         for nat, lines in blocks.items():
             print(f"// {nat} a-tile(s)\n" + "\n".join(lines))

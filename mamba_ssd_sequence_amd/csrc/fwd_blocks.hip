@@ -454,7 +454,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF ? 5 : 1,
   // operand of (Z' Q^T) with Z' the upper tiles of Z, off-diagonal ones
   // doubled: q^T Z' q = q^T Z q); lanes whose tile lies below the diagonal
   // read the diagonal tile and use 0
-  const float* st = state + (bh * nblk + blk) * (int64_t)(DH * DH + DH);
+  // (order 2: the normaliser state entering the block's two-block step, which
+  // the state scan leaves in the slot of the step's first block; the second
+  // block adds the first block's share from its direct term below)
+  const int64_t zslot = (ORDER == 2 && BF) ? (blk & ~(int64_t)1) : blk;
+  const float* st = state + (bh * nblk + zslot) * (int64_t)(DH * DH + DH);
   constexpr int NS4 = DH * DH / 4 / 256;
   static_assert(NS4 * 256 * 4 == DH * DH && (ORDER == 1 || NS4 == 4), "state mapping");
   f32x4 gs[NS4];
@@ -488,6 +492,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF ? 5 : 1,
   // rows are loaded now and staged after the block's own products.
   constexpr bool PAIRS = ORDER == 2 && BF;
   const bool partner = PAIRS && (blk & 1);
+  float den_p = 0.f;  // the first block's share of the normaliser (second blocks)
   uint4 pka = make_uint4(0, 0, 0, 0), pkb = pka, pva = pka, pvb = pka;  // (registers, not an array)
   float pcs = 0.f, pdt = 0.f, pT = 0.f;
   if (PAIRS && partner) {
@@ -760,6 +765,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF ? 5 : 1,
       for (int r = 0; r < 4; ++r) {
         const int j = jt * 16 + 4 * g + r;
         Wp[jt][r] = acc[r] * acc[r] * exp2_fast(cs_i + pT - csl[j]);
+        den_p += Wp[jt][r];
       }
     }
     if constexpr (BF) {
@@ -800,6 +806,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(BF ? 5 : 1,
   } else {
     __syncthreads();  // every wave's part of q^T Z q is in dred
     den_x = (dred[il] + dred[BLK + il]) + (dred[2 * BLK + il] + dred[3 * BLK + il]);
+    // the second block of a step: Z entered the step one block earlier
+    // (decay e^{T'} more), and the first block's keys add their terms
+    if (partner) den_x *= exp2_fast(pT);
+    den_l += sum_over_groups(den_p);
 #pragma unroll
     for (int ct = 0; ct < NT; ++ct) num[ct] += gp[ct];
   }

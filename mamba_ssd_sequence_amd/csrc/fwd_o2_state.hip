@@ -246,8 +246,10 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
 
   // normaliser state Z = sum_j w_j k_j k_j^T (2Mamba2Furious, Algorithm 6:
   // the denominator q_i^T Z q_i), scanned over the blocks in place: the slot
-  // of block b holds Z_blk(b) (from the block-prep kernel) and receives Z
-  // entering b, Z_in(b + 1) = e^{T_b} Z_in(b) + Z_blk(b).  Only the upper
+  // of block b holds Z_blk(b) (from the block-prep kernel), Z_in(b + 1) =
+  // e^{T_b} Z_in(b) + Z_blk(b), and the slot of the first block of each
+  // two-block step receives Z entering the step (the output kernel adds the
+  // first block's share to the second block's rows directly).  Only the upper
   // 16 x 16 tiles of the symmetric Z are stored (Z_FLOATS floats).  Each
   // workgroup scans its 1 / NCS share of them, ZE per thread on the first ZTH
   // compute-first threads, in the slack of those threads' bookkeeping: the
@@ -285,14 +287,9 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
       s2.x = zT1 * s1.x + zd1.x;
       s2.y = zT1 * s1.y + zd1.y;
     }
-    if (zact) {
-      if constexpr (ZE == 2) {
-        *reinterpret_cast<float2*>(zp + b0 * ZS) = s;
-        if (b1 < nblk) *reinterpret_cast<float2*>(zp + b1 * ZS) = s1;
-      } else {
-        zp[b0 * ZS] = s.x;
-        if (b1 < nblk) zp[b1 * ZS] = s1.x;
-      }
+    if (zact) {  // (Z entering the step, in its first block's slot)
+      if constexpr (ZE == 2) *reinterpret_cast<float2*>(zp + b0 * ZS) = s;
+      else zp[b0 * ZS] = s.x;
     }
     zrun[tid][0] = s2.x;
     if constexpr (ZE == 2) zrun[tid][1] = s2.y;

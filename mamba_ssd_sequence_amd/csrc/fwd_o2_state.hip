@@ -369,11 +369,13 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
     // S[1][1] (kk = 2, 3); the first a-tile's chain takes S[0][0] alone
     f16x8 SH[2], SL[2];
     auto cvh = [&](int kk, int p) {
-      const f32x2 x = {S[A1][0][8 * kk + 2 * p], S[A1][0][8 * kk + 2 * p + 1]};
-      f16x2 hh = __builtin_convertvector(x, f16x2);
-      f16x2 ll = __builtin_convertvector(x - __builtin_convertvector(hh, f32x2), f16x2);
-      hh = hh + hh;  // (exact: powers of two, |2 S 2^sig| < 2^14)
-      ll = ll + ll;
+      const float x0 = S[A1][0][8 * kk + 2 * p], x1 = S[A1][0][8 * kk + 2 * p + 1];
+      f16x2 hh = __builtin_convertvector((f32x2){x0, x1}, f16x2);
+      hh = hh + hh;  // = fp16(2 x), exact: |2 S 2^sig| < 2^14
+      // the low part of 2 x: 2 x - hh is exact in fp32, formed by one mixed
+      // fp32 / fp16 fma per value (no conversion of hh back to fp32)
+      const f32x2 r = {fmaf(x0, 2.f, -(float)hh[0]), fmaf(x1, 2.f, -(float)hh[1])};
+      const f16x2 ll = __builtin_convertvector(r, f16x2);
       SH[kk][2 * p] = hh[0];
       SH[kk][2 * p + 1] = hh[1];
       SL[kk][2 * p] = ll[0];
@@ -584,6 +586,11 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
   // staging consumes them.  The loads for step m+2 are issued right after
   // the registers are free, a whole step ahead of their use.
   if (wave < NW / 2) {
+    // the prologue's loads are complete before the loop: a load still in
+    // flight at the loop's entry would make the compiler wait for every
+    // outstanding load at the top of each step (also for the loads of step
+    // st + 2, issued a step ahead)
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
     for (int st = 0; st < nstep; ++st) {
       const Stp nxt = nx;  // scales of step st + 1 (prefetched)
       if constexpr (INIT)

@@ -175,14 +175,17 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
   const int xi2 = tid % (2 * NXW), xhb = xi2 / NXW, xidx = xi2 % NXW, xr = xidx >> 5, xw = xidx & 31;
   auto prefetch = [&](int st) {
     const int b0 = 2 * st, b1 = 2 * st + 1 < nblk ? 2 * st + 1 : nblk - 1;
+    // addresses as one uniform base and unsigned 32-bit per-thread offsets
+    // (the second block's record is d1 bytes after the first's)
     const uint8_t* R0 = rec_h + b0 * (int64_t)REC_BYTES;
     const uint8_t* R1 = rec_h + b1 * (int64_t)REC_BYTES;
+    const uint32_t d1 = (uint32_t)(b1 - b0) * REC_BYTES;
     {
-      const int r = tid >> 3, sg = tid & 7;
-      pq0 = *reinterpret_cast<const uint4*>(R0 + REC_QH + (r * DH + sg * 8) * 2);
-      pk0 = *reinterpret_cast<const uint4*>(R0 + REC_KT + (r * DH + sg * 8) * 2);
-      pq1 = *reinterpret_cast<const uint4*>(R1 + REC_QH + (r * DH + sg * 8) * 2);
-      pk1 = *reinterpret_cast<const uint4*>(R1 + REC_KT + (r * DH + sg * 8) * 2);
+      const uint32_t o = ((tid >> 3) * DH + (tid & 7) * 8) * 2;
+      pq0 = *reinterpret_cast<const uint4*>(R0 + (REC_QH + o));
+      pk0 = *reinterpret_cast<const uint4*>(R0 + (REC_KT + o));
+      pq1 = *reinterpret_cast<const uint4*>(R0 + (d1 + REC_QH + o));
+      pk1 = *reinterpret_cast<const uint4*>(R0 + (d1 + REC_KT + o));
     }
     const int* sc0 = reinterpret_cast<const int*>(R0 + REC_SC);  // uniform addresses
     const int* sc1 = reinterpret_cast<const int*>(R1 + REC_SC);
@@ -195,8 +198,8 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
     nx.xf1 = 2 * st + 1 < nblk ? (uint32_t)sc1[SC_XF] : 0u;  // an empty second block
     nx.epre0 = __int_as_float(sc0[SC_EPRE]);
     nx.epre1 = __int_as_float(sc1[SC_EPRE]);
-    px = *reinterpret_cast<const uint32_t*>((xhb ? R1 : R0) + REC_XT + ((c0 + xr) * DH + 2 * xw) * 2);
-    pe = *reinterpret_cast<const uint32_t*>((((tid >> 6) & 1) ? R1 : R0) + REC_ECS + 4 * (tid & (BLK - 1)));
+    px = *reinterpret_cast<const uint32_t*>(R0 + ((xhb ? d1 : 0u) + REC_XT + (uint32_t)((c0 + xr) * DH + 2 * xw) * 2));
+    pe = *reinterpret_cast<const uint32_t*>(R0 + ((((tid >> 6) & 1) ? d1 : 0u) + REC_ECS + 4u * (tid & (BLK - 1))));
   };
 
   // copy the prefetched step st into its LDS slot, X scaled to the state's
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
       // no intermediate factor leaves the fp32 range
       const float f = st_ecs[st % 3][hb][i] * (hb ? p.epre1 : p.epre0);
       const int sh = -p.sig_in - 2 * (hb ? p.tau1 : p.tau0);
-      float* dst = &part[(bh * Np + (int64_t)(2 * st + hb) * BLK + i) * DH + c0];
+      float* dst = part + (bh * Np + (int64_t)(2 * st) * BLK) * DH + c0 + (uint32_t)((hb * BLK + i) * DH);
       if constexpr (NAT == 2) {
         float2 o;
         o.x = ldexpf(yr[2 * q4] * f, sh);
@@ -261,18 +264,19 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
   constexpr int64_t ZS = DH * DH + DH;  // floats per block slot
   const bool zact = tid < ZTH;
   const int zi = (zact ? tid : ZTH - 1) * ZE;  // this thread's first entry in the share
-  float* zp = zst + bh * nblk * ZS + pc * ZPW + zi;
+  float* const zb = zst + bh * nblk * ZS + pc * ZPW;  // (uniform; zi is added per thread)
+  auto zp = [&](int b) { return zb + b * ZS + (uint32_t)zi; };
   float2 zd0{}, zd1{};
   float zT0 = 0.f, zT1 = 0.f;
   auto zload = [&](int st) {
     const int b0 = 2 * st, b1 = 2 * st + 1;
     zT0 = __int_as_float(reinterpret_cast<const int*>(rec_h + b0 * (int64_t)REC_BYTES + REC_SC)[SC_ET]);
-    if constexpr (ZE == 2) zd0 = *reinterpret_cast<const float2*>(zp + b0 * ZS);
-    else zd0.x = zp[b0 * ZS];
+    if constexpr (ZE == 2) zd0 = *reinterpret_cast<const float2*>(zp(b0));
+    else zd0.x = *zp(b0);
     if (b1 < nblk) {
       zT1 = __int_as_float(reinterpret_cast<const int*>(rec_h + b1 * (int64_t)REC_BYTES + REC_SC)[SC_ET]);
-      if constexpr (ZE == 2) zd1 = *reinterpret_cast<const float2*>(zp + b1 * ZS);
-      else zd1.x = zp[b1 * ZS];
+      if constexpr (ZE == 2) zd1 = *reinterpret_cast<const float2*>(zp(b1));
+      else zd1.x = *zp(b1);
     }
   };
   auto zscan = [&](int st) {
@@ -288,8 +292,8 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
       s2.y = zT1 * s1.y + zd1.y;
     }
     if (zact) {  // (Z entering the step, in its first block's slot)
-      if constexpr (ZE == 2) *reinterpret_cast<float2*>(zp + b0 * ZS) = s;
-      else zp[b0 * ZS] = s.x;
+      if constexpr (ZE == 2) *reinterpret_cast<float2*>(zp(b0)) = s;
+      else *zp(b0) = s.x;
     }
     zrun[tid][0] = s2.x;
     if constexpr (ZE == 2) zrun[tid][1] = s2.y;
@@ -401,7 +405,11 @@ __global__ __launch_bounds__(512) void k_o2_state(const uint8_t* __restrict__ re
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         float y = (Y[t][0] + Y[t][1]) + (Y[t][2] + Y[t][3]);
-        y += __shfl_xor(y, 32, WAVE);
+        // y + (y of lane ^ 32) without an LDS round trip: swapping the
+        // halves of two copies gives the lower and the upper half's value
+        // on every lane
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(y), __float_as_uint(y), false, false);
+        y = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         yo[sl][t >> 1][((t & 1) * 32 + n32) * RP + yi] = y;
       }
     };

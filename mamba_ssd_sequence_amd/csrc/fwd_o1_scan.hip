@@ -536,10 +536,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(128 / DH)))
 
     const float eT = exp2_fast(T);
     Tw += T;
+    if (b != bw0) {  // (the accumulators are still zero at the wave's first block)
 #pragma unroll
-    for (int bt = 0; bt < NT; ++bt) {
+      for (int bt = 0; bt < NT; ++bt) {
 #pragma unroll
-      for (int ct = 0; ct < NT; ++ct) acc[bt][ct] *= eT;
+        for (int ct = 0; ct < NT; ++ct) acc[bt][ct] *= eT;
+      }
     }
     float zp[NT];
 #pragma unroll

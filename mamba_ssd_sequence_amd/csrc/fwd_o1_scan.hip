@@ -15,7 +15,8 @@
 // segment but the last, a prefix pass (k_o1_segprefix) turns them in place
 // into the state entering each following segment (the initial state carried
 // through S <- 2^{T_s'} S + A_s' for s' < s), and the scan of segment s
-// starts from that one slot.
+// starts from that one slot.  With at most O1_FOLD_SEGS segments there is no
+// prefix pass: the scan sums the earlier segments' contributions itself.
 //
 // Per block, wave w owns query rows 16 w .. 16 w + 15 and (for the update)
 // state rows b = 16 w .. 16 w + 15 (d_h 32: waves 0, 1), every value column.
@@ -41,6 +42,10 @@
 #include "launch.h"
 
 namespace ssd {
+
+// up to this many segments per head the scan sums the earlier segments'
+// contributions itself (no prefix pass)
+constexpr int O1_FOLD_SEGS = 8;
 
 namespace {
 
@@ -223,7 +228,38 @@ __global__ __launch_bounds__(256) void k_o1_scan(const uint16_t* __restrict__ q,
   // the state entering the segment, read while the first block's loads are
   // in flight: the initial state for the first segment, else the prefix
   // that k_o1_segprefix left in the previous segment's aggregate slot
-  if (sw) {
+  if (sw && nseg <= O1_FOLD_SEGS && seg > 0) {
+    // few segments: k_o1_segagg left each earlier segment's own contribution
+    // A_s (from a zero state) and log2 decay total T_s, and the entering
+    // state is summed here, latest segment first,
+    //   E = sum_{l < seg} 2^{d_l} A_{seg-1-l} + 2^{d_seg} S0,
+    //   d_l = sum_{l' < l} T_{seg-1-l'};
+    // every slot's loads are issued at once (indices past the first segment
+    // clamped to it, with a zero weight)
+    const float* base = agg + (int64_t)bh * (nseg - 1) * AGGF;
+    float d = 0.f;
+#pragma unroll
+    for (int l = 0; l < O1_FOLD_SEGS - 1; ++l) {
+      const int sl = seg - 1 - l >= 0 ? seg - 1 - l : 0;
+      const float* sp = base + (int64_t)sl * AGGF;
+      const float sc = l < seg ? exp2_fast(d) : 0.f;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[ct][r] += sc * sp[(sb + r) * DH + 16 * ct + n];
+      zs += sc * sp[DH * DH + bs];
+      if (l < seg) d += sp[DH * DH + DH];
+    }
+    if (S0) {
+      const float sc = exp2_fast(d);
+      const float* sp = S0 + (int64_t)bh * DH * DH;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[ct][r] += sc * sp[(sb + r) * DH + 16 * ct + n];
+      zs += sc * z0[(int64_t)bh * DH + bs];
+    }
+  } else if (sw) {
     const float* sp = nullptr;
     const float* zp0 = nullptr;
     if (seg > 0) {
@@ -694,11 +730,13 @@ hipError_t launch_o1_scan(bool agg_pass, int64_t DH, const void* q, const void* 
     if (DH == 64) {
       hipLaunchKernelGGL((k_o1_segagg<64>), grid, blk, 0, stream, kk, vv, dt, a_cs, (int)BH, (int)N, cb,
                          nseg, nbs, agg);
-      hipLaunchKernelGGL((k_o1_segprefix<64>), gp, blk, 0, stream, (int)BH, nseg, S0, z0, agg);
+      if (nseg > O1_FOLD_SEGS)
+        hipLaunchKernelGGL((k_o1_segprefix<64>), gp, blk, 0, stream, (int)BH, nseg, S0, z0, agg);
     } else {
       hipLaunchKernelGGL((k_o1_segagg<32>), grid, blk, 0, stream, kk, vv, dt, a_cs, (int)BH, (int)N, cb,
                          nseg, nbs, agg);
-      hipLaunchKernelGGL((k_o1_segprefix<32>), gp, blk, 0, stream, (int)BH, nseg, S0, z0, agg);
+      if (nseg > O1_FOLD_SEGS)
+        hipLaunchKernelGGL((k_o1_segprefix<32>), gp, blk, 0, stream, (int)BH, nseg, S0, z0, agg);
     }
   } else {
     if (DH == 64) SSD_O1_SCAN(64);

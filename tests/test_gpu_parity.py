@@ -192,10 +192,13 @@ def _forward_arrays(cfg, q, k, v, dtp, bias, alog, order, chunk, S0=None, z0=Non
 # (config, B, H, N, chunk, split point): at order 2, 2 heads use the
 # two-wave-per-column state layout and 32 heads the one-wave layout; the
 # initial state enters in the first step of the suffix (a single step of
-# 70 tokens, or 14 steps)
+# 70 tokens, or 14 steps); order 1 with bf16 inputs: suffixes of 8 segments
+# (the scan sums the earlier segments and the initial state itself) and of
+# 10 segments (the prefix pass carries the initial state)
 @pytest.mark.parametrize("name,B,H,N,chunk,n1", [
     ("o1_f32_small", 1, 2, 200, 64, 100), ("o1_bf16_2k", 1, 2, 300, 128, 191),
-    ("o1_bf16_2k", 1, 2, 3000, 128, 1000), ("o1_bf16_d32", 1, 1, 2300, 64, 700),
+    ("o1_bf16_2k", 1, 2, 3000, 128, 1000), ("o1_bf16_2k", 1, 2, 4000, 64, 1500),
+    ("o1_bf16_d32", 1, 1, 2300, 64, 700),
     ("o2_bf16_4k", 1, 2, 300, 64, 128), ("o2_bf16_4k", 1, 2, 250, 128, 77),
     ("o2_bf16_4k", 2, 16, 300, 64, 150), ("o2_bf16_4k", 2, 16, 400, 64, 330),
     ("o2_bf16_4k", 1, 2, 2000, 64, 300)])
